@@ -1,0 +1,261 @@
+"""ctypes front end of the CPU oracle (oracle/thrift_oracle.c).
+
+TEST INFRASTRUCTURE ONLY: the tests, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import this module; the product
+package never does.  Arrays are numpy, host memory, [batch, head, seq, dim];
+fp16 tensors are passed as ``np.float16`` and read bit by bit by the C side.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import numpy as np
+
+NVFP4 = 0
+MX = 1
+AXIS_D = 0
+AXIS_S = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+# THRIFT_ORACLE_LIB lets the mutation tests load a deliberately broken copy
+_LIB_PATH = os.environ.get("THRIFT_ORACLE_LIB") or os.path.join(_HERE, "libthrift_oracle.so")
+_lib = None
+
+
+def lib():
+    """Load (building first if absent) the oracle shared library."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build_oracle  # noqa: PLC0415
+
+            build_oracle.build()
+        _lib = C.CDLL(_LIB_PATH)
+        _declare(_lib)
+    return _lib
+
+
+_P = C.c_void_p
+_I = C.c_int
+_D = C.c_double
+_SZ = C.c_size_t
+
+
+def _declare(L):
+    L.tho_half_to_double.restype = _D
+    L.tho_half_to_double.argtypes = [C.c_uint16]
+    L.tho_round_to_half.restype = _D
+    L.tho_round_to_half.argtypes = [_D]
+    L.tho_e2m1_value.restype = _D
+    L.tho_e2m1_value.argtypes = [_I]
+    L.tho_e2m1_encode.restype = _I
+    L.tho_e2m1_encode.argtypes = [_D, _D]
+    L.tho_e4m3_value.restype = _D
+    L.tho_e4m3_value.argtypes = [_I]
+    L.tho_e4m3_encode_ratio.restype = _I
+    L.tho_e4m3_encode_ratio.argtypes = [_D, _D]
+    L.tho_mx_exponent.restype = _I
+    L.tho_mx_exponent.argtypes = [_D]
+    L.tho_group_size.restype = _I
+    L.tho_group_size.argtypes = [_I]
+    L.tho_pad_s.restype = _I
+    L.tho_pad_s.argtypes = [_I]
+    L.tho_kmax.restype = _I
+    L.tho_kmax.argtypes = [_I] * 6
+    L.tho_block_means.restype = None
+    L.tho_block_means.argtypes = [_P, _I, _I, _I, _I, _I, _P]
+    L.tho_block_score.restype = C.c_float
+    L.tho_block_score.argtypes = [_P, _P, _I]
+    L.tho_select.restype = None
+    L.tho_select.argtypes = [_P, _P] + [_I] * 10 + [_P, _P, _I, _P]
+    L.tho_quantize.restype = None
+    L.tho_quantize.argtypes = [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P]
+    L.tho_dequantize.restype = None
+    L.tho_dequantize.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
+    L.tho_attention.restype = None
+    L.tho_attention.argtypes = [_P] * 12 + [_I, _P, _P, _I] + [_I] * 8 + [_D, _P, _I, _P, _P]
+    L.tho_fp4_scores.restype = None
+    L.tho_fp4_scores.argtypes = [_P] * 6 + [_I] * 6 + [_P]
+    L.tho_e2m1_encode_array.restype = None
+    L.tho_e2m1_encode_array.argtypes = [_P, _P, _SZ, _P]
+    L.tho_e4m3_encode_ratio_array.restype = None
+    L.tho_e4m3_encode_ratio_array.argtypes = [_P, _P, _SZ, _P]
+    L.tho_round_to_half_array.restype = None
+    L.tho_round_to_half_array.argtypes = [_P, _SZ, _P]
+    L.tho_half_to_double_array.restype = None
+    L.tho_half_to_double_array.argtypes = [_P, _SZ, _P]
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data_as(C.c_void_p)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def group_size(fmt: int) -> int:
+    return 16 if fmt == NVFP4 else 32
+
+
+def pad_s(S: int) -> int:
+    return lib().tho_pad_s(S)
+
+
+def kmax(S, bq, bk, causal, topk_count, topk_bp) -> int:
+    return lib().tho_kmax(S, bq, bk, int(causal), topk_count, topk_bp)
+
+
+# ---- scalar / array format routines ------------------------------------
+
+def e2m1_encode(x, s):
+    x = _c(np.broadcast_to(x, np.broadcast(x, s).shape), np.float64)
+    s = _c(np.broadcast_to(s, x.shape), np.float64)
+    out = np.empty(x.shape, np.uint8)
+    lib().tho_e2m1_encode_array(_ptr(x), _ptr(s), x.size, _ptr(out))
+    return out
+
+
+def e4m3_encode_ratio(num, den):
+    num = _c(np.broadcast_to(num, np.broadcast(num, den).shape), np.float64)
+    den = _c(np.broadcast_to(den, num.shape), np.float64)
+    out = np.empty(num.shape, np.uint8)
+    lib().tho_e4m3_encode_ratio_array(_ptr(num), _ptr(den), num.size, _ptr(out))
+    return out
+
+
+def e2m1_value(code: int) -> float:
+    return lib().tho_e2m1_value(int(code))
+
+
+def e4m3_value(code: int) -> float:
+    return lib().tho_e4m3_value(int(code))
+
+
+def mx_exponent(amax: float) -> int:
+    return lib().tho_mx_exponent(float(amax))
+
+
+def round_to_half(x):
+    x = _c(x, np.float64)
+    out = np.empty_like(x)
+    lib().tho_round_to_half_array(_ptr(x), x.size, _ptr(out))
+    return out
+
+
+def half_to_double(h):
+    h = _c(h, np.float16).view(np.uint16)
+    out = np.empty(h.shape, np.float64)
+    lib().tho_half_to_double_array(_ptr(h), h.size, _ptr(out))
+    return out
+
+
+# ---- selection ------------------------------------------------------------
+
+def block_means(x16, blk):
+    x16 = _c(x16, np.float16)
+    B, H, S, D = x16.shape
+    nb = -(-S // blk)
+    out = np.empty((B, H, nb, D), np.float32)
+    lib().tho_block_means(_ptr(x16), B, H, S, D, blk, _ptr(out))
+    return out
+
+
+def select(q16, k16, bq, bk, causal, topk_count=-1, topk_bp=0, kmax_=None, with_scores=False):
+    """Per-query-block top-k: returns (idx [B,Hq,nQ,kmax] int32, cnt [B,Hq,nQ] int32, scores)."""
+    q16 = _c(q16, np.float16)
+    k16 = _c(k16, np.float16)
+    B, Hq, S, D = q16.shape
+    Hkv = k16.shape[1]
+    nq, nk = -(-S // bq), -(-S // bk)
+    km = kmax(S, bq, bk, causal, topk_count, topk_bp) if kmax_ is None else kmax_
+    idx = np.empty((B, Hq, nq, max(km, 0)), np.int32)
+    cnt = np.empty((B, Hq, nq), np.int32)
+    scores = np.empty((B, Hq, nq, nk), np.float32) if with_scores else None
+    lib().tho_select(_ptr(q16), _ptr(k16), B, Hq, Hkv, S, D, bq, bk, int(causal), topk_count,
+                     topk_bp, _ptr(idx), _ptr(cnt), km, _ptr(scores))
+    return idx, cnt, scores
+
+
+# ---- quantisation -----------------------------------------------------------
+
+class FP4Tensor:
+    """Codes, block scales and (NVFP4-style only) per-slice fp32 scales."""
+
+    def __init__(self, codes, scales, tensor_scale, fmt, axis, shape):
+        self.codes, self.scales, self.tensor_scale = codes, scales, tensor_scale
+        self.fmt, self.axis, self.shape = fmt, axis, shape
+
+
+def quantize(x16, axis, fmt) -> FP4Tensor:
+    x16 = _c(x16, np.float16)
+    B, H, S, D = x16.shape
+    g = group_size(fmt)
+    if axis == AXIS_D:
+        codes = np.empty((B, H, S, D // 2), np.uint8)
+        scales = np.empty((B, H, S, D // g), np.uint8)
+    else:
+        Sp = pad_s(S)
+        codes = np.empty((B, H, D, Sp // 2), np.uint8)
+        scales = np.empty((B, H, D, Sp // g), np.uint8)
+    ts = np.empty((B, H), np.float32) if fmt == NVFP4 else None
+    lib().tho_quantize(_ptr(x16), B, H, S, D, axis, fmt, _ptr(codes), _ptr(scales), _ptr(ts))
+    return FP4Tensor(codes, scales, ts, fmt, axis, (B, H, S, D))
+
+
+def dequantize(t: FP4Tensor):
+    B, H, S, D = t.shape
+    out = np.empty((B, H, S, D), np.float64)
+    lib().tho_dequantize(_ptr(t.codes), _ptr(t.scales), _ptr(t.tensor_scale), B, H, S, D, t.axis,
+                         t.fmt, _ptr(out))
+    return out
+
+
+def fp4_scores(q4: FP4Tensor, k4: FP4Tensor, r, c0, c1):
+    """Raw FP4-path dot products of query row r with keys [c0, c1) (B = H = 1)."""
+    _, _, S, D = q4.shape
+    out = np.empty(c1 - c0, np.float64)
+    lib().tho_fp4_scores(_ptr(q4.codes), _ptr(q4.scales), _ptr(q4.tensor_scale), _ptr(k4.codes),
+                         _ptr(k4.scales), _ptr(k4.tensor_scale), q4.fmt, S, D, r, c0, c1, _ptr(out))
+    return out
+
+
+# ---- attention ----------------------------------------------------------------
+
+def attention(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt, bq, bk,
+              causal, sm_scale=None, work=None):
+    """Forward pass.  Returns (o fp64 [B,Hq,S,D], lse fp64 [B,Hq,S]); with a
+    work list of (b, hq, i) triples only those query blocks are filled (the
+    rest stay NaN)."""
+    B, Hq, S, D = q4.shape
+    Hkv = k4.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(D)
+    q16 = None if q16 is None else _c(q16, np.float16)
+    k16 = None if k16 is None else _c(k16, np.float16)
+    v16 = None if v16 is None else _c(v16, np.float16)
+    idx = _c(idx, np.int32)
+    cnt = _c(cnt, np.int32)
+    km = idx.shape[-1]
+    o = np.full((B, Hq, S, D), np.nan, np.float64)
+    lse = np.full((B, Hq, S), np.nan, np.float64)
+    w = None if work is None else _c(np.asarray(work).reshape(-1, 3), np.int32)
+    nw = 0 if w is None else w.shape[0]
+    lib().tho_attention(_ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
+                        _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales),
+                        _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales),
+                        _ptr(v4.tensor_scale), q4.fmt, _ptr(idx), _ptr(cnt), km, B, Hq, Hkv, S, D,
+                        bq, bk, int(causal), float(sm_scale), _ptr(w), nw, _ptr(o), _ptr(lse))
+    return o, lse
+
+
+def pipeline(q16, k16, v16, fmt, bq, bk, causal, topk_count=-1, topk_bp=0, sm_scale=None,
+             work=None):
+    """Selection, quantisation of Q/K/V and attention, all on the oracle."""
+    idx, cnt, _ = select(q16, k16, bq, bk, causal, topk_count, topk_bp)
+    q4 = quantize(q16, AXIS_D, fmt)
+    k4 = quantize(k16, AXIS_D, fmt)
+    v4 = quantize(v16, AXIS_S, fmt)
+    o, lse = attention(q16, k16, v16, q4, k4, v4, idx, cnt, bq, bk, causal, sm_scale, work)
+    return dict(idx=idx, cnt=cnt, q4=q4, k4=k4, v4=v4, o=o, lse=lse)

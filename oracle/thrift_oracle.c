@@ -1,0 +1,666 @@
+/*
+ * Plain CPU oracle for the ThriftAttention forward pass.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file; only the tests, the smoke check and the CPU-baseline leg of
+ * the benchmark use it.  It shares no code, header, table or helper with the
+ * HIP library: every number format, every rounding decision and every loop
+ * below is written out again from the definitions.
+ *
+ * Source of the method: "ThriftAttention: Selective Mixed Precision for
+ * Long-Context FP4 Attention" (gist.science summaries in Dutch and French,
+ * sections "Methodologie" / "Méthodologie").  What the pages fix:
+ *   - Q and K/V are cut into blocks; each (query block i, key block j) pair is
+ *     scored by the dot product of the blocks' token means, S^_ij = qbar_i.kbar_j;
+ *   - the top-k pairs run in FP16, every other pair in FP4 (NVFP4 micro-scaling);
+ *   - both paths are merged by one online softmax in the style of
+ *     FlashAttention-2, with a two-level quantisation of the probability
+ *     blocks on the FP4 path (taken from SageAttention3);
+ *   - the FP4 path runs first, the FP16 path over the promoted blocks second.
+ * Everything else is a reading of where the pages are silent; each reading is
+ * named at the function that takes it.
+ *
+ * Arithmetic: fp64 throughout, except where the method itself fixes a
+ * precision (the FP4 / FP8 / FP16 roundings) and in the block-selection
+ * scores, whose fp32 fused-multiply-add chain is the precision the selection
+ * decision is taken in on both sides.  No fast-math, no contraction
+ * (-ffp-contract=off): every rounding is the one written.
+ *
+ * Parity pins for each function live in tests/ (see the test files' headers).
+ */
+#include "thrift_oracle.h"
+
+#include <math.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define THO_LOG2E 1.4426950408889634073599246810019
+#define THO_LN2 0.69314718055994530941723212145818
+
+/* ------------------------------------------------------------------ */
+/* fp16 (IEEE binary16) decoding and rounding                          */
+/* ------------------------------------------------------------------ */
+
+double tho_half_to_double(uint16_t h) {
+  int sign = (h >> 15) & 1;
+  int e = (h >> 10) & 0x1F;
+  int m = h & 0x3FF;
+  double v;
+  if (e == 0) {
+    v = ldexp((double)m, -24); /* subnormal: m * 2^-24 */
+  } else if (e == 31) {
+    v = m ? NAN : INFINITY;
+  } else {
+    v = ldexp((double)(1024 + m), e - 25); /* (1 + m/1024) * 2^(e-15) */
+  }
+  return sign ? -v : v;
+}
+
+/* Round a double to the nearest binary16 value, ties to even (the value is
+ * returned as a double).  Overflow gives +-inf, as IEEE rounding does. */
+double tho_round_to_half(double x) {
+  if (x == 0.0 || isnan(x) || isinf(x)) return x;
+  double a = fabs(x);
+  int e;
+  frexp(a, &e); /* a = f * 2^e, f in [0.5, 1) */
+  int ulp_exp = e - 11; /* 11 significant bits */
+  if (ulp_exp < -24) ulp_exp = -24; /* subnormal spacing */
+  double q = nearbyint(ldexp(a, -ulp_exp)); /* default mode: ties to even */
+  double r = ldexp(q, ulp_exp);
+  if (r > 65504.0) r = INFINITY;
+  return x < 0 ? -r : r;
+}
+
+/* ------------------------------------------------------------------ */
+/* FP4 E2M1, FP8 E4M3 and E8M0 (OCP microscaling formats)              */
+/* ------------------------------------------------------------------ */
+
+/* E2M1: one sign bit, two exponent bits (bias 1), one mantissa bit.  The
+ * pages give the bit split and the count of 15 distinct values; the values
+ * themselves follow from the split: 0, 0.5 (subnormal), 1, 1.5, 2, 3, 4, 6. */
+static const double tho_e2m1_mag[8] = {0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0};
+
+double tho_e2m1_value(int code) {
+  double v = tho_e2m1_mag[code & 7];
+  return (code & 8) ? -v : v;
+}
+
+/* Code of the E2M1 value nearest to x/s, ties to the even code, magnitudes
+ * above 6 saturating to 6, the sign of x kept (so -0 and small negatives give
+ * code 8).  s > 0.  The decision is exact: |x| is compared with midpoint*s,
+ * and callers pass an s whose product with a 3-bit midpoint is exact in fp64. */
+int tho_e2m1_encode(double x, double s) {
+  static const double mid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+  double a = fabs(x);
+  int code = 0;
+  for (int k = 0; k < 7; ++k) {
+    double t = mid[k] * s;
+    if (a > t || (a == t && ((k + 1) & 1) == 0)) code = k + 1;
+  }
+  return code | (signbit(x) ? 8 : 0);
+}
+
+/* E4M3 ("FN" variant): bias 7, three mantissa bits, no infinities, codes
+ * 0x7F/0xFF are NaN, largest finite 448, subnormals m * 2^-9. */
+double tho_e4m3_value(int code) {
+  int e = (code >> 3) & 0xF;
+  int m = code & 7;
+  double v;
+  if ((code & 0x7F) == 0x7F) return NAN;
+  if (e == 0)
+    v = ldexp((double)m, -9);
+  else
+    v = ldexp((double)(8 + m), e - 10); /* (1 + m/8) * 2^(e-7) */
+  return (code & 0x80) ? -v : v;
+}
+
+/* Non-negative E4M3 code nearest to num/den (num >= 0, den > 0), ties to the
+ * even code, saturating at 448.  Exact: num is compared with midpoint*den. */
+int tho_e4m3_encode_ratio(double num, double den) {
+  int c = 0;
+  for (int k = 0; k < 126; ++k) {
+    double mid = 0.5 * (tho_e4m3_value(k) + tho_e4m3_value(k + 1));
+    double t = mid * den;
+    if (num > t || (num == t && ((k + 1) & 1) == 0))
+      c = k + 1;
+    else
+      break;
+  }
+  return c;
+}
+
+/* MX shared exponent for an E2M1 group: the largest power of two not above
+ * amax, divided by 2^2 (the largest power of two in E2M1), clamped to the
+ * E8M0 range.  amax == 0 gives the smallest scale, 2^-127. */
+int tho_mx_exponent(double amax) {
+  if (!(amax > 0.0)) return -127;
+  int e;
+  frexp(amax, &e); /* amax in [2^(e-1), 2^e) */
+  int x = (e - 1) - 2;
+  if (x < -127) x = -127;
+  if (x > 127) x = 127;
+  return x;
+}
+
+/* ------------------------------------------------------------------ */
+/* Block selection (pages: "Heuristische Blokkenselectie")             */
+/* ------------------------------------------------------------------ */
+
+static int tho_cdiv(int a, int b) { return (a + b - 1) / b; }
+
+/* Valid key blocks of query block i: every block for non-causal attention;
+ * for causal attention (query and key sequences aligned at their starts)
+ * every block holding at least one key not after the block's last query. */
+static int tho_valid_blocks(int i, int S, int bq, int bk, int causal) {
+  int nk = tho_cdiv(S, bk);
+  if (!causal) return nk;
+  int last_q = (i + 1) * bq < S ? (i + 1) * bq - 1 : S - 1;
+  return last_q / bk + 1;
+}
+
+/* Budget of promoted blocks for a query block with n valid key blocks:
+ * topk_count >= 0 is an absolute count, otherwise ceil(n * topk_bp / 10^4)
+ * (basis points of the valid pairs of that query block); never above n. */
+static int tho_budget(int n, int topk_count, int topk_bp) {
+  long long k;
+  if (topk_count >= 0)
+    k = topk_count;
+  else
+    k = ((long long)n * topk_bp + 9999) / 10000;
+  return (int)(k < n ? k : n);
+}
+
+int tho_kmax(int S, int bq, int bk, int causal, int topk_count, int topk_bp) {
+  int nq = tho_cdiv(S, bq), km = 0;
+  for (int i = 0; i < nq; ++i) {
+    int k = tho_budget(tho_valid_blocks(i, S, bq, bk, causal), topk_count, topk_bp);
+    if (k > km) km = k;
+  }
+  return km;
+}
+
+/* Token mean of each block of rows (reading of the pages' "token means":
+ * the plain arithmetic mean over the block's valid rows, masked or not).
+ * The sum is formed in fp64, which is exact whatever the order: every fp16
+ * value is an integer multiple of 2^-24 below 2^16 in magnitude, so a sum of
+ * up to 2^13 of them is an integer multiple of 2^-24 below 2^53.  It is then
+ * divided by the row count in fp64 and rounded once to fp32.
+ * means: [B, H, nblk, D]. */
+void tho_block_means(const uint16_t* x16, int B, int H, int S, int D, int blk, float* means) {
+  int nb = tho_cdiv(S, blk);
+  for (int bh = 0; bh < B * H; ++bh) {
+    const uint16_t* x = x16 + (size_t)bh * S * D;
+    for (int j = 0; j < nb; ++j) {
+      int r0 = j * blk, r1 = r0 + blk < S ? r0 + blk : S;
+      for (int d = 0; d < D; ++d) {
+        double sum = 0.0;
+        for (int r = r0; r < r1; ++r) sum += tho_half_to_double(x[(size_t)r * D + d]);
+        means[((size_t)bh * nb + j) * D + d] = (float)(sum / (double)(r1 - r0));
+      }
+    }
+  }
+}
+
+/* Importance score of a block pair: the fp32 dot product of the two means,
+ * one fused multiply-add per channel, channels in ascending order. */
+float tho_block_score(const float* qm, const float* km, int D) {
+  float s = 0.0f;
+  for (int d = 0; d < D; ++d) s = fmaf(qm[d], km[d], s);
+  return s;
+}
+
+typedef struct {
+  float s;
+  int j;
+} tho_cand;
+
+/* Higher score first; equal scores (with -0 == +0) by lower block index. */
+static int tho_cand_cmp(const void* a, const void* b) {
+  const tho_cand* x = (const tho_cand*)a;
+  const tho_cand* y = (const tho_cand*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  return x->j - y->j;
+}
+
+static int tho_int_cmp(const void* a, const void* b) {
+  int x = *(const int*)a, y = *(const int*)b;
+  return (x > y) - (x < y);
+}
+
+/* Per query block (reading of "the top-k highest-scoring block pairs": the
+ * budget is taken per query block, so that every query block gets its share;
+ * the pages' "5% of query-key blocks" is then met per block row), keep the
+ * k_i best-scoring valid key blocks.  The query head hq reads key head
+ * hq / (Hq / Hkv).  idx: [B, Hq, nQ, kmax], ascending, padded with -1;
+ * cnt: [B, Hq, nQ].  scores (optional): [B, Hq, nQ, nK], NaN where invalid. */
+void tho_select(const uint16_t* q16, const uint16_t* k16, int B, int Hq, int Hkv, int S, int D,
+                int bq, int bk, int causal, int topk_count, int topk_bp, int32_t* idx,
+                int32_t* cnt, int kmax, float* scores) {
+  int nq = tho_cdiv(S, bq), nk = tho_cdiv(S, bk), G = Hq / Hkv;
+  float* qm = (float*)malloc(sizeof(float) * (size_t)B * Hq * nq * D);
+  float* km = (float*)malloc(sizeof(float) * (size_t)B * Hkv * nk * D);
+  tho_block_means(q16, B, Hq, S, D, bq, qm);
+  tho_block_means(k16, B, Hkv, S, D, bk, km);
+  tho_cand* cand = (tho_cand*)malloc(sizeof(tho_cand) * (size_t)nk);
+  int* sel = (int*)malloc(sizeof(int) * (size_t)nk);
+  for (int b = 0; b < B; ++b)
+    for (int hq = 0; hq < Hq; ++hq) {
+      int hk = hq / G;
+      for (int i = 0; i < nq; ++i) {
+        size_t row = ((size_t)b * Hq + hq) * nq + i;
+        int n = tho_valid_blocks(i, S, bq, bk, causal);
+        int k = tho_budget(n, topk_count, topk_bp);
+        const float* qv = qm + row * D;
+        for (int j = 0; j < n; ++j) {
+          cand[j].s = tho_block_score(qv, km + (((size_t)b * Hkv + hk) * nk + j) * D, D);
+          cand[j].j = j;
+        }
+        if (scores)
+          for (int j = 0; j < nk; ++j) scores[row * nk + j] = j < n ? cand[j].s : NAN;
+        qsort(cand, (size_t)n, sizeof(tho_cand), tho_cand_cmp);
+        for (int t = 0; t < k; ++t) sel[t] = cand[t].j;
+        qsort(sel, (size_t)k, sizeof(int), tho_int_cmp);
+        for (int t = 0; t < kmax; ++t) idx[row * kmax + t] = t < k ? sel[t] : -1;
+        cnt[row] = k;
+      }
+    }
+  free(sel);
+  free(cand);
+  free(km);
+  free(qm);
+}
+
+/* ------------------------------------------------------------------ */
+/* FP4 quantisation of Q, K, V (pages: FP4 path in NVFP4 micro-scaling) */
+/* ------------------------------------------------------------------ */
+
+/* Encode one group of n values with the scale rule of the format.
+ *  NVFP4-style (per-16 E4M3 block scale under a per-slice fp32 scale sg):
+ *    block byte = E4M3(amax_g / (6 sg)), element = E2M1(x / (E4M3 value * sg));
+ *    a block whose scale rounds to 0 gets all-zero codes.
+ *  MXFP4 (per-32 E8M0): exponent X from the group maximum, element = E2M1(x / 2^X).
+ * Codes go to out[] one per value (unpacked); the scale byte is returned. */
+static int tho_encode_group(const double* x, int n, int fmt, double sg, uint8_t* out) {
+  double amax = 0.0;
+  for (int t = 0; t < n; ++t)
+    if (fabs(x[t]) > amax) amax = fabs(x[t]);
+  if (fmt == THO_NVFP4) {
+    int sb = tho_e4m3_encode_ratio(amax, 6.0 * sg);
+    double s = tho_e4m3_value(sb) * sg; /* exact: 4 x 24 significant bits */
+    for (int t = 0; t < n; ++t) out[t] = (uint8_t)(s > 0.0 ? tho_e2m1_encode(x[t], s) : 0);
+    return sb;
+  } else {
+    int X = tho_mx_exponent(amax);
+    double s = ldexp(1.0, X);
+    for (int t = 0; t < n; ++t) out[t] = (uint8_t)tho_e2m1_encode(x[t], s);
+    return X + 127;
+  }
+}
+
+/* The per-slice fp32 scale of the NVFP4-style format (reading: one scale per
+ * (batch, head) slice, so that the largest block maps onto 6 * 448):
+ * sg = amax / (6 * 448) rounded to fp32, or 1 for an all-zero slice. */
+static float tho_slice_scale(const uint16_t* x, size_t n) {
+  double amax = 0.0;
+  for (size_t t = 0; t < n; ++t) {
+    double v = fabs(tho_half_to_double(x[t]));
+    if (v > amax) amax = v;
+  }
+  return amax > 0.0 ? (float)(amax / 2688.0) : 1.0f;
+}
+
+int tho_group_size(int fmt) { return fmt == THO_NVFP4 ? 16 : 32; }
+int tho_pad_s(int S) { return tho_cdiv(S, 64) * 64; }
+
+/* Quantise x16 [B, H, S, D].
+ *  axis THO_AXIS_D (Q, K): groups run along D; codes [B,H,S,D/2], scales [B,H,S,D/g].
+ *  axis THO_AXIS_S (V, stored transposed): groups run along the sequence;
+ *    codes [B,H,D,Sp/2], scales [B,H,D,Sp/g], Sp = S rounded up to 64, the
+ *    padding tokens being zeros.
+ * Two codes per byte, the even element in the low nibble.  tensor_scale
+ * [B,H] is written for the NVFP4-style format only. */
+void tho_quantize(const uint16_t* x16, int B, int H, int S, int D, int axis, int fmt,
+                  uint8_t* codes, uint8_t* scales, float* tensor_scale) {
+  int g = tho_group_size(fmt);
+  int Sp = tho_pad_s(S);
+  double vals[32];
+  uint8_t c[32];
+  for (int bh = 0; bh < B * H; ++bh) {
+    const uint16_t* x = x16 + (size_t)bh * S * D;
+    double sg = 1.0;
+    if (fmt == THO_NVFP4) {
+      float f = tho_slice_scale(x, (size_t)S * D);
+      tensor_scale[bh] = f;
+      sg = f;
+    }
+    if (axis == THO_AXIS_D) {
+      for (int s = 0; s < S; ++s)
+        for (int gi = 0; gi < D / g; ++gi) {
+          for (int t = 0; t < g; ++t) vals[t] = tho_half_to_double(x[(size_t)s * D + gi * g + t]);
+          int sb = tho_encode_group(vals, g, fmt, sg, c);
+          scales[((size_t)bh * S + s) * (D / g) + gi] = (uint8_t)sb;
+          uint8_t* dst = codes + ((size_t)bh * S + s) * (D / 2) + gi * g / 2;
+          for (int t = 0; t < g; t += 2) dst[t / 2] = (uint8_t)(c[t] | (c[t + 1] << 4));
+        }
+    } else {
+      for (int d = 0; d < D; ++d)
+        for (int gi = 0; gi < Sp / g; ++gi) {
+          for (int t = 0; t < g; ++t) {
+            int s = gi * g + t;
+            vals[t] = s < S ? tho_half_to_double(x[(size_t)s * D + d]) : 0.0;
+          }
+          int sb = tho_encode_group(vals, g, fmt, sg, c);
+          scales[((size_t)bh * D + d) * (Sp / g) + gi] = (uint8_t)sb;
+          uint8_t* dst = codes + ((size_t)bh * D + d) * (Sp / 2) + gi * g / 2;
+          for (int t = 0; t < g; t += 2) dst[t / 2] = (uint8_t)(c[t] | (c[t + 1] << 4));
+        }
+    }
+  }
+}
+
+/* Decoded scale of one group. */
+static double tho_group_scale(int fmt, int byte, double sg) {
+  return fmt == THO_NVFP4 ? tho_e4m3_value(byte) * sg : ldexp(1.0, byte - 127);
+}
+
+/* Dequantise row s of slice bh of a tensor quantised along D. */
+void tho_dequant_row(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale,
+                     size_t bh, int S, int D, int s, int fmt, double* out) {
+  int g = tho_group_size(fmt);
+  double sg = fmt == THO_NVFP4 ? (double)tensor_scale[bh] : 1.0;
+  for (int d = 0; d < D; ++d) {
+    size_t e = ((size_t)bh * S + s) * D + d;
+    size_t si = ((size_t)bh * S + s) * (D / g) + d / g;
+    int code = (codes[e / 2] >> (4 * (e & 1))) & 0xF;
+    out[d] = tho_e2m1_value(code) * tho_group_scale(fmt, scales[si], sg);
+  }
+}
+
+/* Dequantise a tensor written by tho_quantize back to fp64, in the original
+ * [B, H, S, D] orientation (padding dropped). */
+void tho_dequantize(const uint8_t* codes, const uint8_t* scales, const float* tensor_scale, int B,
+                    int H, int S, int D, int axis, int fmt, double* out) {
+  int g = tho_group_size(fmt);
+  int Sp = tho_pad_s(S);
+  for (int bh = 0; bh < B * H; ++bh) {
+    double sg = fmt == THO_NVFP4 ? (double)tensor_scale[bh] : 1.0;
+    for (int s = 0; s < S; ++s)
+      for (int d = 0; d < D; ++d) {
+        size_t e, si;
+        if (axis == THO_AXIS_D) {
+          e = ((size_t)bh * S + s) * D + d;
+          si = ((size_t)bh * S + s) * (D / g) + d / g;
+        } else {
+          e = ((size_t)bh * D + d) * Sp + s;
+          si = ((size_t)bh * D + d) * (Sp / g) + s / g;
+        }
+        int code = (codes[e / 2] >> (4 * (e & 1))) & 0xF;
+        out[((size_t)bh * S + s) * D + d] = tho_e2m1_value(code) * tho_group_scale(fmt, scales[si], sg);
+      }
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* Attention forward (pages: "Gemengd-Precisie Berekening & Samenvoeging") */
+/* ------------------------------------------------------------------ */
+
+/* Two-level quantisation of one probability tile on the FP4 path (the pages
+ * take the scheme from SageAttention3 without spelling it out; reading):
+ *   level 1, per query row and key tile: the tile's scores t (log2 units)
+ *     are exponentiated against the tile maximum;
+ *   level 2, per group of keys (16 for NVFP4-style, 32 for MX) aligned like
+ *     the V groups: a block scale and E2M1 codes.
+ *  NVFP4-style: v = 2688 * 2^(t - mt) (the row maximum lands on 6 * 448),
+ *     block scale E4M3(max v / 6), code E2M1(v / block scale); the
+ *     dequantised probability relative to 2^mt is code * scale / 2688.
+ *  MX: v = 2^(t - z) with z = ceil(mt) (a power-of-two level-1 factor; the
+ *     E8M0 block scales absorb any power of two, so every integer z gives the
+ *     same codes), block exponent X from max v, code E2M1(v / 2^X); the
+ *     dequantised probability relative to 2^z is code * 2^X.
+ * Masked keys (mask[c] != 0) hold probability 0.
+ * pq[c] receives the dequantised probability relative to 2^(*ref). */
+static void tho_quantize_p_tile(const double* t, const int* mask, int n, int fmt, double mt,
+                                double* pq, double* ref) {
+  int g = tho_group_size(fmt);
+  double v[64];
+  if (fmt == THO_NVFP4) {
+    for (int c = 0; c < n; ++c) v[c] = mask[c] ? 0.0 : 2688.0 * exp2(t[c] - mt);
+    *ref = mt;
+  } else {
+    double z = ceil(mt);
+    for (int c = 0; c < n; ++c) v[c] = mask[c] ? 0.0 : exp2(t[c] - z);
+    *ref = z;
+  }
+  for (int g0 = 0; g0 < n; g0 += g) {
+    int g1 = g0 + g < n ? g0 + g : n;
+    double amax = 0.0;
+    for (int c = g0; c < g1; ++c)
+      if (v[c] > amax) amax = v[c];
+    if (fmt == THO_NVFP4) {
+      double s2 = tho_e4m3_value(tho_e4m3_encode_ratio(amax, 6.0));
+      for (int c = g0; c < g1; ++c)
+        pq[c] = s2 > 0.0 ? tho_e2m1_value(tho_e2m1_encode(v[c], s2)) * s2 / 2688.0 : 0.0;
+    } else {
+      double s2 = ldexp(1.0, tho_mx_exponent(amax));
+      for (int c = g0; c < g1; ++c) pq[c] = tho_e2m1_value(tho_e2m1_encode(v[c], s2)) * s2;
+    }
+  }
+}
+
+typedef struct {
+  int B, Hq, Hkv, S, D, bq, bk, causal, fmt, kmax;
+  double sm_scale;
+  const uint16_t *q16, *k16, *v16;
+  const uint8_t *q4c, *q4s; /* FP4 query codes and scales as quantised */
+  const float* q4t;
+  const double *k4, *v4; /* dequantised FP4 keys and values, [B,Hkv,S,D] */
+  const int32_t *idx, *cnt;
+} tho_attn_args;
+
+/* One query row r of query block i of head (b, hq). */
+static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, double* o_row,
+                           double* lse_out) {
+  int D = a->D, S = a->S, bk = a->bk;
+  int hk = hq / (a->Hq / a->Hkv);
+  int nq = tho_cdiv(S, a->bq);
+  size_t qoff = (((size_t)b * a->Hq + hq) * S + r) * D;
+  size_t kvbase = ((size_t)b * a->Hkv + hk) * S;
+  const int32_t* sel = a->idx + (((size_t)b * a->Hq + hq) * nq + i) * a->kmax;
+  int nsel = a->cnt[((size_t)b * a->Hq + hq) * nq + i];
+  int nvalid = tho_valid_blocks(i, S, a->bq, bk, a->causal);
+  double t[64], pq[64];
+  int mask[64];
+  double* acc = (double*)calloc((size_t)D, sizeof(double));
+  double* qh = (double*)malloc(sizeof(double) * (size_t)D);
+  double* q4 = (double*)malloc(sizeof(double) * (size_t)D);
+  double m = -INFINITY, l = 0.0;
+  tho_dequant_row(a->q4c, a->q4s, a->q4t, (size_t)b * a->Hq + hq, S, D, r, a->fmt, q4);
+
+  /* FP4 path first, over every valid key block not promoted, ascending. */
+  int sp = 0;
+  for (int j = 0; j < nvalid; ++j) {
+    if (sp < nsel && sel[sp] == j) {
+      ++sp;
+      continue;
+    }
+    int c0 = j * bk, n = (c0 + bk < S ? c0 + bk : S) - c0;
+    double mt = -INFINITY;
+    for (int c = 0; c < n; ++c) {
+      mask[c] = a->causal && (c0 + c > r);
+      double s = 0.0;
+      if (!mask[c]) {
+        const double* qv = q4;
+        const double* kv = a->k4 + (kvbase + c0 + c) * D;
+        for (int d = 0; d < D; ++d) s += qv[d] * kv[d];
+      }
+      t[c] = mask[c] ? -INFINITY : s * a->sm_scale * THO_LOG2E;
+      if (t[c] > mt) mt = t[c];
+    }
+    if (mt == -INFINITY) continue; /* every key of this block is masked for row r */
+    double ref;
+    tho_quantize_p_tile(t, mask, n, a->fmt, mt, pq, &ref);
+    double m_new = m > mt ? m : mt;
+    double alpha = exp2(m - m_new); /* 0 when m = -inf */
+    double w = exp2(ref - m_new);
+    double psum = 0.0;
+    for (int c = 0; c < n; ++c)
+      if (!mask[c]) psum += exp2(t[c] - m_new);
+    l = alpha * l + psum;
+    for (int d = 0; d < D; ++d) {
+      double pv = 0.0;
+      for (int c = 0; c < n; ++c) pv += pq[c] * a->v4[(kvbase + c0 + c) * D + d];
+      acc[d] = alpha * acc[d] + w * pv;
+    }
+    m = m_new;
+  }
+
+  /* FP16 path second, over the promoted blocks, ascending; the FP16 query
+   * row is read only here. */
+  if (nsel > 0)
+    for (int d = 0; d < D; ++d) qh[d] = tho_half_to_double(a->q16[qoff + d]);
+  for (int p = 0; p < nsel; ++p) {
+    int j = sel[p];
+    int c0 = j * bk, n = (c0 + bk < S ? c0 + bk : S) - c0;
+    double mt = -INFINITY;
+    for (int c = 0; c < n; ++c) {
+      mask[c] = a->causal && (c0 + c > r);
+      double s = 0.0;
+      if (!mask[c])
+        for (int d = 0; d < D; ++d)
+          s += qh[d] * tho_half_to_double(a->k16[(kvbase + c0 + c) * D + d]);
+      t[c] = mask[c] ? -INFINITY : s * a->sm_scale * THO_LOG2E;
+      if (t[c] > mt) mt = t[c];
+    }
+    if (mt == -INFINITY) continue;
+    double m_new = m > mt ? m : mt;
+    double alpha = exp2(m - m_new);
+    /* The probabilities enter the FP16 product as fp16 values.  Reading: they
+     * are rounded to fp16 on a power-of-two footing, as fp16(2^(t - z)) with
+     * z = ceil(m_new), which rounds 2^t to fp16's 11 significant bits
+     * whichever integer z is used. */
+    double z = ceil(m_new);
+    double psum = 0.0;
+    for (int c = 0; c < n; ++c) {
+      if (mask[c]) {
+        pq[c] = 0.0;
+        continue;
+      }
+      psum += exp2(t[c] - m_new);
+      pq[c] = tho_round_to_half(exp2(t[c] - z)) * exp2(z - m_new);
+    }
+    l = alpha * l + psum;
+    for (int d = 0; d < D; ++d) {
+      double pv = 0.0;
+      for (int c = 0; c < n; ++c)
+        if (!mask[c]) pv += pq[c] * tho_half_to_double(a->v16[(kvbase + c0 + c) * D + d]);
+      acc[d] = alpha * acc[d] + pv;
+    }
+    m = m_new;
+  }
+
+  for (int d = 0; d < D; ++d) o_row[d] = acc[d] / l;
+  if (lse_out) *lse_out = m * THO_LN2 + log(l);
+  free(q4);
+  free(qh);
+  free(acc);
+}
+
+/* Full forward for a list of work items (b, hq, i) (NULL: all of them).
+ * q4/k4/v4 are the FP4 tensors as written by tho_quantize (V along the
+ * sequence axis); q16/k16/v16 may be NULL when no block is promoted.
+ * o: [B, Hq, S, D] fp64 and lse: [B, Hq, S] (may be NULL); rows outside the
+ * work items are left untouched. */
+void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
+                   const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
+                   const uint8_t* k4s, const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
+                   const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                   int B, int Hq, int Hkv, int S, int D, int bq, int bk, int causal,
+                   double sm_scale, const int32_t* work, int nwork, double* o, double* lse) {
+  tho_attn_args a;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.S = S;
+  a.D = D;
+  a.bq = bq;
+  a.bk = bk;
+  a.causal = causal;
+  a.fmt = fmt;
+  a.kmax = kmax;
+  a.sm_scale = sm_scale;
+  a.q16 = q16;
+  a.k16 = k16;
+  a.v16 = v16;
+  a.idx = idx;
+  a.cnt = cnt;
+  double* k4 = (double*)malloc(sizeof(double) * (size_t)B * Hkv * S * D);
+  double* v4 = (double*)malloc(sizeof(double) * (size_t)B * Hkv * S * D);
+  tho_dequantize(k4c, k4s, k4t, B, Hkv, S, D, THO_AXIS_D, fmt, k4);
+  tho_dequantize(v4c, v4s, v4t, B, Hkv, S, D, THO_AXIS_S, fmt, v4);
+  a.q4c = q4c;
+  a.q4s = q4s;
+  a.q4t = q4t;
+  a.k4 = k4;
+  a.v4 = v4;
+  int nq = tho_cdiv(S, bq);
+  int total = work ? nwork : B * Hq * nq;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int w = 0; w < total; ++w) {
+    int b, hq, i;
+    if (work) {
+      b = work[3 * w];
+      hq = work[3 * w + 1];
+      i = work[3 * w + 2];
+    } else {
+      b = w / (Hq * nq);
+      hq = (w / nq) % Hq;
+      i = w % nq;
+    }
+    int r0 = i * bq, r1 = r0 + bq < S ? r0 + bq : S;
+    for (int r = r0; r < r1; ++r) {
+      size_t row = ((size_t)b * Hq + hq) * S + r;
+      tho_attend_row(&a, b, hq, i, r, o + row * D, lse ? lse + row : NULL);
+    }
+  }
+  free(v4);
+  free(k4);
+}
+
+/* Scores of the FP4 path for one query row against keys [c0, c1) (test hook:
+ * the raw dot products of the dequantised operands, before sm_scale). */
+void tho_fp4_scores(const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
+                    const uint8_t* k4s, const float* k4t, int fmt, int S, int D, int r, int c0,
+                    int c1, double* out) {
+  double* q = (double*)malloc(sizeof(double) * (size_t)S * D);
+  double* k = (double*)malloc(sizeof(double) * (size_t)S * D);
+  tho_dequantize(q4c, q4s, q4t, 1, 1, S, D, THO_AXIS_D, fmt, q);
+  tho_dequantize(k4c, k4s, k4t, 1, 1, S, D, THO_AXIS_D, fmt, k);
+  for (int c = c0; c < c1; ++c) {
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) s += q[(size_t)r * D + d] * k[(size_t)c * D + d];
+    out[c - c0] = s;
+  }
+  free(k);
+  free(q);
+}
+
+/* ------------------------------------------------------------------ */
+/* Array forms of the scalar format routines (test sweeps)            */
+/* ------------------------------------------------------------------ */
+
+void tho_e2m1_encode_array(const double* x, const double* s, size_t n, uint8_t* out) {
+  for (size_t t = 0; t < n; ++t) out[t] = (uint8_t)tho_e2m1_encode(x[t], s[t]);
+}
+
+void tho_e4m3_encode_ratio_array(const double* num, const double* den, size_t n, uint8_t* out) {
+  for (size_t t = 0; t < n; ++t) out[t] = (uint8_t)tho_e4m3_encode_ratio(num[t], den[t]);
+}
+
+void tho_round_to_half_array(const double* x, size_t n, double* out) {
+  for (size_t t = 0; t < n; ++t) out[t] = tho_round_to_half(x[t]);
+}
+
+void tho_half_to_double_array(const uint16_t* h, size_t n, double* out) {
+  for (size_t t = 0; t < n; ++t) out[t] = tho_half_to_double(h[t]);
+}

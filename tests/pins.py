@@ -1,0 +1,188 @@
+"""Independent restatements used to pin the oracle (test helpers only).
+
+Nothing here calls the oracle's C code: formats are rebuilt from their bit
+fields, roundings by brute-force nearest-value search, and the attention
+forward as a dense two-pass computation, so that a slip in the oracle's own
+version (a dropped term, a wrong sign, a transposed operand) shows up as a
+disagreement.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+LOG2E = 1.4426950408889634
+LN2 = 0.6931471805599453
+
+
+def e2m1_values_from_bits():
+    """E2M1 (1 sign, 2 exponent bits with bias 1, 1 mantissa bit)."""
+    out = []
+    for code in range(16):
+        s, e, m = code >> 3, (code >> 1) & 3, code & 1
+        mag = (m / 2.0) if e == 0 else 2.0 ** (e - 1) * (1.0 + m / 2.0)
+        out.append(-mag if s else mag)
+    return np.array(out)
+
+
+def e4m3_values_from_bits():
+    """Non-negative finite E4M3 values, codes 0..126 (bias 7, 3 mantissa bits)."""
+    out = []
+    for code in range(127):
+        e, m = code >> 3, code & 7
+        out.append(m * 2.0 ** -9 if e == 0 else 2.0 ** (e - 7) * (1.0 + m / 8.0))
+    return np.array(out)
+
+
+E2M1_POS = e2m1_values_from_bits()[:8]
+E4M3_POS = e4m3_values_from_bits()
+
+
+def nearest_code(q, table):
+    """Brute-force nearest entry of an ascending non-negative table for |q|,
+    ties to the even code; values past the end saturate to the last entry."""
+    q = np.abs(np.asarray(q, np.float64))
+    d = np.abs(q[..., None] - table)
+    best = d.min(axis=-1, keepdims=True)
+    cand = d == best
+    idx = np.arange(len(table))
+    # among tied candidates prefer the even code
+    even = cand & (idx % 2 == 0)
+    has_even = even.any(axis=-1)
+    first_even = np.argmax(even, axis=-1)
+    first = np.argmax(cand, axis=-1)
+    return np.where(has_even, first_even, first)
+
+
+def e2m1_code(x, s):
+    x = np.asarray(x, np.float64)
+    c = nearest_code(x / s, E2M1_POS)
+    return c | np.where(np.signbit(x), 8, 0)
+
+
+def mx_exponent(amax):
+    amax = np.asarray(amax, np.float64)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))
+    x = np.clip(e - 1 - 2, -127, 127)
+    return np.where(amax > 0, x, -127)
+
+
+def decode_fp4(codes_u8, scales_u8, tensor_scale, fmt, axis, shape):
+    """Decode FP4 tensors (two codes per byte, even element in the low nibble)
+    to fp64 [B, H, S, D]."""
+    B, H, S, D = shape
+    lo = codes_u8 & 0xF
+    hi = codes_u8 >> 4
+    codes = np.stack([lo, hi], -1).reshape(*codes_u8.shape[:-1], -1)
+    vals = e2m1_values_from_bits()[codes]
+    g = 16 if fmt == 0 else 32
+    if fmt == 0:
+        sc = e4m3_values_from_bits()[scales_u8.astype(np.int64) & 0x7F] * np.asarray(
+            tensor_scale, np.float64).reshape(B, H, 1, 1)
+    else:
+        sc = 2.0 ** (scales_u8.astype(np.float64) - 127)
+    vals = vals * np.repeat(sc, g, axis=-1)
+    if axis == 0:
+        return vals
+    return np.swapaxes(vals[..., :S], -1, -2)
+
+
+def valid_blocks(i, S, bq, bk, causal):
+    nk = -(-S // bk)
+    if not causal:
+        return nk
+    return (min(S, (i + 1) * bq) - 1) // bk + 1
+
+
+def fp16_round(x):
+    return np.asarray(x, np.float64).astype(np.float16).astype(np.float64)
+
+
+def quantize_p_tile(t, mask, fmt):
+    """Two-level P quantisation of one tile row (same reading as the oracle,
+    restated with brute-force rounding).  Returns (pq, ref): probabilities
+    relative to 2^ref."""
+    mt = np.max(np.where(mask, -np.inf, t))
+    n = len(t)
+    pq = np.zeros(n)
+    if fmt == 0:
+        v = np.where(mask, 0.0, 2688.0 * np.exp2(np.where(mask, 0, t) - mt))
+        ref = mt
+        for g0 in range(0, n, 16):
+            seg = v[g0:g0 + 16]
+            s2 = E4M3_POS[nearest_code(seg.max() / 6.0, E4M3_POS)]
+            if s2 > 0:
+                pq[g0:g0 + 16] = E2M1_POS[nearest_code(seg / s2, E2M1_POS)] * s2 / 2688.0
+    else:
+        z = np.ceil(mt)
+        v = np.where(mask, 0.0, np.exp2(np.where(mask, 0, t) - z))
+        ref = z
+        for g0 in range(0, n, 32):
+            seg = v[g0:g0 + 32]
+            s2 = 2.0 ** mx_exponent(seg.max())
+            pq[g0:g0 + 32] = E2M1_POS[nearest_code(seg / s2, E2M1_POS)] * s2
+    return pq, ref
+
+
+def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal, sm_scale):
+    """Dense two-pass restatement of the forward pass: every score first,
+    then one global maximum per row, then the weighted sum.  q4/k4/v4 and
+    q16/k16/v16 are fp64 [B,H,S,D] (dequantised FP4 / decoded fp16)."""
+    B, Hq, S, D = q4.shape
+    Hkv = k4.shape[1]
+    G = Hq // Hkv
+    nq, nk = -(-S // bq), -(-S // bk)
+    O = np.zeros((B, Hq, S, D))
+    L = np.zeros((B, Hq, S))
+    for b in range(B):
+        for hq in range(Hq):
+            hk = hq // G
+            t4 = (q4[b, hq] @ k4[b, hk].T) * sm_scale * LOG2E
+            t16 = None if q16 is None else (q16[b, hq] @ k16[b, hk].T) * sm_scale * LOG2E
+            for i in range(nq):
+                promoted = set(int(j) for j in idx[b, hq, i, : cnt[b, hq, i]])
+                nval = valid_blocks(i, S, bq, bk, causal)
+                for r in range(i * bq, min(S, (i + 1) * bq)):
+                    tiles = []  # (t row, mask, is16, c0)
+                    for j in range(nval):
+                        c0, c1 = j * bk, min(S, (j + 1) * bk)
+                        keys = np.arange(c0, c1)
+                        mask = (keys > r) if causal else np.zeros(len(keys), bool)
+                        if mask.all():
+                            continue
+                        src = t16 if j in promoted else t4
+                        tiles.append((src[r, c0:c1], mask, j in promoted, c0, c1))
+                    M = max(np.max(np.where(m, -np.inf, t)) for t, m, _, _, _ in tiles)
+                    l = 0.0
+                    acc = np.zeros(D)
+                    for t, m, is16, c0, c1 in tiles:
+                        e = np.where(m, 0.0, np.exp2(np.where(m, 0, t) - M))
+                        l += e.sum()
+                        if is16:
+                            z = np.ceil(M)
+                            p = np.where(m, 0.0, fp16_round(np.exp2(np.where(m, 0, t) - z))) * np.exp2(z - M)
+                            acc += p @ v16[b, hk, c0:c1]
+                        else:
+                            pq, ref = quantize_p_tile(t, m, fmt)
+                            acc += (pq * np.exp2(ref - M)) @ v4[b, hk, c0:c1]
+                    O[b, hq, r] = acc / l
+                    L[b, hq, r] = M * LN2 + np.log(l)
+    return O, L
+
+
+def exact_attention(q, k, v, causal, sm_scale):
+    """Textbook softmax attention in fp64 (GQA by head groups)."""
+    B, Hq, S, D = q.shape
+    G = Hq // k.shape[1]
+    O = np.zeros_like(q)
+    L = np.zeros((B, Hq, S))
+    for b in range(B):
+        for hq in range(Hq):
+            s = (q[b, hq] @ k[b, hq // G].T) * sm_scale
+            if causal:
+                s = np.where(np.triu(np.ones((S, S), bool), 1), -np.inf, s)
+            m = s.max(axis=1, keepdims=True)
+            p = np.exp(s - m)
+            l = p.sum(axis=1, keepdims=True)
+            O[b, hq] = (p @ v[b, hq // G]) / l
+            L[b, hq] = (m + np.log(l))[:, 0]
+    return O, L

@@ -1,0 +1,54 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case rebuilds the oracle from its source with one deliberate slip (a
+dropped rescale, a wrong rounding rule, a wrong tie-break, a transposed
+index, ...) into a temporary library, runs the pin suites against it in a
+subprocess, and requires them to fail.  The shipped oracle is untouched.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "thrift_oracle.c")
+
+MUTANTS = {
+    "no_rescale_fp4": ("acc[d] = alpha * acc[d] + w * pv;", "acc[d] = acc[d] + w * pv;"),
+    "mx_level1_not_integer": ("double z = ceil(mt);", "double z = mt;"),
+    "topk_ascending": ("if (x->s > y->s) return -1;", "if (x->s > y->s) return 1;"),
+    "e2m1_ties_up": ("if (a > t || (a == t && ((k + 1) & 1) == 0)) code = k + 1;",
+                     "if (a >= t) code = k + 1;"),
+    "rowsum_quantised": ("if (!mask[c]) psum += exp2(t[c] - m_new);\n    l = alpha * l + psum;\n    for (int d = 0; d < D; ++d) {\n      double pv = 0.0;\n      for (int c = 0; c < n; ++c) pv += pq[c]",
+                         "if (!mask[c]) psum += pq[c] * w;\n    l = alpha * l + psum;\n    for (int d = 0; d < D; ++d) {\n      double pv = 0.0;\n      for (int c = 0; c < n; ++c) pv += pq[c]"),
+    "causal_off_by_one": ("mask[c] = a->causal && (c0 + c > r);\n      double s = 0.0;\n      if (!mask[c]) {",
+                          "mask[c] = a->causal && (c0 + c >= r);\n      double s = 0.0;\n      if (!mask[c]) {"),
+    "v_transposed_index": ("e = ((size_t)bh * D + d) * Sp + s;", "e = ((size_t)bh * D + (s % D)) * Sp + d;"),
+    "mean_divides_by_block": ("(float)(sum / (double)(r1 - r0));", "(float)(sum / (double)blk);"),
+    "e4m3_no_saturation_tie": ("if (num > t || (num == t && ((k + 1) & 1) == 0))",
+                               "if (num > t || (num == t && ((k + 1) & 1) == 1))"),
+    "nvfp4_level1_scale": ("2688.0 * exp2(t[c] - mt);", "448.0 * exp2(t[c] - mt);"),
+    "gqa_head_map": ("int hk = hq / (a->Hq / a->Hkv);", "int hk = hq % a->Hkv;"),
+    "fp16_pass_skips_alpha": ("      acc[d] = alpha * acc[d] + pv;\n    }\n    m = m_new;\n  }\n\n  for (int d = 0;",
+                              "      acc[d] = acc[d] + pv;\n    }\n    m = m_new;\n  }\n\n  for (int d = 0;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(tmp_path, name):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mut = tmp_path / "thrift_oracle.c"
+    mut.write_text(src.replace(old, new))
+    sys.path.insert(0, ROOT)
+    from oracle import build_oracle
+
+    lib = build_oracle.build(src=str(mut), out=str(tmp_path / "libmut.so"))
+    env = dict(os.environ, THRIFT_ORACLE_LIB=lib)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "tests/test_oracle_formats.py", "tests/test_oracle_select.py",
+                        "tests/test_oracle_attention.py"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
