@@ -1,0 +1,203 @@
+"""Benchmark of the ThriftAttention forward path on one MI355X.
+
+One step = the whole path on one batch of seeded synthetic input already in
+HBM: block selection (means, scores, per-query-block top-k), FP4
+quantisation of Q, K and V, and the mixed FP4/FP16 attention forward.
+Prints one JSON line (rank 0) with the throughput of the step in attention
+TFLOP/s, the roofline of the attention kernel (the dominant one) and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+P_FP4 = 10.1e15   # MI355X dense MXFP4 MFMA, FLOP/s
+P_FP16 = 2.5e15   # MI355X dense FP16 MFMA, FLOP/s
+HBM = 8.0e12      # bytes/s
+
+
+def unmasked_pairs(S, causal, r0=0, r1=None):
+    """Number of (query, key) pairs with key <= query (causal) for rows [r0, r1)."""
+    r1 = S if r1 is None else r1
+    if not causal:
+        return (r1 - r0) * S
+    return (r1 * (r1 + 1) - r0 * (r0 + 1)) // 2
+
+
+def promoted_pairs(idx, cnt, S, bq, bk, causal):
+    """Unmasked (query, key) pairs inside promoted tiles (host, from idx/cnt)."""
+    B, H, nq, _ = idx.shape
+    total = 0
+    for i in range(nq):
+        r0, r1 = i * bq, min(S, (i + 1) * bq)
+        rows = np.arange(r0, r1)
+        sel = idx[:, :, i]
+        c = cnt[:, :, i]
+        for jj in range(sel.shape[-1]):
+            j = sel[..., jj]
+            on = (jj < c) & (j >= 0)
+            if not on.any():
+                continue
+            for jv in np.unique(j[on]):
+                n_here = int(np.sum(on & (j == jv)))
+                k0, k1 = int(jv) * bk, min(S, (int(jv) + 1) * bk)
+                if causal:  # keys k0.. up to each row
+                    per = int(np.sum(np.clip(rows + 1 - k0, 0, k1 - k0)))
+                else:
+                    per = len(rows) * (k1 - k0)
+                total += n_here * per
+    return total
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long")
+    ap.add_argument("--fmt", default="mx", choices=["mx", "nvfp4"])
+    ap.add_argument("--topk-bp", type=int, default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this path runs on one GPU; multi-GPU runs are not part of this build "
+              "(each (batch, head) is independent, see the sharding notes)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from fp16_attention_amd import api
+    from fp16_attention_amd import workloads as W
+
+    w = W.WORKLOADS[args.workload]
+    if args.topk_bp is not None:
+        w = w.with_(topk_count=-1, topk_bp=args.topk_bp)
+    fmt = api.THRIFT_MXFP4 if args.fmt == "mx" else api.THRIFT_NVFP4
+    t0 = time.time()
+    d = W.generate(w)
+    gen_s = time.time() - t0
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v"))
+    kmax = max(1, api.thrift_select_kmax(w.S, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp))
+    o = torch.empty_like(q)
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(rec=None):
+        if rec:
+            rec[0].record()
+        idx, cnt = api.thrift_select_blocks(q, k, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp, kmax)
+        if rec:
+            rec[1].record()
+        q4 = api.thrift_quantize_fp4(q, api.THRIFT_GROUP_D, fmt)
+        k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, fmt)
+        v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, fmt)
+        if rec:
+            rec[2].record()
+        api.thrift_attention_fwd(q, k, v, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal, out=o)
+        if rec:
+            rec[3].record()
+        return idx, cnt
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    recs = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in recs:
+        idx, cnt = step(r)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1e3 * wall / args.steps
+    sel_ms = float(np.mean([r[0].elapsed_time(r[1]) for r in recs]))
+    q_ms = float(np.mean([r[1].elapsed_time(r[2]) for r in recs]))
+    fwd_ms = float(np.mean([r[2].elapsed_time(r[3]) for r in recs]))
+
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    pairs = w.B * w.Hq * unmasked_pairs(w.S, w.causal)
+    f_alg = 4.0 * w.D * pairs
+    p16 = promoted_pairs(idx_h, cnt_h, w.S, w.bq, w.bk, w.causal)
+    f16 = 4.0 * w.D * p16
+    f4 = f_alg - f16
+    t_roof = f4 / P_FP4 + f16 / P_FP16
+    peak_mixed = f_alg / t_roof
+    achieved = f_alg / (fwd_ms * 1e-3)
+    value = f_alg / (ms_step * 1e-3) / 1e12
+
+    line = {
+        "metric": "attention-fwd TFLOPS + % of mixed FP4/FP16 MFMA roofline at S=32K, D=128, 5% top-k",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4+fp16" if fmt == api.THRIFT_MXFP4 else "nvfp4(fp16 math)+fp16",
+        "data": "synthetic",
+        "config": {
+            "workload": f"{w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} S{w.S} D{w.D} "
+                        f"{'causal' if w.causal else 'non-causal'} blocks {w.bq}x{w.bk} "
+                        f"top-k {w.topk_bp / 100 if w.topk_count < 0 else w.topk_count}"
+                        f"{'%' if w.topk_count < 0 else ' per query block'} {args.fmt}",
+            "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)",
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved / 1e12, 2),
+            "peak": round(peak_mixed / 1e12, 2),
+            "unit": "TFLOP/s",
+            "frac": round(achieved / peak_mixed, 4),
+            "traffic": None,
+            "kernel": "attn_fwd_kernel",
+            "peak_note": "F_alg / (F_fp4 / 10.1 PF + F_fp16 / 2.5 PF) for this launch's FP16 share",
+        },
+        "breakdown_ms": {"select": round(sel_ms, 4), "quantize_qkv": round(q_ms, 4),
+                         "attention_fwd": round(fwd_ms, 4)},
+        "fp16_pair_share": round(p16 / pairs, 5),
+        "attention_fwd_tflops": round(achieved / 1e12, 2),
+        "input_gen_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, d, fmt)
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(s + "\n")
+
+
+def cpu_baseline(w, d, fmt):
+    """The oracle on one query head (and its key head) of the same workload:
+    selection, quantisation of that head's Q, K, V and the forward pass."""
+    from oracle import oracle as O
+
+    nthreads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    q1 = np.ascontiguousarray(d["q"][:1, :1])
+    k1 = np.ascontiguousarray(d["k"][:1, :1])
+    v1 = np.ascontiguousarray(d["v"][:1, :1])
+    O.lib()
+    t0 = time.perf_counter()
+    O.pipeline(q1, k1, v1, fmt, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
+    sec = time.perf_counter() - t0
+    f = 4.0 * w.D * unmasked_pairs(w.S, w.causal)
+    return {"value": round(f / sec / 1e12, 5), "unit": "TFLOP/s", "cores": nthreads,
+            "kind": "oracle", "seconds": round(sec, 2),
+            "sample": f"query head 0 of batch 0 with its key head: selection, FP4 quantisation of "
+                      f"its Q/K/V and the forward pass over all {-(-w.S // w.bq)} query blocks "
+                      f"({f / 1e9:.1f} GFLOP of attention), fp64"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,50 @@
+"""ctypes declarations of libthrift.so (the C ABI in include/thrift.h)."""
+import ctypes as C
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libthrift.so")
+
+THRIFT_OK, THRIFT_EINVAL, THRIFT_EUNSUPPORTED, THRIFT_EALIGN, THRIFT_EWORKSPACE, THRIFT_EHIP = range(6)
+THRIFT_NVFP4, THRIFT_MXFP4 = 0, 1
+THRIFT_GROUP_D, THRIFT_GROUP_S = 0, 1
+
+EXPORTS = ("thrift_select_kmax", "thrift_select_workspace_bytes", "thrift_select_blocks",
+           "thrift_quantize_workspace_bytes", "thrift_quantize_fp4", "thrift_attention_fwd",
+           "thrift_status_string")
+
+_lib = None
+
+
+class ThriftError(RuntimeError):
+    def __init__(self, fn, status):
+        msg = load().thrift_status_string(status).decode()
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+        self.status = status
+
+
+def load():
+    """Load the built HIP library; fails loudly when it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                              "python -m fp16_attention_amd.build")
+        L = C.CDLL(LIB_PATH)
+        P, I, F, SZ = C.c_void_p, C.c_int, C.c_float, C.c_size_t
+        L.thrift_select_kmax.restype = I
+        L.thrift_select_kmax.argtypes = [I] * 6
+        L.thrift_select_workspace_bytes.restype = SZ
+        L.thrift_select_workspace_bytes.argtypes = [I] * 7
+        L.thrift_select_blocks.restype = I
+        L.thrift_select_blocks.argtypes = [P, P] + [I] * 10 + [P, P, I, P, SZ, P]
+        L.thrift_quantize_workspace_bytes.restype = SZ
+        L.thrift_quantize_workspace_bytes.argtypes = [I] * 5
+        L.thrift_quantize_fp4.restype = I
+        L.thrift_quantize_fp4.argtypes = [P, I, I, I, I, I, I, P, P, P, P, SZ, P]
+        L.thrift_attention_fwd.restype = I
+        L.thrift_attention_fwd.argtypes = [P] * 12 + [I, P, P] + [I] * 9 + [F, P, I, P, P]
+        L.thrift_status_string.restype = C.c_char_p
+        L.thrift_status_string.argtypes = [I]
+        _lib = L
+    return _lib

@@ -1,0 +1,130 @@
+"""Python binding of the C ABI: torch tensors in, the same three calls out.
+
+Marshalling only: each function checks dtypes, devices and contiguity,
+allocates outputs and workspace with torch, passes raw device pointers and
+torch's current HIP stream to libthrift.so, and raises ThriftError on a
+non-zero status.  All arithmetic runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import THRIFT_GROUP_D, THRIFT_GROUP_S, THRIFT_MXFP4, THRIFT_NVFP4, ThriftError
+
+__all__ = ["thrift_select_kmax", "thrift_select_blocks", "thrift_quantize_fp4",
+           "thrift_attention_fwd", "FP4Tensor", "thrift_forward", "THRIFT_NVFP4", "THRIFT_MXFP4",
+           "THRIFT_GROUP_D", "THRIFT_GROUP_S", "ThriftError"]
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(t, dtype, name):
+    if not isinstance(t, torch.Tensor) or t.dtype != dtype or not t.is_cuda or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous {dtype} CUDA tensor")
+
+
+def _call(fn, *args):
+    st = getattr(_lib.load(), fn)(*args)
+    if st != _lib.THRIFT_OK:
+        raise ThriftError(fn, st)
+
+
+def thrift_select_kmax(S, block_q, block_k, causal, topk_count, topk_bp) -> int:
+    return _lib.load().thrift_select_kmax(S, block_q, block_k, int(causal), topk_count, topk_bp)
+
+
+def thrift_select_blocks(q16, k16, block_q=128, block_k=64, causal=True, topk_count=-1,
+                         topk_bp=500, kmax=None):
+    """Block means, pair scores and per-query-block top-k.  Returns (idx, cnt)."""
+    _check(q16, torch.float16, "q16")
+    _check(k16, torch.float16, "k16")
+    B, Hq, S, D = q16.shape
+    Hkv = k16.shape[1]
+    if kmax is None:
+        kmax = max(1, thrift_select_kmax(S, block_q, block_k, causal, topk_count, topk_bp))
+    nq = -(-S // block_q)
+    dev = q16.device
+    idx = torch.empty((B, Hq, nq, kmax), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Hq, nq), dtype=torch.int32, device=dev)
+    wsb = _lib.load().thrift_select_workspace_bytes(B, Hq, Hkv, S, D, block_q, block_k)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _call("thrift_select_blocks", _ptr(q16), _ptr(k16), B, Hq, Hkv, S, D, block_q, block_k,
+          int(causal), topk_count, topk_bp, _ptr(idx), _ptr(cnt), kmax, _ptr(ws), wsb, _stream())
+    return idx, cnt
+
+
+@dataclass
+class FP4Tensor:
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tensor_scale: torch.Tensor | None
+    fmt: int
+    axis: int
+
+
+def thrift_quantize_fp4(x16, axis=THRIFT_GROUP_D, fmt=THRIFT_MXFP4) -> FP4Tensor:
+    """FP16 -> E2M1 codes + block scales (+ per-slice fp32 scale for NVFP4)."""
+    _check(x16, torch.float16, "x16")
+    B, H, S, D = x16.shape
+    g = 16 if fmt == THRIFT_NVFP4 else 32
+    dev = x16.device
+    if axis == THRIFT_GROUP_D:
+        codes = torch.empty((B, H, S, D // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((B, H, S, D // g), dtype=torch.uint8, device=dev)
+    else:
+        Sp = -(-S // 64) * 64
+        codes = torch.empty((B, H, D, Sp // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty((B, H, D, Sp // g), dtype=torch.uint8, device=dev)
+    ts = torch.empty((B, H), dtype=torch.float32, device=dev) if fmt == THRIFT_NVFP4 else None
+    wsb = _lib.load().thrift_quantize_workspace_bytes(B, H, S, D, fmt)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _call("thrift_quantize_fp4", _ptr(x16), B, H, S, D, axis, fmt, _ptr(codes), _ptr(scales),
+          _ptr(ts), _ptr(ws), wsb, _stream())
+    return FP4Tensor(codes, scales, ts, fmt, axis)
+
+
+def thrift_attention_fwd(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt,
+                         block_q=128, block_k=64, causal=True, sm_scale=None, out_fp32=False,
+                         with_lse=False, out=None):
+    """Mixed FP4/FP16 forward.  Returns o (and lse if with_lse)."""
+    B, Hq, S = q4.codes.shape[:3]
+    D = q4.codes.shape[3] * 2
+    Hkv = k4.codes.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    for name, t in (("q16", q16), ("k16", k16), ("v16", v16)):
+        if t is not None:
+            _check(t, torch.float16, name)
+    _check(idx, torch.int32, "idx")
+    _check(cnt, torch.int32, "cnt")
+    dev = q4.codes.device
+    if out is None:
+        out = torch.empty((B, Hq, S, D), dtype=torch.float32 if out_fp32 else torch.float16, device=dev)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev) if with_lse else None
+    _call("thrift_attention_fwd", _ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes),
+          _ptr(q4.scales), _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales),
+          _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales), _ptr(v4.tensor_scale), q4.fmt,
+          _ptr(idx), _ptr(cnt), idx.shape[-1], B, Hq, Hkv, S, D, block_q, block_k, int(causal),
+          float(sm_scale), _ptr(out), int(out.dtype == torch.float32), _ptr(lse), _stream())
+    return (out, lse) if with_lse else out
+
+
+def thrift_forward(q16, k16, v16, fmt=THRIFT_MXFP4, block_q=128, block_k=64, causal=True,
+                   topk_count=-1, topk_bp=500, sm_scale=None, out_fp32=False, with_lse=False):
+    """The whole path: selection, quantisation of Q/K/V, mixed attention."""
+    idx, cnt = thrift_select_blocks(q16, k16, block_q, block_k, causal, topk_count, topk_bp)
+    q4 = thrift_quantize_fp4(q16, THRIFT_GROUP_D, fmt)
+    k4 = thrift_quantize_fp4(k16, THRIFT_GROUP_D, fmt)
+    v4 = thrift_quantize_fp4(v16, THRIFT_GROUP_S, fmt)
+    return thrift_attention_fwd(q16, k16, v16, q4, k4, v4, idx, cnt, block_q, block_k, causal,
+                                sm_scale, out_fp32, with_lse)

@@ -1,0 +1,46 @@
+// Shared device/host helpers of the gfx950 ThriftAttention library.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "thrift.h"
+
+namespace thrift {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef _Float16 v4h __attribute__((ext_vector_type(4)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef short v2s_t __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
+
+// Number of valid key blocks of query block i (causal: query and key
+// sequences aligned at their starts; a block is valid when it holds a key not
+// after the query block's last row).
+__host__ __device__ inline int valid_kv_blocks(int i, int S, int bq, int bk, int causal) {
+  if (!causal) return cdiv(S, bk);
+  int last = (i + 1) * bq < S ? (i + 1) * bq - 1 : S - 1;
+  return last / bk + 1;
+}
+
+// Promoted-block budget of a query block with n valid key blocks.
+__host__ __device__ inline int topk_budget(int n, int topk_count, int topk_bp) {
+  long long k = topk_count >= 0 ? (long long)topk_count : ((long long)n * topk_bp + 9999) / 10000;
+  return (int)(k < n ? k : n);
+}
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+inline thrift_status launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
+}
+
+}  // namespace thrift

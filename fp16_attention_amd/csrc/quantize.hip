@@ -1,0 +1,301 @@
+// FP4 quantisation of Q, K and V on gfx950 (the FP4 path of ThriftAttention
+// uses NVFP4 micro-scaling; MXFP4 is the layout of gfx950's block-scaled
+// matrix instructions).  Streaming kernels, bound by HBM: each fp16 element
+// is read once (NVFP4 reads the slice twice, once for its maximum) and each
+// code nibble and scale byte written once, with 16-byte loads and stores.
+//
+// Every rounding decision is exact:
+//  - MXFP4 divides by a power of two (exact in fp32) and uses gfx950's
+//    scaled FP4 conversion, which rounds to nearest even and saturates at 6;
+//  - NVFP4's block scale is E4M3(amax / (6 sg)): the fp64 quotient of an
+//    11-bit and a 26-bit significand can only land on a 5-bit E4M3 midpoint
+//    if the exact quotient is that midpoint, so rounding the fp64 quotient
+//    is exact; element codes compare |x| (fp16, exact in fp32) against the
+//    seven E2M1 midpoints times the block scale, each midpoint rounded down
+//    to fp32 with a flag telling whether it was exact, which decides every
+//    comparison (and every tie) exactly.
+#include "common.h"
+
+namespace thrift {
+
+constexpr int kQThreads = 256;
+constexpr int kAmaxChunk = 65536;  // elements reduced per workgroup
+
+// ---- per-slice maxima (NVFP4 only) ------------------------------------------
+
+__global__ __launch_bounds__(kQThreads) void slice_amax_kernel(const _Float16* __restrict__ x,
+                                                               size_t slice, int nchunk,
+                                                               float* __restrict__ part) {
+  __shared__ float red[kQThreads / kWave];
+  const int c = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const _Float16* base = x + (size_t)bh * slice;
+  size_t e0 = (size_t)c * kAmaxChunk, e1 = e0 + kAmaxChunk < slice ? e0 + kAmaxChunk : slice;
+  float m = 0.0f;
+  for (size_t e = e0 + (size_t)t * 8; e < e1; e += kQThreads * 8) {
+    v8h v = *reinterpret_cast<const v8h*>(base + e);  // slice sizes are multiples of 8
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf((float)v[u]));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, kWave));
+  if (t % kWave == 0) red[t / kWave] = m;
+  __syncthreads();
+  if (t == 0) {
+    for (int w = 1; w < kQThreads / kWave; ++w) m = fmaxf(m, red[w]);
+    part[(size_t)bh * nchunk + c] = m;
+  }
+}
+
+// sg = fp32(amax / 2688) (fp64 division, one rounding), or 1 for an all-zero slice.
+__global__ void slice_scale_kernel(const float* __restrict__ part, int nchunk, int BH,
+                                   float* __restrict__ tscale) {
+  int bh = blockIdx.x * blockDim.x + threadIdx.x;
+  if (bh >= BH) return;
+  float m = 0.0f;
+  for (int c = 0; c < nchunk; ++c) m = fmaxf(m, part[(size_t)bh * nchunk + c]);
+  tscale[bh] = m > 0.0f ? (float)((double)m / 2688.0) : 1.0f;
+}
+
+// ---- exact roundings ---------------------------------------------------------
+
+// Non-negative E4M3 code nearest to q (ties to even), saturating at 448.
+__device__ inline int e4m3_rne(double q) {
+  if (!(q > 0.0)) return 0;
+  if (q >= 448.0) return 126;
+  int e;
+  double f = frexp(q, &e);  // q = f 2^e, f in [0.5, 1)
+  int E = e - 1;            // q in [2^E, 2^(E+1))
+  if (E < -6) {             // subnormal range: multiples of 2^-9
+    int m = (int)rint(ldexp(q, 9));
+    return m;               // m == 8 is the smallest normal, code 8
+  }
+  int m = (int)rint((f * 2.0 - 1.0) * 8.0);  // 3 mantissa bits
+  int code = ((E + 7) << 3) + m;             // m == 8 carries into the exponent
+  return code > 126 ? 126 : code;
+}
+
+__device__ inline double e4m3_value(int code) {
+  int e = code >> 3, m = code & 7;
+  return e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+}
+
+// Largest fp32 value <= x (x >= 0), and whether it equals x.
+__device__ inline float round_down_f32(double x, bool* exact) {
+  float f = (float)x;  // nearest
+  if ((double)f > x) f = nextafterf(f, 0.0f);
+  *exact = (double)f == x;
+  return f;
+}
+
+// E2M1 code of x / s from the seven midpoint thresholds m_k * s.
+struct E2m1Thresholds {
+  float t[7];
+  unsigned exact;  // bit k: t[k] == m_k * s exactly
+};
+
+__device__ inline E2m1Thresholds make_thresholds(double s) {
+  const double mid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+  E2m1Thresholds th;
+  th.exact = 0;
+#pragma unroll
+  for (int k = 0; k < 7; ++k) {
+    bool ex;
+    th.t[k] = round_down_f32(mid[k] * s, &ex);
+    th.exact |= (unsigned)ex << k;
+  }
+  return th;
+}
+
+__device__ inline uint32_t e2m1_code_exact(float x, const E2m1Thresholds& th) {
+  float a = fabsf(x);
+  uint32_t c = 0;
+#pragma unroll
+  for (int k = 0; k < 7; ++k) {
+    // above the midpoint, or on it exactly and the upper neighbour is even
+    bool up = a > th.t[k] || (a == th.t[k] && ((th.exact >> k) & 1u) && ((k + 1) & 1) == 0);
+    c += up ? 1u : 0u;
+  }
+  return c | (__float_as_uint(x) >> 31 << 3);
+}
+
+// ---- encoders -------------------------------------------------------------------
+
+// NVFP4-style group of 16: returns the block scale byte, fills 8 code bytes.
+__device__ inline uint32_t encode_nvfp4_16(const float* v, float sg, uint32_t* w /*2 dwords*/) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 16; ++u) amax = fmaxf(amax, fabsf(v[u]));
+  int sb = e4m3_rne((double)amax / (6.0 * (double)sg));
+  double s = e4m3_value(sb) * (double)sg;
+  w[0] = w[1] = 0;
+  if (s > 0.0) {
+    E2m1Thresholds th = make_thresholds(s);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) w[u / 8] |= e2m1_code_exact(v[u], th) << (4 * (u % 8));
+  }
+  return (uint32_t)sb;
+}
+
+// MXFP4 group of 32: returns the E8M0 byte, fills 4 code dwords.
+__device__ inline uint32_t encode_mx_32(const float* v, uint32_t* w /*4 dwords*/) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 32; ++u) amax = fmaxf(amax, fabsf(v[u]));
+  // floor(log2 amax) - 2 from the exponent field (fp16 values are normal fp32)
+  int X = amax > 0.0f ? (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 2 : -127;
+  float scale = amax > 0.0f ? __uint_as_float((uint32_t)(X + 127) << 23) : 1.0f;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const float* p = v + q * 8;
+    uint32_t d = 0;  // byte u holds elements 2u (low nibble) and 2u+1
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, p[0], p[1], scale, 0);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, p[2], p[3], scale, 1);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, p[4], p[5], scale, 2);
+    d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, p[6], p[7], scale, 3);
+    w[q] = d;
+  }
+  return (uint32_t)(X + 127);
+}
+
+// ---- groups along D (Q, K) -----------------------------------------------------
+
+template <int FMT>
+__global__ __launch_bounds__(kQThreads) void quant_d_kernel(const _Float16* __restrict__ x,
+                                                            size_t ngroups, int groups_per_slice,
+                                                            const float* __restrict__ tscale,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  constexpr int g = FMT == THRIFT_NVFP4 ? 16 : 32;
+  size_t gi = (size_t)blockIdx.x * kQThreads + threadIdx.x;
+  if (gi >= ngroups) return;
+  float v[g];
+  const v8h* src = reinterpret_cast<const v8h*>(x + gi * g);
+#pragma unroll
+  for (int q = 0; q < g / 8; ++q) {
+    v8h h = src[q];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[q * 8 + u] = (float)h[u];
+  }
+  if (FMT == THRIFT_NVFP4) {
+    uint32_t w[2];
+    float sg = tscale[gi / groups_per_slice];
+    scales[gi] = (uint8_t)encode_nvfp4_16(v, sg, w);
+    *reinterpret_cast<uint2*>(codes + gi * 8) = make_uint2(w[0], w[1]);
+  } else {
+    uint32_t w[4];
+    scales[gi] = (uint8_t)encode_mx_32(v, w);
+    *reinterpret_cast<uint4*>(codes + gi * 16) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+// ---- groups along S (V, stored transposed) -------------------------------------
+
+constexpr int kVTile = 128;  // tokens per workgroup
+
+template <int FMT, int D>
+__global__ __launch_bounds__(kQThreads) void quant_s_kernel(const _Float16* __restrict__ x, int S,
+                                                            int Sp, const float* __restrict__ tscale,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  constexpr int g = FMT == THRIFT_NVFP4 ? 16 : 32;
+  constexpr int GPT = kVTile / g;  // groups per d in this tile
+  __shared__ _Float16 tile[kVTile][D + 2];
+  const int tt = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int s0 = tt * kVTile;
+  const _Float16* base = x + (size_t)bh * S * D;
+  // stage kVTile x D fp16 (zeros past S)
+  for (int e = t; e < kVTile * D / 8; e += kQThreads) {
+    int r = e / (D / 8), c = (e % (D / 8)) * 8;
+    v8h h = {};
+    if (s0 + r < S) h = *reinterpret_cast<const v8h*>(base + (size_t)(s0 + r) * D + c);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) tile[r][c + u] = h[u];
+  }
+  __syncthreads();
+  const float sg = FMT == THRIFT_NVFP4 ? tscale[bh] : 1.0f;
+  for (int e = t; e < D * GPT; e += kQThreads) {
+    const int d = e / GPT, gq = e % GPT;
+    const int tok0 = s0 + gq * g;
+    if (tok0 >= Sp) continue;
+    float v[g];
+#pragma unroll
+    for (int u = 0; u < g; ++u) v[u] = (float)tile[gq * g + u][d];
+    const size_t crow = ((size_t)bh * D + d) * (Sp / 2);
+    const size_t srow = ((size_t)bh * D + d) * (Sp / g);
+    if (FMT == THRIFT_NVFP4) {
+      uint32_t w[2];
+      scales[srow + tok0 / g] = (uint8_t)encode_nvfp4_16(v, sg, w);
+      *reinterpret_cast<uint2*>(codes + crow + tok0 / 2) = make_uint2(w[0], w[1]);
+    } else {
+      uint32_t w[4];
+      scales[srow + tok0 / g] = (uint8_t)encode_mx_32(v, w);
+      *reinterpret_cast<uint4*>(codes + crow + tok0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+    }
+  }
+}
+
+}  // namespace thrift
+
+using namespace thrift;
+
+static int pad_s(int S) { return cdiv(S, 64) * 64; }
+
+extern "C" size_t thrift_quantize_workspace_bytes(int B, int H, int S, int D, thrift_format fmt) {
+  if (B < 1 || H < 1 || S < 1 || D < 1) return 0;
+  if (fmt != THRIFT_NVFP4) return 0;
+  size_t nchunk = ((size_t)S * D + kAmaxChunk - 1) / kAmaxChunk;
+  return (size_t)B * H * nchunk * sizeof(float);
+}
+
+extern "C" thrift_status thrift_quantize_fp4(const void* x16, int B, int H, int S, int D,
+                                             thrift_group_axis axis, thrift_format fmt,
+                                             uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                                             void* workspace, size_t workspace_bytes,
+                                             hipStream_t stream) {
+  if (!x16 || !codes || !scales) return THRIFT_EINVAL;
+  if (B < 1 || H < 1 || S < 1) return THRIFT_EINVAL;
+  if (fmt != THRIFT_NVFP4 && fmt != THRIFT_MXFP4) return THRIFT_EINVAL;
+  if (axis != THRIFT_GROUP_D && axis != THRIFT_GROUP_S) return THRIFT_EINVAL;
+  if (fmt == THRIFT_NVFP4 && !tensor_scale) return THRIFT_EINVAL;
+  if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
+  if (S > 262144) return THRIFT_EUNSUPPORTED;
+  if (!aligned16(x16) || !aligned16(codes)) return THRIFT_EALIGN;
+  const size_t need = thrift_quantize_workspace_bytes(B, H, S, D, fmt);
+  if (need && (!workspace || workspace_bytes < need)) return THRIFT_EWORKSPACE;
+  const int BH = B * H;
+  auto x = (const _Float16*)x16;
+  if (fmt == THRIFT_NVFP4) {
+    const size_t slice = (size_t)S * D;
+    const int nchunk = (int)((slice + kAmaxChunk - 1) / kAmaxChunk);
+    float* part = (float*)workspace;
+    slice_amax_kernel<<<dim3(nchunk, BH), kQThreads, 0, stream>>>(x, slice, nchunk, part);
+    slice_scale_kernel<<<cdiv(BH, 256), 256, 0, stream>>>(part, nchunk, BH, tensor_scale);
+  }
+  if (axis == THRIFT_GROUP_D) {
+    const int g = fmt == THRIFT_NVFP4 ? 16 : 32;
+    const size_t ngroups = (size_t)BH * S * (D / g);
+    const int blocks = (int)((ngroups + kQThreads - 1) / kQThreads);
+    const int gps = S * (D / g);
+    if (fmt == THRIFT_NVFP4)
+      quant_d_kernel<THRIFT_NVFP4><<<blocks, kQThreads, 0, stream>>>(x, ngroups, gps, tensor_scale,
+                                                                       codes, scales);
+    else
+      quant_d_kernel<THRIFT_MXFP4><<<blocks, kQThreads, 0, stream>>>(x, ngroups, gps, tensor_scale,
+                                                                       codes, scales);
+  } else {
+    const int Sp = pad_s(S);
+    dim3 grid(cdiv(Sp, kVTile), BH);
+    if (fmt == THRIFT_NVFP4) {
+      if (D == 128)
+        quant_s_kernel<THRIFT_NVFP4, 128><<<grid, kQThreads, 0, stream>>>(x, S, Sp, tensor_scale, codes, scales);
+      else
+        quant_s_kernel<THRIFT_NVFP4, 64><<<grid, kQThreads, 0, stream>>>(x, S, Sp, tensor_scale, codes, scales);
+    } else {
+      if (D == 128)
+        quant_s_kernel<THRIFT_MXFP4, 128><<<grid, kQThreads, 0, stream>>>(x, S, Sp, tensor_scale, codes, scales);
+      else
+        quant_s_kernel<THRIFT_MXFP4, 64><<<grid, kQThreads, 0, stream>>>(x, S, Sp, tensor_scale, codes, scales);
+    }
+  }
+  return launch_status();
+}

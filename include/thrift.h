@@ -1,0 +1,180 @@
+/*
+ * thrift.h - C ABI of the ThriftAttention forward pass on AMD MI355X (gfx950).
+ *
+ * ThriftAttention ("ThriftAttention: Selective Mixed Precision for
+ * Long-Context FP4 Attention"; summaries at gist.science, Dutch section
+ * "Methodologie", French section "Methodologie") computes softmax attention
+ * in two precisions at once: a cheap score per (query block, key block) pair,
+ * the dot product of the two blocks' token means, picks the top-k pairs of
+ * every query block; those pairs run in FP16 and every other pair runs in
+ * 4-bit E2M1 with micro-scaling; one online softmax merges both.
+ *
+ * Three calls make up the path, in this order:
+ *   thrift_select_blocks  - block means, pair scores and per-query-block top-k
+ *   thrift_quantize_fp4   - FP16 -> E2M1 codes + block scales (Q, K and V)
+ *   thrift_attention_fwd  - the mixed FP4/FP16 forward pass
+ *
+ * Conventions (all calls):
+ *   - Tensors are contiguous, row-major, [batch, head, seq, dim] unless stated.
+ *   - Every pointer is a DEVICE pointer except where marked "host".
+ *   - The caller owns and allocates every buffer, workspace included; the
+ *     library never allocates, frees or synchronises, and keeps no state.
+ *   - Every call is asynchronous on `stream`; calls on different streams
+ *     may run concurrently when they share no output buffer.
+ *   - Arguments are validated before anything is launched; on failure the
+ *     call returns a non-zero thrift_status and launches nothing.  A launch
+ *     failure reported by the HIP runtime returns THRIFT_EHIP.  No exception
+ *     or signal crosses the ABI.
+ *   - Results are deterministic: the kernels use no floating-point atomics,
+ *     so two calls on the same inputs give identical bits.
+ *   - Supported shapes: D in {64, 128}; block_q in {64, 128}; block_k = 64;
+ *     1 <= S <= 262144; Hq a multiple of Hkv; B, Hq >= 1.
+ */
+#ifndef THRIFT_H
+#define THRIFT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  THRIFT_OK = 0,
+  THRIFT_EINVAL = 1,       /* a size, flag or pointer argument is invalid */
+  THRIFT_EUNSUPPORTED = 2, /* a shape outside the supported set above */
+  THRIFT_EALIGN = 3,       /* a pointer is not 16-byte aligned */
+  THRIFT_EWORKSPACE = 4,   /* workspace missing or smaller than required */
+  THRIFT_EHIP = 5          /* the HIP runtime reported a launch error */
+} thrift_status;
+
+/* FP4 micro-scaling formats.  Both store E2M1 elements (1 sign, 2 exponent,
+ * 1 mantissa bit: 0, 0.5, 1, 1.5, 2, 3, 4, 6), two per byte with the even
+ * element in the low nibble.
+ *   THRIFT_NVFP4: the format the pages name for the FP4 path: one E4M3 block
+ *     scale per 16 elements, plus one fp32 scale per (batch, head) slice,
+ *     sg = amax / (6 * 448) of the slice (1 for an all-zero slice); block byte
+ *     = E4M3(amax_block / (6 sg)), element = E2M1(x / (block * sg)).
+ *   THRIFT_MXFP4: one E8M0 scale per 32 elements (OCP MX): exponent
+ *     floor(log2 amax_block) - 2, element = E2M1(x / 2^exponent); this is the
+ *     layout gfx950's block-scaled FP4 matrix instructions consume.
+ * All roundings are to nearest, ties to even, saturating (E2M1 at 6, E4M3 at
+ * 448); the sign of a value that rounds to zero is kept. */
+typedef enum { THRIFT_NVFP4 = 0, THRIFT_MXFP4 = 1 } thrift_format;
+
+/* Grouping axis of a quantised tensor.
+ *   THRIFT_GROUP_D (Q, K): groups run along dim; codes [B,H,S,D/2] u8,
+ *     scales [B,H,S,D/g] u8 (g = 16 NVFP4, 32 MXFP4).
+ *   THRIFT_GROUP_S (V): groups run along the sequence and the tensor is
+ *     stored transposed: codes [B,H,D,Sp/2] u8, scales [B,H,D,Sp/g] u8, with
+ *     Sp = S rounded up to a multiple of 64 and the padding tokens zero. */
+typedef enum { THRIFT_GROUP_D = 0, THRIFT_GROUP_S = 1 } thrift_group_axis;
+
+/* ---------------------------------------------------------------------- */
+/* Block selection ("Heuristische Blokkenselectie" on the Dutch page)       */
+/* ---------------------------------------------------------------------- */
+
+/* Host helper: the largest per-query-block budget k_i, i.e. the minimum
+ * `kmax` that thrift_select_blocks accepts.  Query block i covers rows
+ * [i*block_q, min(S,(i+1)*block_q)); its valid key blocks are all key
+ * blocks, or (causal, query and key sequences aligned at their starts) the
+ * blocks j with j*block_k <= min(S,(i+1)*block_q) - 1; n_i is their count and
+ * k_i = min(n_i, topk_count) if topk_count >= 0, else
+ * min(n_i, ceil(n_i * topk_bp / 10000)).  Returns -1 on invalid arguments. */
+int thrift_select_kmax(int S, int block_q, int block_k, int causal, int topk_count, int topk_bp);
+
+/* Workspace bytes thrift_select_blocks needs (the fp32 block means). */
+size_t thrift_select_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int block_q,
+                                     int block_k);
+
+/* Importance scores and top-k (pages: S^_ij = qbar_i . kbar_j, the top-k
+ * highest-scoring pairs go to FP16).
+ *   q16 [B,Hq,S,D] fp16, k16 [B,Hkv,S,D] fp16: inputs (read only).
+ *   qbar_i, kbar_j: the arithmetic mean of the block's valid rows, summed in
+ *     fp64 (exact) and rounded once to fp32.
+ *   score: fp32, one fused multiply-add per channel in ascending order.
+ *   Query head hq reads key head hq / (Hq / Hkv).
+ *   The k_i best valid key blocks of each query block are kept (ties: the
+ *   lower block index wins; -0 == +0; inputs must be finite).
+ *   idx [B,Hq,nQ,kmax] int32 (out): the kept block indices, ascending,
+ *     padded with -1; cnt [B,Hq,nQ] int32 (out): k_i.  nQ = ceil(S/block_q).
+ *   kmax: row length of idx, >= thrift_select_kmax(...).
+ *   workspace: device buffer of at least thrift_select_workspace_bytes. */
+thrift_status thrift_select_blocks(const void* q16, const void* k16, int B, int Hq, int Hkv, int S,
+                                   int D, int block_q, int block_k, int causal, int topk_count,
+                                   int topk_bp, int32_t* idx, int32_t* cnt, int kmax,
+                                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* FP4 quantisation (the FP4 path's NVFP4 micro-scaling)                    */
+/* ---------------------------------------------------------------------- */
+
+/* Workspace bytes thrift_quantize_fp4 needs (per-slice maxima, NVFP4 only;
+ * 0 for MXFP4). */
+size_t thrift_quantize_workspace_bytes(int B, int H, int S, int D, thrift_format fmt);
+
+/* Quantise x16 [B,H,S,D] fp16 to FP4 along `axis` (layouts above).
+ *   codes, scales (out): as laid out for the axis;
+ *   tensor_scale [B,H] fp32 (out): the per-slice scale, NVFP4 only (may be
+ *     NULL for MXFP4).
+ * Every code and scale byte equals the exact round-to-nearest-even result of
+ * the rule stated with thrift_format, whatever the hardware's own
+ * conversion instructions do. */
+thrift_status thrift_quantize_fp4(const void* x16, int B, int H, int S, int D,
+                                  thrift_group_axis axis, thrift_format fmt, uint8_t* codes,
+                                  uint8_t* scales, float* tensor_scale, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Mixed FP4/FP16 attention ("Gemengd-Precisie Berekening & Samenvoeging")  */
+/* ---------------------------------------------------------------------- */
+
+/* Forward pass.  For every query row r of query block i (head hq, key head
+ * hk = hq / (Hq/Hkv)), with t = sm_scale * q.k in log2 units:
+ *  1. FP4 path, over every valid key block of i that idx does not list,
+ *     ascending: scores from the FP4 Q and K; causal mask (key > r) and keys
+ *     past S get probability 0; the tile's probabilities are quantised in two
+ *     levels (level 1 per row and tile, level 2 per key group aligned with V's
+ *     groups):
+ *       NVFP4: v = 2688 * 2^(t - tile max), per-16 E4M3 scale E4M3(max v / 6),
+ *              E2M1 codes of v / scale;
+ *       MXFP4: v = 2^(t - z), z an integer (the E8M0 scales absorb any power
+ *              of two, so the codes do not depend on z), per-32 E8M0 scale
+ *              from max v, E2M1 codes of v / 2^exponent;
+ *     then multiplied with the FP4 V.
+ *  2. FP16 path, over the promoted blocks idx[.., :cnt] ascending (FP16 Q is
+ *     read only for query blocks with cnt > 0, FP16 K/V only for promoted
+ *     blocks): scores from fp16 Q and K, probabilities rounded to fp16 (on a
+ *     power-of-two footing: 2^t to 11 significant bits), times fp16 V.
+ *  3. Both paths feed one online softmax (running max, running sum of the
+ *     unquantised probabilities, fp32 accumulator); O = acc / sum.
+ * Arguments:
+ *   q16 [B,Hq,S,D], k16/v16 [B,Hkv,S,D] fp16: may be NULL only if every cnt is 0.
+ *   q4_codes/q4_scales/q4_tscale, k4_*: Q and K from thrift_quantize_fp4 along
+ *     THRIFT_GROUP_D; v4_*: V along THRIFT_GROUP_S; *_tscale NULL for MXFP4.
+ *   idx, cnt, kmax: from thrift_select_blocks (or any ascending, -1 padded
+ *     list of valid blocks per query block).
+ *   sm_scale: softmax scale (1/sqrt(D) is customary).
+ *   o [B,Hq,S,D] (out): fp16 if o_is_fp32 == 0, fp32 otherwise.
+ *   lse [B,Hq,S] fp32 (out, may be NULL): natural-log log-sum-exp of the
+ *     scores with the unquantised probabilities. */
+thrift_status thrift_attention_fwd(const void* q16, const void* k16, const void* v16,
+                                   const uint8_t* q4_codes, const uint8_t* q4_scales,
+                                   const float* q4_tscale, const uint8_t* k4_codes,
+                                   const uint8_t* k4_scales, const float* k4_tscale,
+                                   const uint8_t* v4_codes, const uint8_t* v4_scales,
+                                   const float* v4_tscale, thrift_format fmt, const int32_t* idx,
+                                   const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S,
+                                   int D, int block_q, int block_k, int causal, float sm_scale,
+                                   void* o, int o_is_fp32, float* lse, hipStream_t stream);
+
+/* Static string for a status code (host). */
+const char* thrift_status_string(thrift_status s);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* THRIFT_H */

@@ -74,7 +74,7 @@ def _declare(L):
     L.tho_dequantize.restype = None
     L.tho_dequantize.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
     L.tho_attention.restype = None
-    L.tho_attention.argtypes = [_P] * 12 + [_I, _P, _P, _I] + [_I] * 8 + [_D, _P, _I, _P, _P]
+    L.tho_attention.argtypes = [_P] * 12 + [_I, _P, _P, _I] + [_I] * 8 + [_D, _P, _I, _P, _P, _P]
     L.tho_fp4_scores.restype = None
     L.tho_fp4_scores.argtypes = [_P] * 6 + [_I] * 6 + [_P]
     L.tho_e2m1_encode_array.restype = None
@@ -224,10 +224,10 @@ def fp4_scores(q4: FP4Tensor, k4: FP4Tensor, r, c0, c1):
 # ---- attention ----------------------------------------------------------------
 
 def attention(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt, bq, bk,
-              causal, sm_scale=None, work=None):
-    """Forward pass.  Returns (o fp64 [B,Hq,S,D], lse fp64 [B,Hq,S]); with a
-    work list of (b, hq, i) triples only those query blocks are filled (the
-    rest stay NaN)."""
+              causal, sm_scale=None, work=None, with_u=False):
+    """Forward pass.  Returns (o fp64 [B,Hq,S,D], lse fp64 [B,Hq,S]) and, with
+    with_u, the decision-uncertainty bound u [B,Hq,S,D]; with a work list of
+    (b, hq, i) triples only those query blocks are filled (the rest stay NaN)."""
     B, Hq, S, D = q4.shape
     Hkv = k4.shape[1]
     if sm_scale is None:
@@ -240,14 +240,16 @@ def attention(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, c
     km = idx.shape[-1]
     o = np.full((B, Hq, S, D), np.nan, np.float64)
     lse = np.full((B, Hq, S), np.nan, np.float64)
+    u = np.full((B, Hq, S, D), np.nan, np.float64) if with_u else None
     w = None if work is None else _c(np.asarray(work).reshape(-1, 3), np.int32)
     nw = 0 if w is None else w.shape[0]
     lib().tho_attention(_ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
                         _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales),
                         _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales),
                         _ptr(v4.tensor_scale), q4.fmt, _ptr(idx), _ptr(cnt), km, B, Hq, Hkv, S, D,
-                        bq, bk, int(causal), float(sm_scale), _ptr(w), nw, _ptr(o), _ptr(lse))
-    return o, lse
+                        bq, bk, int(causal), float(sm_scale), _ptr(w), nw, _ptr(o), _ptr(lse),
+                        _ptr(u))
+    return (o, lse, u) if with_u else (o, lse)
 
 
 def pipeline(q16, k16, v16, fmt, bq, bk, causal, topk_count=-1, topk_bp=0, sm_scale=None,
@@ -257,5 +259,6 @@ def pipeline(q16, k16, v16, fmt, bq, bk, causal, topk_count=-1, topk_bp=0, sm_sc
     q4 = quantize(q16, AXIS_D, fmt)
     k4 = quantize(k16, AXIS_D, fmt)
     v4 = quantize(v16, AXIS_S, fmt)
-    o, lse = attention(q16, k16, v16, q4, k4, v4, idx, cnt, bq, bk, causal, sm_scale, work)
-    return dict(idx=idx, cnt=cnt, q4=q4, k4=k4, v4=v4, o=o, lse=lse)
+    o, lse, u = attention(q16, k16, v16, q4, k4, v4, idx, cnt, bq, bk, causal, sm_scale, work,
+                          with_u=True)
+    return dict(idx=idx, cnt=cnt, q4=q4, k4=k4, v4=v4, o=o, lse=lse, u=u)

@@ -420,10 +420,49 @@ void tho_dequantize(const uint8_t* codes, const uint8_t* scales, const float* te
  *     dequantised probability relative to 2^z is code * 2^X.
  * Masked keys (mask[c] != 0) hold probability 0.
  * pq[c] receives the dequantised probability relative to 2^(*ref). */
+/* ---- decisions a finite-precision evaluation may take either way ----
+ * The probabilities that feed a rounding decision (the fp16 rounding of P on
+ * the FP16 path, the E2M1 codes and block scales of P on the FP4 path) come
+ * from exponentials of scores.  An implementation that evaluates them in
+ * fp32 carries a relative error of a few 2^-24 |t| (t: score in log2 units)
+ * plus that of its exp2; a decision whose input lies closer than that to its
+ * rounding boundary may legitimately go either way, so the method's result
+ * is not unique there.  tho_eval_eps is that error, taken four times over;
+ * the uncertainty outputs below add up what flipping such decisions can
+ * change in O. */
+static double tho_eval_eps(double t) { return THO_LN2 * ldexp(fabs(t) + 16.0, -20); }
+
+/* Change of the dequantised E2M1 value (in units of s) if y/s sits within
+ * relative eps of a rounding midpoint and the other neighbour is taken. */
+static double tho_e2m1_flip(double y, double s, double eps) {
+  static const double mid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+  if (!(y > 0.0) || !(s > 0.0)) return 0.0;
+  double q = y / s;
+  for (int k = 0; k < 7; ++k)
+    if (fabs(q - mid[k]) <= eps * q) return (tho_e2m1_mag[k + 1] - tho_e2m1_mag[k]) * s;
+  return 0.0;
+}
+
+/* One fp16 spacing at y if y sits within relative eps of an fp16 midpoint. */
+static double tho_half_flip(double y, double eps) {
+  if (!(y > 0.0)) return 0.0;
+  int e;
+  frexp(y, &e);
+  int ue = e - 11 < -24 ? -24 : e - 11;
+  double sp = ldexp(1.0, ue);
+  double mid = floor(y / sp) * sp + 0.5 * sp;
+  return fabs(y - mid) <= eps * y ? sp : 0.0;
+}
+
+/* Quantise v[g0..g1) of one group with block scale s2 into out[] (values). */
+static void tho_quantize_group_values(const double* v, int g0, int g1, double s2, double* out) {
+  for (int c = g0; c < g1; ++c) out[c] = s2 > 0.0 ? tho_e2m1_value(tho_e2m1_encode(v[c], s2)) * s2 : 0.0;
+}
+
 static void tho_quantize_p_tile(const double* t, const int* mask, int n, int fmt, double mt,
-                                double* pq, double* ref) {
+                                double* pq, double* dq, double* ref) {
   int g = tho_group_size(fmt);
-  double v[64];
+  double v[64], alt[64];
   if (fmt == THO_NVFP4) {
     for (int c = 0; c < n; ++c) v[c] = mask[c] ? 0.0 : 2688.0 * exp2(t[c] - mt);
     *ref = mt;
@@ -445,6 +484,40 @@ static void tho_quantize_p_tile(const double* t, const int* mask, int n, int fmt
       double s2 = ldexp(1.0, tho_mx_exponent(amax));
       for (int c = g0; c < g1; ++c) pq[c] = tho_e2m1_value(tho_e2m1_encode(v[c], s2)) * s2;
     }
+    if (!dq) continue;
+    /* uncertainty: element codes near a midpoint, and a block scale near its
+     * own rounding boundary (NVFP4 values carry the error of two
+     * exponentials, the element's and the tile maximum's) */
+    double unit = fmt == THO_NVFP4 ? 1.0 / 2688.0 : 1.0;
+    double tg = -INFINITY;
+    for (int c = g0; c < g1; ++c)
+      if (!mask[c] && t[c] > tg) tg = t[c];
+    double eg = (fmt == THO_NVFP4 ? 2.0 : 1.0) * tho_eval_eps(tg);
+    double s2, s2alt;
+    if (fmt == THO_NVFP4) {
+      int code = tho_e4m3_encode_ratio(amax, 6.0);
+      int lo = tho_e4m3_encode_ratio(amax * (1.0 - 2.0 * eg), 6.0);
+      int hi = tho_e4m3_encode_ratio(amax * (1.0 + 2.0 * eg), 6.0);
+      s2 = tho_e4m3_value(code);
+      s2alt = tho_e4m3_value(lo != code ? lo : hi);
+    } else {
+      int X = tho_mx_exponent(amax);
+      int lo = tho_mx_exponent(amax * (1.0 - 2.0 * eg));
+      int hi = tho_mx_exponent(amax * (1.0 + 2.0 * eg));
+      s2 = ldexp(1.0, X);
+      s2alt = ldexp(1.0, lo != X ? lo : hi);
+    }
+    if (s2alt != s2) tho_quantize_group_values(v, g0, g1, s2alt, alt);
+    for (int c = g0; c < g1; ++c) {
+      if (mask[c]) {
+        dq[c] = 0.0;
+        continue;
+      }
+      double ec = (fmt == THO_NVFP4 ? 2.0 : 1.0) * tho_eval_eps(t[c]);
+      double d = tho_e2m1_flip(v[c], s2, ec);
+      if (s2alt != s2) d += fabs(alt[c] - pq[c] / unit) + tho_e2m1_flip(v[c], s2alt, ec);
+      dq[c] = d * unit;
+    }
   }
 }
 
@@ -460,7 +533,7 @@ typedef struct {
 
 /* One query row r of query block i of head (b, hq). */
 static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, double* o_row,
-                           double* lse_out) {
+                           double* lse_out, double* u_row) {
   int D = a->D, S = a->S, bk = a->bk;
   int hk = hq / (a->Hq / a->Hkv);
   int nq = tho_cdiv(S, a->bq);
@@ -469,9 +542,10 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
   const int32_t* sel = a->idx + (((size_t)b * a->Hq + hq) * nq + i) * a->kmax;
   int nsel = a->cnt[((size_t)b * a->Hq + hq) * nq + i];
   int nvalid = tho_valid_blocks(i, S, a->bq, bk, a->causal);
-  double t[64], pq[64];
+  double t[64], pq[64], dq[64];
   int mask[64];
   double* acc = (double*)calloc((size_t)D, sizeof(double));
+  double* uacc = (double*)calloc((size_t)D, sizeof(double)); /* uncertainty, like acc */
   double* qh = (double*)malloc(sizeof(double) * (size_t)D);
   double* q4 = (double*)malloc(sizeof(double) * (size_t)D);
   double m = -INFINITY, l = 0.0;
@@ -499,10 +573,16 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
     }
     if (mt == -INFINITY) continue; /* every key of this block is masked for row r */
     double ref;
-    tho_quantize_p_tile(t, mask, n, a->fmt, mt, pq, &ref);
+    tho_quantize_p_tile(t, mask, n, a->fmt, mt, pq, u_row ? dq : NULL, &ref);
     double m_new = m > mt ? m : mt;
     double alpha = exp2(m - m_new); /* 0 when m = -inf */
     double w = exp2(ref - m_new);
+    if (u_row)
+      for (int d = 0; d < D; ++d) {
+        double uv = 0.0;
+        for (int c = 0; c < n; ++c) uv += dq[c] * fabs(a->v4[(kvbase + c0 + c) * D + d]);
+        uacc[d] = alpha * uacc[d] + w * uv;
+      }
     double psum = 0.0;
     for (int c = 0; c < n; ++c)
       if (!mask[c]) psum += exp2(t[c] - m_new);
@@ -544,11 +624,20 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
     for (int c = 0; c < n; ++c) {
       if (mask[c]) {
         pq[c] = 0.0;
+        dq[c] = 0.0;
         continue;
       }
       psum += exp2(t[c] - m_new);
       pq[c] = tho_round_to_half(exp2(t[c] - z)) * exp2(z - m_new);
+      dq[c] = tho_half_flip(exp2(t[c] - z), tho_eval_eps(t[c])) * exp2(z - m_new);
     }
+    if (u_row)
+      for (int d = 0; d < D; ++d) {
+        double uv = 0.0;
+        for (int c = 0; c < n; ++c)
+          if (!mask[c]) uv += dq[c] * fabs(tho_half_to_double(a->v16[(kvbase + c0 + c) * D + d]));
+        uacc[d] = alpha * uacc[d] + uv;
+      }
     l = alpha * l + psum;
     for (int d = 0; d < D; ++d) {
       double pv = 0.0;
@@ -560,7 +649,10 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
   }
 
   for (int d = 0; d < D; ++d) o_row[d] = acc[d] / l;
+  if (u_row)
+    for (int d = 0; d < D; ++d) u_row[d] = uacc[d] / l;
   if (lse_out) *lse_out = m * THO_LN2 + log(l);
+  free(uacc);
   free(q4);
   free(qh);
   free(acc);
@@ -569,14 +661,17 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
 /* Full forward for a list of work items (b, hq, i) (NULL: all of them).
  * q4/k4/v4 are the FP4 tensors as written by tho_quantize (V along the
  * sequence axis); q16/k16/v16 may be NULL when no block is promoted.
- * o: [B, Hq, S, D] fp64 and lse: [B, Hq, S] (may be NULL); rows outside the
- * work items are left untouched. */
+ * o: [B, Hq, S, D] fp64, lse: [B, Hq, S] (may be NULL) and u: [B, Hq, S, D]
+ * (may be NULL), the bound on what decisions within fp32 evaluation error of
+ * their rounding boundary can change in o; rows outside the work items are
+ * left untouched. */
 void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
                    const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
                    const uint8_t* k4s, const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
                    const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
                    int B, int Hq, int Hkv, int S, int D, int bq, int bk, int causal,
-                   double sm_scale, const int32_t* work, int nwork, double* o, double* lse) {
+                   double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
+                   double* u) {
   tho_attn_args a;
   a.B = B;
   a.Hq = Hq;
@@ -620,7 +715,7 @@ void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16
     int r0 = i * bq, r1 = r0 + bq < S ? r0 + bq : S;
     for (int r = r0; r < r1; ++r) {
       size_t row = ((size_t)b * Hq + hq) * S + r;
-      tho_attend_row(&a, b, hq, i, r, o + row * D, lse ? lse + row : NULL);
+      tho_attend_row(&a, b, hq, i, r, o + row * D, lse ? lse + row : NULL, u ? u + row * D : NULL);
     }
   }
   free(v4);

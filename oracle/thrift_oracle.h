@@ -43,7 +43,8 @@ void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16
                    const uint8_t* k4s, const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
                    const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
                    int B, int Hq, int Hkv, int S, int D, int bq, int bk, int causal,
-                   double sm_scale, const int32_t* work, int nwork, double* o, double* lse);
+                   double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
+                   double* u);
 void tho_fp4_scores(const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
                     const uint8_t* k4s, const float* k4t, int fmt, int S, int D, int r, int c0,
                     int c1, double* out);

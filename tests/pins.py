@@ -123,10 +123,13 @@ def quantize_p_tile(t, mask, fmt):
     return pq, ref
 
 
-def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal, sm_scale):
+def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal, sm_scale,
+                       perturb=None):
     """Dense two-pass restatement of the forward pass: every score first,
     then one global maximum per row, then the weighted sum.  q4/k4/v4 and
-    q16/k16/v16 are fp64 [B,H,S,D] (dequantised FP4 / decoded fp16)."""
+    q16/k16/v16 are fp64 [B,H,S,D] (dequantised FP4 / decoded fp16).
+    perturb(t) -> t', if given, moves the scores that feed the rounding
+    decisions of P (not the row sum), as a lower-precision evaluation would."""
     B, Hq, S, D = q4.shape
     Hkv = k4.shape[1]
     G = Hq // Hkv
@@ -157,12 +160,18 @@ def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal,
                     for t, m, is16, c0, c1 in tiles:
                         e = np.where(m, 0.0, np.exp2(np.where(m, 0, t) - M))
                         l += e.sum()
+                        tq = t if perturb is None else np.where(m, t, perturb(t))
                         if is16:
                             z = np.ceil(M)
-                            p = np.where(m, 0.0, fp16_round(np.exp2(np.where(m, 0, t) - z))) * np.exp2(z - M)
+                            p = np.where(m, 0.0, fp16_round(np.exp2(np.where(m, 0, tq) - z))) * np.exp2(z - M)
                             acc += p @ v16[b, hk, c0:c1]
                         else:
-                            pq, ref = quantize_p_tile(t, m, fmt)
+                            pq, ref = quantize_p_tile(tq, m, fmt)
+                            if perturb is not None and fmt == 0:
+                                # NVFP4 level 1 divides by the tile maximum: keep the
+                                # unperturbed one so that only the decisions move (MX
+                                # codes carry their own power-of-two offset)
+                                ref += np.max(np.where(m, -np.inf, t)) - np.max(np.where(m, -np.inf, tq))
                             acc += (pq * np.exp2(ref - M)) @ v4[b, hk, c0:c1]
                     O[b, hq, r] = acc / l
                     L[b, hq, r] = M * LN2 + np.log(l)

@@ -1,0 +1,102 @@
+"""The C-ABI library loads, exports every call its header declares, and
+rejects invalid arguments before launching anything (CPU only: every call
+below fails validation, so no kernel runs and no GPU is needed)."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from fp16_attention_amd import _lib
+
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libthrift.so is not built (run __graft_entry__.build())")
+    return _lib.load()
+
+
+def test_header_symbols_exported(lib):
+    hdr = open(os.path.join(ROOT, "include", "thrift.h")).read()
+    names = set(re.findall(r"\b(thrift_[a-z0-9_]+)\s*\(", hdr))
+    assert names == set(__import__("fp16_attention_amd._lib", fromlist=["EXPORTS"]).EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_kmax_matches_oracle(lib, oracle):
+    for args in [(32768, 128, 64, 1, -1, 500), (17550, 128, 64, 0, -1, 500), (256, 64, 64, 0, 2, 0),
+                 (131072, 128, 64, 1, -1, 200), (1000, 64, 64, 1, -1, 10000), (100, 128, 64, 1, 0, 0)]:
+        assert lib.thrift_select_kmax(*args) == oracle.kmax(*args)
+    assert lib.thrift_select_kmax(0, 128, 64, 1, -1, 500) == -1
+
+
+def test_status_strings(lib):
+    for s in range(6):
+        assert lib.thrift_status_string(s)
+    assert b"unknown" in lib.thrift_status_string(99)
+
+
+A = 4096  # a non-null, 16-byte aligned fake device address (never dereferenced)
+
+
+def test_select_validation(lib):
+    f = lib.thrift_select_blocks
+    ok = dict(q=A, k=A, B=1, Hq=4, Hkv=2, S=1024, D=128, bq=128, bk=64, causal=1, tc=-1, bp=500,
+              idx=A, cnt=A, kmax=2, ws=A, wsb=1 << 30, st=None)
+
+    def call(**kw):
+        a = dict(ok, **kw)
+        return f(a["q"], a["k"], a["B"], a["Hq"], a["Hkv"], a["S"], a["D"], a["bq"], a["bk"],
+                 a["causal"], a["tc"], a["bp"], a["idx"], a["cnt"], a["kmax"], a["ws"], a["wsb"], a["st"])
+
+    assert call(q=None) == 1
+    assert call(Hq=3) == 1  # Hq % Hkv
+    assert call(D=96) == 2
+    assert call(bk=128) == 2
+    assert call(S=300000) == 2
+    assert call(kmax=0) == 1  # budget needs 2 per block at the end
+    assert call(bp=-5) == 1
+    assert call(causal=2) == 1
+    assert call(q=A + 8) == 3
+    assert call(wsb=16) == 4
+
+
+def test_quantize_validation(lib):
+    f = lib.thrift_quantize_fp4
+
+    def call(x=A, B=1, H=2, S=100, D=128, axis=0, fmt=1, codes=A, scales=A, ts=A, ws=A, wsb=1 << 20):
+        return f(x, B, H, S, D, axis, fmt, codes, scales, ts, ws, wsb, None)
+
+    assert call(x=None) == 1
+    assert call(fmt=3) == 1
+    assert call(axis=2) == 1
+    assert call(fmt=0, ts=None) == 1
+    assert call(D=256) == 2
+    assert call(codes=A + 4) == 3
+    assert call(fmt=0, wsb=0) == 4
+    assert lib.thrift_quantize_workspace_bytes(1, 2, 100, 128, 1) == 0
+    assert lib.thrift_quantize_workspace_bytes(1, 2, 100, 128, 0) > 0
+
+
+def test_attention_validation(lib):
+    f = lib.thrift_attention_fwd
+
+    def call(q16=A, k16=A, v16=A, fmt=1, ts=A, kmax=4, B=1, Hq=2, Hkv=1, S=512, D=128, bq=128, bk=64,
+             causal=1, sm=0.088, o=A, o32=1):
+        return f(q16, k16, v16, A, A, ts, A, A, ts, A, A, ts, fmt, A, A, kmax, B, Hq, Hkv, S, D, bq, bk,
+                 causal, sm, o, o32, None, None)
+
+    assert call(o=None) == 1
+    assert call(k16=None) == 1  # all three fp16 tensors or none
+    assert call(fmt=0, ts=None) == 1
+    assert call(Hq=3, Hkv=2) == 1
+    assert call(sm=0.0) == 1
+    assert call(sm=float("nan")) == 1
+    assert call(D=80) == 2
+    assert call(bq=96) == 2
+    assert call(kmax=9) == 2  # more than the 8 key blocks of S = 512
+    assert call(o=A + 2) == 3
+    assert call(o32=3) == 1
