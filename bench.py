@@ -66,6 +66,9 @@ def main():
     ap.add_argument("--topk-bp", type=int, default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--copy-mib", type=int, default=0,
+                    help="run one plain device copy of this many MiB before the steps (a "
+                         "kernel of known traffic, to calibrate profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this path runs on one GPU; multi-GPU runs are not part of this build "
@@ -90,6 +93,13 @@ def main():
     o = torch.empty_like(q)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    if args.copy_mib:
+        src = torch.empty(args.copy_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     def step(rec=None):
         if rec:

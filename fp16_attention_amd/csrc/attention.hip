@@ -13,6 +13,12 @@
 //    scores are computed transposed, S^T = K Q^T, so the 32x32 MFMA output
 //    puts a query in each lane column, and O^T = V^T P^T keeps it there.  The
 //    softmax state (running max, running sum) is then one scalar per lane.
+//  * The rows of the K operand are permuted so that the MFMA output hands
+//    each lane 32 CONSECUTIVE keys of its query (lanes 0-31 keys 0-31 of the
+//    tile, lanes 32-63 keys 32-63): that is one MX group of P, already in the
+//    order the P^T operand of the second product wants, so the softmax and P
+//    quantisation need no cross-lane traffic (the pair of lanes sharing a
+//    query exchanges its maximum only when the running offset moves).
 //  * MXFP4: both products use the block-scaled MFMA
 //    v_mfma_scale_f32_32x32x64_f8f6f4 with E2M1 operands and E8M0 scales per
 //    32 elements of the contraction: Q/K groups run along D, V and P groups
@@ -73,14 +79,16 @@ struct Lds {
   static constexpr int VC = KS + kBk * 4;
   static constexpr int VS = VC + D * VROW4;    // u32 [2][32]: byte dt = scale(dt*32+r, kb)
   static constexpr int STAGE4 = VS + 2 * 32 * 4;
+  static constexpr int STAGE4R = (STAGE4 + 255) / 256 * 256;  // MX ring: three of these
   // fp16 stage (FP16 path, NVFP4 FP4 path)
   static constexpr int KROWH = D + 8;    // halves per key row
-  static constexpr int VROWH = kBk + 4;  // halves per V^T row
+  static constexpr int VROWH = kBk + 8;  // halves per V^T row (16-byte aligned)
   static constexpr int KH = 0;
   static constexpr int VT = KH + kBk * KROWH * 2;
   static constexpr int STAGEH = VT + D * VROWH * 2;
   static constexpr int STAGE = ((STAGE4 > STAGEH ? STAGE4 : STAGEH) + 255) / 256 * 256;
-  static constexpr int PROM = 2 * STAGE;  // int[kmax] promoted list
+  static constexpr int RING = (3 * STAGE4R > 2 * STAGE ? 3 * STAGE4R : 2 * STAGE);
+  static constexpr int PROM = RING;  // int[kmax] promoted list
 };
 
 // ---- small helpers ---------------------------------------------------------------
@@ -116,8 +124,26 @@ __device__ inline v4h fp4x4_to_h(uint32_t codes16, _Float16 f) {
   return v4h{a.x, a.y, b.x, b.y};
 }
 
-// Key index of register i of a 32x32 S^T tile mt, in the lane's half.
-__device__ inline int key_of(int mt, int i, int hi) { return mt * 32 + (i >> 2) * 8 + hi * 4 + (i & 3); }
+// Key (within the 64-key tile) that A-operand row m of 32x32 S^T tile mt
+// reads.  The MFMA output puts row (i/4)*8 + hi*4 + i%4 in register i of a
+// lane of half hi, so register i of tile mt holds key hi*32 + mt*16 + i.
+__device__ inline int krow(int mt, int m) { return ((m >> 2) & 1) * 32 + mt * 16 + (m >> 3) * 4 + (m & 3); }
+// K tiles are stored in LDS in that read order (key krow(mt, m) at row
+// mt*32 + m), so the 32 lanes of a half-wave read consecutive rows; kslot is
+// the inverse map, key -> LDS row.
+__device__ inline int kslot(int key) {
+  const int h = key >> 5, mt = (key >> 4) & 1, i = key & 15;
+  return mt * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
+}
+__device__ inline int key_of(int mt, int i, int hi) { return hi * 32 + mt * 16 + i; }
+
+// Value of the other lane holding the same query (lane +- 32).
+__device__ inline float pair_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---- online-softmax state ------------------------------------------------------
 
@@ -129,14 +155,17 @@ struct RowState {
   float g;           // acc holds O^T / g (NVFP4 FP4 path; 1 elsewhere)
 };
 
-// Lazy rescale: if the tile maximum tml2 (log2 units) exceeds m + kTau,
-// move m to ceil(tml2) and rescale by the exact power of two.
+// Lazy rescale: if the tile maximum (log2 units) of a query exceeds m +
+// kTau, move m to its ceiling and rescale by the exact power of two.  own is
+// this lane's half of the tile maximum (raw score units, c > 0); both lanes
+// of the query decide on the pair's maximum, so they keep the same m.
 template <int D>
-__device__ inline void maybe_rescale(RowState<D>& st, float tml2) {
-  bool need = tml2 > st.m + kTau;
-  if (__builtin_amdgcn_ballot_w64(need)) {
-    float mn = need ? ceilf(tml2) : st.m;
-    float f = need ? exp2f(st.m - mn) : 1.0f;  // integer difference: exact
+__device__ inline void maybe_rescale(RowState<D>& st, float own, float c) {
+  if (__builtin_amdgcn_ballot_w64(own * c > st.m + kTau)) {
+    const float tml2 = pair_max(own) * c;
+    const bool need = tml2 > st.m + kTau;
+    const float mn = need ? ceilf(tml2) : st.m;
+    const float f = need ? exp2f(st.m - mn) : 1.0f;  // integer difference: exact
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] *= f;
     st.l *= f;
@@ -166,38 +195,45 @@ __device__ inline float max16(const v16f& v) {
 
 // ---- MX FP4 tile ------------------------------------------------------------------
 
+// S^T = K Q^T for one MX tile: two 32-row tiles, D/64 contraction steps of
+// 64 channels, block-scaled by the E8M0 bytes of K and Q.
 template <int D>
-__device__ inline void fp4_mx_tile(RowState<D>& st, const char* stage, const v4i* qB, uint32_t qsc,
-                                   float c, int key0, int qrow, int S, int causal, bool need_mask,
-                                   int lane) {
+__device__ inline void qk_mx(v16f s[2], const char* stage, const v4i* qB, uint32_t qsc, int lane) {
   using L = Lds<D>;
   const int hi = lane >> 5, r32 = lane & 31;
   const uint8_t* kc = (const uint8_t*)(stage + L::KC);
   const uint32_t* ks = (const uint32_t*)(stage + L::KS);
-  const uint8_t* vc = (const uint8_t*)(stage + L::VC);
-  const uint32_t* vs = (const uint32_t*)(stage + L::VS);
-
-  // S^T = K Q^T: two 32-key tiles, D/64 contraction steps of 64 channels.
-  v16f s[2];
+  uint32_t ksc[2];
+  v4i a[2][D / 64];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    const int row = mt * 32 + r32;
-    const uint32_t ksc = ks[row] >> (8 * hi);  // byte 2*kstep: this lane's 32-channel group
-    s[mt] = v16f{};
-    v4i a0 = *(const v4i*)(kc + row * L::KROW4 + hi * 16);
-    s[mt] = mfma_fp4<0, 0>(a0, qB[0], s[mt], ksc, qsc);
-    if constexpr (D == 128) {
-      v4i a1 = *(const v4i*)(kc + row * L::KROW4 + 32 + hi * 16);
-      s[mt] = mfma_fp4<2, 2>(a1, qB[1], s[mt], ksc, qsc);
-    }
+    const int row = mt * 32 + r32;       // holds key krow(mt, r32)
+    ksc[mt] = ks[row] >> (8 * hi);       // byte 2*kstep: this lane's 32-channel group
+#pragma unroll
+    for (int kk = 0; kk < D / 64; ++kk) a[mt][kk] = *(const v4i*)(kc + row * L::KROW4 + kk * 32 + hi * 16);
   }
+  s[0] = mfma_fp4<0, 0>(a[0][0], qB[0], v16f{}, ksc[0], qsc);
+  s[1] = mfma_fp4<0, 0>(a[1][0], qB[0], v16f{}, ksc[1], qsc);
+  if constexpr (D == 128) {
+    s[0] = mfma_fp4<2, 2>(a[0][1], qB[1], s[0], ksc[0], qsc);
+    s[1] = mfma_fp4<2, 2>(a[1][1], qB[1], s[1], ksc[1], qsc);
+  }
+}
+
+// Softmax, two-level MX quantisation of P and O^T += V^T P^T for one tile.
+template <int D>
+__device__ inline void softmax_pv_mx(RowState<D>& st, v16f s[2], const char* stage, float c,
+                                     int key0, int qrow, int S, int causal, bool need_mask,
+                                     int lane) {
+  using L = Lds<D>;
+  const int hi = lane >> 5, r32 = lane & 31;
+  const uint8_t* vc = (const uint8_t*)(stage + L::VC);
+  const uint32_t* vs = (const uint32_t*)(stage + L::VS);
   if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
 
-  // group maxima (32 keys each: this lane's 16 and its partner's 16)
-  float g0 = max16(s[0]), g1 = max16(s[1]);
-  g0 = fmaxf(g0, xlane32(g0));
-  g1 = fmaxf(g1, xlane32(g1));
-  maybe_rescale<D>(st, fmaxf(g0, g1) * c);
+  // this lane's 32 keys are one P group: its maximum sets the E8M0 exponent
+  const float gmax = fmaxf(max16(s[0]), max16(s[1]));
+  maybe_rescale<D>(st, gmax, c);
   const float nm = -st.m;
 
   // probabilities relative to 2^m, unquantised row sum
@@ -206,38 +242,31 @@ __device__ inline void fp4_mx_tile(RowState<D>& st, const char* stage, const v4i
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float p = exp2f(__builtin_fmaf(s[mt][i], c, nm));
+      float p = exp2_fast(__builtin_fmaf(s[mt][i], c, nm));
       s[mt][i] = p;
       lsum += p;
     }
   st.l += lsum;
 
-  // E8M0 group exponents: floor(log2(max p)) - 2, from the exponent field
-  const uint32_t E0 = (__float_as_uint(exp2f(__builtin_fmaf(g0, c, nm))) >> 23) & 0xFF;
-  const uint32_t E1 = (__float_as_uint(exp2f(__builtin_fmaf(g1, c, nm))) >> 23) & 0xFF;
-  const uint32_t b0 = E0 > 3 ? E0 - 2 : 1, b1 = E1 > 3 ? E1 - 2 : 1;
-  const float sf0 = __uint_as_float(b0 << 23), sf1 = __uint_as_float(b1 << 23);
+  // E8M0 exponent floor(log2(max p)) - 2 from the exponent field of the
+  // group maximum's probability (computed like the elements' own)
+  const uint32_t E = (__float_as_uint(exp2_fast(__builtin_fmaf(gmax, c, nm))) >> 23) & 0xFF;
+  const uint32_t psc = E > 3 ? E - 2 : 1;
+  const float sf = __uint_as_float(psc << 23);
 
-  // E2M1 codes; dword r: bytes 0-1 = run r of tile 0, bytes 2-3 = run r of tile 1
-  uint32_t X[4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    uint32_t x = 0;
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[0][4 * r + 0], s[0][4 * r + 1], sf0, 0);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[0][4 * r + 2], s[0][4 * r + 3], sf0, 1);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[1][4 * r + 0], s[1][4 * r + 1], sf1, 2);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, s[1][4 * r + 2], s[1][4 * r + 3], sf1, 3);
-    X[r] = x;
-  }
-  // P^T operand: lanes 0-31 take keys 0-31 (group 0), lanes 32-63 keys 32-63,
-  // each in contiguous nibble order; the partner lane holds the other runs.
+  // P^T operand: nibble n of this lane = key hi*32 + n = register n%16 of tile n/16
   v4i P;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    uint32_t y = xlane32u(X[r]);
-    P[r] = (int)(hi ? ((y >> 16) | (X[r] & 0xFFFF0000u)) : ((X[r] & 0xFFFFu) | (y << 16)));
+    const v16f& v = s[r >> 1];
+    const int o = (r & 1) * 8;
+    uint32_t x = 0;
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[o + 0], v[o + 1], sf, 0);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[o + 2], v[o + 3], sf, 1);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[o + 4], v[o + 5], sf, 2);
+    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[o + 6], v[o + 7], sf, 3);
+    P[r] = (int)x;
   }
-  const uint32_t psc = hi ? b1 : b0;
 
   // O^T += V^T P^T
   const uint32_t vsw = vs[hi * 32 + r32];
@@ -260,14 +289,15 @@ __device__ inline void qk_f16(v16f s[2], const char* stage, const v8h* qh, int l
   const _Float16* kh = (const _Float16*)(stage + L::KH);
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    const _Float16* row = kh + (mt * 32 + r32) * L::KROWH + hi * 8;
+    const _Float16* row = kh + (mt * 32 + r32) * L::KROWH + hi * 8;  // key krow(mt, r32)
     s[mt] = v16f{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) s[mt] = mfma_f16(*(const v8h*)(row + kk * 16), qh[kk], s[mt]);
   }
 }
 
-// O^T += V^T P^T, P given as four 8-key operands (keys st*16 + (u/4)*8 + hi*4 + u%4).
+// O^T += V^T P^T over four 16-key steps; in step st this lane supplies
+// keys hi*32 + 8*st + u (u = 0..7), its registers 8*(st%2)+u of tile st/2.
 template <int D>
 __device__ inline void pv_f16(RowState<D>& st, const char* stage, const v8h* pB, int lane) {
   using L = Lds<D>;
@@ -277,10 +307,7 @@ __device__ inline void pv_f16(RowState<D>& st, const char* stage, const v8h* pB,
   for (int stp = 0; stp < 4; ++stp)
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
-      const _Float16* row = vt + (dt * 32 + r32) * L::VROWH + stp * 16 + hi * 4;
-      v4h a0 = *(const v4h*)(row);
-      v4h a1 = *(const v4h*)(row + 8);
-      v8h a = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      const v8h a = *(const v8h*)(vt + (dt * 32 + r32) * L::VROWH + hi * 32 + stp * 8);
       st.acc[dt] = mfma_f16(a, pB[stp], st.acc[dt]);
     }
 }
@@ -293,9 +320,7 @@ __device__ inline void fp16_tile(RowState<D>& st, const char* stage, const v8h* 
   v16f s[2];
   qk_f16<D>(s, stage, qh, lane);
   if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
-  float tm = fmaxf(max16(s[0]), max16(s[1]));
-  tm = fmaxf(tm, xlane32(tm));
-  maybe_rescale<D>(st, tm * c);
+  maybe_rescale<D>(st, fmaxf(max16(s[0]), max16(s[1])), c);
   const float nm = -st.m;
   float lsum = 0.0f;
   v8h pB[4];
@@ -303,7 +328,7 @@ __device__ inline void fp16_tile(RowState<D>& st, const char* stage, const v8h* 
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float p = exp2f(__builtin_fmaf(s[mt][i], c, nm));
+      float p = exp2_fast(__builtin_fmaf(s[mt][i], c, nm));
       lsum += p;
       pB[mt * 2 + i / 8][i % 8] = (_Float16)p;
     }
@@ -325,21 +350,21 @@ __device__ inline void fp4_nv_tile(RowState<D>& st, const char* stage, const v8h
   v16f s[2];
   qk_f16<D>(s, stage, qh, lane);
   if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
-  float tm = fmaxf(max16(s[0]), max16(s[1]));
-  tm = fmaxf(tm, xlane32(tm));
-  maybe_rescale<D>(st, tm * c);
+  const float gm0 = max16(s[0]), gm1 = max16(s[1]);  // this lane's two 16-key groups
+  maybe_rescale<D>(st, fmaxf(gm0, gm1), c);
+  const float tm = pair_max(fmaxf(gm0, gm1));  // the query's tile maximum (level 1)
   const float nm = -st.m;
   float lsum = 0.0f;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      float p = exp2f(__builtin_fmaf(s[mt][i], c, nm));
+      float p = exp2_fast(__builtin_fmaf(s[mt][i], c, nm));
       s[mt][i] = p;
       lsum += p;
     }
   st.l += lsum;
-  const float em = exp2f(__builtin_fmaf(tm, c, nm));  // probability of the tile maximum
+  const float em = exp2_fast(__builtin_fmaf(tm, c, nm));  // probability of the tile maximum
   // a tile more than 2^60 below the running maximum contributes nothing
   const bool live = em > 0x1p-60f;
   const float r = live ? 2688.0f / em : 0.0f;  // level 1: maximum -> 6 * 448
@@ -350,26 +375,27 @@ __device__ inline void fp4_nv_tile(RowState<D>& st, const char* stage, const v8h
   st.g = f;
   v8h pB[4];
 #pragma unroll
-  for (int g = 0; g < 4; ++g) {  // 16-key groups: regs 8(g%2).. of tile g/2, both lanes
-    const v16f& v = s[g / 2];
-    const int o = (g % 2) * 8;
-    float gm = fmaxf(fmaxf(fmaxf(v[o], v[o + 1]), fmaxf(v[o + 2], v[o + 3])),
-                     fmaxf(fmaxf(v[o + 4], v[o + 5]), fmaxf(v[o + 6], v[o + 7])));
-    gm = fmaxf(gm, xlane32(gm)) * r;
+  for (int g = 0; g < 2; ++g) {  // group g = keys hi*32 + 16g .. +15 = registers of tile g
+    const v16f& v = s[g];
+    const float gm = exp2_fast(__builtin_fmaf(g ? gm1 : gm0, c, nm)) * r;
     // level 2: E4M3 block scale (the conversion does not saturate: clamp)
     v2s_t sb = {0, 0};
     sb = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(sb, fminf(gm * (1.0f / 6.0f), 448.0f), 0.0f, 1.0f, false);
     const float s2 = e4m3_to_float((uint32_t)sb[0] & 0xFF);
     const float k = s2 > 0.0f ? r / s2 : 0.0f;
-    uint32_t cw = 0;
-    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[o + 0] * k, v[o + 1] * k, 1.0f, 0);
-    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[o + 2] * k, v[o + 3] * k, 1.0f, 1);
-    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[o + 4] * k, v[o + 5] * k, 1.0f, 2);
-    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[o + 6] * k, v[o + 7] * k, 1.0f, 3);
     const _Float16 s2h = (_Float16)(live ? s2 : 0.0f);  // exact: E4M3 has 4 significant bits
-    v4h lo = fp4x4_to_h(cw & 0xFFFFu, s2h);
-    v4h hi4 = fp4x4_to_h(cw >> 16, s2h);
-    pB[g] = v8h{lo.x, lo.y, lo.z, lo.w, hi4.x, hi4.y, hi4.z, hi4.w};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {  // 8 keys per P^T operand
+      const int o = h * 8;
+      uint32_t cw = 0;
+      cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[o + 0] * k, v[o + 1] * k, 1.0f, 0);
+      cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[o + 2] * k, v[o + 3] * k, 1.0f, 1);
+      cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[o + 4] * k, v[o + 5] * k, 1.0f, 2);
+      cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[o + 6] * k, v[o + 7] * k, 1.0f, 3);
+      v4h lo = fp4x4_to_h(cw & 0xFFFFu, s2h);
+      v4h hi4 = fp4x4_to_h(cw >> 16, s2h);
+      pB[g * 2 + h] = v8h{lo.x, lo.y, lo.z, lo.w, hi4.x, hi4.y, hi4.z, hi4.w};
+    }
   }
   pv_f16<D>(st, stage, pB, lane);
 }
@@ -382,7 +408,9 @@ namespace thrift {
 
 // MX FP4 tile: K codes [64 keys][D/2 B], K scales (one u32 per key row),
 // V^T codes [D][32 B], V^T scales regrouped so that a lane reads the scale
-// bytes of its four d-tiles with one 32-bit load.
+// bytes of its four d-tiles with one 32-bit load.  Loads are unconditional:
+// key rows past S (last tile only) read row S-1 instead, and their scores
+// are masked anyway.
 template <int D, int NT>
 struct Mx4Stager {
   static constexpr int NKC = kBk * D / 32;  // 16-byte chunks of K codes
@@ -391,53 +419,56 @@ struct Mx4Stager {
   v4i kc[PK], vc[PV];
   uint32_t ksc, vsc;
 
-  __device__ void load(const AttnArgs& a, size_t bhk, int j, int t) {
+  struct Base {  // per-workgroup bases of the key head's FP4 tensors
+    const uint8_t *kc, *ks, *vc, *vs;
+    int S, Sp;
+  };
+
+  __device__ static Base base(const AttnArgs& a, size_t bhk) {
+    return Base{a.k4c + bhk * a.S * (D / 2), a.k4s + bhk * a.S * (D / 32),
+                a.v4c + bhk * D * (a.Sp / 2), a.v4s + bhk * D * (a.Sp / 32), a.S, a.Sp};
+  }
+
+  // Every thread issues the same number of loads on every tile (threads past
+  // a table re-read an in-range entry and drop it), so the compiler can wait
+  // for exactly the older tile's loads and leave the newer ones in flight.
+  __device__ void load(const Base& g, int j, int t) {
 #pragma unroll
     for (int p = 0; p < PK; ++p) {
-      int c = t + p * NT;
-      kc[p] = v4i{};
-      if (c < NKC) {
-        int row = c / (D / 32), col = c % (D / 32), key = j * kBk + row;
-        if (key < a.S) kc[p] = *(const v4i*)(a.k4c + ((bhk * a.S + key) * (D / 2)) + col * 16);
-      }
+      const int c = (t + p * NT) % NKC;
+      const int row = c / (D / 32), col = c % (D / 32);
+      const uint32_t key = (uint32_t)min(j * kBk + row, g.S - 1);
+      kc[p] = *(const v4i*)(g.kc + (key * (D / 2) + col * 16));
     }
 #pragma unroll
     for (int p = 0; p < PV; ++p) {
-      int c = t + p * NT;
-      vc[p] = v4i{};
-      if (c < NVC) {
-        int d = c / 2, h = c % 2;
-        vc[p] = *(const v4i*)(a.v4c + (bhk * D + d) * (a.Sp / 2) + j * 32 + h * 16);
-      }
+      const int c = (t + p * NT) % NVC;
+      vc[p] = *(const v4i*)(g.vc + ((uint32_t)(c / 2) * (uint32_t)(g.Sp / 2) + j * 32 + (c % 2) * 16));
     }
-    ksc = 0x7F7F7F7Fu;  // padded keys: unit scales (their codes are zero)
-    if (t < kBk) {
-      int key = j * kBk + t;
-      if (key < a.S) {
-        const uint8_t* p = a.k4s + (bhk * a.S + key) * (D / 32);
-        ksc = D == 128 ? *(const uint32_t*)p : (uint32_t)(*(const uint16_t*)p);
-      }
+    {
+      const uint32_t key = (uint32_t)min(j * kBk + t % kBk, g.S - 1);
+      const uint8_t* p = g.ks + key * (D / 32);
+      ksc = D == 128 ? *(const uint32_t*)p : (uint32_t)(*(const uint16_t*)p);
     }
-    vsc = 0;
-    if (t < D) vsc = *(const uint16_t*)(a.v4s + (bhk * D + t) * (a.Sp / 32) + j * 2);
+    vsc = *(const uint16_t*)(g.vs + ((uint32_t)(t % D) * (uint32_t)(g.Sp / 32) + j * 2));
   }
 
   __device__ void store(char* stage, int t) const {
     using L = Lds<D>;
 #pragma unroll
     for (int p = 0; p < PK; ++p) {
-      int c = t + p * NT;
-      if (c < NKC) {
-        int row = c / (D / 32), col = c % (D / 32);
-        *(v4i*)(stage + L::KC + row * L::KROW4 + col * 16) = kc[p];
+      const int c = t + p * NT;
+      if (NKC % NT == 0 || c < NKC) {
+        const int row = c / (D / 32), col = c % (D / 32);
+        *(v4i*)(stage + L::KC + kslot(row) * L::KROW4 + col * 16) = kc[p];
       }
     }
 #pragma unroll
     for (int p = 0; p < PV; ++p) {
-      int c = t + p * NT;
-      if (c < NVC) *(v4i*)(stage + L::VC + (c / 2) * L::VROW4 + (c % 2) * 16) = vc[p];
+      const int c = t + p * NT;
+      if (NVC % NT == 0 || c < NVC) *(v4i*)(stage + L::VC + (c / 2) * L::VROW4 + (c % 2) * 16) = vc[p];
     }
-    if (t < kBk) ((uint32_t*)(stage + L::KS))[t] = ksc;
+    if (t < kBk) ((uint32_t*)(stage + L::KS))[kslot(t)] = ksc;
     if (t < D) {
       uint8_t* vs = (uint8_t*)(stage + L::VS);
       vs[((0 * 32) + (t & 31)) * 4 + (t >> 5)] = (uint8_t)(vsc & 0xFF);
@@ -446,26 +477,37 @@ struct Mx4Stager {
   }
 };
 
-// fp16 tile of the promoted path: K row-major, V transposed into V^T.
+// fp16 tile of the promoted path: K row-major (rows in MFMA read order), V
+// transposed into V^T.  The transpose goes through registers: a thread takes
+// two consecutive keys x 8 channels and writes eight 4-byte (key pair) words,
+// so a wavefront's stores hit consecutive words of one V^T row.
 template <int D, int NT>
 struct F16Stager {
-  static constexpr int NC = kBk * D / 8;  // 16-byte chunks per tensor
-  static constexpr int P = (NC + NT - 1) / NT;
-  v8h kr[P], vr[P];
+  static constexpr int NK = kBk * D / 8;        // 16-byte chunks of K
+  static constexpr int NV = (kBk / 2) * (D / 8);  // (key pair, 8 channels) items of V
+  static constexpr int PK = (NK + NT - 1) / NT, PV = (NV + NT - 1) / NT;
+  v8h kr[PK], v0[PV], v1[PV];
 
   __device__ void load(const AttnArgs& a, size_t bhk, int j, int t) {
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
+    for (int p = 0; p < PK; ++p) {
       int c = t + p * NT;
       kr[p] = v8h{};
-      vr[p] = v8h{};
-      if (c < NC) {
+      if (c < NK) {
         int row = c / (D / 8), col = (c % (D / 8)) * 8, key = j * kBk + row;
-        if (key < a.S) {
-          size_t off = (bhk * a.S + key) * D + col;
-          kr[p] = *(const v8h*)(a.k16 + off);
-          vr[p] = *(const v8h*)(a.v16 + off);
-        }
+        if (key < a.S) kr[p] = *(const v8h*)(a.k16 + (bhk * a.S + key) * D + col);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PV; ++p) {
+      int c = t + p * NT;
+      v0[p] = v8h{};
+      v1[p] = v8h{};
+      if (c < NV) {
+        int kp = c % (kBk / 2), col = (c / (kBk / 2)) * 8, key = j * kBk + 2 * kp;
+        const _Float16* src = a.v16 + (bhk * a.S + key) * D + col;
+        if (key < a.S) v0[p] = *(const v8h*)src;
+        if (key + 1 < a.S) v1[p] = *(const v8h*)(src + D);
       }
     }
   }
@@ -475,13 +517,25 @@ struct F16Stager {
     _Float16* kh = (_Float16*)(stage + L::KH);
     _Float16* vt = (_Float16*)(stage + L::VT);
 #pragma unroll
-    for (int p = 0; p < P; ++p) {
+    for (int p = 0; p < PK; ++p) {
       int c = t + p * NT;
-      if (c < NC) {
+      if (c < NK) {
         int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        *(v8h*)(kh + row * L::KROWH + col) = kr[p];
+        *(v8h*)(kh + kslot(row) * L::KROWH + col) = kr[p];
+      }
+    }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) vt[(col + u) * L::VROWH + row] = vr[p][u];
+    for (int p = 0; p < PV; ++p) {
+      int c = t + p * NT;
+      if (c < NV) {
+        int kp = c % (kBk / 2), col = (c / (kBk / 2)) * 8;
+        const v4i a = __builtin_bit_cast(v4i, v0[p]), b = __builtin_bit_cast(v4i, v1[p]);
+        uint32_t* dst = (uint32_t*)(vt + col * L::VROWH + 2 * kp);
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {  // channels 2w, 2w+1: (key, key+1) half pairs
+          dst[(2 * w) * (L::VROWH / 2)] = __builtin_amdgcn_perm((uint32_t)b[w], (uint32_t)a[w], 0x05040100u);
+          dst[(2 * w + 1) * (L::VROWH / 2)] = __builtin_amdgcn_perm((uint32_t)b[w], (uint32_t)a[w], 0x07060302u);
+        }
       }
     }
   }
@@ -543,7 +597,7 @@ struct Nv4Stager {
 #pragma unroll
     for (int p = 0; p < PK; ++p) {
       int c = t + p * NT;
-      if (c < NKC) expand(kh + (c / (D / 32)) * L::KROWH + (c % (D / 32)) * 32, kc[p], ks[p]);
+      if (c < NKC) expand(kh + kslot(c / (D / 32)) * L::KROWH + (c % (D / 32)) * 32, kc[p], ks[p]);
     }
 #pragma unroll
     for (int p = 0; p < PV; ++p) {
@@ -555,6 +609,43 @@ struct Nv4Stager {
 
 // ---- the kernel ----------------------------------------------------------------------
 
+// Work item of workgroup `id`.  Workgroups are dispatched round-robin over
+// the 8 XCDs (id % 8), each with its own L2; items are mapped so that one XCD
+// streams the K/V of one key head (all its query blocks and the query heads
+// that share it), heaviest causal blocks first, which keeps that head's FP4
+// K/V resident in the XCD's L2:
+//  - B*Hkv a multiple of 8: XCD x takes key heads x, x+8, ...;
+//  - B*Hkv dividing 8: key head x % (B*Hkv), every (8/(B*Hkv))-th block of it;
+//  - otherwise: plain heaviest-first order.
+// The grid is a multiple of 8; workgroups past the last item return.
+constexpr int kXcds = 8;
+__device__ inline bool work_item(const AttnArgs& a, int id, int& i, int& bhq) {
+  const int G = a.Hq / a.Hkv, nbh = a.B * a.Hkv, per_head = G * a.nq;
+  const int N = a.B * a.Hq * a.nq;
+  int h, p;  // key head (b*Hkv + hk) and position in its heaviest-first list
+  if (nbh % kXcds == 0) {
+    const int x = id % kXcds, k = id / kXcds, heads = nbh / kXcds;
+    if (k >= heads * per_head) return false;
+    h = x + kXcds * (k / per_head);
+    p = k % per_head;
+  } else if (kXcds % nbh == 0) {
+    const int x = id % kXcds, k = id / kXcds, st = kXcds / nbh;
+    h = x % nbh;
+    p = k * st + x / nbh;
+    if (p >= per_head) return false;
+  } else {
+    if (id >= N) return false;
+    const int BHq = a.B * a.Hq;
+    i = a.causal ? a.nq - 1 - id / BHq : id / BHq;
+    bhq = id % BHq;
+    return true;
+  }
+  const int ii = p / G, g = p % G;  // query block rank (heaviest first), head in group
+  i = a.causal ? a.nq - 1 - ii : ii;
+  bhq = (h / a.Hkv) * a.Hq + (h % a.Hkv) * G + g;
+  return true;
+}
+
 template <int D, int NW, int FMT>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
   using L = Lds<D>;
@@ -563,14 +654,11 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int t = threadIdx.x, lane = t & 63, w = t >> 6, hi = lane >> 5;
   const int S = a.S;
-  const int BHq = a.B * a.Hq;
-  const int id = blockIdx.x;
-  // heaviest (longest causal prefix) query blocks first
-  const int i = a.causal ? a.nq - 1 - id / BHq : id / BHq;
-  const int bhq = id % BHq;
+  int i, bhq;
+  if (!work_item(a, blockIdx.x, i, bhq)) return;
   const int b = bhq / a.Hq, hq = bhq % a.Hq;
   const size_t bhk = (size_t)b * a.Hkv + hq / (a.Hq / a.Hkv);
-  const int q0 = i * BQ + w * 32;
+  const int q0 = __builtin_amdgcn_readfirstlane(i * BQ + w * 32);  // wave-uniform
   const int qrow = q0 + (lane & 31);
   const bool qvalid = qrow < S;
   const int nvalid = valid_kv_blocks(i, S, BQ, kBk, a.causal);
@@ -578,7 +666,15 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
   int ncnt = a.cnt[rowid];
   ncnt = ncnt < 0 ? 0 : (ncnt > a.kmax ? a.kmax : ncnt);
   int* prom = (int*)(smem + L::PROM);
-  for (int e = t; e < ncnt; e += NT) prom[e] = a.idx[rowid * a.kmax + e];
+  uint32_t* pbits = (uint32_t*)prom + a.kmax;  // bit j: key block j is promoted
+  const int nwords = (nvalid + 31) >> 5;
+  for (int e = t; e < nwords; e += NT) pbits[e] = 0;
+  __syncthreads();
+  for (int e = t; e < ncnt; e += NT) {
+    const int j = a.idx[rowid * a.kmax + e];
+    prom[e] = j;
+    if (j >= 0 && j < nvalid) atomicOr(&pbits[j >> 5], 1u << (j & 31));
+  }
   __syncthreads();
 
   RowState<D> st;
@@ -613,25 +709,58 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
       }
       qsc >>= 8 * hi;
       const float c = a.sm_log2;
-      Mx4Stager<D, NT> stg;
-      if (jc < nvalid) {
-        stg.load(a, bhk, jc, t);
+      // Three-stage LDS ring over every valid key block in order, one barrier
+      // per block; promoted blocks are staged but not computed (their FP16
+      // pass comes later), which keeps the load stream regular.  Iteration n
+      // issues the loads of block n+2 into registers, the QK MFMAs of block
+      // n+1 (K from ring slot n+1) before the softmax of block n, so the
+      // matrix core works while this wave's VALU does, the PV product of
+      // block n (V from slot n), and finally stores block n+2 into slot n+2,
+      // whose previous block (n-1) every wave finished before the last
+      // barrier.
+      using Stg = Mx4Stager<D, NT>;
+      const typename Stg::Base g = Stg::base(a, bhk);
+      Stg stg;
+      constexpr int R = L::STAGE4R;
+      const uint32_t* pbits = (const uint32_t*)(smem + L::PROM) + a.kmax;
+      auto active_of = [&](int j) {
+        return j < nvalid && !((pbits[j >> 5] >> (j & 31)) & 1u) && (!a.causal || j * kBk <= q0 + 31);
+      };
+      auto mask_of = [&](int j) {
+        const int key0 = j * kBk;
+        return (a.causal && key0 + kBk - 1 > q0) || key0 + kBk > S;
+      };
+      if (ncnt < nvalid) {
+        int jc = 0;
+        stg.load(g, 0, t);
         stg.store(smem, t);
-      }
-      __syncthreads();
-      int buf = 0;
-      while (jc < nvalid) {
-        const int jn = next_fp4(jc + 1);
-        if (jn < nvalid) stg.load(a, bhk, jn, t);
-        const int key0 = jc * kBk;
-        const bool active = !a.causal || key0 <= q0 + 31;
-        const bool need_mask = (a.causal && key0 + kBk - 1 > q0) || key0 + kBk > S;
-        if (active)
-          fp4_mx_tile<D>(st, smem + buf * L::STAGE, qB, qsc, c, key0, qrow, S, a.causal, need_mask, lane);
-        if (jn < nvalid) stg.store(smem + (buf ^ 1) * L::STAGE, t);
+        if (1 < nvalid) {
+          stg.load(g, 1, t);
+          stg.store(smem + R, t);
+        }
         __syncthreads();
-        buf ^= 1;
-        jc = jn;
+        v16f sA[2], sB[2];
+        bool actc = active_of(0);
+        if (actc) qk_mx<D>(sA, smem, qB, qsc, lane);
+        int b = 0;
+        // cur/nxt: score registers of blocks n, n+1
+        auto step = [&](v16f (&cur)[2], v16f (&nxt)[2]) -> bool {
+          const bool more2 = jc + 2 < nvalid;
+          if (more2) stg.load(g, jc + 2, t);
+          const int b1 = b == 2 ? 0 : b + 1, b2 = b1 == 2 ? 0 : b1 + 1;
+          const bool actn = active_of(jc + 1);
+          if (actn) qk_mx<D>(nxt, smem + b1 * R, qB, qsc, lane);
+          if (actc)
+            softmax_pv_mx<D>(st, cur, smem + b * R, c, jc * kBk, qrow, S, a.causal, mask_of(jc), lane);
+          if (more2) stg.store(smem + b2 * R, t);
+          __syncthreads();
+          ++jc;
+          actc = actn;
+          b = b1;
+          return jc < nvalid;
+        };
+        while (step(sA, sB) && step(sB, sA)) {
+        }
       }
     } else {
       v8h qh[D / 16];
@@ -732,7 +861,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
 template <int D, int NW, int FMT>
 static thrift_status launch_attn(const AttnArgs& a, hipStream_t stream) {
   using L = Lds<D>;
-  const size_t lds = (size_t)L::PROM + (size_t)a.kmax * 4;
+  const size_t lds = (size_t)L::PROM + (size_t)a.kmax * 4 + (size_t)((a.S + 64 * 32 - 1) / (64 * 32)) * 4;
   static bool configured = false;
   if (!configured) {
     if (hipFuncSetAttribute((const void*)attn_fwd_kernel<D, NW, FMT>,
@@ -740,7 +869,8 @@ static thrift_status launch_attn(const AttnArgs& a, hipStream_t stream) {
       return THRIFT_EHIP;
     configured = true;
   }
-  const int grid = a.B * a.Hq * a.nq;
+  const int items = a.B * a.Hq * a.nq;
+  const int grid = (items + kXcds - 1) / kXcds * kXcds;
   attn_fwd_kernel<D, NW, FMT><<<grid, NW * 64, lds, stream>>>(a);
   return launch_status();
 }
