@@ -37,6 +37,8 @@
 //    tile maximum), so this is the pages' online softmax up to fp32 rounding.
 //  * K/V tiles stream through double-buffered LDS, one barrier per tile; the
 //    next tile's global loads are in flight while the current one computes.
+#include <type_traits>
+
 #include "common.h"
 
 namespace thrift {
@@ -67,27 +69,47 @@ struct AttnArgs {
   float sm_log2;  // sm_scale * log2(e)
 };
 
+// ---- MX stage layout -------------------------------------------------------
+// A stage holds two 64-key blocks, filled by direct global->LDS loads (each
+// lane of a load writes 16 consecutive bytes, so the layout is dense and the
+// lanes' source addresses choose it).  K rows are in MFMA read order (row r =
+// mt*32 + m holds key krow(mt, m)), 16-byte chunks XOR-swizzled by the row so
+// that eight lanes reading eight rows hit eight different bank groups; V^T
+// rows likewise.  Scales: K one u32 (D/32 bytes) per row in read order; V a
+// [2][32] u32 table whose byte dt is the scale of (d = dt*32 + r, group kb).
+template <int D>
+struct MxStage {
+  static constexpr int CPR = D / 32;        // 16-byte chunks per K row
+  static constexpr int KCODE = kBk * D / 2;  // bytes of K codes per block
+  static constexpr int VCODE = D * 32;       // bytes of V^T codes per block
+  static constexpr int KSB = D / 32;         // K scale bytes per row
+  static constexpr int KC = 0;                          // [2][KCODE]
+  static constexpr int VC = KC + 2 * KCODE;             // [2][VCODE]
+  static constexpr int KS = VC + 2 * VCODE;             // [2][64][KSB]
+  static constexpr int VS = KS + 2 * kBk * KSB;         // [2][2][32] u32
+  static constexpr int SIZE = (VS + 2 * 256 + 255) / 256 * 256;
+  // Swizzled chunk of K row r / V^T row d.  A half-wave reads one chunk of
+  // 16 consecutive rows: with 64 four-byte banks, 16 rows x 16 bytes must
+  // land on 16 distinct 16-byte slots modulo 256 bytes (and any 8 of them
+  // on distinct slots modulo 128 bytes).
+  __device__ static int kswz(int r, int c) {
+    return CPR == 4 ? c ^ (((r >> 1) ^ (r >> 3)) & 3) : c ^ (((r >> 2) ^ (r >> 3)) & 1);
+  }
+  __device__ static int vswz(int d, int h) { return h ^ (((d >> 2) ^ (d >> 3)) & 1); }
+};
+
 // ---- LDS layout --------------------------------------------------------------
 
 template <int D>
 struct Lds {
-  // FP4 (MX) stage
-  static constexpr int KROW4 = D / 2 + 16;  // bytes per key row of codes (padded)
-  static constexpr int VROW4 = 32 + 16;     // bytes per V^T row of codes (64 keys)
-  static constexpr int KC = 0;
-  static constexpr int KS = KC + kBk * KROW4;  // u32 per key row: its D/32 scale bytes
-  static constexpr int VC = KS + kBk * 4;
-  static constexpr int VS = VC + D * VROW4;    // u32 [2][32]: byte dt = scale(dt*32+r, kb)
-  static constexpr int STAGE4 = VS + 2 * 32 * 4;
-  static constexpr int STAGE4R = (STAGE4 + 255) / 256 * 256;  // MX ring: three of these
   // fp16 stage (FP16 path, NVFP4 FP4 path)
   static constexpr int KROWH = D + 8;    // halves per key row
   static constexpr int VROWH = kBk + 8;  // halves per V^T row (16-byte aligned)
   static constexpr int KH = 0;
   static constexpr int VT = KH + kBk * KROWH * 2;
   static constexpr int STAGEH = VT + D * VROWH * 2;
-  static constexpr int STAGE = ((STAGE4 > STAGEH ? STAGE4 : STAGEH) + 255) / 256 * 256;
-  static constexpr int RING = (3 * STAGE4R > 2 * STAGE ? 3 * STAGE4R : 2 * STAGE);
+  static constexpr int STAGE = (STAGEH + 255) / 256 * 256;
+  static constexpr int RING = (3 * MxStage<D>::SIZE > 2 * STAGE ? 3 * MxStage<D>::SIZE : 2 * STAGE);
   static constexpr int PROM = RING;  // int[kmax] promoted list
 };
 
@@ -193,42 +215,64 @@ __device__ inline float max16(const v16f& v) {
   return fmaxf(fmaxf(fmaxf(a, b), c), fmaxf(fmaxf(d, e), v[15]));
 }
 
-// ---- MX FP4 tile ------------------------------------------------------------------
-
-// S^T = K Q^T for one MX tile: two 32-row tiles, D/64 contraction steps of
-// 64 channels, block-scaled by the E8M0 bytes of K and Q.
+// MFMA operands of one MX block read from LDS into registers ahead of use.
 template <int D>
-__device__ inline void qk_mx(v16f s[2], const char* stage, const v4i* qB, uint32_t qsc, int lane) {
-  using L = Lds<D>;
+struct MxKOps {
+  v4i a[2][D / 64];  // K codes of S^T tiles mt = 0, 1
+  uint32_t sc[2];    // their E8M0 scales (this lane's contraction half)
+};
+template <int D>
+struct MxVOps {
+  v4i a[D / 32];  // V^T codes, one 32-row tile per dt
+  uint32_t sc;    // byte dt: scale of V^T row dt*32 + r, key group hi
+};
+
+template <int D>
+__device__ inline void load_k_mx(MxKOps<D>& k, const char* stage, int t, int lane) {
+  using M = MxStage<D>;
   const int hi = lane >> 5, r32 = lane & 31;
-  const uint8_t* kc = (const uint8_t*)(stage + L::KC);
-  const uint32_t* ks = (const uint32_t*)(stage + L::KS);
-  uint32_t ksc[2];
-  v4i a[2][D / 64];
+  const uint8_t* kc = (const uint8_t*)(stage + M::KC + t * M::KCODE);
+  const uint8_t* ks = (const uint8_t*)(stage + M::KS + t * kBk * M::KSB);
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    const int row = mt * 32 + r32;       // holds key krow(mt, r32)
-    ksc[mt] = ks[row] >> (8 * hi);       // byte 2*kstep: this lane's 32-channel group
+    const int row = mt * 32 + r32;  // holds key krow(mt, r32)
+    k.sc[mt] = (D == 128 ? *(const uint32_t*)(ks + row * 4) : (uint32_t)(*(const uint16_t*)(ks + row * 2))) >> (8 * hi);
 #pragma unroll
-    for (int kk = 0; kk < D / 64; ++kk) a[mt][kk] = *(const v4i*)(kc + row * L::KROW4 + kk * 32 + hi * 16);
-  }
-  s[0] = mfma_fp4<0, 0>(a[0][0], qB[0], v16f{}, ksc[0], qsc);
-  s[1] = mfma_fp4<0, 0>(a[1][0], qB[0], v16f{}, ksc[1], qsc);
-  if constexpr (D == 128) {
-    s[0] = mfma_fp4<2, 2>(a[0][1], qB[1], s[0], ksc[0], qsc);
-    s[1] = mfma_fp4<2, 2>(a[1][1], qB[1], s[1], ksc[1], qsc);
+    for (int kk = 0; kk < D / 64; ++kk)
+      k.a[mt][kk] = *(const v4i*)(kc + row * (D / 2) + M::kswz(row, kk * 2 + hi) * 16);
   }
 }
 
-// Softmax, two-level MX quantisation of P and O^T += V^T P^T for one tile.
 template <int D>
-__device__ inline void softmax_pv_mx(RowState<D>& st, v16f s[2], const char* stage, float c,
-                                     int key0, int qrow, int S, int causal, bool need_mask,
-                                     int lane) {
-  using L = Lds<D>;
+__device__ inline void load_v_mx(MxVOps<D>& v, const char* stage, int t, int lane) {
+  using M = MxStage<D>;
   const int hi = lane >> 5, r32 = lane & 31;
-  const uint8_t* vc = (const uint8_t*)(stage + L::VC);
-  const uint32_t* vs = (const uint32_t*)(stage + L::VS);
+  const uint8_t* vc = (const uint8_t*)(stage + M::VC + t * M::VCODE);
+  v.sc = ((const uint32_t*)(stage + M::VS + t * 256))[hi * 32 + r32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) {
+    const int d = dt * 32 + r32;
+    v.a[dt] = *(const v4i*)(vc + d * 32 + M::vswz(d, hi) * 16);
+  }
+}
+
+// S^T = K Q^T: two 32-row tiles, D/64 contraction steps of 64 channels,
+// block-scaled by the E8M0 bytes of K and Q.
+template <int D>
+__device__ inline void qk_mx(v16f s[2], const MxKOps<D>& k, const v4i* qB, uint32_t qsc) {
+  s[0] = mfma_fp4<0, 0>(k.a[0][0], qB[0], v16f{}, k.sc[0], qsc);
+  s[1] = mfma_fp4<0, 0>(k.a[1][0], qB[0], v16f{}, k.sc[1], qsc);
+  if constexpr (D == 128) {
+    s[0] = mfma_fp4<2, 2>(k.a[0][1], qB[1], s[0], k.sc[0], qsc);
+    s[1] = mfma_fp4<2, 2>(k.a[1][1], qB[1], s[1], k.sc[1], qsc);
+  }
+}
+
+// Softmax, two-level MX quantisation of P and O^T += V^T P^T for one block.
+template <int D>
+__device__ inline void softmax_pv_mx(RowState<D>& st, v16f s[2], const MxVOps<D>& v, float c, int key0,
+                                     int qrow, int S, int causal, bool need_mask, int lane) {
+  const int hi = lane >> 5;
   if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
 
   // this lane's 32 keys are one P group: its maximum sets the E8M0 exponent
@@ -258,24 +302,22 @@ __device__ inline void softmax_pv_mx(RowState<D>& st, v16f s[2], const char* sta
   v4i P;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
-    const v16f& v = s[r >> 1];
+    const v16f& x = s[r >> 1];
     const int o = (r & 1) * 8;
-    uint32_t x = 0;
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[o + 0], v[o + 1], sf, 0);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[o + 2], v[o + 3], sf, 1);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[o + 4], v[o + 5], sf, 2);
-    x = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(x, v[o + 6], v[o + 7], sf, 3);
-    P[r] = (int)x;
+    uint32_t y = 0;
+    y = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(y, x[o + 0], x[o + 1], sf, 0);
+    y = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(y, x[o + 2], x[o + 3], sf, 1);
+    y = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(y, x[o + 4], x[o + 5], sf, 2);
+    y = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(y, x[o + 6], x[o + 7], sf, 3);
+    P[r] = (int)y;
   }
 
   // O^T += V^T P^T
-  const uint32_t vsw = vs[hi * 32 + r32];
-  const uint8_t* vrow = vc + r32 * L::VROW4 + hi * 16;
-  st.acc[0] = mfma_fp4<0, 0>(*(const v4i*)(vrow), P, st.acc[0], vsw, psc);
-  st.acc[1] = mfma_fp4<1, 0>(*(const v4i*)(vrow + 32 * L::VROW4), P, st.acc[1], vsw, psc);
+  st.acc[0] = mfma_fp4<0, 0>(v.a[0], P, st.acc[0], v.sc, psc);
+  st.acc[1] = mfma_fp4<1, 0>(v.a[1], P, st.acc[1], v.sc, psc);
   if constexpr (D == 128) {
-    st.acc[2] = mfma_fp4<2, 0>(*(const v4i*)(vrow + 64 * L::VROW4), P, st.acc[2], vsw, psc);
-    st.acc[3] = mfma_fp4<3, 0>(*(const v4i*)(vrow + 96 * L::VROW4), P, st.acc[3], vsw, psc);
+    st.acc[2] = mfma_fp4<2, 0>(v.a[2], P, st.acc[2], v.sc, psc);
+    st.acc[3] = mfma_fp4<3, 0>(v.a[3], P, st.acc[3], v.sc, psc);
   }
 }
 
@@ -406,73 +448,102 @@ namespace thrift {
 
 // ---- staging: global -> registers (next tile) -> LDS --------------------------
 
-// MX FP4 tile: K codes [64 keys][D/2 B], K scales (one u32 per key row),
-// V^T codes [D][32 B], V^T scales regrouped so that a lane reads the scale
-// bytes of its four d-tiles with one 32-bit load.  Loads are unconditional:
-// key rows past S (last tile only) read row S-1 instead, and their scores
-// are masked anyway.
-template <int D, int NT>
-struct Mx4Stager {
-  static constexpr int NKC = kBk * D / 32;  // 16-byte chunks of K codes
-  static constexpr int NVC = D * 2;         // 16-byte chunks of V^T codes
-  static constexpr int PK = (NKC + NT - 1) / NT, PV = (NVC + NT - 1) / NT;
-  v4i kc[PK], vc[PV];
-  uint32_t ksc, vsc;
+// MX stage fill.  K codes, V^T codes and (D = 128) K scales go global -> LDS
+// directly with buffer loads (buffer_load_dwordx4 / _dword ... lds: no
+// registers, no LDS store instructions); V scales (two bytes per V^T row and
+// block) and the D = 64 K scales go through registers.  Every per-lane source
+// offset is fixed for the whole key sweep; the block moves only the base of
+// the buffer resource (scalar work).  The resource's record count ends at the
+// tensor's end, so key rows past S (last block) read as out of range and
+// never touch memory; their scores are masked.
+template <int D, int NW>
+struct MxDma {
+  using M = MxStage<D>;
+  static constexpr int KINST = M::KCODE / 1024;  // wave loads (64 lanes x 16 B) per block of K codes
+  static constexpr int VINST = M::VCODE / 1024;  // ... of V^T codes
+  static constexpr int NK = 2 * KINST / NW;      // per wave and stage
+  static constexpr int NV = 2 * VINST / NW;
+  static_assert(NK * NW == 2 * KINST && NV * NW == 2 * VINST, "wave loads must split evenly");
+  static constexpr int NT = NW * 64;
+  static constexpr int NVS = 2 * D;  // V scale entries (one per V^T row and block) per stage
+  static constexpr int NVR = (NVS + NT - 1) / NT;
+  static constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
-  struct Base {  // per-workgroup bases of the key head's FP4 tensors
-    const uint8_t *kc, *ks, *vc, *vs;
-    int S, Sp;
-  };
+  __amdgpu_buffer_rsrc_t kc, ks, vc, vs;  // this head's tensors, record counts ending at their ends
+  int nv, w;
+  uint32_t koff[NK], voff[NV], ksoff, vsoff[NVR];
+  uint32_t vreg[NVR], kreg;
 
-  __device__ static Base base(const AttnArgs& a, size_t bhk) {
-    return Base{a.k4c + bhk * a.S * (D / 2), a.k4s + bhk * a.S * (D / 32),
-                a.v4c + bhk * D * (a.Sp / 2), a.v4s + bhk * D * (a.Sp / 32), a.S, a.Sp};
+  __device__ static __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kRsrcWord3);
+  }
+  __device__ static __attribute__((address_space(3))) void* lds(char* p) {
+    return (__attribute__((address_space(3))) void*)p;
   }
 
-  // Every thread issues the same number of loads on every tile (threads past
-  // a table re-read an in-range entry and drop it), so the compiler can wait
-  // for exactly the older tile's loads and leave the newer ones in flight.
-  __device__ void load(const Base& g, int j, int t) {
+  __device__ MxDma(const AttnArgs& a, size_t bhk, int nv_, int w_, int lane, int t)
+      : kc(rsrc(a.k4c + bhk * a.S * (D / 2), a.S * (D / 2))),
+        ks(rsrc(a.k4s + bhk * a.S * (D / 32), a.S * (D / 32))),
+        vc(rsrc(a.v4c + bhk * D * (a.Sp / 2), D * (a.Sp / 2))),
+        vs(rsrc(a.v4s + bhk * D * (a.Sp / 32), D * (a.Sp / 32))),
+        nv(nv_), w(w_) {
 #pragma unroll
-    for (int p = 0; p < PK; ++p) {
-      const int c = (t + p * NT) % NKC;
-      const int row = c / (D / 32), col = c % (D / 32);
-      const uint32_t key = (uint32_t)min(j * kBk + row, g.S - 1);
-      kc[p] = *(const v4i*)(g.kc + (key * (D / 2) + col * 16));
+    for (int k = 0; k < NK; ++k) {  // LDS chunk ci of the block -> row r, swizzled chunk
+      const int ci = ((w * NK + k) % KINST) * 64 + lane, r = ci / M::CPR;
+      const int c = M::kswz(r, ci % M::CPR);  // the swizzle is an involution per row
+      koff[k] = krow(r >> 5, r & 31) * (D / 2) + c * 16;
     }
 #pragma unroll
-    for (int p = 0; p < PV; ++p) {
-      const int c = (t + p * NT) % NVC;
-      vc[p] = *(const v4i*)(g.vc + ((uint32_t)(c / 2) * (uint32_t)(g.Sp / 2) + j * 32 + (c % 2) * 16));
+    for (int k = 0; k < NV; ++k) {
+      const int ci = ((w * NV + k) % VINST) * 64 + lane, d = ci / 2;
+      voff[k] = d * (a.Sp / 2) + M::vswz(d, ci % 2) * 16;
     }
-    {
-      const uint32_t key = (uint32_t)min(j * kBk + t % kBk, g.S - 1);
-      const uint8_t* p = g.ks + key * (D / 32);
-      ksc = D == 128 ? *(const uint32_t*)p : (uint32_t)(*(const uint16_t*)p);
+    ksoff = krow(lane >> 5, lane & 31) * (D / 32);
+#pragma unroll
+    for (int p = 0; p < NVR; ++p) {
+      const int e = t + p * NT;
+      vsoff[p] = (e % D) * (a.Sp / 32) + ((e / D) & 1) * 2;
     }
-    vsc = *(const uint16_t*)(g.vs + ((uint32_t)(t % D) * (uint32_t)(g.Sp / 32) + j * 2));
   }
 
-  __device__ void store(char* stage, int t) const {
-    using L = Lds<D>;
+  // Issue the loads of blocks j0 and j0+1 into `stage` (a block past the last
+  // valid one reloads the last one; it is never computed).  The block offset
+  // goes into the per-lane offset, which the resource's record count checks.
+  __device__ void issue(char* stage, int j0) {
 #pragma unroll
-    for (int p = 0; p < PK; ++p) {
-      const int c = t + p * NT;
-      if (NKC % NT == 0 || c < NKC) {
-        const int row = c / (D / 32), col = c % (D / 32);
-        *(v4i*)(stage + L::KC + kslot(row) * L::KROW4 + col * 16) = kc[p];
-      }
+    for (int k = 0; k < NK; ++k) {
+      const int g = w * NK + k, jj = min(j0 + g / KINST, nv - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kc, lds(stage + M::KC + g * 1024), 16, koff[k] + jj * M::KCODE,
+                                               0, 0, 0);
     }
 #pragma unroll
-    for (int p = 0; p < PV; ++p) {
-      const int c = t + p * NT;
-      if (NVC % NT == 0 || c < NVC) *(v4i*)(stage + L::VC + (c / 2) * L::VROW4 + (c % 2) * 16) = vc[p];
+    for (int k = 0; k < NV; ++k) {
+      const int g = w * NV + k, jj = min(j0 + g / VINST, nv - 1);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vc, lds(stage + M::VC + g * 1024), 16, voff[k] + jj * 32, 0, 0, 0);
     }
-    if (t < kBk) ((uint32_t*)(stage + L::KS))[kslot(t)] = ksc;
-    if (t < D) {
-      uint8_t* vs = (uint8_t*)(stage + L::VS);
-      vs[((0 * 32) + (t & 31)) * 4 + (t >> 5)] = (uint8_t)(vsc & 0xFF);
-      vs[((1 * 32) + (t & 31)) * 4 + (t >> 5)] = (uint8_t)(vsc >> 8);
+    if (w < 2) {  // K scales of block j0 + w, rows in read order
+      const uint32_t o = ksoff + min(j0 + w, nv - 1) * (kBk * (D / 32));
+      if constexpr (D == 128)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ks, lds(stage + M::KS + w * kBk * 4), 4, o, 0, 0, 0);
+      else
+        kreg = __builtin_amdgcn_raw_buffer_load_b16(ks, o, 0, 0);
+    }
+#pragma unroll
+    for (int p = 0; p < NVR; ++p) vreg[p] = __builtin_amdgcn_raw_buffer_load_b16(vs, vsoff[p] + j0 * 2, 0, 0);
+  }
+
+  // Store what issue() loaded into registers (after the compute, before the barrier).
+  __device__ void finish(char* stage, int t) const {
+    if constexpr (D == 64)
+      if (w < 2) ((uint16_t*)(stage + M::KS + w * kBk * 2))[t & 63] = (uint16_t)kreg;
+#pragma unroll
+    for (int p = 0; p < NVR; ++p) {
+      const int e = t + p * NT;
+      if (NVS % NT != 0 && e >= NVS) continue;
+      const int tb = (e / D) & 1, d = e % D;
+      uint8_t* vsb = (uint8_t*)(stage + M::VS + tb * 256);
+      vsb[(d & 31) * 4 + (d >> 5)] = (uint8_t)(vreg[p] & 0xFF);
+      vsb[(32 + (d & 31)) * 4 + (d >> 5)] = (uint8_t)(vreg[p] >> 8);
     }
   }
 };
@@ -652,7 +723,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
   constexpr int NT = NW * 64;
   constexpr int BQ = NW * 32;
   extern __shared__ __attribute__((aligned(16))) char smem[];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, hi = lane >> 5;
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), hi = lane >> 5;
   const int S = a.S;
   int i, bhq;
   if (!work_item(a, blockIdx.x, i, bhq)) return;
@@ -709,20 +780,17 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
       }
       qsc >>= 8 * hi;
       const float c = a.sm_log2;
-      // Three-stage LDS ring over every valid key block in order, one barrier
-      // per block; promoted blocks are staged but not computed (their FP16
-      // pass comes later), which keeps the load stream regular.  Iteration n
-      // issues the loads of block n+2 into registers, the QK MFMAs of block
-      // n+1 (K from ring slot n+1) before the softmax of block n, so the
-      // matrix core works while this wave's VALU does, the PV product of
-      // block n (V from slot n), and finally stores block n+2 into slot n+2,
-      // whose previous block (n-1) every wave finished before the last
-      // barrier.
-      using Stg = Mx4Stager<D, NT>;
-      const typename Stg::Base g = Stg::base(a, bhk);
-      Stg stg;
-      constexpr int R = L::STAGE4R;
-      const uint32_t* pbits = (const uint32_t*)(smem + L::PROM) + a.kmax;
+      // Three-stage LDS ring of two-block stages over every valid key block in
+      // order, one barrier per stage; promoted blocks are loaded but not
+      // computed (their FP16 pass comes later), which keeps the load stream
+      // regular.  Iteration s issues the direct loads of stage s+2 into ring
+      // slot s+2 (whose previous stage, s-1, every wave finished before the
+      // last barrier) and computes blocks 2s and 2s+1; each block's QK MFMAs
+      // are issued before the previous block's softmax, so the matrix core
+      // works while this wave's VALU does.
+      using Dma = MxDma<D, NW>;
+      using M = MxStage<D>;
+      Dma dma(a, bhk, nvalid, w, lane, t);
       auto active_of = [&](int j) {
         return j < nvalid && !((pbits[j >> 5] >> (j & 31)) & 1u) && (!a.causal || j * kBk <= q0 + 31);
       };
@@ -730,36 +798,63 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
         const int key0 = j * kBk;
         return (a.causal && key0 + kBk - 1 > q0) || key0 + kBk > S;
       };
+      auto slot = [&](int k) { return smem + (k % 3) * M::SIZE; };
       if (ncnt < nvalid) {
-        int jc = 0;
-        stg.load(g, 0, t);
-        stg.store(smem, t);
-        if (1 < nvalid) {
-          stg.load(g, 1, t);
-          stg.store(smem + R, t);
+        const int nst = (nvalid + 1) / 2;  // stages
+        dma.issue(slot(0), 0);
+        dma.finish(slot(0), t);
+        if (nst > 1) {
+          dma.issue(slot(1), 2);
+          dma.finish(slot(1), t);
         }
         __syncthreads();
         v16f sA[2], sB[2];
-        bool actc = active_of(0);
-        if (actc) qk_mx<D>(sA, smem, qB, qsc, lane);
-        int b = 0;
-        // cur/nxt: score registers of blocks n, n+1
-        auto step = [&](v16f (&cur)[2], v16f (&nxt)[2]) -> bool {
-          const bool more2 = jc + 2 < nvalid;
-          if (more2) stg.load(g, jc + 2, t);
-          const int b1 = b == 2 ? 0 : b + 1, b2 = b1 == 2 ? 0 : b1 + 1;
-          const bool actn = active_of(jc + 1);
-          if (actn) qk_mx<D>(nxt, smem + b1 * R, qB, qsc, lane);
-          if (actc)
-            softmax_pv_mx<D>(st, cur, smem + b * R, c, jc * kBk, qrow, S, a.causal, mask_of(jc), lane);
-          if (more2) stg.store(smem + b2 * R, t);
+        MxKOps<D> kop;
+        MxVOps<D> vop;
+        bool act0 = active_of(0);
+        if (act0) {
+          load_k_mx<D>(kop, slot(0), 0, lane);
+          qk_mx<D>(sA, kop, qB, qsc);
+        }
+        int sg = 0;
+        // one stage; the ring slot is a compile-time constant so that every
+        // LDS address is a per-lane base plus an immediate offset
+        auto stage_step = [&](auto slot_c) {
+          constexpr int SL = decltype(slot_c)::value;
+          char* const cur = smem + SL * M::SIZE;
+          char* const nxt = smem + ((SL + 1) % 3) * M::SIZE;
+          char* const fut = smem + ((SL + 2) % 3) * M::SIZE;
+          const int j0 = 2 * sg;
+          const bool more = sg + 2 < nst;
+          if (more) dma.issue(fut, j0 + 4);
+          // block j0 (scores in sA), then j0+1 (scores in sB)
+          const bool act1 = active_of(j0 + 1);
+          if (act1) {
+            load_k_mx<D>(kop, cur, 1, lane);
+            qk_mx<D>(sB, kop, qB, qsc);
+          }
+          if (act0) {
+            load_v_mx<D>(vop, cur, 0, lane);
+            softmax_pv_mx<D>(st, sA, vop, c, j0 * kBk, qrow, S, a.causal, mask_of(j0), lane);
+          }
+          const bool act2 = active_of(j0 + 2);
+          if (act2) {
+            load_k_mx<D>(kop, nxt, 0, lane);
+            qk_mx<D>(sA, kop, qB, qsc);
+          }
+          if (act1) {
+            load_v_mx<D>(vop, cur, 1, lane);
+            softmax_pv_mx<D>(st, sB, vop, c, (j0 + 1) * kBk, qrow, S, a.causal, mask_of(j0 + 1), lane);
+          }
+          if (more) dma.finish(fut, t);
           __syncthreads();
-          ++jc;
-          actc = actn;
-          b = b1;
-          return jc < nvalid;
+          act0 = act2;
+          return ++sg < nst;
         };
-        while (step(sA, sB) && step(sB, sA)) {
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        while (stage_step(I0{}) && stage_step(I1{}) && stage_step(I2{})) {
         }
       }
     } else {
