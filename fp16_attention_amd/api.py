@@ -16,7 +16,7 @@ from . import _lib
 from ._lib import THRIFT_GROUP_D, THRIFT_GROUP_S, THRIFT_MXFP4, THRIFT_NVFP4, ThriftError
 
 __all__ = ["thrift_select_kmax", "thrift_select_blocks", "thrift_quantize_fp4",
-           "thrift_attention_fwd", "FP4Tensor", "thrift_forward", "THRIFT_NVFP4", "THRIFT_MXFP4",
+           "thrift_attention_fwd", "FP4Tensor", "fp4_transposed", "thrift_forward", "THRIFT_NVFP4", "THRIFT_MXFP4",
            "THRIFT_GROUP_D", "THRIFT_GROUP_S", "ThriftError"]
 
 
@@ -82,15 +82,28 @@ def thrift_quantize_fp4(x16, axis=THRIFT_GROUP_D, fmt=THRIFT_MXFP4) -> FP4Tensor
         codes = torch.empty((B, H, S, D // 2), dtype=torch.uint8, device=dev)
         scales = torch.empty((B, H, S, D // g), dtype=torch.uint8, device=dev)
     else:
-        Sp = -(-S // 64) * 64
-        codes = torch.empty((B, H, D, Sp // 2), dtype=torch.uint8, device=dev)
-        scales = torch.empty((B, H, D, Sp // g), dtype=torch.uint8, device=dev)
+        Sp = -(-S // 64) * 64  # key-block-major V^T: [B, H, Sp/64, D, ...]
+        codes = torch.empty((B, H, Sp // 64, D, 32), dtype=torch.uint8, device=dev)
+        scales = torch.empty((B, H, Sp // 64, D, 64 // g), dtype=torch.uint8, device=dev)
     ts = torch.empty((B, H), dtype=torch.float32, device=dev) if fmt == THRIFT_NVFP4 else None
     wsb = _lib.load().thrift_quantize_workspace_bytes(B, H, S, D, fmt)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
     _call("thrift_quantize_fp4", _ptr(x16), B, H, S, D, axis, fmt, _ptr(codes), _ptr(scales),
           _ptr(ts), _ptr(ws), wsb, _stream())
     return FP4Tensor(codes, scales, ts, fmt, axis)
+
+
+def fp4_transposed(t: FP4Tensor):
+    """(codes, scales) of a THRIFT_GROUP_S tensor as plain transposed arrays
+    [B,H,D,Sp/2] and [B,H,D,Sp/g] (copies; the stored order is key-block-major).
+    THRIFT_GROUP_D tensors are returned as stored."""
+    if t.axis != THRIFT_GROUP_S:
+        return t.codes, t.scales
+    B, H, nb, D, cb = t.codes.shape
+    sb = t.scales.shape[-1]
+    codes = t.codes.permute(0, 1, 3, 2, 4).reshape(B, H, D, nb * cb)
+    scales = t.scales.permute(0, 1, 3, 2, 4).reshape(B, H, D, nb * sb)
+    return codes, scales
 
 
 def thrift_attention_fwd(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt,

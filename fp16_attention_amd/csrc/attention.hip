@@ -496,13 +496,13 @@ struct MxDma {
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int ci = ((w * NV + k) % VINST) * 64 + lane, d = ci / 2;
-      voff[k] = d * (a.Sp / 2) + M::vswz(d, ci % 2) * 16;
+      voff[k] = d * 32 + M::vswz(d, ci % 2) * 16;  // key-block-major V^T
     }
     ksoff = krow(lane >> 5, lane & 31) * (D / 32);
 #pragma unroll
     for (int p = 0; p < NVR; ++p) {
       const int e = t + p * NT;
-      vsoff[p] = (e % D) * (a.Sp / 32) + ((e / D) & 1) * 2;
+      vsoff[p] = (e % D) * 2 + ((e / D) & 1) * (2 * D);
     }
   }
 
@@ -519,7 +519,8 @@ struct MxDma {
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int g = w * NV + k, jj = min(j0 + g / VINST, nv - 1);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vc, lds(stage + M::VC + g * 1024), 16, voff[k] + jj * 32, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vc, lds(stage + M::VC + g * 1024), 16, voff[k] + jj * M::VCODE,
+                                               0, 0, 0);
     }
     if (w < 2) {  // K scales of block j0 + w, rows in read order
       const uint32_t o = ksoff + min(j0 + w, nv - 1) * (kBk * (D / 32));
@@ -529,7 +530,7 @@ struct MxDma {
         kreg = __builtin_amdgcn_raw_buffer_load_b16(ks, o, 0, 0);
     }
 #pragma unroll
-    for (int p = 0; p < NVR; ++p) vreg[p] = __builtin_amdgcn_raw_buffer_load_b16(vs, vsoff[p] + j0 * 2, 0, 0);
+    for (int p = 0; p < NVR; ++p) vreg[p] = __builtin_amdgcn_raw_buffer_load_b16(vs, vsoff[p] + j0 * (2 * D), 0, 0);
   }
 
   // Store what issue() loaded into registers (after the compute, before the barrier).
@@ -643,8 +644,9 @@ struct Nv4Stager {
       vs[p] = 0;
       if (c < NVC) {
         int d = c / 2, h = c % 2;
-        vc[p] = *(const v4i*)(a.v4c + (bhk * D + d) * (a.Sp / 2) + j * 32 + h * 16);
-        vs[p] = *(const uint16_t*)(a.v4s + (bhk * D + d) * (a.Sp / 16) + j * 4 + h * 2);
+        const size_t blk = bhk * (a.Sp / 64) + j;  // key-block-major V^T
+        vc[p] = *(const v4i*)(a.v4c + (blk * D + d) * 32 + h * 16);
+        vs[p] = *(const uint16_t*)(a.v4s + (blk * D + d) * 4 + h * 2);
       }
     }
   }

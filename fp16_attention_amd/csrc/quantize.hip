@@ -220,16 +220,18 @@ __global__ __launch_bounds__(kQThreads) void quant_s_kernel(const _Float16* __re
     float v[g];
 #pragma unroll
     for (int u = 0; u < g; ++u) v[u] = (float)tile[gq * g + u][d];
-    const size_t crow = ((size_t)bh * D + d) * (Sp / 2);
-    const size_t srow = ((size_t)bh * D + d) * (Sp / g);
+    // key-block-major: block jb = tok0 / 64 holds [D][32 B] codes, [D][64/g] scales
+    const size_t blk = (size_t)bh * (Sp / 64) + tok0 / 64;
+    const size_t crow = (blk * D + d) * 32 + (tok0 % 64) / 2;
+    const size_t srow = (blk * D + d) * (64 / g) + (tok0 % 64) / g;
     if (FMT == THRIFT_NVFP4) {
       uint32_t w[2];
-      scales[srow + tok0 / g] = (uint8_t)encode_nvfp4_16(v, sg, w);
-      *reinterpret_cast<uint2*>(codes + crow + tok0 / 2) = make_uint2(w[0], w[1]);
+      scales[srow] = (uint8_t)encode_nvfp4_16(v, sg, w);
+      *reinterpret_cast<uint2*>(codes + crow) = make_uint2(w[0], w[1]);
     } else {
       uint32_t w[4];
-      scales[srow + tok0 / g] = (uint8_t)encode_mx_32(v, w);
-      *reinterpret_cast<uint4*>(codes + crow + tok0 / 2) = make_uint4(w[0], w[1], w[2], w[3]);
+      scales[srow] = (uint8_t)encode_mx_32(v, w);
+      *reinterpret_cast<uint4*>(codes + crow) = make_uint4(w[0], w[1], w[2], w[3]);
     }
   }
 }

@@ -69,8 +69,11 @@ typedef enum { THRIFT_NVFP4 = 0, THRIFT_MXFP4 = 1 } thrift_format;
  *   THRIFT_GROUP_D (Q, K): groups run along dim; codes [B,H,S,D/2] u8,
  *     scales [B,H,S,D/g] u8 (g = 16 NVFP4, 32 MXFP4).
  *   THRIFT_GROUP_S (V): groups run along the sequence and the tensor is
- *     stored transposed: codes [B,H,D,Sp/2] u8, scales [B,H,D,Sp/g] u8, with
- *     Sp = S rounded up to a multiple of 64 and the padding tokens zero. */
+ *     stored transposed in 64-token blocks, so that one key block of V^T is
+ *     contiguous: codes [B,H,Sp/64,D,32] u8 (byte i of row d of block jb
+ *     holds tokens jb*64 + 2i, +2i+1, low nibble first), scales
+ *     [B,H,Sp/64,D,64/g] u8, with Sp = S rounded up to a multiple of 64 and
+ *     the padding tokens zero. */
 typedef enum { THRIFT_GROUP_D = 0, THRIFT_GROUP_S = 1 } thrift_group_axis;
 
 /* ---------------------------------------------------------------------- */

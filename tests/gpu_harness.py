@@ -37,8 +37,11 @@ def run_gpu(d, w, fmt, topk_count, topk_bp, no_fp16=False):
 
 
 def same_fp4(g, r):
-    assert np.array_equal(g.codes.cpu().numpy(), r.codes), "FP4 codes differ"
-    assert np.array_equal(g.scales.cpu().numpy(), r.scales), "FP4 block scales differ"
+    from fp16_attention_amd import api
+
+    codes, scales = api.fp4_transposed(g)  # the oracle keeps V^T in plain transposed order
+    assert np.array_equal(codes.cpu().numpy(), r.codes), "FP4 codes differ"
+    assert np.array_equal(scales.cpu().numpy(), r.scales), "FP4 block scales differ"
     if r.tensor_scale is not None:
         assert np.array_equal(g.tensor_scale.cpu().numpy(), r.tensor_scale), "slice scales differ"
 
