@@ -18,6 +18,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_kernel_long_mx_traffic.txt")
+KERNEL_SRC = os.path.join(ROOT, "fp16_attention_amd", "csrc", "attention.hip")
+
 P_FP4 = 10.1e15   # MI355X dense MXFP4 MFMA, FLOP/s
 P_FP16 = 2.5e15   # MI355X dense FP16 MFMA, FLOP/s
 HBM = 8.0e12      # bytes/s
@@ -56,11 +59,46 @@ def promoted_pairs(idx, cnt, S, bq, bk, causal):
     return total
 
 
+def measured_traffic(workload, fmt_name):
+    """HBM bytes per attention launch from the committed profiler counters
+    (FETCH_SIZE + WRITE_SIZE, each scaled by its reading on a copy kernel of
+    known size), or None when they were taken on another workload or on an
+    attention kernel source other than the one built now."""
+    import hashlib
+
+    if (workload, fmt_name) != ("long", "mx") or not os.path.exists(TRAFFIC_FILE):
+        return None
+    rec = {}
+    with open(TRAFFIC_FILE) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith((" ", "#", "|")):
+                k, v = ln.split(":", 1)
+                rec[k.strip()] = v.strip()
+    with open(KERNEL_SRC, "rb") as f:
+        h = hashlib.sha256(f.read()).hexdigest()
+    if rec.get("kernel_source_sha256") != h:
+        return None
+    return int(rec["traffic_bytes_per_launch"])
+
+
+def algorithmic_bytes(w, p16_tiles_q, fmt):
+    """Bytes one attention launch must move at least: FP4 Q/K/V (codes +
+    scales) once, the FP16 Q rows of query blocks with promoted tiles and the
+    FP16 K/V of promoted key blocks once each, and the fp16 output."""
+    g = 16 if fmt == 0 else 32
+    fp4_row = w.D // 2 + w.D // g
+    b = w.B * (w.Hq + 2 * w.Hkv) * w.S * fp4_row
+    b += p16_tiles_q * w.bq * w.D * 2
+    b += w.B * w.Hkv * w.S * w.D * 2 * 2  # every key block may be promoted by some query block
+    b += w.B * w.Hq * w.S * w.D * 2        # output
+    return b
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="long")
     ap.add_argument("--fmt", default="mx", choices=["mx", "nvfp4"])
     ap.add_argument("--topk-bp", type=int, default=None)
@@ -71,8 +109,9 @@ def main():
                          "kernel of known traffic, to calibrate profiler byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this path runs on one GPU; multi-GPU runs are not part of this build "
-              "(each (batch, head) is independent, see the sharding notes)", file=sys.stderr)
+        print("bench.py: the path is measured on one GPU only; --gpus above 1 is not supported "
+              "(the path shards by independent (batch, head) slices, nothing to measure across GPUs)",
+              file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -169,7 +208,8 @@ def main():
             "peak": round(peak_mixed / 1e12, 2),
             "unit": "TFLOP/s",
             "frac": round(achieved / peak_mixed, 4),
-            "traffic": None,
+            "traffic": measured_traffic(w.name, args.fmt),
+            "traffic_algorithmic": algorithmic_bytes(w, int((cnt_h > 0).sum()), fmt),
             "kernel": "attn_fwd_kernel",
             "peak_note": "F_alg / (F_fp4 / 10.1 PF + F_fp16 / 2.5 PF) for this launch's FP16 share",
         },
