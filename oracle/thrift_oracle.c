@@ -423,14 +423,19 @@ void tho_dequantize(const uint8_t* codes, const uint8_t* scales, const float* te
 /* ---- decisions a finite-precision evaluation may take either way ----
  * The probabilities that feed a rounding decision (the fp16 rounding of P on
  * the FP16 path, the E2M1 codes and block scales of P on the FP4 path) come
- * from exponentials of scores.  An implementation that evaluates them in
- * fp32 carries a relative error of a few 2^-24 |t| (t: score in log2 units)
- * plus that of its exp2; a decision whose input lies closer than that to its
- * rounding boundary may legitimately go either way, so the method's result
- * is not unique there.  tho_eval_eps is that error, taken four times over;
- * the uncertainty outputs below add up what flipping such decisions can
- * change in O. */
-static double tho_eval_eps(double t) { return THO_LN2 * ldexp(fabs(t) + 16.0, -20); }
+ * from exponentials of scores.  An implementation that accumulates a score's
+ * D products in fp32 carries an error of a few 2^-24 times the sum of the
+ * products' magnitudes, A (in the score's log2 units; A >= |t|, and A >> |t|
+ * where the products cancel), plus that of its exp2; a decision whose input
+ * lies closer than that to its rounding boundary may legitimately go either
+ * way, so the method's result is not unique there.  tho_eval_eps is that
+ * error, taken sixteen times over; the uncertainty outputs below add up what
+ * flipping such decisions can change in O, plus what the same error changes
+ * continuously: the unquantised row sum, and (NVFP4) each tile's level-1
+ * factor 2^mt.  Where one key dominates a row with a large score, the row
+ * sum's part is |O| ln2 times the score's error, which no fp32 evaluation
+ * avoids. */
+static double tho_eval_eps(double A) { return THO_LN2 * ldexp(A + 16.0, -20); }
 
 /* Change of the dequantised E2M1 value (in units of s) if y/s sits within
  * relative eps of a rounding midpoint and the other neighbour is taken. */
@@ -459,8 +464,8 @@ static void tho_quantize_group_values(const double* v, int g0, int g1, double s2
   for (int c = g0; c < g1; ++c) out[c] = s2 > 0.0 ? tho_e2m1_value(tho_e2m1_encode(v[c], s2)) * s2 : 0.0;
 }
 
-static void tho_quantize_p_tile(const double* t, const int* mask, int n, int fmt, double mt,
-                                double* pq, double* dq, double* ref) {
+static void tho_quantize_p_tile(const double* t, const double* ta, const int* mask, int n, int fmt,
+                                double mt, double* pq, double* dq, double* ref) {
   int g = tho_group_size(fmt);
   double v[64], alt[64];
   if (fmt == THO_NVFP4) {
@@ -489,10 +494,10 @@ static void tho_quantize_p_tile(const double* t, const int* mask, int n, int fmt
      * own rounding boundary (NVFP4 values carry the error of two
      * exponentials, the element's and the tile maximum's) */
     double unit = fmt == THO_NVFP4 ? 1.0 / 2688.0 : 1.0;
-    double tg = -INFINITY;
-    for (int c = g0; c < g1; ++c)
-      if (!mask[c] && t[c] > tg) tg = t[c];
-    double eg = (fmt == THO_NVFP4 ? 2.0 : 1.0) * tho_eval_eps(tg);
+    double ag = 0.0; /* largest magnitude sum among the tile's scores */
+    for (int c = 0; c < n; ++c)
+      if (!mask[c] && ta[c] > ag) ag = ta[c];
+    double eg = (fmt == THO_NVFP4 ? 2.0 : 1.0) * tho_eval_eps(ag);
     double s2, s2alt;
     if (fmt == THO_NVFP4) {
       int code = tho_e4m3_encode_ratio(amax, 6.0);
@@ -513,7 +518,7 @@ static void tho_quantize_p_tile(const double* t, const int* mask, int n, int fmt
         dq[c] = 0.0;
         continue;
       }
-      double ec = (fmt == THO_NVFP4 ? 2.0 : 1.0) * tho_eval_eps(t[c]);
+      double ec = fmt == THO_NVFP4 ? tho_eval_eps(ta[c]) + tho_eval_eps(ag) : tho_eval_eps(ta[c]);
       double d = tho_e2m1_flip(v[c], s2, ec);
       if (s2alt != s2) d += fabs(alt[c] - pq[c] / unit) + tho_e2m1_flip(v[c], s2alt, ec);
       dq[c] = d * unit;
@@ -542,10 +547,11 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
   const int32_t* sel = a->idx + (((size_t)b * a->Hq + hq) * nq + i) * a->kmax;
   int nsel = a->cnt[((size_t)b * a->Hq + hq) * nq + i];
   int nvalid = tho_valid_blocks(i, S, a->bq, bk, a->causal);
-  double t[64], pq[64], dq[64];
+  double t[64], ta[64], pq[64], dq[64];
   int mask[64];
   double* acc = (double*)calloc((size_t)D, sizeof(double));
   double* uacc = (double*)calloc((size_t)D, sizeof(double)); /* uncertainty, like acc */
+  double ul = 0.0; /* uncertainty of the row sum, like l */
   double* qh = (double*)malloc(sizeof(double) * (size_t)D);
   double* q4 = (double*)malloc(sizeof(double) * (size_t)D);
   double m = -INFINITY, l = 0.0;
@@ -562,31 +568,46 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
     double mt = -INFINITY;
     for (int c = 0; c < n; ++c) {
       mask[c] = a->causal && (c0 + c > r);
-      double s = 0.0;
+      double s = 0.0, sa = 0.0;
       if (!mask[c]) {
         const double* qv = q4;
         const double* kv = a->k4 + (kvbase + c0 + c) * D;
-        for (int d = 0; d < D; ++d) s += qv[d] * kv[d];
+        for (int d = 0; d < D; ++d) {
+          s += qv[d] * kv[d];
+          sa += fabs(qv[d] * kv[d]);
+        }
       }
       t[c] = mask[c] ? -INFINITY : s * a->sm_scale * THO_LOG2E;
+      ta[c] = sa * a->sm_scale * THO_LOG2E;
       if (t[c] > mt) mt = t[c];
     }
     if (mt == -INFINITY) continue; /* every key of this block is masked for row r */
     double ref;
-    tho_quantize_p_tile(t, mask, n, a->fmt, mt, pq, u_row ? dq : NULL, &ref);
+    tho_quantize_p_tile(t, ta, mask, n, a->fmt, mt, pq, u_row ? dq : NULL, &ref);
     double m_new = m > mt ? m : mt;
     double alpha = exp2(m - m_new); /* 0 when m = -inf */
     double w = exp2(ref - m_new);
+    double emt = 0.0; /* NVFP4: error of the level-1 factor 2^mt */
+    if (a->fmt == THO_NVFP4)
+      for (int c = 0; c < n; ++c)
+        if (!mask[c] && t[c] == mt) emt = tho_eval_eps(ta[c]);
     if (u_row)
       for (int d = 0; d < D; ++d) {
-        double uv = 0.0;
-        for (int c = 0; c < n; ++c) uv += dq[c] * fabs(a->v4[(kvbase + c0 + c) * D + d]);
-        uacc[d] = alpha * uacc[d] + w * uv;
+        double uv = 0.0, pv = 0.0;
+        for (int c = 0; c < n; ++c) {
+          uv += dq[c] * fabs(a->v4[(kvbase + c0 + c) * D + d]);
+          pv += fabs(pq[c] * a->v4[(kvbase + c0 + c) * D + d]);
+        }
+        uacc[d] = alpha * uacc[d] + w * (uv + emt * pv);
       }
-    double psum = 0.0;
+    double psum = 0.0, upsum = 0.0;
     for (int c = 0; c < n; ++c)
-      if (!mask[c]) psum += exp2(t[c] - m_new);
+      if (!mask[c]) {
+        psum += exp2(t[c] - m_new);
+        upsum += exp2(t[c] - m_new) * tho_eval_eps(ta[c]);
+      }
     l = alpha * l + psum;
+    ul = alpha * ul + upsum;
     for (int d = 0; d < D; ++d) {
       double pv = 0.0;
       for (int c = 0; c < n; ++c) pv += pq[c] * a->v4[(kvbase + c0 + c) * D + d];
@@ -605,11 +626,15 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
     double mt = -INFINITY;
     for (int c = 0; c < n; ++c) {
       mask[c] = a->causal && (c0 + c > r);
-      double s = 0.0;
+      double s = 0.0, sa = 0.0;
       if (!mask[c])
-        for (int d = 0; d < D; ++d)
-          s += qh[d] * tho_half_to_double(a->k16[(kvbase + c0 + c) * D + d]);
+        for (int d = 0; d < D; ++d) {
+          double pr = qh[d] * tho_half_to_double(a->k16[(kvbase + c0 + c) * D + d]);
+          s += pr;
+          sa += fabs(pr);
+        }
       t[c] = mask[c] ? -INFINITY : s * a->sm_scale * THO_LOG2E;
+      ta[c] = sa * a->sm_scale * THO_LOG2E;
       if (t[c] > mt) mt = t[c];
     }
     if (mt == -INFINITY) continue;
@@ -620,7 +645,7 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
      * z = ceil(m_new), which rounds 2^t to fp16's 11 significant bits
      * whichever integer z is used. */
     double z = ceil(m_new);
-    double psum = 0.0;
+    double psum = 0.0, upsum = 0.0;
     for (int c = 0; c < n; ++c) {
       if (mask[c]) {
         pq[c] = 0.0;
@@ -628,8 +653,9 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
         continue;
       }
       psum += exp2(t[c] - m_new);
+      upsum += exp2(t[c] - m_new) * tho_eval_eps(ta[c]);
       pq[c] = tho_round_to_half(exp2(t[c] - z)) * exp2(z - m_new);
-      dq[c] = tho_half_flip(exp2(t[c] - z), tho_eval_eps(t[c])) * exp2(z - m_new);
+      dq[c] = tho_half_flip(exp2(t[c] - z), tho_eval_eps(ta[c])) * exp2(z - m_new);
     }
     if (u_row)
       for (int d = 0; d < D; ++d) {
@@ -639,6 +665,7 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
         uacc[d] = alpha * uacc[d] + uv;
       }
     l = alpha * l + psum;
+    ul = alpha * ul + upsum;
     for (int d = 0; d < D; ++d) {
       double pv = 0.0;
       for (int c = 0; c < n; ++c)
@@ -650,7 +677,7 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
 
   for (int d = 0; d < D; ++d) o_row[d] = acc[d] / l;
   if (u_row)
-    for (int d = 0; d < D; ++d) u_row[d] = uacc[d] / l;
+    for (int d = 0; d < D; ++d) u_row[d] = uacc[d] / l + fabs(o_row[d]) * ul / l;
   if (lse_out) *lse_out = m * THO_LN2 + log(l);
   free(uacc);
   free(q4);

@@ -128,8 +128,10 @@ def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal,
     """Dense two-pass restatement of the forward pass: every score first,
     then one global maximum per row, then the weighted sum.  q4/k4/v4 and
     q16/k16/v16 are fp64 [B,H,S,D] (dequantised FP4 / decoded fp16).
-    perturb(t) -> t', if given, moves the scores that feed the rounding
-    decisions of P (not the row sum), as a lower-precision evaluation would."""
+    perturb(t, a) -> t', if given, moves every score (the rounding decisions
+    of P, the row sum and the NVFP4 level-1 factor alike), as a
+    lower-precision evaluation would; a holds each score's sum of product
+    magnitudes in the same log2 units."""
     B, Hq, S, D = q4.shape
     Hkv = k4.shape[1]
     G = Hq // Hkv
@@ -141,6 +143,8 @@ def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal,
             hk = hq // G
             t4 = (q4[b, hq] @ k4[b, hk].T) * sm_scale * LOG2E
             t16 = None if q16 is None else (q16[b, hq] @ k16[b, hk].T) * sm_scale * LOG2E
+            a4 = (np.abs(q4[b, hq]) @ np.abs(k4[b, hk]).T) * sm_scale * LOG2E
+            a16 = None if q16 is None else (np.abs(q16[b, hq]) @ np.abs(k16[b, hk]).T) * sm_scale * LOG2E
             for i in range(nq):
                 promoted = set(int(j) for j in idx[b, hq, i, : cnt[b, hq, i]])
                 nval = valid_blocks(i, S, bq, bk, causal)
@@ -152,26 +156,21 @@ def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal,
                         mask = (keys > r) if causal else np.zeros(len(keys), bool)
                         if mask.all():
                             continue
-                        src = t16 if j in promoted else t4
-                        tiles.append((src[r, c0:c1], mask, j in promoted, c0, c1))
-                    M = max(np.max(np.where(m, -np.inf, t)) for t, m, _, _, _ in tiles)
+                        src, asrc = (t16, a16) if j in promoted else (t4, a4)
+                        tiles.append((src[r, c0:c1], mask, j in promoted, c0, c1, asrc[r, c0:c1]))
+                    M = max(np.max(np.where(m, -np.inf, t)) for t, m, _, _, _, _ in tiles)
                     l = 0.0
                     acc = np.zeros(D)
-                    for t, m, is16, c0, c1 in tiles:
-                        e = np.where(m, 0.0, np.exp2(np.where(m, 0, t) - M))
+                    for t, m, is16, c0, c1, a in tiles:
+                        tq = t if perturb is None else np.where(m, t, perturb(t, a))
+                        e = np.where(m, 0.0, np.exp2(np.where(m, 0, tq) - M))
                         l += e.sum()
-                        tq = t if perturb is None else np.where(m, t, perturb(t))
                         if is16:
                             z = np.ceil(M)
                             p = np.where(m, 0.0, fp16_round(np.exp2(np.where(m, 0, tq) - z))) * np.exp2(z - M)
                             acc += p @ v16[b, hk, c0:c1]
                         else:
                             pq, ref = quantize_p_tile(tq, m, fmt)
-                            if perturb is not None and fmt == 0:
-                                # NVFP4 level 1 divides by the tile maximum: keep the
-                                # unperturbed one so that only the decisions move (MX
-                                # codes carry their own power-of-two offset)
-                                ref += np.max(np.where(m, -np.inf, t)) - np.max(np.where(m, -np.inf, tq))
                             acc += (pq * np.exp2(ref - M)) @ v4[b, hk, c0:c1]
                     O[b, hq, r] = acc / l
                     L[b, hq, r] = M * LN2 + np.log(l)

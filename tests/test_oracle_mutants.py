@@ -20,10 +20,10 @@ MUTANTS = {
     "topk_ascending": ("if (x->s > y->s) return -1;", "if (x->s > y->s) return 1;"),
     "e2m1_ties_up": ("if (a > t || (a == t && ((k + 1) & 1) == 0)) code = k + 1;",
                      "if (a >= t) code = k + 1;"),
-    "rowsum_quantised": ("if (!mask[c]) psum += exp2(t[c] - m_new);\n    l = alpha * l + psum;\n    for (int d = 0; d < D; ++d) {\n      double pv = 0.0;\n      for (int c = 0; c < n; ++c) pv += pq[c]",
-                         "if (!mask[c]) psum += pq[c] * w;\n    l = alpha * l + psum;\n    for (int d = 0; d < D; ++d) {\n      double pv = 0.0;\n      for (int c = 0; c < n; ++c) pv += pq[c]"),
-    "causal_off_by_one": ("mask[c] = a->causal && (c0 + c > r);\n      double s = 0.0;\n      if (!mask[c]) {",
-                          "mask[c] = a->causal && (c0 + c >= r);\n      double s = 0.0;\n      if (!mask[c]) {"),
+    "rowsum_quantised": ("      if (!mask[c]) {\n        psum += exp2(t[c] - m_new);\n        upsum += exp2(t[c] - m_new) * tho_eval_eps(ta[c]);\n      }\n    l = alpha * l + psum;",
+                         "      if (!mask[c]) {\n        psum += pq[c] * w;\n        upsum += exp2(t[c] - m_new) * tho_eval_eps(ta[c]);\n      }\n    l = alpha * l + psum;"),
+    "causal_off_by_one": ("mask[c] = a->causal && (c0 + c > r);\n      double s = 0.0, sa = 0.0;\n      if (!mask[c]) {",
+                          "mask[c] = a->causal && (c0 + c >= r);\n      double s = 0.0, sa = 0.0;\n      if (!mask[c]) {"),
     "v_transposed_index": ("e = ((size_t)bh * D + d) * Sp + s;", "e = ((size_t)bh * D + (s % D)) * Sp + d;"),
     "mean_divides_by_block": ("(float)(sum / (double)(r1 - r0));", "(float)(sum / (double)blk);"),
     "e4m3_no_saturation_tie": ("if (num > t || (num == t && ((k + 1) & 1) == 0))",
