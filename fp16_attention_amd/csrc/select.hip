@@ -9,7 +9,11 @@
 //  - score_topk gives one workgroup to each (batch, key head, query block),
 //    scoring all query heads of the GQA group against key-block means staged
 //    through LDS (each kbar is read once per group, not once per head), then
-//    keeps the top-k by rounds of a workgroup-wide argmax.
+//    gives each head's row of scores to one wavefront, which finds the k-th
+//    largest (score, block) key with wavefront reductions only (k rounds of
+//    argmax below the previous one for small k, a bitwise search from the
+//    top bit otherwise) and writes the blocks at or above it in ascending
+//    order by ballot compaction: no workgroup barrier in the selection.
 #include "common.h"
 
 namespace thrift {
@@ -63,11 +67,67 @@ __device__ inline uint64_t wave_max_u64(uint64_t v) {
   return v;
 }
 
+__device__ inline int wave_sum_i32(int v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// One wavefront selects the k best of the n scores srow[0..n) (LDS) and
+// writes them ascending into out[0..k), -1 into out[k..kmax).  The
+// (score, block) keys are unique, so the k-th largest key is a threshold
+// that selects exactly k blocks.
+__device__ inline void wave_topk(const float* srow, int n, int k, int32_t* __restrict__ out, int kmax,
+                                 int lane) {
+  if (k >= n) {
+    for (int e = lane; e < kmax; e += kWave) out[e] = e < n ? e : -1;
+    return;
+  }
+  const int nc = cdiv(n, kWave);  // this lane's candidates: j = c*64 + lane
+  uint64_t thr = ~0ull;
+  if (k == 0) {
+  } else if (k <= 32) {  // k rounds: the largest key below the previous round's
+    uint64_t prev = ~0ull;
+    for (int r = 0; r < k; ++r) {
+      uint64_t best = 0;
+      for (int c = 0; c < nc; ++c) {
+        const int j = c * kWave + lane;
+        if (j < n) {
+          const uint64_t key = pair_key(srow[j], j);
+          if (key < prev && key > best) best = key;
+        }
+      }
+      prev = wave_max_u64(best);
+    }
+    thr = prev;
+  } else {  // the largest t with at least k keys >= t, one bit at a time
+    uint64_t prefix = 0;
+    for (int bit = 63; bit >= 0; --bit) {
+      const uint64_t cand = prefix | (1ull << bit);
+      int cntv = 0;
+      for (int c = 0; c < nc; ++c) {
+        const int j = c * kWave + lane;
+        cntv += (j < n && pair_key(srow[j], j) >= cand) ? 1 : 0;
+      }
+      if (wave_sum_i32(cntv) >= k) prefix = cand;
+    }
+    thr = prefix;
+  }
+  int base = 0;
+  for (int c = 0; c < nc; ++c) {
+    const int j = c * kWave + lane;
+    const bool sel = k > 0 && j < n && pair_key(srow[j], j) >= thr;
+    const uint64_t bal = __ballot(sel);
+    if (sel) out[base + __popcll(bal & ((1ull << lane) - 1))] = j;
+    base += __popcll(bal);
+  }
+  for (int e = k + lane; e < kmax; e += kWave) out[e] = -1;
+}
+
 constexpr int kTopkThreads = 256;
 constexpr int kHeadChunk = 4;     // query heads scored together per pass
 constexpr int kKeyChunk = 256;    // key blocks staged per pass (one per thread)
 constexpr int kDimChunk = 32;     // channels staged per pass
-constexpr int kMaxPartialTopk = 1024;  // budgets below all-valid are at most this
 
 template <int D>
 __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
@@ -77,8 +137,6 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
   extern __shared__ float sc[];  // [kHeadChunk][nK] scores
   __shared__ float qv[kHeadChunk][D];
   __shared__ float kst[kKeyChunk][kDimChunk + 1];
-  __shared__ uint64_t wred[kTopkThreads / kWave];
-  __shared__ int sel_list[kMaxPartialTopk];
 
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int i = blockIdx.x, bhk = blockIdx.y;
@@ -120,50 +178,12 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
     }
     __syncthreads();
 
-    for (int h = 0; h < nh; ++h) {
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    for (int h = wave_u; h < nh; h += kTopkThreads / kWave) {  // one wavefront per head row
       const int hq = hk * G + h0 + h;
       const size_t row = ((size_t)b * Hq + hq) * nq + i;
-      int32_t* out = idx + row * kmax;
-      if (k == n) {  // every valid block is promoted
-        for (int e = t; e < kmax; e += kTopkThreads) out[e] = e < n ? e : -1;
-      } else {
-        const float* srow = sc + h * nK;
-        uint32_t taken = 0;  // bit c: candidate j = t + c*256 already chosen
-        uint64_t best = 0;
-        bool have = false;
-        for (int r = 0; r < k; ++r) {
-          if (!have) {  // (re)scan this thread's candidates
-            best = 0;
-            for (int c = 0, j = t; j < n; ++c, j += kTopkThreads)
-              if (!(taken >> c & 1u)) {
-                uint64_t key = pair_key(srow[j], j);
-                best = key > best ? key : best;
-              }
-            have = true;
-          }
-          uint64_t m = wave_max_u64(best);
-          if (lane == 0) wred[wave] = m;
-          __syncthreads();
-          uint64_t g = wred[0];
-          for (int w = 1; w < kTopkThreads / kWave; ++w) g = wred[w] > g ? wred[w] : g;
-          const int jw = (int)(0xFFFFFFFFu - (uint32_t)g);
-          if (jw % kTopkThreads == t) {
-            taken |= 1u << (jw / kTopkThreads);
-            have = false;
-          }
-          if (t == 0) sel_list[r] = jw;
-          __syncthreads();
-        }
-        // ascending order by rank among the chosen
-        for (int e = t; e < k; e += kTopkThreads) {
-          int je = sel_list[e], rank = 0;
-          for (int u = 0; u < k; ++u) rank += sel_list[u] < je;
-          out[rank] = je;
-        }
-        for (int e = k + t; e < kmax; e += kTopkThreads) out[e] = -1;
-        __syncthreads();
-      }
-      if (t == 0) cnt[row] = k;
+      wave_topk(sc + h * nK, n, k, idx + row * kmax, kmax, lane);
+      if (lane == 0) cnt[row] = k;
     }
   }
 }
@@ -206,11 +226,6 @@ extern "C" thrift_status thrift_select_blocks(const void* q16, const void* k16, 
   if (S > 262144) return THRIFT_EUNSUPPORTED;
   int need = thrift_select_kmax(S, block_q, block_k, causal, topk_count, topk_bp);
   if (kmax < need || kmax < 1) return THRIFT_EINVAL;
-  for (int i = 0; i < cdiv(S, block_q); ++i) {  // partial budgets are bounded
-    int n = valid_kv_blocks(i, S, block_q, block_k, causal);
-    int k = topk_budget(n, topk_count, topk_bp);
-    if (k < n && k > kMaxPartialTopk) return THRIFT_EUNSUPPORTED;
-  }
   if (!aligned16(q16) || !aligned16(k16) || !aligned16(workspace)) return THRIFT_EALIGN;
   if (workspace_bytes < thrift_select_workspace_bytes(B, Hq, Hkv, S, D, block_q, block_k))
     return THRIFT_EWORKSPACE;
