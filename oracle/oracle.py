@@ -69,12 +69,18 @@ def _declare(L):
     L.tho_block_score.argtypes = [_P, _P, _I]
     L.tho_select.restype = None
     L.tho_select.argtypes = [_P, _P] + [_I] * 10 + [_P, _P, _I, _P]
+    L.tho_kmax_kv.restype = _I
+    L.tho_kmax_kv.argtypes = [_I] * 7
+    L.tho_select_kv.restype = None
+    L.tho_select_kv.argtypes = [_P, _P] + [_I] * 11 + [_P, _P, _I, _P]
     L.tho_quantize.restype = None
     L.tho_quantize.argtypes = [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P]
     L.tho_dequantize.restype = None
     L.tho_dequantize.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
     L.tho_attention.restype = None
     L.tho_attention.argtypes = [_P] * 12 + [_I, _P, _P, _I] + [_I] * 8 + [_D, _P, _I, _P, _P, _P]
+    L.tho_attention_kv.restype = None
+    L.tho_attention_kv.argtypes = [_P] * 12 + [_I, _P, _P, _I] + [_I] * 9 + [_D, _P, _I, _P, _P, _P]
     L.tho_fp4_scores.restype = None
     L.tho_fp4_scores.argtypes = [_P] * 6 + [_I] * 6 + [_P]
     L.tho_e2m1_encode_array.restype = None
@@ -103,8 +109,10 @@ def pad_s(S: int) -> int:
     return lib().tho_pad_s(S)
 
 
-def kmax(S, bq, bk, causal, topk_count, topk_bp) -> int:
-    return lib().tho_kmax(S, bq, bk, int(causal), topk_count, topk_bp)
+def kmax(S, bq, bk, causal, topk_count, topk_bp, Sk=None) -> int:
+    """Largest per-query-block budget; Sk (keys, default S) for S queries at
+    the end of a longer key sequence."""
+    return lib().tho_kmax_kv(S, S if Sk is None else Sk, bq, bk, int(causal), topk_count, topk_bp)
 
 
 # ---- scalar / array format routines ------------------------------------
@@ -163,18 +171,19 @@ def block_means(x16, blk):
 
 
 def select(q16, k16, bq, bk, causal, topk_count=-1, topk_bp=0, kmax_=None, with_scores=False):
-    """Per-query-block top-k: returns (idx [B,Hq,nQ,kmax] int32, cnt [B,Hq,nQ] int32, scores)."""
+    """Per-query-block top-k: returns (idx [B,Hq,nQ,kmax] int32, cnt [B,Hq,nQ] int32, scores).
+    k16 may hold more positions than q16 (queries = the last positions)."""
     q16 = _c(q16, np.float16)
     k16 = _c(k16, np.float16)
     B, Hq, S, D = q16.shape
-    Hkv = k16.shape[1]
-    nq, nk = -(-S // bq), -(-S // bk)
-    km = kmax(S, bq, bk, causal, topk_count, topk_bp) if kmax_ is None else kmax_
+    Hkv, Sk = k16.shape[1], k16.shape[2]
+    nq, nk = -(-S // bq), -(-Sk // bk)
+    km = kmax(S, bq, bk, causal, topk_count, topk_bp, Sk) if kmax_ is None else kmax_
     idx = np.empty((B, Hq, nq, max(km, 0)), np.int32)
     cnt = np.empty((B, Hq, nq), np.int32)
     scores = np.empty((B, Hq, nq, nk), np.float32) if with_scores else None
-    lib().tho_select(_ptr(q16), _ptr(k16), B, Hq, Hkv, S, D, bq, bk, int(causal), topk_count,
-                     topk_bp, _ptr(idx), _ptr(cnt), km, _ptr(scores))
+    lib().tho_select_kv(_ptr(q16), _ptr(k16), B, Hq, Hkv, S, Sk, D, bq, bk, int(causal), topk_count,
+                        topk_bp, _ptr(idx), _ptr(cnt), km, _ptr(scores))
     return idx, cnt, scores
 
 
@@ -229,7 +238,7 @@ def attention(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, c
     with_u, the decision-uncertainty bound u [B,Hq,S,D]; with a work list of
     (b, hq, i) triples only those query blocks are filled (the rest stay NaN)."""
     B, Hq, S, D = q4.shape
-    Hkv = k4.shape[1]
+    Hkv, Sk = k4.shape[1], k4.shape[2]
     if sm_scale is None:
         sm_scale = 1.0 / np.sqrt(D)
     q16 = None if q16 is None else _c(q16, np.float16)
@@ -243,12 +252,12 @@ def attention(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, c
     u = np.full((B, Hq, S, D), np.nan, np.float64) if with_u else None
     w = None if work is None else _c(np.asarray(work).reshape(-1, 3), np.int32)
     nw = 0 if w is None else w.shape[0]
-    lib().tho_attention(_ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
-                        _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales),
-                        _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales),
-                        _ptr(v4.tensor_scale), q4.fmt, _ptr(idx), _ptr(cnt), km, B, Hq, Hkv, S, D,
-                        bq, bk, int(causal), float(sm_scale), _ptr(w), nw, _ptr(o), _ptr(lse),
-                        _ptr(u))
+    lib().tho_attention_kv(_ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
+                           _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales),
+                           _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales),
+                           _ptr(v4.tensor_scale), q4.fmt, _ptr(idx), _ptr(cnt), km, B, Hq, Hkv, S,
+                           Sk, D, bq, bk, int(causal), float(sm_scale), _ptr(w), nw, _ptr(o),
+                           _ptr(lse), _ptr(u))
     return (o, lse, u) if with_u else (o, lse)
 
 

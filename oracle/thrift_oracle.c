@@ -148,15 +148,19 @@ int tho_mx_exponent(double amax) {
 
 static int tho_cdiv(int a, int b) { return (a + b - 1) / b; }
 
-/* Valid key blocks of query block i: every block for non-causal attention;
- * for causal attention (query and key sequences aligned at their starts)
- * every block holding at least one key not after the block's last query. */
-static int tho_valid_blocks(int i, int S, int bq, int bk, int causal) {
-  int nk = tho_cdiv(S, bk);
+/* Valid key blocks of query block i for Sq queries against Sk keys
+ * (Sq <= Sk): every block for non-causal attention; for causal attention
+ * every block holding at least one key not after the block's last query,
+ * the queries being the last Sq positions of the key sequence (for Sq = Sk
+ * the two sequences are aligned at their starts; for Sq < Sk, as when new
+ * tokens attend to a cache, at their ends). */
+static int tho_valid_blocks_kv(int i, int Sq, int Sk, int bq, int bk, int causal) {
+  int nk = tho_cdiv(Sk, bk);
   if (!causal) return nk;
-  int last_q = (i + 1) * bq < S ? (i + 1) * bq - 1 : S - 1;
-  return last_q / bk + 1;
+  int last_q = (i + 1) * bq < Sq ? (i + 1) * bq - 1 : Sq - 1;
+  return (Sk - Sq + last_q) / bk + 1;
 }
+
 
 /* Budget of promoted blocks for a query block with n valid key blocks:
  * topk_count >= 0 is an absolute count, otherwise ceil(n * topk_bp / 10^4)
@@ -170,13 +174,17 @@ static int tho_budget(int n, int topk_count, int topk_bp) {
   return (int)(k < n ? k : n);
 }
 
-int tho_kmax(int S, int bq, int bk, int causal, int topk_count, int topk_bp) {
-  int nq = tho_cdiv(S, bq), km = 0;
+int tho_kmax_kv(int Sq, int Sk, int bq, int bk, int causal, int topk_count, int topk_bp) {
+  int nq = tho_cdiv(Sq, bq), km = 0;
   for (int i = 0; i < nq; ++i) {
-    int k = tho_budget(tho_valid_blocks(i, S, bq, bk, causal), topk_count, topk_bp);
+    int k = tho_budget(tho_valid_blocks_kv(i, Sq, Sk, bq, bk, causal), topk_count, topk_bp);
     if (k > km) km = k;
   }
   return km;
+}
+
+int tho_kmax(int S, int bq, int bk, int causal, int topk_count, int topk_bp) {
+  return tho_kmax_kv(S, S, bq, bk, causal, topk_count, topk_bp);
 }
 
 /* Token mean of each block of rows (reading of the pages' "token means":
@@ -234,14 +242,14 @@ static int tho_int_cmp(const void* a, const void* b) {
  * k_i best-scoring valid key blocks.  The query head hq reads key head
  * hq / (Hq / Hkv).  idx: [B, Hq, nQ, kmax], ascending, padded with -1;
  * cnt: [B, Hq, nQ].  scores (optional): [B, Hq, nQ, nK], NaN where invalid. */
-void tho_select(const uint16_t* q16, const uint16_t* k16, int B, int Hq, int Hkv, int S, int D,
-                int bq, int bk, int causal, int topk_count, int topk_bp, int32_t* idx,
-                int32_t* cnt, int kmax, float* scores) {
-  int nq = tho_cdiv(S, bq), nk = tho_cdiv(S, bk), G = Hq / Hkv;
+void tho_select_kv(const uint16_t* q16, const uint16_t* k16, int B, int Hq, int Hkv, int Sq, int Sk,
+                   int D, int bq, int bk, int causal, int topk_count, int topk_bp, int32_t* idx,
+                   int32_t* cnt, int kmax, float* scores) {
+  int nq = tho_cdiv(Sq, bq), nk = tho_cdiv(Sk, bk), G = Hq / Hkv;
   float* qm = (float*)malloc(sizeof(float) * (size_t)B * Hq * nq * D);
   float* km = (float*)malloc(sizeof(float) * (size_t)B * Hkv * nk * D);
-  tho_block_means(q16, B, Hq, S, D, bq, qm);
-  tho_block_means(k16, B, Hkv, S, D, bk, km);
+  tho_block_means(q16, B, Hq, Sq, D, bq, qm);
+  tho_block_means(k16, B, Hkv, Sk, D, bk, km);
   tho_cand* cand = (tho_cand*)malloc(sizeof(tho_cand) * (size_t)nk);
   int* sel = (int*)malloc(sizeof(int) * (size_t)nk);
   for (int b = 0; b < B; ++b)
@@ -249,7 +257,7 @@ void tho_select(const uint16_t* q16, const uint16_t* k16, int B, int Hq, int Hkv
       int hk = hq / G;
       for (int i = 0; i < nq; ++i) {
         size_t row = ((size_t)b * Hq + hq) * nq + i;
-        int n = tho_valid_blocks(i, S, bq, bk, causal);
+        int n = tho_valid_blocks_kv(i, Sq, Sk, bq, bk, causal);
         int k = tho_budget(n, topk_count, topk_bp);
         const float* qv = qm + row * D;
         for (int j = 0; j < n; ++j) {
@@ -269,6 +277,13 @@ void tho_select(const uint16_t* q16, const uint16_t* k16, int B, int Hq, int Hkv
   free(cand);
   free(km);
   free(qm);
+}
+
+void tho_select(const uint16_t* q16, const uint16_t* k16, int B, int Hq, int Hkv, int S, int D,
+                int bq, int bk, int causal, int topk_count, int topk_bp, int32_t* idx,
+                int32_t* cnt, int kmax, float* scores) {
+  tho_select_kv(q16, k16, B, Hq, Hkv, S, S, D, bq, bk, causal, topk_count, topk_bp, idx, cnt, kmax,
+                scores);
 }
 
 /* ------------------------------------------------------------------ */
@@ -527,26 +542,27 @@ static void tho_quantize_p_tile(const double* t, const double* ta, const int* ma
 }
 
 typedef struct {
-  int B, Hq, Hkv, S, D, bq, bk, causal, fmt, kmax;
+  int B, Hq, Hkv, S, Sk, D, bq, bk, causal, fmt, kmax; /* S: queries, Sk: keys */
   double sm_scale;
   const uint16_t *q16, *k16, *v16;
   const uint8_t *q4c, *q4s; /* FP4 query codes and scales as quantised */
   const float* q4t;
-  const double *k4, *v4; /* dequantised FP4 keys and values, [B,Hkv,S,D] */
+  const double *k4, *v4; /* dequantised FP4 keys and values, [B,Hkv,Sk,D] */
   const int32_t *idx, *cnt;
 } tho_attn_args;
 
 /* One query row r of query block i of head (b, hq). */
 static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, double* o_row,
                            double* lse_out, double* u_row) {
-  int D = a->D, S = a->S, bk = a->bk;
+  int D = a->D, S = a->S, Sk = a->Sk, bk = a->bk;
   int hk = hq / (a->Hq / a->Hkv);
   int nq = tho_cdiv(S, a->bq);
+  int qpos = Sk - S + r; /* the query's position in the key sequence */
   size_t qoff = (((size_t)b * a->Hq + hq) * S + r) * D;
-  size_t kvbase = ((size_t)b * a->Hkv + hk) * S;
+  size_t kvbase = ((size_t)b * a->Hkv + hk) * Sk;
   const int32_t* sel = a->idx + (((size_t)b * a->Hq + hq) * nq + i) * a->kmax;
   int nsel = a->cnt[((size_t)b * a->Hq + hq) * nq + i];
-  int nvalid = tho_valid_blocks(i, S, a->bq, bk, a->causal);
+  int nvalid = tho_valid_blocks_kv(i, S, Sk, a->bq, bk, a->causal);
   double t[64], ta[64], pq[64], dq[64];
   int mask[64];
   double* acc = (double*)calloc((size_t)D, sizeof(double));
@@ -564,10 +580,10 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
       ++sp;
       continue;
     }
-    int c0 = j * bk, n = (c0 + bk < S ? c0 + bk : S) - c0;
+    int c0 = j * bk, n = (c0 + bk < Sk ? c0 + bk : Sk) - c0;
     double mt = -INFINITY;
     for (int c = 0; c < n; ++c) {
-      mask[c] = a->causal && (c0 + c > r);
+      mask[c] = a->causal && (c0 + c > qpos);
       double s = 0.0, sa = 0.0;
       if (!mask[c]) {
         const double* qv = q4;
@@ -622,10 +638,10 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
     for (int d = 0; d < D; ++d) qh[d] = tho_half_to_double(a->q16[qoff + d]);
   for (int p = 0; p < nsel; ++p) {
     int j = sel[p];
-    int c0 = j * bk, n = (c0 + bk < S ? c0 + bk : S) - c0;
+    int c0 = j * bk, n = (c0 + bk < Sk ? c0 + bk : Sk) - c0;
     double mt = -INFINITY;
     for (int c = 0; c < n; ++c) {
-      mask[c] = a->causal && (c0 + c > r);
+      mask[c] = a->causal && (c0 + c > qpos);
       double s = 0.0, sa = 0.0;
       if (!mask[c])
         for (int d = 0; d < D; ++d) {
@@ -692,18 +708,19 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
  * (may be NULL), the bound on what decisions within fp32 evaluation error of
  * their rounding boundary can change in o; rows outside the work items are
  * left untouched. */
-void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
-                   const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
-                   const uint8_t* k4s, const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
-                   const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
-                   int B, int Hq, int Hkv, int S, int D, int bq, int bk, int causal,
-                   double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
-                   double* u) {
+void tho_attention_kv(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
+                      const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
+                      const uint8_t* k4s, const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
+                      const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                      int B, int Hq, int Hkv, int S, int Sk, int D, int bq, int bk, int causal,
+                      double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
+                      double* u) {
   tho_attn_args a;
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
   a.S = S;
+  a.Sk = Sk;
   a.D = D;
   a.bq = bq;
   a.bk = bk;
@@ -716,10 +733,10 @@ void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16
   a.v16 = v16;
   a.idx = idx;
   a.cnt = cnt;
-  double* k4 = (double*)malloc(sizeof(double) * (size_t)B * Hkv * S * D);
-  double* v4 = (double*)malloc(sizeof(double) * (size_t)B * Hkv * S * D);
-  tho_dequantize(k4c, k4s, k4t, B, Hkv, S, D, THO_AXIS_D, fmt, k4);
-  tho_dequantize(v4c, v4s, v4t, B, Hkv, S, D, THO_AXIS_S, fmt, v4);
+  double* k4 = (double*)malloc(sizeof(double) * (size_t)B * Hkv * Sk * D);
+  double* v4 = (double*)malloc(sizeof(double) * (size_t)B * Hkv * Sk * D);
+  tho_dequantize(k4c, k4s, k4t, B, Hkv, Sk, D, THO_AXIS_D, fmt, k4);
+  tho_dequantize(v4c, v4s, v4t, B, Hkv, Sk, D, THO_AXIS_S, fmt, v4);
   a.q4c = q4c;
   a.q4s = q4s;
   a.q4t = q4t;
@@ -747,6 +764,17 @@ void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16
   }
   free(v4);
   free(k4);
+}
+
+void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
+                   const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
+                   const uint8_t* k4s, const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
+                   const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                   int B, int Hq, int Hkv, int S, int D, int bq, int bk, int causal,
+                   double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
+                   double* u) {
+  tho_attention_kv(q16, k16, v16, q4c, q4s, q4t, k4c, k4s, k4t, v4c, v4s, v4t, fmt, idx, cnt, kmax, B,
+                   Hq, Hkv, S, S, D, bq, bk, causal, sm_scale, work, nwork, o, lse, u);
 }
 
 /* Scores of the FP4 path for one query row against keys [c0, c1) (test hook:

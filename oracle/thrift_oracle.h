@@ -25,11 +25,16 @@ int tho_group_size(int fmt);
 int tho_pad_s(int S);
 
 int tho_kmax(int S, int bq, int bk, int causal, int topk_count, int topk_bp);
+int tho_kmax_kv(int Sq, int Sk, int bq, int bk, int causal, int topk_count, int topk_bp);
 void tho_block_means(const uint16_t* x16, int B, int H, int S, int D, int blk, float* means);
 float tho_block_score(const float* qm, const float* km, int D);
 void tho_select(const uint16_t* q16, const uint16_t* k16, int B, int Hq, int Hkv, int S, int D,
                 int bq, int bk, int causal, int topk_count, int topk_bp, int32_t* idx,
                 int32_t* cnt, int kmax, float* scores);
+/* Sq queries (the last Sq positions) against Sk keys; tho_select is Sq = Sk. */
+void tho_select_kv(const uint16_t* q16, const uint16_t* k16, int B, int Hq, int Hkv, int Sq, int Sk,
+                   int D, int bq, int bk, int causal, int topk_count, int topk_bp, int32_t* idx,
+                   int32_t* cnt, int kmax, float* scores);
 
 void tho_quantize(const uint16_t* x16, int B, int H, int S, int D, int axis, int fmt,
                   uint8_t* codes, uint8_t* scales, float* tensor_scale);
@@ -45,6 +50,13 @@ void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16
                    int B, int Hq, int Hkv, int S, int D, int bq, int bk, int causal,
                    double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
                    double* u);
+void tho_attention_kv(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
+                      const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
+                      const uint8_t* k4s, const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
+                      const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                      int B, int Hq, int Hkv, int S, int Sk, int D, int bq, int bk, int causal,
+                      double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
+                      double* u);
 void tho_fp4_scores(const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
                     const uint8_t* k4s, const float* k4t, int fmt, int S, int D, int r, int c0,
                     int c1, double* out);

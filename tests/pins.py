@@ -86,11 +86,14 @@ def decode_fp4(codes_u8, scales_u8, tensor_scale, fmt, axis, shape):
     return np.swapaxes(vals[..., :S], -1, -2)
 
 
-def valid_blocks(i, S, bq, bk, causal):
-    nk = -(-S // bk)
+def valid_blocks(i, S, bq, bk, causal, Sk=None):
+    """Key blocks query block i may see; with Sk keys (default S) the S
+    queries are the last S positions of the key sequence."""
+    Sk = S if Sk is None else Sk
+    nk = -(-Sk // bk)
     if not causal:
         return nk
-    return (min(S, (i + 1) * bq) - 1) // bk + 1
+    return (Sk - S + min(S, (i + 1) * bq) - 1) // bk + 1
 
 
 def fp16_round(x):
@@ -133,9 +136,10 @@ def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal,
     lower-precision evaluation would; a holds each score's sum of product
     magnitudes in the same log2 units."""
     B, Hq, S, D = q4.shape
-    Hkv = k4.shape[1]
+    Hkv, Sk = k4.shape[1], k4.shape[2]
     G = Hq // Hkv
-    nq, nk = -(-S // bq), -(-S // bk)
+    nq, nk = -(-S // bq), -(-Sk // bk)
+    off = Sk - S  # queries are the last S positions
     O = np.zeros((B, Hq, S, D))
     L = np.zeros((B, Hq, S))
     for b in range(B):
@@ -147,13 +151,13 @@ def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal,
             a16 = None if q16 is None else (np.abs(q16[b, hq]) @ np.abs(k16[b, hk]).T) * sm_scale * LOG2E
             for i in range(nq):
                 promoted = set(int(j) for j in idx[b, hq, i, : cnt[b, hq, i]])
-                nval = valid_blocks(i, S, bq, bk, causal)
+                nval = valid_blocks(i, S, bq, bk, causal, Sk)
                 for r in range(i * bq, min(S, (i + 1) * bq)):
                     tiles = []  # (t row, mask, is16, c0)
                     for j in range(nval):
-                        c0, c1 = j * bk, min(S, (j + 1) * bk)
+                        c0, c1 = j * bk, min(Sk, (j + 1) * bk)
                         keys = np.arange(c0, c1)
-                        mask = (keys > r) if causal else np.zeros(len(keys), bool)
+                        mask = (keys > r + off) if causal else np.zeros(len(keys), bool)
                         if mask.all():
                             continue
                         src, asrc = (t16, a16) if j in promoted else (t4, a4)
@@ -178,16 +182,17 @@ def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal,
 
 
 def exact_attention(q, k, v, causal, sm_scale):
-    """Textbook softmax attention in fp64 (GQA by head groups)."""
+    """Textbook softmax attention in fp64 (GQA by head groups); with more
+    keys than queries, the queries are the last positions."""
     B, Hq, S, D = q.shape
-    G = Hq // k.shape[1]
+    G, Sk = Hq // k.shape[1], k.shape[2]
     O = np.zeros_like(q)
     L = np.zeros((B, Hq, S))
     for b in range(B):
         for hq in range(Hq):
             s = (q[b, hq] @ k[b, hq // G].T) * sm_scale
             if causal:
-                s = np.where(np.triu(np.ones((S, S), bool), 1), -np.inf, s)
+                s = np.where(np.triu(np.ones((S, Sk), bool), 1 + Sk - S), -np.inf, s)
             m = s.max(axis=1, keepdims=True)
             p = np.exp(s - m)
             l = p.sum(axis=1, keepdims=True)

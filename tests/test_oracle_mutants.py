@@ -18,12 +18,14 @@ MUTANTS = {
     "no_rescale_fp4": ("acc[d] = alpha * acc[d] + w * pv;", "acc[d] = acc[d] + w * pv;"),
     "mx_level1_not_integer": ("double z = ceil(mt);", "double z = mt;"),
     "topk_ascending": ("if (x->s > y->s) return -1;", "if (x->s > y->s) return 1;"),
+    "decode_start_aligned": ("int qpos = Sk - S + r;", "int qpos = r;"),
+    "decode_valid_blocks_start_aligned": ("return (Sk - Sq + last_q) / bk + 1;", "return last_q / bk + 1;"),
     "e2m1_ties_up": ("if (a > t || (a == t && ((k + 1) & 1) == 0)) code = k + 1;",
                      "if (a >= t) code = k + 1;"),
     "rowsum_quantised": ("      if (!mask[c]) {\n        psum += exp2(t[c] - m_new);\n        upsum += exp2(t[c] - m_new) * tho_eval_eps(ta[c]);\n      }\n    l = alpha * l + psum;",
                          "      if (!mask[c]) {\n        psum += pq[c] * w;\n        upsum += exp2(t[c] - m_new) * tho_eval_eps(ta[c]);\n      }\n    l = alpha * l + psum;"),
-    "causal_off_by_one": ("mask[c] = a->causal && (c0 + c > r);\n      double s = 0.0, sa = 0.0;\n      if (!mask[c]) {",
-                          "mask[c] = a->causal && (c0 + c >= r);\n      double s = 0.0, sa = 0.0;\n      if (!mask[c]) {"),
+    "causal_off_by_one": ("mask[c] = a->causal && (c0 + c > qpos);\n      double s = 0.0, sa = 0.0;\n      if (!mask[c]) {",
+                          "mask[c] = a->causal && (c0 + c >= qpos);\n      double s = 0.0, sa = 0.0;\n      if (!mask[c]) {"),
     "v_transposed_index": ("e = ((size_t)bh * D + d) * Sp + s;", "e = ((size_t)bh * D + (s % D)) * Sp + d;"),
     "mean_divides_by_block": ("(float)(sum / (double)(r1 - r0));", "(float)(sum / (double)blk);"),
     "e4m3_no_saturation_tie": ("if (num > t || (num == t && ((k + 1) & 1) == 0))",
@@ -49,6 +51,6 @@ def test_mutant_is_caught(tmp_path, name):
     env = dict(os.environ, THRIFT_ORACLE_LIB=lib)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_formats.py", "tests/test_oracle_select.py",
-                        "tests/test_oracle_attention.py"],
+                        "tests/test_oracle_attention.py", "tests/test_oracle_decode.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
