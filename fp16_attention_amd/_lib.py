@@ -10,7 +10,9 @@ THRIFT_NVFP4, THRIFT_MXFP4 = 0, 1
 THRIFT_GROUP_D, THRIFT_GROUP_S = 0, 1
 
 EXPORTS = ("thrift_select_kmax", "thrift_select_workspace_bytes", "thrift_select_blocks",
+           "thrift_select_kmax_kv", "thrift_select_workspace_bytes_kv", "thrift_select_blocks_kv",
            "thrift_quantize_workspace_bytes", "thrift_quantize_fp4", "thrift_attention_fwd",
+           "thrift_attention_decode_workspace_bytes", "thrift_attention_decode",
            "thrift_status_string")
 
 _lib = None
@@ -38,6 +40,16 @@ def load():
         L.thrift_select_workspace_bytes.argtypes = [I] * 7
         L.thrift_select_blocks.restype = I
         L.thrift_select_blocks.argtypes = [P, P] + [I] * 10 + [P, P, I, P, SZ, P]
+        L.thrift_select_kmax_kv.restype = I
+        L.thrift_select_kmax_kv.argtypes = [I] * 7
+        L.thrift_select_workspace_bytes_kv.restype = SZ
+        L.thrift_select_workspace_bytes_kv.argtypes = [I] * 8
+        L.thrift_select_blocks_kv.restype = I
+        L.thrift_select_blocks_kv.argtypes = [P, P] + [I] * 11 + [P, P, I, P, SZ, P]
+        L.thrift_attention_decode_workspace_bytes.restype = SZ
+        L.thrift_attention_decode_workspace_bytes.argtypes = [I] * 7
+        L.thrift_attention_decode.restype = I
+        L.thrift_attention_decode.argtypes = [P] * 12 + [I, P, P] + [I] * 9 + [F, P, I, P, P, SZ, P]
         L.thrift_quantize_workspace_bytes.restype = SZ
         L.thrift_quantize_workspace_bytes.argtypes = [I] * 5
         L.thrift_quantize_fp4.restype = I

@@ -16,8 +16,9 @@ from . import _lib
 from ._lib import THRIFT_GROUP_D, THRIFT_GROUP_S, THRIFT_MXFP4, THRIFT_NVFP4, ThriftError
 
 __all__ = ["thrift_select_kmax", "thrift_select_blocks", "thrift_quantize_fp4",
-           "thrift_attention_fwd", "FP4Tensor", "fp4_transposed", "thrift_forward", "THRIFT_NVFP4", "THRIFT_MXFP4",
-           "THRIFT_GROUP_D", "THRIFT_GROUP_S", "ThriftError"]
+           "thrift_attention_fwd", "thrift_attention_decode", "thrift_decode", "FP4Tensor",
+           "fp4_transposed", "thrift_forward", "THRIFT_NVFP4", "THRIFT_MXFP4", "THRIFT_GROUP_D",
+           "THRIFT_GROUP_S", "ThriftError"]
 
 
 def _ptr(t):
@@ -39,26 +40,29 @@ def _call(fn, *args):
         raise ThriftError(fn, st)
 
 
-def thrift_select_kmax(S, block_q, block_k, causal, topk_count, topk_bp) -> int:
-    return _lib.load().thrift_select_kmax(S, block_q, block_k, int(causal), topk_count, topk_bp)
+def thrift_select_kmax(S, block_q, block_k, causal, topk_count, topk_bp, Sk=None) -> int:
+    """Largest per-query-block budget; Sk (default S) keys for S queries at their end."""
+    return _lib.load().thrift_select_kmax_kv(S, S if Sk is None else Sk, block_q, block_k, int(causal),
+                                             topk_count, topk_bp)
 
 
 def thrift_select_blocks(q16, k16, block_q=128, block_k=64, causal=True, topk_count=-1,
                          topk_bp=500, kmax=None):
-    """Block means, pair scores and per-query-block top-k.  Returns (idx, cnt)."""
+    """Block means, pair scores and per-query-block top-k.  Returns (idx, cnt).
+    k16 may hold more positions than q16: the queries are then its last ones."""
     _check(q16, torch.float16, "q16")
     _check(k16, torch.float16, "k16")
     B, Hq, S, D = q16.shape
-    Hkv = k16.shape[1]
+    Hkv, Sk = k16.shape[1], k16.shape[2]
     if kmax is None:
-        kmax = max(1, thrift_select_kmax(S, block_q, block_k, causal, topk_count, topk_bp))
+        kmax = max(1, thrift_select_kmax(S, block_q, block_k, causal, topk_count, topk_bp, Sk))
     nq = -(-S // block_q)
     dev = q16.device
     idx = torch.empty((B, Hq, nq, kmax), dtype=torch.int32, device=dev)
     cnt = torch.empty((B, Hq, nq), dtype=torch.int32, device=dev)
-    wsb = _lib.load().thrift_select_workspace_bytes(B, Hq, Hkv, S, D, block_q, block_k)
+    wsb = _lib.load().thrift_select_workspace_bytes_kv(B, Hq, Hkv, S, Sk, D, block_q, block_k)
     ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
-    _call("thrift_select_blocks", _ptr(q16), _ptr(k16), B, Hq, Hkv, S, D, block_q, block_k,
+    _call("thrift_select_blocks_kv", _ptr(q16), _ptr(k16), B, Hq, Hkv, S, Sk, D, block_q, block_k,
           int(causal), topk_count, topk_bp, _ptr(idx), _ptr(cnt), kmax, _ptr(ws), wsb, _stream())
     return idx, cnt
 
@@ -130,6 +134,45 @@ def thrift_attention_fwd(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Ten
           _ptr(idx), _ptr(cnt), idx.shape[-1], B, Hq, Hkv, S, D, block_q, block_k, int(causal),
           float(sm_scale), _ptr(out), int(out.dtype == torch.float32), _ptr(lse), _stream())
     return (out, lse) if with_lse else out
+
+
+def thrift_attention_decode(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt,
+                            block_k=64, causal=True, sm_scale=None, out_fp32=False, with_lse=False,
+                            out=None):
+    """Decode-shaped forward: the Sq rows of q16 are the last positions of the
+    Sk-key cache (k16, v16 and their FP4 copies).  Returns o (and lse)."""
+    B, Hq, Sq, D = q16.shape
+    Hkv, Sk = k16.shape[1], k16.shape[2]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    for name, t in (("q16", q16), ("k16", k16), ("v16", v16)):
+        _check(t, torch.float16, name)
+    _check(idx, torch.int32, "idx")
+    _check(cnt, torch.int32, "cnt")
+    dev = q16.device
+    kmax = idx.shape[-1]
+    if out is None:
+        out = torch.empty((B, Hq, Sq, D), dtype=torch.float32 if out_fp32 else torch.float16, device=dev)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev) if with_lse else None
+    wsb = _lib.load().thrift_attention_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, kmax)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _call("thrift_attention_decode", _ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes),
+          _ptr(q4.scales), _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales),
+          _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales), _ptr(v4.tensor_scale), q4.fmt,
+          _ptr(idx), _ptr(cnt), kmax, B, Hq, Hkv, Sq, Sk, D, block_k, int(causal), float(sm_scale),
+          _ptr(out), int(out.dtype == torch.float32), _ptr(lse), _ptr(ws), wsb, _stream())
+    return (out, lse) if with_lse else out
+
+
+def thrift_decode(q16, k16, v16, k4: FP4Tensor, v4: FP4Tensor, fmt=THRIFT_MXFP4, block_q=128,
+                  block_k=64, causal=True, topk_count=-1, topk_bp=500, sm_scale=None,
+                  out_fp32=False, with_lse=False):
+    """One decode step against a dual cache (fp16 k16/v16 and their FP4 k4/v4):
+    selection, FP4 quantisation of the new queries, decode forward."""
+    idx, cnt = thrift_select_blocks(q16, k16, block_q, block_k, causal, topk_count, topk_bp)
+    q4 = thrift_quantize_fp4(q16, THRIFT_GROUP_D, fmt)
+    return thrift_attention_decode(q16, k16, v16, q4, k4, v4, idx, cnt, block_k, causal, sm_scale,
+                                   out_fp32, with_lse)
 
 
 def thrift_forward(q16, k16, v16, fmt=THRIFT_MXFP4, block_q=128, block_k=64, causal=True,

@@ -972,6 +972,267 @@ static thrift_status launch_attn(const AttnArgs& a, hipStream_t stream) {
   return launch_status();
 }
 
+// ---- decode-shaped forward: Sq new queries against an Sk-key cache ------------
+//
+// The new queries are the last Sq positions (causal masks aligned at the
+// sequence ends).  One query block holds all of them, so each query head has
+// one promoted list.  The G query heads sharing a key head and their Sq rows
+// are packed as the 32 query columns of the transposed products (column c =
+// g*Sq + r), so one K/V tile serves the whole group; the key range is split
+// across workgroups and, inside one, across its four waves (each wave its own
+// blocks of the shared stages), every wave leaving a partial (m, l, acc)
+// per column.  Promoted blocks run in one-wave units of their own (one per
+// query head and promoted block) and a last kernel merges all partials of a
+// row by their log-sum-exp.  Order does not change the result: codes and
+// fp16 roundings of P do not depend on the running maximum.
+
+struct DecodeArgs {
+  AttnArgs kv;     // K/V (S = Sk keys), Q pointers with Sq rows, idx/cnt of the one query block
+  int Sq, G, nsplit, bpw, nvalid;
+  float* part4;    // [B*Hkv*nsplit*4][G*Sq][D + 4]: acc[D], m, l, 2 pad
+  float* part16;   // [B*Hq*kmax][Sq][D + 4]
+};
+
+template <int D>
+constexpr int kPartStride = D + 4;  // floats per partial row (16-byte aligned)
+
+constexpr int kDecWaves = 4;
+
+template <int D>
+__device__ inline void store_partial(float* dst, const RowState<D>& st, int lane) {
+  // dst = this column's partial row; lanes c and c + 32 hold alternate d groups
+  const int hi = lane >> 5;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = dt * 32 + i4 * 8 + hi * 4;
+      *(float4*)(dst + d0) = make_float4(st.acc[dt][i4 * 4 + 0], st.acc[dt][i4 * 4 + 1],
+                                         st.acc[dt][i4 * 4 + 2], st.acc[dt][i4 * 4 + 3]);
+    }
+  const float lt = st.l + xlane32(st.l);
+  if (hi == 0) {
+    dst[D] = st.m;
+    dst[D + 1] = lt;
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(kDecWaves * 64, 2) void decode_fp4_kernel(DecodeArgs d) {
+  using M = MxStage<D>;
+  constexpr int NT = kDecWaves * 64;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const AttnArgs& a = d.kv;
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), hi = lane >> 5;
+  const int unit = blockIdx.x, sidx = unit % d.nsplit;
+  const size_t bhk = unit / d.nsplit;
+  const int b = (int)(bhk / a.Hkv), hk = (int)(bhk % a.Hkv);
+  const int Sk = a.S, Sq = d.Sq, G = d.G, ncol = G * Sq;
+  const int jb = sidx * d.bpw, je = min(jb + d.bpw, d.nvalid);
+  const int col = lane & 31, g = col / Sq, r = col % Sq;
+  const bool col_ok = col < ncol;
+  const int hq = hk * G + (col_ok ? g : 0);
+  const int qpos = Sk - Sq + r;
+
+  // promoted-block bits of the group's heads: [G][nwords]
+  const int nwords = (d.nvalid + 31) >> 5;
+  uint32_t* pb = (uint32_t*)(smem + 4 * M::SIZE);
+  for (int e = t; e < G * nwords; e += NT) pb[e] = 0;
+  __syncthreads();
+  for (int e = t; e < G * a.kmax; e += NT) {
+    const int gg = e / a.kmax, p = e % a.kmax;
+    const size_t row = (size_t)b * a.Hq + hk * G + gg;
+    const int c = min(max(a.cnt[row], 0), a.kmax);
+    const int j = p < c ? a.idx[row * a.kmax + p] : -1;
+    if (j >= 0 && j < d.nvalid) atomicOr(&pb[gg * nwords + (j >> 5)], 1u << (j & 31));
+  }
+
+  // this column's FP4 query operand
+  v4i qB[D / 64];
+  uint32_t qsc = 0x7F7F7F7Fu;
+  const size_t qoff = ((size_t)b * a.Hq + hq) * Sq + r;
+#pragma unroll
+  for (int kk = 0; kk < D / 64; ++kk)
+    qB[kk] = col_ok ? *(const v4i*)(a.q4c + qoff * (D / 2) + kk * 32 + hi * 16) : v4i{};
+  if (col_ok) {
+    const uint8_t* pq = a.q4s + qoff * (D / 32);
+    qsc = D == 128 ? *(const uint32_t*)pq : (uint32_t)(*(const uint16_t*)pq);
+  }
+  qsc >>= 8 * hi;
+
+  RowState<D> st;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] = v16f{};
+  st.m = kMInit;
+  st.l = 0.0f;
+  st.g = 1.0f;
+
+  // Two ring halves of four blocks (two MX stages each); wave w computes
+  // block j0 + w of every super-stage.
+  MxDma<D, kDecWaves> dma0(a, bhk, d.nvalid, w, lane, t), dma1(a, bhk, d.nvalid, w, lane, t);
+  const int nss = je > jb ? cdiv(je - jb, 4) : 0;
+  auto half = [&](int k) { return smem + (k & 1) * 2 * M::SIZE; };
+  if (nss > 0) {
+    dma0.issue(half(0), jb);
+    dma1.issue(half(0) + M::SIZE, jb + 2);
+    dma0.finish(half(0), t);
+    dma1.finish(half(0) + M::SIZE, t);
+  }
+  __syncthreads();
+  MxKOps<D> kop;
+  MxVOps<D> vop;
+  v16f sc[2];
+  for (int k = 0; k < nss; ++k) {
+    char* h = half(k);
+    const bool more = k + 1 < nss;
+    // next super-stage: issue now, store its register part after the compute
+    if (more) {
+      dma0.issue(half(k + 1), jb + 4 * (k + 1));
+      dma1.issue(half(k + 1) + M::SIZE, jb + 4 * (k + 1) + 2);
+    }
+    const int j = jb + 4 * k + w;
+    if (j < je) {
+      const char* stg = h + (w >> 1) * M::SIZE;
+      const int tb = w & 1;
+      load_k_mx<D>(kop, stg, tb, lane);
+      qk_mx<D>(sc, kop, qB, qsc);
+      const bool prom = col_ok && ((pb[g * nwords + (j >> 5)] >> (j & 31)) & 1u);
+      // Columns whose head promotes this block (the FP16 units take it) or
+      // that hold no query get probability 0.  Branch-free on purpose: a
+      // lane-divergent branch here would let the compiler sink the QK MFMAs
+      // into it, and an MFMA under a partial EXEC mask drops the inactive
+      // lanes' operands for every column.
+      const float lim = (!col_ok || prom) ? -INFINITY : INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[mt][i] = fminf(sc[mt][i], lim);
+      const int key0 = j * kBk;
+      const bool need_mask = (a.causal && key0 + kBk - 1 > Sk - Sq) || key0 + kBk > Sk;
+      load_v_mx<D>(vop, stg, tb, lane);
+      softmax_pv_mx<D>(st, sc, vop, a.sm_log2, key0, qpos, Sk, a.causal, need_mask, lane);
+    }
+    if (more) {
+      dma0.finish(half(k + 1), t);
+      dma1.finish(half(k + 1) + M::SIZE, t);
+    }
+    __syncthreads();
+  }
+  if (col_ok) {
+    const size_t u4 = (bhk * d.nsplit + sidx) * kDecWaves + w;
+    store_partial<D>(d.part4 + (u4 * ncol + col) * kPartStride<D>, st, lane);
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_f16_kernel(DecodeArgs d) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const AttnArgs& a = d.kv;
+  const int lane = threadIdx.x, hi = lane >> 5;
+  const int unit = blockIdx.x, p = unit % a.kmax;
+  const size_t bhq = unit / a.kmax;
+  const int ncnt = min(max(a.cnt[bhq], 0), a.kmax);
+  if (p >= ncnt) return;  // the merge reads units p < cnt only
+  const int b = (int)(bhq / a.Hq), hq = (int)(bhq % a.Hq);
+  const size_t bhk = (size_t)b * a.Hkv + hq / d.G;
+  const int Sk = a.S, Sq = d.Sq;
+  const int col = lane & 31, r = col < Sq ? col : 0;
+  const int qpos = Sk - Sq + r;
+  const int j = a.idx[bhq * a.kmax + p];
+
+  RowState<D> st;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] = v16f{};
+  st.m = kMInit;
+  st.l = 0.0f;
+  st.g = 1.0f;
+  if (j >= 0 && j < d.nvalid) {
+    F16Stager<D, 64> stg;
+    stg.load(a, bhk, j, lane);
+    stg.store(smem, lane);
+    __syncthreads();
+    v8h qh[D / 16];
+    const size_t qoff = (bhq * Sq + r) * D + hi * 8;
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) qh[kk] = col < Sq ? *(const v8h*)(a.q16 + qoff + kk * 16) : v8h{};
+    const int key0 = j * kBk;
+    const bool need_mask = (a.causal && key0 + kBk - 1 > Sk - Sq) || key0 + kBk > Sk;
+    fp16_tile<D>(st, smem, qh, a.sm_log2, key0, qpos, Sk, a.causal, need_mask, lane);
+  }
+  if (col < Sq) store_partial<D>(d.part16 + ((bhq * a.kmax + p) * Sq + col) * kPartStride<D>, st, lane);
+}
+
+// O and LSE of one (batch, query head, row) from every partial that holds it.
+template <int D>
+__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs d) {
+  const AttnArgs& a = d.kv;
+  const int lane = threadIdx.x;
+  const size_t row = blockIdx.x;  // (b*Hq + hq)*Sq + r
+  const int r = (int)(row % d.Sq);
+  const size_t bhq = row / d.Sq;
+  const int b = (int)(bhq / a.Hq), hq = (int)(bhq % a.Hq);
+  const size_t bhk = (size_t)b * a.Hkv + hq / d.G;
+  const int ncol = d.G * d.Sq, col = (hq % d.G) * d.Sq + r;
+  const int n4 = d.nsplit * kDecWaves;
+  const int n16 = min(max(a.cnt[bhq], 0), a.kmax);
+  auto p4 = [&](int u) { return d.part4 + ((bhk * n4 + u) * ncol + col) * kPartStride<D>; };
+  auto p16 = [&](int u) { return d.part16 + ((bhq * a.kmax + u) * d.Sq + r) * kPartStride<D>; };
+  float M = kMInit;
+  for (int u = 0; u < n4; ++u) M = fmaxf(M, p4(u)[D]);
+  for (int u = 0; u < n16; ++u) M = fmaxf(M, p16(u)[D]);
+  float l = 0.0f, acc[D / 64];
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) acc[e] = 0.0f;
+  auto add = [&](const float* q) {
+    const float f = exp2f(q[D] - M);  // partial offsets are integers: exact powers of two
+    l += f * q[D + 1];
+#pragma unroll
+    for (int e = 0; e < D / 64; ++e) acc[e] += f * q[lane + 64 * e];
+  };
+  for (int u = 0; u < n4; ++u) add(p4(u));
+  for (int u = 0; u < n16; ++u) add(p16(u));
+  const float inv = 1.0f / l;
+  const size_t ob = row * D;
+#pragma unroll
+  for (int e = 0; e < D / 64; ++e) {
+    const float x = acc[e] * inv;
+    if (a.o_fp32)
+      ((float*)a.o)[ob + lane + 64 * e] = x;
+    else
+      ((_Float16*)a.o)[ob + lane + 64 * e] = (_Float16)x;
+  }
+  if (a.lse && lane == 0) a.lse[row] = (M + log2f(l)) * kLn2;
+}
+
+// Work split: about two workgroups per compute unit, at least one block per
+// wave, a multiple of four blocks per workgroup.
+inline void decode_split(int B, int Hkv, int nvalid, int& nsplit, int& bpw) {
+  int want = cdiv(512, B * Hkv);
+  want = want < 1 ? 1 : want;
+  const int most = cdiv(nvalid, kDecWaves);
+  want = want > most ? most : want;
+  bpw = cdiv(cdiv(nvalid, want), kDecWaves) * kDecWaves;
+  nsplit = cdiv(nvalid, bpw);
+}
+
+// Every kernel the entry points launch, instantiated explicitly (the host
+// compiler does not always emit the launch stubs of templates used only
+// through launch helpers).
+template __global__ void attn_fwd_kernel<128, 4, THRIFT_MXFP4>(AttnArgs);
+template __global__ void attn_fwd_kernel<128, 2, THRIFT_MXFP4>(AttnArgs);
+template __global__ void attn_fwd_kernel<64, 4, THRIFT_MXFP4>(AttnArgs);
+template __global__ void attn_fwd_kernel<64, 2, THRIFT_MXFP4>(AttnArgs);
+template __global__ void attn_fwd_kernel<128, 4, THRIFT_NVFP4>(AttnArgs);
+template __global__ void attn_fwd_kernel<128, 2, THRIFT_NVFP4>(AttnArgs);
+template __global__ void attn_fwd_kernel<64, 4, THRIFT_NVFP4>(AttnArgs);
+template __global__ void attn_fwd_kernel<64, 2, THRIFT_NVFP4>(AttnArgs);
+template __global__ void decode_fp4_kernel<128>(DecodeArgs);
+template __global__ void decode_fp4_kernel<64>(DecodeArgs);
+template __global__ void decode_f16_kernel<128>(DecodeArgs);
+template __global__ void decode_f16_kernel<64>(DecodeArgs);
+template __global__ void decode_merge_kernel<128>(DecodeArgs);
+template __global__ void decode_merge_kernel<64>(DecodeArgs);
+
 }  // namespace thrift
 
 using namespace thrift;
@@ -1033,6 +1294,110 @@ extern "C" thrift_status thrift_attention_fwd(
   }
   if (D == 128) return block_q == 128 ? launch_attn<128, 4, THRIFT_NVFP4>(a, stream) : launch_attn<128, 2, THRIFT_NVFP4>(a, stream);
   return block_q == 128 ? launch_attn<64, 4, THRIFT_NVFP4>(a, stream) : launch_attn<64, 2, THRIFT_NVFP4>(a, stream);
+}
+
+static size_t decode_part_floats(int B, int Hq, int Hkv, int Sq, int Sk, int D, int kmax,
+                                 size_t* n4_out) {
+  int nsplit, bpw;
+  decode_split(B, Hkv, cdiv(Sk, 64), nsplit, bpw);
+  const size_t stride = (size_t)D + 4;
+  const size_t n4 = (size_t)B * Hkv * nsplit * kDecWaves * (Hq / Hkv) * Sq * stride;
+  const size_t n16 = (size_t)B * Hq * kmax * Sq * stride;
+  if (n4_out) *n4_out = n4;
+  return n4 + n16;
+}
+
+extern "C" size_t thrift_attention_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                                          int kmax) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || Sq < 1 || Sk < Sq || D < 1 || kmax < 1) return 0;
+  return decode_part_floats(B, Hq, Hkv, Sq, Sk, D, kmax, nullptr) * sizeof(float);
+}
+
+template <int D>
+static thrift_status launch_decode(DecodeArgs& d, hipStream_t stream) {
+  using M = MxStage<D>;
+  const AttnArgs& a = d.kv;
+  static bool configured = false;
+  if (!configured) {
+    if (hipFuncSetAttribute((const void*)decode_fp4_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024) != hipSuccess ||
+        hipFuncSetAttribute((const void*)decode_f16_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
+                            160 * 1024) != hipSuccess)
+      return THRIFT_EHIP;
+    configured = true;
+  }
+  const size_t lds4 = 4 * (size_t)M::SIZE + (size_t)d.G * ((d.nvalid + 31) / 32) * 4;
+  decode_fp4_kernel<D><<<a.B * a.Hkv * d.nsplit, kDecWaves * 64, lds4, stream>>>(d);
+  decode_f16_kernel<D><<<a.B * a.Hq * a.kmax, 64, Lds<D>::STAGE, stream>>>(d);
+  decode_merge_kernel<D><<<a.B * a.Hq * d.Sq, 64, 0, stream>>>(d);
+  return launch_status();
+}
+
+extern "C" thrift_status thrift_attention_decode(
+    const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes,
+    const uint8_t* q4_scales, const float* q4_tscale, const uint8_t* k4_codes,
+    const uint8_t* k4_scales, const float* k4_tscale, const uint8_t* v4_codes,
+    const uint8_t* v4_scales, const float* v4_tscale, thrift_format fmt, const int32_t* idx,
+    const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int Sq, int Sk, int D, int block_k,
+    int causal, float sm_scale, void* o, int o_is_fp32, float* lse, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  if (!q16 || !k16 || !v16 || !q4_codes || !q4_scales || !k4_codes || !k4_scales || !v4_codes ||
+      !v4_scales || !idx || !cnt || !o || !workspace)
+    return THRIFT_EINVAL;
+  if (fmt != THRIFT_NVFP4 && fmt != THRIFT_MXFP4) return THRIFT_EINVAL;
+  if (fmt != THRIFT_MXFP4) return THRIFT_EUNSUPPORTED;
+  (void)q4_tscale;
+  (void)k4_tscale;
+  (void)v4_tscale;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < Sq || kmax < 1 || (causal != 0 && causal != 1))
+    return THRIFT_EINVAL;
+  if (Hq % Hkv != 0 || (o_is_fp32 != 0 && o_is_fp32 != 1)) return THRIFT_EINVAL;
+  if (!(sm_scale > 0.0f) || !(sm_scale < 1e30f)) return THRIFT_EINVAL;
+  if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
+  if (block_k != 64 || (Hq / Hkv) * Sq > 32 || Sq > 128) return THRIFT_EUNSUPPORTED;
+  if (Sk > 262144 || kmax > cdiv(Sk, block_k)) return THRIFT_EUNSUPPORTED;
+  for (const void* p : {q16, k16, v16, (const void*)q4_codes, (const void*)k4_codes,
+                        (const void*)v4_codes, (const void*)o, (const void*)workspace})
+    if (!aligned16(p)) return THRIFT_EALIGN;
+  if (((uintptr_t)q4_scales | (uintptr_t)k4_scales | (uintptr_t)v4_scales) & 3) return THRIFT_EALIGN;
+  size_t n4 = 0;
+  const size_t need = decode_part_floats(B, Hq, Hkv, Sq, Sk, D, kmax, &n4) * sizeof(float);
+  if (workspace_bytes < need) return THRIFT_EWORKSPACE;
+  DecodeArgs d;
+  AttnArgs& a = d.kv;
+  a.q16 = (const _Float16*)q16;
+  a.k16 = (const _Float16*)k16;
+  a.v16 = (const _Float16*)v16;
+  a.q4c = q4_codes;
+  a.q4s = q4_scales;
+  a.q4t = nullptr;
+  a.k4c = k4_codes;
+  a.k4s = k4_scales;
+  a.k4t = nullptr;
+  a.v4c = v4_codes;
+  a.v4s = v4_scales;
+  a.v4t = nullptr;
+  a.idx = idx;
+  a.cnt = cnt;
+  a.o = o;
+  a.lse = lse;
+  a.kmax = kmax;
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.S = Sk;
+  a.Sp = cdiv(Sk, 64) * 64;
+  a.nq = 1;
+  a.causal = causal;
+  a.o_fp32 = o_is_fp32;
+  a.sm_log2 = sm_scale * 1.4426950408889634f;
+  d.Sq = Sq;
+  d.G = Hq / Hkv;
+  d.nvalid = valid_kv_blocks_kv(0, Sq, Sk, 128, 64, causal);
+  decode_split(B, Hkv, d.nvalid, d.nsplit, d.bpw);
+  d.part4 = (float*)workspace;
+  d.part16 = (float*)workspace + n4;
+  return D == 128 ? launch_decode<128>(d, stream) : launch_decode<64>(d, stream);
 }
 
 extern "C" const char* thrift_status_string(thrift_status s) {

@@ -21,13 +21,18 @@ constexpr int kWave = 64;
 
 __host__ __device__ inline int cdiv(int a, int b) { return (a + b - 1) / b; }
 
-// Number of valid key blocks of query block i (causal: query and key
-// sequences aligned at their starts; a block is valid when it holds a key not
-// after the query block's last row).
+// Number of valid key blocks of query block i for Sq queries against Sk keys
+// (Sq <= Sk; causal: the queries are the last Sq positions of the key
+// sequence, so that for Sq = Sk the two are aligned at their starts; a block
+// is valid when it holds a key not after the query block's last row).
+__host__ __device__ inline int valid_kv_blocks_kv(int i, int Sq, int Sk, int bq, int bk, int causal) {
+  if (!causal) return cdiv(Sk, bk);
+  int last = (i + 1) * bq < Sq ? (i + 1) * bq - 1 : Sq - 1;
+  return (Sk - Sq + last) / bk + 1;
+}
+
 __host__ __device__ inline int valid_kv_blocks(int i, int S, int bq, int bk, int causal) {
-  if (!causal) return cdiv(S, bk);
-  int last = (i + 1) * bq < S ? (i + 1) * bq - 1 : S - 1;
-  return last / bk + 1;
+  return valid_kv_blocks_kv(i, S, S, bq, bk, causal);
 }
 
 // Promoted-block budget of a query block with n valid key blocks.

@@ -131,7 +131,7 @@ constexpr int kDimChunk = 32;     // channels staged per pass
 
 template <int D>
 __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
-    const float* __restrict__ qm, const float* __restrict__ km, int Hq, int Hkv, int S, int bq,
+    const float* __restrict__ qm, const float* __restrict__ km, int Hq, int Hkv, int Sq, int Sk, int bq,
     int bk, int causal, int topk_count, int topk_bp, int32_t* __restrict__ idx,
     int32_t* __restrict__ cnt, int kmax) {
   extern __shared__ float sc[];  // [kHeadChunk][nK] scores
@@ -141,8 +141,8 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int i = blockIdx.x, bhk = blockIdx.y;
   const int b = bhk / Hkv, hk = bhk % Hkv, G = Hq / Hkv;
-  const int nq = cdiv(S, bq), nK = cdiv(S, bk);
-  const int n = valid_kv_blocks(i, S, bq, bk, causal);
+  const int nq = cdiv(Sq, bq), nK = cdiv(Sk, bk);
+  const int n = valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal);
   const int k = topk_budget(n, topk_count, topk_bp);
   const float* kbase = km + (size_t)bhk * nK * D;
 
@@ -192,44 +192,54 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
 
 using namespace thrift;
 
-extern "C" int thrift_select_kmax(int S, int block_q, int block_k, int causal, int topk_count,
-                                  int topk_bp) {
-  if (S < 1 || block_q < 1 || block_k < 1 || (topk_count < 0 && topk_bp < 0)) return -1;
-  int nq = cdiv(S, block_q), km = 0;
+extern "C" int thrift_select_kmax_kv(int Sq, int Sk, int block_q, int block_k, int causal,
+                                     int topk_count, int topk_bp) {
+  if (Sq < 1 || Sk < Sq || block_q < 1 || block_k < 1 || (topk_count < 0 && topk_bp < 0)) return -1;
+  int nq = cdiv(Sq, block_q), km = 0;
   for (int i = 0; i < nq; ++i) {
-    int k = topk_budget(valid_kv_blocks(i, S, block_q, block_k, causal), topk_count, topk_bp);
+    int k = topk_budget(valid_kv_blocks_kv(i, Sq, Sk, block_q, block_k, causal), topk_count, topk_bp);
     km = k > km ? k : km;
   }
   return km;
 }
 
-extern "C" size_t thrift_select_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int block_q,
-                                                int block_k) {
-  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1 || block_q < 1 || block_k < 1) return 0;
-  size_t qbytes = (size_t)B * Hq * cdiv(S, block_q) * D * sizeof(float);
-  size_t kbytes = (size_t)B * Hkv * cdiv(S, block_k) * D * sizeof(float);
+extern "C" int thrift_select_kmax(int S, int block_q, int block_k, int causal, int topk_count,
+                                  int topk_bp) {
+  return thrift_select_kmax_kv(S, S, block_q, block_k, causal, topk_count, topk_bp);
+}
+
+extern "C" size_t thrift_select_workspace_bytes_kv(int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                                   int block_q, int block_k) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < 1 || D < 1 || block_q < 1 || block_k < 1) return 0;
+  size_t qbytes = (size_t)B * Hq * cdiv(Sq, block_q) * D * sizeof(float);
+  size_t kbytes = (size_t)B * Hkv * cdiv(Sk, block_k) * D * sizeof(float);
   return ((qbytes + 255) / 256) * 256 + kbytes;
 }
 
-extern "C" thrift_status thrift_select_blocks(const void* q16, const void* k16, int B, int Hq,
-                                              int Hkv, int S, int D, int block_q, int block_k,
-                                              int causal, int topk_count, int topk_bp,
-                                              int32_t* idx, int32_t* cnt, int kmax,
-                                              void* workspace, size_t workspace_bytes,
-                                              hipStream_t stream) {
+extern "C" size_t thrift_select_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int block_q,
+                                                int block_k) {
+  return thrift_select_workspace_bytes_kv(B, Hq, Hkv, S, S, D, block_q, block_k);
+}
+
+extern "C" thrift_status thrift_select_blocks_kv(const void* q16, const void* k16, int B, int Hq,
+                                                 int Hkv, int Sq, int Sk, int D, int block_q,
+                                                 int block_k, int causal, int topk_count,
+                                                 int topk_bp, int32_t* idx, int32_t* cnt, int kmax,
+                                                 void* workspace, size_t workspace_bytes,
+                                                 hipStream_t stream) {
   if (!q16 || !k16 || !idx || !cnt || !workspace) return THRIFT_EINVAL;
-  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || (causal != 0 && causal != 1)) return THRIFT_EINVAL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < Sq || (causal != 0 && causal != 1)) return THRIFT_EINVAL;
   if (Hq % Hkv != 0) return THRIFT_EINVAL;
   if (topk_count < 0 && (topk_bp < 0 || topk_bp > 10000)) return THRIFT_EINVAL;
   if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
   if ((block_q != 64 && block_q != 128) || block_k != 64) return THRIFT_EUNSUPPORTED;
-  if (S > 262144) return THRIFT_EUNSUPPORTED;
-  int need = thrift_select_kmax(S, block_q, block_k, causal, topk_count, topk_bp);
+  if (Sk > 262144) return THRIFT_EUNSUPPORTED;
+  int need = thrift_select_kmax_kv(Sq, Sk, block_q, block_k, causal, topk_count, topk_bp);
   if (kmax < need || kmax < 1) return THRIFT_EINVAL;
   if (!aligned16(q16) || !aligned16(k16) || !aligned16(workspace)) return THRIFT_EALIGN;
-  if (workspace_bytes < thrift_select_workspace_bytes(B, Hq, Hkv, S, D, block_q, block_k))
+  if (workspace_bytes < thrift_select_workspace_bytes_kv(B, Hq, Hkv, Sq, Sk, D, block_q, block_k))
     return THRIFT_EWORKSPACE;
-  const int nq = cdiv(S, block_q), nk = cdiv(S, block_k);
+  const int nq = cdiv(Sq, block_q), nk = cdiv(Sk, block_k);
   float* qm = (float*)workspace;
   size_t qbytes = (size_t)B * Hq * nq * D * sizeof(float);
   float* km = (float*)((char*)workspace + ((qbytes + 255) / 256) * 256);
@@ -246,15 +256,25 @@ extern "C" thrift_status thrift_select_blocks(const void* q16, const void* k16, 
     configured = true;
   }
   if (D == 128) {
-    block_means_kernel<128><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, S, block_q, nq, qm);
-    block_means_kernel<128><<<dim3(nk, B * Hkv), kMeansThreads, 0, stream>>>(k, S, block_k, nk, km);
+    block_means_kernel<128><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, Sq, block_q, nq, qm);
+    block_means_kernel<128><<<dim3(nk, B * Hkv), kMeansThreads, 0, stream>>>(k, Sk, block_k, nk, km);
     score_topk_kernel<128><<<dim3(nq, B * Hkv), kTopkThreads, lds, stream>>>(
-        qm, km, Hq, Hkv, S, block_q, block_k, causal, topk_count, topk_bp, idx, cnt, kmax);
+        qm, km, Hq, Hkv, Sq, Sk, block_q, block_k, causal, topk_count, topk_bp, idx, cnt, kmax);
   } else {
-    block_means_kernel<64><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, S, block_q, nq, qm);
-    block_means_kernel<64><<<dim3(nk, B * Hkv), kMeansThreads, 0, stream>>>(k, S, block_k, nk, km);
+    block_means_kernel<64><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, Sq, block_q, nq, qm);
+    block_means_kernel<64><<<dim3(nk, B * Hkv), kMeansThreads, 0, stream>>>(k, Sk, block_k, nk, km);
     score_topk_kernel<64><<<dim3(nq, B * Hkv), kTopkThreads, lds, stream>>>(
-        qm, km, Hq, Hkv, S, block_q, block_k, causal, topk_count, topk_bp, idx, cnt, kmax);
+        qm, km, Hq, Hkv, Sq, Sk, block_q, block_k, causal, topk_count, topk_bp, idx, cnt, kmax);
   }
   return launch_status();
+}
+
+extern "C" thrift_status thrift_select_blocks(const void* q16, const void* k16, int B, int Hq,
+                                              int Hkv, int S, int D, int block_q, int block_k,
+                                              int causal, int topk_count, int topk_bp,
+                                              int32_t* idx, int32_t* cnt, int kmax,
+                                              void* workspace, size_t workspace_bytes,
+                                              hipStream_t stream) {
+  return thrift_select_blocks_kv(q16, k16, B, Hq, Hkv, S, S, D, block_q, block_k, causal, topk_count,
+                                 topk_bp, idx, cnt, kmax, workspace, workspace_bytes, stream);
 }

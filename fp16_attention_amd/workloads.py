@@ -40,6 +40,7 @@ class Workload:
     dist: str  # "gauss_outliers" | "heavy" | "ar1"
     sink: bool = False
     planted: int = 0
+    Sq: int = 0  # > 0: decode shape, the last Sq positions are the queries (S = cache length)
     extra: dict = field(default_factory=dict)
 
     def with_(self, **kw) -> "Workload":
@@ -60,6 +61,10 @@ WORKLOADS = {
     "verylong": Workload("verylong", 1, 8, 2, 131072, 128, True, 128, 64, -1, 200, MX, 5, "heavy"),
     # non-causal video-DiT shape with smooth AR(1) queries and keys, ragged tail
     "dit": Workload("dit", 1, 24, 24, 17550, 64, False, 128, 64, -1, 500, MX, 6, "ar1"),
+    # decode: one new token per sequence against a 32K-token cache (GQA 32/8,
+    # the long-context distribution with its sink), 5% of the key blocks in FP16
+    "decode": Workload("decode", 8, 32, 8, 32768, 128, True, 128, 64, -1, 500, MX, 7, "heavy",
+                       sink=True, Sq=1),
 }
 
 
@@ -88,32 +93,34 @@ def _ar1(rng, B, H, S, D, rho=0.9):
 
 
 def generate(w: Workload):
-    """Return dict(q, k, v) of fp16 arrays [B, H, S, D] plus 'planted' pairs."""
+    """Return dict(q, k, v) of fp16 arrays [B, H, S, D] plus 'planted' pairs;
+    for a decode shape (w.Sq > 0) q holds w.Sq positions, the last ones."""
     rng = np.random.default_rng(w.seed)
     B, Hq, Hkv, S, D = w.B, w.Hq, w.Hkv, w.S, w.D
+    Sq = w.Sq if w.Sq else S
     planted = []
     if w.dist == "gauss_outliers":
-        q = rng.standard_normal((B, Hq, S, D))
+        q = rng.standard_normal((B, Hq, Sq, D))
         k = rng.standard_normal((B, Hkv, S, D))
         v = rng.standard_normal((B, Hkv, S, D))
         for t in (q, k, v):  # two outlier channels in distinct 16- and 32-groups
             t[..., 5] *= 20.0
             t[..., 40 % D] *= 20.0
     elif w.dist == "heavy":
-        q = _heavy(rng, B, Hq, S, D)
+        q = _heavy(rng, B, Hq, Sq, D)
         k = _heavy(rng, B, Hkv, S, D)
         v = _heavy(rng, B, Hkv, S, D)
     elif w.dist == "ar1":
-        q = _ar1(rng, B, Hq, S, D)
+        q = _ar1(rng, B, Hq, Sq, D)
         k = _ar1(rng, B, Hkv, S, D)
         v = rng.standard_normal((B, Hkv, S, D))
     else:
         raise ValueError(w.dist)
     if w.sink:  # the first key block carries an attention sink: norm x8
         k[:, :, : min(w.bk, S)] *= 8.0
-    if w.planted:
+    if w.planted and not w.Sq:
         planted = _plant(rng, w, q, k)
-    return dict(q=_to_half(q), k=_to_half(k), v=_to_half(v), planted=planted)
+    return dict(q=_to_half(np.ascontiguousarray(q)), k=_to_half(k), v=_to_half(v), planted=planted)
 
 
 def _block_mean(x, blk):

@@ -111,6 +111,22 @@ thrift_status thrift_select_blocks(const void* q16, const void* k16, int B, int 
                                    int topk_bp, int32_t* idx, int32_t* cnt, int kmax,
                                    void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* Selection for Sq queries that are the last Sq positions of an Sk-key
+ * sequence (Sq <= Sk; decode: new tokens against the KV cache).  Everything
+ * as thrift_select_blocks with q16 [B,Hq,Sq,D] and k16 [B,Hkv,Sk,D]; nQ =
+ * ceil(Sq/block_q); under causal masking query block i may see key block j
+ * when j*block_k <= Sk - Sq + min(Sq,(i+1)*block_q) - 1.  The three calls
+ * above are the Sq = Sk case of these. */
+int thrift_select_kmax_kv(int Sq, int Sk, int block_q, int block_k, int causal, int topk_count,
+                          int topk_bp);
+size_t thrift_select_workspace_bytes_kv(int B, int Hq, int Hkv, int Sq, int Sk, int D, int block_q,
+                                        int block_k);
+thrift_status thrift_select_blocks_kv(const void* q16, const void* k16, int B, int Hq, int Hkv,
+                                      int Sq, int Sk, int D, int block_q, int block_k, int causal,
+                                      int topk_count, int topk_bp, int32_t* idx, int32_t* cnt,
+                                      int kmax, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
 /* ---------------------------------------------------------------------- */
 /* FP4 quantisation (the FP4 path's NVFP4 micro-scaling)                    */
 /* ---------------------------------------------------------------------- */
@@ -173,6 +189,44 @@ thrift_status thrift_attention_fwd(const void* q16, const void* k16, const void*
                                    const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S,
                                    int D, int block_q, int block_k, int causal, float sm_scale,
                                    void* o, int o_is_fp32, float* lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
+/* Decode-shaped forward (new tokens against the dual FP16/FP4 KV cache;    */
+/* decode results in "Resultaten", the cache in "Betekenis en Beweringen")  */
+/* ---------------------------------------------------------------------- */
+
+/* Workspace bytes thrift_attention_decode needs (per-split partial results). */
+size_t thrift_attention_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                                               int kmax);
+
+/* The forward pass of thrift_attention_fwd for Sq new queries that are the
+ * last Sq positions of an Sk-key sequence (causal masks aligned at the
+ * ends: query row r sees keys <= Sk - Sq + r), computed split over the keys
+ * and merged by log-sum-exp.  Same per-row arithmetic, so the same result up
+ * to fp32 rounding order.
+ *   q16 [B,Hq,Sq,D], k16/v16 [B,Hkv,Sk,D] fp16 (required);
+ *   q4_*: Q along THRIFT_GROUP_D (S = Sq); k4_*, v4_*: the cache's K and V
+ *     along THRIFT_GROUP_D / THRIFT_GROUP_S (S = Sk);
+ *   idx [B,Hq,1,kmax], cnt [B,Hq,1]: thrift_select_blocks_kv with one query
+ *     block (block_q >= Sq);
+ *   o [B,Hq,Sq,D] (fp16 or fp32), lse [B,Hq,Sq] (may be NULL);
+ *   workspace: device buffer of at least
+ *     thrift_attention_decode_workspace_bytes(...), caller-owned, 16-byte
+ *     aligned; its contents are scratch.
+ * Supported: THRIFT_MXFP4 (THRIFT_NVFP4 returns THRIFT_EUNSUPPORTED), D 64 or
+ * 128, block_k 64, Sq <= 128 and (Hq/Hkv)*Sq <= 32 (the query heads of a key
+ * head and their rows share one 32-column tile), Sk <= 262144. */
+thrift_status thrift_attention_decode(const void* q16, const void* k16, const void* v16,
+                                      const uint8_t* q4_codes, const uint8_t* q4_scales,
+                                      const float* q4_tscale, const uint8_t* k4_codes,
+                                      const uint8_t* k4_scales, const float* k4_tscale,
+                                      const uint8_t* v4_codes, const uint8_t* v4_scales,
+                                      const float* v4_tscale, thrift_format fmt,
+                                      const int32_t* idx, const int32_t* cnt, int kmax, int B,
+                                      int Hq, int Hkv, int Sq, int Sk, int D, int block_k,
+                                      int causal, float sm_scale, void* o, int o_is_fp32,
+                                      float* lse, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
 
 /* Static string for a status code (host). */
 const char* thrift_status_string(thrift_status s);

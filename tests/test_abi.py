@@ -100,3 +100,33 @@ def test_attention_validation(lib):
     assert call(kmax=9) == 2  # more than the 8 key blocks of S = 512
     assert call(o=A + 2) == 3
     assert call(o32=3) == 1
+
+
+def test_kmax_kv_matches_oracle(lib, oracle):
+    for Sq, Sk, bq, causal, bp in [(1, 32768, 128, 1, 500), (5, 513, 128, 1, 2500), (64, 300, 64, 1, 1000),
+                                   (16, 1000, 128, 0, 500), (1000, 1000, 128, 1, 500)]:
+        assert lib.thrift_select_kmax_kv(Sq, Sk, bq, 64, causal, -1, bp) == oracle.kmax(Sq, bq, 64, causal, -1, bp, Sk)
+    assert lib.thrift_select_kmax_kv(10, 5, 128, 64, 1, -1, 500) == -1  # more queries than keys
+    assert lib.thrift_select_kmax(1000, 128, 64, 1, -1, 500) == lib.thrift_select_kmax_kv(1000, 1000, 128, 64, 1, -1, 500)
+
+
+def test_decode_validation(lib):
+    f = lib.thrift_attention_decode
+
+    def call(q16=A, fmt=1, kmax=4, B=1, Hq=8, Hkv=2, Sq=1, Sk=512, D=128, bk=64, causal=1, sm=0.088,
+             o=A, o32=1, ws=A, wsb=1 << 30):
+        return f(q16, A, A, A, A, None, A, A, None, A, A, None, fmt, A, A, kmax, B, Hq, Hkv, Sq, Sk, D, bk,
+                 causal, sm, o, o32, None, ws, wsb, None)
+
+    assert call(q16=None) == 1
+    assert call(ws=None) == 1
+    assert call(fmt=0) == 2  # NVFP4 decode is not built
+    assert call(fmt=5) == 1
+    assert call(Sq=600) == 1  # more queries than keys
+    assert call(Sq=9, Hq=8, Hkv=2) == 2  # 4 heads x 9 rows > 32 columns
+    assert call(D=96) == 2
+    assert call(kmax=9) == 2
+    assert call(o=A + 4) == 3
+    assert call(wsb=16) == 4
+    need = lib.thrift_attention_decode_workspace_bytes(1, 8, 2, 1, 512, 128, 4)
+    assert need > 0 and call(wsb=need) != 4

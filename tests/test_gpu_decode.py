@@ -1,0 +1,91 @@
+"""GPU parity of the decode-shaped forward (thrift_select_blocks_kv,
+thrift_attention_decode) against the CPU oracle, through the C ABI.
+
+Bit-exact: selected blocks, counts and FP4 codes/scales.  Output: fp32 O and
+LSE to the bounds of the prefill parity tests (max-abs 2e-3 beyond the
+oracle's evaluation uncertainty u, rel-L2 1e-3).  Sizes span one to several
+workgroup key splits, ragged cache lengths, GQA packing of several heads and
+rows into one query tile, both masks, and the budget extremes; the last case
+is the decode workload at full size, every row compared.
+"""
+import numpy as np
+import pytest
+
+from fp16_attention_amd import workloads as W
+from tests.gpu_harness import compare_out, note, same_fp4
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    # name: (B, Hq, Hkv, Sq, Sk, D, causal, topk_bp)
+    "one_token_gqa4": (2, 8, 2, 1, 2048, 128, True, 500),
+    "rows5_ragged": (1, 4, 1, 5, 1000, 128, True, 1000),
+    "rows8_gqa4": (1, 8, 2, 8, 4096, 128, True, 500),
+    "d64_noncausal": (1, 4, 2, 3, 777, 64, False, 2500),
+    "no_fp16": (1, 8, 2, 2, 1500, 128, True, 0),
+    "all_fp16": (1, 4, 4, 4, 640, 128, True, 10000),
+    "short_cache": (1, 2, 1, 16, 40, 128, True, 5000),
+    "g32_one_token": (1, 32, 1, 1, 3000, 128, True, 500),
+}
+
+
+def _run(oracle, w, bp):
+    import torch
+
+    from fp16_attention_amd import api
+
+    d = W.generate(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(d[n])).to(dev) for n in ("q", "k", "v"))
+    idx, cnt = api.thrift_select_blocks(q, k, 128, 64, w.causal, -1, bp)
+    q4 = api.thrift_quantize_fp4(q, api.THRIFT_GROUP_D, api.THRIFT_MXFP4)
+    k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, api.THRIFT_MXFP4)
+    v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, api.THRIFT_MXFP4)
+    o, lse = api.thrift_attention_decode(q, k, v, q4, k4, v4, idx, cnt, 64, w.causal, out_fp32=True,
+                                         with_lse=True)
+    torch.cuda.synchronize()
+    r = oracle.pipeline(d["q"], d["k"], d["v"], oracle.MX, 128, 64, w.causal, -1, bp)
+    g_cnt, g_idx = cnt.cpu().numpy(), idx.cpu().numpy()
+    assert np.array_equal(g_cnt, r["cnt"]), "cnt differs"
+    km = r["idx"].shape[-1]
+    assert np.array_equal(g_idx[..., :km], r["idx"]), "idx differs"
+    assert np.all(g_idx[..., km:] == -1)
+    same_fp4(q4, r["q4"])
+    same_fp4(k4, r["k4"])
+    same_fp4(v4, r["v4"])
+    compare_out(o.cpu().numpy().astype(np.float64), r["o"], lse.cpu().numpy().astype(np.float64),
+                r["lse"], r["u"])
+    return o, r
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_decode_parity(oracle, name):
+    B, Hq, Hkv, Sq, Sk, D, causal, bp = CASES[name]
+    w = W.WORKLOADS["decode"].with_(B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, S=Sk, D=D, causal=causal, topk_bp=bp,
+                                    seed=len(name))
+    note(f"[decode] {name}: B{B} Hq{Hq} Hkv{Hkv} Sq{Sq} Sk{Sk} D{D} causal{int(causal)} bp{bp}")
+    _run(oracle, w, bp)
+
+
+def test_decode_fp16_output_matches_fp32(oracle):
+    import torch
+
+    from fp16_attention_amd import api
+
+    w = W.WORKLOADS["decode"].with_(B=1, Hq=8, Hkv=2, Sq=2, S=1100, seed=11)
+    d = W.generate(w)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(d[n])).to(dev) for n in ("q", "k", "v"))
+    k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, api.THRIFT_MXFP4)
+    v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, api.THRIFT_MXFP4)
+    o32 = api.thrift_decode(q, k, v, k4, v4, out_fp32=True)
+    o16 = api.thrift_decode(q, k, v, k4, v4)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(o16.cpu().numpy(), o32.cpu().numpy().astype(np.float16))
+
+
+@pytest.mark.slow
+def test_decode_full_size(oracle):
+    w = W.WORKLOADS["decode"]
+    note(f"[decode] full size: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} Sk{w.S} D{w.D} bp{w.topk_bp}")
+    _run(oracle, w, w.topk_bp)
