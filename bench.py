@@ -18,7 +18,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_fwd_kernel_long_mx_traffic.txt")
+# committed profiler counters, per (workload, format) that has them
+TRAFFIC_FILES = {("long", "mx"): os.path.join(ROOT, "profiles", "attn_fwd_kernel_long_mx_traffic.txt"),
+                 ("decode", "mx"): os.path.join(ROOT, "profiles", "decode_kernels_decode_mx_traffic.txt")}
 KERNEL_SRC = os.path.join(ROOT, "fp16_attention_amd", "csrc", "attention.hip")
 
 P_FP4 = 10.1e15   # MI355X dense MXFP4 MFMA, FLOP/s
@@ -60,16 +62,17 @@ def promoted_pairs(idx, cnt, S, bq, bk, causal):
 
 
 def measured_traffic(workload, fmt_name):
-    """HBM bytes per attention launch from the committed profiler counters
+    """HBM bytes per forward from the committed profiler counters
     (FETCH_SIZE + WRITE_SIZE, each scaled by its reading on a copy kernel of
-    known size), or None when they were taken on another workload or on an
-    attention kernel source other than the one built now."""
+    known size), or None when none were taken on this workload or they were
+    taken on an attention kernel source other than the one built now."""
     import hashlib
 
-    if (workload, fmt_name) != ("long", "mx") or not os.path.exists(TRAFFIC_FILE):
+    path = TRAFFIC_FILES.get((workload, fmt_name))
+    if path is None or not os.path.exists(path):
         return None
     rec = {}
-    with open(TRAFFIC_FILE) as f:
+    with open(path) as f:
         for ln in f:
             if ":" in ln and not ln.startswith((" ", "#", "|")):
                 k, v = ln.split(":", 1)
@@ -79,6 +82,16 @@ def measured_traffic(workload, fmt_name):
     if rec.get("kernel_source_sha256") != h:
         return None
     return int(rec["traffic_bytes_per_launch"])
+
+
+def copy_calibration(torch, dev, mib):
+    """One plain device copy of mib MiB: a kernel whose HBM traffic is known."""
+    src = torch.empty(mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def algorithmic_bytes(w, p16_tiles_q, fmt):
@@ -126,6 +139,8 @@ def main():
     t0 = time.time()
     d = W.generate(w)
     gen_s = time.time() - t0
+    if w.Sq:
+        return run_decode(args, w, d, gen_s)
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v"))
     kmax = max(1, api.thrift_select_kmax(w.S, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp))
@@ -133,12 +148,7 @@ def main():
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
     if args.copy_mib:
-        src = torch.empty(args.copy_mib << 18, dtype=torch.float32, device=dev).fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration(torch, dev, args.copy_mib)
 
     def step(rec=None):
         if rec:
@@ -221,6 +231,123 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(w, d, fmt)
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(s + "\n")
+
+
+def run_decode(args, w, d, gen_s):
+    """Decode step: selection of the new rows against the cache, FP4
+    quantisation of the new rows, decode forward.  The cache's FP4 copy is
+    built once before timing (cache maintenance; appending one token's codes
+    per step is negligible).  HBM-bound: the roofline is 8 TB/s on the
+    algorithmic bytes of the decode forward."""
+    import torch
+
+    from fp16_attention_amd import api
+
+    if args.fmt != "mx":
+        print("bench.py: the decode forward runs MXFP4 only", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v"))
+    k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, api.THRIFT_MXFP4)
+    v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, api.THRIFT_MXFP4)
+    if args.copy_mib:
+        copy_calibration(torch, dev, args.copy_mib)
+    kmax = max(1, api.thrift_select_kmax(w.Sq, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp, w.S))
+    o = torch.empty_like(q)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def step(rec=None):
+        if rec:
+            rec[0].record()
+        idx, cnt = api.thrift_select_blocks(q, k, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp, kmax)
+        q4 = api.thrift_quantize_fp4(q, api.THRIFT_GROUP_D, api.THRIFT_MXFP4)
+        if rec:
+            rec[1].record()
+        api.thrift_attention_decode(q, k, v, q4, k4, v4, idx, cnt, w.bk, w.causal, out=o)
+        if rec:
+            rec[2].record()
+        return idx, cnt
+
+    for _ in range(args.warmup):
+        step()
+    recs = [[ev() for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in recs:
+        idx, cnt = step(r)
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    prep_ms = float(np.mean([r[0].elapsed_time(r[1]) for r in recs]))
+    fwd_ms = float(np.mean([r[1].elapsed_time(r[2]) for r in recs]))
+    idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
+    # algorithmic bytes: the FP4 cache (codes + E8M0 scales) of every valid key block once,
+    # the fp16 K/V of each distinct promoted block of a key head once, Q (fp16 + FP4), O fp16
+    G = w.Hq // w.Hkv
+    nkb = -(-w.S // w.bk)
+    fp4_cache = w.B * w.Hkv * nkb * w.bk * (w.D // 2 + w.D // 32) * 2
+    distinct = 0
+    for b in range(w.B):
+        for hk in range(w.Hkv):
+            sel = set()
+            for g in range(G):
+                c = int(cnt_h[b, hk * G + g, 0])
+                sel.update(int(j) for j in idx_h[b, hk * G + g, 0, :c])
+            distinct += len(sel)
+    fp16_tiles = distinct * w.bk * w.D * 2 * 2
+    qo = w.B * w.Hq * w.Sq * w.D * (2 + 0.5 + 1 / 32 + 2)
+    alg = fp4_cache + fp16_tiles + qo
+    achieved = alg / (fwd_ms * 1e-3)
+    rows = w.B * w.Hq * w.Sq
+    line = {
+        "metric": "decode query rows/s (new tokens x query heads) against a 32K dual FP16/FP4 cache, D=128, 5% top-k",
+        "value": round(rows / (ms_step * 1e-3), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4+fp16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} Sk{w.S} D{w.D} "
+                               f"{'causal' if w.causal else 'non-causal'} top-k {w.topk_bp / 100}% mx",
+                   "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM / 1e9, "unit": "GB/s",
+                     "frac": round(achieved / HBM, 4), "traffic": measured_traffic(w.name, "mx"),
+                     "traffic_algorithmic": int(alg),
+                     "kernel": "decode_fp4_kernel + decode_f16_kernel + decode_merge_kernel"},
+        "breakdown_ms": {"select_and_quantize_q": round(prep_ms, 4), "attention_decode": round(fwd_ms, 4)},
+        "bytes": {"fp4_cache": int(fp4_cache), "fp16_promoted_tiles": int(fp16_tiles), "q_and_o": int(qo)},
+        "input_gen_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        from oracle import oracle as O
+
+        nthreads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        O.lib()
+        sec = 0.0
+        for b in range(w.B):  # the whole workload, one batch element at a time
+            qb, kb, vb = (np.ascontiguousarray(d[n][b:b + 1]) for n in ("q", "k", "v"))
+            k4b = O.quantize(kb, O.AXIS_D, O.MX)  # the cache's FP4 copy: outside the step, as on the GPU
+            v4b = O.quantize(vb, O.AXIS_S, O.MX)
+            t0 = time.perf_counter()
+            ib, cb, _ = O.select(qb, kb, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
+            q4b = O.quantize(qb, O.AXIS_D, O.MX)
+            O.attention(qb, kb, vb, q4b, k4b, v4b, ib, cb, w.bq, w.bk, w.causal)
+            sec += time.perf_counter() - t0
+        line["cpu_baseline"] = {"value": round(rows / sec, 2), "unit": "rows/s", "cores": nthreads,
+                                "kind": "oracle", "seconds": round(sec, 3),
+                                "sample": f"the whole workload ({w.B} batch elements x {w.Hq} query heads "
+                                          f"against the {w.S}-key cache), one batch element at a time: "
+                                          f"selection, FP4 quantisation of the rows, forward, fp64; the "
+                                          f"cache's FP4 copy built outside the timer"}
     s = json.dumps(line)
     print(s, flush=True)
     if args.out:
