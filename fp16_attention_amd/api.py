@@ -15,7 +15,8 @@ import torch
 from . import _lib
 from ._lib import THRIFT_GROUP_D, THRIFT_GROUP_S, THRIFT_MXFP4, THRIFT_NVFP4, ThriftError
 
-__all__ = ["thrift_select_kmax", "thrift_select_blocks", "thrift_quantize_fp4",
+__all__ = ["thrift_select_kmax", "thrift_select_blocks", "thrift_block_means",
+           "thrift_select_blocks_kbar", "thrift_quantize_fp4", "thrift_quantize_fp4_range",
            "thrift_attention_fwd", "thrift_attention_decode", "thrift_decode", "FP4Tensor",
            "fp4_transposed", "thrift_forward", "THRIFT_NVFP4", "THRIFT_MXFP4", "THRIFT_GROUP_D",
            "THRIFT_GROUP_S", "ThriftError"]
@@ -67,6 +68,46 @@ def thrift_select_blocks(q16, k16, block_q=128, block_k=64, causal=True, topk_co
     return idx, cnt
 
 
+def thrift_block_means(x16, blk=64, j0=0, j1=None, out=None):
+    """fp32 means [B,H,ceil(S/blk),D] of the blocks of x16; with out given,
+    only blocks j0 <= j < j1 of it are rewritten (a cache's last block after
+    new keys)."""
+    _check(x16, torch.float16, "x16")
+    B, H, S, D = x16.shape
+    nb = -(-S // blk)
+    if out is None:
+        out = torch.empty((B, H, nb, D), dtype=torch.float32, device=x16.device)
+    _check(out, torch.float32, "out")
+    if tuple(out.shape) != (B, H, nb, D):
+        raise ValueError(f"out must have shape {(B, H, nb, D)}")
+    _call("thrift_block_means", _ptr(x16), B, H, S, D, blk, j0, nb if j1 is None else j1, _ptr(out),
+          _stream())
+    return out
+
+
+def thrift_select_blocks_kbar(q16, kbar, Sk, block_q=128, block_k=64, causal=True, topk_count=-1,
+                              topk_bp=500, kmax=None):
+    """thrift_select_blocks against Sk keys given by their block means kbar
+    [B,Hkv,ceil(Sk/block_k),D] (thrift_block_means).  Returns (idx, cnt)."""
+    _check(q16, torch.float16, "q16")
+    _check(kbar, torch.float32, "kbar")
+    B, Hq, S, D = q16.shape
+    Hkv = kbar.shape[1]
+    if tuple(kbar.shape) != (B, Hkv, -(-Sk // block_k), D):
+        raise ValueError("kbar must be [B, Hkv, ceil(Sk/block_k), D]")
+    if kmax is None:
+        kmax = max(1, thrift_select_kmax(S, block_q, block_k, causal, topk_count, topk_bp, Sk))
+    nq = -(-S // block_q)
+    dev = q16.device
+    idx = torch.empty((B, Hq, nq, kmax), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Hq, nq), dtype=torch.int32, device=dev)
+    wsb = B * Hq * nq * D * 4
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _call("thrift_select_blocks_kbar", _ptr(q16), _ptr(kbar), B, Hq, Hkv, S, Sk, D, block_q, block_k,
+          int(causal), topk_count, topk_bp, _ptr(idx), _ptr(cnt), kmax, _ptr(ws), wsb, _stream())
+    return idx, cnt
+
+
 @dataclass
 class FP4Tensor:
     codes: torch.Tensor
@@ -95,6 +136,16 @@ def thrift_quantize_fp4(x16, axis=THRIFT_GROUP_D, fmt=THRIFT_MXFP4) -> FP4Tensor
     _call("thrift_quantize_fp4", _ptr(x16), B, H, S, D, axis, fmt, _ptr(codes), _ptr(scales),
           _ptr(ts), _ptr(ws), wsb, _stream())
     return FP4Tensor(codes, scales, ts, fmt, axis)
+
+
+def thrift_quantize_fp4_range(x16, t: FP4Tensor, s0, s1):
+    """Re-encode, in place in t (an MXFP4 copy of x16), the groups that hold
+    positions s0 <= s < s1 of x16."""
+    _check(x16, torch.float16, "x16")
+    B, H, S, D = x16.shape
+    _call("thrift_quantize_fp4_range", _ptr(x16), B, H, S, D, t.axis, t.fmt, s0, s1, _ptr(t.codes),
+          _ptr(t.scales), _stream())
+    return t
 
 
 def fp4_transposed(t: FP4Tensor):

@@ -1147,14 +1147,15 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeArgs d) {
   st.l = 0.0f;
   st.g = 1.0f;
   if (j >= 0 && j < d.nvalid) {
-    F16Stager<D, 64> stg;
-    stg.load(a, bhk, j, lane);
-    stg.store(smem, lane);
-    __syncthreads();
+    // the query rows are loaded together with the tile (one memory latency)
     v8h qh[D / 16];
     const size_t qoff = (bhq * Sq + r) * D + hi * 8;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qh[kk] = col < Sq ? *(const v8h*)(a.q16 + qoff + kk * 16) : v8h{};
+    F16Stager<D, 64> stg;
+    stg.load(a, bhk, j, lane);
+    stg.store(smem, lane);
+    __syncthreads();
     const int key0 = j * kBk;
     const bool need_mask = (a.causal && key0 + kBk - 1 > Sk - Sq) || key0 + kBk > Sk;
     fp16_tile<D>(st, smem, qh, a.sm_log2, key0, qpos, Sk, a.causal, need_mask, lane);
@@ -1162,11 +1163,20 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeArgs d) {
   if (col < Sq) store_partial<D>(d.part16 + ((bhq * a.kmax + p) * Sq + col) * kPartStride<D>, st, lane);
 }
 
-// O and LSE of one (batch, query head, row) from every partial that holds it.
+constexpr int kMergeThreads = 256;
+
+// O and LSE of one (batch, query head, row) from every partial that holds it:
+// one workgroup per row.  Thread t takes float4 column t % (D/4) of the
+// partials u = t / (D/4), + 256/(D/4), ...; loads of several partials are in
+// flight at once, and the per-group sums meet in LDS.
 template <int D>
-__global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs d) {
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs d) {
+  constexpr int C4 = D / 4, PG = kMergeThreads / C4, NW = kMergeThreads / 64;
+  __shared__ float red_m[NW];
+  __shared__ __attribute__((aligned(16))) float red_acc[PG][D];
+  __shared__ float red_l[PG];
   const AttnArgs& a = d.kv;
-  const int lane = threadIdx.x;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
   const size_t row = blockIdx.x;  // (b*Hq + hq)*Sq + r
   const int r = (int)(row % d.Sq);
   const size_t bhq = row / d.Sq;
@@ -1174,34 +1184,52 @@ __global__ __launch_bounds__(64) void decode_merge_kernel(DecodeArgs d) {
   const size_t bhk = (size_t)b * a.Hkv + hq / d.G;
   const int ncol = d.G * d.Sq, col = (hq % d.G) * d.Sq + r;
   const int n4 = d.nsplit * kDecWaves;
-  const int n16 = min(max(a.cnt[bhq], 0), a.kmax);
-  auto p4 = [&](int u) { return d.part4 + ((bhk * n4 + u) * ncol + col) * kPartStride<D>; };
-  auto p16 = [&](int u) { return d.part16 + ((bhq * a.kmax + u) * d.Sq + r) * kPartStride<D>; };
-  float M = kMInit;
-  for (int u = 0; u < n4; ++u) M = fmaxf(M, p4(u)[D]);
-  for (int u = 0; u < n16; ++u) M = fmaxf(M, p16(u)[D]);
-  float l = 0.0f, acc[D / 64];
-#pragma unroll
-  for (int e = 0; e < D / 64; ++e) acc[e] = 0.0f;
-  auto add = [&](const float* q) {
-    const float f = exp2f(q[D] - M);  // partial offsets are integers: exact powers of two
-    l += f * q[D + 1];
-#pragma unroll
-    for (int e = 0; e < D / 64; ++e) acc[e] += f * q[lane + 64 * e];
+  const int n = n4 + min(max(a.cnt[bhq], 0), a.kmax);
+  auto part = [&](int u) -> const float* {
+    return u < n4 ? d.part4 + ((bhk * n4 + u) * ncol + col) * kPartStride<D>
+                  : d.part16 + ((bhq * a.kmax + (u - n4)) * d.Sq + r) * kPartStride<D>;
   };
-  for (int u = 0; u < n4; ++u) add(p4(u));
-  for (int u = 0; u < n16; ++u) add(p16(u));
-  const float inv = 1.0f / l;
-  const size_t ob = row * D;
+  float M = kMInit;
+  for (int u = t; u < n; u += kMergeThreads) M = fmaxf(M, part(u)[D]);
 #pragma unroll
-  for (int e = 0; e < D / 64; ++e) {
-    const float x = acc[e] * inv;
-    if (a.o_fp32)
-      ((float*)a.o)[ob + lane + 64 * e] = x;
-    else
-      ((_Float16*)a.o)[ob + lane + 64 * e] = (_Float16)x;
+  for (int off = 32; off >= 1; off >>= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+  if (lane == 0) red_m[w] = M;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NW; ++i) M = fmaxf(M, red_m[i]);
+
+  const int c4 = t % C4, pg = t / C4;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  float l = 0.0f;
+#pragma unroll 4
+  for (int u = pg; u < n; u += PG) {
+    const float* q = part(u);
+    const float2 ml = *(const float2*)(q + D);
+    const float4 x = *(const float4*)(q + 4 * c4);
+    const float f = exp2f(ml.x - M);  // partial offsets are integers: exact powers of two
+    l += f * ml.y;
+    acc.x += f * x.x;
+    acc.y += f * x.y;
+    acc.z += f * x.z;
+    acc.w += f * x.w;
   }
-  if (a.lse && lane == 0) a.lse[row] = (M + log2f(l)) * kLn2;
+  *(float4*)&red_acc[pg][4 * c4] = acc;
+  if (c4 == 0) red_l[pg] = l;
+  __syncthreads();
+  if (t < D) {
+    float o = 0.0f, lt = 0.0f;
+#pragma unroll
+    for (int g = 0; g < PG; ++g) {
+      o += red_acc[g][t];
+      lt += red_l[g];
+    }
+    const float x = o / lt;
+    if (a.o_fp32)
+      ((float*)a.o)[row * D + t] = x;
+    else
+      ((_Float16*)a.o)[row * D + t] = (_Float16)x;
+    if (a.lse && t == 0) a.lse[row] = (M + log2f(lt)) * kLn2;
+  }
 }
 
 // Work split: about two workgroups per compute unit, at least one block per
@@ -1329,7 +1357,7 @@ static thrift_status launch_decode(DecodeArgs& d, hipStream_t stream) {
   const size_t lds4 = 4 * (size_t)M::SIZE + (size_t)d.G * ((d.nvalid + 31) / 32) * 4;
   decode_fp4_kernel<D><<<a.B * a.Hkv * d.nsplit, kDecWaves * 64, lds4, stream>>>(d);
   decode_f16_kernel<D><<<a.B * a.Hq * a.kmax, 64, Lds<D>::STAGE, stream>>>(d);
-  decode_merge_kernel<D><<<a.B * a.Hq * d.Sq, 64, 0, stream>>>(d);
+  decode_merge_kernel<D><<<a.B * a.Hq * d.Sq, kMergeThreads, 0, stream>>>(d);
   return launch_status();
 }
 

@@ -159,15 +159,22 @@ __device__ inline uint32_t encode_mx_32(const float* v, uint32_t* w /*4 dwords*/
 
 // ---- groups along D (Q, K) -----------------------------------------------------
 
+// Thread li encodes group gi = (li / range) * groups_per_slice + first + li % range:
+// `range` groups from group `first` of every (batch, head) slice (the whole
+// slice when range == groups_per_slice and first == 0).
 template <int FMT>
 __global__ __launch_bounds__(kQThreads) void quant_d_kernel(const _Float16* __restrict__ x,
                                                             size_t ngroups, int groups_per_slice,
+                                                            int range, int first,
                                                             const float* __restrict__ tscale,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
   constexpr int g = FMT == THRIFT_NVFP4 ? 16 : 32;
-  size_t gi = (size_t)blockIdx.x * kQThreads + threadIdx.x;
-  if (gi >= ngroups) return;
+  const size_t li = (size_t)blockIdx.x * kQThreads + threadIdx.x;
+  if (li >= ngroups) return;
+  const size_t gi = range == groups_per_slice
+                        ? li
+                        : (li / range) * groups_per_slice + first + li % range;
   float v[g];
   const v8h* src = reinterpret_cast<const v8h*>(x + gi * g);
 #pragma unroll
@@ -194,13 +201,14 @@ constexpr int kVTile = 128;  // tokens per workgroup
 
 template <int FMT, int D>
 __global__ __launch_bounds__(kQThreads) void quant_s_kernel(const _Float16* __restrict__ x, int S,
-                                                            int Sp, const float* __restrict__ tscale,
+                                                            int Sp, int tile0,
+                                                            const float* __restrict__ tscale,
                                                             uint8_t* __restrict__ codes,
                                                             uint8_t* __restrict__ scales) {
   constexpr int g = FMT == THRIFT_NVFP4 ? 16 : 32;
   constexpr int GPT = kVTile / g;  // groups per d in this tile
   __shared__ _Float16 tile[kVTile][D + 2];
-  const int tt = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int tt = tile0 + blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int s0 = tt * kVTile;
   const _Float16* base = x + (size_t)bh * S * D;
   // stage kVTile x D fp16 (zeros past S)
@@ -279,25 +287,57 @@ extern "C" thrift_status thrift_quantize_fp4(const void* x16, int B, int H, int 
     const int blocks = (int)((ngroups + kQThreads - 1) / kQThreads);
     const int gps = S * (D / g);
     if (fmt == THRIFT_NVFP4)
-      quant_d_kernel<THRIFT_NVFP4><<<blocks, kQThreads, 0, stream>>>(x, ngroups, gps, tensor_scale,
-                                                                       codes, scales);
+      quant_d_kernel<THRIFT_NVFP4><<<blocks, kQThreads, 0, stream>>>(x, ngroups, gps, gps, 0,
+                                                                       tensor_scale, codes, scales);
     else
-      quant_d_kernel<THRIFT_MXFP4><<<blocks, kQThreads, 0, stream>>>(x, ngroups, gps, tensor_scale,
-                                                                       codes, scales);
+      quant_d_kernel<THRIFT_MXFP4><<<blocks, kQThreads, 0, stream>>>(x, ngroups, gps, gps, 0,
+                                                                       tensor_scale, codes, scales);
   } else {
     const int Sp = pad_s(S);
     dim3 grid(cdiv(Sp, kVTile), BH);
     if (fmt == THRIFT_NVFP4) {
       if (D == 128)
-        quant_s_kernel<THRIFT_NVFP4, 128><<<grid, kQThreads, 0, stream>>>(x, S, Sp, tensor_scale, codes, scales);
+        quant_s_kernel<THRIFT_NVFP4, 128><<<grid, kQThreads, 0, stream>>>(x, S, Sp, 0, tensor_scale, codes, scales);
       else
-        quant_s_kernel<THRIFT_NVFP4, 64><<<grid, kQThreads, 0, stream>>>(x, S, Sp, tensor_scale, codes, scales);
+        quant_s_kernel<THRIFT_NVFP4, 64><<<grid, kQThreads, 0, stream>>>(x, S, Sp, 0, tensor_scale, codes, scales);
     } else {
       if (D == 128)
-        quant_s_kernel<THRIFT_MXFP4, 128><<<grid, kQThreads, 0, stream>>>(x, S, Sp, tensor_scale, codes, scales);
+        quant_s_kernel<THRIFT_MXFP4, 128><<<grid, kQThreads, 0, stream>>>(x, S, Sp, 0, tensor_scale, codes, scales);
       else
-        quant_s_kernel<THRIFT_MXFP4, 64><<<grid, kQThreads, 0, stream>>>(x, S, Sp, tensor_scale, codes, scales);
+        quant_s_kernel<THRIFT_MXFP4, 64><<<grid, kQThreads, 0, stream>>>(x, S, Sp, 0, tensor_scale, codes, scales);
     }
+  }
+  return launch_status();
+}
+
+extern "C" thrift_status thrift_quantize_fp4_range(const void* x16, int B, int H, int S, int D,
+                                                   thrift_group_axis axis, thrift_format fmt, int s0,
+                                                   int s1, uint8_t* codes, uint8_t* scales,
+                                                   hipStream_t stream) {
+  if (!x16 || !codes || !scales) return THRIFT_EINVAL;
+  if (B < 1 || H < 1 || S < 1 || s0 < 0 || s1 > S || s0 >= s1) return THRIFT_EINVAL;
+  if (fmt != THRIFT_NVFP4 && fmt != THRIFT_MXFP4) return THRIFT_EINVAL;
+  if (axis != THRIFT_GROUP_D && axis != THRIFT_GROUP_S) return THRIFT_EINVAL;
+  if (fmt != THRIFT_MXFP4) return THRIFT_EUNSUPPORTED;  // NVFP4's slice scale spans the whole slice
+  if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
+  if (S > 262144) return THRIFT_EUNSUPPORTED;
+  if (!aligned16(x16) || !aligned16(codes)) return THRIFT_EALIGN;
+  const int BH = B * H;
+  auto x = (const _Float16*)x16;
+  if (axis == THRIFT_GROUP_D) {
+    const int gpr = D / 32;  // groups per row
+    const int gps = S * gpr, range = (s1 - s0) * gpr;
+    const size_t ngroups = (size_t)BH * range;
+    const int blocks = (int)((ngroups + kQThreads - 1) / kQThreads);
+    quant_d_kernel<THRIFT_MXFP4><<<blocks, kQThreads, 0, stream>>>(x, ngroups, gps, range, s0 * gpr,
+                                                                     nullptr, codes, scales);
+  } else {
+    const int Sp = pad_s(S), t0 = s0 / kVTile, t1 = cdiv(s1, kVTile);
+    dim3 grid(t1 - t0, BH);
+    if (D == 128)
+      quant_s_kernel<THRIFT_MXFP4, 128><<<grid, kQThreads, 0, stream>>>(x, S, Sp, t0, nullptr, codes, scales);
+    else
+      quant_s_kernel<THRIFT_MXFP4, 64><<<grid, kQThreads, 0, stream>>>(x, S, Sp, t0, nullptr, codes, scales);
   }
   return launch_status();
 }

@@ -6,14 +6,14 @@
 //  - block_means reads every fp16 element of Q and K once (coalesced 16-byte
 //    loads) and sums in fp64, which is exact in any order, so the means are
 //    bit-identical to any other exact summation;
-//  - score_topk gives one workgroup to each (batch, key head, query block),
-//    scoring all query heads of the GQA group against key-block means staged
-//    through LDS (each kbar is read once per group, not once per head), then
-//    gives each head's row of scores to one wavefront, which finds the k-th
-//    largest (score, block) key with wavefront reductions only (k rounds of
-//    argmax below the previous one for small k, a bitwise search from the
-//    top bit otherwise) and writes the blocks at or above it in ascending
-//    order by ballot compaction: no workgroup barrier in the selection.
+//  - score_topk gives one workgroup to each (batch, key head, query block);
+//    each thread scores one key block against up to four query heads of the
+//    GQA group at once (each kbar row read once per four heads, all of it in
+//    flight at once), then each head's row of scores goes to one wavefront,
+//    which finds the k-th largest score by a bitwise search counted with
+//    ballots, breaks ties at it by lower block index, and writes the blocks
+//    in ascending order by ballot compaction: no workgroup barrier in the
+//    selection.
 #include "common.h"
 
 namespace thrift {
@@ -23,12 +23,12 @@ constexpr int kMeansThreads = 256;
 // means[bh][j][d] = fp32( sum_{rows of block j} x[bh][row][d] / rows ), sum in fp64.
 template <int D>
 __global__ __launch_bounds__(kMeansThreads) void block_means_kernel(const _Float16* __restrict__ x,
-                                                                    int S, int blk, int nb,
+                                                                    int S, int blk, int nb, int j0,
                                                                     float* __restrict__ means) {
   constexpr int CG = D / 8;                   // 16-byte column groups per row
   constexpr int RP = kMeansThreads / CG;      // row phases
   __shared__ double red[RP][D + 1];
-  const int j = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int j = j0 + blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int cg = t % CG, rp = t / CG;
   const int r0 = j * blk, r1 = min(S, r0 + blk);
   const _Float16* base = x + (size_t)bh * S * D + cg * 8;
@@ -48,86 +48,75 @@ __global__ __launch_bounds__(kMeansThreads) void block_means_kernel(const _Float
   }
 }
 
-// Total order on (score, block): higher score first, then lower block index.
-// -0 is treated as +0.  The returned key is larger for the preferred pair.
-__device__ inline uint64_t pair_key(float s, int j) {
-  uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
-  u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  return ((uint64_t)u << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)j);
+// Scores as unsigned keys with the order of the floats: -0 maps to +0, and
+// every finite score maps above 0, so 0 can stand for "no block here".
+__device__ inline uint32_t score_key(float s) {
+  const uint32_t u = __float_as_uint(s == 0.0f ? 0.0f : s);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-__device__ inline uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
-}
+// The keys of the first kRegChunks chunks of a row stay in registers during
+// the search; chunks beyond (rows of more than 512 blocks) are re-read from LDS.
+constexpr int kRegChunks = 8;
 
-__device__ inline int wave_sum_i32(int v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
-  return v;
-}
-
-// One wavefront selects the k best of the n scores srow[0..n) (LDS) and
-// writes them ascending into out[0..k), -1 into out[k..kmax).  The
-// (score, block) keys are unique, so the k-th largest key is a threshold
-// that selects exactly k blocks.
+// One wavefront selects the k best of the n scores srow[0..n) (LDS): higher
+// score first, equal scores by lower block index.  It writes them ascending
+// into out[0..k) and -1 into out[k..kmax).
+//   1. T = the k-th largest key: the largest t with at least k keys >= t,
+//      found one bit at a time from the top; each count is a sum of ballot
+//      popcounts over the row's chunks (lane l of chunk c holds block c*64+l).
+//   2. Every block with key > T is selected (fewer than k of them); of the
+//      blocks with key == T the lowest-indexed k - count(> T) are selected,
+//      ranked by a running ballot prefix in ascending block order.
 __device__ inline void wave_topk(const float* srow, int n, int k, int32_t* __restrict__ out, int kmax,
                                  int lane) {
   if (k >= n) {
     for (int e = lane; e < kmax; e += kWave) out[e] = e < n ? e : -1;
     return;
   }
-  const int nc = cdiv(n, kWave);  // this lane's candidates: j = c*64 + lane
-  uint64_t thr = ~0ull;
-  if (k == 0) {
-  } else if (k <= 32) {  // k rounds: the largest key below the previous round's
-    uint64_t prev = ~0ull;
-    for (int r = 0; r < k; ++r) {
-      uint64_t best = 0;
-      for (int c = 0; c < nc; ++c) {
-        const int j = c * kWave + lane;
-        if (j < n) {
-          const uint64_t key = pair_key(srow[j], j);
-          if (key < prev && key > best) best = key;
-        }
-      }
-      prev = wave_max_u64(best);
-    }
-    thr = prev;
-  } else {  // the largest t with at least k keys >= t, one bit at a time
-    uint64_t prefix = 0;
-    for (int bit = 63; bit >= 0; --bit) {
-      const uint64_t cand = prefix | (1ull << bit);
-      int cntv = 0;
-      for (int c = 0; c < nc; ++c) {
-        const int j = c * kWave + lane;
-        cntv += (j < n && pair_key(srow[j], j) >= cand) ? 1 : 0;
-      }
-      if (wave_sum_i32(cntv) >= k) prefix = cand;
-    }
-    thr = prefix;
-  }
-  int base = 0;
-  for (int c = 0; c < nc; ++c) {
+  const int nc = cdiv(n, kWave);
+  const uint64_t below = (1ull << lane) - 1;
+  auto key_at = [&](int c) -> uint32_t {
     const int j = c * kWave + lane;
-    const bool sel = k > 0 && j < n && pair_key(srow[j], j) >= thr;
+    return j < n ? score_key(srow[j]) : 0u;
+  };
+  uint32_t kr[kRegChunks];
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c) kr[c] = c < nc ? key_at(c) : 0u;
+  auto count_ge = [&](uint32_t t) {
+    int m = 0;
+#pragma unroll
+    for (int c = 0; c < kRegChunks; ++c)
+      if (c < nc) m += __popcll(__ballot(kr[c] >= t));
+    for (int c = kRegChunks; c < nc; ++c) m += __popcll(__ballot(key_at(c) >= t));
+    return m;
+  };
+  uint32_t thr = 0;
+  if (k > 0)
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      if (count_ge(cand) >= k) thr = cand;
+    }
+  // k > 0: thr >= the smallest finite key > 0, so padding (key 0) never ties
+  const int need = k > 0 ? k - (thr == 0xFFFFFFFFu ? 0 : count_ge(thr + 1)) : 0;
+  int base = 0, eq_seen = 0;
+  auto emit = [&](int c, uint32_t u) {
+    const uint64_t eq = __ballot(k > 0 && u == thr);
+    const bool sel = k > 0 && (u > thr || (u == thr && eq_seen + __popcll(eq & below) < need));
     const uint64_t bal = __ballot(sel);
-    if (sel) out[base + __popcll(bal & ((1ull << lane) - 1))] = j;
+    if (sel) out[base + __popcll(bal & below)] = c * kWave + lane;
     base += __popcll(bal);
-  }
+    eq_seen += __popcll(eq);
+  };
+#pragma unroll
+  for (int c = 0; c < kRegChunks; ++c)
+    if (c < nc) emit(c, kr[c]);
+  for (int c = kRegChunks; c < nc; ++c) emit(c, key_at(c));
   for (int e = k + lane; e < kmax; e += kWave) out[e] = -1;
 }
 
 constexpr int kTopkThreads = 256;
-constexpr int kHeadChunk = 4;     // query heads scored together per pass
-constexpr int kKeyChunk = 256;    // key blocks staged per pass (one per thread)
-constexpr int kDimChunk = 32;     // channels staged per pass
+constexpr int kHeadChunk = 4;  // query heads scored together per pass
 
 template <int D>
 __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
@@ -135,8 +124,7 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
     int bk, int causal, int topk_count, int topk_bp, int32_t* __restrict__ idx,
     int32_t* __restrict__ cnt, int kmax) {
   extern __shared__ float sc[];  // [kHeadChunk][nK] scores
-  __shared__ float qv[kHeadChunk][D];
-  __shared__ float kst[kKeyChunk][kDimChunk + 1];
+  __shared__ __attribute__((aligned(16))) float qv[kHeadChunk][D];
 
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
   const int i = blockIdx.x, bhk = blockIdx.y;
@@ -154,27 +142,41 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
       int hq = hk * G + h0 + h;
       qv[h][d] = h < nh ? qm[(((size_t)b * Hq + hq) * nq + i) * D + d] : 0.0f;
     }
-    // scores: one key block per thread, fp32 FMA chain over ascending channels
-    for (int jc = 0; jc < n; jc += kKeyChunk) {
-      float s[kHeadChunk];
+    __syncthreads();
+    // scores: one key block per thread, its whole mean row loaded at once
+    // (independent loads, one memory latency per 256 blocks), then an fp32
+    // FMA chain over ascending channels per head
+    for (int jc = 0; jc < n; jc += kTopkThreads) {
+      const int j = jc + t;
+      if (j < n) {
+        const float4* kr = reinterpret_cast<const float4*>(kbase + (size_t)j * D);
+        float s[kHeadChunk];
 #pragma unroll
-      for (int h = 0; h < kHeadChunk; ++h) s[h] = 0.0f;
-      for (int dc = 0; dc < D; dc += kDimChunk) {
-        __syncthreads();
-        for (int e = t; e < kKeyChunk * kDimChunk; e += kTopkThreads) {
-          int kk = e / kDimChunk, dd = e % kDimChunk;
-          kst[kk][dd] = (jc + kk < n) ? kbase[(size_t)(jc + kk) * D + dc + dd] : 0.0f;
-        }
-        __syncthreads();
-#pragma unroll 8
-        for (int dd = 0; dd < kDimChunk; ++dd) {
-          float kvv = kst[t][dd];
+        for (int h = 0; h < kHeadChunk; ++h) s[h] = 0.0f;
+        // the whole key row in flight at once; the scheduling barriers keep
+        // the compiler from reading every query mean (4 x D floats) ahead of
+        // the FMAs, which would not fit in registers
+        float4 kv[D / 4];
 #pragma unroll
-          for (int h = 0; h < kHeadChunk; ++h) s[h] = __builtin_fmaf(qv[h][dc + dd], kvv, s[h]);
+        for (int c = 0; c < D / 4; ++c) kv[c] = kr[c];
+#pragma unroll
+        for (int c = 0; c < D / 4; ++c) {
+#pragma unroll
+          for (int h = 0; h < kHeadChunk; ++h) {
+            const float4 qq = *reinterpret_cast<const float4*>(&qv[h][4 * c]);
+            s[h] = __builtin_fmaf(qq.x, kv[c].x, s[h]);
+            s[h] = __builtin_fmaf(qq.y, kv[c].y, s[h]);
+            s[h] = __builtin_fmaf(qq.z, kv[c].z, s[h]);
+            s[h] = __builtin_fmaf(qq.w, kv[c].w, s[h]);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
+        // every row of sc is written (rows h >= nh are never read): a store
+        // under "h < nh" would let the compiler sink the FMA chains below
+        // all the query-mean reads
+#pragma unroll
+        for (int h = 0; h < kHeadChunk; ++h) sc[h * nK + j] = s[h];
       }
-      if (jc + t < n)
-        for (int h = 0; h < nh; ++h) sc[h * nK + jc + t] = s[h];
     }
     __syncthreads();
 
@@ -221,13 +223,14 @@ extern "C" size_t thrift_select_workspace_bytes(int B, int Hq, int Hkv, int S, i
   return thrift_select_workspace_bytes_kv(B, Hq, Hkv, S, S, D, block_q, block_k);
 }
 
-extern "C" thrift_status thrift_select_blocks_kv(const void* q16, const void* k16, int B, int Hq,
-                                                 int Hkv, int Sq, int Sk, int D, int block_q,
-                                                 int block_k, int causal, int topk_count,
-                                                 int topk_bp, int32_t* idx, int32_t* cnt, int kmax,
-                                                 void* workspace, size_t workspace_bytes,
-                                                 hipStream_t stream) {
-  if (!q16 || !k16 || !idx || !cnt || !workspace) return THRIFT_EINVAL;
+// Selection from fp16 keys (k16, means computed here into the workspace) or
+// from the key means a caller keeps (kbar).
+static thrift_status select_common(const void* q16, const void* k16, const float* kbar, int B, int Hq,
+                                   int Hkv, int Sq, int Sk, int D, int block_q, int block_k,
+                                   int causal, int topk_count, int topk_bp, int32_t* idx,
+                                   int32_t* cnt, int kmax, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
+  if (!q16 || (!k16 && !kbar) || !idx || !cnt || !workspace) return THRIFT_EINVAL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < Sq || (causal != 0 && causal != 1)) return THRIFT_EINVAL;
   if (Hq % Hkv != 0) return THRIFT_EINVAL;
   if (topk_count < 0 && (topk_bp < 0 || topk_bp > 10000)) return THRIFT_EINVAL;
@@ -236,15 +239,16 @@ extern "C" thrift_status thrift_select_blocks_kv(const void* q16, const void* k1
   if (Sk > 262144) return THRIFT_EUNSUPPORTED;
   int need = thrift_select_kmax_kv(Sq, Sk, block_q, block_k, causal, topk_count, topk_bp);
   if (kmax < need || kmax < 1) return THRIFT_EINVAL;
-  if (!aligned16(q16) || !aligned16(k16) || !aligned16(workspace)) return THRIFT_EALIGN;
-  if (workspace_bytes < thrift_select_workspace_bytes_kv(B, Hq, Hkv, Sq, Sk, D, block_q, block_k))
-    return THRIFT_EWORKSPACE;
+  if (!aligned16(q16) || (k16 && !aligned16(k16)) || (kbar && !aligned16(kbar)) || !aligned16(workspace))
+    return THRIFT_EALIGN;
   const int nq = cdiv(Sq, block_q), nk = cdiv(Sk, block_k);
+  const size_t qbytes = (size_t)B * Hq * nq * D * sizeof(float);
+  if (workspace_bytes < (kbar ? qbytes : thrift_select_workspace_bytes_kv(B, Hq, Hkv, Sq, Sk, D, block_q, block_k)))
+    return THRIFT_EWORKSPACE;
   float* qm = (float*)workspace;
-  size_t qbytes = (size_t)B * Hq * nq * D * sizeof(float);
-  float* km = (float*)((char*)workspace + ((qbytes + 255) / 256) * 256);
+  float* km = kbar ? (float*)kbar : (float*)((char*)workspace + ((qbytes + 255) / 256) * 256);
   auto q = (const _Float16*)q16;
-  auto k = (const _Float16*)k16;
+  auto k = kbar ? nullptr : (const _Float16*)k16;
   const size_t lds = (size_t)kHeadChunk * nk * sizeof(float);
   static bool configured = false;  // allow more than the default dynamic LDS for long S
   if (!configured) {
@@ -256,16 +260,54 @@ extern "C" thrift_status thrift_select_blocks_kv(const void* q16, const void* k1
     configured = true;
   }
   if (D == 128) {
-    block_means_kernel<128><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, Sq, block_q, nq, qm);
-    block_means_kernel<128><<<dim3(nk, B * Hkv), kMeansThreads, 0, stream>>>(k, Sk, block_k, nk, km);
+    block_means_kernel<128><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, Sq, block_q, nq, 0, qm);
+    if (k) block_means_kernel<128><<<dim3(nk, B * Hkv), kMeansThreads, 0, stream>>>(k, Sk, block_k, nk, 0, km);
     score_topk_kernel<128><<<dim3(nq, B * Hkv), kTopkThreads, lds, stream>>>(
         qm, km, Hq, Hkv, Sq, Sk, block_q, block_k, causal, topk_count, topk_bp, idx, cnt, kmax);
   } else {
-    block_means_kernel<64><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, Sq, block_q, nq, qm);
-    block_means_kernel<64><<<dim3(nk, B * Hkv), kMeansThreads, 0, stream>>>(k, Sk, block_k, nk, km);
+    block_means_kernel<64><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, Sq, block_q, nq, 0, qm);
+    if (k) block_means_kernel<64><<<dim3(nk, B * Hkv), kMeansThreads, 0, stream>>>(k, Sk, block_k, nk, 0, km);
     score_topk_kernel<64><<<dim3(nq, B * Hkv), kTopkThreads, lds, stream>>>(
         qm, km, Hq, Hkv, Sq, Sk, block_q, block_k, causal, topk_count, topk_bp, idx, cnt, kmax);
   }
+  return launch_status();
+}
+
+extern "C" thrift_status thrift_select_blocks_kv(const void* q16, const void* k16, int B, int Hq,
+                                                 int Hkv, int Sq, int Sk, int D, int block_q,
+                                                 int block_k, int causal, int topk_count,
+                                                 int topk_bp, int32_t* idx, int32_t* cnt, int kmax,
+                                                 void* workspace, size_t workspace_bytes,
+                                                 hipStream_t stream) {
+  if (!k16) return THRIFT_EINVAL;
+  return select_common(q16, k16, nullptr, B, Hq, Hkv, Sq, Sk, D, block_q, block_k, causal, topk_count,
+                       topk_bp, idx, cnt, kmax, workspace, workspace_bytes, stream);
+}
+
+extern "C" thrift_status thrift_select_blocks_kbar(const void* q16, const float* kbar, int B, int Hq,
+                                                   int Hkv, int Sq, int Sk, int D, int block_q,
+                                                   int block_k, int causal, int topk_count,
+                                                   int topk_bp, int32_t* idx, int32_t* cnt, int kmax,
+                                                   void* workspace, size_t workspace_bytes,
+                                                   hipStream_t stream) {
+  if (!kbar) return THRIFT_EINVAL;
+  return select_common(q16, nullptr, kbar, B, Hq, Hkv, Sq, Sk, D, block_q, block_k, causal, topk_count,
+                       topk_bp, idx, cnt, kmax, workspace, workspace_bytes, stream);
+}
+
+extern "C" thrift_status thrift_block_means(const void* x16, int B, int H, int S, int D, int blk, int j0,
+                                            int j1, float* means, hipStream_t stream) {
+  if (!x16 || !means || B < 1 || H < 1 || S < 1 || blk < 1) return THRIFT_EINVAL;
+  const int nb = cdiv(S, blk);
+  if (j0 < 0 || j1 > nb || j0 >= j1) return THRIFT_EINVAL;
+  if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
+  if (S > 262144 || B * H > 65535) return THRIFT_EUNSUPPORTED;
+  if (!aligned16(x16)) return THRIFT_EALIGN;
+  auto x = (const _Float16*)x16;
+  if (D == 128)
+    block_means_kernel<128><<<dim3(j1 - j0, B * H), kMeansThreads, 0, stream>>>(x, S, blk, nb, j0, means);
+  else
+    block_means_kernel<64><<<dim3(j1 - j0, B * H), kMeansThreads, 0, stream>>>(x, S, blk, nb, j0, means);
   return launch_status();
 }
 

@@ -127,6 +127,29 @@ thrift_status thrift_select_blocks_kv(const void* q16, const void* k16, int B, i
                                       int kmax, void* workspace, size_t workspace_bytes,
                                       hipStream_t stream);
 
+/* Key-block means kept beside a KV cache (the cache holds FP16 and FP4
+ * copies of K/V, summaries "Betekenis en Beweringen"), so that a decode step
+ * recomputes only the block its new keys land in.
+ *   x16 [B,H,S,D] fp16 (read only).
+ *   means [B,H,ceil(S/blk),D] fp32 (in/out): blocks j0 <= j < j1 of every
+ *     (batch, head) slice are written - the mean of the block's rows that lie
+ *     below S, summed in fp64 and rounded once to fp32, bit-identical to the
+ *     kbar thrift_select_blocks computes; every other block is left as is.
+ *   0 <= j0 < j1 <= ceil(S/blk), else THRIFT_EINVAL. */
+thrift_status thrift_block_means(const void* x16, int B, int H, int S, int D, int blk, int j0, int j1,
+                                 float* means, hipStream_t stream);
+
+/* thrift_select_blocks_kv with the key-block means given instead of the fp16
+ * keys: kbar [B,Hkv,ceil(Sk/block_k),D] fp32 as thrift_block_means writes
+ * them with blk = block_k (read only).  Same idx and cnt.  workspace: at
+ * least B*Hq*ceil(Sq/block_q)*D*4 bytes (the query means;
+ * thrift_select_workspace_bytes_kv is always enough). */
+thrift_status thrift_select_blocks_kbar(const void* q16, const float* kbar, int B, int Hq, int Hkv,
+                                        int Sq, int Sk, int D, int block_q, int block_k, int causal,
+                                        int topk_count, int topk_bp, int32_t* idx, int32_t* cnt,
+                                        int kmax, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
 /* ---------------------------------------------------------------------- */
 /* FP4 quantisation (the FP4 path's NVFP4 micro-scaling)                    */
 /* ---------------------------------------------------------------------- */
@@ -146,6 +169,18 @@ thrift_status thrift_quantize_fp4(const void* x16, int B, int H, int S, int D,
                                   thrift_group_axis axis, thrift_format fmt, uint8_t* codes,
                                   uint8_t* scales, float* tensor_scale, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
+
+/* Re-encode part of an MXFP4 KV-cache copy after new tokens were written to
+ * positions s0 <= s < s1 of x16 [B,H,S,D] (the FP4 copy of the cache,
+ * summaries "Betekenis en Beweringen").  Along THRIFT_GROUP_D the rows
+ * s0..s1-1 are re-encoded; along THRIFT_GROUP_S every 128-position tile that
+ * holds one of them.  Each byte written equals the byte thrift_quantize_fp4
+ * writes for the tensor as it is now; bytes outside those rows or tiles are
+ * not touched.  MXFP4 only (an NVFP4 slice scale depends on the whole slice:
+ * THRIFT_EUNSUPPORTED); 0 <= s0 < s1 <= S, else THRIFT_EINVAL. */
+thrift_status thrift_quantize_fp4_range(const void* x16, int B, int H, int S, int D,
+                                        thrift_group_axis axis, thrift_format fmt, int s0, int s1,
+                                        uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
 /* Mixed FP4/FP16 attention ("Gemengd-Precisie Berekening & Samenvoeging")  */

@@ -130,3 +130,38 @@ def test_decode_validation(lib):
     assert call(wsb=16) == 4
     need = lib.thrift_attention_decode_workspace_bytes(1, 8, 2, 1, 512, 128, 4)
     assert need > 0 and call(wsb=need) != 4
+
+
+def test_cache_maintenance_validation(lib):
+    bm = lib.thrift_block_means
+    assert bm(None, 1, 2, 1000, 128, 64, 0, 16, A, None) == 1
+    assert bm(A, 1, 2, 1000, 128, 64, 0, 17, A, None) == 1  # 16 blocks of 64 in 1000 rows
+    assert bm(A, 1, 2, 1000, 128, 64, 5, 5, A, None) == 1  # empty range
+    assert bm(A, 1, 2, 1000, 128, 64, -1, 3, A, None) == 1
+    assert bm(A, 1, 2, 1000, 96, 64, 0, 16, A, None) == 2
+    assert bm(A + 2, 1, 2, 1000, 128, 64, 0, 16, A, None) == 3
+
+    sk = lib.thrift_select_blocks_kbar
+
+    def call(q=A, kbar=A, Sq=1, Sk=4096, kmax=4, ws=A, wsb=1 << 20, D=128):
+        return sk(q, kbar, 1, 8, 2, Sq, Sk, D, 128, 64, 1, -1, 500, A, A, kmax, ws, wsb, None)
+
+    assert call(kbar=None) == 1
+    assert call(Sq=5000) == 1  # more queries than keys
+    assert call(kmax=0) == 1
+    assert call(D=80) == 2
+    assert call(kbar=A + 4) == 3
+    assert call(wsb=8 * 128 * 4 - 1) == 4  # the query means of 8 heads x 1 block
+
+    qr = lib.thrift_quantize_fp4_range
+
+    def qcall(x=A, S=1000, axis=1, fmt=1, s0=999, s1=1000, codes=A):
+        return qr(x, 1, 2, S, 128, axis, fmt, s0, s1, codes, A, None)
+
+    assert qcall(x=None) == 1
+    assert qcall(s0=1000) == 1  # empty range
+    assert qcall(s1=1001) == 1
+    assert qcall(s0=-1) == 1
+    assert qcall(axis=3) == 1
+    assert qcall(fmt=0) == 2  # NVFP4: the slice scale spans the whole slice
+    assert qcall(codes=A + 1) == 3

@@ -89,3 +89,54 @@ def test_decode_full_size(oracle):
     w = W.WORKLOADS["decode"]
     note(f"[decode] full size: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} Sk{w.S} D{w.D} bp{w.topk_bp}")
     _run(oracle, w, w.topk_bp)
+
+
+def test_cache_maintenance_matches_oracle(oracle):
+    """Key-block means kept beside the cache and range re-encoding of its
+    FP4 copy: bit-identical to the oracle's means and codes of the cache as
+    it is after new tokens are written, with blocks and groups outside the
+    updated range untouched; selection from the kept means equals selection
+    from the fp16 keys."""
+    import torch
+
+    from fp16_attention_amd import api
+
+    w = W.WORKLOADS["decode"].with_(B=2, Hq=8, Hkv=2, Sq=3, S=1000, seed=21)
+    d = W.generate(w)
+    note(f"[decode] cache maintenance: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} Sk{w.S}")
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(np.ascontiguousarray(d[n])).to(dev) for n in ("q", "k", "v"))
+    kbar = api.thrift_block_means(k, 64)
+    k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, api.THRIFT_MXFP4)
+    v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, api.THRIFT_MXFP4)
+    torch.cuda.synchronize()
+    assert np.array_equal(kbar.cpu().numpy(), oracle.block_means(d["k"], 64))
+    # new tokens at positions 990..999 (the last key block, two V tiles' worth of groups)
+    s0, s1 = 990, 1000
+    rng = np.random.default_rng(5)
+    knew, vnew = d["k"].copy(), d["v"].copy()
+    knew[:, :, s0:s1] = rng.standard_normal(knew[:, :, s0:s1].shape).astype(np.float16)
+    vnew[:, :, s0:s1] = rng.standard_normal(vnew[:, :, s0:s1].shape).astype(np.float16)
+    k.copy_(torch.from_numpy(knew))
+    v.copy_(torch.from_numpy(vnew))
+    before = kbar.clone(), k4.codes.clone(), k4.scales.clone(), v4.codes.clone(), v4.scales.clone()
+    api.thrift_block_means(k, 64, s0 // 64, -(-s1 // 64), out=kbar)
+    api.thrift_quantize_fp4_range(k, k4, s0, s1)
+    api.thrift_quantize_fp4_range(v, v4, s0, s1)
+    torch.cuda.synchronize()
+    assert np.array_equal(kbar.cpu().numpy(), oracle.block_means(knew, 64))
+    assert torch.equal(kbar[:, :, : s0 // 64], before[0][:, :, : s0 // 64])
+    same_fp4(k4, oracle.quantize(knew, oracle.AXIS_D, oracle.MX))
+    same_fp4(v4, oracle.quantize(vnew, oracle.AXIS_S, oracle.MX))
+    assert torch.equal(k4.codes[:, :, :s0], before[1][:, :, :s0])
+    assert torch.equal(k4.scales[:, :, :s0], before[2][:, :, :s0])
+    t0 = s0 // 128 * 2  # V: key blocks of 64 before the first re-encoded 128-position tile
+    assert torch.equal(v4.codes[:, :, :t0], before[3][:, :, :t0])
+    assert torch.equal(v4.scales[:, :, :t0], before[4][:, :, :t0])
+    idx_a, cnt_a = api.thrift_select_blocks_kbar(q, kbar, w.S, 128, 64, True, -1, 1000)
+    idx_b, cnt_b = api.thrift_select_blocks(q, k, 128, 64, True, -1, 1000)
+    torch.cuda.synchronize()
+    assert torch.equal(cnt_a, cnt_b) and torch.equal(idx_a, idx_b)
+    ridx, rcnt, _ = oracle.select(d["q"], knew, 128, 64, True, -1, 1000)
+    assert np.array_equal(cnt_a.cpu().numpy(), rcnt)
+    assert np.array_equal(idx_a.cpu().numpy()[..., : ridx.shape[-1]], ridx)
