@@ -16,7 +16,8 @@ from . import _lib
 from ._lib import THRIFT_GROUP_D, THRIFT_GROUP_S, THRIFT_MXFP4, THRIFT_NVFP4, ThriftError
 
 __all__ = ["thrift_select_kmax", "thrift_select_blocks", "thrift_block_means",
-           "thrift_select_blocks_kbar", "thrift_quantize_fp4", "thrift_quantize_fp4_range",
+           "thrift_select_blocks_kbar", "thrift_select_blocks_means", "thrift_quantize_fp4",
+           "thrift_quantize_fp4_means", "thrift_quantize_fp4_range",
            "thrift_attention_fwd", "thrift_attention_decode", "thrift_decode", "FP4Tensor",
            "fp4_transposed", "thrift_forward", "THRIFT_NVFP4", "THRIFT_MXFP4", "THRIFT_GROUP_D",
            "THRIFT_GROUP_S", "ThriftError"]
@@ -108,6 +109,26 @@ def thrift_select_blocks_kbar(q16, kbar, Sk, block_q=128, block_k=64, causal=Tru
     return idx, cnt
 
 
+def thrift_select_blocks_means(qbar, kbar, Sq, Sk, block_q=128, block_k=64, causal=True, topk_count=-1,
+                               topk_bp=500, kmax=None):
+    """Selection from block means computed beforehand: qbar [B,Hq,ceil(Sq/block_q),D],
+    kbar [B,Hkv,ceil(Sk/block_k),D] (thrift_quantize_fp4_means, thrift_block_means)."""
+    _check(qbar, torch.float32, "qbar")
+    _check(kbar, torch.float32, "kbar")
+    B, Hq, nq, D = qbar.shape
+    Hkv = kbar.shape[1]
+    if nq != -(-Sq // block_q) or tuple(kbar.shape) != (B, Hkv, -(-Sk // block_k), D):
+        raise ValueError("qbar / kbar do not match Sq, Sk and the block sizes")
+    if kmax is None:
+        kmax = max(1, thrift_select_kmax(Sq, block_q, block_k, causal, topk_count, topk_bp, Sk))
+    dev = qbar.device
+    idx = torch.empty((B, Hq, nq, kmax), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Hq, nq), dtype=torch.int32, device=dev)
+    _call("thrift_select_blocks_means", _ptr(qbar), _ptr(kbar), B, Hq, Hkv, Sq, Sk, D, block_q, block_k,
+          int(causal), topk_count, topk_bp, _ptr(idx), _ptr(cnt), kmax, _stream())
+    return idx, cnt
+
+
 @dataclass
 class FP4Tensor:
     codes: torch.Tensor
@@ -136,6 +157,24 @@ def thrift_quantize_fp4(x16, axis=THRIFT_GROUP_D, fmt=THRIFT_MXFP4) -> FP4Tensor
     _call("thrift_quantize_fp4", _ptr(x16), B, H, S, D, axis, fmt, _ptr(codes), _ptr(scales),
           _ptr(ts), _ptr(ws), wsb, _stream())
     return FP4Tensor(codes, scales, ts, fmt, axis)
+
+
+def thrift_quantize_fp4_means(x16, fmt=THRIFT_MXFP4, blk=128):
+    """FP4 codes along D (as thrift_quantize_fp4 with THRIFT_GROUP_D) and the
+    fp32 block means [B,H,ceil(S/blk),D] from one pass.  Returns (FP4Tensor, means)."""
+    _check(x16, torch.float16, "x16")
+    B, H, S, D = x16.shape
+    g = 16 if fmt == THRIFT_NVFP4 else 32
+    dev = x16.device
+    codes = torch.empty((B, H, S, D // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty((B, H, S, D // g), dtype=torch.uint8, device=dev)
+    ts = torch.empty((B, H), dtype=torch.float32, device=dev) if fmt == THRIFT_NVFP4 else None
+    means = torch.empty((B, H, -(-S // blk), D), dtype=torch.float32, device=dev)
+    wsb = _lib.load().thrift_quantize_means_workspace_bytes(B, H, S, D, fmt, blk)
+    ws = torch.empty(max(wsb, 16), dtype=torch.uint8, device=dev)
+    _call("thrift_quantize_fp4_means", _ptr(x16), B, H, S, D, fmt, blk, _ptr(codes), _ptr(scales), _ptr(ts),
+          _ptr(means), _ptr(ws), wsb, _stream())
+    return FP4Tensor(codes, scales, ts, fmt, THRIFT_GROUP_D), means
 
 
 def thrift_quantize_fp4_range(x16, t: FP4Tensor, s0, s1):
@@ -228,10 +267,12 @@ def thrift_decode(q16, k16, v16, k4: FP4Tensor, v4: FP4Tensor, fmt=THRIFT_MXFP4,
 
 def thrift_forward(q16, k16, v16, fmt=THRIFT_MXFP4, block_q=128, block_k=64, causal=True,
                    topk_count=-1, topk_bp=500, sm_scale=None, out_fp32=False, with_lse=False):
-    """The whole path: selection, quantisation of Q/K/V, mixed attention."""
-    idx, cnt = thrift_select_blocks(q16, k16, block_q, block_k, causal, topk_count, topk_bp)
-    q4 = thrift_quantize_fp4(q16, THRIFT_GROUP_D, fmt)
-    k4 = thrift_quantize_fp4(k16, THRIFT_GROUP_D, fmt)
+    """The whole path: Q and K each read once for their block means and FP4
+    codes, V quantised, selection from the means, mixed attention."""
+    q4, qbar = thrift_quantize_fp4_means(q16, fmt, block_q)
+    k4, kbar = thrift_quantize_fp4_means(k16, fmt, block_k)
     v4 = thrift_quantize_fp4(v16, THRIFT_GROUP_S, fmt)
+    idx, cnt = thrift_select_blocks_means(qbar, kbar, q16.shape[2], k16.shape[2], block_q, block_k, causal,
+                                          topk_count, topk_bp)
     return thrift_attention_fwd(q16, k16, v16, q4, k4, v4, idx, cnt, block_q, block_k, causal,
                                 sm_scale, out_fp32, with_lse)

@@ -244,6 +244,82 @@ __global__ __launch_bounds__(kQThreads) void quant_s_kernel(const _Float16* __re
   }
 }
 
+// ---- block means and FP4 along D in one read (Q, K) -------------------------------
+
+// One workgroup per (slice, block of blk rows); thread t holds the 16-byte
+// column chunk cg = t % (D/8) of rows rp, rp + RP, ... (rp = t / (D/8)), so
+// the four lanes of a 32-element MX group are adjacent and share their rows.
+//  - Block means as block_means_kernel computes them (fp64 column sums in
+//    any order are exact; one rounding to fp32).
+//  - MXFP4: the group maximum by two lane exchanges, then each lane encodes
+//    its 8 elements with the group's E8M0 scale, exactly as quant_d_kernel.
+//  - NVFP4: the block's absolute maximum goes to part[bh * nb + j] for the
+//    slice scale; the codes follow in quant_d_kernel (a second read).
+template <int D, int FMT>
+__global__ __launch_bounds__(kQThreads) void means_quant_kernel(const _Float16* __restrict__ x, int S,
+                                                                int blk, int nb,
+                                                                float* __restrict__ means,
+                                                                uint8_t* __restrict__ codes,
+                                                                uint8_t* __restrict__ scales,
+                                                                float* __restrict__ part) {
+  constexpr int CG = D / 8;              // 16-byte column chunks per row
+  constexpr int RP = kQThreads / CG;     // row phases
+  static_assert(CG % 4 == 0, "an MX group is four chunks");
+  __shared__ double red[RP][D + 1];
+  __shared__ float redm[kQThreads / kWave];
+  const int j = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  const int cg = t % CG, rp = t / CG;
+  const int r0 = j * blk, r1 = min(S, r0 + blk);
+  const size_t row0 = (size_t)bh * S;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  float amax = 0.0f;
+  for (int r = r0 + rp; r < r1; r += RP) {
+    const v8h h = *reinterpret_cast<const v8h*>(x + (row0 + r) * D + cg * 8);
+    float f[8];
+    float m = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      f[u] = (float)h[u];
+      acc[u] += (double)f[u];
+      m = fmaxf(m, fabsf(f[u]));
+    }
+    if constexpr (FMT == THRIFT_MXFP4) {
+      m = fmaxf(m, __shfl_xor(m, 1, kWave));  // the group's four chunks
+      m = fmaxf(m, __shfl_xor(m, 2, kWave));
+      // floor(log2 amax) - 2 from the exponent field (fp16 values are normal fp32)
+      const int X = m > 0.0f ? (int)((__float_as_uint(m) >> 23) & 0xFF) - 127 - 2 : -127;
+      const float scale = m > 0.0f ? __uint_as_float((uint32_t)(X + 127) << 23) : 1.0f;
+      uint32_t d = 0;  // byte u holds elements 2u (low nibble) and 2u+1
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, f[0], f[1], scale, 0);
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, f[2], f[3], scale, 1);
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, f[4], f[5], scale, 2);
+      d = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(d, f[6], f[7], scale, 3);
+      *reinterpret_cast<uint32_t*>(codes + (row0 + r) * (D / 2) + cg * 4) = d;
+      if ((cg & 3) == 0) scales[(row0 + r) * (D / 32) + cg / 4] = (uint8_t)(X + 127);
+    } else {
+      amax = fmaxf(amax, m);
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) red[rp][cg * 8 + e] = acc[e];
+  if constexpr (FMT == THRIFT_NVFP4) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, kWave));
+    if (t % kWave == 0) redm[t / kWave] = amax;
+  }
+  __syncthreads();
+  if (t < D) {
+    double sum = 0.0;
+    for (int k = 0; k < RP; ++k) sum += red[k][t];
+    means[((size_t)bh * nb + j) * D + t] = (float)(sum / (double)(r1 - r0));
+  }
+  if constexpr (FMT == THRIFT_NVFP4)
+    if (t == 0) {
+      for (int w = 1; w < kQThreads / kWave; ++w) amax = fmaxf(amax, redm[w]);
+      part[(size_t)bh * nb + j] = amax;
+    }
+}
+
 }  // namespace thrift
 
 using namespace thrift;
@@ -338,6 +414,51 @@ extern "C" thrift_status thrift_quantize_fp4_range(const void* x16, int B, int H
       quant_s_kernel<THRIFT_MXFP4, 128><<<grid, kQThreads, 0, stream>>>(x, S, Sp, t0, nullptr, codes, scales);
     else
       quant_s_kernel<THRIFT_MXFP4, 64><<<grid, kQThreads, 0, stream>>>(x, S, Sp, t0, nullptr, codes, scales);
+  }
+  return launch_status();
+}
+
+extern "C" size_t thrift_quantize_means_workspace_bytes(int B, int H, int S, int D, thrift_format fmt,
+                                                        int blk) {
+  if (B < 1 || H < 1 || S < 1 || D < 1 || blk < 1) return 0;
+  if (fmt != THRIFT_NVFP4) return 0;
+  return (size_t)B * H * cdiv(S, blk) * sizeof(float);
+}
+
+extern "C" thrift_status thrift_quantize_fp4_means(const void* x16, int B, int H, int S, int D,
+                                                   thrift_format fmt, int blk, uint8_t* codes,
+                                                   uint8_t* scales, float* tensor_scale, float* means,
+                                                   void* workspace, size_t workspace_bytes,
+                                                   hipStream_t stream) {
+  if (!x16 || !codes || !scales || !means) return THRIFT_EINVAL;
+  if (B < 1 || H < 1 || S < 1 || blk < 1) return THRIFT_EINVAL;
+  if (fmt != THRIFT_NVFP4 && fmt != THRIFT_MXFP4) return THRIFT_EINVAL;
+  if (fmt == THRIFT_NVFP4 && !tensor_scale) return THRIFT_EINVAL;
+  if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
+  if (S > 262144 || B * H > 65535) return THRIFT_EUNSUPPORTED;
+  if (!aligned16(x16) || !aligned16(codes) || !aligned16(means)) return THRIFT_EALIGN;
+  const size_t need = thrift_quantize_means_workspace_bytes(B, H, S, D, fmt, blk);
+  if (need && (!workspace || workspace_bytes < need)) return THRIFT_EWORKSPACE;
+  const int BH = B * H, nb = cdiv(S, blk);
+  auto x = (const _Float16*)x16;
+  dim3 grid(nb, BH);
+  if (fmt == THRIFT_MXFP4) {
+    if (D == 128)
+      means_quant_kernel<128, THRIFT_MXFP4><<<grid, kQThreads, 0, stream>>>(x, S, blk, nb, means, codes, scales, nullptr);
+    else
+      means_quant_kernel<64, THRIFT_MXFP4><<<grid, kQThreads, 0, stream>>>(x, S, blk, nb, means, codes, scales, nullptr);
+  } else {
+    float* part = (float*)workspace;
+    if (D == 128)
+      means_quant_kernel<128, THRIFT_NVFP4><<<grid, kQThreads, 0, stream>>>(x, S, blk, nb, means, codes, scales, part);
+    else
+      means_quant_kernel<64, THRIFT_NVFP4><<<grid, kQThreads, 0, stream>>>(x, S, blk, nb, means, codes, scales, part);
+    slice_scale_kernel<<<cdiv(BH, 256), 256, 0, stream>>>(part, nb, BH, tensor_scale);
+    const size_t ngroups = (size_t)BH * S * (D / 16);
+    const int blocks = (int)((ngroups + kQThreads - 1) / kQThreads);
+    const int gps = S * (D / 16);
+    quant_d_kernel<THRIFT_NVFP4><<<blocks, kQThreads, 0, stream>>>(x, ngroups, gps, gps, 0, tensor_scale,
+                                                                     codes, scales);
   }
   return launch_status();
 }

@@ -223,14 +223,15 @@ extern "C" size_t thrift_select_workspace_bytes(int B, int Hq, int Hkv, int S, i
   return thrift_select_workspace_bytes_kv(B, Hq, Hkv, S, S, D, block_q, block_k);
 }
 
-// Selection from fp16 keys (k16, means computed here into the workspace) or
-// from the key means a caller keeps (kbar).
-static thrift_status select_common(const void* q16, const void* k16, const float* kbar, int B, int Hq,
-                                   int Hkv, int Sq, int Sk, int D, int block_q, int block_k,
-                                   int causal, int topk_count, int topk_bp, int32_t* idx,
+// Selection from fp16 queries and keys (q16, k16: means computed here into
+// the workspace) or from means the caller computed (qbar, kbar).
+static thrift_status select_common(const void* q16, const float* qbar, const void* k16, const float* kbar,
+                                   int B, int Hq, int Hkv, int Sq, int Sk, int D, int block_q,
+                                   int block_k, int causal, int topk_count, int topk_bp, int32_t* idx,
                                    int32_t* cnt, int kmax, void* workspace, size_t workspace_bytes,
                                    hipStream_t stream) {
-  if (!q16 || (!k16 && !kbar) || !idx || !cnt || !workspace) return THRIFT_EINVAL;
+  if ((!q16 && !qbar) || (!k16 && !kbar) || !idx || !cnt) return THRIFT_EINVAL;
+  if (!qbar && !workspace) return THRIFT_EINVAL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < Sq || (causal != 0 && causal != 1)) return THRIFT_EINVAL;
   if (Hq % Hkv != 0) return THRIFT_EINVAL;
   if (topk_count < 0 && (topk_bp < 0 || topk_bp > 10000)) return THRIFT_EINVAL;
@@ -239,15 +240,16 @@ static thrift_status select_common(const void* q16, const void* k16, const float
   if (Sk > 262144) return THRIFT_EUNSUPPORTED;
   int need = thrift_select_kmax_kv(Sq, Sk, block_q, block_k, causal, topk_count, topk_bp);
   if (kmax < need || kmax < 1) return THRIFT_EINVAL;
-  if (!aligned16(q16) || (k16 && !aligned16(k16)) || (kbar && !aligned16(kbar)) || !aligned16(workspace))
+  if ((q16 && !aligned16(q16)) || (qbar && !aligned16(qbar)) || (k16 && !aligned16(k16)) ||
+      (kbar && !aligned16(kbar)) || (workspace && !aligned16(workspace)))
     return THRIFT_EALIGN;
   const int nq = cdiv(Sq, block_q), nk = cdiv(Sk, block_k);
   const size_t qbytes = (size_t)B * Hq * nq * D * sizeof(float);
-  if (workspace_bytes < (kbar ? qbytes : thrift_select_workspace_bytes_kv(B, Hq, Hkv, Sq, Sk, D, block_q, block_k)))
-    return THRIFT_EWORKSPACE;
-  float* qm = (float*)workspace;
+  const size_t wneed = qbar ? 0 : (kbar ? qbytes : thrift_select_workspace_bytes_kv(B, Hq, Hkv, Sq, Sk, D, block_q, block_k));
+  if (workspace_bytes < wneed) return THRIFT_EWORKSPACE;
+  float* qm = qbar ? (float*)qbar : (float*)workspace;
   float* km = kbar ? (float*)kbar : (float*)((char*)workspace + ((qbytes + 255) / 256) * 256);
-  auto q = (const _Float16*)q16;
+  auto q = qbar ? nullptr : (const _Float16*)q16;
   auto k = kbar ? nullptr : (const _Float16*)k16;
   const size_t lds = (size_t)kHeadChunk * nk * sizeof(float);
   static bool configured = false;  // allow more than the default dynamic LDS for long S
@@ -260,12 +262,12 @@ static thrift_status select_common(const void* q16, const void* k16, const float
     configured = true;
   }
   if (D == 128) {
-    block_means_kernel<128><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, Sq, block_q, nq, 0, qm);
+    if (q) block_means_kernel<128><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, Sq, block_q, nq, 0, qm);
     if (k) block_means_kernel<128><<<dim3(nk, B * Hkv), kMeansThreads, 0, stream>>>(k, Sk, block_k, nk, 0, km);
     score_topk_kernel<128><<<dim3(nq, B * Hkv), kTopkThreads, lds, stream>>>(
         qm, km, Hq, Hkv, Sq, Sk, block_q, block_k, causal, topk_count, topk_bp, idx, cnt, kmax);
   } else {
-    block_means_kernel<64><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, Sq, block_q, nq, 0, qm);
+    if (q) block_means_kernel<64><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, Sq, block_q, nq, 0, qm);
     if (k) block_means_kernel<64><<<dim3(nk, B * Hkv), kMeansThreads, 0, stream>>>(k, Sk, block_k, nk, 0, km);
     score_topk_kernel<64><<<dim3(nq, B * Hkv), kTopkThreads, lds, stream>>>(
         qm, km, Hq, Hkv, Sq, Sk, block_q, block_k, causal, topk_count, topk_bp, idx, cnt, kmax);
@@ -279,8 +281,8 @@ extern "C" thrift_status thrift_select_blocks_kv(const void* q16, const void* k1
                                                  int topk_bp, int32_t* idx, int32_t* cnt, int kmax,
                                                  void* workspace, size_t workspace_bytes,
                                                  hipStream_t stream) {
-  if (!k16) return THRIFT_EINVAL;
-  return select_common(q16, k16, nullptr, B, Hq, Hkv, Sq, Sk, D, block_q, block_k, causal, topk_count,
+  if (!q16 || !k16) return THRIFT_EINVAL;
+  return select_common(q16, nullptr, k16, nullptr, B, Hq, Hkv, Sq, Sk, D, block_q, block_k, causal, topk_count,
                        topk_bp, idx, cnt, kmax, workspace, workspace_bytes, stream);
 }
 
@@ -290,9 +292,19 @@ extern "C" thrift_status thrift_select_blocks_kbar(const void* q16, const float*
                                                    int topk_bp, int32_t* idx, int32_t* cnt, int kmax,
                                                    void* workspace, size_t workspace_bytes,
                                                    hipStream_t stream) {
-  if (!kbar) return THRIFT_EINVAL;
-  return select_common(q16, nullptr, kbar, B, Hq, Hkv, Sq, Sk, D, block_q, block_k, causal, topk_count,
+  if (!q16 || !kbar) return THRIFT_EINVAL;
+  return select_common(q16, nullptr, nullptr, kbar, B, Hq, Hkv, Sq, Sk, D, block_q, block_k, causal, topk_count,
                        topk_bp, idx, cnt, kmax, workspace, workspace_bytes, stream);
+}
+
+extern "C" thrift_status thrift_select_blocks_means(const float* qbar, const float* kbar, int B, int Hq,
+                                                    int Hkv, int Sq, int Sk, int D, int block_q,
+                                                    int block_k, int causal, int topk_count,
+                                                    int topk_bp, int32_t* idx, int32_t* cnt, int kmax,
+                                                    hipStream_t stream) {
+  if (!qbar || !kbar) return THRIFT_EINVAL;
+  return select_common(nullptr, qbar, nullptr, kbar, B, Hq, Hkv, Sq, Sk, D, block_q, block_k, causal,
+                       topk_count, topk_bp, idx, cnt, kmax, nullptr, 0, stream);
 }
 
 extern "C" thrift_status thrift_block_means(const void* x16, int B, int H, int S, int D, int blk, int j0,

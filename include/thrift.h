@@ -150,6 +150,16 @@ thrift_status thrift_select_blocks_kbar(const void* q16, const float* kbar, int 
                                         int kmax, void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 
+/* Selection from query and key block means computed beforehand: qbar
+ * [B,Hq,ceil(Sq/block_q),D] fp32 (blk = block_q) and kbar
+ * [B,Hkv,ceil(Sk/block_k),D] fp32 (blk = block_k), as thrift_block_means or
+ * thrift_quantize_fp4_means write them (read only).  Same idx and cnt as
+ * thrift_select_blocks_kv on the tensors they came from; no workspace. */
+thrift_status thrift_select_blocks_means(const float* qbar, const float* kbar, int B, int Hq, int Hkv,
+                                         int Sq, int Sk, int D, int block_q, int block_k, int causal,
+                                         int topk_count, int topk_bp, int32_t* idx, int32_t* cnt,
+                                         int kmax, hipStream_t stream);
+
 /* ---------------------------------------------------------------------- */
 /* FP4 quantisation (the FP4 path's NVFP4 micro-scaling)                    */
 /* ---------------------------------------------------------------------- */
@@ -178,6 +188,22 @@ thrift_status thrift_quantize_fp4(const void* x16, int B, int H, int S, int D,
  * writes for the tensor as it is now; bytes outside those rows or tiles are
  * not touched.  MXFP4 only (an NVFP4 slice scale depends on the whole slice:
  * THRIFT_EUNSUPPORTED); 0 <= s0 < s1 <= S, else THRIFT_EINVAL. */
+/* Block means and FP4 codes along D (Q or K) from one read of x16: the
+ * selection's block means and the FP4 path's operand in a single pass
+ * (summaries "Methodologie": both come from the same fp16 Q and K).
+ *   means [B,H,ceil(S/blk),D] fp32 (out): as thrift_block_means over all
+ *     blocks, bit for bit;
+ *   codes, scales, tensor_scale (out): as thrift_quantize_fp4 with
+ *     THRIFT_GROUP_D, byte for byte.
+ * NVFP4 reads x16 twice (its slice scale must precede the codes) and needs
+ * thrift_quantize_means_workspace_bytes of workspace; MXFP4 reads it once
+ * and needs none. */
+size_t thrift_quantize_means_workspace_bytes(int B, int H, int S, int D, thrift_format fmt, int blk);
+thrift_status thrift_quantize_fp4_means(const void* x16, int B, int H, int S, int D, thrift_format fmt,
+                                        int blk, uint8_t* codes, uint8_t* scales, float* tensor_scale,
+                                        float* means, void* workspace, size_t workspace_bytes,
+                                        hipStream_t stream);
+
 thrift_status thrift_quantize_fp4_range(const void* x16, int B, int H, int S, int D,
                                         thrift_group_axis axis, thrift_format fmt, int s0, int s1,
                                         uint8_t* codes, uint8_t* scales, hipStream_t stream);

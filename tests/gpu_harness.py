@@ -16,16 +16,24 @@ def note(msg):
     sys.stdout.flush()
 
 
-def run_gpu(d, w, fmt, topk_count, topk_bp, no_fp16=False):
+def run_gpu(d, w, fmt, topk_count, topk_bp, no_fp16=False, fused=False):
+    """The path on the GPU: separate selection and quantisation calls, or
+    (fused) Q and K each read once for means and codes, as the benchmark runs it."""
     import torch
 
     from fp16_attention_amd import api
 
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(np.ascontiguousarray(d[n])).to(dev) for n in ("q", "k", "v"))
-    idx, cnt = api.thrift_select_blocks(q, k, w.bq, w.bk, w.causal, topk_count, topk_bp)
-    q4 = api.thrift_quantize_fp4(q, api.THRIFT_GROUP_D, fmt)
-    k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, fmt)
+    if fused:
+        q4, qbar = api.thrift_quantize_fp4_means(q, fmt, w.bq)
+        k4, kbar = api.thrift_quantize_fp4_means(k, fmt, w.bk)
+        idx, cnt = api.thrift_select_blocks_means(qbar, kbar, w.S, w.S, w.bq, w.bk, w.causal, topk_count,
+                                                  topk_bp)
+    else:
+        idx, cnt = api.thrift_select_blocks(q, k, w.bq, w.bk, w.causal, topk_count, topk_bp)
+        q4 = api.thrift_quantize_fp4(q, api.THRIFT_GROUP_D, fmt)
+        k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, fmt)
     v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, fmt)
     args = (None, None, None) if no_fp16 else (q, k, v)
     o, lse = api.thrift_attention_fwd(*args, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal,

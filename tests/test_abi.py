@@ -165,3 +165,31 @@ def test_cache_maintenance_validation(lib):
     assert qcall(axis=3) == 1
     assert qcall(fmt=0) == 2  # NVFP4: the slice scale spans the whole slice
     assert qcall(codes=A + 1) == 3
+
+
+def test_fused_pass_validation(lib):
+    f = lib.thrift_quantize_fp4_means
+
+    def call(x=A, S=1000, D=128, fmt=1, blk=128, ts=A, means=A, ws=A, wsb=1 << 20):
+        return f(x, 1, 2, S, D, fmt, blk, A, A, ts, means, ws, wsb, None)
+
+    assert call(means=None) == 1
+    assert call(blk=0) == 1
+    assert call(fmt=0, ts=None) == 1
+    assert call(fmt=4) == 1
+    assert call(D=96) == 2
+    assert call(means=A + 8) == 3
+    assert call(fmt=0, wsb=4) == 4
+    assert lib.thrift_quantize_means_workspace_bytes(1, 2, 1000, 128, 1, 128) == 0
+    assert lib.thrift_quantize_means_workspace_bytes(1, 2, 1000, 128, 0, 128) == 2 * 8 * 4
+
+    s = lib.thrift_select_blocks_means
+
+    def scall(qbar=A, kbar=A, Sq=1000, Sk=1000, kmax=16, bq=128):
+        return s(qbar, kbar, 1, 4, 2, Sq, Sk, 128, bq, 64, 1, -1, 1000, A, A, kmax, None)
+
+    assert scall(qbar=None) == 1
+    assert scall(Sq=2000) == 1
+    assert scall(kmax=1) == 1
+    assert scall(bq=96) == 2
+    assert scall(kbar=A + 4) == 3

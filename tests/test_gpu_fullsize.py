@@ -1,5 +1,6 @@
 """GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (same entry points, same block sizes and budgets).
+benchmark times (same entry points: Q and K each read once for block means
+and FP4 codes, selection from the means; same block sizes and budgets).
 
 Bit-exact over the whole tensors: selected block indices and counts, FP4
 codes, block scales and slice scales.  The output is compared on sampled
@@ -75,7 +76,7 @@ def test_fullsize_parity(oracle, name):
     note(f"[fullsize] {name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} S{w.S} D{w.D} causal{int(w.causal)} "
          f"bq{w.bq} bk{w.bk} fmt{fmt} topk({tc},{bp})")
     d = _data(wname)
-    g = run_gpu(d, w, fmt, tc, bp)
+    g = run_gpu(d, w, fmt, tc, bp, fused=True)
     idx, cnt, _ = oracle.select(d["q"], d["k"], w.bq, w.bk, w.causal, tc, bp)
     assert np.array_equal(g["cnt"], cnt), "cnt differs"
     km = idx.shape[-1]
