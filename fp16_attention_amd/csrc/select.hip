@@ -6,10 +6,10 @@
 //  - block_means reads every fp16 element of Q and K once (coalesced 16-byte
 //    loads) and sums in fp64, which is exact in any order, so the means are
 //    bit-identical to any other exact summation;
-//  - score_topk gives one workgroup to each (batch, key head, query block);
-//    each thread scores one key block against up to four query heads of the
-//    GQA group at once (each kbar row read once per four heads, all of it in
-//    flight at once), then each head's row of scores goes to one wavefront,
+//  - score_topk gives one workgroup to each (batch, key head, run of up to
+//    four query blocks); each thread scores one key block against up to four
+//    query heads of the GQA group in each of those query blocks (each kbar
+//    row read once per sixteen score rows, all of it in flight at once), then each head's row of scores goes to one wavefront,
 //    which finds the k-th largest score by a bitwise search counted with
 //    ballots, breaks ties at it by lower block index, and writes the blocks
 //    in ascending order by ballot compaction: no workgroup barrier in the
@@ -118,76 +118,107 @@ __device__ inline void wave_topk(const float* srow, int n, int k, int32_t* __res
 constexpr int kTopkThreads = 256;
 constexpr int kHeadChunk = 4;  // query heads scored together per pass
 
-template <int D>
+// QB consecutive query blocks share a workgroup, so each k̄ row is read once
+// for QB x (up to) four query-head rows.
+template <int D, int QB>
 __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
     const float* __restrict__ qm, const float* __restrict__ km, int Hq, int Hkv, int Sq, int Sk, int bq,
     int bk, int causal, int topk_count, int topk_bp, int32_t* __restrict__ idx,
     int32_t* __restrict__ cnt, int kmax) {
-  extern __shared__ float sc[];  // [kHeadChunk][nK] scores
-  __shared__ __attribute__((aligned(16))) float qv[kHeadChunk][D];
+  constexpr int NR = QB * kHeadChunk;  // score rows per pass: (query block, head)
+  extern __shared__ float sc[];         // [NR][nK] scores
+  __shared__ __attribute__((aligned(16))) float qv[NR][D];
 
   const int t = threadIdx.x, lane = t % kWave, wave = t / kWave;
-  const int i = blockIdx.x, bhk = blockIdx.y;
+  const int i0 = blockIdx.x * QB, bhk = blockIdx.y;
   const int b = bhk / Hkv, hk = bhk % Hkv, G = Hq / Hkv;
   const int nq = cdiv(Sq, bq), nK = cdiv(Sk, bk);
-  const int n = valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal);
-  const int k = topk_budget(n, topk_count, topk_bp);
+  const int nqb = min(QB, nq - i0);  // query blocks of this workgroup
+  // valid key blocks grow with the query block under causal masking
+  const int nmax = valid_kv_blocks_kv(i0 + nqb - 1, Sq, Sk, bq, bk, causal);
   const float* kbase = km + (size_t)bhk * nK * D;
 
   for (int h0 = 0; h0 < G; h0 += kHeadChunk) {
     const int nh = min(kHeadChunk, G - h0);
     __syncthreads();
-    for (int e = t; e < kHeadChunk * D; e += kTopkThreads) {
-      int h = e / D, d = e % D;
-      int hq = hk * G + h0 + h;
-      qv[h][d] = h < nh ? qm[(((size_t)b * Hq + hq) * nq + i) * D + d] : 0.0f;
+    for (int e = t; e < NR * D; e += kTopkThreads) {
+      const int rr = e / D, d = e % D, qb = rr / kHeadChunk, h = rr % kHeadChunk;
+      const int hq = hk * G + h0 + h;
+      qv[rr][d] = (h < nh && qb < nqb) ? qm[(((size_t)b * Hq + hq) * nq + i0 + qb) * D + d] : 0.0f;
     }
     __syncthreads();
     // scores: one key block per thread, its whole mean row loaded at once
     // (independent loads, one memory latency per 256 blocks), then an fp32
-    // FMA chain over ascending channels per head
-    for (int jc = 0; jc < n; jc += kTopkThreads) {
+    // FMA chain over ascending channels per (query block, head) row
+    for (int jc = 0; jc < nmax; jc += kTopkThreads) {
       const int j = jc + t;
-      if (j < n) {
+      if (j < nmax) {
         const float4* kr = reinterpret_cast<const float4*>(kbase + (size_t)j * D);
-        float s[kHeadChunk];
+        float s[NR];
 #pragma unroll
-        for (int h = 0; h < kHeadChunk; ++h) s[h] = 0.0f;
-        // the whole key row in flight at once; the scheduling barriers keep
-        // the compiler from reading every query mean (4 x D floats) ahead of
-        // the FMAs, which would not fit in registers
+        for (int r = 0; r < NR; ++r) s[r] = 0.0f;
         float4 kv[D / 4];
 #pragma unroll
         for (int c = 0; c < D / 4; ++c) kv[c] = kr[c];
+        // the scheduling barriers keep the compiler from reading every
+        // query mean (NR x D floats) ahead of the FMAs, which would not fit
+        // in registers
 #pragma unroll
         for (int c = 0; c < D / 4; ++c) {
 #pragma unroll
-          for (int h = 0; h < kHeadChunk; ++h) {
-            const float4 qq = *reinterpret_cast<const float4*>(&qv[h][4 * c]);
-            s[h] = __builtin_fmaf(qq.x, kv[c].x, s[h]);
-            s[h] = __builtin_fmaf(qq.y, kv[c].y, s[h]);
-            s[h] = __builtin_fmaf(qq.z, kv[c].z, s[h]);
-            s[h] = __builtin_fmaf(qq.w, kv[c].w, s[h]);
+          for (int r = 0; r < NR; ++r) {
+            const float4 qq = *reinterpret_cast<const float4*>(&qv[r][4 * c]);
+            s[r] = __builtin_fmaf(qq.x, kv[c].x, s[r]);
+            s[r] = __builtin_fmaf(qq.y, kv[c].y, s[r]);
+            s[r] = __builtin_fmaf(qq.z, kv[c].z, s[r]);
+            s[r] = __builtin_fmaf(qq.w, kv[c].w, s[r]);
           }
           __builtin_amdgcn_sched_barrier(0);
         }
-        // every row of sc is written (rows h >= nh are never read): a store
-        // under "h < nh" would let the compiler sink the FMA chains below
-        // all the query-mean reads
+        // every row of sc is written (rows past the valid ones are never
+        // read): a conditional store would let the compiler sink the FMA
+        // chains below all the query-mean reads
 #pragma unroll
-        for (int h = 0; h < kHeadChunk; ++h) sc[h * nK + j] = s[h];
+        for (int r = 0; r < NR; ++r) sc[r * nK + j] = s[r];
       }
     }
     __syncthreads();
 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    for (int h = wave_u; h < nh; h += kTopkThreads / kWave) {  // one wavefront per head row
-      const int hq = hk * G + h0 + h;
+    for (int rr = wave_u; rr < NR; rr += kTopkThreads / kWave) {  // one wavefront per row
+      const int qb = rr / kHeadChunk, h = rr % kHeadChunk;
+      if (qb >= nqb || h >= nh) continue;
+      const int i = i0 + qb, hq = hk * G + h0 + h;
+      const int n = valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal);
+      const int k = topk_budget(n, topk_count, topk_bp);
       const size_t row = ((size_t)b * Hq + hq) * nq + i;
-      wave_topk(sc + h * nK, n, k, idx + row * kmax, kmax, lane);
+      wave_topk(sc + rr * nK, n, k, idx + row * kmax, kmax, lane);
       if (lane == 0) cnt[row] = k;
     }
   }
+}
+
+// Query blocks per workgroup: as many as keep the score rows within 64 KB of
+// LDS, and one when there are few query blocks (the workgroups are then few
+// and their length, not the k̄ reads, sets the time).
+inline int topk_qb(int nq, int nk) { return nq < 64 ? 1 : (nk <= 1024 ? (nk <= 512 ? 4 : 2) : 1); }
+
+template <int D>
+void launch_score_topk(const float* qm, const float* km, int B, int Hq, int Hkv, int Sq, int Sk, int bq, int bk,
+                       int causal, int topk_count, int topk_bp, int32_t* idx, int32_t* cnt, int kmax,
+                       hipStream_t stream) {
+  const int nq = cdiv(Sq, bq), nk = cdiv(Sk, bk), qb = topk_qb(nq, nk);
+  const size_t lds = (size_t)qb * kHeadChunk * nk * sizeof(float);
+  const dim3 grid(cdiv(nq, qb), B * Hkv);
+  if (qb == 4)
+    score_topk_kernel<D, 4><<<grid, kTopkThreads, lds, stream>>>(qm, km, Hq, Hkv, Sq, Sk, bq, bk, causal,
+                                                                 topk_count, topk_bp, idx, cnt, kmax);
+  else if (qb == 2)
+    score_topk_kernel<D, 2><<<grid, kTopkThreads, lds, stream>>>(qm, km, Hq, Hkv, Sq, Sk, bq, bk, causal,
+                                                                 topk_count, topk_bp, idx, cnt, kmax);
+  else
+    score_topk_kernel<D, 1><<<grid, kTopkThreads, lds, stream>>>(qm, km, Hq, Hkv, Sq, Sk, bq, bk, causal,
+                                                                 topk_count, topk_bp, idx, cnt, kmax);
 }
 
 }  // namespace thrift
@@ -251,26 +282,26 @@ static thrift_status select_common(const void* q16, const float* qbar, const voi
   float* km = kbar ? (float*)kbar : (float*)((char*)workspace + ((qbytes + 255) / 256) * 256);
   auto q = qbar ? nullptr : (const _Float16*)q16;
   auto k = kbar ? nullptr : (const _Float16*)k16;
-  const size_t lds = (size_t)kHeadChunk * nk * sizeof(float);
   static bool configured = false;  // allow more than the default dynamic LDS for long S
   if (!configured) {
-    if (hipFuncSetAttribute((const void*)score_topk_kernel<128>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024) != hipSuccess ||
-        hipFuncSetAttribute((const void*)score_topk_kernel<64>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024) != hipSuccess)
-      return THRIFT_EHIP;
+    const void* kernels[] = {(const void*)score_topk_kernel<128, 1>, (const void*)score_topk_kernel<128, 2>,
+                             (const void*)score_topk_kernel<128, 4>, (const void*)score_topk_kernel<64, 1>,
+                             (const void*)score_topk_kernel<64, 2>, (const void*)score_topk_kernel<64, 4>};
+    for (const void* kf : kernels)
+      if (hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024) != hipSuccess)
+        return THRIFT_EHIP;
     configured = true;
   }
   if (D == 128) {
     if (q) block_means_kernel<128><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, Sq, block_q, nq, 0, qm);
     if (k) block_means_kernel<128><<<dim3(nk, B * Hkv), kMeansThreads, 0, stream>>>(k, Sk, block_k, nk, 0, km);
-    score_topk_kernel<128><<<dim3(nq, B * Hkv), kTopkThreads, lds, stream>>>(
-        qm, km, Hq, Hkv, Sq, Sk, block_q, block_k, causal, topk_count, topk_bp, idx, cnt, kmax);
+    launch_score_topk<128>(qm, km, B, Hq, Hkv, Sq, Sk, block_q, block_k, causal, topk_count, topk_bp, idx, cnt,
+                           kmax, stream);
   } else {
     if (q) block_means_kernel<64><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, Sq, block_q, nq, 0, qm);
     if (k) block_means_kernel<64><<<dim3(nk, B * Hkv), kMeansThreads, 0, stream>>>(k, Sk, block_k, nk, 0, km);
-    score_topk_kernel<64><<<dim3(nq, B * Hkv), kTopkThreads, lds, stream>>>(
-        qm, km, Hq, Hkv, Sq, Sk, block_q, block_k, causal, topk_count, topk_bp, idx, cnt, kmax);
+    launch_score_topk<64>(qm, km, B, Hq, Hkv, Sq, Sk, block_q, block_k, causal, topk_count, topk_bp, idx, cnt,
+                          kmax, stream);
   }
   return launch_status();
 }

@@ -74,3 +74,22 @@ def test_select_from_means(oracle, Sq, Sk, causal):
     ridx, rcnt, _ = oracle.select(q, k, 128, 64, causal, -1, 1500)
     assert np.array_equal(cnt_a.cpu().numpy(), rcnt)
     assert np.array_equal(idx_a.cpu().numpy()[..., : ridx.shape[-1]], ridx)
+
+
+@pytest.mark.parametrize("S,causal", [(8300, True), (40000, True), (40000, False)])
+def test_select_query_block_runs(oracle, S, causal):
+    """Selection when several query blocks share a workgroup: a ragged last
+    run (65 query blocks in runs of four) and runs of two (625 key blocks)."""
+    import torch
+
+    from fp16_attention_amd import api
+
+    note(f"[fused] select, query-block runs: S{S} causal{int(causal)}")
+    q = _tensor((1, 4, S, 64), 3)
+    k = _tensor((1, 1, S, 64), 4)
+    qd, kd = torch.from_numpy(q).to("cuda:0"), torch.from_numpy(k).to("cuda:0")
+    idx, cnt = api.thrift_select_blocks(qd, kd, 128, 64, causal, -1, 300)
+    torch.cuda.synchronize()
+    ridx, rcnt, _ = oracle.select(q, k, 128, 64, causal, -1, 300)
+    assert np.array_equal(cnt.cpu().numpy(), rcnt)
+    assert np.array_equal(idx.cpu().numpy()[..., : ridx.shape[-1]], ridx)
