@@ -341,10 +341,9 @@ __device__ inline void qk_f16(v16f s[2], const char* stage, const v8h* qh, int l
 // O^T += V^T P^T over four 16-key steps; in step st this lane supplies
 // keys hi*32 + 8*st + u (u = 0..7), its registers 8*(st%2)+u of tile st/2.
 template <int D>
-__device__ inline void pv_f16(RowState<D>& st, const char* stage, const v8h* pB, int lane) {
+__device__ inline void pv_f16(RowState<D>& st, const _Float16* vt, const v8h* pB, int lane) {
   using L = Lds<D>;
   const int hi = lane >> 5, r32 = lane & 31;
-  const _Float16* vt = (const _Float16*)(stage + L::VT);
 #pragma unroll
   for (int stp = 0; stp < 4; ++stp)
 #pragma unroll
@@ -354,13 +353,12 @@ __device__ inline void pv_f16(RowState<D>& st, const char* stage, const v8h* pB,
     }
 }
 
-// Promoted tile: fp16 scores, probabilities rounded to fp16.
+// Promoted tile after its scores: mask, probabilities rounded to fp16, times
+// fp16 V^T (vt: D rows of Lds<D>::VROWH halves).
 template <int D>
-__device__ inline void fp16_tile(RowState<D>& st, const char* stage, const v8h* qh, float c, int key0,
-                                 int qrow, int S, int causal, bool need_mask, int lane) {
+__device__ inline void fp16_softmax_pv(RowState<D>& st, v16f s[2], const _Float16* vt, float c, int key0,
+                                       int qrow, int S, int causal, bool need_mask, int lane) {
   const int hi = lane >> 5;
-  v16f s[2];
-  qk_f16<D>(s, stage, qh, lane);
   if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
   maybe_rescale<D>(st, fmaxf(max16(s[0]), max16(s[1])), c);
   const float nm = -st.m;
@@ -375,7 +373,16 @@ __device__ inline void fp16_tile(RowState<D>& st, const char* stage, const v8h* 
       pB[mt * 2 + i / 8][i % 8] = (_Float16)p;
     }
   st.l += lsum;
-  pv_f16<D>(st, stage, pB, lane);
+  pv_f16<D>(st, vt, pB, lane);
+}
+
+// Promoted tile: fp16 scores, probabilities rounded to fp16.
+template <int D>
+__device__ inline void fp16_tile(RowState<D>& st, const char* stage, const v8h* qh, float c, int key0,
+                                 int qrow, int S, int causal, bool need_mask, int lane) {
+  v16f s[2];
+  qk_f16<D>(s, stage, qh, lane);
+  fp16_softmax_pv<D>(st, s, (const _Float16*)(stage + Lds<D>::VT), c, key0, qrow, S, causal, need_mask, lane);
 }
 
 // NVFP4 FP4 tile: scores from the dequantised fp16 stage, P quantised in two
@@ -439,7 +446,7 @@ __device__ inline void fp4_nv_tile(RowState<D>& st, const char* stage, const v8h
       pB[g * 2 + h] = v8h{lo.x, lo.y, lo.z, lo.w, hi4.x, hi4.y, hi4.z, hi4.w};
     }
   }
-  pv_f16<D>(st, stage, pB, lane);
+  pv_f16<D>(st, (const _Float16*)(stage + Lds<D>::VT), pB, lane);
 }
 
 }  // namespace thrift
@@ -1147,18 +1154,57 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeArgs d) {
   st.l = 0.0f;
   st.g = 1.0f;
   if (j >= 0 && j < d.nvalid) {
-    // the query rows are loaded together with the tile (one memory latency)
+    // Every load goes out first: the query rows; K in MFMA operand order
+    // (the rows krow(mt, r32), 16-byte chunks straight into registers, no
+    // LDS); V as (key pair, 8 channels) items, transposed into LDS below.
+    // Rows past the cache's end read as zeros through the buffer resources'
+    // record counts (their scores are masked).
+    using L = Lds<D>;
+    constexpr int w3 = 0x00020000;  // raw buffer, 32-bit data format
+    const int r32 = lane & 31;
+    const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k16 + bhk * Sk * D), 0, Sk * D * 2, w3);
+    const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v16 + bhk * Sk * D), 0, Sk * D * 2, w3);
     v8h qh[D / 16];
     const size_t qoff = (bhq * Sq + r) * D + hi * 8;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qh[kk] = col < Sq ? *(const v8h*)(a.q16 + qoff + kk * 16) : v8h{};
-    F16Stager<D, 64> stg;
-    stg.load(a, bhk, j, lane);
-    stg.store(smem, lane);
+    v8h ka[2][D / 16];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk)
+        ka[mt][kk] = __builtin_bit_cast(
+            v8h, __builtin_amdgcn_raw_buffer_load_b128(krs, ((j * kBk + krow(mt, r32)) * D + kk * 16 + hi * 8) * 2, 0, 0));
+    constexpr int PV = (kBk / 2) * (D / 8) / 64;
+    v4i v0[PV], v1[PV];
+#pragma unroll
+    for (int p = 0; p < PV; ++p) {
+      const int c = lane + p * 64, kp = c % (kBk / 2), cv = (c / (kBk / 2)) * 8, key = j * kBk + 2 * kp;
+      v0[p] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(vrs, (key * D + cv) * 2, 0, 0));
+      v1[p] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(vrs, ((key + 1) * D + cv) * 2, 0, 0));
+    }
+    _Float16* vt = (_Float16*)smem;  // V^T: D rows of VROWH halves
+#pragma unroll
+    for (int p = 0; p < PV; ++p) {
+      const int c = lane + p * 64, kp = c % (kBk / 2), cv = (c / (kBk / 2)) * 8;
+      uint32_t* dst = (uint32_t*)(vt + cv * L::VROWH + 2 * kp);
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {  // channels 2w, 2w+1: (key, key+1) half pairs
+        dst[(2 * w) * (L::VROWH / 2)] = __builtin_amdgcn_perm((uint32_t)v1[p][w], (uint32_t)v0[p][w], 0x05040100u);
+        dst[(2 * w + 1) * (L::VROWH / 2)] = __builtin_amdgcn_perm((uint32_t)v1[p][w], (uint32_t)v0[p][w], 0x07060302u);
+      }
+    }
     __syncthreads();
+    v16f sc[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      sc[mt] = v16f{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) sc[mt] = mfma_f16(ka[mt][kk], qh[kk], sc[mt]);
+    }
     const int key0 = j * kBk;
     const bool need_mask = (a.causal && key0 + kBk - 1 > Sk - Sq) || key0 + kBk > Sk;
-    fp16_tile<D>(st, smem, qh, a.sm_log2, key0, qpos, Sk, a.causal, need_mask, lane);
+    fp16_softmax_pv<D>(st, sc, vt, a.sm_log2, key0, qpos, Sk, a.causal, need_mask, lane);
   }
   if (col < Sq) store_partial<D>(d.part16 + ((bhq * a.kmax + p) * Sq + col) * kPartStride<D>, st, lane);
 }
@@ -1356,7 +1402,7 @@ static thrift_status launch_decode(DecodeArgs& d, hipStream_t stream) {
   }
   const size_t lds4 = 4 * (size_t)M::SIZE + (size_t)d.G * ((d.nvalid + 31) / 32) * 4;
   decode_fp4_kernel<D><<<a.B * a.Hkv * d.nsplit, kDecWaves * 64, lds4, stream>>>(d);
-  decode_f16_kernel<D><<<a.B * a.Hq * a.kmax, 64, Lds<D>::STAGE, stream>>>(d);
+  decode_f16_kernel<D><<<a.B * a.Hq * a.kmax, 64, D * Lds<D>::VROWH * 2, stream>>>(d);
   decode_merge_kernel<D><<<a.B * a.Hq * d.Sq, kMergeThreads, 0, stream>>>(d);
   return launch_status();
 }
