@@ -73,6 +73,8 @@ def _declare(L):
     L.tho_kmax_kv.argtypes = [_I] * 7
     L.tho_select_kv.restype = None
     L.tho_select_kv.argtypes = [_P, _P] + [_I] * 11 + [_P, _P, _I, _P]
+    L.tho_select_head_kv.restype = None
+    L.tho_select_head_kv.argtypes = [_P, _P] + [_I] * 11 + [_P, _P, _I]
     L.tho_quantize.restype = None
     L.tho_quantize.argtypes = [_P, _I, _I, _I, _I, _I, _I, _P, _P, _P]
     L.tho_dequantize.restype = None
@@ -185,6 +187,29 @@ def select(q16, k16, bq, bk, causal, topk_count=-1, topk_bp=0, kmax_=None, with_
     lib().tho_select_kv(_ptr(q16), _ptr(k16), B, Hq, Hkv, S, Sk, D, bq, bk, int(causal), topk_count,
                         topk_bp, _ptr(idx), _ptr(cnt), km, _ptr(scores))
     return idx, cnt, scores
+
+
+def kmax_head(S, bq, bk, causal, Sk=None) -> int:
+    """Row length that always holds a per-head selection: the largest n_i."""
+    Sk = S if Sk is None else Sk
+    nq = -(-S // bq)
+    return max(((Sk - S + min(S, (i + 1) * bq) - 1) // bk + 1) if causal else -(-Sk // bk) for i in range(nq))
+
+
+def select_head(q16, k16, bq, bk, causal, topk_count=-1, topk_bp=0, kmax_=None):
+    """One budget per query head over all its valid block pairs: returns
+    (idx [B,Hq,nQ,kmax] int32, cnt [B,Hq,nQ] int32)."""
+    q16 = _c(q16, np.float16)
+    k16 = _c(k16, np.float16)
+    B, Hq, S, D = q16.shape
+    Hkv, Sk = k16.shape[1], k16.shape[2]
+    nq = -(-S // bq)
+    km = kmax_head(S, bq, bk, causal, Sk) if kmax_ is None else kmax_
+    idx = np.empty((B, Hq, nq, km), np.int32)
+    cnt = np.empty((B, Hq, nq), np.int32)
+    lib().tho_select_head_kv(_ptr(q16), _ptr(k16), B, Hq, Hkv, S, Sk, D, bq, bk, int(causal), topk_count,
+                             topk_bp, _ptr(idx), _ptr(cnt), km)
+    return idx, cnt
 
 
 # ---- quantisation -----------------------------------------------------------

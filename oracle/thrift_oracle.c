@@ -279,6 +279,75 @@ void tho_select_kv(const uint16_t* q16, const uint16_t* k16, int B, int Hq, int 
   free(qm);
 }
 
+typedef struct {
+  float s;
+  int i, j;
+} tho_pair;
+
+/* Higher score first; equal scores (with -0 == +0) by lower query block, then lower key block. */
+static int tho_pair_cmp(const void* a, const void* b) {
+  const tho_pair* x = (const tho_pair*)a;
+  const tho_pair* y = (const tho_pair*)b;
+  if (x->s > y->s) return -1;
+  if (x->s < y->s) return 1;
+  if (x->i != y->i) return x->i - y->i;
+  return x->j - y->j;
+}
+
+/* Per-head budget: the other reading of "the top-k highest-scoring block
+ * pairs" (ThriftAttention summaries, "Heuristische Blokkenselectie"), one
+ * budget over all valid pairs of a query head: K = min(P, topk_count) or
+ * ceil(P * topk_bp / 10^4) of its P valid pairs, the K best-scoring pairs
+ * kept.  Scores as tho_select_kv.  idx [B, Hq, nQ, kmax]: each query block's
+ * kept key blocks ascending, padded with -1; cnt [B, Hq, nQ]: their number.
+ * kmax must be at least the largest count (at most the largest n_i). */
+void tho_select_head_kv(const uint16_t* q16, const uint16_t* k16, int B, int Hq, int Hkv, int Sq,
+                        int Sk, int D, int bq, int bk, int causal, int topk_count, int topk_bp,
+                        int32_t* idx, int32_t* cnt, int kmax) {
+  int nq = tho_cdiv(Sq, bq), nk = tho_cdiv(Sk, bk), G = Hq / Hkv;
+  float* qm = (float*)malloc(sizeof(float) * (size_t)B * Hq * nq * D);
+  float* km = (float*)malloc(sizeof(float) * (size_t)B * Hkv * nk * D);
+  tho_block_means(q16, B, Hq, Sq, D, bq, qm);
+  tho_block_means(k16, B, Hkv, Sk, D, bk, km);
+  tho_pair* cand = (tho_pair*)malloc(sizeof(tho_pair) * (size_t)nq * nk);
+  unsigned char* keep = (unsigned char*)malloc((size_t)nq * nk);
+  for (int b = 0; b < B; ++b)
+    for (int hq = 0; hq < Hq; ++hq) {
+      int hk = hq / G;
+      long long P = 0;
+      for (int i = 0; i < nq; ++i) {
+        const float* qv = qm + (((size_t)b * Hq + hq) * nq + i) * D;
+        int n = tho_valid_blocks_kv(i, Sq, Sk, bq, bk, causal);
+        for (int j = 0; j < n; ++j) {
+          cand[P].s = tho_block_score(qv, km + (((size_t)b * Hkv + hk) * nk + j) * D, D);
+          cand[P].i = i;
+          cand[P].j = j;
+          ++P;
+        }
+      }
+      long long K = topk_count >= 0 ? (long long)topk_count : (P * topk_bp + 9999) / 10000;
+      if (K > P) K = P;
+      qsort(cand, (size_t)P, sizeof(tho_pair), tho_pair_cmp);
+      memset(keep, 0, (size_t)nq * nk);
+      for (long long t = 0; t < K; ++t) keep[(size_t)cand[t].i * nk + cand[t].j] = 1;
+      for (int i = 0; i < nq; ++i) {
+        size_t row = ((size_t)b * Hq + hq) * nq + i;
+        int c = 0;
+        for (int j = 0; j < nk; ++j)
+          if (keep[(size_t)i * nk + j]) {
+            if (c < kmax) idx[row * kmax + c] = j;
+            ++c;
+          }
+        for (int t = c; t < kmax; ++t) idx[row * kmax + t] = -1;
+        cnt[row] = c;
+      }
+    }
+  free(keep);
+  free(cand);
+  free(km);
+  free(qm);
+}
+
 void tho_select(const uint16_t* q16, const uint16_t* k16, int B, int Hq, int Hkv, int S, int D,
                 int bq, int bk, int causal, int topk_count, int topk_bp, int32_t* idx,
                 int32_t* cnt, int kmax, float* scores) {

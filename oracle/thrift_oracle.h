@@ -35,6 +35,10 @@ void tho_select(const uint16_t* q16, const uint16_t* k16, int B, int Hq, int Hkv
 void tho_select_kv(const uint16_t* q16, const uint16_t* k16, int B, int Hq, int Hkv, int Sq, int Sk,
                    int D, int bq, int bk, int causal, int topk_count, int topk_bp, int32_t* idx,
                    int32_t* cnt, int kmax, float* scores);
+/* One budget per query head over all its valid pairs (K = ceil(P bp / 10^4)). */
+void tho_select_head_kv(const uint16_t* q16, const uint16_t* k16, int B, int Hq, int Hkv, int Sq,
+                        int Sk, int D, int bq, int bk, int causal, int topk_count, int topk_bp,
+                        int32_t* idx, int32_t* cnt, int kmax);
 
 void tho_quantize(const uint16_t* x16, int B, int H, int S, int D, int axis, int fmt,
                   uint8_t* codes, uint8_t* scales, float* tensor_scale);

@@ -17,7 +17,10 @@ SRC = os.path.join(ROOT, "oracle", "thrift_oracle.c")
 MUTANTS = {
     "no_rescale_fp4": ("acc[d] = alpha * acc[d] + w * pv;", "acc[d] = acc[d] + w * pv;"),
     "mx_level1_not_integer": ("double z = ceil(mt);", "double z = mt;"),
-    "topk_ascending": ("if (x->s > y->s) return -1;", "if (x->s > y->s) return 1;"),
+    "topk_ascending": ("const tho_cand* y = (const tho_cand*)b;\n  if (x->s > y->s) return -1;",
+                       "const tho_cand* y = (const tho_cand*)b;\n  if (x->s > y->s) return 1;"),
+    "head_budget_ascending": ("const tho_pair* y = (const tho_pair*)b;\n  if (x->s > y->s) return -1;",
+                              "const tho_pair* y = (const tho_pair*)b;\n  if (x->s > y->s) return 1;"),
     "decode_start_aligned": ("int qpos = Sk - S + r;", "int qpos = r;"),
     "decode_valid_blocks_start_aligned": ("return (Sk - Sq + last_q) / bk + 1;", "return last_q / bk + 1;"),
     "e2m1_ties_up": ("if (a > t || (a == t && ((k + 1) & 1) == 0)) code = k + 1;",
@@ -31,6 +34,9 @@ MUTANTS = {
     "e4m3_no_saturation_tie": ("if (num > t || (num == t && ((k + 1) & 1) == 0))",
                                "if (num > t || (num == t && ((k + 1) & 1) == 1))"),
     "nvfp4_level1_scale": ("2688.0 * exp2(t[c] - mt);", "448.0 * exp2(t[c] - mt);"),
+    "head_budget_ties_late_block_first": ("if (x->i != y->i) return x->i - y->i;",
+                                          "if (x->i != y->i) return y->i - x->i;"),
+    "head_budget_floor": ("(P * topk_bp + 9999) / 10000", "(P * topk_bp) / 10000"),
     "gqa_head_map": ("int hk = hq / (a->Hq / a->Hkv);", "int hk = hq % a->Hkv;"),
     "fp16_pass_skips_alpha": ("      acc[d] = alpha * acc[d] + pv;\n    }\n    m = m_new;\n  }\n\n  for (int d = 0;",
                               "      acc[d] = acc[d] + pv;\n    }\n    m = m_new;\n  }\n\n  for (int d = 0;"),
@@ -51,6 +57,7 @@ def test_mutant_is_caught(tmp_path, name):
     env = dict(os.environ, THRIFT_ORACLE_LIB=lib)
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_formats.py", "tests/test_oracle_select.py",
-                        "tests/test_oracle_attention.py", "tests/test_oracle_decode.py"],
+                        "tests/test_oracle_attention.py", "tests/test_oracle_decode.py",
+                        "tests/test_oracle_select_head.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
