@@ -115,6 +115,8 @@ def main():
     ap.add_argument("--workload", default="long")
     ap.add_argument("--fmt", default="mx", choices=["mx", "nvfp4"])
     ap.add_argument("--topk-bp", type=int, default=None)
+    ap.add_argument("--budget", default="block", choices=["block", "head"],
+                    help="top-k per query block (default) or one budget per query head")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -143,7 +145,12 @@ def main():
         return run_decode(args, w, d, gen_s)
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v"))
-    kmax = max(1, api.thrift_select_kmax(w.S, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp))
+    if args.budget == "head":
+        select = api.thrift_select_blocks_head
+        kmax = api._lib.load().thrift_select_head_kmax(w.S, w.S, w.bq, w.bk, int(w.causal))
+    else:
+        select = api.thrift_select_blocks_means
+        kmax = max(1, api.thrift_select_kmax(w.S, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp))
     o = torch.empty_like(q)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -160,8 +167,7 @@ def main():
         v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, fmt)
         if rec:
             rec[1].record()
-        idx, cnt = api.thrift_select_blocks_means(qbar, kbar, w.S, w.S, w.bq, w.bk, w.causal, w.topk_count,
-                                                  w.topk_bp, kmax)
+        idx, cnt = select(qbar, kbar, w.S, w.S, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp, kmax)
         if rec:
             rec[2].record()
         api.thrift_attention_fwd(q, k, v, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal, out=o)
@@ -212,7 +218,8 @@ def main():
             "workload": f"{w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} S{w.S} D{w.D} "
                         f"{'causal' if w.causal else 'non-causal'} blocks {w.bq}x{w.bk} "
                         f"top-k {w.topk_bp / 100 if w.topk_count < 0 else w.topk_count}"
-                        f"{'%' if w.topk_count < 0 else ' per query block'} {args.fmt}",
+                        f"{'%' if w.topk_count < 0 else ' per query block'} {args.fmt}"
+                        f"{', one budget per query head' if args.budget == 'head' else ''}",
             "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)",
         },
         "roofline": {
@@ -233,7 +240,7 @@ def main():
         "input_gen_s": round(gen_s, 1),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, d, fmt)
+        line["cpu_baseline"] = cpu_baseline(w, d, fmt, args.budget)
     s = json.dumps(line)
     print(s, flush=True)
     if args.out:
@@ -367,7 +374,7 @@ def run_decode(args, w, d, gen_s):
             f.write(s + "\n")
 
 
-def cpu_baseline(w, d, fmt):
+def cpu_baseline(w, d, fmt, budget="block"):
     """The oracle on one query head (and its key head) of the same workload:
     selection, quantisation of that head's Q, K, V and the forward pass."""
     from oracle import oracle as O
@@ -378,12 +385,17 @@ def cpu_baseline(w, d, fmt):
     v1 = np.ascontiguousarray(d["v"][:1, :1])
     O.lib()
     t0 = time.perf_counter()
-    O.pipeline(q1, k1, v1, fmt, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
+    if budget == "head":
+        idx, cnt = O.select_head(q1, k1, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
+        q4, k4, v4 = (O.quantize(x, ax, fmt) for x, ax in ((q1, O.AXIS_D), (k1, O.AXIS_D), (v1, O.AXIS_S)))
+        O.attention(q1, k1, v1, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal)
+    else:
+        O.pipeline(q1, k1, v1, fmt, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
     sec = time.perf_counter() - t0
     f = 4.0 * w.D * unmasked_pairs(w.S, w.causal)
     return {"value": round(f / sec / 1e12, 5), "unit": "TFLOP/s", "cores": nthreads,
             "kind": "oracle", "seconds": round(sec, 2),
-            "sample": f"query head 0 of batch 0 with its key head: selection, FP4 quantisation of "
+            "sample": f"query head 0 of batch 0 with its key head: selection ({budget} budget), FP4 quantisation of "
                       f"its Q/K/V and the forward pass over all {-(-w.S // w.bq)} query blocks "
                       f"({f / 1e9:.1f} GFLOP of attention), fp64"}
 

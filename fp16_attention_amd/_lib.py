@@ -12,6 +12,7 @@ THRIFT_GROUP_D, THRIFT_GROUP_S = 0, 1
 EXPORTS = ("thrift_select_kmax", "thrift_select_workspace_bytes", "thrift_select_blocks",
            "thrift_select_kmax_kv", "thrift_select_workspace_bytes_kv", "thrift_select_blocks_kv",
            "thrift_block_means", "thrift_select_blocks_kbar", "thrift_select_blocks_means",
+           "thrift_select_head_kmax", "thrift_select_head_workspace_bytes", "thrift_select_blocks_head",
            "thrift_quantize_means_workspace_bytes", "thrift_quantize_fp4_means",
            "thrift_quantize_workspace_bytes", "thrift_quantize_fp4", "thrift_quantize_fp4_range",
            "thrift_attention_fwd",
@@ -59,6 +60,12 @@ def load():
         L.thrift_quantize_means_workspace_bytes.argtypes = [I] * 6
         L.thrift_quantize_fp4_means.restype = I
         L.thrift_quantize_fp4_means.argtypes = [P] + [I] * 6 + [P, P, P, P, P, SZ, P]
+        L.thrift_select_head_kmax.restype = I
+        L.thrift_select_head_kmax.argtypes = [I] * 5
+        L.thrift_select_head_workspace_bytes.restype = SZ
+        L.thrift_select_head_workspace_bytes.argtypes = [I] * 6
+        L.thrift_select_blocks_head.restype = I
+        L.thrift_select_blocks_head.argtypes = [P, P] + [I] * 11 + [P, P, I, P, SZ, P]
         L.thrift_quantize_fp4_range.restype = I
         L.thrift_quantize_fp4_range.argtypes = [P] + [I] * 8 + [P, P, P]
         L.thrift_attention_decode_workspace_bytes.restype = SZ

@@ -16,7 +16,8 @@ from . import _lib
 from ._lib import THRIFT_GROUP_D, THRIFT_GROUP_S, THRIFT_MXFP4, THRIFT_NVFP4, ThriftError
 
 __all__ = ["thrift_select_kmax", "thrift_select_blocks", "thrift_block_means",
-           "thrift_select_blocks_kbar", "thrift_select_blocks_means", "thrift_quantize_fp4",
+           "thrift_select_blocks_kbar", "thrift_select_blocks_means", "thrift_select_blocks_head",
+           "thrift_quantize_fp4",
            "thrift_quantize_fp4_means", "thrift_quantize_fp4_range",
            "thrift_attention_fwd", "thrift_attention_decode", "thrift_decode", "FP4Tensor",
            "fp4_transposed", "thrift_forward", "THRIFT_NVFP4", "THRIFT_MXFP4", "THRIFT_GROUP_D",
@@ -126,6 +127,29 @@ def thrift_select_blocks_means(qbar, kbar, Sq, Sk, block_q=128, block_k=64, caus
     cnt = torch.empty((B, Hq, nq), dtype=torch.int32, device=dev)
     _call("thrift_select_blocks_means", _ptr(qbar), _ptr(kbar), B, Hq, Hkv, Sq, Sk, D, block_q, block_k,
           int(causal), topk_count, topk_bp, _ptr(idx), _ptr(cnt), kmax, _stream())
+    return idx, cnt
+
+
+def thrift_select_blocks_head(qbar, kbar, Sq, Sk, block_q=128, block_k=64, causal=True, topk_count=-1,
+                              topk_bp=500, kmax=None):
+    """Per-head budget: one top-k over all valid block pairs of each query
+    head, from block means as thrift_select_blocks_means takes them."""
+    _check(qbar, torch.float32, "qbar")
+    _check(kbar, torch.float32, "kbar")
+    B, Hq, nq, D = qbar.shape
+    Hkv = kbar.shape[1]
+    if nq != -(-Sq // block_q) or tuple(kbar.shape) != (B, Hkv, -(-Sk // block_k), D):
+        raise ValueError("qbar / kbar do not match Sq, Sk and the block sizes")
+    L = _lib.load()
+    if kmax is None:
+        kmax = L.thrift_select_head_kmax(Sq, Sk, block_q, block_k, int(causal))
+    dev = qbar.device
+    idx = torch.empty((B, Hq, nq, kmax), dtype=torch.int32, device=dev)
+    cnt = torch.empty((B, Hq, nq), dtype=torch.int32, device=dev)
+    wsb = L.thrift_select_head_workspace_bytes(B, Hq, Sq, Sk, block_q, block_k)
+    ws = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _call("thrift_select_blocks_head", _ptr(qbar), _ptr(kbar), B, Hq, Hkv, Sq, Sk, D, block_q, block_k,
+          int(causal), topk_count, topk_bp, _ptr(idx), _ptr(cnt), kmax, _ptr(ws), wsb, _stream())
     return idx, cnt
 
 
@@ -266,13 +290,15 @@ def thrift_decode(q16, k16, v16, k4: FP4Tensor, v4: FP4Tensor, fmt=THRIFT_MXFP4,
 
 
 def thrift_forward(q16, k16, v16, fmt=THRIFT_MXFP4, block_q=128, block_k=64, causal=True,
-                   topk_count=-1, topk_bp=500, sm_scale=None, out_fp32=False, with_lse=False):
+                   topk_count=-1, topk_bp=500, sm_scale=None, out_fp32=False, with_lse=False,
+                   budget="block"):
     """The whole path: Q and K each read once for their block means and FP4
-    codes, V quantised, selection from the means, mixed attention."""
+    codes, V quantised, selection from the means (budget "block": per query
+    block; "head": one budget over each query head's pairs), mixed attention."""
     q4, qbar = thrift_quantize_fp4_means(q16, fmt, block_q)
     k4, kbar = thrift_quantize_fp4_means(k16, fmt, block_k)
     v4 = thrift_quantize_fp4(v16, THRIFT_GROUP_S, fmt)
-    idx, cnt = thrift_select_blocks_means(qbar, kbar, q16.shape[2], k16.shape[2], block_q, block_k, causal,
-                                          topk_count, topk_bp)
+    sel = {"block": thrift_select_blocks_means, "head": thrift_select_blocks_head}[budget]
+    idx, cnt = sel(qbar, kbar, q16.shape[2], k16.shape[2], block_q, block_k, causal, topk_count, topk_bp)
     return thrift_attention_fwd(q16, k16, v16, q4, k4, v4, idx, cnt, block_q, block_k, causal,
                                 sm_scale, out_fp32, with_lse)

@@ -119,12 +119,14 @@ constexpr int kTopkThreads = 256;
 constexpr int kHeadChunk = 4;  // query heads scored together per pass
 
 // QB consecutive query blocks share a workgroup, so each k̄ row is read once
-// for QB x (up to) four query-head rows.
-template <int D, int QB>
+// for QB x (up to) four query-head rows.  With OUT (per-head budgets) the
+// scores of the valid pairs go to scores_out [B,Hq,nQ,nK] instead of a
+// per-row top-k.
+template <int D, int QB, bool OUT = false>
 __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
     const float* __restrict__ qm, const float* __restrict__ km, int Hq, int Hkv, int Sq, int Sk, int bq,
     int bk, int causal, int topk_count, int topk_bp, int32_t* __restrict__ idx,
-    int32_t* __restrict__ cnt, int kmax) {
+    int32_t* __restrict__ cnt, int kmax, float* __restrict__ scores_out = nullptr) {
   constexpr int NR = QB * kHeadChunk;  // score rows per pass: (query block, head)
   extern __shared__ float sc[];         // [NR][nK] scores
   __shared__ __attribute__((aligned(16))) float qv[NR][D];
@@ -192,10 +194,149 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
       const int n = valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal);
       const int k = topk_budget(n, topk_count, topk_bp);
       const size_t row = ((size_t)b * Hq + hq) * nq + i;
-      wave_topk(sc + rr * nK, n, k, idx + row * kmax, kmax, lane);
-      if (lane == 0) cnt[row] = k;
+      if constexpr (OUT) {
+        for (int j = lane; j < n; j += kWave) scores_out[row * nK + j] = sc[rr * nK + j];
+      } else {
+        wave_topk(sc + rr * nK, n, k, idx + row * kmax, kmax, lane);
+        if (lane == 0) cnt[row] = k;
+      }
     }
   }
+}
+
+// ---- per-head budget: one top-k over all valid pairs of a query head ----------
+
+constexpr int kHeadThreads = 1024;
+
+// One workgroup per (batch, query head).  The K-th largest key T of the
+// head's valid pairs by a most-significant-digit-first radix select (eight
+// 4-bit digits, each a 16-bin histogram of the keys that match the digits
+// fixed so far, counted with LDS atomics over the flat [nQ][nK] score array,
+// four independent loads per thread in flight); then, for the ties at T,
+// each query block's count of keys equal to T (one wavefront per query
+// block, ballots) and their exclusive prefix over the query blocks (ties go
+// to the lower query block, then the lower key block).  state[bh] = {T,
+// need}: the pairs above T are all kept and the first `need` equal to T.
+constexpr int kHeadMaxQ = 4096;  // query blocks: S <= 262144 with block_q >= 64
+
+__global__ __launch_bounds__(kHeadThreads) void head_threshold_kernel(
+    const float* __restrict__ scores, int Sq, int Sk, int bq, int bk, int causal, int topk_count,
+    int topk_bp, uint32_t* __restrict__ state, int32_t* __restrict__ eqbase) {
+  __shared__ uint32_t hist[16];
+  __shared__ int eqc[kHeadMaxQ];
+  __shared__ int part[kHeadThreads];
+  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave, bh = blockIdx.x;
+  const int nq = cdiv(Sq, bq), nK = cdiv(Sk, bk);
+  const float* sh = scores + (size_t)bh * nq * nK;
+  long long P = 0;
+  for (int i = 0; i < nq; ++i) P += valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal);
+  long long K = topk_count >= 0 ? (long long)topk_count : (P * topk_bp + 9999) / 10000;
+  K = K < P ? K : P;
+  const int total = nq * nK;
+  // key of flat entry e, 0 (below every finite score) where the pair is not valid
+  auto key_at = [&](int e) -> uint32_t {
+    const int i = e / nK, jj = e - i * nK;
+    return jj < valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal) ? score_key(sh[e]) : 0u;
+  };
+  uint32_t prefix = 0, mask = 0;
+  long long kk = K;
+  if (K > 0)
+    for (int shift = 28; shift >= 0; shift -= 4) {
+      if (t < 16) hist[t] = 0;
+      __syncthreads();
+      for (int e0 = t; e0 < total; e0 += 4 * kHeadThreads) {
+        uint32_t u[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int e = e0 + r * kHeadThreads;
+          u[r] = e < total ? key_at(e) : 0u;
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          if (u[r] != 0u && (u[r] & mask) == prefix) atomicAdd(&hist[(u[r] >> shift) & 15u], 1u);
+      }
+      __syncthreads();
+      // the digit where the count from the top reaches kk (same in every thread)
+      long long cum = 0;
+      int dsel = 0;
+      for (int d = 15; d >= 0; --d) {
+        if (cum + hist[d] >= kk) {
+          dsel = d;
+          break;
+        }
+        cum += hist[d];
+      }
+      prefix |= (uint32_t)dsel << shift;
+      mask |= 15u << shift;
+      kk -= cum;
+      __syncthreads();
+    }
+  // ties at T: per query block counts (a wavefront per query block) ...
+  for (int i = wave; i < nq; i += kHeadThreads / kWave) {
+    const int n = valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal);
+    int c = 0;
+    if (K > 0)
+      for (int j = lane; j - lane < n; j += kWave)
+        c += __popcll(__ballot(j < n && score_key(sh[(size_t)i * nK + j]) == prefix));
+    if (lane == 0) eqc[i] = c;
+  }
+  __syncthreads();
+  // ... and their exclusive prefix: segment sums, a scan over the segments
+  const int per = cdiv(nq, kHeadThreads);
+  int mine = 0;
+  for (int i = t * per; i < min(nq, (t + 1) * per); ++i) mine += eqc[i];
+  part[t] = mine;
+  __syncthreads();
+  for (int off = 1; off < kHeadThreads; off <<= 1) {  // inclusive scan
+    const int v = t >= off ? part[t - off] : 0;
+    __syncthreads();
+    part[t] += v;
+    __syncthreads();
+  }
+  int run = t > 0 ? part[t - 1] : 0;
+  for (int i = t * per; i < min(nq, (t + 1) * per); ++i) {
+    eqbase[(size_t)bh * nq + i] = run;
+    run += eqc[i];
+  }
+  if (t == 0) {
+    state[2 * bh] = K > 0 ? prefix : 0xFFFFFFFFu;
+    state[2 * bh + 1] = (uint32_t)(K > 0 ? kk : 0);
+  }
+}
+
+// One wavefront per (batch, query head, query block): the kept key blocks
+// ascending, by ballot compaction (key > T, or key == T within the head's
+// first `need` ties).
+__global__ __launch_bounds__(256) void head_emit_kernel(const float* __restrict__ scores, int rows, int nq,
+                                                         int Sq, int Sk, int bq, int bk, int causal,
+                                                         const uint32_t* __restrict__ state,
+                                                         const int32_t* __restrict__ eqbase,
+                                                         int32_t* __restrict__ idx,
+                                                         int32_t* __restrict__ cnt, int kmax) {
+  const int lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (row >= rows) return;
+  const int bh = row / nq, i = row % nq, nK = cdiv(Sk, bk);
+  const int n = valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal);
+  const uint32_t T = state[2 * bh];
+  const int need = (int)state[2 * bh + 1];
+  const int eq0 = eqbase[row];
+  const float* sr = scores + (size_t)row * nK;
+  int32_t* out = idx + (size_t)row * kmax;
+  const uint64_t below = (1ull << lane) - 1;
+  int base = 0, eq_seen = 0;
+  for (int c = 0; c * kWave < n; ++c) {
+    const int j = c * kWave + lane;
+    const uint32_t u = j < n ? score_key(sr[j]) : 0u;
+    const uint64_t eq = __ballot(j < n && u == T);
+    const bool sel = j < n && (u > T || (u == T && eq0 + eq_seen + __popcll(eq & below) < need));
+    const uint64_t bal = __ballot(sel);
+    if (sel) out[base + __popcll(bal & below)] = j;
+    base += __popcll(bal);
+    eq_seen += __popcll(eq);
+  }
+  for (int e = base + lane; e < kmax; e += kWave) out[e] = -1;
+  if (lane == 0) cnt[row] = base;
 }
 
 // Query blocks per workgroup: as many as keep the score rows within 64 KB of
@@ -203,22 +344,41 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
 // and their length, not the k̄ reads, sets the time).
 inline int topk_qb(int nq, int nk) { return nq < 64 ? 1 : (nk <= 1024 ? (nk <= 512 ? 4 : 2) : 1); }
 
-template <int D>
+template <int D, bool OUT = false>
 void launch_score_topk(const float* qm, const float* km, int B, int Hq, int Hkv, int Sq, int Sk, int bq, int bk,
                        int causal, int topk_count, int topk_bp, int32_t* idx, int32_t* cnt, int kmax,
-                       hipStream_t stream) {
+                       hipStream_t stream, float* scores_out = nullptr) {
   const int nq = cdiv(Sq, bq), nk = cdiv(Sk, bk), qb = topk_qb(nq, nk);
   const size_t lds = (size_t)qb * kHeadChunk * nk * sizeof(float);
   const dim3 grid(cdiv(nq, qb), B * Hkv);
   if (qb == 4)
-    score_topk_kernel<D, 4><<<grid, kTopkThreads, lds, stream>>>(qm, km, Hq, Hkv, Sq, Sk, bq, bk, causal,
-                                                                 topk_count, topk_bp, idx, cnt, kmax);
+    score_topk_kernel<D, 4, OUT><<<grid, kTopkThreads, lds, stream>>>(
+        qm, km, Hq, Hkv, Sq, Sk, bq, bk, causal, topk_count, topk_bp, idx, cnt, kmax, scores_out);
   else if (qb == 2)
-    score_topk_kernel<D, 2><<<grid, kTopkThreads, lds, stream>>>(qm, km, Hq, Hkv, Sq, Sk, bq, bk, causal,
-                                                                 topk_count, topk_bp, idx, cnt, kmax);
+    score_topk_kernel<D, 2, OUT><<<grid, kTopkThreads, lds, stream>>>(
+        qm, km, Hq, Hkv, Sq, Sk, bq, bk, causal, topk_count, topk_bp, idx, cnt, kmax, scores_out);
   else
-    score_topk_kernel<D, 1><<<grid, kTopkThreads, lds, stream>>>(qm, km, Hq, Hkv, Sq, Sk, bq, bk, causal,
-                                                                 topk_count, topk_bp, idx, cnt, kmax);
+    score_topk_kernel<D, 1, OUT><<<grid, kTopkThreads, lds, stream>>>(
+        qm, km, Hq, Hkv, Sq, Sk, bq, bk, causal, topk_count, topk_bp, idx, cnt, kmax, scores_out);
+}
+
+// Raise the dynamic LDS limit of every score kernel once (long sequences).
+static thrift_status configure_score_kernels() {
+  static bool configured = false;
+  if (!configured) {
+    const void* kernels[] = {
+        (const void*)score_topk_kernel<128, 1>,       (const void*)score_topk_kernel<128, 2>,
+        (const void*)score_topk_kernel<128, 4>,       (const void*)score_topk_kernel<64, 1>,
+        (const void*)score_topk_kernel<64, 2>,        (const void*)score_topk_kernel<64, 4>,
+        (const void*)score_topk_kernel<128, 1, true>, (const void*)score_topk_kernel<128, 2, true>,
+        (const void*)score_topk_kernel<128, 4, true>, (const void*)score_topk_kernel<64, 1, true>,
+        (const void*)score_topk_kernel<64, 2, true>,  (const void*)score_topk_kernel<64, 4, true>};
+    for (const void* kf : kernels)
+      if (hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024) != hipSuccess)
+        return THRIFT_EHIP;
+    configured = true;
+  }
+  return THRIFT_OK;
 }
 
 }  // namespace thrift
@@ -282,16 +442,7 @@ static thrift_status select_common(const void* q16, const float* qbar, const voi
   float* km = kbar ? (float*)kbar : (float*)((char*)workspace + ((qbytes + 255) / 256) * 256);
   auto q = qbar ? nullptr : (const _Float16*)q16;
   auto k = kbar ? nullptr : (const _Float16*)k16;
-  static bool configured = false;  // allow more than the default dynamic LDS for long S
-  if (!configured) {
-    const void* kernels[] = {(const void*)score_topk_kernel<128, 1>, (const void*)score_topk_kernel<128, 2>,
-                             (const void*)score_topk_kernel<128, 4>, (const void*)score_topk_kernel<64, 1>,
-                             (const void*)score_topk_kernel<64, 2>, (const void*)score_topk_kernel<64, 4>};
-    for (const void* kf : kernels)
-      if (hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024) != hipSuccess)
-        return THRIFT_EHIP;
-    configured = true;
-  }
+  if (configure_score_kernels() != THRIFT_OK) return THRIFT_EHIP;
   if (D == 128) {
     if (q) block_means_kernel<128><<<dim3(nq, B * Hq), kMeansThreads, 0, stream>>>(q, Sq, block_q, nq, 0, qm);
     if (k) block_means_kernel<128><<<dim3(nk, B * Hkv), kMeansThreads, 0, stream>>>(k, Sk, block_k, nk, 0, km);
@@ -362,4 +513,53 @@ extern "C" thrift_status thrift_select_blocks(const void* q16, const void* k16, 
                                               hipStream_t stream) {
   return thrift_select_blocks_kv(q16, k16, B, Hq, Hkv, S, S, D, block_q, block_k, causal, topk_count,
                                  topk_bp, idx, cnt, kmax, workspace, workspace_bytes, stream);
+}
+
+extern "C" int thrift_select_head_kmax(int Sq, int Sk, int block_q, int block_k, int causal) {
+  if (Sq < 1 || Sk < Sq || block_q < 1 || block_k < 1) return -1;
+  return valid_kv_blocks_kv(cdiv(Sq, block_q) - 1, Sq, Sk, block_q, block_k, causal);  // the largest n_i
+}
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+extern "C" size_t thrift_select_head_workspace_bytes(int B, int Hq, int Sq, int Sk, int block_q, int block_k) {
+  if (B < 1 || Hq < 1 || Sq < 1 || Sk < 1 || block_q < 1 || block_k < 1) return 0;
+  const size_t rows = (size_t)B * Hq * cdiv(Sq, block_q);
+  return align256(rows * cdiv(Sk, block_k) * sizeof(float)) + align256((size_t)B * Hq * 2 * sizeof(uint32_t)) +
+         align256(rows * sizeof(int32_t));
+}
+
+extern "C" thrift_status thrift_select_blocks_head(const float* qbar, const float* kbar, int B, int Hq,
+                                                   int Hkv, int Sq, int Sk, int D, int block_q,
+                                                   int block_k, int causal, int topk_count, int topk_bp,
+                                                   int32_t* idx, int32_t* cnt, int kmax, void* workspace,
+                                                   size_t workspace_bytes, hipStream_t stream) {
+  if (!qbar || !kbar || !idx || !cnt || !workspace) return THRIFT_EINVAL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < Sq || (causal != 0 && causal != 1)) return THRIFT_EINVAL;
+  if (Hq % Hkv != 0) return THRIFT_EINVAL;
+  if (topk_count < 0 && (topk_bp < 0 || topk_bp > 10000)) return THRIFT_EINVAL;
+  if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
+  if ((block_q != 64 && block_q != 128) || block_k != 64) return THRIFT_EUNSUPPORTED;
+  if (Sk > 262144 || cdiv(Sq, block_q) > kHeadMaxQ) return THRIFT_EUNSUPPORTED;
+  if (kmax < thrift_select_head_kmax(Sq, Sk, block_q, block_k, causal)) return THRIFT_EINVAL;
+  if (!aligned16(qbar) || !aligned16(kbar) || !aligned16(workspace)) return THRIFT_EALIGN;
+  if (workspace_bytes < thrift_select_head_workspace_bytes(B, Hq, Sq, Sk, block_q, block_k))
+    return THRIFT_EWORKSPACE;
+  if (configure_score_kernels() != THRIFT_OK) return THRIFT_EHIP;
+  const int nq = cdiv(Sq, block_q), nk = cdiv(Sk, block_k);
+  const size_t rows = (size_t)B * Hq * nq;
+  float* scores = (float*)workspace;
+  uint32_t* state = (uint32_t*)((char*)workspace + align256(rows * nk * sizeof(float)));
+  int32_t* eqbase = (int32_t*)((char*)state + align256((size_t)B * Hq * 2 * sizeof(uint32_t)));
+  if (D == 128)
+    launch_score_topk<128, true>(qbar, kbar, B, Hq, Hkv, Sq, Sk, block_q, block_k, causal, topk_count, topk_bp,
+                                 idx, cnt, kmax, stream, scores);
+  else
+    launch_score_topk<64, true>(qbar, kbar, B, Hq, Hkv, Sq, Sk, block_q, block_k, causal, topk_count, topk_bp,
+                                idx, cnt, kmax, stream, scores);
+  head_threshold_kernel<<<B * Hq, kHeadThreads, 0, stream>>>(scores, Sq, Sk, block_q, block_k, causal,
+                                                             topk_count, topk_bp, state, eqbase);
+  head_emit_kernel<<<(int)((rows + 3) / 4), 256, 0, stream>>>(scores, (int)rows, nq, Sq, Sk, block_q, block_k,
+                                                              causal, state, eqbase, idx, cnt, kmax);
+  return launch_status();
 }

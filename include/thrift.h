@@ -188,6 +188,25 @@ thrift_status thrift_quantize_fp4(const void* x16, int B, int H, int S, int D,
  * writes for the tensor as it is now; bytes outside those rows or tiles are
  * not touched.  MXFP4 only (an NVFP4 slice scale depends on the whole slice:
  * THRIFT_EUNSUPPORTED); 0 <= s0 < s1 <= S, else THRIFT_EINVAL. */
+/* Per-head budget: the other reading of "the top-k highest-scoring block
+ * pairs" (summaries "Heuristische Blokkenselectie"): one budget over all
+ * valid pairs of a query head, K = min(P, topk_count) or
+ * ceil(P * topk_bp / 10^4) of its P valid pairs, the K best-scoring pairs
+ * kept (ties: lower query block, then lower key block).  Scores as
+ * thrift_select_blocks; means as thrift_select_blocks_means takes them.
+ *   idx [B,Hq,nQ,kmax] (out): each query block's kept key blocks ascending,
+ *     padded with -1; cnt [B,Hq,nQ] (out): their number (0 .. n_i);
+ *   kmax >= thrift_select_head_kmax(...) (the largest n_i), else EINVAL;
+ *   workspace: thrift_select_head_workspace_bytes (every pair's score, the
+ *     per-head threshold and the per-query-block tie offsets).
+ * The idx/cnt it writes drive thrift_attention_fwd unchanged. */
+int thrift_select_head_kmax(int Sq, int Sk, int block_q, int block_k, int causal);
+size_t thrift_select_head_workspace_bytes(int B, int Hq, int Sq, int Sk, int block_q, int block_k);
+thrift_status thrift_select_blocks_head(const float* qbar, const float* kbar, int B, int Hq, int Hkv, int Sq,
+                                        int Sk, int D, int block_q, int block_k, int causal, int topk_count,
+                                        int topk_bp, int32_t* idx, int32_t* cnt, int kmax, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
+
 /* Block means and FP4 codes along D (Q or K) from one read of x16: the
  * selection's block means and the FP4 path's operand in a single pass
  * (summaries "Methodologie": both come from the same fp16 Q and K).

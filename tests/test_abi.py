@@ -193,3 +193,24 @@ def test_fused_pass_validation(lib):
     assert scall(kmax=1) == 1
     assert scall(bq=96) == 2
     assert scall(kbar=A + 4) == 3
+
+
+def test_head_budget_validation(lib):
+    f = lib.thrift_select_blocks_head
+
+    def call(qbar=A, Sq=1000, Sk=1000, kmax=16, ws=A, wsb=1 << 24, bq=128, D=128):
+        return f(qbar, A, 1, 4, 2, Sq, Sk, D, bq, 64, 1, -1, 500, A, A, kmax, ws, wsb, None)
+
+    assert lib.thrift_select_head_kmax(1000, 1000, 128, 64, 1) == 16
+    assert lib.thrift_select_head_kmax(1, 32768, 128, 64, 1) == 512
+    assert lib.thrift_select_head_kmax(1000, 1000, 128, 64, 0) == 16
+    assert call(qbar=None) == 1
+    assert call(ws=None) == 1
+    assert call(kmax=15) == 1  # a row may keep all 16 of its blocks
+    assert call(Sq=2000) == 1
+    assert call(D=96) == 2
+    assert call(bq=32) == 2
+    assert call(qbar=A + 4) == 3
+    need = lib.thrift_select_head_workspace_bytes(1, 4, 1000, 1000, 128, 64)
+    assert need >= 4 * 8 * 16 * 4
+    assert call(wsb=need - 1) == 4
