@@ -206,107 +206,145 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
 
 // ---- per-head budget: one top-k over all valid pairs of a query head ----------
 
-constexpr int kHeadThreads = 1024;
+// The K-th largest key T of each head's valid pairs, by a most-significant-
+// digit-first radix select over the flat [nQ][nK] score array: four 8-bit
+// digits, each pass a 256-bin histogram of the keys that match the digits
+// fixed so far.  Every pass runs over many workgroups per head (LDS
+// histograms, added into the head's global one), then one small kernel per
+// pass picks the digit.  Per head, hs[bh] = {prefix, mask, kk, K}: the
+// digits fixed so far, their mask, how many keys are still to take below
+// the fixed prefix, and the budget.
+constexpr int kHistChunk = 4096;  // flat entries per histogram workgroup
 
-// One workgroup per (batch, query head).  The K-th largest key T of the
-// head's valid pairs by a most-significant-digit-first radix select (eight
-// 4-bit digits, each a 16-bin histogram of the keys that match the digits
-// fixed so far, counted with LDS atomics over the flat [nQ][nK] score array,
-// four independent loads per thread in flight); then, for the ties at T,
-// each query block's count of keys equal to T (one wavefront per query
-// block, ballots) and their exclusive prefix over the query blocks (ties go
-// to the lower query block, then the lower key block).  state[bh] = {T,
-// need}: the pairs above T are all kept and the first `need` equal to T.
-constexpr int kHeadMaxQ = 4096;  // query blocks: S <= 262144 with block_q >= 64
-
-__global__ __launch_bounds__(kHeadThreads) void head_threshold_kernel(
-    const float* __restrict__ scores, int Sq, int Sk, int bq, int bk, int causal, int topk_count,
-    int topk_bp, uint32_t* __restrict__ state, int32_t* __restrict__ eqbase) {
-  __shared__ uint32_t hist[16];
-  __shared__ int eqc[kHeadMaxQ];
-  __shared__ int part[kHeadThreads];
-  const int t = threadIdx.x, lane = t % kWave, wave = t / kWave, bh = blockIdx.x;
-  const int nq = cdiv(Sq, bq), nK = cdiv(Sk, bk);
-  const float* sh = scores + (size_t)bh * nq * nK;
+__device__ inline long long head_pairs(int Sq, int Sk, int bq, int bk, int causal) {
   long long P = 0;
-  for (int i = 0; i < nq; ++i) P += valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal);
-  long long K = topk_count >= 0 ? (long long)topk_count : (P * topk_bp + 9999) / 10000;
-  K = K < P ? K : P;
-  const int total = nq * nK;
-  // key of flat entry e, 0 (below every finite score) where the pair is not valid
-  auto key_at = [&](int e) -> uint32_t {
-    const int i = e / nK, jj = e - i * nK;
-    return jj < valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal) ? score_key(sh[e]) : 0u;
-  };
-  uint32_t prefix = 0, mask = 0;
-  long long kk = K;
-  if (K > 0)
-    for (int shift = 28; shift >= 0; shift -= 4) {
-      if (t < 16) hist[t] = 0;
-      __syncthreads();
-      for (int e0 = t; e0 < total; e0 += 4 * kHeadThreads) {
-        uint32_t u[4];
+  for (int i = 0, nq = cdiv(Sq, bq); i < nq; ++i) P += valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal);
+  return P;
+}
+
+// hs[bh] = {0, 0, K, K}; the global histograms cleared.
+__global__ __launch_bounds__(256) void head_init_kernel(int Sq, int Sk, int bq, int bk, int causal, int topk_count,
+                                                        int topk_bp, uint32_t* __restrict__ hs,
+                                                        uint32_t* __restrict__ ghist) {
+  const int bh = blockIdx.x, t = threadIdx.x;
+  ghist[(size_t)bh * 256 + t] = 0;
+  if (t == 0) {
+    const long long P = head_pairs(Sq, Sk, bq, bk, causal);
+    long long K = topk_count >= 0 ? (long long)topk_count : (P * topk_bp + 9999) / 10000;
+    K = K < P ? K : P;
+    hs[4 * bh + 0] = 0;
+    hs[4 * bh + 1] = 0;
+    hs[4 * bh + 2] = (uint32_t)K;
+    hs[4 * bh + 3] = (uint32_t)K;
+  }
+}
+
+// One pass: the histogram of digit `shift` over the keys matching hs's prefix.
+__global__ __launch_bounds__(256) void head_hist_kernel(const float* __restrict__ scores, int Sq, int Sk, int bq,
+                                                        int bk, int causal, int shift,
+                                                        const uint32_t* __restrict__ hs,
+                                                        uint32_t* __restrict__ ghist) {
+  __shared__ uint32_t hist[256];
+  const int t = threadIdx.x, bh = blockIdx.y;
+  const int nq = cdiv(Sq, bq), nK = cdiv(Sk, bk), total = nq * nK;
+  const uint32_t prefix = hs[4 * bh + 0], mask = hs[4 * bh + 1];
+  if (hs[4 * bh + 3] == 0) return;  // K == 0: nothing to select
+  hist[t] = 0;
+  __syncthreads();
+  const float* sh = scores + (size_t)bh * nq * nK;
+  const int e_end = min(total, (blockIdx.x + 1) * kHistChunk);
+  for (int e0 = blockIdx.x * kHistChunk + t; e0 < e_end; e0 += 8 * 256) {
+    uint32_t u[8];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int e = e0 + r * kHeadThreads;
-          u[r] = e < total ? key_at(e) : 0u;
-        }
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-          if (u[r] != 0u && (u[r] & mask) == prefix) atomicAdd(&hist[(u[r] >> shift) & 15u], 1u);
+    for (int r = 0; r < 8; ++r) {  // eight independent loads in flight
+      const int e = e0 + r * 256;
+      u[r] = 0u;
+      if (e < e_end) {
+        const int i = e / nK;
+        if (e - i * nK < valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal)) u[r] = score_key(sh[e]);
       }
-      __syncthreads();
-      // the digit where the count from the top reaches kk (same in every thread)
-      long long cum = 0;
-      int dsel = 0;
-      for (int d = 15; d >= 0; --d) {
-        if (cum + hist[d] >= kk) {
-          dsel = d;
-          break;
-        }
-        cum += hist[d];
-      }
-      prefix |= (uint32_t)dsel << shift;
-      mask |= 15u << shift;
-      kk -= cum;
-      __syncthreads();
     }
-  // ties at T: per query block counts (a wavefront per query block) ...
-  for (int i = wave; i < nq; i += kHeadThreads / kWave) {
-    const int n = valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal);
-    int c = 0;
-    if (K > 0)
-      for (int j = lane; j - lane < n; j += kWave)
-        c += __popcll(__ballot(j < n && score_key(sh[(size_t)i * nK + j]) == prefix));
-    if (lane == 0) eqc[i] = c;
+#pragma unroll
+    for (int r = 0; r < 8; ++r)
+      if (u[r] != 0u && (u[r] & mask) == prefix) atomicAdd(&hist[(u[r] >> shift) & 255u], 1u);
   }
   __syncthreads();
-  // ... and their exclusive prefix: segment sums, a scan over the segments
-  const int per = cdiv(nq, kHeadThreads);
+  if (hist[t]) atomicAdd(&ghist[(size_t)bh * 256 + t], hist[t]);
+}
+
+// One pass: the digit where the count from the top reaches kk; hs updated,
+// the global histogram cleared for the next pass.
+__global__ __launch_bounds__(256) void head_pick_kernel(int shift, uint32_t* __restrict__ hs,
+                                                        uint32_t* __restrict__ ghist) {
+  __shared__ uint32_t h[256];
+  const int t = threadIdx.x, bh = blockIdx.x;
+  h[t] = ghist[(size_t)bh * 256 + t];
+  ghist[(size_t)bh * 256 + t] = 0;
+  __syncthreads();
+  if (t == 0 && hs[4 * bh + 3] != 0) {
+    const uint32_t kk = hs[4 * bh + 2];
+    uint32_t cum = 0;
+    int dsel = 0;
+    for (int d = 255; d >= 0; --d) {
+      if (cum + h[d] >= kk) {
+        dsel = d;
+        break;
+      }
+      cum += h[d];
+    }
+    hs[4 * bh + 0] |= (uint32_t)dsel << shift;
+    hs[4 * bh + 1] |= 255u << shift;
+    hs[4 * bh + 2] = kk - cum;
+  }
+}
+
+// Ties at T (= the full prefix): each query block's count of keys equal to
+// T, one wavefront per (batch, query head, query block).
+__global__ __launch_bounds__(256) void head_eqcount_kernel(const float* __restrict__ scores, int rows, int nq,
+                                                           int Sq, int Sk, int bq, int bk, int causal,
+                                                           const uint32_t* __restrict__ hs,
+                                                           int32_t* __restrict__ eqc) {
+  const int lane = threadIdx.x % kWave;
+  const int row = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (row >= rows) return;
+  const int bh = row / nq, i = row % nq, nK = cdiv(Sk, bk);
+  const int n = valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal);
+  const uint32_t T = hs[4 * bh + 0];
+  const float* sr = scores + (size_t)row * nK;
+  int c = 0;
+  if (hs[4 * bh + 3] != 0)
+    for (int j = lane; j - lane < n; j += kWave) c += __popcll(__ballot(j < n && score_key(sr[j]) == T));
+  if (lane == 0) eqc[row] = c;
+}
+
+// Exclusive prefix of the tie counts over each head's query blocks (ties go
+// to the lower query block, then the lower key block).
+__global__ __launch_bounds__(1024) void head_scan_kernel(int nq, int32_t* __restrict__ eq) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x, bh = blockIdx.x;
+  int32_t* e = eq + (size_t)bh * nq;
+  const int per = cdiv(nq, 1024), i0 = min(nq, t * per), i1 = min(nq, i0 + per);
   int mine = 0;
-  for (int i = t * per; i < min(nq, (t + 1) * per); ++i) mine += eqc[i];
+  for (int i = i0; i < i1; ++i) mine += e[i];
   part[t] = mine;
   __syncthreads();
-  for (int off = 1; off < kHeadThreads; off <<= 1) {  // inclusive scan
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan of the segment sums
     const int v = t >= off ? part[t - off] : 0;
     __syncthreads();
     part[t] += v;
     __syncthreads();
   }
   int run = t > 0 ? part[t - 1] : 0;
-  for (int i = t * per; i < min(nq, (t + 1) * per); ++i) {
-    eqbase[(size_t)bh * nq + i] = run;
-    run += eqc[i];
-  }
-  if (t == 0) {
-    state[2 * bh] = K > 0 ? prefix : 0xFFFFFFFFu;
-    state[2 * bh + 1] = (uint32_t)(K > 0 ? kk : 0);
+  for (int i = i0; i < i1; ++i) {
+    const int c = e[i];
+    e[i] = run;
+    run += c;
   }
 }
 
 // One wavefront per (batch, query head, query block): the kept key blocks
 // ascending, by ballot compaction (key > T, or key == T within the head's
-// first `need` ties).
+// first `need` ties; state = hs after the last pass).
 __global__ __launch_bounds__(256) void head_emit_kernel(const float* __restrict__ scores, int rows, int nq,
                                                          int Sq, int Sk, int bq, int bk, int causal,
                                                          const uint32_t* __restrict__ state,
@@ -318,8 +356,8 @@ __global__ __launch_bounds__(256) void head_emit_kernel(const float* __restrict_
   if (row >= rows) return;
   const int bh = row / nq, i = row % nq, nK = cdiv(Sk, bk);
   const int n = valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal);
-  const uint32_t T = state[2 * bh];
-  const int need = (int)state[2 * bh + 1];
+  const uint32_t T = state[4 * bh + 3] != 0 ? state[4 * bh + 0] : 0xFFFFFFFFu;
+  const int need = state[4 * bh + 3] != 0 ? (int)state[4 * bh + 2] : 0;
   const int eq0 = eqbase[row];
   const float* sr = scores + (size_t)row * nK;
   int32_t* out = idx + (size_t)row * kmax;
@@ -525,8 +563,8 @@ static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
 extern "C" size_t thrift_select_head_workspace_bytes(int B, int Hq, int Sq, int Sk, int block_q, int block_k) {
   if (B < 1 || Hq < 1 || Sq < 1 || Sk < 1 || block_q < 1 || block_k < 1) return 0;
   const size_t rows = (size_t)B * Hq * cdiv(Sq, block_q);
-  return align256(rows * cdiv(Sk, block_k) * sizeof(float)) + align256((size_t)B * Hq * 2 * sizeof(uint32_t)) +
-         align256(rows * sizeof(int32_t));
+  return align256(rows * cdiv(Sk, block_k) * sizeof(float)) + align256((size_t)B * Hq * 4 * sizeof(uint32_t)) +
+         align256((size_t)B * Hq * 256 * sizeof(uint32_t)) + align256(rows * sizeof(int32_t));
 }
 
 extern "C" thrift_status thrift_select_blocks_head(const float* qbar, const float* kbar, int B, int Hq,
@@ -540,7 +578,7 @@ extern "C" thrift_status thrift_select_blocks_head(const float* qbar, const floa
   if (topk_count < 0 && (topk_bp < 0 || topk_bp > 10000)) return THRIFT_EINVAL;
   if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
   if ((block_q != 64 && block_q != 128) || block_k != 64) return THRIFT_EUNSUPPORTED;
-  if (Sk > 262144 || cdiv(Sq, block_q) > kHeadMaxQ) return THRIFT_EUNSUPPORTED;
+  if (Sk > 262144) return THRIFT_EUNSUPPORTED;
   if (kmax < thrift_select_head_kmax(Sq, Sk, block_q, block_k, causal)) return THRIFT_EINVAL;
   if (!aligned16(qbar) || !aligned16(kbar) || !aligned16(workspace)) return THRIFT_EALIGN;
   if (workspace_bytes < thrift_select_head_workspace_bytes(B, Hq, Sq, Sk, block_q, block_k))
@@ -549,17 +587,26 @@ extern "C" thrift_status thrift_select_blocks_head(const float* qbar, const floa
   const int nq = cdiv(Sq, block_q), nk = cdiv(Sk, block_k);
   const size_t rows = (size_t)B * Hq * nq;
   float* scores = (float*)workspace;
-  uint32_t* state = (uint32_t*)((char*)workspace + align256(rows * nk * sizeof(float)));
-  int32_t* eqbase = (int32_t*)((char*)state + align256((size_t)B * Hq * 2 * sizeof(uint32_t)));
+  uint32_t* hs = (uint32_t*)((char*)workspace + align256(rows * nk * sizeof(float)));
+  uint32_t* ghist = (uint32_t*)((char*)hs + align256((size_t)B * Hq * 4 * sizeof(uint32_t)));
+  int32_t* eqbase = (int32_t*)((char*)ghist + align256((size_t)B * Hq * 256 * sizeof(uint32_t)));
   if (D == 128)
     launch_score_topk<128, true>(qbar, kbar, B, Hq, Hkv, Sq, Sk, block_q, block_k, causal, topk_count, topk_bp,
                                  idx, cnt, kmax, stream, scores);
   else
     launch_score_topk<64, true>(qbar, kbar, B, Hq, Hkv, Sq, Sk, block_q, block_k, causal, topk_count, topk_bp,
                                 idx, cnt, kmax, stream, scores);
-  head_threshold_kernel<<<B * Hq, kHeadThreads, 0, stream>>>(scores, Sq, Sk, block_q, block_k, causal,
-                                                             topk_count, topk_bp, state, eqbase);
-  head_emit_kernel<<<(int)((rows + 3) / 4), 256, 0, stream>>>(scores, (int)rows, nq, Sq, Sk, block_q, block_k,
-                                                              causal, state, eqbase, idx, cnt, kmax);
+  head_init_kernel<<<B * Hq, 256, 0, stream>>>(Sq, Sk, block_q, block_k, causal, topk_count, topk_bp, hs, ghist);
+  const dim3 hgrid(cdiv(nq * nk, kHistChunk), B * Hq);
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    head_hist_kernel<<<hgrid, 256, 0, stream>>>(scores, Sq, Sk, block_q, block_k, causal, shift, hs, ghist);
+    head_pick_kernel<<<B * Hq, 256, 0, stream>>>(shift, hs, ghist);
+  }
+  const int rgrid = (int)((rows + 3) / 4);
+  head_eqcount_kernel<<<rgrid, 256, 0, stream>>>(scores, (int)rows, nq, Sq, Sk, block_q, block_k, causal, hs,
+                                                 eqbase);
+  head_scan_kernel<<<B * Hq, 1024, 0, stream>>>(nq, eqbase);
+  head_emit_kernel<<<rgrid, 256, 0, stream>>>(scores, (int)rows, nq, Sq, Sk, block_q, block_k, causal, hs, eqbase,
+                                              idx, cnt, kmax);
   return launch_status();
 }
