@@ -260,13 +260,11 @@ def run_decode(args, w, d, gen_s):
 
     from fp16_attention_amd import api
 
-    if args.fmt != "mx":
-        print("bench.py: the decode forward runs MXFP4 only", file=sys.stderr)
-        sys.exit(2)
+    fmt = api.THRIFT_MXFP4 if args.fmt == "mx" else api.THRIFT_NVFP4
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v"))
-    k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, api.THRIFT_MXFP4)
-    v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, api.THRIFT_MXFP4)
+    k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, fmt)
+    v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, fmt)
     kbar = api.thrift_block_means(k, w.bk)
     if args.copy_mib:
         copy_calibration(torch, dev, args.copy_mib)
@@ -281,7 +279,7 @@ def run_decode(args, w, d, gen_s):
         api.thrift_block_means(k, w.bk, s0 // w.bk, nkb, out=kbar)
         api.thrift_quantize_fp4_range(k, k4, s0, w.S)
         api.thrift_quantize_fp4_range(v, v4, s0, w.S)
-        q4, qbar = api.thrift_quantize_fp4_means(q, api.THRIFT_MXFP4, w.bq)
+        q4, qbar = api.thrift_quantize_fp4_means(q, fmt, w.bq)
         idx, cnt = api.thrift_select_blocks_means(qbar, kbar, w.Sq, w.S, w.bq, w.bk, w.causal, w.topk_count,
                                                   w.topk_bp, kmax)
         if rec:
@@ -307,7 +305,8 @@ def run_decode(args, w, d, gen_s):
     # the fp16 K/V of each distinct promoted block of a key head once, Q (fp16 + FP4), O fp16
     G = w.Hq // w.Hkv
     nkb = -(-w.S // w.bk)
-    fp4_cache = w.B * w.Hkv * nkb * w.bk * (w.D // 2 + w.D // 32) * 2
+    g = 32 if fmt == api.THRIFT_MXFP4 else 16
+    fp4_cache = w.B * w.Hkv * nkb * w.bk * (w.D // 2 + w.D // g) * 2
     distinct = 0
     for b in range(w.B):
         for hk in range(w.Hkv):
@@ -317,7 +316,7 @@ def run_decode(args, w, d, gen_s):
                 sel.update(int(j) for j in idx_h[b, hk * G + g, 0, :c])
             distinct += len(sel)
     fp16_tiles = distinct * w.bk * w.D * 2 * 2
-    qo = w.B * w.Hq * w.Sq * w.D * (2 + 0.5 + 1 / 32 + 2)
+    qo = w.B * w.Hq * w.Sq * w.D * (2 + 0.5 + 1 / g + 2)
     alg = fp4_cache + fp16_tiles + qo
     achieved = alg / (fwd_ms * 1e-3)
     rows = w.B * w.Hq * w.Sq
@@ -332,15 +331,16 @@ def run_decode(args, w, d, gen_s):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4+fp16",
+        "dtype": "mxfp4+fp16" if fmt == api.THRIFT_MXFP4 else "nvfp4(fp16 math)+fp16",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} Sk{w.S} D{w.D} "
-                               f"{'causal' if w.causal else 'non-causal'} top-k {w.topk_bp / 100}% mx",
+                               f"{'causal' if w.causal else 'non-causal'} top-k {w.topk_bp / 100}% {args.fmt}",
                    "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM / 1e9, "unit": "GB/s",
-                     "frac": round(achieved / HBM, 4), "traffic": measured_traffic(w.name, "mx"),
+                     "frac": round(achieved / HBM, 4), "traffic": measured_traffic(w.name, args.fmt),
                      "traffic_algorithmic": int(alg),
-                     "kernel": "decode_fp4_kernel + decode_f16_kernel + decode_merge_kernel"},
+                     "kernel": ("decode_fp4_kernel" if fmt == api.THRIFT_MXFP4 else "decode_nv4_kernel")
+                     + " + decode_f16_kernel + decode_merge_kernel"},
         "breakdown_ms": {"cache_update_select_quantize_q": round(prep_ms, 4), "attention_decode": round(fwd_ms, 4)},
         "bytes": {"fp4_cache": int(fp4_cache), "fp16_promoted_tiles": int(fp16_tiles), "q_and_o": int(qo)},
         "input_gen_s": round(gen_s, 1),
@@ -353,11 +353,11 @@ def run_decode(args, w, d, gen_s):
         sec = 0.0
         for b in range(w.B):  # the whole workload, one batch element at a time
             qb, kb, vb = (np.ascontiguousarray(d[n][b:b + 1]) for n in ("q", "k", "v"))
-            k4b = O.quantize(kb, O.AXIS_D, O.MX)  # the cache's FP4 copy: outside the step, as on the GPU
-            v4b = O.quantize(vb, O.AXIS_S, O.MX)
+            k4b = O.quantize(kb, O.AXIS_D, fmt)  # the cache's FP4 copy: outside the step, as on the GPU
+            v4b = O.quantize(vb, O.AXIS_S, fmt)
             t0 = time.perf_counter()
             ib, cb, _ = O.select(qb, kb, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
-            q4b = O.quantize(qb, O.AXIS_D, O.MX)
+            q4b = O.quantize(qb, O.AXIS_D, fmt)
             O.attention(qb, kb, vb, q4b, k4b, v4b, ib, cb, w.bq, w.bk, w.causal)
             sec += time.perf_counter() - t0
         line["cpu_baseline"] = {"value": round(rows / sec, 2), "unit": "rows/s", "cores": nthreads,

@@ -67,7 +67,7 @@ def load():
         L.thrift_select_blocks_head.restype = I
         L.thrift_select_blocks_head.argtypes = [P, P] + [I] * 11 + [P, P, I, P, SZ, P]
         L.thrift_quantize_fp4_range.restype = I
-        L.thrift_quantize_fp4_range.argtypes = [P] + [I] * 8 + [P, P, P]
+        L.thrift_quantize_fp4_range.argtypes = [P] + [I] * 8 + [P, P, P, P]
         L.thrift_attention_decode_workspace_bytes.restype = SZ
         L.thrift_attention_decode_workspace_bytes.argtypes = [I] * 7
         L.thrift_attention_decode.restype = I

@@ -202,12 +202,12 @@ def thrift_quantize_fp4_means(x16, fmt=THRIFT_MXFP4, blk=128):
 
 
 def thrift_quantize_fp4_range(x16, t: FP4Tensor, s0, s1):
-    """Re-encode, in place in t (an MXFP4 copy of x16), the groups that hold
-    positions s0 <= s < s1 of x16."""
+    """Re-encode, in place in t (an FP4 copy of x16), the groups that hold
+    positions s0 <= s < s1 of x16 (NVFP4: under t's slice scales, kept)."""
     _check(x16, torch.float16, "x16")
     B, H, S, D = x16.shape
     _call("thrift_quantize_fp4_range", _ptr(x16), B, H, S, D, t.axis, t.fmt, s0, s1, _ptr(t.codes),
-          _ptr(t.scales), _stream())
+          _ptr(t.scales), _ptr(t.tensor_scale), _stream())
     return t
 
 

@@ -392,12 +392,9 @@ __device__ inline void fp16_tile(RowState<D>& st, const char* stage, const v8h* 
 // V's per-slice scale) is carried in the accumulator scale g instead of being
 // rounded into P: acc becomes acc * g / f before the tile and g becomes f.
 template <int D>
-__device__ inline void fp4_nv_tile(RowState<D>& st, const char* stage, const v8h* qh, float c,
-                                   float sv, int key0, int qrow, int S, int causal, bool need_mask,
-                                   int lane) {
+__device__ inline void fp4_nv_softmax_pv(RowState<D>& st, v16f s[2], const char* stage, float c, float sv,
+                                         int key0, int qrow, int S, int causal, bool need_mask, int lane) {
   const int hi = lane >> 5;
-  v16f s[2];
-  qk_f16<D>(s, stage, qh, lane);
   if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
   const float gm0 = max16(s[0]), gm1 = max16(s[1]);  // this lane's two 16-key groups
   maybe_rescale<D>(st, fmaxf(gm0, gm1), c);
@@ -447,6 +444,15 @@ __device__ inline void fp4_nv_tile(RowState<D>& st, const char* stage, const v8h
     }
   }
   pv_f16<D>(st, (const _Float16*)(stage + Lds<D>::VT), pB, lane);
+}
+
+template <int D>
+__device__ inline void fp4_nv_tile(RowState<D>& st, const char* stage, const v8h* qh, float c,
+                                   float sv, int key0, int qrow, int S, int causal, bool need_mask,
+                                   int lane) {
+  v16f s[2];
+  qk_f16<D>(s, stage, qh, lane);
+  fp4_nv_softmax_pv<D>(st, s, stage, c, sv, key0, qrow, S, causal, need_mask, lane);
 }
 
 }  // namespace thrift
@@ -1131,6 +1137,106 @@ __global__ __launch_bounds__(kDecWaves * 64, 2) void decode_fp4_kernel(DecodeArg
   }
 }
 
+// FP4 pass of the decode shape, NVFP4: the same work split as the MXFP4
+// kernel (wave w takes blocks jb + w + 4n).  gfx950 has no matrix
+// instruction with E4M3 block scales, so each wave dequantises its block
+// exactly to fp16 in its own LDS stage (the next block's codes already in
+// registers) and runs the NVFP4 tile of the prefill kernel on the fp16
+// matrix cores.  Each column's score scale carries its own head's Q slice
+// scale.
+template <int D>
+__global__ __launch_bounds__(kDecWaves * 64, 1) void decode_nv4_kernel(DecodeArgs d) {
+  using L = Lds<D>;
+  constexpr int NT = kDecWaves * 64;
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const AttnArgs& a = d.kv;
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), hi = lane >> 5;
+  const int unit = blockIdx.x, sidx = unit % d.nsplit;
+  const size_t bhk = unit / d.nsplit;
+  const int b = (int)(bhk / a.Hkv), hk = (int)(bhk % a.Hkv);
+  const int Sk = a.S, Sq = d.Sq, G = d.G, ncol = G * Sq;
+  const int jb = sidx * d.bpw, je = min(jb + d.bpw, d.nvalid);
+  const int col = lane & 31, g = col / Sq, r = col % Sq;
+  const bool col_ok = col < ncol;
+  const int hq = hk * G + (col_ok ? g : 0);
+  const int qpos = Sk - Sq + r;
+  char* stage = smem + w * L::STAGE;  // this wave's fp16 stage
+
+  // promoted-block bits of the group's heads: [G][nwords]
+  const int nwords = (d.nvalid + 31) >> 5;
+  uint32_t* pb = (uint32_t*)(smem + kDecWaves * L::STAGE);
+  for (int e = t; e < G * nwords; e += NT) pb[e] = 0;
+  __syncthreads();
+  for (int e = t; e < G * a.kmax; e += NT) {
+    const int gg = e / a.kmax, p = e % a.kmax;
+    const size_t row = (size_t)b * a.Hq + hk * G + gg;
+    const int c = min(max(a.cnt[row], 0), a.kmax);
+    const int j = p < c ? a.idx[row * a.kmax + p] : -1;
+    if (j >= 0 && j < d.nvalid) atomicOr(&pb[gg * nwords + (j >> 5)], 1u << (j & 31));
+  }
+
+  // this column's query, dequantised exactly to fp16, and its score scale
+  v8h qh[D / 16];
+  const size_t qoff = ((size_t)b * a.Hq + hq) * Sq + r;
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    qh[kk] = v8h{};
+    if (col_ok) {
+      const uint32_t cw = *(const uint32_t*)(a.q4c + qoff * (D / 2) + kk * 8 + hi * 4);
+      const _Float16 f = (_Float16)e4m3_to_float(a.q4s[qoff * (D / 16) + kk]);
+      const v4h lo = fp4x4_to_h(cw & 0xFFFFu, f), h4 = fp4x4_to_h(cw >> 16, f);
+      qh[kk] = v8h{lo.x, lo.y, lo.z, lo.w, h4.x, h4.y, h4.z, h4.w};
+    }
+  }
+  const float c = a.sm_log2 * a.q4t[(size_t)b * a.Hq + hq] * a.k4t[bhk];
+  const float sv = a.v4t[bhk];
+
+  RowState<D> st;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] = v16f{};
+  st.m = kMInit;
+  st.l = 0.0f;
+  st.g = 1.0f;
+
+  const int nss = je > jb ? cdiv(je - jb, kDecWaves) : 0;
+  Nv4Stager<D, 64> stg;
+  if (nss > 0 && jb + w < je) {
+    stg.load(a, bhk, jb + w, lane);
+    stg.store(stage, lane);
+  }
+  __syncthreads();
+  for (int k = 0; k < nss; ++k) {
+    const int j = jb + kDecWaves * k + w, jn = j + kDecWaves;
+    const bool next = k + 1 < nss && jn < je;
+    if (next) stg.load(a, bhk, jn, lane);  // registers, while this block is computed
+    if (j < je) {
+      v16f sc[2];
+      qk_f16<D>(sc, stage, qh, lane);
+      const bool prom = col_ok && ((pb[g * nwords + (j >> 5)] >> (j & 31)) & 1u);
+      // promoted blocks of this column's head and columns without a query:
+      // probability 0, branch-free (see the MXFP4 kernel)
+      const float lim = (!col_ok || prom) ? -INFINITY : INFINITY;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) sc[mt][i] = fminf(sc[mt][i], lim);
+      const int key0 = j * kBk;
+      const bool need_mask = (a.causal && key0 + kBk - 1 > Sk - Sq) || key0 + kBk > Sk;
+      fp4_nv_softmax_pv<D>(st, sc, stage, c, sv, key0, qpos, Sk, a.causal, need_mask, lane);
+    }
+    __syncthreads();
+    if (next) stg.store(stage, lane);
+    __syncthreads();
+  }
+  // back to plain units: acc holds O^T / g
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] *= st.g;
+  if (col_ok) {
+    const size_t u4 = (bhk * d.nsplit + sidx) * kDecWaves + w;
+    store_partial<D>(d.part4 + (u4 * ncol + col) * kPartStride<D>, st, lane);
+  }
+}
+
 template <int D>
 __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeArgs d) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
@@ -1302,6 +1408,8 @@ template __global__ void attn_fwd_kernel<64, 4, THRIFT_NVFP4>(AttnArgs);
 template __global__ void attn_fwd_kernel<64, 2, THRIFT_NVFP4>(AttnArgs);
 template __global__ void decode_fp4_kernel<128>(DecodeArgs);
 template __global__ void decode_fp4_kernel<64>(DecodeArgs);
+template __global__ void decode_nv4_kernel<128>(DecodeArgs);
+template __global__ void decode_nv4_kernel<64>(DecodeArgs);
 template __global__ void decode_f16_kernel<128>(DecodeArgs);
 template __global__ void decode_f16_kernel<64>(DecodeArgs);
 template __global__ void decode_merge_kernel<128>(DecodeArgs);
@@ -1388,20 +1496,23 @@ extern "C" size_t thrift_attention_decode_workspace_bytes(int B, int Hq, int Hkv
 }
 
 template <int D>
-static thrift_status launch_decode(DecodeArgs& d, hipStream_t stream) {
+static thrift_status launch_decode(DecodeArgs& d, int fmt, hipStream_t stream) {
   using M = MxStage<D>;
   const AttnArgs& a = d.kv;
   static bool configured = false;
   if (!configured) {
-    if (hipFuncSetAttribute((const void*)decode_fp4_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024) != hipSuccess ||
-        hipFuncSetAttribute((const void*)decode_f16_kernel<D>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                            160 * 1024) != hipSuccess)
-      return THRIFT_EHIP;
+    for (const void* kf : {(const void*)decode_fp4_kernel<D>, (const void*)decode_nv4_kernel<D>,
+                           (const void*)decode_f16_kernel<D>})
+      if (hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+        return THRIFT_EHIP;
     configured = true;
   }
-  const size_t lds4 = 4 * (size_t)M::SIZE + (size_t)d.G * ((d.nvalid + 31) / 32) * 4;
-  decode_fp4_kernel<D><<<a.B * a.Hkv * d.nsplit, kDecWaves * 64, lds4, stream>>>(d);
+  const size_t pbytes = (size_t)d.G * ((d.nvalid + 31) / 32) * 4;
+  if (fmt == THRIFT_MXFP4)
+    decode_fp4_kernel<D><<<a.B * a.Hkv * d.nsplit, kDecWaves * 64, 4 * (size_t)M::SIZE + pbytes, stream>>>(d);
+  else
+    decode_nv4_kernel<D><<<a.B * a.Hkv * d.nsplit, kDecWaves * 64, kDecWaves * (size_t)Lds<D>::STAGE + pbytes,
+                           stream>>>(d);
   decode_f16_kernel<D><<<a.B * a.Hq * a.kmax, 64, D * Lds<D>::VROWH * 2, stream>>>(d);
   decode_merge_kernel<D><<<a.B * a.Hq * d.Sq, kMergeThreads, 0, stream>>>(d);
   return launch_status();
@@ -1419,10 +1530,7 @@ extern "C" thrift_status thrift_attention_decode(
       !v4_scales || !idx || !cnt || !o || !workspace)
     return THRIFT_EINVAL;
   if (fmt != THRIFT_NVFP4 && fmt != THRIFT_MXFP4) return THRIFT_EINVAL;
-  if (fmt != THRIFT_MXFP4) return THRIFT_EUNSUPPORTED;
-  (void)q4_tscale;
-  (void)k4_tscale;
-  (void)v4_tscale;
+  if (fmt == THRIFT_NVFP4 && (!q4_tscale || !k4_tscale || !v4_tscale)) return THRIFT_EINVAL;
   if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 1 || Sk < Sq || kmax < 1 || (causal != 0 && causal != 1))
     return THRIFT_EINVAL;
   if (Hq % Hkv != 0 || (o_is_fp32 != 0 && o_is_fp32 != 1)) return THRIFT_EINVAL;
@@ -1444,13 +1552,13 @@ extern "C" thrift_status thrift_attention_decode(
   a.v16 = (const _Float16*)v16;
   a.q4c = q4_codes;
   a.q4s = q4_scales;
-  a.q4t = nullptr;
+  a.q4t = fmt == THRIFT_NVFP4 ? q4_tscale : nullptr;
   a.k4c = k4_codes;
   a.k4s = k4_scales;
-  a.k4t = nullptr;
+  a.k4t = fmt == THRIFT_NVFP4 ? k4_tscale : nullptr;
   a.v4c = v4_codes;
   a.v4s = v4_scales;
-  a.v4t = nullptr;
+  a.v4t = fmt == THRIFT_NVFP4 ? v4_tscale : nullptr;
   a.idx = idx;
   a.cnt = cnt;
   a.o = o;
@@ -1471,7 +1579,7 @@ extern "C" thrift_status thrift_attention_decode(
   decode_split(B, Hkv, d.nvalid, d.nsplit, d.bpw);
   d.part4 = (float*)workspace;
   d.part16 = (float*)workspace + n4;
-  return D == 128 ? launch_decode<128>(d, stream) : launch_decode<64>(d, stream);
+  return D == 128 ? launch_decode<128>(d, fmt, stream) : launch_decode<64>(d, fmt, stream);
 }
 
 extern "C" const char* thrift_status_string(thrift_status s) {

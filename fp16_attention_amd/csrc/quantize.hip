@@ -389,31 +389,43 @@ extern "C" thrift_status thrift_quantize_fp4(const void* x16, int B, int H, int 
 extern "C" thrift_status thrift_quantize_fp4_range(const void* x16, int B, int H, int S, int D,
                                                    thrift_group_axis axis, thrift_format fmt, int s0,
                                                    int s1, uint8_t* codes, uint8_t* scales,
-                                                   hipStream_t stream) {
+                                                   const float* tensor_scale, hipStream_t stream) {
   if (!x16 || !codes || !scales) return THRIFT_EINVAL;
   if (B < 1 || H < 1 || S < 1 || s0 < 0 || s1 > S || s0 >= s1) return THRIFT_EINVAL;
   if (fmt != THRIFT_NVFP4 && fmt != THRIFT_MXFP4) return THRIFT_EINVAL;
   if (axis != THRIFT_GROUP_D && axis != THRIFT_GROUP_S) return THRIFT_EINVAL;
-  if (fmt != THRIFT_MXFP4) return THRIFT_EUNSUPPORTED;  // NVFP4's slice scale spans the whole slice
+  if (fmt == THRIFT_NVFP4 && !tensor_scale) return THRIFT_EINVAL;
   if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
   if (S > 262144) return THRIFT_EUNSUPPORTED;
   if (!aligned16(x16) || !aligned16(codes)) return THRIFT_EALIGN;
   const int BH = B * H;
   auto x = (const _Float16*)x16;
+  const bool nv = fmt == THRIFT_NVFP4;
   if (axis == THRIFT_GROUP_D) {
-    const int gpr = D / 32;  // groups per row
+    const int gpr = D / (nv ? 16 : 32);  // groups per row
     const int gps = S * gpr, range = (s1 - s0) * gpr;
     const size_t ngroups = (size_t)BH * range;
     const int blocks = (int)((ngroups + kQThreads - 1) / kQThreads);
-    quant_d_kernel<THRIFT_MXFP4><<<blocks, kQThreads, 0, stream>>>(x, ngroups, gps, range, s0 * gpr,
-                                                                     nullptr, codes, scales);
+    if (nv)
+      quant_d_kernel<THRIFT_NVFP4><<<blocks, kQThreads, 0, stream>>>(x, ngroups, gps, range, s0 * gpr,
+                                                                       tensor_scale, codes, scales);
+    else
+      quant_d_kernel<THRIFT_MXFP4><<<blocks, kQThreads, 0, stream>>>(x, ngroups, gps, range, s0 * gpr,
+                                                                       nullptr, codes, scales);
   } else {
     const int Sp = pad_s(S), t0 = s0 / kVTile, t1 = cdiv(s1, kVTile);
     dim3 grid(t1 - t0, BH);
-    if (D == 128)
-      quant_s_kernel<THRIFT_MXFP4, 128><<<grid, kQThreads, 0, stream>>>(x, S, Sp, t0, nullptr, codes, scales);
-    else
-      quant_s_kernel<THRIFT_MXFP4, 64><<<grid, kQThreads, 0, stream>>>(x, S, Sp, t0, nullptr, codes, scales);
+    if (nv) {
+      if (D == 128)
+        quant_s_kernel<THRIFT_NVFP4, 128><<<grid, kQThreads, 0, stream>>>(x, S, Sp, t0, tensor_scale, codes, scales);
+      else
+        quant_s_kernel<THRIFT_NVFP4, 64><<<grid, kQThreads, 0, stream>>>(x, S, Sp, t0, tensor_scale, codes, scales);
+    } else {
+      if (D == 128)
+        quant_s_kernel<THRIFT_MXFP4, 128><<<grid, kQThreads, 0, stream>>>(x, S, Sp, t0, nullptr, codes, scales);
+      else
+        quant_s_kernel<THRIFT_MXFP4, 64><<<grid, kQThreads, 0, stream>>>(x, S, Sp, t0, nullptr, codes, scales);
+    }
   }
   return launch_status();
 }

@@ -160,6 +160,25 @@ thrift_status thrift_select_blocks_means(const float* qbar, const float* kbar, i
                                          int topk_count, int topk_bp, int32_t* idx, int32_t* cnt,
                                          int kmax, hipStream_t stream);
 
+/* Per-head budget: the other reading of "the top-k highest-scoring block
+ * pairs" (summaries "Heuristische Blokkenselectie"): one budget over all
+ * valid pairs of a query head, K = min(P, topk_count) or
+ * ceil(P * topk_bp / 10^4) of its P valid pairs, the K best-scoring pairs
+ * kept (ties: lower query block, then lower key block).  Scores as
+ * thrift_select_blocks; means as thrift_select_blocks_means takes them.
+ *   idx [B,Hq,nQ,kmax] (out): each query block's kept key blocks ascending,
+ *     padded with -1; cnt [B,Hq,nQ] (out): their number (0 .. n_i);
+ *   kmax >= thrift_select_head_kmax(...) (the largest n_i), else EINVAL;
+ *   workspace: thrift_select_head_workspace_bytes (every pair's score, the
+ *     per-head threshold and the per-query-block tie offsets).
+ * The idx/cnt it writes drive thrift_attention_fwd unchanged. */
+int thrift_select_head_kmax(int Sq, int Sk, int block_q, int block_k, int causal);
+size_t thrift_select_head_workspace_bytes(int B, int Hq, int Sq, int Sk, int block_q, int block_k);
+thrift_status thrift_select_blocks_head(const float* qbar, const float* kbar, int B, int Hq, int Hkv, int Sq,
+                                        int Sk, int D, int block_q, int block_k, int causal, int topk_count,
+                                        int topk_bp, int32_t* idx, int32_t* cnt, int kmax, void* workspace,
+                                        size_t workspace_bytes, hipStream_t stream);
+
 /* ---------------------------------------------------------------------- */
 /* FP4 quantisation (the FP4 path's NVFP4 micro-scaling)                    */
 /* ---------------------------------------------------------------------- */
@@ -180,33 +199,6 @@ thrift_status thrift_quantize_fp4(const void* x16, int B, int H, int S, int D,
                                   uint8_t* scales, float* tensor_scale, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
-/* Re-encode part of an MXFP4 KV-cache copy after new tokens were written to
- * positions s0 <= s < s1 of x16 [B,H,S,D] (the FP4 copy of the cache,
- * summaries "Betekenis en Beweringen").  Along THRIFT_GROUP_D the rows
- * s0..s1-1 are re-encoded; along THRIFT_GROUP_S every 128-position tile that
- * holds one of them.  Each byte written equals the byte thrift_quantize_fp4
- * writes for the tensor as it is now; bytes outside those rows or tiles are
- * not touched.  MXFP4 only (an NVFP4 slice scale depends on the whole slice:
- * THRIFT_EUNSUPPORTED); 0 <= s0 < s1 <= S, else THRIFT_EINVAL. */
-/* Per-head budget: the other reading of "the top-k highest-scoring block
- * pairs" (summaries "Heuristische Blokkenselectie"): one budget over all
- * valid pairs of a query head, K = min(P, topk_count) or
- * ceil(P * topk_bp / 10^4) of its P valid pairs, the K best-scoring pairs
- * kept (ties: lower query block, then lower key block).  Scores as
- * thrift_select_blocks; means as thrift_select_blocks_means takes them.
- *   idx [B,Hq,nQ,kmax] (out): each query block's kept key blocks ascending,
- *     padded with -1; cnt [B,Hq,nQ] (out): their number (0 .. n_i);
- *   kmax >= thrift_select_head_kmax(...) (the largest n_i), else EINVAL;
- *   workspace: thrift_select_head_workspace_bytes (every pair's score, the
- *     per-head threshold and the per-query-block tie offsets).
- * The idx/cnt it writes drive thrift_attention_fwd unchanged. */
-int thrift_select_head_kmax(int Sq, int Sk, int block_q, int block_k, int causal);
-size_t thrift_select_head_workspace_bytes(int B, int Hq, int Sq, int Sk, int block_q, int block_k);
-thrift_status thrift_select_blocks_head(const float* qbar, const float* kbar, int B, int Hq, int Hkv, int Sq,
-                                        int Sk, int D, int block_q, int block_k, int causal, int topk_count,
-                                        int topk_bp, int32_t* idx, int32_t* cnt, int kmax, void* workspace,
-                                        size_t workspace_bytes, hipStream_t stream);
-
 /* Block means and FP4 codes along D (Q or K) from one read of x16: the
  * selection's block means and the FP4 path's operand in a single pass
  * (summaries "Methodologie": both come from the same fp16 Q and K).
@@ -223,9 +215,22 @@ thrift_status thrift_quantize_fp4_means(const void* x16, int B, int H, int S, in
                                         float* means, void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
 
+/* Re-encode part of a KV-cache FP4 copy after new tokens were written to
+ * positions s0 <= s < s1 of x16 [B,H,S,D] (the FP4 copy of the cache,
+ * summaries "Betekenis en Beweringen").  Along THRIFT_GROUP_D the rows
+ * s0..s1-1 are re-encoded; along THRIFT_GROUP_S every 128-position tile that
+ * holds one of them.  Bytes outside those rows or tiles are not touched.
+ *   MXFP4: each byte written equals the byte thrift_quantize_fp4 writes for
+ *     the tensor as it is now (MX groups depend on nothing else);
+ *   NVFP4: tensor_scale [B,H] (in, required) is the slice scale the copy was
+ *     encoded with and is kept, so the bytes equal a whole-tensor encode as
+ *     long as the new positions do not raise the slice's maximum (a caller
+ *     whose new tokens do re-encodes the slice with thrift_quantize_fp4).
+ * 0 <= s0 < s1 <= S, else THRIFT_EINVAL. */
 thrift_status thrift_quantize_fp4_range(const void* x16, int B, int H, int S, int D,
                                         thrift_group_axis axis, thrift_format fmt, int s0, int s1,
-                                        uint8_t* codes, uint8_t* scales, hipStream_t stream);
+                                        uint8_t* codes, uint8_t* scales, const float* tensor_scale,
+                                        hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
 /* Mixed FP4/FP16 attention ("Gemengd-Precisie Berekening & Samenvoeging")  */
@@ -293,9 +298,11 @@ size_t thrift_attention_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, i
  *   workspace: device buffer of at least
  *     thrift_attention_decode_workspace_bytes(...), caller-owned, 16-byte
  *     aligned; its contents are scratch.
- * Supported: THRIFT_MXFP4 (THRIFT_NVFP4 returns THRIFT_EUNSUPPORTED), D 64 or
- * 128, block_k 64, Sq <= 128 and (Hq/Hkv)*Sq <= 32 (the query heads of a key
- * head and their rows share one 32-column tile), Sk <= 262144. */
+ *   q4_tscale, k4_tscale, v4_tscale: the slice scales, required for
+ *     THRIFT_NVFP4 (EINVAL if NULL), ignored for THRIFT_MXFP4.
+ * Supported: both formats, D 64 or 128, block_k 64, Sq <= 128 and
+ * (Hq/Hkv)*Sq <= 32 (the query heads of a key head and their rows share one
+ * 32-column tile), Sk <= 262144. */
 thrift_status thrift_attention_decode(const void* q16, const void* k16, const void* v16,
                                       const uint8_t* q4_codes, const uint8_t* q4_scales,
                                       const float* q4_tscale, const uint8_t* k4_codes,

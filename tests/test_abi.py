@@ -120,7 +120,7 @@ def test_decode_validation(lib):
 
     assert call(q16=None) == 1
     assert call(ws=None) == 1
-    assert call(fmt=0) == 2  # NVFP4 decode is not built
+    assert call(fmt=0) == 1  # NVFP4 needs its slice scales
     assert call(fmt=5) == 1
     assert call(Sq=600) == 1  # more queries than keys
     assert call(Sq=9, Hq=8, Hkv=2) == 2  # 4 heads x 9 rows > 32 columns
@@ -155,15 +155,15 @@ def test_cache_maintenance_validation(lib):
 
     qr = lib.thrift_quantize_fp4_range
 
-    def qcall(x=A, S=1000, axis=1, fmt=1, s0=999, s1=1000, codes=A):
-        return qr(x, 1, 2, S, 128, axis, fmt, s0, s1, codes, A, None)
+    def qcall(x=A, S=1000, axis=1, fmt=1, s0=999, s1=1000, codes=A, ts=A):
+        return qr(x, 1, 2, S, 128, axis, fmt, s0, s1, codes, A, ts, None)
 
     assert qcall(x=None) == 1
     assert qcall(s0=1000) == 1  # empty range
     assert qcall(s1=1001) == 1
     assert qcall(s0=-1) == 1
     assert qcall(axis=3) == 1
-    assert qcall(fmt=0) == 2  # NVFP4: the slice scale spans the whole slice
+    assert qcall(fmt=0, ts=None) == 1  # NVFP4 re-encodes under the kept slice scales
     assert qcall(codes=A + 1) == 3
 
 

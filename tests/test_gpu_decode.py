@@ -1,5 +1,6 @@
 """GPU parity of the decode-shaped forward (thrift_select_blocks_kv,
-thrift_attention_decode) against the CPU oracle, through the C ABI.
+thrift_attention_decode) against the CPU oracle, through the C ABI, in both
+FP4 formats.
 
 Bit-exact: selected blocks, counts and FP4 codes/scales.  Output: fp32 O and
 LSE to the bounds of the prefill parity tests (max-abs 2e-3 beyond the
@@ -17,19 +18,25 @@ from tests.gpu_harness import compare_out, note, same_fp4
 pytestmark = pytest.mark.gpu
 
 CASES = {
-    # name: (B, Hq, Hkv, Sq, Sk, D, causal, topk_bp)
-    "one_token_gqa4": (2, 8, 2, 1, 2048, 128, True, 500),
-    "rows5_ragged": (1, 4, 1, 5, 1000, 128, True, 1000),
-    "rows8_gqa4": (1, 8, 2, 8, 4096, 128, True, 500),
-    "d64_noncausal": (1, 4, 2, 3, 777, 64, False, 2500),
-    "no_fp16": (1, 8, 2, 2, 1500, 128, True, 0),
-    "all_fp16": (1, 4, 4, 4, 640, 128, True, 10000),
-    "short_cache": (1, 2, 1, 16, 40, 128, True, 5000),
-    "g32_one_token": (1, 32, 1, 1, 3000, 128, True, 500),
+    # name: (B, Hq, Hkv, Sq, Sk, D, causal, topk_bp, fmt)
+    "one_token_gqa4": (2, 8, 2, 1, 2048, 128, True, 500, 1),
+    "rows5_ragged": (1, 4, 1, 5, 1000, 128, True, 1000, 1),
+    "rows8_gqa4": (1, 8, 2, 8, 4096, 128, True, 500, 1),
+    "d64_noncausal": (1, 4, 2, 3, 777, 64, False, 2500, 1),
+    "no_fp16": (1, 8, 2, 2, 1500, 128, True, 0, 1),
+    "all_fp16": (1, 4, 4, 4, 640, 128, True, 10000, 1),
+    "short_cache": (1, 2, 1, 16, 40, 128, True, 5000, 1),
+    "g32_one_token": (1, 32, 1, 1, 3000, 128, True, 500, 1),
+    "nv_one_token_gqa4": (2, 8, 2, 1, 2048, 128, True, 500, 0),
+    "nv_rows5_ragged": (1, 4, 1, 5, 1000, 128, True, 1000, 0),
+    "nv_d64_noncausal": (1, 4, 2, 3, 777, 64, False, 2500, 0),
+    "nv_no_fp16": (1, 8, 2, 2, 1500, 128, True, 0, 0),
+    "nv_g32_one_token": (1, 32, 1, 1, 3000, 128, True, 500, 0),
+    "nv_long_cache": (1, 8, 2, 1, 8192, 128, True, 500, 0),
 }
 
 
-def _run(oracle, w, bp):
+def _run(oracle, w, bp, fmt=1):
     import torch
 
     from fp16_attention_amd import api
@@ -38,13 +45,13 @@ def _run(oracle, w, bp):
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(np.ascontiguousarray(d[n])).to(dev) for n in ("q", "k", "v"))
     idx, cnt = api.thrift_select_blocks(q, k, 128, 64, w.causal, -1, bp)
-    q4 = api.thrift_quantize_fp4(q, api.THRIFT_GROUP_D, api.THRIFT_MXFP4)
-    k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, api.THRIFT_MXFP4)
-    v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, api.THRIFT_MXFP4)
+    q4 = api.thrift_quantize_fp4(q, api.THRIFT_GROUP_D, fmt)
+    k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, fmt)
+    v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, fmt)
     o, lse = api.thrift_attention_decode(q, k, v, q4, k4, v4, idx, cnt, 64, w.causal, out_fp32=True,
                                          with_lse=True)
     torch.cuda.synchronize()
-    r = oracle.pipeline(d["q"], d["k"], d["v"], oracle.MX, 128, 64, w.causal, -1, bp)
+    r = oracle.pipeline(d["q"], d["k"], d["v"], fmt, 128, 64, w.causal, -1, bp)
     g_cnt, g_idx = cnt.cpu().numpy(), idx.cpu().numpy()
     assert np.array_equal(g_cnt, r["cnt"]), "cnt differs"
     km = r["idx"].shape[-1]
@@ -60,11 +67,11 @@ def _run(oracle, w, bp):
 
 @pytest.mark.parametrize("name", list(CASES))
 def test_decode_parity(oracle, name):
-    B, Hq, Hkv, Sq, Sk, D, causal, bp = CASES[name]
+    B, Hq, Hkv, Sq, Sk, D, causal, bp, fmt = CASES[name]
     w = W.WORKLOADS["decode"].with_(B=B, Hq=Hq, Hkv=Hkv, Sq=Sq, S=Sk, D=D, causal=causal, topk_bp=bp,
                                     seed=len(name))
-    note(f"[decode] {name}: B{B} Hq{Hq} Hkv{Hkv} Sq{Sq} Sk{Sk} D{D} causal{int(causal)} bp{bp}")
-    _run(oracle, w, bp)
+    note(f"[decode] {name}: B{B} Hq{Hq} Hkv{Hkv} Sq{Sq} Sk{Sk} D{D} causal{int(causal)} bp{bp} fmt{fmt}")
+    _run(oracle, w, bp, fmt)
 
 
 def test_decode_fp16_output_matches_fp32(oracle):
@@ -91,32 +98,38 @@ def test_decode_full_size(oracle):
     _run(oracle, w, w.topk_bp)
 
 
-def test_cache_maintenance_matches_oracle(oracle):
+@pytest.mark.parametrize("fmt", [1, 0])
+def test_cache_maintenance_matches_oracle(oracle, fmt):
     """Key-block means kept beside the cache and range re-encoding of its
     FP4 copy: bit-identical to the oracle's means and codes of the cache as
     it is after new tokens are written, with blocks and groups outside the
     updated range untouched; selection from the kept means equals selection
-    from the fp16 keys."""
+    from the fp16 keys.  NVFP4 keeps its slice scales: the new tokens are
+    drawn from the slice's own rows, so its maximum does not change."""
     import torch
 
     from fp16_attention_amd import api
 
     w = W.WORKLOADS["decode"].with_(B=2, Hq=8, Hkv=2, Sq=3, S=1000, seed=21)
     d = W.generate(w)
-    note(f"[decode] cache maintenance: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} Sk{w.S}")
+    note(f"[decode] cache maintenance: B{w.B} Hq{w.Hq} Hkv{w.Hkv} Sq{w.Sq} Sk{w.S} fmt{fmt}")
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(np.ascontiguousarray(d[n])).to(dev) for n in ("q", "k", "v"))
     kbar = api.thrift_block_means(k, 64)
-    k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, api.THRIFT_MXFP4)
-    v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, api.THRIFT_MXFP4)
+    k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, fmt)
+    v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, fmt)
     torch.cuda.synchronize()
     assert np.array_equal(kbar.cpu().numpy(), oracle.block_means(d["k"], 64))
     # new tokens at positions 990..999 (the last key block, two V tiles' worth of groups)
     s0, s1 = 990, 1000
     rng = np.random.default_rng(5)
     knew, vnew = d["k"].copy(), d["v"].copy()
-    knew[:, :, s0:s1] = rng.standard_normal(knew[:, :, s0:s1].shape).astype(np.float16)
-    vnew[:, :, s0:s1] = rng.standard_normal(vnew[:, :, s0:s1].shape).astype(np.float16)
+    src = rng.integers(0, s0, size=s1 - s0)
+    knew[:, :, s0:s1] = d["k"][:, :, src][:, :, ::-1] * np.float16(0.5)
+    vnew[:, :, s0:s1] = d["v"][:, :, src] * np.float16(-0.5)
+    if fmt == 0:  # the premise of keeping the slice scales
+        for old, new, ax in ((d["k"], knew, oracle.AXIS_D), (d["v"], vnew, oracle.AXIS_S)):
+            assert np.array_equal(oracle.quantize(old, ax, 0).tensor_scale, oracle.quantize(new, ax, 0).tensor_scale)
     k.copy_(torch.from_numpy(knew))
     v.copy_(torch.from_numpy(vnew))
     before = kbar.clone(), k4.codes.clone(), k4.scales.clone(), v4.codes.clone(), v4.scales.clone()
@@ -126,8 +139,8 @@ def test_cache_maintenance_matches_oracle(oracle):
     torch.cuda.synchronize()
     assert np.array_equal(kbar.cpu().numpy(), oracle.block_means(knew, 64))
     assert torch.equal(kbar[:, :, : s0 // 64], before[0][:, :, : s0 // 64])
-    same_fp4(k4, oracle.quantize(knew, oracle.AXIS_D, oracle.MX))
-    same_fp4(v4, oracle.quantize(vnew, oracle.AXIS_S, oracle.MX))
+    same_fp4(k4, oracle.quantize(knew, oracle.AXIS_D, fmt))
+    same_fp4(v4, oracle.quantize(vnew, oracle.AXIS_S, fmt))
     assert torch.equal(k4.codes[:, :, :s0], before[1][:, :, :s0])
     assert torch.equal(k4.scales[:, :, :s0], before[2][:, :, :s0])
     t0 = s0 // 128 * 2  # V: key blocks of 64 before the first re-encoded 128-position tile
