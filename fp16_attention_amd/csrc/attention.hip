@@ -972,13 +972,14 @@ template <int D, int NW, int FMT>
 static thrift_status launch_attn(const AttnArgs& a, hipStream_t stream) {
   using L = Lds<D>;
   const size_t lds = (size_t)L::PROM + (size_t)a.kmax * 4 + (size_t)((a.S + 64 * 32 - 1) / (64 * 32)) * 4;
-  static bool configured = false;
-  if (!configured) {
-    if (hipFuncSetAttribute((const void*)attn_fwd_kernel<D, NW, FMT>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-      return THRIFT_EHIP;
-    configured = true;
-  }
+  static std::atomic<uint64_t> configured{0};
+  if (once_per_device(configured, [] {
+        return hipFuncSetAttribute((const void*)attn_fwd_kernel<D, NW, FMT>,
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess
+                   ? THRIFT_OK
+                   : THRIFT_EHIP;
+      }) != THRIFT_OK)
+    return THRIFT_EHIP;
   const int items = a.B * a.Hq * a.nq;
   const int grid = (items + kXcds - 1) / kXcds * kXcds;
   attn_fwd_kernel<D, NW, FMT><<<grid, NW * 64, lds, stream>>>(a);
@@ -1499,14 +1500,15 @@ template <int D>
 static thrift_status launch_decode(DecodeArgs& d, int fmt, hipStream_t stream) {
   using M = MxStage<D>;
   const AttnArgs& a = d.kv;
-  static bool configured = false;
-  if (!configured) {
-    for (const void* kf : {(const void*)decode_fp4_kernel<D>, (const void*)decode_nv4_kernel<D>,
-                           (const void*)decode_f16_kernel<D>})
-      if (hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-        return THRIFT_EHIP;
-    configured = true;
-  }
+  static std::atomic<uint64_t> configured{0};
+  if (once_per_device(configured, [] {
+        for (const void* kf : {(const void*)decode_fp4_kernel<D>, (const void*)decode_nv4_kernel<D>,
+                               (const void*)decode_f16_kernel<D>})
+          if (hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+            return THRIFT_EHIP;
+        return THRIFT_OK;
+      }) != THRIFT_OK)
+    return THRIFT_EHIP;
   const size_t pbytes = (size_t)d.G * ((d.nvalid + 31) / 32) * 4;
   if (fmt == THRIFT_MXFP4)
     decode_fp4_kernel<D><<<a.B * a.Hkv * d.nsplit, kDecWaves * 64, 4 * (size_t)M::SIZE + pbytes, stream>>>(d);

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "thrift.h"
 
 namespace thrift {
@@ -42,6 +44,20 @@ __host__ __device__ inline int topk_budget(int n, int topk_count, int topk_bp) {
 }
 
 inline bool aligned16(const void* p) { return ((uintptr_t)p & 15) == 0; }
+
+// Runs set_up() once per device for the caller's flag word (kernel attributes
+// such as the dynamic LDS limit are per device).  Concurrent first calls may
+// both run set_up(), which only sets the same attributes twice.
+template <class F>
+inline thrift_status once_per_device(std::atomic<uint64_t>& done, F&& set_up) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return THRIFT_EHIP;
+  const uint64_t bit = 1ull << dev;
+  if (done.load(std::memory_order_acquire) & bit) return THRIFT_OK;
+  if (set_up() != THRIFT_OK) return THRIFT_EHIP;
+  done.fetch_or(bit, std::memory_order_release);
+  return THRIFT_OK;
+}
 
 inline thrift_status launch_status() {
   hipError_t e = hipGetLastError();

@@ -400,10 +400,10 @@ void launch_score_topk(const float* qm, const float* km, int B, int Hq, int Hkv,
         qm, km, Hq, Hkv, Sq, Sk, bq, bk, causal, topk_count, topk_bp, idx, cnt, kmax, scores_out);
 }
 
-// Raise the dynamic LDS limit of every score kernel once (long sequences).
+// Raise the dynamic LDS limit of every score kernel once per device (long sequences).
 static thrift_status configure_score_kernels() {
-  static bool configured = false;
-  if (!configured) {
+  static std::atomic<uint64_t> configured{0};
+  return once_per_device(configured, [] {
     const void* kernels[] = {
         (const void*)score_topk_kernel<128, 1>,       (const void*)score_topk_kernel<128, 2>,
         (const void*)score_topk_kernel<128, 4>,       (const void*)score_topk_kernel<64, 1>,
@@ -414,9 +414,8 @@ static thrift_status configure_score_kernels() {
     for (const void* kf : kernels)
       if (hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024) != hipSuccess)
         return THRIFT_EHIP;
-    configured = true;
-  }
-  return THRIFT_OK;
+    return THRIFT_OK;
+  });
 }
 
 }  // namespace thrift

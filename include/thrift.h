@@ -18,7 +18,8 @@
  *   - Tensors are contiguous, row-major, [batch, head, seq, dim] unless stated.
  *   - Every pointer is a DEVICE pointer except where marked "host".
  *   - The caller owns and allocates every buffer, workspace included; the
- *     library never allocates, frees or synchronises, and keeps no state.
+ *     library never allocates, frees or synchronises; its only state is a
+ *     per-device flag that its kernels' LDS limits have been raised.
  *   - Every call is asynchronous on `stream`; calls on different streams
  *     may run concurrently when they share no output buffer.
  *   - Arguments are validated before anything is launched; on failure the
