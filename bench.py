@@ -268,7 +268,7 @@ def run_decode(args, w, d, gen_s):
     kbar = api.thrift_block_means(k, w.bk)
     if args.copy_mib:
         copy_calibration(torch, dev, args.copy_mib)
-    s0, nkb = w.S - w.Sq, -(-w.S // w.bk)
+    s0 = w.S - w.Sq
     kmax = max(1, api.thrift_select_kmax(w.Sq, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp, w.S))
     o = torch.empty_like(q)
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -276,9 +276,7 @@ def run_decode(args, w, d, gen_s):
     def step(rec=None):
         if rec:
             rec[0].record()
-        api.thrift_block_means(k, w.bk, s0 // w.bk, nkb, out=kbar)
-        api.thrift_quantize_fp4_range(k, k4, s0, w.S)
-        api.thrift_quantize_fp4_range(v, v4, s0, w.S)
+        api.thrift_cache_update(k, v, kbar, k4, v4, s0, w.S, w.bk)
         q4, qbar = api.thrift_quantize_fp4_means(q, fmt, w.bq)
         idx, cnt = api.thrift_select_blocks_means(qbar, kbar, w.Sq, w.S, w.bq, w.bk, w.causal, w.topk_count,
                                                   w.topk_bp, kmax)

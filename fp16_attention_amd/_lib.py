@@ -14,7 +14,7 @@ EXPORTS = ("thrift_select_kmax", "thrift_select_workspace_bytes", "thrift_select
            "thrift_block_means", "thrift_select_blocks_kbar", "thrift_select_blocks_means",
            "thrift_select_head_kmax", "thrift_select_head_workspace_bytes", "thrift_select_blocks_head",
            "thrift_quantize_means_workspace_bytes", "thrift_quantize_fp4_means",
-           "thrift_quantize_workspace_bytes", "thrift_quantize_fp4", "thrift_quantize_fp4_range",
+           "thrift_quantize_workspace_bytes", "thrift_quantize_fp4", "thrift_quantize_fp4_range", "thrift_cache_update",
            "thrift_attention_fwd",
            "thrift_attention_decode_workspace_bytes", "thrift_attention_decode",
            "thrift_status_string")
@@ -66,6 +66,8 @@ def load():
         L.thrift_select_head_workspace_bytes.argtypes = [I] * 6
         L.thrift_select_blocks_head.restype = I
         L.thrift_select_blocks_head.argtypes = [P, P] + [I] * 11 + [P, P, I, P, SZ, P]
+        L.thrift_cache_update.restype = I
+        L.thrift_cache_update.argtypes = [P, P] + [I] * 8 + [P] * 7 + [P]
         L.thrift_quantize_fp4_range.restype = I
         L.thrift_quantize_fp4_range.argtypes = [P] + [I] * 8 + [P, P, P, P]
         L.thrift_attention_decode_workspace_bytes.restype = SZ

@@ -18,7 +18,7 @@ from ._lib import THRIFT_GROUP_D, THRIFT_GROUP_S, THRIFT_MXFP4, THRIFT_NVFP4, Th
 __all__ = ["thrift_select_kmax", "thrift_select_blocks", "thrift_block_means",
            "thrift_select_blocks_kbar", "thrift_select_blocks_means", "thrift_select_blocks_head",
            "thrift_quantize_fp4",
-           "thrift_quantize_fp4_means", "thrift_quantize_fp4_range",
+           "thrift_quantize_fp4_means", "thrift_quantize_fp4_range", "thrift_cache_update",
            "thrift_attention_fwd", "thrift_attention_decode", "thrift_decode", "FP4Tensor",
            "fp4_transposed", "thrift_forward", "THRIFT_NVFP4", "THRIFT_MXFP4", "THRIFT_GROUP_D",
            "THRIFT_GROUP_S", "ThriftError"]
@@ -209,6 +209,20 @@ def thrift_quantize_fp4_range(x16, t: FP4Tensor, s0, s1):
     _call("thrift_quantize_fp4_range", _ptr(x16), B, H, S, D, t.axis, t.fmt, s0, s1, _ptr(t.codes),
           _ptr(t.scales), _ptr(t.tensor_scale), _stream())
     return t
+
+
+def thrift_cache_update(k16, v16, kbar, k4: FP4Tensor, v4: FP4Tensor, s0, s1, block_k=64):
+    """After new tokens were written to positions s0..s1-1 of the fp16 cache
+    (k16, v16): their key blocks' means into kbar, their K rows' and V tiles'
+    FP4 codes into k4, v4 (in place), in one launch."""
+    _check(k16, torch.float16, "k16")
+    _check(v16, torch.float16, "v16")
+    _check(kbar, torch.float32, "kbar")
+    B, H, S, D = k16.shape
+    _call("thrift_cache_update", _ptr(k16), _ptr(v16), B, H, S, D, block_k, s0, s1, k4.fmt, _ptr(kbar),
+          _ptr(k4.codes), _ptr(k4.scales), _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales),
+          _ptr(v4.tensor_scale), _stream())
+    return kbar, k4, v4
 
 
 def fp4_transposed(t: FP4Tensor):

@@ -162,19 +162,12 @@ __device__ inline uint32_t encode_mx_32(const float* v, uint32_t* w /*4 dwords*/
 // Thread li encodes group gi = (li / range) * groups_per_slice + first + li % range:
 // `range` groups from group `first` of every (batch, head) slice (the whole
 // slice when range == groups_per_slice and first == 0).
+// Group gi (g consecutive elements along D) of x: its code bytes and scale byte.
 template <int FMT>
-__global__ __launch_bounds__(kQThreads) void quant_d_kernel(const _Float16* __restrict__ x,
-                                                            size_t ngroups, int groups_per_slice,
-                                                            int range, int first,
-                                                            const float* __restrict__ tscale,
-                                                            uint8_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales) {
+__device__ inline void quant_d_group(const _Float16* __restrict__ x, size_t gi, int groups_per_slice,
+                                     const float* __restrict__ tscale, uint8_t* __restrict__ codes,
+                                     uint8_t* __restrict__ scales) {
   constexpr int g = FMT == THRIFT_NVFP4 ? 16 : 32;
-  const size_t li = (size_t)blockIdx.x * kQThreads + threadIdx.x;
-  if (li >= ngroups) return;
-  const size_t gi = range == groups_per_slice
-                        ? li
-                        : (li / range) * groups_per_slice + first + li % range;
   float v[g];
   const v8h* src = reinterpret_cast<const v8h*>(x + gi * g);
 #pragma unroll
@@ -195,20 +188,32 @@ __global__ __launch_bounds__(kQThreads) void quant_d_kernel(const _Float16* __re
   }
 }
 
+template <int FMT>
+__global__ __launch_bounds__(kQThreads) void quant_d_kernel(const _Float16* __restrict__ x,
+                                                            size_t ngroups, int groups_per_slice,
+                                                            int range, int first,
+                                                            const float* __restrict__ tscale,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  const size_t li = (size_t)blockIdx.x * kQThreads + threadIdx.x;
+  if (li >= ngroups) return;
+  const size_t gi = range == groups_per_slice
+                        ? li
+                        : (li / range) * groups_per_slice + first + li % range;
+  quant_d_group<FMT>(x, gi, groups_per_slice, tscale, codes, scales);
+}
+
 // ---- groups along S (V, stored transposed) -------------------------------------
 
 constexpr int kVTile = 128;  // tokens per workgroup
 
+// Tile tt (kVTile positions) of slice bh of x, staged through tile[][] (LDS).
 template <int FMT, int D>
-__global__ __launch_bounds__(kQThreads) void quant_s_kernel(const _Float16* __restrict__ x, int S,
-                                                            int Sp, int tile0,
-                                                            const float* __restrict__ tscale,
-                                                            uint8_t* __restrict__ codes,
-                                                            uint8_t* __restrict__ scales) {
+__device__ inline void quant_s_tile(const _Float16* __restrict__ x, int S, int Sp, int tt, int bh, int t,
+                                    _Float16 (*tile)[D + 2], const float* __restrict__ tscale,
+                                    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales) {
   constexpr int g = FMT == THRIFT_NVFP4 ? 16 : 32;
   constexpr int GPT = kVTile / g;  // groups per d in this tile
-  __shared__ _Float16 tile[kVTile][D + 2];
-  const int tt = tile0 + blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
   const int s0 = tt * kVTile;
   const _Float16* base = x + (size_t)bh * S * D;
   // stage kVTile x D fp16 (zeros past S)
@@ -241,6 +246,62 @@ __global__ __launch_bounds__(kQThreads) void quant_s_kernel(const _Float16* __re
       scales[srow] = (uint8_t)encode_mx_32(v, w);
       *reinterpret_cast<uint4*>(codes + crow) = make_uint4(w[0], w[1], w[2], w[3]);
     }
+  }
+}
+
+template <int FMT, int D>
+__global__ __launch_bounds__(kQThreads) void quant_s_kernel(const _Float16* __restrict__ x, int S,
+                                                            int Sp, int tile0,
+                                                            const float* __restrict__ tscale,
+                                                            uint8_t* __restrict__ codes,
+                                                            uint8_t* __restrict__ scales) {
+  __shared__ _Float16 tile[kVTile][D + 2];
+  quant_s_tile<FMT, D>(x, S, Sp, tile0 + blockIdx.x, blockIdx.y, threadIdx.x, tile, tscale, codes, scales);
+}
+
+// ---- KV-cache update: what new positions change, in one launch ----------------------
+
+// For new positions s0 <= s < s1 of a cache slice (blockIdx.y): workgroups
+// [0, nmeans) compute the mean of key block j0 + blockIdx.x (as
+// block_means_kernel: fp64 column sums, one rounding); the next ndg encode
+// K's groups along D of rows s0..s1-1 (as quant_d_kernel); the rest encode
+// the V tiles from t0 on (as quant_s_kernel).  The branch is uniform per
+// workgroup.
+template <int FMT, int D>
+__global__ __launch_bounds__(kQThreads) void cache_update_kernel(
+    const _Float16* __restrict__ k16, const _Float16* __restrict__ v16, int S, int blk, int nb, int j0,
+    int nmeans, int s0, int s1, int ndg, int t0, float* __restrict__ kbar, const float* __restrict__ k4t,
+    uint8_t* __restrict__ k4c, uint8_t* __restrict__ k4s, const float* __restrict__ v4t,
+    uint8_t* __restrict__ v4c, uint8_t* __restrict__ v4s) {
+  constexpr int CG = D / 8, RP = kQThreads / CG;
+  constexpr int g = FMT == THRIFT_NVFP4 ? 16 : 32;
+  __shared__ double red[RP][D + 1];
+  __shared__ _Float16 tile[kVTile][D + 2];
+  const int x = blockIdx.x, bh = blockIdx.y, t = threadIdx.x;
+  if (x < nmeans) {
+    const int j = j0 + x, cg = t % CG, rp = t / CG;
+    const int r0 = j * blk, r1 = min(S, r0 + blk);
+    const _Float16* base = k16 + (size_t)bh * S * D + cg * 8;
+    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int r = r0 + rp; r < r1; r += RP) {
+      const v8h h = *reinterpret_cast<const v8h*>(base + (size_t)r * D);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] += (double)(float)h[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) red[rp][cg * 8 + e] = acc[e];
+    __syncthreads();
+    if (t < D) {
+      double sum = 0.0;
+      for (int k = 0; k < RP; ++k) sum += red[k][t];
+      kbar[((size_t)bh * nb + j) * D + t] = (float)(sum / (double)(r1 - r0));
+    }
+  } else if (x < nmeans + ndg) {
+    const int gpr = D / g, li = (x - nmeans) * kQThreads + t;
+    if (li < (s1 - s0) * gpr)
+      quant_d_group<FMT>(k16, (size_t)bh * S * gpr + (size_t)s0 * gpr + li, S * gpr, k4t, k4c, k4s);
+  } else {
+    quant_s_tile<FMT, D>(v16, S, cdiv(S, 64) * 64, t0 + (x - nmeans - ndg), bh, t, tile, v4t, v4c, v4s);
   }
 }
 
@@ -472,5 +533,44 @@ extern "C" thrift_status thrift_quantize_fp4_means(const void* x16, int B, int H
     quant_d_kernel<THRIFT_NVFP4><<<blocks, kQThreads, 0, stream>>>(x, ngroups, gps, gps, 0, tensor_scale,
                                                                      codes, scales);
   }
+  return launch_status();
+}
+
+extern "C" thrift_status thrift_cache_update(const void* k16, const void* v16, int B, int H, int S, int D,
+                                             int block_k, int s0, int s1, thrift_format fmt, float* kbar,
+                                             uint8_t* k4_codes, uint8_t* k4_scales, const float* k4_tscale,
+                                             uint8_t* v4_codes, uint8_t* v4_scales, const float* v4_tscale,
+                                             hipStream_t stream) {
+  if (!k16 || !v16 || !kbar || !k4_codes || !k4_scales || !v4_codes || !v4_scales) return THRIFT_EINVAL;
+  if (B < 1 || H < 1 || S < 1 || block_k < 1 || s0 < 0 || s1 > S || s0 >= s1) return THRIFT_EINVAL;
+  if (fmt != THRIFT_NVFP4 && fmt != THRIFT_MXFP4) return THRIFT_EINVAL;
+  if (fmt == THRIFT_NVFP4 && (!k4_tscale || !v4_tscale)) return THRIFT_EINVAL;
+  if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
+  if (S > 262144 || B * H > 65535) return THRIFT_EUNSUPPORTED;
+  if (!aligned16(k16) || !aligned16(v16) || !aligned16(kbar) || !aligned16(k4_codes) || !aligned16(v4_codes))
+    return THRIFT_EALIGN;
+  const int g = fmt == THRIFT_NVFP4 ? 16 : 32;
+  const int j0 = s0 / block_k, nmeans = (s1 - 1) / block_k - j0 + 1, nb = cdiv(S, block_k);
+  const int ndg = cdiv((s1 - s0) * (D / g), kQThreads);
+  const int t0 = s0 / kVTile, ntiles = cdiv(s1, kVTile) - t0;
+  const dim3 grid(nmeans + ndg + ntiles, B * H);
+  auto k = (const _Float16*)k16;
+  auto v = (const _Float16*)v16;
+#define THRIFT_CACHE_UPDATE(F, DD)                                                                          \
+  cache_update_kernel<F, DD><<<grid, kQThreads, 0, stream>>>(k, v, S, block_k, nb, j0, nmeans, s0, s1, ndg, t0, \
+                                                            kbar, k4_tscale, k4_codes, k4_scales, v4_tscale,   \
+                                                            v4_codes, v4_scales)
+  if (fmt == THRIFT_MXFP4) {
+    if (D == 128)
+      THRIFT_CACHE_UPDATE(THRIFT_MXFP4, 128);
+    else
+      THRIFT_CACHE_UPDATE(THRIFT_MXFP4, 64);
+  } else {
+    if (D == 128)
+      THRIFT_CACHE_UPDATE(THRIFT_NVFP4, 128);
+    else
+      THRIFT_CACHE_UPDATE(THRIFT_NVFP4, 64);
+  }
+#undef THRIFT_CACHE_UPDATE
   return launch_status();
 }

@@ -122,12 +122,14 @@ constexpr int kHeadChunk = 4;  // query heads scored together per pass
 // for QB x (up to) four query-head rows.  With OUT (per-head budgets) the
 // scores of the valid pairs go to scores_out [B,Hq,nQ,nK] instead of a
 // per-row top-k.
-template <int D, int QB, bool OUT = false>
+template <int D, int QB, bool OUT = false, int HC = kHeadChunk>
 __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
     const float* __restrict__ qm, const float* __restrict__ km, int Hq, int Hkv, int Sq, int Sk, int bq,
     int bk, int causal, int topk_count, int topk_bp, int32_t* __restrict__ idx,
     int32_t* __restrict__ cnt, int kmax, float* __restrict__ scores_out = nullptr) {
-  constexpr int NR = QB * kHeadChunk;  // score rows per pass: (query block, head)
+  // HC query heads per pass; with HC < kHeadChunk the group's heads are
+  // spread over blockIdx.z (more workgroups when there are few query blocks)
+  constexpr int NR = QB * HC;  // score rows per pass: (query block, head)
   extern __shared__ float sc[];         // [NR][nK] scores
   __shared__ __attribute__((aligned(16))) float qv[NR][D];
 
@@ -140,11 +142,13 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
   const int nmax = valid_kv_blocks_kv(i0 + nqb - 1, Sq, Sk, bq, bk, causal);
   const float* kbase = km + (size_t)bhk * nK * D;
 
-  for (int h0 = 0; h0 < G; h0 += kHeadChunk) {
-    const int nh = min(kHeadChunk, G - h0);
+  const int hz = HC < kHeadChunk ? (int)blockIdx.z * HC : 0;
+  const int hend = HC < kHeadChunk ? min(G, hz + HC) : G;
+  for (int h0 = hz; h0 < hend; h0 += HC) {
+    const int nh = min(HC, hend - h0);
     __syncthreads();
     for (int e = t; e < NR * D; e += kTopkThreads) {
-      const int rr = e / D, d = e % D, qb = rr / kHeadChunk, h = rr % kHeadChunk;
+      const int rr = e / D, d = e % D, qb = rr / HC, h = rr % HC;
       const int hq = hk * G + h0 + h;
       qv[rr][d] = (h < nh && qb < nqb) ? qm[(((size_t)b * Hq + hq) * nq + i0 + qb) * D + d] : 0.0f;
     }
@@ -188,7 +192,7 @@ __global__ __launch_bounds__(kTopkThreads) void score_topk_kernel(
 
     const int wave_u = __builtin_amdgcn_readfirstlane(wave);
     for (int rr = wave_u; rr < NR; rr += kTopkThreads / kWave) {  // one wavefront per row
-      const int qb = rr / kHeadChunk, h = rr % kHeadChunk;
+      const int qb = rr / HC, h = rr % HC;
       if (qb >= nqb || h >= nh) continue;
       const int i = i0 + qb, hq = hk * G + h0 + h;
       const int n = valid_kv_blocks_kv(i, Sq, Sk, bq, bk, causal);
@@ -387,6 +391,12 @@ void launch_score_topk(const float* qm, const float* km, int B, int Hq, int Hkv,
                        int causal, int topk_count, int topk_bp, int32_t* idx, int32_t* cnt, int kmax,
                        hipStream_t stream, float* scores_out = nullptr) {
   const int nq = cdiv(Sq, bq), nk = cdiv(Sk, bk), qb = topk_qb(nq, nk);
+  if (nq < 8) {  // few query blocks (decode): one query head per workgroup
+    const dim3 grid(nq, B * Hkv, Hq / Hkv);
+    score_topk_kernel<D, 1, OUT, 1><<<grid, kTopkThreads, (size_t)nk * sizeof(float), stream>>>(
+        qm, km, Hq, Hkv, Sq, Sk, bq, bk, causal, topk_count, topk_bp, idx, cnt, kmax, scores_out);
+    return;
+  }
   const size_t lds = (size_t)qb * kHeadChunk * nk * sizeof(float);
   const dim3 grid(cdiv(nq, qb), B * Hkv);
   if (qb == 4)
@@ -410,7 +420,9 @@ static thrift_status configure_score_kernels() {
         (const void*)score_topk_kernel<64, 2>,        (const void*)score_topk_kernel<64, 4>,
         (const void*)score_topk_kernel<128, 1, true>, (const void*)score_topk_kernel<128, 2, true>,
         (const void*)score_topk_kernel<128, 4, true>, (const void*)score_topk_kernel<64, 1, true>,
-        (const void*)score_topk_kernel<64, 2, true>,  (const void*)score_topk_kernel<64, 4, true>};
+        (const void*)score_topk_kernel<64, 2, true>,  (const void*)score_topk_kernel<64, 4, true>,
+        (const void*)score_topk_kernel<128, 1, false, 1>, (const void*)score_topk_kernel<64, 1, false, 1>,
+        (const void*)score_topk_kernel<128, 1, true, 1>,  (const void*)score_topk_kernel<64, 1, true, 1>};
     for (const void* kf : kernels)
       if (hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024) != hipSuccess)
         return THRIFT_EHIP;

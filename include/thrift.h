@@ -233,6 +233,18 @@ thrift_status thrift_quantize_fp4_range(const void* x16, int B, int H, int S, in
                                         uint8_t* codes, uint8_t* scales, const float* tensor_scale,
                                         hipStream_t stream);
 
+/* The same cache maintenance in one launch: after new tokens were written to
+ * positions s0 <= s < s1 of the cache's fp16 k16 and v16 [B,H,S,D], the
+ * means of the key blocks (block_k rows) that hold them into kbar
+ * [B,H,ceil(S/block_k),D] (as thrift_block_means), K's FP4 rows (as
+ * thrift_quantize_fp4_range along THRIFT_GROUP_D) and V's FP4 tiles (along
+ * THRIFT_GROUP_S).  Byte for byte the results of those three calls; the
+ * NVFP4 slice scales k4_tscale, v4_tscale are read, not changed. */
+thrift_status thrift_cache_update(const void* k16, const void* v16, int B, int H, int S, int D, int block_k,
+                                  int s0, int s1, thrift_format fmt, float* kbar, uint8_t* k4_codes,
+                                  uint8_t* k4_scales, const float* k4_tscale, uint8_t* v4_codes,
+                                  uint8_t* v4_scales, const float* v4_tscale, hipStream_t stream);
+
 /* ---------------------------------------------------------------------- */
 /* Mixed FP4/FP16 attention ("Gemengd-Precisie Berekening & Samenvoeging")  */
 /* ---------------------------------------------------------------------- */

@@ -214,3 +214,18 @@ def test_head_budget_validation(lib):
     need = lib.thrift_select_head_workspace_bytes(1, 4, 1000, 1000, 128, 64)
     assert need >= 4 * 8 * 16 * 4
     assert call(wsb=need - 1) == 4
+
+
+def test_cache_update_validation(lib):
+    f = lib.thrift_cache_update
+
+    def call(k=A, S=1000, s0=990, s1=1000, fmt=1, kbar=A, kt=None, vt=None, D=128):
+        return f(k, A, 1, 2, S, D, 64, s0, s1, fmt, kbar, A, A, kt, A, A, vt, None)
+
+    assert call(k=None) == 1
+    assert call(s0=1000) == 1
+    assert call(s1=1001) == 1
+    assert call(fmt=0) == 1  # NVFP4 needs the kept slice scales
+    assert call(fmt=7) == 1
+    assert call(D=80) == 2
+    assert call(kbar=A + 4) == 3

@@ -133,10 +133,17 @@ def test_cache_maintenance_matches_oracle(oracle, fmt):
     k.copy_(torch.from_numpy(knew))
     v.copy_(torch.from_numpy(vnew))
     before = kbar.clone(), k4.codes.clone(), k4.scales.clone(), v4.codes.clone(), v4.scales.clone()
+    # the one-launch update on copies, against the three separate calls below
+    copies = (kbar.clone(), api.FP4Tensor(k4.codes.clone(), k4.scales.clone(), k4.tensor_scale, k4.fmt, k4.axis),
+              api.FP4Tensor(v4.codes.clone(), v4.scales.clone(), v4.tensor_scale, v4.fmt, v4.axis))
+    api.thrift_cache_update(k, v, *copies, s0, s1)
     api.thrift_block_means(k, 64, s0 // 64, -(-s1 // 64), out=kbar)
     api.thrift_quantize_fp4_range(k, k4, s0, s1)
     api.thrift_quantize_fp4_range(v, v4, s0, s1)
     torch.cuda.synchronize()
+    assert torch.equal(copies[0], kbar)
+    assert torch.equal(copies[1].codes, k4.codes) and torch.equal(copies[1].scales, k4.scales)
+    assert torch.equal(copies[2].codes, v4.codes) and torch.equal(copies[2].scales, v4.scales)
     assert np.array_equal(kbar.cpu().numpy(), oracle.block_means(knew, 64))
     assert torch.equal(kbar[:, :, : s0 // 64], before[0][:, :, : s0 // 64])
     same_fp4(k4, oracle.quantize(knew, oracle.AXIS_D, fmt))
