@@ -337,8 +337,8 @@ def run_decode(args, w, d, gen_s):
         "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": HBM / 1e9, "unit": "GB/s",
                      "frac": round(achieved / HBM, 4), "traffic": measured_traffic(w.name, args.fmt),
                      "traffic_algorithmic": int(alg),
-                     "kernel": ("decode_fp4_kernel" if fmt == api.THRIFT_MXFP4 else "decode_nv4_kernel")
-                     + " + decode_f16_kernel + decode_merge_kernel"},
+                     "kernel": ("decode_mx_fused_kernel" if fmt == api.THRIFT_MXFP4
+                                else "decode_nv4_kernel + decode_f16_kernel") + " + decode_merge_kernel"},
         "breakdown_ms": {"cache_update_select_quantize_q": round(prep_ms, 4), "attention_decode": round(fwd_ms, 4)},
         "bytes": {"fp4_cache": int(fp4_cache), "fp16_promoted_tiles": int(fp16_tiles), "q_and_o": int(qo)},
         "input_gen_s": round(gen_s, 1),

@@ -1032,13 +1032,12 @@ __device__ inline void store_partial(float* dst, const RowState<D>& st, int lane
 }
 
 template <int D>
-__global__ __launch_bounds__(kDecWaves * 64, 2) void decode_fp4_kernel(DecodeArgs d) {
+__device__ inline void decode_fp4_body(const DecodeArgs& d, int unit, char* smem) {
   using M = MxStage<D>;
   constexpr int NT = kDecWaves * 64;
-  extern __shared__ __attribute__((aligned(16))) char smem[];
   const AttnArgs& a = d.kv;
   const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), hi = lane >> 5;
-  const int unit = blockIdx.x, sidx = unit % d.nsplit;
+  const int sidx = unit % d.nsplit;
   const size_t bhk = unit / d.nsplit;
   const int b = (int)(bhk / a.Hkv), hk = (int)(bhk % a.Hkv);
   const int Sk = a.S, Sq = d.Sq, G = d.G, ncol = G * Sq;
@@ -1238,21 +1237,24 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void decode_nv4_kernel(DecodeArg
   }
 }
 
+// One FP16 unit per wave: (batch, query head, promoted slot) `unit`, V^T
+// staged in this wave's LDS slice vt_smem.  Every wave of the workgroup
+// passes the one barrier, also with no unit (unit < 0 or past cnt).
 template <int D>
-__global__ __launch_bounds__(64) void decode_f16_kernel(DecodeArgs d) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
+__device__ inline void decode_f16_body(const DecodeArgs& d, int unit, char* vt_smem) {
   const AttnArgs& a = d.kv;
-  const int lane = threadIdx.x, hi = lane >> 5;
-  const int unit = blockIdx.x, p = unit % a.kmax;
-  const size_t bhq = unit / a.kmax;
-  const int ncnt = min(max(a.cnt[bhq], 0), a.kmax);
-  if (p >= ncnt) return;  // the merge reads units p < cnt only
+  const int lane = threadIdx.x & 63, hi = lane >> 5;
+  const int p = unit >= 0 ? unit % a.kmax : 0;
+  const size_t bhq = unit >= 0 ? unit / a.kmax : 0;
+  const int ncnt = unit >= 0 ? min(max(a.cnt[bhq], 0), a.kmax) : 0;
+  const bool live = p < ncnt;  // the merge reads units p < cnt only
   const int b = (int)(bhq / a.Hq), hq = (int)(bhq % a.Hq);
   const size_t bhk = (size_t)b * a.Hkv + hq / d.G;
   const int Sk = a.S, Sq = d.Sq;
   const int col = lane & 31, r = col < Sq ? col : 0;
   const int qpos = Sk - Sq + r;
-  const int j = a.idx[bhq * a.kmax + p];
+  const int j = live ? a.idx[bhq * a.kmax + p] : -1;
+  const bool act = j >= 0 && j < d.nvalid;
 
   RowState<D> st;
 #pragma unroll
@@ -1260,22 +1262,22 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeArgs d) {
   st.m = kMInit;
   st.l = 0.0f;
   st.g = 1.0f;
-  if (j >= 0 && j < d.nvalid) {
+  using L = Lds<D>;
+  _Float16* vt = (_Float16*)vt_smem;  // V^T: D rows of VROWH halves
+  v8h qh[D / 16], ka[2][D / 16];
+  if (act) {
     // Every load goes out first: the query rows; K in MFMA operand order
     // (the rows krow(mt, r32), 16-byte chunks straight into registers, no
     // LDS); V as (key pair, 8 channels) items, transposed into LDS below.
     // Rows past the cache's end read as zeros through the buffer resources'
     // record counts (their scores are masked).
-    using L = Lds<D>;
     constexpr int w3 = 0x00020000;  // raw buffer, 32-bit data format
     const int r32 = lane & 31;
     const auto krs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k16 + bhk * Sk * D), 0, Sk * D * 2, w3);
     const auto vrs = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v16 + bhk * Sk * D), 0, Sk * D * 2, w3);
-    v8h qh[D / 16];
     const size_t qoff = (bhq * Sq + r) * D + hi * 8;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qh[kk] = col < Sq ? *(const v8h*)(a.q16 + qoff + kk * 16) : v8h{};
-    v8h ka[2][D / 16];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -1290,7 +1292,6 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeArgs d) {
       v0[p] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(vrs, (key * D + cv) * 2, 0, 0));
       v1[p] = __builtin_bit_cast(v4i, __builtin_amdgcn_raw_buffer_load_b128(vrs, ((key + 1) * D + cv) * 2, 0, 0));
     }
-    _Float16* vt = (_Float16*)smem;  // V^T: D rows of VROWH halves
 #pragma unroll
     for (int p = 0; p < PV; ++p) {
       const int c = lane + p * 64, kp = c % (kBk / 2), cv = (c / (kBk / 2)) * 8;
@@ -1301,7 +1302,9 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeArgs d) {
         dst[(2 * w + 1) * (L::VROWH / 2)] = __builtin_amdgcn_perm((uint32_t)v1[p][w], (uint32_t)v0[p][w], 0x07060302u);
       }
     }
-    __syncthreads();
+  }
+  __syncthreads();
+  if (act) {
     v16f sc[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -1313,7 +1316,29 @@ __global__ __launch_bounds__(64) void decode_f16_kernel(DecodeArgs d) {
     const bool need_mask = (a.causal && key0 + kBk - 1 > Sk - Sq) || key0 + kBk > Sk;
     fp16_softmax_pv<D>(st, sc, vt, a.sm_log2, key0, qpos, Sk, a.causal, need_mask, lane);
   }
-  if (col < Sq) store_partial<D>(d.part16 + ((bhq * a.kmax + p) * Sq + col) * kPartStride<D>, st, lane);
+  if (live && col < Sq) store_partial<D>(d.part16 + ((bhq * a.kmax + p) * Sq + col) * kPartStride<D>, st, lane);
+}
+
+template <int D>
+__global__ __launch_bounds__(64) void decode_f16_kernel(DecodeArgs d) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  decode_f16_body<D>(d, blockIdx.x, smem);
+}
+
+// MXFP4 decode forward in one launch: the first n4wg workgroups are the FP4
+// splits (the long chains, so they start first); the rest hold four FP16
+// units each, one per wave, and fill the compute units as the splits drain
+// instead of waiting for the last of them.  Units past n16 do nothing.
+template <int D>
+__global__ __launch_bounds__(kDecWaves * 64, 2) void decode_mx_fused_kernel(DecodeArgs d, int n4wg, int n16) {
+  extern __shared__ __attribute__((aligned(16))) char smem[];
+  const int x = blockIdx.x;
+  if (x < n4wg) {
+    decode_fp4_body<D>(d, x, smem);
+    return;
+  }
+  const int w = threadIdx.x >> 6, unit = (x - n4wg) * kDecWaves + w;
+  decode_f16_body<D>(d, unit < n16 ? unit : -1, smem + w * (D * Lds<D>::VROWH * 2));
 }
 
 constexpr int kMergeThreads = 256;
@@ -1407,8 +1432,8 @@ template __global__ void attn_fwd_kernel<128, 4, THRIFT_NVFP4>(AttnArgs);
 template __global__ void attn_fwd_kernel<128, 2, THRIFT_NVFP4>(AttnArgs);
 template __global__ void attn_fwd_kernel<64, 4, THRIFT_NVFP4>(AttnArgs);
 template __global__ void attn_fwd_kernel<64, 2, THRIFT_NVFP4>(AttnArgs);
-template __global__ void decode_fp4_kernel<128>(DecodeArgs);
-template __global__ void decode_fp4_kernel<64>(DecodeArgs);
+template __global__ void decode_mx_fused_kernel<128>(DecodeArgs, int, int);
+template __global__ void decode_mx_fused_kernel<64>(DecodeArgs, int, int);
 template __global__ void decode_nv4_kernel<128>(DecodeArgs);
 template __global__ void decode_nv4_kernel<64>(DecodeArgs);
 template __global__ void decode_f16_kernel<128>(DecodeArgs);
@@ -1502,7 +1527,7 @@ static thrift_status launch_decode(DecodeArgs& d, int fmt, hipStream_t stream) {
   const AttnArgs& a = d.kv;
   static std::atomic<uint64_t> configured{0};
   if (once_per_device(configured, [] {
-        for (const void* kf : {(const void*)decode_fp4_kernel<D>, (const void*)decode_nv4_kernel<D>,
+        for (const void* kf : {(const void*)decode_mx_fused_kernel<D>, (const void*)decode_nv4_kernel<D>,
                                (const void*)decode_f16_kernel<D>})
           if (hipFuncSetAttribute(kf, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
             return THRIFT_EHIP;
@@ -1510,12 +1535,15 @@ static thrift_status launch_decode(DecodeArgs& d, int fmt, hipStream_t stream) {
       }) != THRIFT_OK)
     return THRIFT_EHIP;
   const size_t pbytes = (size_t)d.G * ((d.nvalid + 31) / 32) * 4;
-  if (fmt == THRIFT_MXFP4)
-    decode_fp4_kernel<D><<<a.B * a.Hkv * d.nsplit, kDecWaves * 64, 4 * (size_t)M::SIZE + pbytes, stream>>>(d);
-  else
-    decode_nv4_kernel<D><<<a.B * a.Hkv * d.nsplit, kDecWaves * 64, kDecWaves * (size_t)Lds<D>::STAGE + pbytes,
-                           stream>>>(d);
-  decode_f16_kernel<D><<<a.B * a.Hq * a.kmax, 64, D * Lds<D>::VROWH * 2, stream>>>(d);
+  const int n4wg = a.B * a.Hkv * d.nsplit, n16 = a.B * a.Hq * a.kmax;
+  if (fmt == THRIFT_MXFP4) {
+    const size_t l4 = 4 * (size_t)M::SIZE + pbytes, l16 = (size_t)kDecWaves * D * Lds<D>::VROWH * 2;
+    const size_t lds = l4 > l16 ? l4 : l16;
+    decode_mx_fused_kernel<D><<<n4wg + cdiv(n16, kDecWaves), kDecWaves * 64, lds, stream>>>(d, n4wg, n16);
+  } else {
+    decode_nv4_kernel<D><<<n4wg, kDecWaves * 64, kDecWaves * (size_t)Lds<D>::STAGE + pbytes, stream>>>(d);
+    decode_f16_kernel<D><<<n16, 64, D * Lds<D>::VROWH * 2, stream>>>(d);
+  }
   decode_merge_kernel<D><<<a.B * a.Hq * d.Sq, kMergeThreads, 0, stream>>>(d);
   return launch_status();
 }
