@@ -83,6 +83,13 @@ def _declare(L):
     L.tho_attention.argtypes = [_P] * 12 + [_I, _P, _P, _I] + [_I] * 8 + [_D, _P, _I, _P, _P, _P]
     L.tho_attention_kv.restype = None
     L.tho_attention_kv.argtypes = [_P] * 12 + [_I, _P, _P, _I] + [_I] * 9 + [_D, _P, _I, _P, _P, _P]
+    L.tho_attention_hp.restype = None
+    L.tho_attention_hp.argtypes = [_P] * 12 + [_I, _P, _P, _I] + [_I] * 8 + [_D, _P, _I, _P, _P, _P]
+    L.tho_attention_bwd.restype = None
+    L.tho_attention_bwd.argtypes = ([_P] * 12 + [_I, _P, _P, _I] + [_I] * 8 + [_D, _P, _P, _P]
+                                    + [_P, _I, _P, _I] + [_P] * 4)
+    L.tho_row_probs.restype = None
+    L.tho_row_probs.argtypes = [_P] * 12 + [_I, _P, _P, _I] + [_I] * 8 + [_D, _P, _I, _I, _I] + [_P] * 3
     L.tho_fp4_scores.restype = None
     L.tho_fp4_scores.argtypes = [_P] * 6 + [_I] * 6 + [_P]
     L.tho_e2m1_encode_array.restype = None
@@ -284,6 +291,96 @@ def attention(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, c
                            Sk, D, bq, bk, int(causal), float(sm_scale), _ptr(w), nw, _ptr(o),
                            _ptr(lse), _ptr(u))
     return (o, lse, u) if with_u else (o, lse)
+
+
+def attention_hp(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt, bq, bk,
+                 causal, sm_scale=None, work=None):
+    """Forward with Attn-QAT's high-precision output: (o, lse, ohp), ohp the
+    output with the exact softmax probabilities (fp64 [B,Hq,S,D]).  Sq = Sk."""
+    B, Hq, S, D = q4.shape
+    Hkv = k4.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(D)
+    q16 = None if q16 is None else _c(q16, np.float16)
+    k16 = None if k16 is None else _c(k16, np.float16)
+    v16 = None if v16 is None else _c(v16, np.float16)
+    idx = _c(idx, np.int32)
+    cnt = _c(cnt, np.int32)
+    o = np.full((B, Hq, S, D), np.nan, np.float64)
+    lse = np.full((B, Hq, S), np.nan, np.float64)
+    ohp = np.full((B, Hq, S, D), np.nan, np.float64)
+    w = None if work is None else _c(np.asarray(work).reshape(-1, 3), np.int32)
+    nw = 0 if w is None else w.shape[0]
+    lib().tho_attention_hp(_ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
+                           _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales),
+                           _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales),
+                           _ptr(v4.tensor_scale), q4.fmt, _ptr(idx), _ptr(cnt), idx.shape[-1], B, Hq,
+                           Hkv, S, D, bq, bk, int(causal), float(sm_scale), _ptr(w), nw, _ptr(o),
+                           _ptr(lse), _ptr(ohp))
+    return o, lse, ohp
+
+
+def attention_bwd(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt, bq, bk,
+                  causal, lse, ohp, do16, sm_scale=None, qwork=None, kwork=None, with_u=False):
+    """Backward (Attn-QAT).  Returns (dq, dk, dv) fp64, and with with_u the
+    decision-uncertainty bound of dv; with work lists of (b, hq, i) query
+    blocks and (b, hk, j) key blocks only those rows are filled (the rest
+    stay NaN)."""
+    B, Hq, S, D = q4.shape
+    Hkv = k4.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(D)
+    q16 = None if q16 is None else _c(q16, np.float16)
+    k16 = None if k16 is None else _c(k16, np.float16)
+    v16 = None if v16 is None else _c(v16, np.float16)
+    idx = _c(idx, np.int32)
+    cnt = _c(cnt, np.int32)
+    lse = _c(lse, np.float64)
+    ohp = _c(ohp, np.float64)
+    do16 = _c(do16, np.float16)
+    dq = np.full((B, Hq, S, D), np.nan, np.float64)
+    dk = np.full((B, Hkv, S, D), np.nan, np.float64)
+    dv = np.full((B, Hkv, S, D), np.nan, np.float64)
+    udv = np.full((B, Hkv, S, D), np.nan, np.float64) if with_u else None
+    qw = None if qwork is None else _c(np.asarray(qwork).reshape(-1, 3), np.int32)
+    kw = None if kwork is None else _c(np.asarray(kwork).reshape(-1, 3), np.int32)
+    lib().tho_attention_bwd(_ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
+                            _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales),
+                            _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales),
+                            _ptr(v4.tensor_scale), q4.fmt, _ptr(idx), _ptr(cnt), idx.shape[-1], B,
+                            Hq, Hkv, S, D, bq, bk, int(causal), float(sm_scale), _ptr(lse),
+                            _ptr(ohp), _ptr(do16), _ptr(qw), 0 if qw is None else qw.shape[0],
+                            _ptr(kw), 0 if kw is None else kw.shape[0], _ptr(dq), _ptr(dk),
+                            _ptr(dv), _ptr(udv))
+    return (dq, dk, dv, udv) if with_u else (dq, dk, dv)
+
+
+def row_probs(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt, bq, bk, causal,
+              lse, b, hq, r, sm_scale=None):
+    """Test hook: (kind, p, pt) of query row r of head (b, hq) against every
+    key, as the backward recomputes them (kind 0 masked/invalid, 1 FP4 path,
+    2 FP16 path; p the exact probability; pt the one the forward's PV product
+    used)."""
+    B, Hq, S, D = q4.shape
+    Hkv = k4.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(D)
+    q16 = None if q16 is None else _c(q16, np.float16)
+    k16 = None if k16 is None else _c(k16, np.float16)
+    v16 = None if v16 is None else _c(v16, np.float16)
+    idx = _c(idx, np.int32)
+    cnt = _c(cnt, np.int32)
+    lse = _c(lse, np.float64)
+    kind = np.zeros(S, np.int32)
+    p = np.zeros(S, np.float64)
+    pt = np.zeros(S, np.float64)
+    lib().tho_row_probs(_ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
+                        _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales),
+                        _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales),
+                        _ptr(v4.tensor_scale), q4.fmt, _ptr(idx), _ptr(cnt), idx.shape[-1], B, Hq,
+                        Hkv, S, D, bq, bk, int(causal), float(sm_scale), _ptr(lse), b, hq, r,
+                        _ptr(kind), _ptr(p), _ptr(pt))
+    return kind, p, pt
 
 
 def pipeline(q16, k16, v16, fmt, bq, bk, causal, topk_count=-1, topk_bp=0, sm_scale=None,

@@ -622,7 +622,7 @@ typedef struct {
 
 /* One query row r of query block i of head (b, hq). */
 static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, double* o_row,
-                           double* lse_out, double* u_row) {
+                           double* lse_out, double* u_row, double* ohp_row) {
   int D = a->D, S = a->S, Sk = a->Sk, bk = a->bk;
   int hk = hq / (a->Hq / a->Hkv);
   int nq = tho_cdiv(S, a->bq);
@@ -636,6 +636,9 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
   int mask[64];
   double* acc = (double*)calloc((size_t)D, sizeof(double));
   double* uacc = (double*)calloc((size_t)D, sizeof(double)); /* uncertainty, like acc */
+  /* the high-precision output O' (Attn-QAT): the same sum with the exact
+   * probabilities in place of the quantised or fp16-rounded ones */
+  double* hacc = (double*)calloc((size_t)D, sizeof(double));
   double ul = 0.0; /* uncertainty of the row sum, like l */
   double* qh = (double*)malloc(sizeof(double) * (size_t)D);
   double* q4 = (double*)malloc(sizeof(double) * (size_t)D);
@@ -694,9 +697,13 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
     l = alpha * l + psum;
     ul = alpha * ul + upsum;
     for (int d = 0; d < D; ++d) {
-      double pv = 0.0;
-      for (int c = 0; c < n; ++c) pv += pq[c] * a->v4[(kvbase + c0 + c) * D + d];
+      double pv = 0.0, hv = 0.0;
+      for (int c = 0; c < n; ++c) {
+        pv += pq[c] * a->v4[(kvbase + c0 + c) * D + d];
+        if (!mask[c]) hv += exp2(t[c] - m_new) * a->v4[(kvbase + c0 + c) * D + d];
+      }
       acc[d] = alpha * acc[d] + w * pv;
+      hacc[d] = alpha * hacc[d] + hv;
     }
     m = m_new;
   }
@@ -752,18 +759,26 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
     l = alpha * l + psum;
     ul = alpha * ul + upsum;
     for (int d = 0; d < D; ++d) {
-      double pv = 0.0;
+      double pv = 0.0, hv = 0.0;
       for (int c = 0; c < n; ++c)
-        if (!mask[c]) pv += pq[c] * tho_half_to_double(a->v16[(kvbase + c0 + c) * D + d]);
+        if (!mask[c]) {
+          double vv = tho_half_to_double(a->v16[(kvbase + c0 + c) * D + d]);
+          pv += pq[c] * vv;
+          hv += exp2(t[c] - m_new) * vv;
+        }
       acc[d] = alpha * acc[d] + pv;
+      hacc[d] = alpha * hacc[d] + hv;
     }
     m = m_new;
   }
 
   for (int d = 0; d < D; ++d) o_row[d] = acc[d] / l;
+  if (ohp_row)
+    for (int d = 0; d < D; ++d) ohp_row[d] = hacc[d] / l;
   if (u_row)
     for (int d = 0; d < D; ++d) u_row[d] = uacc[d] / l + fabs(o_row[d]) * ul / l;
   if (lse_out) *lse_out = m * THO_LN2 + log(l);
+  free(hacc);
   free(uacc);
   free(q4);
   free(qh);
@@ -777,13 +792,14 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
  * (may be NULL), the bound on what decisions within fp32 evaluation error of
  * their rounding boundary can change in o; rows outside the work items are
  * left untouched. */
-void tho_attention_kv(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
-                      const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
-                      const uint8_t* k4s, const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
-                      const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
-                      int B, int Hq, int Hkv, int S, int Sk, int D, int bq, int bk, int causal,
-                      double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
-                      double* u) {
+static void tho_attention_impl(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
+                               const uint8_t* q4c, const uint8_t* q4s, const float* q4t,
+                               const uint8_t* k4c, const uint8_t* k4s, const float* k4t,
+                               const uint8_t* v4c, const uint8_t* v4s, const float* v4t, int fmt,
+                               const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq,
+                               int Hkv, int S, int Sk, int D, int bq, int bk, int causal,
+                               double sm_scale, const int32_t* work, int nwork, double* o,
+                               double* lse, double* u, double* ohp) {
   tho_attn_args a;
   a.B = B;
   a.Hq = Hq;
@@ -828,11 +844,38 @@ void tho_attention_kv(const uint16_t* q16, const uint16_t* k16, const uint16_t* 
     int r0 = i * bq, r1 = r0 + bq < S ? r0 + bq : S;
     for (int r = r0; r < r1; ++r) {
       size_t row = ((size_t)b * Hq + hq) * S + r;
-      tho_attend_row(&a, b, hq, i, r, o + row * D, lse ? lse + row : NULL, u ? u + row * D : NULL);
+      tho_attend_row(&a, b, hq, i, r, o + row * D, lse ? lse + row : NULL, u ? u + row * D : NULL,
+                     ohp ? ohp + row * D : NULL);
     }
   }
   free(v4);
   free(k4);
+}
+
+void tho_attention_kv(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
+                      const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
+                      const uint8_t* k4s, const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
+                      const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                      int B, int Hq, int Hkv, int S, int Sk, int D, int bq, int bk, int causal,
+                      double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
+                      double* u) {
+  tho_attention_impl(q16, k16, v16, q4c, q4s, q4t, k4c, k4s, k4t, v4c, v4s, v4t, fmt, idx, cnt, kmax,
+                     B, Hq, Hkv, S, Sk, D, bq, bk, causal, sm_scale, work, nwork, o, lse, u, NULL);
+}
+
+/* The forward with Attn-QAT's extra output: ohp [B,Hq,S,D] receives O', the
+ * attention output computed with the exact softmax probabilities (each key
+ * and value in the precision of its block's path), which the backward uses
+ * for its row term.  Sq = Sk (training shape). */
+void tho_attention_hp(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
+                      const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
+                      const uint8_t* k4s, const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
+                      const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                      int B, int Hq, int Hkv, int S, int D, int bq, int bk, int causal,
+                      double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
+                      double* ohp) {
+  tho_attention_impl(q16, k16, v16, q4c, q4s, q4t, k4c, k4s, k4t, v4c, v4s, v4t, fmt, idx, cnt, kmax,
+                     B, Hq, Hkv, S, S, D, bq, bk, causal, sm_scale, work, nwork, o, lse, NULL, ohp);
 }
 
 void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
@@ -844,6 +887,310 @@ void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16
                    double* u) {
   tho_attention_kv(q16, k16, v16, q4c, q4s, q4t, k4c, k4s, k4t, v4c, v4s, v4t, fmt, idx, cnt, kmax, B,
                    Hq, Hkv, S, S, D, bq, bk, causal, sm_scale, work, nwork, o, lse, u);
+}
+
+/* ------------------------------------------------------------------ */
+/* Backward pass (Attn-QAT, "Methodik": precision-consistent          */
+/* recomputation of P from L, and the row term from O')               */
+/* ------------------------------------------------------------------ */
+/*
+ * The gradient of the forward above with the selection (idx, cnt) held
+ * fixed and every quantiser passed straight through (its derivative taken
+ * as the identity), which is how quantisation-aware training differentiates
+ * through fake quantisation.  For query row r (log2-domain log-sum-exp
+ * L2 = lse * log2 e from the forward) and every key c of a valid pair, in
+ * the precision of the path its block takes for this row's query block
+ * (q4, k4, v4 dequantised on the FP4 path; the fp16 tensors on the FP16
+ * path):
+ *   t = sm_scale log2(e) q.k,  p = 2^(t - L2)          (exact probability)
+ *   pt = the probability the forward's PV product used, recomputed from L:
+ *        FP4 path: the two-level quantised value (relative to the tile's own
+ *        maximum, so its codes do not depend on L) times 2^(ref - L2);
+ *        FP16 path: fp16(p)
+ *   dV[c] += pt dO[r]          dP = dO[r].v[c]
+ *   Dr = dO[r].O'[r]           (O' from the forward: the exact-probability
+ *                               output, so Dr = sum_c p dP)
+ *   dS = p (dP - Dr)
+ *   dQ[r] += sm_scale dS k[c]  dK[c] += sm_scale dS q[r]
+ * Query heads sharing a key head add into the same dK, dV.
+ */
+
+/* Probabilities of query row r against key block j (the block must be
+ * valid for r's query block): kind[c] 0 masked, 1 FP4 path, 2 FP16 path;
+ * p, pt as above; dpt (may be NULL) the change in pt that a decision within
+ * fp32 evaluation error of its rounding boundary can make.  q4 and qh are
+ * the row's dequantised FP4 and fp16 query; k16d, v16d the fp16 keys and
+ * values as doubles.  Returns the number of keys in the block. */
+static int tho_tile_probs(const tho_attn_args* a, const double* k16d, int b, int hq, int r, int j,
+                          double L2, const double* q4, const double* qh, int* kind, double* p,
+                          double* pt, double* dpt) {
+  int D = a->D, S = a->S, Sk = a->Sk, bk = a->bk;
+  int i = r / a->bq, nq = tho_cdiv(S, a->bq);
+  int hk = hq / (a->Hq / a->Hkv);
+  int qpos = Sk - S + r;
+  size_t kvbase = ((size_t)b * a->Hkv + hk) * Sk;
+  const int32_t* sel = a->idx + (((size_t)b * a->Hq + hq) * nq + i) * a->kmax;
+  int nsel = a->cnt[((size_t)b * a->Hq + hq) * nq + i];
+  int prom = 0;
+  for (int s = 0; s < nsel; ++s)
+    if (sel[s] == j) prom = 1;
+  int c0 = j * bk, n = (c0 + bk < Sk ? c0 + bk : Sk) - c0;
+  double t[64], ta[64], pq[64], dq[64];
+  int mask[64];
+  double mt = -INFINITY;
+  for (int c = 0; c < n; ++c) {
+    mask[c] = a->causal && (c0 + c > qpos);
+    double sd = 0.0, sa = 0.0;
+    if (!mask[c]) {
+      const double* qv = prom ? qh : q4;
+      const double* kv = (prom ? k16d : a->k4) + (kvbase + c0 + c) * D;
+      for (int d = 0; d < D; ++d) {
+        sd += qv[d] * kv[d];
+        sa += fabs(qv[d] * kv[d]);
+      }
+    }
+    t[c] = mask[c] ? -INFINITY : sd * a->sm_scale * THO_LOG2E;
+    ta[c] = sa * a->sm_scale * THO_LOG2E;
+    if (t[c] > mt) mt = t[c];
+  }
+  for (int c = 0; c < n; ++c) {
+    kind[c] = 0;
+    p[c] = pt[c] = 0.0;
+    if (dpt) dpt[c] = 0.0;
+  }
+  if (mt == -INFINITY) return n;
+  if (!prom) {
+    double ref;
+    tho_quantize_p_tile(t, ta, mask, n, a->fmt, mt, pq, dpt ? dq : NULL, &ref);
+    for (int c = 0; c < n; ++c)
+      if (!mask[c]) {
+        kind[c] = 1;
+        p[c] = exp2(t[c] - L2);
+        pt[c] = pq[c] * exp2(ref - L2);
+        if (dpt) dpt[c] = dq[c] * exp2(ref - L2);
+      }
+  } else {
+    for (int c = 0; c < n; ++c)
+      if (!mask[c]) {
+        kind[c] = 2;
+        p[c] = exp2(t[c] - L2);
+        pt[c] = tho_round_to_half(p[c]);
+        /* p carries the score's error and that of an fp32 log-sum-exp */
+        if (dpt) dpt[c] = tho_half_flip(p[c], tho_eval_eps(ta[c]) + tho_eval_eps(fabs(L2)));
+      }
+  }
+  return n;
+}
+
+static void tho_bwd_setup(tho_attn_args* a, const uint16_t* q16, const uint16_t* k16,
+                          const uint16_t* v16, const uint8_t* q4c, const uint8_t* q4s,
+                          const float* q4t, const uint8_t* k4c, const uint8_t* k4s,
+                          const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
+                          const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt,
+                          int kmax, int B, int Hq, int Hkv, int S, int D, int bq, int bk,
+                          int causal, double sm_scale, double** k16d, double** v16d) {
+  a->B = B;
+  a->Hq = Hq;
+  a->Hkv = Hkv;
+  a->S = S;
+  a->Sk = S;
+  a->D = D;
+  a->bq = bq;
+  a->bk = bk;
+  a->causal = causal;
+  a->fmt = fmt;
+  a->kmax = kmax;
+  a->sm_scale = sm_scale;
+  a->q16 = q16;
+  a->k16 = k16;
+  a->v16 = v16;
+  a->idx = idx;
+  a->cnt = cnt;
+  a->q4c = q4c;
+  a->q4s = q4s;
+  a->q4t = q4t;
+  size_t nkv = (size_t)B * Hkv * S * D;
+  double* k4 = (double*)malloc(sizeof(double) * nkv);
+  double* v4 = (double*)malloc(sizeof(double) * nkv);
+  tho_dequantize(k4c, k4s, k4t, B, Hkv, S, D, THO_AXIS_D, fmt, k4);
+  tho_dequantize(v4c, v4s, v4t, B, Hkv, S, D, THO_AXIS_S, fmt, v4);
+  a->k4 = k4;
+  a->v4 = v4;
+  *k16d = (double*)malloc(sizeof(double) * nkv);
+  *v16d = (double*)malloc(sizeof(double) * nkv);
+  for (size_t e = 0; e < nkv; ++e) {
+    (*k16d)[e] = k16 ? tho_half_to_double(k16[e]) : 0.0;
+    (*v16d)[e] = v16 ? tho_half_to_double(v16[e]) : 0.0;
+  }
+}
+
+/* The row's query in both precisions and its term Dr = dO[r].O'[r]. */
+static double tho_bwd_row(const tho_attn_args* a, int b, int hq, int r, const double* ohp,
+                          const uint16_t* do16, double* q4, double* qh, double* dor) {
+  int D = a->D, S = a->S;
+  size_t row = ((size_t)b * a->Hq + hq) * S + r;
+  tho_dequant_row(a->q4c, a->q4s, a->q4t, (size_t)b * a->Hq + hq, S, D, r, a->fmt, q4);
+  double Dr = 0.0;
+  for (int d = 0; d < D; ++d) {
+    qh[d] = a->q16 ? tho_half_to_double(a->q16[row * D + d]) : 0.0;
+    dor[d] = tho_half_to_double(do16[row * D + d]);
+    Dr += dor[d] * ohp[row * D + d];
+  }
+  return Dr;
+}
+
+/* Backward pass.  lse [B,Hq,S] and ohp [B,Hq,S,D] come from the forward
+ * (tho_attention_hp), do16 [B,Hq,S,D] is the output gradient.  dq
+ * [B,Hq,S,D] is filled for the query blocks listed in qwork ((b, hq, i)
+ * triples; NULL: all), dk and dv [B,Hkv,S,D] for the key blocks in kwork
+ * ((b, hk, j) triples; NULL: all); udv (may be NULL) bounds what decisions
+ * within fp32 evaluation error of their rounding boundary can change in dv.
+ * Rows outside the work items are left untouched.  Sq = Sk. */
+void tho_attention_bwd(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
+                       const uint8_t* q4c, const uint8_t* q4s, const float* q4t,
+                       const uint8_t* k4c, const uint8_t* k4s, const float* k4t,
+                       const uint8_t* v4c, const uint8_t* v4s, const float* v4t, int fmt,
+                       const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq, int Hkv,
+                       int S, int D, int bq, int bk, int causal, double sm_scale,
+                       const double* lse, const double* ohp, const uint16_t* do16,
+                       const int32_t* qwork, int nqwork, const int32_t* kwork, int nkwork,
+                       double* dq, double* dk, double* dv, double* udv) {
+  tho_attn_args a;
+  double *k16d, *v16d;
+  tho_bwd_setup(&a, q16, k16, v16, q4c, q4s, q4t, k4c, k4s, k4t, v4c, v4s, v4t, fmt, idx, cnt, kmax,
+                B, Hq, Hkv, S, D, bq, bk, causal, sm_scale, &k16d, &v16d);
+  int nq = tho_cdiv(S, bq), nk = tho_cdiv(S, bk), G = Hq / Hkv;
+
+  /* dQ, one query block at a time */
+  int totq = qwork ? nqwork : B * Hq * nq;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int w = 0; w < totq; ++w) {
+    int b = qwork ? qwork[3 * w] : w / (Hq * nq);
+    int hq = qwork ? qwork[3 * w + 1] : (w / nq) % Hq;
+    int i = qwork ? qwork[3 * w + 2] : w % nq;
+    int hk = hq / G;
+    size_t kvbase = ((size_t)b * Hkv + hk) * S;
+    double *q4 = malloc(sizeof(double) * D), *qh = malloc(sizeof(double) * D);
+    double* dor = malloc(sizeof(double) * D);
+    double p[64], pt[64];
+    int kind[64];
+    int r1 = (i + 1) * bq < S ? (i + 1) * bq : S;
+    int nvalid = tho_valid_blocks_kv(i, S, S, bq, bk, causal);
+    for (int r = i * bq; r < r1; ++r) {
+      size_t row = ((size_t)b * Hq + hq) * S + r;
+      double Dr = tho_bwd_row(&a, b, hq, r, ohp, do16, q4, qh, dor);
+      double L2 = lse[row] * THO_LOG2E;
+      double* g = dq + row * D;
+      for (int d = 0; d < D; ++d) g[d] = 0.0;
+      for (int j = 0; j < nvalid; ++j) {
+        int n = tho_tile_probs(&a, k16d, b, hq, r, j, L2, q4, qh, kind, p, pt, NULL);
+        for (int c = 0; c < n; ++c) {
+          if (!kind[c]) continue;
+          size_t key = kvbase + (size_t)j * bk + c;
+          const double* kv = (kind[c] == 1 ? a.k4 : k16d) + key * D;
+          const double* vv = (kind[c] == 1 ? a.v4 : v16d) + key * D;
+          double dP = 0.0;
+          for (int d = 0; d < D; ++d) dP += dor[d] * vv[d];
+          double dS = p[c] * (dP - Dr);
+          for (int d = 0; d < D; ++d) g[d] += sm_scale * dS * kv[d];
+        }
+      }
+    }
+    free(dor);
+    free(qh);
+    free(q4);
+  }
+
+  /* dK and dV, one key block at a time, over every query row of the G
+   * query heads of its key head whose query block sees it */
+  int totk = kwork ? nkwork : B * Hkv * nk;
+#pragma omp parallel for schedule(dynamic, 1)
+  for (int w = 0; w < totk; ++w) {
+    int b = kwork ? kwork[3 * w] : w / (Hkv * nk);
+    int hk = kwork ? kwork[3 * w + 1] : (w / nk) % Hkv;
+    int j = kwork ? kwork[3 * w + 2] : w % nk;
+    size_t kvbase = ((size_t)b * Hkv + hk) * S;
+    int c0 = j * bk, n = (c0 + bk < S ? c0 + bk : S) - c0;
+    for (int c = 0; c < n; ++c)
+      for (int d = 0; d < D; ++d) {
+        dk[(kvbase + c0 + c) * D + d] = 0.0;
+        dv[(kvbase + c0 + c) * D + d] = 0.0;
+        if (udv) udv[(kvbase + c0 + c) * D + d] = 0.0;
+      }
+    double *q4 = malloc(sizeof(double) * D), *qh = malloc(sizeof(double) * D);
+    double* dor = malloc(sizeof(double) * D);
+    double p[64], pt[64], dpt[64];
+    int kind[64];
+    for (int hq = hk * G; hq < (hk + 1) * G; ++hq)
+      for (int i = 0; i < nq; ++i) {
+        if (j >= tho_valid_blocks_kv(i, S, S, bq, bk, causal)) continue;
+        int r1 = (i + 1) * bq < S ? (i + 1) * bq : S;
+        for (int r = i * bq; r < r1; ++r) {
+          size_t row = ((size_t)b * Hq + hq) * S + r;
+          double Dr = tho_bwd_row(&a, b, hq, r, ohp, do16, q4, qh, dor);
+          double L2 = lse[row] * THO_LOG2E;
+          tho_tile_probs(&a, k16d, b, hq, r, j, L2, q4, qh, kind, p, pt, udv ? dpt : NULL);
+          for (int c = 0; c < n; ++c) {
+            if (!kind[c]) continue;
+            size_t key = kvbase + c0 + c;
+            const double* vv = (kind[c] == 1 ? a.v4 : v16d) + key * D;
+            const double* qv = kind[c] == 1 ? q4 : qh;
+            double dP = 0.0;
+            for (int d = 0; d < D; ++d) dP += dor[d] * vv[d];
+            double dS = p[c] * (dP - Dr);
+            for (int d = 0; d < D; ++d) {
+              dk[key * D + d] += sm_scale * dS * qv[d];
+              dv[key * D + d] += pt[c] * dor[d];
+              if (udv) udv[key * D + d] += dpt[c] * fabs(dor[d]);
+            }
+          }
+        }
+      }
+    free(dor);
+    free(qh);
+    free(q4);
+  }
+  free(v16d);
+  free(k16d);
+  free((void*)a.v4);
+  free((void*)a.k4);
+}
+
+/* Test hook: the probabilities of query row r of head (b, hq) against every
+ * key, as the backward recomputes them (kind, p, pt [S] each; keys outside
+ * valid blocks get kind 0). */
+void tho_row_probs(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
+                   const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
+                   const uint8_t* k4s, const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
+                   const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                   int B, int Hq, int Hkv, int S, int D, int bq, int bk, int causal,
+                   double sm_scale, const double* lse, int b, int hq, int r, int32_t* kind,
+                   double* p, double* pt) {
+  tho_attn_args a;
+  double *k16d, *v16d;
+  tho_bwd_setup(&a, q16, k16, v16, q4c, q4s, q4t, k4c, k4s, k4t, v4c, v4s, v4t, fmt, idx, cnt, kmax,
+                B, Hq, Hkv, S, D, bq, bk, causal, sm_scale, &k16d, &v16d);
+  double *q4 = malloc(sizeof(double) * D), *qh = malloc(sizeof(double) * D);
+  size_t row = ((size_t)b * Hq + hq) * S + r;
+  tho_dequant_row(q4c, q4s, q4t, (size_t)b * Hq + hq, S, D, r, fmt, q4);
+  for (int d = 0; d < D; ++d) qh[d] = q16 ? tho_half_to_double(q16[row * D + d]) : 0.0;
+  for (int c = 0; c < S; ++c) {
+    kind[c] = 0;
+    p[c] = pt[c] = 0.0;
+  }
+  int nvalid = tho_valid_blocks_kv(r / bq, S, S, bq, bk, causal);
+  for (int j = 0; j < nvalid; ++j) {
+    int kd[64];
+    int n = tho_tile_probs(&a, k16d, b, hq, r, j, lse[row] * THO_LOG2E, q4, qh, kd, p + j * bk,
+                           pt + j * bk, NULL);
+    for (int c = 0; c < n; ++c) kind[j * bk + c] = kd[c];
+  }
+  free(qh);
+  free(q4);
+  free(v16d);
+  free(k16d);
+  free((void*)a.v4);
+  free((void*)a.k4);
 }
 
 /* Scores of the FP4 path for one query row against keys [c0, c1) (test hook:

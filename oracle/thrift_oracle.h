@@ -61,6 +61,32 @@ void tho_attention_kv(const uint16_t* q16, const uint16_t* k16, const uint16_t* 
                       int B, int Hq, int Hkv, int S, int Sk, int D, int bq, int bk, int causal,
                       double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
                       double* u);
+/* Forward with Attn-QAT's high-precision output O' (ohp [B,Hq,S,D]); Sq = Sk. */
+void tho_attention_hp(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
+                      const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
+                      const uint8_t* k4s, const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
+                      const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                      int B, int Hq, int Hkv, int S, int D, int bq, int bk, int causal,
+                      double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
+                      double* ohp);
+/* Backward (Attn-QAT): dq [B,Hq,S,D], dk and dv [B,Hkv,S,D] from the
+ * forward's lse and O' and the output gradient do16; Sq = Sk. */
+void tho_attention_bwd(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
+                       const uint8_t* q4c, const uint8_t* q4s, const float* q4t,
+                       const uint8_t* k4c, const uint8_t* k4s, const float* k4t,
+                       const uint8_t* v4c, const uint8_t* v4s, const float* v4t, int fmt,
+                       const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq, int Hkv,
+                       int S, int D, int bq, int bk, int causal, double sm_scale,
+                       const double* lse, const double* ohp, const uint16_t* do16,
+                       const int32_t* qwork, int nqwork, const int32_t* kwork, int nkwork,
+                       double* dq, double* dk, double* dv, double* udv);
+void tho_row_probs(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
+                   const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
+                   const uint8_t* k4s, const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
+                   const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                   int B, int Hq, int Hkv, int S, int D, int bq, int bk, int causal,
+                   double sm_scale, const double* lse, int b, int hq, int r, int32_t* kind,
+                   double* p, double* pt);
 void tho_fp4_scores(const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
                     const uint8_t* k4s, const float* k4t, int fmt, int S, int D, int r, int c0,
                     int c1, double* out);

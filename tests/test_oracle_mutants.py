@@ -21,7 +21,7 @@ MUTANTS = {
                        "const tho_cand* y = (const tho_cand*)b;\n  if (x->s > y->s) return 1;"),
     "head_budget_ascending": ("const tho_pair* y = (const tho_pair*)b;\n  if (x->s > y->s) return -1;",
                               "const tho_pair* y = (const tho_pair*)b;\n  if (x->s > y->s) return 1;"),
-    "decode_start_aligned": ("int qpos = Sk - S + r;", "int qpos = r;"),
+    "decode_start_aligned": ("int qpos = Sk - S + r; /* the query's", "int qpos = r; /* the query's"),
     "decode_valid_blocks_start_aligned": ("return (Sk - Sq + last_q) / bk + 1;", "return last_q / bk + 1;"),
     "e2m1_ties_up": ("if (a > t || (a == t && ((k + 1) & 1) == 0)) code = k + 1;",
                      "if (a >= t) code = k + 1;"),
@@ -37,9 +37,21 @@ MUTANTS = {
     "head_budget_ties_late_block_first": ("if (x->i != y->i) return x->i - y->i;",
                                           "if (x->i != y->i) return y->i - x->i;"),
     "head_budget_floor": ("(P * topk_bp + 9999) / 10000", "(P * topk_bp) / 10000"),
-    "gqa_head_map": ("int hk = hq / (a->Hq / a->Hkv);", "int hk = hq % a->Hkv;"),
-    "fp16_pass_skips_alpha": ("      acc[d] = alpha * acc[d] + pv;\n    }\n    m = m_new;\n  }\n\n  for (int d = 0;",
-                              "      acc[d] = acc[d] + pv;\n    }\n    m = m_new;\n  }\n\n  for (int d = 0;"),
+    "gqa_head_map": ("int hk = hq / (a->Hq / a->Hkv);\n  int nq = tho_cdiv(S, a->bq);",
+                     "int hk = hq % a->Hkv;\n  int nq = tho_cdiv(S, a->bq);"),
+    "fp16_pass_skips_alpha": ("      acc[d] = alpha * acc[d] + pv;\n      hacc[d] = alpha * hacc[d] + hv;\n    }\n    m = m_new;\n  }\n\n  for (int d = 0;",
+                              "      acc[d] = acc[d] + pv;\n      hacc[d] = alpha * hacc[d] + hv;\n    }\n    m = m_new;\n  }\n\n  for (int d = 0;"),
+    # backward (Attn-QAT)
+    "bwd_dv_exact_p": ("dv[key * D + d] += pt[c] * dor[d];", "dv[key * D + d] += p[c] * dor[d];"),
+    "bwd_ds_quantised_p": ("          double dS = p[c] * (dP - Dr);\n          for (int d = 0; d < D; ++d) g[d]",
+                           "          double dS = pt[c] * (dP - Dr);\n          for (int d = 0; d < D; ++d) g[d]"),
+    "bwd_no_row_term": ("Dr += dor[d] * ohp[row * D + d];", "Dr += 0.0 * ohp[row * D + d];"),
+    "bwd_fp16_query_on_fp4_pairs": ("const double* qv = kind[c] == 1 ? q4 : qh;", "const double* qv = qh;"),
+    "bwd_dk_unscaled": ("dk[key * D + d] += sm_scale * dS * qv[d];", "dk[key * D + d] += dS * qv[d];"),
+    "bwd_one_head_per_key_head": ("for (int hq = hk * G; hq < (hk + 1) * G; ++hq)",
+                                  "for (int hq = hk; hq < hk + 1; ++hq)"),
+    "ohp_from_quantised_p": ("if (!mask[c]) hv += exp2(t[c] - m_new) * a->v4[(kvbase + c0 + c) * D + d];",
+                             "if (!mask[c]) hv += w * pq[c] * a->v4[(kvbase + c0 + c) * D + d];"),
 }
 
 
@@ -58,6 +70,6 @@ def test_mutant_is_caught(tmp_path, name):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_formats.py", "tests/test_oracle_select.py",
                         "tests/test_oracle_attention.py", "tests/test_oracle_decode.py",
-                        "tests/test_oracle_select_head.py"],
+                        "tests/test_oracle_select_head.py", "tests/test_oracle_backward.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
