@@ -17,6 +17,7 @@ EXPORTS = ("thrift_select_kmax", "thrift_select_workspace_bytes", "thrift_select
            "thrift_quantize_workspace_bytes", "thrift_quantize_fp4", "thrift_quantize_fp4_range", "thrift_cache_update",
            "thrift_attention_fwd",
            "thrift_attention_decode_workspace_bytes", "thrift_attention_decode",
+           "thrift_attention_bwd_workspace_bytes", "thrift_attention_fwd_hp", "thrift_attention_bwd",
            "thrift_status_string")
 
 _lib = None
@@ -80,6 +81,12 @@ def load():
         L.thrift_quantize_fp4.argtypes = [P, I, I, I, I, I, I, P, P, P, P, SZ, P]
         L.thrift_attention_fwd.restype = I
         L.thrift_attention_fwd.argtypes = [P] * 12 + [I, P, P] + [I] * 9 + [F, P, I, P, P]
+        L.thrift_attention_bwd_workspace_bytes.restype = SZ
+        L.thrift_attention_bwd_workspace_bytes.argtypes = [I] * 6
+        L.thrift_attention_fwd_hp.restype = I
+        L.thrift_attention_fwd_hp.argtypes = [P] * 9 + [I, P, P, I] + [I] * 8 + [F, P, P, P, SZ, P]
+        L.thrift_attention_bwd.restype = I
+        L.thrift_attention_bwd.argtypes = [P] * 9 + [I, P, P, I] + [I] * 8 + [F] + [P] * 7 + [SZ, P]
         L.thrift_status_string.restype = C.c_char_p
         L.thrift_status_string.argtypes = [I]
         _lib = L

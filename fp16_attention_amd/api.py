@@ -20,7 +20,8 @@ __all__ = ["thrift_select_kmax", "thrift_select_blocks", "thrift_block_means",
            "thrift_quantize_fp4",
            "thrift_quantize_fp4_means", "thrift_quantize_fp4_range", "thrift_cache_update",
            "thrift_attention_fwd", "thrift_attention_decode", "thrift_decode", "FP4Tensor",
-           "fp4_transposed", "thrift_forward", "THRIFT_NVFP4", "THRIFT_MXFP4", "THRIFT_GROUP_D",
+           "fp4_transposed", "thrift_forward", "thrift_attention_bwd_workspace", "thrift_attention_fwd_hp",
+           "thrift_attention_bwd", "THRIFT_NVFP4", "THRIFT_MXFP4", "THRIFT_GROUP_D",
            "THRIFT_GROUP_S", "ThriftError"]
 
 
@@ -262,6 +263,63 @@ def thrift_attention_fwd(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Ten
           _ptr(idx), _ptr(cnt), idx.shape[-1], B, Hq, Hkv, S, D, block_q, block_k, int(causal),
           float(sm_scale), _ptr(out), int(out.dtype == torch.float32), _ptr(lse), _stream())
     return (out, lse) if with_lse else out
+
+
+def thrift_attention_bwd_workspace(B, Hq, Hkv, S, D, block_q=128, device="cuda"):
+    """Workspace tensor for thrift_attention_fwd_hp / thrift_attention_bwd."""
+    n = _lib.load().thrift_attention_bwd_workspace_bytes(B, Hq, Hkv, S, D, block_q)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def thrift_attention_fwd_hp(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt, lse,
+                            block_q=128, block_k=64, causal=True, sm_scale=None, workspace=None, out=None):
+    """Attn-QAT's high-precision output O' (fp32 [B,Hq,S,D]): the forward with
+    the exact softmax probabilities, from the forward's lse.  MXFP4 only."""
+    B, Hq, S, D = q16.shape
+    Hkv = k16.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    for name, t in (("q16", q16), ("k16", k16), ("v16", v16)):
+        _check(t, torch.float16, name)
+    _check(idx, torch.int32, "idx")
+    _check(cnt, torch.int32, "cnt")
+    _check(lse, torch.float32, "lse")
+    if workspace is None:
+        workspace = thrift_attention_bwd_workspace(B, Hq, Hkv, S, D, block_q, q16.device)
+    if out is None:
+        out = torch.empty((B, Hq, S, D), dtype=torch.float32, device=q16.device)
+    _call("thrift_attention_fwd_hp", _ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
+          _ptr(k4.codes), _ptr(k4.scales), _ptr(v4.codes), _ptr(v4.scales), q4.fmt, _ptr(idx), _ptr(cnt),
+          idx.shape[-1], B, Hq, Hkv, S, D, block_q, block_k, int(causal), float(sm_scale), _ptr(lse),
+          _ptr(out), _ptr(workspace), workspace.numel(), _stream())
+    return out
+
+
+def thrift_attention_bwd(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt, lse, ohp,
+                         do16, block_q=128, block_k=64, causal=True, sm_scale=None, workspace=None):
+    """Attn-QAT backward: (dq fp32 [B,Hq,S,D], dk, dv fp32 [B,Hkv,S,D]) from the
+    output gradient do16, the forward's lse and O'.  MXFP4 only."""
+    B, Hq, S, D = q16.shape
+    Hkv = k16.shape[1]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    for name, t in (("q16", q16), ("k16", k16), ("v16", v16), ("do16", do16)):
+        _check(t, torch.float16, name)
+    _check(idx, torch.int32, "idx")
+    _check(cnt, torch.int32, "cnt")
+    _check(lse, torch.float32, "lse")
+    _check(ohp, torch.float32, "ohp")
+    if workspace is None:
+        workspace = thrift_attention_bwd_workspace(B, Hq, Hkv, S, D, block_q, q16.device)
+    dev = q16.device
+    dq = torch.empty((B, Hq, S, D), dtype=torch.float32, device=dev)
+    dk = torch.empty((B, Hkv, S, D), dtype=torch.float32, device=dev)
+    dv = torch.empty((B, Hkv, S, D), dtype=torch.float32, device=dev)
+    _call("thrift_attention_bwd", _ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
+          _ptr(k4.codes), _ptr(k4.scales), _ptr(v4.codes), _ptr(v4.scales), q4.fmt, _ptr(idx), _ptr(cnt),
+          idx.shape[-1], B, Hq, Hkv, S, D, block_q, block_k, int(causal), float(sm_scale), _ptr(lse),
+          _ptr(ohp), _ptr(do16), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream())
+    return dq, dk, dv
 
 
 def thrift_attention_decode(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt,

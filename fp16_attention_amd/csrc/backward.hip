@@ -1,0 +1,650 @@
+// Attn-QAT backward of the mixed FP4/FP16 attention, and the forward's
+// high-precision output O' that it needs (Attn-QAT, "Methodik": the
+// probabilities are recomputed from the forward's log-sum-exp in the forward's
+// own precision, and the row term of the softmax gradient comes from O', the
+// output with unquantised probabilities, not from the FP4 output).
+//
+// Every quantiser is passed straight through.  For query row r, key c of a
+// valid pair, in the precision of the path the pair's block takes for r's
+// query block (FP4-decoded Q, K, V on the FP4 path, fp16 on the FP16 path):
+//   t = sm_scale log2(e) q.k, p = 2^(t - L2), L2 = lse log2(e)
+//   pt = the forward's probability (FP4 path: MX two-level quantised; FP16
+//        path: p rounded to fp16)
+//   dV[c] += pt dO[r], dS = p (dO[r].v[c] - dO[r].O'[r]),
+//   dQ[r] += sm_scale dS k[c], dK[c] += sm_scale dS q[r].
+//
+// All products run on the fp16 matrix cores: MX-decoded FP4 operands are
+// exact in fp16.  Three kernels after a preparation pass: the row kernel
+// (one lane per query, as the forward: O' or dQ), and the key kernel (one
+// lane per key: dK and dV).
+#include <hip/hip_runtime.h>
+
+#include "common.h"
+
+namespace thrift {
+namespace {
+
+constexpr int kBlkK = 64;  // key block
+constexpr float kLog2eB = 1.44269504088896341f;
+
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+__device__ inline v16f mma16(v8h a, v8h b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maximum of this lane's value and the one of lane +- 32.
+__device__ inline float max_pair(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// Key of A-operand row m of 32x32 S^T tile mt in a 64-key block: the MFMA
+// output then puts key hi*32 + mt*16 + i in register i of a lane of half hi.
+__device__ inline int krow_b(int mt, int m) {
+  return ((m >> 2) & 1) * 32 + mt * 16 + (m >> 3) * 4 + (m & 3);
+}
+// The same for one 32-row tile: row m reads query qperm(m), so register i of
+// a lane of half hi holds query hi*16 + i.
+__device__ inline int qperm(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
+
+__device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)p, 0, bytes, 0x00020000);
+}
+// 16 bytes at byte offset off; reads past the record count return zeros.
+__device__ inline v8h ld8h(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+}
+__device__ inline v4f ld4f(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
+}
+
+struct BwdArgs {
+  const _Float16 *q16, *k16, *v16, *do16;  // [B,H,S,D]
+  const _Float16 *qd, *kd;                 // FP4-decoded Q, K rows [B,H,S,D]
+  const _Float16* vd;                      // FP4-decoded V rows [B,Hkv,Sp,D]
+  const _Float16 *qt, *qdt, *dot;          // transposed [B,Hq,D,Sp]
+  const _Float16 *kt, *kdt, *vt, *vdt;     // transposed [B,Hkv,D,Sp]
+  const uint32_t* prom;                    // promoted-block bits [B,Hq,nq,nkw]
+  const float *lse, *drow;                 // [B,Hq,S]
+  float* out;                              // row kernel: O' or dQ [B,Hq,S,D]
+  float *dk, *dv;                          // [B,Hkv,S,D]
+  int B, Hq, Hkv, S, Sp, bq, nq, nkw, causal;
+  float c;         // sm_scale * log2(e)
+  float sm_scale;
+};
+
+// ---- preparation ------------------------------------------------------------------
+
+// MX-decoded FP4 rows to fp16: codes [R][L/2] (even element in the low
+// nibble), E8M0 scales [R][L/32]; one thread per 8 elements.  Out [R][L];
+// or, with vD > 0, rows are V's stored (batch*head, 64-token block, channel)
+// rows of L = 64 tokens and go to V^T [batch*head][vD][nb*64].
+// E2M1 times a power of two is exact in fp16 down to its subnormal range.
+__global__ __launch_bounds__(256) void decode_mx_kernel(const uint8_t* codes, const uint8_t* scales, size_t R,
+                                                        int L, _Float16* out, int vD, int vnb) {
+  const size_t e8 = (size_t)blockIdx.x * 256 + threadIdx.x;
+  const size_t n8 = R * (size_t)(L / 8);
+  if (e8 >= n8) return;
+  const size_t row = e8 / (L / 8);
+  const int c8 = (int)(e8 % (L / 8)) * 8;
+  const uint32_t cw = *(const uint32_t*)(codes + row * (L / 2) + c8 / 2);
+  const int X = (int)scales[row * (L / 32) + c8 / 32] - 127;
+  const v2f v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0),
+                    __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1),
+                    __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2),
+                    __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3)};
+  v8h o;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = (_Float16)ldexpf(v[e / 2][e % 2], X);
+  size_t dst = row * L + c8;
+  if (vD > 0) {
+    const size_t d = row % vD, jb = (row / vD) % vnb, bh = row / ((size_t)vD * vnb);
+    dst = (bh * vD + d) * ((size_t)vnb * 64) + jb * 64 + c8;
+  }
+  *(v8h*)(out + dst) = o;
+}
+
+// out[bh][c][r] = in[bh][r][c] for r < R, zero for R <= r < Rout; in rows of
+// C halves.  64x64 tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_kernel(const _Float16* in, int R, int C, int Rout,
+                                                        _Float16* out) {
+  __shared__ _Float16 tile[64][66];
+  const size_t bh = blockIdx.y;
+  const int ct = cdiv(C, 64);
+  const int r0 = (blockIdx.x / ct) * 64, c0 = (blockIdx.x % ct) * 64;
+  const int t = threadIdx.x, tc = t & 63, tr = t >> 6;
+  const _Float16* src = in + bh * (size_t)R * C;
+  for (int k = 0; k < 64; k += 4) {
+    const int r = r0 + tr + k, c = c0 + tc;
+    tile[tr + k][tc] = (r < R && c < C) ? src[(size_t)r * C + c] : (_Float16)0.0f;
+  }
+  __syncthreads();
+  _Float16* dst = out + bh * (size_t)C * Rout;
+  for (int k = 0; k < 64; k += 4) {
+    const int c = c0 + tr + k, r = r0 + tc;
+    if (c < C && r < Rout) dst[(size_t)c * Rout + r] = tile[tc][tr + k];
+  }
+}
+
+// Promoted-block bits of each (batch, query head, query block).
+__global__ __launch_bounds__(256) void prom_bits_kernel(const int32_t* idx, const int32_t* cnt, int nrows,
+                                                        int kmax, int nk, int nkw, uint32_t* bits) {
+  const int row = blockIdx.x * 256 + threadIdx.x;
+  if (row >= nrows) return;
+  uint32_t* w = bits + (size_t)row * nkw;
+  for (int k = 0; k < nkw; ++k) w[k] = 0;
+  const int n = min(max(cnt[row], 0), kmax);
+  for (int s = 0; s < n; ++s) {
+    const int j = idx[(size_t)row * kmax + s];
+    if (j >= 0 && j < nk) w[j >> 5] |= 1u << (j & 31);
+  }
+}
+
+// Row term dO[r] . O'[r], one wave per row.
+template <int D>
+__global__ __launch_bounds__(256) void row_term_kernel(const _Float16* do16, const float* ohp, size_t nrows,
+                                                       float* drow) {
+  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= nrows) return;
+  float s = 0.0f;
+#pragma unroll
+  for (int d = lane; d < D; d += 64) s += (float)do16[row * D + d] * ohp[row * D + d];
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
+  if (lane == 0) drow[row] = s;
+}
+
+// ---- row kernel: one lane per query (O' or dQ) ---------------------------------
+
+constexpr int kModeOhp = 0;
+constexpr int kModeDq = 1;
+
+// Workgroup = query block i of (batch, query head), one wave per 32 rows.
+// Per valid key block j, in the precision of its path: S^T = K Q^T (keys in
+// krow_b order), p = 2^(t - L2); then O'^T += V^T P^T, or dP^T = V dO^T,
+// dS = p (dP - Dr) and dQ^T += K^T dS^T.
+template <int D, int MODE>
+__global__ __launch_bounds__(256) void bwd_row_kernel(BwdArgs a) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hi = lane >> 5, r32 = lane & 31;
+  const int BHq = a.B * a.Hq, G = a.Hq / a.Hkv;
+  const int x = blockIdx.x;
+  const int i = a.causal ? a.nq - 1 - x / BHq : x / BHq;  // longest rows first
+  const int bhq = x % BHq;
+  const int b = bhq / a.Hq, hq = bhq % a.Hq;
+  const size_t bhk = (size_t)b * a.Hkv + hq / G;
+  const int S = a.S, Sp = a.Sp;
+  const int q0 = i * a.bq + w * 32;
+  if (q0 >= S) return;  // no barrier in this kernel
+  const int qrow = q0 + r32;
+
+  const auto qrs = rsrc(a.q16 + (size_t)bhq * S * D, S * D * 2);
+  const auto qdrs = rsrc(a.qd + (size_t)bhq * S * D, S * D * 2);
+  v8h qh[D / 16], qd[D / 16], dh[D / 16];
+#pragma unroll
+  for (int kk = 0; kk < D / 16; ++kk) {
+    const int off = (qrow * D + kk * 16 + hi * 8) * 2;
+    qh[kk] = ld8h(qrs, off);
+    qd[kk] = ld8h(qdrs, off);
+  }
+  if constexpr (MODE == kModeDq) {
+    const auto drs = rsrc(a.do16 + (size_t)bhq * S * D, S * D * 2);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) dh[kk] = ld8h(drs, (qrow * D + kk * 16 + hi * 8) * 2);
+  }
+  const bool qok = qrow < S;
+  const float L2 = qok ? a.lse[(size_t)bhq * S + qrow] * kLog2eB : 0.0f;
+  const float Dr = (MODE == kModeDq && qok) ? a.drow[(size_t)bhq * S + qrow] : 0.0f;
+
+  v16f acc[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = v16f{};
+
+  const auto k16rs = rsrc(a.k16 + bhk * S * D, S * D * 2);
+  const auto kdrs = rsrc(a.kd + bhk * S * D, S * D * 2);
+  const auto v16rs = rsrc(a.v16 + bhk * S * D, S * D * 2);
+  const auto vdrs = rsrc(a.vd + bhk * Sp * D, Sp * D * 2);
+  const uint32_t* pm = a.prom + ((size_t)bhq * a.nq + i) * a.nkw;
+  const int nvalid = valid_kv_blocks(i, S, a.bq, kBlkK, a.causal);
+  for (int j = 0; j < nvalid; ++j) {
+    const bool f16 = (pm[j >> 5] >> (j & 31)) & 1u;
+    const auto krs = f16 ? k16rs : kdrs;
+    v16f s[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      s[mt] = v16f{};
+      const int kb = (j * kBlkK + krow_b(mt, r32)) * D + hi * 8;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) s[mt] = mma16(ld8h(krs, (kb + kk * 16) * 2), f16 ? qh[kk] : qd[kk], s[mt]);
+    }
+    v16f dp[2];
+    if constexpr (MODE == kModeDq) {
+      const auto vrs = f16 ? v16rs : vdrs;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        dp[mt] = v16f{};
+        const int vb = (j * kBlkK + krow_b(mt, r32)) * D + hi * 8;
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) dp[mt] = mma16(ld8h(vrs, (vb + kk * 16) * 2), dh[kk], dp[mt]);
+      }
+    }
+    // B operand of the second product: step st holds keys hi*32 + 8 st + u,
+    // registers 8 (st % 2) + u of tile st / 2
+    v8h pb[4];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) {
+        const int key = j * kBlkK + hi * 32 + mt * 16 + ii;
+        const bool ok = qok && key < S && !(a.causal && key > qrow);
+        const float p = ok ? ex2(__builtin_fmaf(s[mt][ii], a.c, -L2)) : 0.0f;
+        float v = p;
+        if constexpr (MODE == kModeDq) v = p * (dp[mt][ii] - Dr);
+        pb[mt * 2 + ii / 8][ii % 8] = (_Float16)v;
+      }
+    const _Float16* T = MODE == kModeOhp ? (f16 ? a.vt : a.vdt) : (f16 ? a.kt : a.kdt);
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const v8h t = *(const v8h*)(T + (bhk * D + dt * 32 + r32) * Sp + j * kBlkK + hi * 32 + st * 8);
+        acc[dt] = mma16(t, pb[st], acc[dt]);
+      }
+  }
+  if (!qok) return;
+  const float f = MODE == kModeDq ? a.sm_scale : 1.0f;
+  float* dst = a.out + ((size_t)bhq * S + qrow) * D;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d0 = dt * 32 + i4 * 8 + hi * 4;
+      *(float4*)(dst + d0) = make_float4(acc[dt][i4 * 4] * f, acc[dt][i4 * 4 + 1] * f, acc[dt][i4 * 4 + 2] * f,
+                                         acc[dt][i4 * 4 + 3] * f);
+    }
+}
+
+// ---- key kernel: one lane per key (dK, dV) -------------------------------------
+
+// Workgroup = key block j of (batch, key head), two waves of 32 keys.  Loops
+// over the G query heads of the key head and the query rows that see the
+// block, 32 rows a step: S = Q K^T and dP = dO V^T with this lane's key as the
+// column, p and dS per element; on FP4 pairs the probability the forward used
+// is rebuilt from its MX group (this wave's 32 keys), whose maximum comes from
+// S^T = K Q^T (one lane per query) and is handed over through LDS.  Then
+// dV += pt^T dO and dK += dS^T Q.
+template <int D>
+__global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
+  __shared__ __attribute__((aligned(16))) float sh_a[2][2][32], sh_h[2][2][32];  // [step parity][wave][query]
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hi = lane >> 5, r32 = lane & 31;
+  const int BHk = a.B * a.Hkv, G = a.Hq / a.Hkv;
+  const int x = blockIdx.x;
+  const int j = x / BHk;  // causal: the lowest key blocks have the most rows
+  const size_t bhk = x % BHk;
+  const int b = (int)(bhk / a.Hkv), hk = (int)(bhk % a.Hkv);
+  const int S = a.S, Sp = a.Sp;
+  const int key = j * kBlkK + w * 32 + r32;  // this lane's key (column of S)
+
+  v8h kh[D / 16], kd[D / 16], vh[D / 16], vd[D / 16];
+  {
+    const auto k16rs = rsrc(a.k16 + bhk * S * D, S * D * 2);
+    const auto kdrs = rsrc(a.kd + bhk * S * D, S * D * 2);
+    const auto v16rs = rsrc(a.v16 + bhk * S * D, S * D * 2);
+    const auto vdrs = rsrc(a.vd + bhk * Sp * D, Sp * D * 2);
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      const int off = (key * D + kk * 16 + hi * 8) * 2;
+      kh[kk] = ld8h(k16rs, off);
+      kd[kk] = ld8h(kdrs, off);
+      vh[kk] = ld8h(v16rs, off);
+      vd[kk] = ld8h(vdrs, off);
+    }
+  }
+  v16f dk[D / 32], dv[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) dk[dt] = dv[dt] = v16f{};
+
+  const int i0 = a.causal ? (j * kBlkK) / a.bq : 0;
+  int par = 0;
+  for (int g = 0; g < G; ++g) {
+    const int bhq = b * a.Hq + hk * G + g;
+    const auto qrs = rsrc(a.q16 + (size_t)bhq * S * D, S * D * 2);
+    const auto qdrs = rsrc(a.qd + (size_t)bhq * S * D, S * D * 2);
+    const auto drs = rsrc(a.do16 + (size_t)bhq * S * D, S * D * 2);
+    const auto lrs = rsrc(a.lse + (size_t)bhq * S, S * 4);
+    const auto rrs = rsrc(a.drow + (size_t)bhq * S, S * 4);
+    for (int i = i0; i < a.nq; ++i) {
+      const bool f16 = (a.prom[((size_t)bhq * a.nq + i) * a.nkw + (j >> 5)] >> (j & 31)) & 1u;
+      const int qend = min(S, (i + 1) * a.bq);
+      for (int q0 = i * a.bq; q0 < qend; q0 += 32) {
+        if (a.causal && q0 + 31 < j * kBlkK) continue;  // every pair of the step is masked
+        const auto ars = f16 ? qrs : qdrs;
+        v8h qa[D / 16], da[D / 16];
+        const int qm = q0 + qperm(r32);
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          const int off = (qm * D + kk * 16 + hi * 8) * 2;
+          qa[kk] = ld8h(ars, off);
+          da[kk] = ld8h(drs, off);
+        }
+        v16f s = v16f{}, dp = v16f{};
+#pragma unroll
+        for (int kk = 0; kk < D / 16; ++kk) {
+          s = mma16(qa[kk], f16 ? kh[kk] : kd[kk], s);
+          dp = mma16(da[kk], f16 ? vh[kk] : vd[kk], dp);
+        }
+        // this lane's queries q0 + hi*16 + ii: log2-domain LSE and row term
+        float L2[16], Dr[16];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const v4f l4 = ld4f(lrs, (q0 + hi * 16 + u * 4) * 4);
+          const v4f r4 = ld4f(rrs, (q0 + hi * 16 + u * 4) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            L2[u * 4 + e] = l4[e] * kLog2eB;
+            Dr[u * 4 + e] = r4[e];
+          }
+        }
+        float qa_s[16], qh_s[16];  // FP4 pairs: x = p * qa_s is P / 2^X of the MX group, pt = code * qh_s
+        if (!f16) {
+          v16f st = v16f{};
+#pragma unroll
+          for (int kk = 0; kk < D / 16; ++kk) st = mma16(kd[kk], qa[kk], st);
+          // column r32 is query qm; register ii is key w*32 + (ii/4)*8 + hi*4 + ii%4
+          float gm = -INFINITY;
+#pragma unroll
+          for (int ii = 0; ii < 16; ++ii) {
+            const int kx = j * kBlkK + w * 32 + (ii >> 2) * 8 + hi * 4 + (ii & 3);
+            const bool ok = qm < S && kx < S && !(a.causal && kx > qm);
+            gm = fmaxf(gm, ok ? st[ii] : -INFINITY);
+          }
+          gm = max_pair(gm);
+          const float Lq = qm < S ? a.lse[(size_t)bhq * S + qm] * kLog2eB : 0.0f;
+          // MX level 1 is any power of two (the E8M0 block scale absorbs it):
+          // z = ceil(L2); block exponent from the group maximum's probability
+          const float z = ceilf(Lq);
+          const uint32_t E = (__float_as_uint(ex2(__builtin_fmaf(gm, a.c, -z))) >> 23) & 0xFF;
+          const int X = (int)(E > 3 ? E - 2 : 1) - 127;
+          const float zx = z + (float)X;
+          const bool any = gm > -INFINITY;
+          if (hi == 0) {
+            sh_a[par][w][qperm(r32)] = any ? ex2(Lq - zx) : 0.0f;
+            sh_h[par][w][qperm(r32)] = any ? ex2(zx - Lq) : 0.0f;
+          }
+          __syncthreads();
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            const float4 a4 = *(const float4*)&sh_a[par][w][hi * 16 + u * 4];
+            const float4 h4 = *(const float4*)&sh_h[par][w][hi * 16 + u * 4];
+            qa_s[u * 4] = a4.x, qa_s[u * 4 + 1] = a4.y, qa_s[u * 4 + 2] = a4.z, qa_s[u * 4 + 3] = a4.w;
+            qh_s[u * 4] = h4.x, qh_s[u * 4 + 1] = h4.y, qh_s[u * 4 + 2] = h4.z, qh_s[u * 4 + 3] = h4.w;
+          }
+          par ^= 1;
+        }
+        // A operands of the two products: step st holds queries hi*16 + 8 st + u
+        v8h pA[2], sA[2];
+#pragma unroll
+        for (int ii = 0; ii < 16; ii += 2) {
+          float p[2], pt[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int q = q0 + hi * 16 + ii + e;
+            const bool ok = q < S && key < S && !(a.causal && key > q);
+            p[e] = ok ? ex2(__builtin_fmaf(s[ii + e], a.c, -L2[ii + e])) : 0.0f;
+            sA[ii / 8][ii % 8 + e] = (_Float16)(p[e] * (dp[ii + e] - Dr[ii + e]));
+          }
+          if (f16) {
+            pt[0] = p[0], pt[1] = p[1];
+          } else {
+            const uint32_t y = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, p[0] * qa_s[ii], p[1] * qa_s[ii + 1],
+                                                                        1.0f, 0);
+            const v2f cv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(y, 1.0f, 0);
+            pt[0] = cv[0] * qh_s[ii];
+            pt[1] = cv[1] * qh_s[ii + 1];
+          }
+          pA[ii / 8][ii % 8] = (_Float16)pt[0];
+          pA[ii / 8][ii % 8 + 1] = (_Float16)pt[1];
+        }
+        const _Float16* qT = (f16 ? a.qt : a.qdt) + (size_t)bhq * D * Sp;
+        const _Float16* oT = a.dot + (size_t)bhq * D * Sp;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+            const size_t off = (size_t)(dt * 32 + r32) * Sp + q0 + hi * 16 + st * 8;
+            dv[dt] = mma16(pA[st], *(const v8h*)(oT + off), dv[dt]);
+            dk[dt] = mma16(sA[st], *(const v8h*)(qT + off), dk[dt]);
+          }
+      }
+    }
+  }
+  // C layout: column d = dt*32 + r32, register ii is key w*32 + (ii/4)*8 + hi*4 + ii%4
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) {
+      const int kx = j * kBlkK + w * 32 + (ii >> 2) * 8 + hi * 4 + (ii & 3);
+      if (kx < S) {
+        const size_t e = (bhk * S + kx) * D + dt * 32 + r32;
+        a.dk[e] = dk[dt][ii] * a.sm_scale;
+        a.dv[e] = dv[dt][ii];
+      }
+    }
+}
+
+// ---- host side -----------------------------------------------------------------------
+
+struct BwdLayout {
+  size_t qd, qt, qdt, dot, kd, kt, kdt, vd, vt, vdt, prom, drow, total;
+};
+
+inline size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+BwdLayout bwd_layout(int B, int Hq, int Hkv, int S, int D, int bq) {
+  const size_t Sp = (size_t)cdiv(S, kBlkK) * kBlkK;
+  const size_t bhq = (size_t)B * Hq, bhk = (size_t)B * Hkv;
+  const int nq = cdiv(S, bq), nkw = cdiv(cdiv(S, kBlkK), 32);
+  BwdLayout l;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += al256(bytes);
+    return at;
+  };
+  l.qd = take(bhq * S * D * 2);
+  l.qt = take(bhq * D * Sp * 2);
+  l.qdt = take(bhq * D * Sp * 2);
+  l.dot = take(bhq * D * Sp * 2);
+  l.kd = take(bhk * S * D * 2);
+  l.kt = take(bhk * D * Sp * 2);
+  l.kdt = take(bhk * D * Sp * 2);
+  l.vd = take(bhk * Sp * D * 2);
+  l.vt = take(bhk * D * Sp * 2);
+  l.vdt = take(bhk * D * Sp * 2);
+  l.prom = take(bhq * nq * nkw * 4);
+  l.drow = take(bhq * S * 4);
+  l.total = o;
+  return l;
+}
+
+thrift_status check_bwd(const void* q16, const void* k16, const void* v16, const uint8_t* q4c,
+                        const uint8_t* q4s, const uint8_t* k4c, const uint8_t* k4s, const uint8_t* v4c,
+                        const uint8_t* v4s, thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                        int B, int Hq, int Hkv, int S, int D, int block_q, int block_k, int causal,
+                        float sm_scale, const float* lse, const void* workspace, size_t workspace_bytes) {
+  if (!q16 || !k16 || !v16 || !q4c || !q4s || !k4c || !k4s || !v4c || !v4s || !idx || !cnt || !lse ||
+      !workspace)
+    return THRIFT_EINVAL;
+  if (fmt != THRIFT_NVFP4 && fmt != THRIFT_MXFP4) return THRIFT_EINVAL;
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || kmax < 1 || Hq % Hkv != 0 || (causal != 0 && causal != 1))
+    return THRIFT_EINVAL;
+  if (!(sm_scale > 0.0f) || !(sm_scale < 1e30f)) return THRIFT_EINVAL;
+  if (fmt != THRIFT_MXFP4) return THRIFT_EUNSUPPORTED;
+  if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
+  if ((block_q != 64 && block_q != 128) || block_k != kBlkK) return THRIFT_EUNSUPPORTED;
+  if ((size_t)S * D * 2 > 0x7fffffffu || (size_t)D * cdiv(S, kBlkK) * kBlkK * 2 > 0x7fffffffu)
+    return THRIFT_EUNSUPPORTED;
+  for (const void* p : {q16, k16, v16, (const void*)q4c, (const void*)k4c, (const void*)v4c, workspace})
+    if (!aligned16(p)) return THRIFT_EALIGN;
+  if (((uintptr_t)lse & 15) != 0) return THRIFT_EALIGN;
+  if (workspace_bytes < bwd_layout(B, Hq, Hkv, S, D, block_q).total) return THRIFT_EWORKSPACE;
+  return THRIFT_OK;
+}
+
+void launch_decode_mx(const uint8_t* codes, const uint8_t* scales, size_t R, int L, _Float16* out,
+                      hipStream_t stream, int vD = 0, int vnb = 0) {
+  const size_t n8 = R * (size_t)(L / 8);
+  decode_mx_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, stream>>>(codes, scales, R, L, out, vD, vnb);
+}
+
+void launch_transpose(const _Float16* in, int BH, int R, int C, int Rout, _Float16* out, hipStream_t stream) {
+  dim3 grid(cdiv(Rout > R ? Rout : R, 64) * cdiv(C, 64), BH);
+  transpose_kernel<<<grid, 256, 0, stream>>>(in, R, C, Rout, out);
+}
+
+// Fills the FP4-decoded and transposed operands both entry points share.
+void prepare(BwdArgs& a, char* ws, const BwdLayout& l, const void* q16, const void* k16, const void* v16,
+             const uint8_t* q4c, const uint8_t* q4s, const uint8_t* k4c, const uint8_t* k4s,
+             const uint8_t* v4c, const uint8_t* v4s, const int32_t* idx, const int32_t* cnt, int kmax, int B,
+             int Hq, int Hkv, int S, int D, int block_q, int causal, float sm_scale, const float* lse,
+             bool backward, hipStream_t stream) {
+  const int Sp = cdiv(S, kBlkK) * kBlkK, nk = cdiv(S, kBlkK);
+  a.q16 = (const _Float16*)q16;
+  a.k16 = (const _Float16*)k16;
+  a.v16 = (const _Float16*)v16;
+  a.qd = (const _Float16*)(ws + l.qd);
+  a.kd = (const _Float16*)(ws + l.kd);
+  a.vd = (const _Float16*)(ws + l.vd);
+  a.qt = (const _Float16*)(ws + l.qt);
+  a.qdt = (const _Float16*)(ws + l.qdt);
+  a.dot = (const _Float16*)(ws + l.dot);
+  a.kt = (const _Float16*)(ws + l.kt);
+  a.kdt = (const _Float16*)(ws + l.kdt);
+  a.vt = (const _Float16*)(ws + l.vt);
+  a.vdt = (const _Float16*)(ws + l.vdt);
+  a.prom = (const uint32_t*)(ws + l.prom);
+  a.lse = lse;
+  a.drow = (const float*)(ws + l.drow);
+  a.B = B;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.S = S;
+  a.Sp = Sp;
+  a.bq = block_q;
+  a.nq = cdiv(S, block_q);
+  a.nkw = cdiv(nk, 32);
+  a.causal = causal;
+  a.sm_scale = sm_scale;
+  a.c = sm_scale * kLog2eB;
+  const int BHq = B * Hq, BHk = B * Hkv;
+  launch_decode_mx(q4c, q4s, (size_t)BHq * S, D, (_Float16*)a.qd, stream);
+  launch_decode_mx(k4c, k4s, (size_t)BHk * S, D, (_Float16*)a.kd, stream);
+  launch_decode_mx(v4c, v4s, (size_t)BHk * nk * D, kBlkK, (_Float16*)a.vdt, stream, D, nk);  // to V^T
+  const int nrows = BHq * a.nq;
+  prom_bits_kernel<<<cdiv(nrows, 256), 256, 0, stream>>>(idx, cnt, nrows, kmax, nk, a.nkw, (uint32_t*)a.prom);
+  if (backward) {
+    launch_transpose(a.vdt, BHk, D, Sp, D, (_Float16*)a.vd, stream);  // [Sp][D]
+    launch_transpose(a.q16, BHq, S, D, Sp, (_Float16*)a.qt, stream);
+    launch_transpose(a.qd, BHq, S, D, Sp, (_Float16*)a.qdt, stream);
+    launch_transpose(a.k16, BHk, S, D, Sp, (_Float16*)a.kt, stream);
+    launch_transpose(a.kd, BHk, S, D, Sp, (_Float16*)a.kdt, stream);
+  } else {
+    launch_transpose(a.v16, BHk, S, D, Sp, (_Float16*)a.vt, stream);
+  }
+}
+
+template <int D>
+void launch_row(const BwdArgs& a, int mode, hipStream_t stream) {
+  const int grid = a.B * a.Hq * a.nq, threads = (a.bq / 32) * 64;
+  if (mode == kModeOhp)
+    bwd_row_kernel<D, kModeOhp><<<grid, threads, 0, stream>>>(a);
+  else
+    bwd_row_kernel<D, kModeDq><<<grid, threads, 0, stream>>>(a);
+}
+
+template __global__ void bwd_row_kernel<128, kModeOhp>(BwdArgs);
+template __global__ void bwd_row_kernel<128, kModeDq>(BwdArgs);
+template __global__ void bwd_row_kernel<64, kModeOhp>(BwdArgs);
+template __global__ void bwd_row_kernel<64, kModeDq>(BwdArgs);
+template __global__ void bwd_key_kernel<128>(BwdArgs);
+template __global__ void bwd_key_kernel<64>(BwdArgs);
+template __global__ void row_term_kernel<128>(const _Float16*, const float*, size_t, float*);
+template __global__ void row_term_kernel<64>(const _Float16*, const float*, size_t, float*);
+
+}  // namespace
+
+}  // namespace thrift
+
+using namespace thrift;
+
+extern "C" size_t thrift_attention_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int block_q) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || D < 1 || block_q < 1) return 0;
+  return bwd_layout(B, Hq, Hkv, S, D, block_q).total;
+}
+
+extern "C" thrift_status thrift_attention_fwd_hp(
+    const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes, const uint8_t* q4_scales,
+    const uint8_t* k4_codes, const uint8_t* k4_scales, const uint8_t* v4_codes, const uint8_t* v4_scales,
+    thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D,
+    int block_q, int block_k, int causal, float sm_scale, const float* lse, float* ohp, void* workspace,
+    size_t workspace_bytes, hipStream_t stream) {
+  thrift_status st = check_bwd(q16, k16, v16, q4_codes, q4_scales, k4_codes, k4_scales, v4_codes, v4_scales, fmt,
+                               idx, cnt, kmax, B, Hq, Hkv, S, D, block_q, block_k, causal, sm_scale, lse,
+                               workspace, workspace_bytes);
+  if (st != THRIFT_OK) return st;
+  if (!ohp) return THRIFT_EINVAL;
+  if (!aligned16(ohp)) return THRIFT_EALIGN;
+  const BwdLayout l = bwd_layout(B, Hq, Hkv, S, D, block_q);
+  BwdArgs a{};
+  prepare(a, (char*)workspace, l, q16, k16, v16, q4_codes, q4_scales, k4_codes, k4_scales, v4_codes, v4_scales,
+          idx, cnt, kmax, B, Hq, Hkv, S, D, block_q, causal, sm_scale, lse, false, stream);
+  a.out = ohp;
+  if (D == 128)
+    launch_row<128>(a, kModeOhp, stream);
+  else
+    launch_row<64>(a, kModeOhp, stream);
+  return launch_status();
+}
+
+extern "C" thrift_status thrift_attention_bwd(
+    const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes, const uint8_t* q4_scales,
+    const uint8_t* k4_codes, const uint8_t* k4_scales, const uint8_t* v4_codes, const uint8_t* v4_scales,
+    thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D,
+    int block_q, int block_k, int causal, float sm_scale, const float* lse, const float* ohp, const void* do16,
+    float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  thrift_status st = check_bwd(q16, k16, v16, q4_codes, q4_scales, k4_codes, k4_scales, v4_codes, v4_scales, fmt,
+                               idx, cnt, kmax, B, Hq, Hkv, S, D, block_q, block_k, causal, sm_scale, lse,
+                               workspace, workspace_bytes);
+  if (st != THRIFT_OK) return st;
+  if (!ohp || !do16 || !dq || !dk || !dv) return THRIFT_EINVAL;
+  for (const void* p : {(const void*)ohp, do16, (const void*)dq, (const void*)dk, (const void*)dv})
+    if (!aligned16(p)) return THRIFT_EALIGN;
+  const BwdLayout l = bwd_layout(B, Hq, Hkv, S, D, block_q);
+  BwdArgs a{};
+  char* ws = (char*)workspace;
+  prepare(a, ws, l, q16, k16, v16, q4_codes, q4_scales, k4_codes, k4_scales, v4_codes, v4_scales, idx, cnt, kmax,
+          B, Hq, Hkv, S, D, block_q, causal, sm_scale, lse, true, stream);
+  const int Sp = a.Sp, BHq = B * Hq;
+  a.do16 = (const _Float16*)do16;
+  launch_transpose(a.do16, BHq, S, D, Sp, (_Float16*)a.dot, stream);
+  const size_t nrows = (size_t)BHq * S;
+  if (D == 128)
+    row_term_kernel<128><<<(unsigned)((nrows + 3) / 4), 256, 0, stream>>>(a.do16, ohp, nrows, (float*)a.drow);
+  else
+    row_term_kernel<64><<<(unsigned)((nrows + 3) / 4), 256, 0, stream>>>(a.do16, ohp, nrows, (float*)a.drow);
+  a.out = dq;
+  a.dk = dk;
+  a.dv = dv;
+  const int kgrid = B * Hkv * cdiv(S, kBlkK);
+  if (D == 128) {
+    launch_row<128>(a, kModeDq, stream);
+    bwd_key_kernel<128><<<kgrid, 128, 0, stream>>>(a);
+  } else {
+    launch_row<64>(a, kModeDq, stream);
+    bwd_key_kernel<64><<<kgrid, 128, 0, stream>>>(a);
+  }
+  return launch_status();
+}

@@ -328,6 +328,63 @@ thrift_status thrift_attention_decode(const void* q16, const void* k16, const vo
                                       float* lse, void* workspace, size_t workspace_bytes,
                                       hipStream_t stream);
 
+/* ---------------------------------------------------------------------- */
+/* Backward pass for quantisation-aware training ("Attn-QAT: 4-Bit         */
+/* Attention With Quantization-Aware Training"; gist.science summary in     */
+/* German, section 2 "Methodik", and the paper's abstract)                  */
+/* ---------------------------------------------------------------------- */
+
+/* The gradient of thrift_attention_fwd with the selection (idx, cnt) held
+ * fixed and every quantiser taken as the identity in the backward pass
+ * (straight-through), as quantisation-aware training differentiates through
+ * fake quantisation.  The two Attn-QAT rules:
+ *   - the backward recomputes each probability from the forward's
+ *     log-sum-exp in the precision the forward used for it: on FP4 pairs the
+ *     two-level quantised value (its codes are relative to the tile, so they
+ *     do not depend on the LSE), on FP16 pairs p rounded to fp16;
+ *   - the row term of the softmax gradient is dO . O', where O' is the
+ *     output with the exact (unquantised) probabilities, which the forward
+ *     stores besides O; dO . O (the FP4 output) would be wrong.
+ * For row r and key c of a valid pair (operands in the pair's path's
+ * precision): p = exp(sm_scale q.k - lse), dV[c] += pt dO[r],
+ * dS = p (dO[r].v[c] - dO[r].O'[r]), dQ[r] += sm_scale dS k[c],
+ * dK[c] += sm_scale dS q[r].  Training shape only: Sq = Sk = S.
+ * Supported: THRIFT_MXFP4 (THRIFT_EUNSUPPORTED for NVFP4), D 64 or 128,
+ * block_q 64 or 128, block_k 64. */
+
+/* Workspace bytes both calls below need: FP4-decoded and transposed fp16
+ * copies of the operands, the promoted-block bit table and the row terms
+ * (about 4 Q-sized and 6 K-sized fp16 tensors). */
+size_t thrift_attention_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int block_q);
+
+/* O' of the forward: ohp [B,Hq,S,D] fp32 (out) from the same inputs as
+ * thrift_attention_fwd (FP4 tensors as written by thrift_quantize_fp4:
+ * Q and K along THRIFT_GROUP_D, V along THRIFT_GROUP_S) and its lse
+ * [B,Hq,S] (in, natural log, 16-byte aligned).  Rows past S are not
+ * written.  The workspace contents are scratch. */
+thrift_status thrift_attention_fwd_hp(const void* q16, const void* k16, const void* v16,
+                                      const uint8_t* q4_codes, const uint8_t* q4_scales,
+                                      const uint8_t* k4_codes, const uint8_t* k4_scales,
+                                      const uint8_t* v4_codes, const uint8_t* v4_scales,
+                                      thrift_format fmt, const int32_t* idx, const int32_t* cnt,
+                                      int kmax, int B, int Hq, int Hkv, int S, int D, int block_q,
+                                      int block_k, int causal, float sm_scale, const float* lse,
+                                      float* ohp, void* workspace, size_t workspace_bytes,
+                                      hipStream_t stream);
+
+/* Gradients: do16 [B,Hq,S,D] fp16 (in), lse and ohp from the forward (in);
+ * dq [B,Hq,S,D], dk and dv [B,Hkv,S,D] fp32 (out, overwritten; query heads
+ * sharing a key head are summed into it).  Deterministic: no atomics. */
+thrift_status thrift_attention_bwd(const void* q16, const void* k16, const void* v16,
+                                   const uint8_t* q4_codes, const uint8_t* q4_scales,
+                                   const uint8_t* k4_codes, const uint8_t* k4_scales,
+                                   const uint8_t* v4_codes, const uint8_t* v4_scales,
+                                   thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                                   int B, int Hq, int Hkv, int S, int D, int block_q, int block_k,
+                                   int causal, float sm_scale, const float* lse, const float* ohp,
+                                   const void* do16, float* dq, float* dk, float* dv, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
+
 /* Static string for a status code (host). */
 const char* thrift_status_string(thrift_status s);
 

@@ -1,0 +1,148 @@
+"""GPU parity of the Attn-QAT backward (Attn-QAT summary, "Methodik": P
+recomputed from the forward's log-sum-exp in the forward's own precision, row
+term from the high-precision output O') and of O' itself, through the C ABI,
+against the oracle (MXFP4).
+
+Selection, FP4 codes and scales are checked bit for bit on the way.  O', dQ,
+dK and dV: max-abs within 2e-3 times max(1, the largest magnitude of the
+oracle's tensor) and rel-L2 within 1e-3.  The bound is relative to the
+tensor's scale because gradients are sums over a whole row or column of
+products with dO: their size grows with the sequence and the attention's
+concentration, while each term carries the fp16 rounding of one MFMA operand
+(probability or dS, 2^-11 relative) and fp32 accumulation.  dV's bound is
+widened element by element by the oracle's decision uncertainty (E2M1 codes
+and block scales of P, fp16 rounding on FP16 pairs, whose inputs lie within
+fp32 evaluation error of a boundary).
+"""
+import numpy as np
+import pytest
+
+from fp16_attention_amd import workloads as W
+from tests.gpu_harness import note, same_fp4, workload
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-3
+REL_L2 = 1e-3
+
+CASES = {
+    # name: (workload, topk_count, topk_bp)
+    "prefill_mixed": (workload("prefill", Hq=2, Hkv=2, S=700), -1, 1000),
+    "gqa_ragged_b2": (workload("sweep", B=2, Hq=4, Hkv=2, S=333), -1, 2500),
+    "dit_noncausal_d64_bq64": (workload("dit", Hq=2, Hkv=2, S=300, bq=64), -1, 500),
+    "all_fp16": (workload("prefill", Hq=2, Hkv=1, S=256), -1, 10000),
+    "no_fp16": (workload("prefill", Hq=2, Hkv=1, S=256), -1, 0),
+    "short_tail": (workload("prefill", Hq=1, Hkv=1, S=37), -1, 500),
+    "long_sink_planted_gqa4": (workload("long", Hq=4, Hkv=1, S=1024, planted=2), -1, 500),
+}
+
+
+def compare(name, g, r, u=None):
+    assert np.all(np.isfinite(g)), f"{name}: non-finite values"
+    err = np.abs(g - r)
+    scale = max(1.0, float(np.abs(r).max()))
+    rel = np.linalg.norm(g - r) / max(np.linalg.norm(r), 1e-30)
+    excess = err - (0.0 if u is None else u)
+    note(f"    {name}: max-abs {err.max():.3e} (scale {scale:.2f}, beyond u {excess.max():.3e})  rel-L2 {rel:.3e}")
+    assert excess.max() <= MAX_ABS * scale, f"{name}: max-abs {excess.max():.3e} > {MAX_ABS * scale:.3e}"
+    assert rel <= REL_L2, f"{name}: rel-L2 {rel:.3e}"
+    if u is not None:
+        assert np.mean(u > MAX_ABS * scale) < 0.05, f"{name}: decision uncertainty covers too many elements"
+
+
+def gpu_backward(d, w, do, tc, bp, fmt=1):
+    import torch
+
+    from fp16_attention_amd import api
+
+    dev = torch.device("cuda:0")
+    q, k, v, dot = (torch.from_numpy(np.ascontiguousarray(x)).to(dev) for x in (d["q"], d["k"], d["v"], do))
+    idx, cnt = api.thrift_select_blocks(q, k, w.bq, w.bk, w.causal, tc, bp)
+    q4 = api.thrift_quantize_fp4(q, api.THRIFT_GROUP_D, fmt)
+    k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, fmt)
+    v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, fmt)
+    _, lse = api.thrift_attention_fwd(q, k, v, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal, out_fp32=True,
+                                      with_lse=True)
+    ws = api.thrift_attention_bwd_workspace(w.B, w.Hq, w.Hkv, w.S, w.D, w.bq, dev)
+    ohp = api.thrift_attention_fwd_hp(q, k, v, q4, k4, v4, idx, cnt, lse, w.bq, w.bk, w.causal, workspace=ws)
+    dq, dk, dv = api.thrift_attention_bwd(q, k, v, q4, k4, v4, idx, cnt, lse, ohp, dot, w.bq, w.bk, w.causal,
+                                          workspace=ws)
+    torch.cuda.synchronize()
+    cpu = lambda t: t.cpu().numpy()  # noqa: E731
+    return dict(idx=cpu(idx), cnt=cpu(cnt), q4=q4, k4=k4, v4=v4, ohp=cpu(ohp).astype(np.float64),
+                dq=cpu(dq).astype(np.float64), dk=cpu(dk).astype(np.float64), dv=cpu(dv).astype(np.float64))
+
+
+def output_grad(w, seed):
+    rng = np.random.default_rng(seed)
+    return rng.standard_normal((w.B, w.Hq, w.S, w.D)).astype(np.float16)
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_backward_parity(oracle, name):
+    w, tc, bp = CASES[name]
+    note(f"[backward] {name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} S{w.S} D{w.D} causal{int(w.causal)} bq{w.bq} "
+         f"topk({tc},{bp})")
+    d = W.generate(w)
+    do = output_grad(w, 7 + len(name))
+    g = gpu_backward(d, w, do, tc, bp)
+    idx, cnt, _ = oracle.select(d["q"], d["k"], w.bq, w.bk, w.causal, tc, bp)
+    assert np.array_equal(g["cnt"], cnt), "cnt differs"
+    km = idx.shape[-1]
+    assert np.array_equal(g["idx"][..., :km], idx), "idx differs"
+    q4 = oracle.quantize(d["q"], oracle.AXIS_D, 1)
+    k4 = oracle.quantize(d["k"], oracle.AXIS_D, 1)
+    v4 = oracle.quantize(d["v"], oracle.AXIS_S, 1)
+    same_fp4(g["q4"], q4)
+    same_fp4(g["k4"], k4)
+    same_fp4(g["v4"], v4)
+    _, lse, ohp = oracle.attention_hp(d["q"], d["k"], d["v"], q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal)
+    dq, dk, dv, udv = oracle.attention_bwd(d["q"], d["k"], d["v"], q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal,
+                                           lse, ohp, do, with_u=True)
+    compare("O'", g["ohp"], ohp)
+    compare("dQ", g["dq"], dq)
+    compare("dK", g["dk"], dk)
+    compare("dV", g["dv"], dv, udv)
+
+
+def test_backward_fullsize_prefill(oracle):
+    """The prefill workload at full size (B1 H32 S8192 D128 causal, 5%), in the
+    benchmark's launch configuration; the oracle computes head 0: dQ of three
+    query blocks, dK and dV of three key blocks."""
+    w = W.WORKLOADS["prefill"].with_(fmt=1)
+    note(f"[backward] prefill full size: B{w.B} Hq{w.Hq} S{w.S} D{w.D}")
+    d = W.generate(w)
+    do = output_grad(w, 99)
+    g = gpu_backward(d, w, do, w.topk_count, w.topk_bp)
+    idx, cnt, _ = oracle.select(d["q"], d["k"], w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
+    km = idx.shape[-1]
+    assert np.array_equal(g["cnt"], cnt) and np.array_equal(g["idx"][..., :km], idx)
+    q4 = oracle.quantize(d["q"], oracle.AXIS_D, 1)
+    k4 = oracle.quantize(d["k"], oracle.AXIS_D, 1)
+    v4 = oracle.quantize(d["v"], oracle.AXIS_S, 1)
+    same_fp4(g["q4"], q4)
+    nq, nk = -(-w.S // w.bq), -(-w.S // w.bk)
+    head0 = [(0, 0, i) for i in range(nq)]
+    _, lse, ohp = oracle.attention_hp(d["q"], d["k"], d["v"], q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal,
+                                      work=head0)
+    qb, kb = [0, nq // 2, nq - 1], [0, nk // 3, nk - 1]
+    dq, dk, dv, udv = oracle.attention_bwd(d["q"], d["k"], d["v"], q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal,
+                                           lse, ohp, do, qwork=[(0, 0, i) for i in qb],
+                                           kwork=[(0, 0, j) for j in kb], with_u=True)
+    compare("O' (head 0)", g["ohp"][0, 0], ohp[0, 0])
+    rq = np.concatenate([np.arange(i * w.bq, min(w.S, (i + 1) * w.bq)) for i in qb])
+    rk = np.concatenate([np.arange(j * w.bk, min(w.S, (j + 1) * w.bk)) for j in kb])
+    compare("dQ (3 query blocks)", g["dq"][0, 0, rq], dq[0, 0, rq])
+    compare("dK (3 key blocks)", g["dk"][0, 0, rk], dk[0, 0, rk])
+    compare("dV (3 key blocks)", g["dv"][0, 0, rk], dv[0, 0, rk], udv[0, 0, rk])
+
+
+def test_backward_deterministic():
+    """Two runs give bit-identical gradients (no atomics)."""
+    w = workload("sweep", B=1, Hq=4, Hkv=2, S=700)
+    d = W.generate(w)
+    do = output_grad(w, 5)
+    a = gpu_backward(d, w, do, -1, 2500)
+    b = gpu_backward(d, w, do, -1, 2500)
+    for key in ("ohp", "dq", "dk", "dv"):
+        assert np.array_equal(a[key], b[key]), key
