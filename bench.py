@@ -112,7 +112,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="long")
+    ap.add_argument("--workload", default=None, help="default: long (forward), prefill (--pass bwd)")
+    ap.add_argument("--pass", dest="pass_", default="fwd", choices=["fwd", "bwd"],
+                    help="fwd: the forward path (default); bwd: the Attn-QAT backward pass")
     ap.add_argument("--fmt", default="mx", choices=["mx", "nvfp4"])
     ap.add_argument("--topk-bp", type=int, default=None)
     ap.add_argument("--budget", default="block", choices=["block", "head"],
@@ -134,6 +136,8 @@ def main():
     from fp16_attention_amd import api
     from fp16_attention_amd import workloads as W
 
+    if args.workload is None:
+        args.workload = "prefill" if args.pass_ == "bwd" else "long"
     w = W.WORKLOADS[args.workload]
     if args.topk_bp is not None:
         w = w.with_(topk_count=-1, topk_bp=args.topk_bp)
@@ -143,6 +147,8 @@ def main():
     gen_s = time.time() - t0
     if w.Sq:
         return run_decode(args, w, d, gen_s)
+    if args.pass_ == "bwd":
+        return run_backward(args, w, d, gen_s)
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v"))
     if args.budget == "head":
@@ -370,6 +376,129 @@ def run_decode(args, w, d, gen_s):
     if args.out:
         with open(args.out, "a") as f:
             f.write(s + "\n")
+
+
+def run_backward(args, w, d, gen_s):
+    """Attn-QAT backward.  One step = thrift_attention_bwd on resident inputs
+    (Q, K, V, their FP4 copies, the selection, the forward's lse and O', and
+    an output gradient dO ~ N(0, 1)).  Algorithmic flops: five products of
+    2 D flops per unmasked pair (recomputed scores, dP, dV, dK, dQ), all on the
+    fp16 matrix cores (MX-decoded FP4 operands are exact in fp16)."""
+    import torch
+
+    from fp16_attention_amd import api
+
+    if args.fmt != "mx":
+        print("bench.py: the backward pass supports MXFP4 only", file=sys.stderr)
+        sys.exit(2)
+    fmt = api.THRIFT_MXFP4
+    dev = torch.device("cuda:0")
+    q, k, v = (torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v"))
+    rng = np.random.default_rng(w.seed + 1)
+    do_h = rng.standard_normal((w.B, w.Hq, w.S, w.D)).astype(np.float16)
+    do = torch.from_numpy(do_h).to(dev)
+    idx, cnt = api.thrift_select_blocks(q, k, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
+    q4 = api.thrift_quantize_fp4(q, api.THRIFT_GROUP_D, fmt)
+    k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, fmt)
+    v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, fmt)
+    _, lse = api.thrift_attention_fwd(q, k, v, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal, with_lse=True)
+    ws = api.thrift_attention_bwd_workspace(w.B, w.Hq, w.Hkv, w.S, w.D, w.bq, dev)
+    ohp = torch.empty((w.B, w.Hq, w.S, w.D), dtype=torch.float32, device=dev)
+    if args.copy_mib:
+        copy_calibration(torch, dev, args.copy_mib)
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+
+    def hp():
+        api.thrift_attention_fwd_hp(q, k, v, q4, k4, v4, idx, cnt, lse, w.bq, w.bk, w.causal, workspace=ws,
+                                    out=ohp)
+
+    def step(rec=None):
+        if rec:
+            rec[0].record()
+        grads = api.thrift_attention_bwd(q, k, v, q4, k4, v4, idx, cnt, lse, ohp, do, w.bq, w.bk, w.causal,
+                                         workspace=ws)
+        if rec:
+            rec[1].record()
+        return grads
+
+    hp()
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    hp_recs = [[ev(), ev()] for _ in range(3)]
+    for r in hp_recs:
+        r[0].record()
+        hp()
+        r[1].record()
+    recs = [[ev(), ev()] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for r in recs:
+        step(r)
+    torch.cuda.synchronize()
+    ms_step = 1e3 * (time.perf_counter() - t0) / args.steps
+    bwd_ms = float(np.mean([r[0].elapsed_time(r[1]) for r in recs]))
+    hp_ms = float(np.mean([r[0].elapsed_time(r[1]) for r in hp_recs]))
+    pairs = w.B * w.Hq * unmasked_pairs(w.S, w.causal)
+    f_bwd = 10.0 * w.D * pairs
+    achieved = f_bwd / (bwd_ms * 1e-3)
+    line = {
+        "metric": "attention-bwd (Attn-QAT) TFLOPS + % of the fp16 MFMA roofline",
+        "value": round(f_bwd / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 (MX-decoded FP4 operands)",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} S{w.S} D{w.D} "
+                               f"{'causal' if w.causal else 'non-causal'} blocks {w.bq}x{w.bk} "
+                               f"top-k {w.topk_bp / 100}% mx, backward",
+                   "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)"},
+        "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": P_FP16 / 1e12,
+                     "unit": "TFLOP/s", "frac": round(achieved / P_FP16, 4), "traffic": None,
+                     "kernel": "thrift_attention_bwd (operand preparation, bwd_row_kernel, bwd_key_kernel)"},
+        "breakdown_ms": {"attention_bwd": round(bwd_ms, 4), "fwd_hp_O_prime": round(hp_ms, 4)},
+        "input_gen_s": round(gen_s, 1),
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_bwd(w, d, do_h)
+    s = json.dumps(line)
+    print(s, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(s + "\n")
+
+
+def cpu_baseline_bwd(w, d, do_h):
+    """The oracle's backward of query head 0 and its key head (one head per key
+    head in this workload): selection, quantisation, the forward with O' and
+    the backward over every query and key block of that head."""
+    from oracle import oracle as O
+
+    nthreads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    G = w.Hq // w.Hkv
+    q1 = np.ascontiguousarray(d["q"][:1, :G])
+    k1 = np.ascontiguousarray(d["k"][:1, :1])
+    v1 = np.ascontiguousarray(d["v"][:1, :1])
+    do1 = np.ascontiguousarray(do_h[:1, :G])
+    O.lib()
+    t0 = time.perf_counter()
+    idx, cnt, _ = O.select(q1, k1, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
+    q4, k4, v4 = (O.quantize(x, ax, O.MX) for x, ax in ((q1, O.AXIS_D), (k1, O.AXIS_D), (v1, O.AXIS_S)))
+    _, lse, ohp = O.attention_hp(q1, k1, v1, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal)
+    O.attention_bwd(q1, k1, v1, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal, lse, ohp, do1)
+    sec = time.perf_counter() - t0
+    f = 10.0 * w.D * G * unmasked_pairs(w.S, w.causal)
+    return {"value": round(f / sec / 1e12, 5), "unit": "TFLOP/s", "cores": nthreads, "kind": "oracle",
+            "seconds": round(sec, 2),
+            "sample": f"key head 0 of batch 0 with its {G} query head(s): selection, FP4 quantisation, the forward "
+                      f"with O' and the backward over all query and key blocks ({f / 1e9:.1f} GFLOP of backward), "
+                      f"fp64"}
 
 
 def cpu_baseline(w, d, fmt, budget="block"):
