@@ -163,13 +163,32 @@ __global__ __launch_bounds__(256) void row_term_kernel(const _Float16* do16, con
 constexpr int kModeOhp = 0;
 constexpr int kModeDq = 1;
 
+// LDS stage of one key block for the row kernel: K rows, V rows (dQ mode)
+// and the transposed operand of the second product (K^T or V^T).
+template <int D>
+struct RowLds {
+  static constexpr int KR = D + 8;      // halves per K/V row
+  static constexpr int TR = kBlkK + 8;  // halves per transposed row
+  static constexpr int K = 0;
+  static constexpr int V = K + kBlkK * KR * 2;
+  static constexpr int T = V + kBlkK * KR * 2;
+  static constexpr int SIZE = T + D * TR * 2;
+};
+
 // Workgroup = query block i of (batch, query head), one wave per 32 rows.
 // Per valid key block j, in the precision of its path: S^T = K Q^T (keys in
 // krow_b order), p = 2^(t - L2); then O'^T += V^T P^T, or dP^T = V dO^T,
-// dS = p (dP - Dr) and dQ^T += K^T dS^T.
-template <int D, int MODE>
-__global__ __launch_bounds__(256) void bwd_row_kernel(BwdArgs a) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hi = lane >> 5, r32 = lane & 31;
+// dS = p (dP - Dr) and dQ^T += K^T dS^T.  The waves share each key block's
+// operands through one LDS stage; the next block's are loaded into
+// registers while the current one is computed.
+template <int D, int MODE, int NW>
+__global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
+  using L = RowLds<D>;
+  constexpr int NT = NW * 64;
+  constexpr int PK = kBlkK * D / 8 / NT;  // 16-byte pieces of a K or V block per thread
+  constexpr int PT = D * kBlkK / 8 / NT;  // of the transposed block
+  __shared__ __attribute__((aligned(16))) char smem[L::SIZE];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, hi = lane >> 5, r32 = lane & 31;
   const int BHq = a.B * a.Hq, G = a.Hq / a.Hkv;
   const int x = blockIdx.x;
   const int i = a.causal ? a.nq - 1 - x / BHq : x / BHq;  // longest rows first
@@ -178,8 +197,8 @@ __global__ __launch_bounds__(256) void bwd_row_kernel(BwdArgs a) {
   const size_t bhk = (size_t)b * a.Hkv + hq / G;
   const int S = a.S, Sp = a.Sp;
   const int q0 = i * a.bq + w * 32;
-  if (q0 >= S) return;  // no barrier in this kernel
   const int qrow = q0 + r32;
+  const bool qok = qrow < S;  // waves past S still pass every barrier
 
   const auto qrs = rsrc(a.q16 + (size_t)bhq * S * D, S * D * 2);
   const auto qdrs = rsrc(a.qd + (size_t)bhq * S * D, S * D * 2);
@@ -195,7 +214,6 @@ __global__ __launch_bounds__(256) void bwd_row_kernel(BwdArgs a) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) dh[kk] = ld8h(drs, (qrow * D + kk * 16 + hi * 8) * 2);
   }
-  const bool qok = qrow < S;
   const float L2 = qok ? a.lse[(size_t)bhq * S + qrow] * kLog2eB : 0.0f;
   const float Dr = (MODE == kModeDq && qok) ? a.drow[(size_t)bhq * S + qrow] : 0.0f;
 
@@ -209,26 +227,66 @@ __global__ __launch_bounds__(256) void bwd_row_kernel(BwdArgs a) {
   const auto vdrs = rsrc(a.vd + bhk * Sp * D, Sp * D * 2);
   const uint32_t* pm = a.prom + ((size_t)bhq * a.nq + i) * a.nkw;
   const int nvalid = valid_kv_blocks(i, S, a.bq, kBlkK, a.causal);
-  for (int j = 0; j < nvalid; ++j) {
-    const bool f16 = (pm[j >> 5] >> (j & 31)) & 1u;
+
+  v4i pk[PK], pv[PK], pt[PT];
+  auto promoted = [&](int j) { return ((pm[j >> 5] >> (j & 31)) & 1u) != 0; };
+  auto fetch = [&](int j) {
+    const bool f16 = promoted(j);
     const auto krs = f16 ? k16rs : kdrs;
+    const auto vrs = f16 ? v16rs : vdrs;
+    const _Float16* T = (MODE == kModeOhp ? (f16 ? a.vt : a.vdt) : (f16 ? a.kt : a.kdt)) + bhk * D * Sp;
+#pragma unroll
+    for (int u = 0; u < PK; ++u) {
+      const int c = t + u * NT, row = c / (D / 8), c8 = c % (D / 8);
+      const int off = ((j * kBlkK + row) * D + c8 * 8) * 2;
+      pk[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
+      if constexpr (MODE == kModeDq) pv[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int c = t + u * NT, d = c / (kBlkK / 8), k8 = c % (kBlkK / 8);
+      pt[u] = *(const v4i*)(T + (size_t)d * Sp + j * kBlkK + k8 * 8);
+    }
+  };
+  auto stash = [&]() {
+#pragma unroll
+    for (int u = 0; u < PK; ++u) {
+      const int c = t + u * NT, row = c / (D / 8), c8 = c % (D / 8);
+      *(v4i*)(smem + L::K + (row * L::KR + c8 * 8) * 2) = pk[u];
+      if constexpr (MODE == kModeDq) *(v4i*)(smem + L::V + (row * L::KR + c8 * 8) * 2) = pv[u];
+    }
+#pragma unroll
+    for (int u = 0; u < PT; ++u) {
+      const int c = t + u * NT, d = c / (kBlkK / 8), k8 = c % (kBlkK / 8);
+      *(v4i*)(smem + L::T + (d * L::TR + k8 * 8) * 2) = pt[u];
+    }
+  };
+
+  if (nvalid > 0) fetch(0);
+  for (int j = 0; j < nvalid; ++j) {
+    const bool f16 = promoted(j);
+    __syncthreads();  // every wave is done with the previous block
+    stash();
+    __syncthreads();
+    if (j + 1 < nvalid) fetch(j + 1);
+    const _Float16* ks = (const _Float16*)(smem + L::K);
     v16f s[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       s[mt] = v16f{};
-      const int kb = (j * kBlkK + krow_b(mt, r32)) * D + hi * 8;
+      const _Float16* kr = ks + krow_b(mt, r32) * L::KR + hi * 8;
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) s[mt] = mma16(ld8h(krs, (kb + kk * 16) * 2), f16 ? qh[kk] : qd[kk], s[mt]);
+      for (int kk = 0; kk < D / 16; ++kk) s[mt] = mma16(*(const v8h*)(kr + kk * 16), f16 ? qh[kk] : qd[kk], s[mt]);
     }
     v16f dp[2];
     if constexpr (MODE == kModeDq) {
-      const auto vrs = f16 ? v16rs : vdrs;
+      const _Float16* vs = (const _Float16*)(smem + L::V);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         dp[mt] = v16f{};
-        const int vb = (j * kBlkK + krow_b(mt, r32)) * D + hi * 8;
+        const _Float16* vr = vs + krow_b(mt, r32) * L::KR + hi * 8;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) dp[mt] = mma16(ld8h(vrs, (vb + kk * 16) * 2), dh[kk], dp[mt]);
+        for (int kk = 0; kk < D / 16; ++kk) dp[mt] = mma16(*(const v8h*)(vr + kk * 16), dh[kk], dp[mt]);
       }
     }
     // B operand of the second product: step st holds keys hi*32 + 8 st + u,
@@ -245,13 +303,13 @@ __global__ __launch_bounds__(256) void bwd_row_kernel(BwdArgs a) {
         if constexpr (MODE == kModeDq) v = p * (dp[mt][ii] - Dr);
         pb[mt * 2 + ii / 8][ii % 8] = (_Float16)v;
       }
-    const _Float16* T = MODE == kModeOhp ? (f16 ? a.vt : a.vdt) : (f16 ? a.kt : a.kdt);
+    const _Float16* ts = (const _Float16*)(smem + L::T);
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const v8h t = *(const v8h*)(T + (bhk * D + dt * 32 + r32) * Sp + j * kBlkK + hi * 32 + st * 8);
-        acc[dt] = mma16(t, pb[st], acc[dt]);
+        const v8h tv = *(const v8h*)(ts + (dt * 32 + r32) * L::TR + hi * 32 + st * 8);
+        acc[dt] = mma16(tv, pb[st], acc[dt]);
       }
   }
   if (!qok) return;
@@ -558,17 +616,28 @@ void prepare(BwdArgs& a, char* ws, const BwdLayout& l, const void* q16, const vo
 
 template <int D>
 void launch_row(const BwdArgs& a, int mode, hipStream_t stream) {
-  const int grid = a.B * a.Hq * a.nq, threads = (a.bq / 32) * 64;
-  if (mode == kModeOhp)
-    bwd_row_kernel<D, kModeOhp><<<grid, threads, 0, stream>>>(a);
-  else
-    bwd_row_kernel<D, kModeDq><<<grid, threads, 0, stream>>>(a);
+  const int grid = a.B * a.Hq * a.nq;
+  if (a.bq == 128) {
+    if (mode == kModeOhp)
+      bwd_row_kernel<D, kModeOhp, 4><<<grid, 256, 0, stream>>>(a);
+    else
+      bwd_row_kernel<D, kModeDq, 4><<<grid, 256, 0, stream>>>(a);
+  } else {
+    if (mode == kModeOhp)
+      bwd_row_kernel<D, kModeOhp, 2><<<grid, 128, 0, stream>>>(a);
+    else
+      bwd_row_kernel<D, kModeDq, 2><<<grid, 128, 0, stream>>>(a);
+  }
 }
 
-template __global__ void bwd_row_kernel<128, kModeOhp>(BwdArgs);
-template __global__ void bwd_row_kernel<128, kModeDq>(BwdArgs);
-template __global__ void bwd_row_kernel<64, kModeOhp>(BwdArgs);
-template __global__ void bwd_row_kernel<64, kModeDq>(BwdArgs);
+template __global__ void bwd_row_kernel<128, kModeOhp, 4>(BwdArgs);
+template __global__ void bwd_row_kernel<128, kModeDq, 4>(BwdArgs);
+template __global__ void bwd_row_kernel<64, kModeOhp, 4>(BwdArgs);
+template __global__ void bwd_row_kernel<64, kModeDq, 4>(BwdArgs);
+template __global__ void bwd_row_kernel<128, kModeOhp, 2>(BwdArgs);
+template __global__ void bwd_row_kernel<128, kModeDq, 2>(BwdArgs);
+template __global__ void bwd_row_kernel<64, kModeOhp, 2>(BwdArgs);
+template __global__ void bwd_row_kernel<64, kModeDq, 2>(BwdArgs);
 template __global__ void bwd_key_kernel<128>(BwdArgs);
 template __global__ void bwd_key_kernel<64>(BwdArgs);
 template __global__ void row_term_kernel<128>(const _Float16*, const float*, size_t, float*);
