@@ -327,164 +327,235 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
 
 // ---- key kernel: one lane per key (dK, dV) -------------------------------------
 
-// Workgroup = key block j of (batch, key head), two waves of 32 keys.  Loops
-// over the G query heads of the key head and the query rows that see the
-// block, 32 rows a step: S = Q K^T and dP = dO V^T with this lane's key as the
-// column, p and dS per element; on FP4 pairs the probability the forward used
-// is rebuilt from its MX group (this wave's 32 keys), whose maximum comes from
-// S^T = K Q^T (one lane per query) and is handed over through LDS.  Then
-// dV += pt^T dO and dK += dS^T Q.
+// LDS stage of one 32-query step for the key kernel: query rows (fp16 and
+// FP4-decoded, as needed), dO rows, their transposes, and the rows' LSE and
+// row terms; plus each wave's per-query MX factors.
 template <int D>
-__global__ __launch_bounds__(128) void bwd_key_kernel(BwdArgs a) {
-  __shared__ __attribute__((aligned(16))) float sh_a[2][2][32], sh_h[2][2][32];  // [step parity][wave][query]
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, hi = lane >> 5, r32 = lane & 31;
+struct KeyLds {
+  static constexpr int RR = D + 8;  // halves per query row
+  static constexpr int TR = 32 + 8; // halves per transposed row (32 queries)
+  static constexpr int QR16 = 0;
+  static constexpr int QRD = QR16 + 32 * RR * 2;
+  static constexpr int DOR = QRD + 32 * RR * 2;
+  static constexpr int QT16 = DOR + 32 * RR * 2;
+  static constexpr int QTD = QT16 + D * TR * 2;
+  static constexpr int DOT = QTD + D * TR * 2;
+  static constexpr int L2 = DOT + D * TR * 2;  // 32 floats
+  static constexpr int DR = L2 + 32 * 4;       // 32 floats
+  static constexpr int FA = DR + 32 * 4;       // [4 waves][32] floats
+  static constexpr int FH = FA + 4 * 32 * 4;   // [4 waves][32] floats
+  static constexpr int SIZE = FH + 4 * 32 * 4;
+};
+
+// Workgroup = two key blocks (2 x 64 keys) of (batch, key head), four waves
+// of 32 keys each, one lane per key.  Steps of 32 query rows run over the G
+// query heads of the key head and the rows that see the blocks; each step's
+// query rows, dO rows and their transposes come once into LDS for all four
+// waves (the next step's are loaded into registers meanwhile).  Per step and
+// wave: S = Q K^T and dP = dO V^T with this lane's key as the column, p and
+// dS per element; on FP4 pairs the probability the forward used is rebuilt
+// from its MX group (the wave's 32 keys), whose maximum comes from
+// S^T = K Q^T (same operands swapped, one lane per query) and is handed to
+// the key-major lanes through the wave's own LDS slot.  Then dV += pt^T dO
+// and dK += dS^T Q.  Only the K and V operands of the precision in use are
+// held in registers; they are reloaded when a step switches path.
+template <int D>
+__global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
+  using L = KeyLds<D>;
+  constexpr int PR = 32 * D / 8 / 256;  // 16-byte pieces of a 32-row tile per thread
+  __shared__ __attribute__((aligned(16))) char smem[L::SIZE];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6, hi = lane >> 5, r32 = lane & 31;
   const int BHk = a.B * a.Hkv, G = a.Hq / a.Hkv;
+  const int nk = cdiv(a.S, kBlkK);
   const int x = blockIdx.x;
-  const int j = x / BHk;  // causal: the lowest key blocks have the most rows
+  const int j0 = (x / BHk) * 2;  // causal: the lowest key blocks have the most rows
   const size_t bhk = x % BHk;
   const int b = (int)(bhk / a.Hkv), hk = (int)(bhk % a.Hkv);
   const int S = a.S, Sp = a.Sp;
-  const int key = j * kBlkK + w * 32 + r32;  // this lane's key (column of S)
+  const int jb = j0 + (w >> 1);              // this wave's key block
+  const int key = jb * kBlkK + (w & 1) * 32 + r32;  // this lane's key (column of S)
 
-  v8h kh[D / 16], kd[D / 16], vh[D / 16], vd[D / 16];
-  {
-    const auto k16rs = rsrc(a.k16 + bhk * S * D, S * D * 2);
-    const auto kdrs = rsrc(a.kd + bhk * S * D, S * D * 2);
-    const auto v16rs = rsrc(a.v16 + bhk * S * D, S * D * 2);
-    const auto vdrs = rsrc(a.vd + bhk * Sp * D, Sp * D * 2);
+  const auto k16rs = rsrc(a.k16 + bhk * S * D, S * D * 2);
+  const auto kdrs = rsrc(a.kd + bhk * S * D, S * D * 2);
+  const auto v16rs = rsrc(a.v16 + bhk * S * D, S * D * 2);
+  const auto vdrs = rsrc(a.vd + bhk * Sp * D, Sp * D * 2);
+  v8h kr[D / 16], vr[D / 16];
+  int cur = -1;  // path whose K and V operands kr, vr hold (1 FP16, 0 FP4)
+  auto load_kv = [&](bool f16) {
+    const auto krs = f16 ? k16rs : kdrs;
+    const auto vrs = f16 ? v16rs : vdrs;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
       const int off = (key * D + kk * 16 + hi * 8) * 2;
-      kh[kk] = ld8h(k16rs, off);
-      kd[kk] = ld8h(kdrs, off);
-      vh[kk] = ld8h(v16rs, off);
-      vd[kk] = ld8h(vdrs, off);
+      kr[kk] = ld8h(krs, off);
+      vr[kk] = ld8h(vrs, off);
     }
-  }
+    cur = f16;
+  };
   v16f dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) dk[dt] = dv[dt] = v16f{};
 
-  const int i0 = a.causal ? (j * kBlkK) / a.bq : 0;
-  int par = 0;
-  for (int g = 0; g < G; ++g) {
+  // step sequence: for g < G, q0 from the first row that sees block j0, by 32
+  const int qstart = a.causal ? (j0 * kBlkK / 32) * 32 : 0;
+  const int nsteps_g = cdiv(S - qstart, 32);
+  const int nsteps = G * nsteps_g;
+  auto kind = [&](int bhq, int i, int j) {
+    return j < nk && ((a.prom[((size_t)bhq * a.nq + i) * a.nkw + (j >> 5)] >> (j & 31)) & 1u) != 0;
+  };
+  v4i pq16[PR], pqd[PR], pdo[PR], pt16[PR], ptd[PR], pdt[PR];
+  float pl = 0.0f, pr = 0.0f;
+  auto fetch = [&](int n) {
+    const int g = n / nsteps_g, q0 = qstart + (n % nsteps_g) * 32, i = q0 / a.bq;
     const int bhq = b * a.Hq + hk * G + g;
+    const bool f0 = kind(bhq, i, j0), f1 = kind(bhq, i, j0 + 1);
+    const bool need16 = f0 || f1, needd = !f0 || !f1;
     const auto qrs = rsrc(a.q16 + (size_t)bhq * S * D, S * D * 2);
     const auto qdrs = rsrc(a.qd + (size_t)bhq * S * D, S * D * 2);
     const auto drs = rsrc(a.do16 + (size_t)bhq * S * D, S * D * 2);
-    const auto lrs = rsrc(a.lse + (size_t)bhq * S, S * 4);
-    const auto rrs = rsrc(a.drow + (size_t)bhq * S, S * 4);
-    for (int i = i0; i < a.nq; ++i) {
-      const bool f16 = (a.prom[((size_t)bhq * a.nq + i) * a.nkw + (j >> 5)] >> (j & 31)) & 1u;
-      const int qend = min(S, (i + 1) * a.bq);
-      for (int q0 = i * a.bq; q0 < qend; q0 += 32) {
-        if (a.causal && q0 + 31 < j * kBlkK) continue;  // every pair of the step is masked
-        const auto ars = f16 ? qrs : qdrs;
-        v8h qa[D / 16], da[D / 16];
-        const int qm = q0 + qperm(r32);
+    const size_t tb = (size_t)bhq * D * Sp;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          const int off = (qm * D + kk * 16 + hi * 8) * 2;
-          qa[kk] = ld8h(ars, off);
-          da[kk] = ld8h(drs, off);
-        }
-        v16f s = v16f{}, dp = v16f{};
-#pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) {
-          s = mma16(qa[kk], f16 ? kh[kk] : kd[kk], s);
-          dp = mma16(da[kk], f16 ? vh[kk] : vd[kk], dp);
-        }
-        // this lane's queries q0 + hi*16 + ii: log2-domain LSE and row term
-        float L2[16], Dr[16];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const v4f l4 = ld4f(lrs, (q0 + hi * 16 + u * 4) * 4);
-          const v4f r4 = ld4f(rrs, (q0 + hi * 16 + u * 4) * 4);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            L2[u * 4 + e] = l4[e] * kLog2eB;
-            Dr[u * 4 + e] = r4[e];
-          }
-        }
-        float qa_s[16], qh_s[16];  // FP4 pairs: x = p * qa_s is P / 2^X of the MX group, pt = code * qh_s
-        if (!f16) {
-          v16f st = v16f{};
-#pragma unroll
-          for (int kk = 0; kk < D / 16; ++kk) st = mma16(kd[kk], qa[kk], st);
-          // column r32 is query qm; register ii is key w*32 + (ii/4)*8 + hi*4 + ii%4
-          float gm = -INFINITY;
-#pragma unroll
-          for (int ii = 0; ii < 16; ++ii) {
-            const int kx = j * kBlkK + w * 32 + (ii >> 2) * 8 + hi * 4 + (ii & 3);
-            const bool ok = qm < S && kx < S && !(a.causal && kx > qm);
-            gm = fmaxf(gm, ok ? st[ii] : -INFINITY);
-          }
-          gm = max_pair(gm);
-          const float Lq = qm < S ? a.lse[(size_t)bhq * S + qm] * kLog2eB : 0.0f;
-          // MX level 1 is any power of two (the E8M0 block scale absorbs it):
-          // z = ceil(L2); block exponent from the group maximum's probability
-          const float z = ceilf(Lq);
-          const uint32_t E = (__float_as_uint(ex2(__builtin_fmaf(gm, a.c, -z))) >> 23) & 0xFF;
-          const int X = (int)(E > 3 ? E - 2 : 1) - 127;
-          const float zx = z + (float)X;
-          const bool any = gm > -INFINITY;
-          if (hi == 0) {
-            sh_a[par][w][qperm(r32)] = any ? ex2(Lq - zx) : 0.0f;
-            sh_h[par][w][qperm(r32)] = any ? ex2(zx - Lq) : 0.0f;
-          }
-          __syncthreads();
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            const float4 a4 = *(const float4*)&sh_a[par][w][hi * 16 + u * 4];
-            const float4 h4 = *(const float4*)&sh_h[par][w][hi * 16 + u * 4];
-            qa_s[u * 4] = a4.x, qa_s[u * 4 + 1] = a4.y, qa_s[u * 4 + 2] = a4.z, qa_s[u * 4 + 3] = a4.w;
-            qh_s[u * 4] = h4.x, qh_s[u * 4 + 1] = h4.y, qh_s[u * 4 + 2] = h4.z, qh_s[u * 4 + 3] = h4.w;
-          }
-          par ^= 1;
-        }
-        // A operands of the two products: step st holds queries hi*16 + 8 st + u
-        v8h pA[2], sA[2];
-#pragma unroll
-        for (int ii = 0; ii < 16; ii += 2) {
-          float p[2], pt[2];
-#pragma unroll
-          for (int e = 0; e < 2; ++e) {
-            const int q = q0 + hi * 16 + ii + e;
-            const bool ok = q < S && key < S && !(a.causal && key > q);
-            p[e] = ok ? ex2(__builtin_fmaf(s[ii + e], a.c, -L2[ii + e])) : 0.0f;
-            sA[ii / 8][ii % 8 + e] = (_Float16)(p[e] * (dp[ii + e] - Dr[ii + e]));
-          }
-          if (f16) {
-            pt[0] = p[0], pt[1] = p[1];
-          } else {
-            const uint32_t y = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, p[0] * qa_s[ii], p[1] * qa_s[ii + 1],
-                                                                        1.0f, 0);
-            const v2f cv = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(y, 1.0f, 0);
-            pt[0] = cv[0] * qh_s[ii];
-            pt[1] = cv[1] * qh_s[ii + 1];
-          }
-          pA[ii / 8][ii % 8] = (_Float16)pt[0];
-          pA[ii / 8][ii % 8 + 1] = (_Float16)pt[1];
-        }
-        const _Float16* qT = (f16 ? a.qt : a.qdt) + (size_t)bhq * D * Sp;
-        const _Float16* oT = a.dot + (size_t)bhq * D * Sp;
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt) {
-            const size_t off = (size_t)(dt * 32 + r32) * Sp + q0 + hi * 16 + st * 8;
-            dv[dt] = mma16(pA[st], *(const v8h*)(oT + off), dv[dt]);
-            dk[dt] = mma16(sA[st], *(const v8h*)(qT + off), dk[dt]);
-          }
-      }
+    for (int u = 0; u < PR; ++u) {
+      const int c = t + u * 256;
+      const int row = c / (D / 8), c8 = c % (D / 8);  // row-major tiles
+      const int off = ((q0 + row) * D + c8 * 8) * 2;
+      if (need16) pq16[u] = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
+      if (needd) pqd[u] = __builtin_amdgcn_raw_buffer_load_b128(qdrs, off, 0, 0);
+      pdo[u] = __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0);
+      const int d = c / 4, c4 = c % 4;  // transposed tiles: row d, 8 queries
+      const size_t toff = tb + (size_t)d * Sp + q0 + c4 * 8;
+      if (need16) pt16[u] = *(const v4i*)(a.qt + toff);
+      if (needd) ptd[u] = *(const v4i*)(a.qdt + toff);
+      pdt[u] = *(const v4i*)(a.dot + toff);
     }
+    if (t < 32) {
+      const int q = q0 + t;
+      pl = q < S ? a.lse[(size_t)bhq * S + q] * kLog2eB : 0.0f;
+      pr = q < S ? a.drow[(size_t)bhq * S + q] : 0.0f;
+    }
+    return need16 * 2 + needd;
+  };
+  auto stash = [&](int need) {
+#pragma unroll
+    for (int u = 0; u < PR; ++u) {
+      const int c = t + u * 256;
+      const int row = c / (D / 8), c8 = c % (D / 8);
+      const int ro = (row * L::RR + c8 * 8) * 2;
+      if (need & 2) *(v4i*)(smem + L::QR16 + ro) = pq16[u];
+      if (need & 1) *(v4i*)(smem + L::QRD + ro) = pqd[u];
+      *(v4i*)(smem + L::DOR + ro) = pdo[u];
+      const int d = c / 4, c4 = c % 4;
+      const int to = (d * L::TR + c4 * 8) * 2;
+      if (need & 2) *(v4i*)(smem + L::QT16 + to) = pt16[u];
+      if (need & 1) *(v4i*)(smem + L::QTD + to) = ptd[u];
+      *(v4i*)(smem + L::DOT + to) = pdt[u];
+    }
+    if (t < 32) {
+      ((float*)(smem + L::L2))[t] = pl;
+      ((float*)(smem + L::DR))[t] = pr;
+    }
+  };
+
+  int need = nsteps > 0 ? fetch(0) : 0;
+  for (int n = 0; n < nsteps; ++n) {
+    const int g = n / nsteps_g, q0 = qstart + (n % nsteps_g) * 32, i = q0 / a.bq;
+    const int bhq = b * a.Hq + hk * G + g;
+    const bool f16 = kind(bhq, i, jb);
+    __syncthreads();  // every wave is done with the previous step
+    stash(need);
+    __syncthreads();
+    if (n + 1 < nsteps) need = fetch(n + 1);
+    if (a.causal && q0 + 31 < jb * kBlkK) continue;  // this wave's pairs are all masked
+    if ((int)f16 != cur) load_kv(f16);
+    const _Float16* qrow = (const _Float16*)(smem + (f16 ? L::QR16 : L::QRD)) + qperm(r32) * L::RR + hi * 8;
+    const _Float16* drow = (const _Float16*)(smem + L::DOR) + qperm(r32) * L::RR + hi * 8;
+    v16f s = v16f{}, dp = v16f{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk) {
+      s = mma16(*(const v8h*)(qrow + kk * 16), kr[kk], s);
+      dp = mma16(*(const v8h*)(drow + kk * 16), vr[kk], dp);
+    }
+    // FP4 pairs: per query, p * fa is P / 2^X of the MX group and pt = code * fh
+    const float* wa = (const float*)(smem + L::FA) + w * 32;
+    const float* wh = (const float*)(smem + L::FH) + w * 32;
+    if (!f16) {
+      v16f st = v16f{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) st = mma16(kr[kk], *(const v8h*)(qrow + kk * 16), st);
+      // column r32 is query q0 + qperm(r32); register ii is key (ii/4)*8 + hi*4 + ii%4 of the wave's 32
+      const int qm = q0 + qperm(r32);
+      float gm = -INFINITY;
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) {
+        const int kx = jb * kBlkK + (w & 1) * 32 + (ii >> 2) * 8 + hi * 4 + (ii & 3);
+        const bool ok = qm < S && kx < S && !(a.causal && kx > qm);
+        gm = fmaxf(gm, ok ? st[ii] : -INFINITY);
+      }
+      gm = max_pair(gm);
+      const float Lq = ((const float*)(smem + L::L2))[qperm(r32)];
+      // MX level 1 is any power of two (the E8M0 block scale absorbs it):
+      // z = ceil(L2); block exponent from the group maximum's probability
+      const float z = ceilf(Lq);
+      const uint32_t E = (__float_as_uint(ex2(__builtin_fmaf(gm, a.c, -z))) >> 23) & 0xFF;
+      const int X = (int)(E > 3 ? E - 2 : 1) - 127;
+      const float zx = z + (float)X;
+      const bool any = gm > -INFINITY;
+      if (hi == 0) {
+        ((float*)wa)[qperm(r32)] = any ? ex2(Lq - zx) : 0.0f;
+        ((float*)wh)[qperm(r32)] = any ? ex2(zx - Lq) : 0.0f;
+      }
+      // the wave reads back its own slot: its LDS operations complete in order
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    // A operands of the two products: step st holds queries hi*16 + 8 st + u;
+    // this lane's queries are q0 + hi*16 + ii, four at a time
+    v8h pA[2], sA[2];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const float4 l4 = *(const float4*)(smem + L::L2 + (hi * 16 + u * 4) * 4);
+      const float4 r4 = *(const float4*)(smem + L::DR + (hi * 16 + u * 4) * 4);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
+      float p[4], pt[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ii = u * 4 + e, q = q0 + hi * 16 + ii;
+        const bool ok = q < S && key < S && !(a.causal && key > q);
+        p[e] = ok ? ex2(__builtin_fmaf(s[ii], a.c, -lv[e])) : 0.0f;
+        sA[ii / 8][ii % 8] = (_Float16)(p[e] * (dp[ii] - rv[e]));
+        pt[e] = p[e];
+      }
+      if (!f16) {
+        const float4 a4 = *(const float4*)(wa + hi * 16 + u * 4);
+        const float4 h4 = *(const float4*)(wh + hi * 16 + u * 4);
+        const uint32_t y0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, p[0] * a4.x, p[1] * a4.y, 1.0f, 0);
+        const uint32_t y1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, p[2] * a4.z, p[3] * a4.w, 1.0f, 0);
+        const v2f c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(y0, 1.0f, 0);
+        const v2f c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(y1, 1.0f, 0);
+        pt[0] = c0[0] * h4.x;
+        pt[1] = c0[1] * h4.y;
+        pt[2] = c1[0] * h4.z;
+        pt[3] = c1[1] * h4.w;
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pA[(u * 4 + e) / 8][(u * 4 + e) % 8] = (_Float16)pt[e];
+    }
+    const _Float16* qT = (const _Float16*)(smem + (f16 ? L::QT16 : L::QTD));
+    const _Float16* oT = (const _Float16*)(smem + L::DOT);
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const int off = (dt * 32 + r32) * L::TR + hi * 16 + st * 8;
+        dv[dt] = mma16(pA[st], *(const v8h*)(oT + off), dv[dt]);
+        dk[dt] = mma16(sA[st], *(const v8h*)(qT + off), dk[dt]);
+      }
   }
-  // C layout: column d = dt*32 + r32, register ii is key w*32 + (ii/4)*8 + hi*4 + ii%4
+  // C layout: column d = dt*32 + r32, register ii is key (ii/4)*8 + hi*4 + ii%4 of the wave's 32
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int ii = 0; ii < 16; ++ii) {
-      const int kx = j * kBlkK + w * 32 + (ii >> 2) * 8 + hi * 4 + (ii & 3);
+      const int kx = jb * kBlkK + (w & 1) * 32 + (ii >> 2) * 8 + hi * 4 + (ii & 3);
       if (kx < S) {
         const size_t e = (bhk * S + kx) * D + dt * 32 + r32;
         a.dk[e] = dk[dt][ii] * a.sm_scale;
@@ -707,13 +778,13 @@ extern "C" thrift_status thrift_attention_bwd(
   a.out = dq;
   a.dk = dk;
   a.dv = dv;
-  const int kgrid = B * Hkv * cdiv(S, kBlkK);
+  const int kgrid = B * Hkv * cdiv(cdiv(S, kBlkK), 2);
   if (D == 128) {
     launch_row<128>(a, kModeDq, stream);
-    bwd_key_kernel<128><<<kgrid, 128, 0, stream>>>(a);
+    bwd_key_kernel<128><<<kgrid, 256, 0, stream>>>(a);
   } else {
     launch_row<64>(a, kModeDq, stream);
-    bwd_key_kernel<64><<<kgrid, 128, 0, stream>>>(a);
+    bwd_key_kernel<64><<<kgrid, 256, 0, stream>>>(a);
   }
   return launch_status();
 }
