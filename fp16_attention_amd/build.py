@@ -3,6 +3,9 @@
 Each HIP source is compiled for gfx950 only, in parallel, then linked into
 one shared library next to this file.  Packed fp32 instructions are turned
 off (-packed-fp32-ops): fp32 code stays on the scalar-per-lane VALU forms.
+The backward's kernels ask for the VGPR form of the matrix instructions:
+their products feed VALU work directly, and with results in accumulation
+registers the compiler copied every one of them back per tile.
 """
 import concurrent.futures as cf
 import os
@@ -17,10 +20,11 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["select.hip", "quantize.hip", "attention.hip", "backward.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"),
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
+EXTRA = {"backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
 
 
 def _compile(src: str, obj: str, verbose: bool) -> None:
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + FLAGS + EXTRA.get(src, []) + ["-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)

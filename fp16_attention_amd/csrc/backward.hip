@@ -465,7 +465,8 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     stash(need);
     __syncthreads();
     if (n + 1 < nsteps) need = fetch(n + 1);
-    if (a.causal && q0 + 31 < jb * kBlkK) continue;  // this wave's pairs are all masked
+    // (steps whose pairs are all masked for this wave add zeros: a branch
+    // around the products would make the compiler copy the accumulators)
     if ((int)f16 != cur) load_kv(f16);
     const _Float16* qrow = (const _Float16*)(smem + (f16 ? L::QR16 : L::QRD)) + qperm(r32) * L::RR + hi * 8;
     const _Float16* drow = (const _Float16*)(smem + L::DOR) + qperm(r32) * L::RR + hi * 8;
