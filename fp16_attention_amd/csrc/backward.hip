@@ -25,6 +25,8 @@ namespace thrift {
 namespace {
 
 constexpr int kBlkK = 64;  // key block
+constexpr int kMaxS = 262144;
+constexpr int kMaxKw = kMaxS / kBlkK / 32;  // promoted-bit words per query block row
 constexpr float kLog2eB = 1.44269504088896341f;
 
 typedef float v2f __attribute__((ext_vector_type(2)));
@@ -188,7 +190,8 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
   constexpr int PK = kBlkK * D / 8 / NT;  // 16-byte pieces of a K or V block per thread
   constexpr int PT = D * kBlkK / 8 / NT;  // of the transposed block
   __shared__ __attribute__((aligned(16))) char smem[L::SIZE];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, hi = lane >> 5, r32 = lane & 31;
+  __shared__ uint32_t pmw[kMaxKw];  // this row of promoted-block bits
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), hi = lane >> 5, r32 = lane & 31;
   const int BHq = a.B * a.Hq, G = a.Hq / a.Hkv;
   const int x = blockIdx.x;
   const int i = a.causal ? a.nq - 1 - x / BHq : x / BHq;  // longest rows first
@@ -227,9 +230,11 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
   const auto vdrs = rsrc(a.vd + bhk * Sp * D, Sp * D * 2);
   const uint32_t* pm = a.prom + ((size_t)bhq * a.nq + i) * a.nkw;
   const int nvalid = valid_kv_blocks(i, S, a.bq, kBlkK, a.causal);
+  for (int k = t; k < a.nkw; k += NT) pmw[k] = pm[k];
+  __syncthreads();
 
   v4i pk[PK], pv[PK], pt[PT];
-  auto promoted = [&](int j) { return ((pm[j >> 5] >> (j & 31)) & 1u) != 0; };
+  auto promoted = [&](int j) { return ((pmw[j >> 5] >> (j & 31)) & 1u) != 0; };
   auto fetch = [&](int j) {
     const bool f16 = promoted(j);
     const auto krs = f16 ? k16rs : kdrs;
@@ -364,7 +369,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   using L = KeyLds<D>;
   constexpr int PR = 32 * D / 8 / 256;  // 16-byte pieces of a 32-row tile per thread
   __shared__ __attribute__((aligned(16))) char smem[L::SIZE];
-  const int t = threadIdx.x, lane = t & 63, w = t >> 6, hi = lane >> 5, r32 = lane & 31;
+  const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), hi = lane >> 5, r32 = lane & 31;
   const int BHk = a.B * a.Hkv, G = a.Hq / a.Hkv;
   const int nk = cdiv(a.S, kBlkK);
   const int x = blockIdx.x;
@@ -400,15 +405,25 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   const int qstart = a.causal ? (j0 * kBlkK / 32) * 32 : 0;
   const int nsteps_g = cdiv(S - qstart, 32);
   const int nsteps = G * nsteps_g;
-  auto kind = [&](int bhq, int i, int j) {
-    return j < nk && ((a.prom[((size_t)bhq * a.nq + i) * a.nkw + (j >> 5)] >> (j & 31)) & 1u) != 0;
+  // the promoted bits of blocks j0 and j0+1 (one word: j0 is even) for step n,
+  // loaded two steps ahead so that no step waits for them
+  auto step_at = [&](int n, int& bhq, int& q0) {
+    const int g = n / nsteps_g;
+    q0 = qstart + (n - g * nsteps_g) * 32;
+    bhq = b * a.Hq + hk * G + g;
   };
+  auto word_addr = [&](int n) {
+    int bhq, q0;
+    step_at(n < nsteps ? n : nsteps - 1, bhq, q0);
+    return a.prom + ((size_t)bhq * a.nq + q0 / a.bq) * a.nkw + (j0 >> 5);
+  };
+  auto bit = [&](uint32_t word, int j) { return j < nk && ((word >> (j & 31)) & 1u) != 0; };
   v4i pq16[PR], pqd[PR], pdo[PR], pt16[PR], ptd[PR], pdt[PR];
   float pl = 0.0f, pr = 0.0f;
-  auto fetch = [&](int n) {
-    const int g = n / nsteps_g, q0 = qstart + (n % nsteps_g) * 32, i = q0 / a.bq;
-    const int bhq = b * a.Hq + hk * G + g;
-    const bool f0 = kind(bhq, i, j0), f1 = kind(bhq, i, j0 + 1);
+  auto fetch = [&](int n, uint32_t word) {
+    int bhq, q0;
+    step_at(n, bhq, q0);
+    const bool f0 = bit(word, j0), f1 = bit(word, j0 + 1);
     const bool need16 = f0 || f1, needd = !f0 || !f1;
     const auto qrs = rsrc(a.q16 + (size_t)bhq * S * D, S * D * 2);
     const auto qdrs = rsrc(a.qd + (size_t)bhq * S * D, S * D * 2);
@@ -456,15 +471,22 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     }
   };
 
-  int need = nsteps > 0 ? fetch(0) : 0;
+  uint32_t wcur = nsteps > 0 ? __builtin_amdgcn_readfirstlane(*word_addr(0)) : 0u;
+  uint32_t wnext = nsteps > 1 ? *word_addr(1) : 0u;  // in flight
+  int need = nsteps > 0 ? fetch(0, wcur) : 0;
   for (int n = 0; n < nsteps; ++n) {
-    const int g = n / nsteps_g, q0 = qstart + (n % nsteps_g) * 32, i = q0 / a.bq;
-    const int bhq = b * a.Hq + hk * G + g;
-    const bool f16 = kind(bhq, i, jb);
+    int bhq, q0;
+    step_at(n, bhq, q0);
+    const bool f16 = bit(wcur, jb);
     __syncthreads();  // every wave is done with the previous step
     stash(need);
     __syncthreads();
-    if (n + 1 < nsteps) need = fetch(n + 1);
+    if (n + 1 < nsteps) {
+      const uint32_t w1 = __builtin_amdgcn_readfirstlane(wnext);
+      wnext = *word_addr(n + 2);
+      need = fetch(n + 1, w1);
+      wcur = w1;
+    }
     // (steps whose pairs are all masked for this wave add zeros: a branch
     // around the products would make the compiler copy the accumulators)
     if ((int)f16 != cur) load_kv(f16);
@@ -614,7 +636,7 @@ thrift_status check_bwd(const void* q16, const void* k16, const void* v16, const
   if (!(sm_scale > 0.0f) || !(sm_scale < 1e30f)) return THRIFT_EINVAL;
   if (fmt != THRIFT_MXFP4) return THRIFT_EUNSUPPORTED;
   if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
-  if ((block_q != 64 && block_q != 128) || block_k != kBlkK) return THRIFT_EUNSUPPORTED;
+  if ((block_q != 64 && block_q != 128) || block_k != kBlkK || S > kMaxS) return THRIFT_EUNSUPPORTED;
   if ((size_t)S * D * 2 > 0x7fffffffu || (size_t)D * cdiv(S, kBlkK) * kBlkK * 2 > 0x7fffffffu)
     return THRIFT_EUNSUPPORTED;
   for (const void* p : {q16, k16, v16, (const void*)q4c, (const void*)k4c, (const void*)v4c, workspace})
