@@ -84,9 +84,9 @@ def load():
         L.thrift_attention_bwd_workspace_bytes.restype = SZ
         L.thrift_attention_bwd_workspace_bytes.argtypes = [I] * 6
         L.thrift_attention_fwd_hp.restype = I
-        L.thrift_attention_fwd_hp.argtypes = [P] * 9 + [I, P, P, I] + [I] * 8 + [F, P, P, P, SZ, P]
+        L.thrift_attention_fwd_hp.argtypes = [P] * 12 + [I, P, P, I] + [I] * 8 + [F, P, P, P, SZ, P]
         L.thrift_attention_bwd.restype = I
-        L.thrift_attention_bwd.argtypes = [P] * 9 + [I, P, P, I] + [I] * 8 + [F] + [P] * 7 + [SZ, P]
+        L.thrift_attention_bwd.argtypes = [P] * 12 + [I, P, P, I] + [I] * 8 + [F] + [P] * 7 + [SZ, P]
         L.thrift_status_string.restype = C.c_char_p
         L.thrift_status_string.argtypes = [I]
         _lib = L

@@ -274,7 +274,7 @@ def thrift_attention_bwd_workspace(B, Hq, Hkv, S, D, block_q=128, device="cuda")
 def thrift_attention_fwd_hp(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt, lse,
                             block_q=128, block_k=64, causal=True, sm_scale=None, workspace=None, out=None):
     """Attn-QAT's high-precision output O' (fp32 [B,Hq,S,D]): the forward with
-    the exact softmax probabilities, from the forward's lse.  MXFP4 only."""
+    the exact softmax probabilities, from the forward's lse."""
     B, Hq, S, D = q16.shape
     Hkv = k16.shape[1]
     if sm_scale is None:
@@ -289,7 +289,8 @@ def thrift_attention_fwd_hp(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4
     if out is None:
         out = torch.empty((B, Hq, S, D), dtype=torch.float32, device=q16.device)
     _call("thrift_attention_fwd_hp", _ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
-          _ptr(k4.codes), _ptr(k4.scales), _ptr(v4.codes), _ptr(v4.scales), q4.fmt, _ptr(idx), _ptr(cnt),
+          _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales), _ptr(k4.tensor_scale), _ptr(v4.codes),
+          _ptr(v4.scales), _ptr(v4.tensor_scale), q4.fmt, _ptr(idx), _ptr(cnt),
           idx.shape[-1], B, Hq, Hkv, S, D, block_q, block_k, int(causal), float(sm_scale), _ptr(lse),
           _ptr(out), _ptr(workspace), workspace.numel(), _stream())
     return out
@@ -298,7 +299,7 @@ def thrift_attention_fwd_hp(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4
 def thrift_attention_bwd(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt, lse, ohp,
                          do16, block_q=128, block_k=64, causal=True, sm_scale=None, workspace=None):
     """Attn-QAT backward: (dq fp32 [B,Hq,S,D], dk, dv fp32 [B,Hkv,S,D]) from the
-    output gradient do16, the forward's lse and O'.  MXFP4 only."""
+    output gradient do16, the forward's lse and O'."""
     B, Hq, S, D = q16.shape
     Hkv = k16.shape[1]
     if sm_scale is None:
@@ -316,7 +317,8 @@ def thrift_attention_bwd(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Ten
     dk = torch.empty((B, Hkv, S, D), dtype=torch.float32, device=dev)
     dv = torch.empty((B, Hkv, S, D), dtype=torch.float32, device=dev)
     _call("thrift_attention_bwd", _ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
-          _ptr(k4.codes), _ptr(k4.scales), _ptr(v4.codes), _ptr(v4.scales), q4.fmt, _ptr(idx), _ptr(cnt),
+          _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales), _ptr(k4.tensor_scale), _ptr(v4.codes),
+          _ptr(v4.scales), _ptr(v4.tensor_scale), q4.fmt, _ptr(idx), _ptr(cnt),
           idx.shape[-1], B, Hq, Hkv, S, D, block_q, block_k, int(causal), float(sm_scale), _ptr(lse),
           _ptr(ohp), _ptr(do16), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace), workspace.numel(), _stream())
     return dq, dk, dv

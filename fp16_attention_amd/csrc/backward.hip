@@ -71,36 +71,51 @@ struct BwdArgs {
   const _Float16 *kt, *kdt, *vt, *vdt;     // transposed [B,Hkv,D,Sp]
   const uint32_t* prom;                    // promoted-block bits [B,Hq,nq,nkw]
   const float *lse, *drow;                 // [B,Hq,S]
+  const float *tq, *tk, *tv;               // NVFP4 slice scales [B,H] (NULL for MXFP4)
   float* out;                              // row kernel: O' or dQ [B,Hq,S,D]
   float *dk, *dv;                          // [B,Hkv,S,D]
-  int B, Hq, Hkv, S, Sp, bq, nq, nkw, causal;
+  int B, Hq, Hkv, S, Sp, bq, nq, nkw, causal, fmt;
   float c;         // sm_scale * log2(e)
   float sm_scale;
 };
 
 // ---- preparation ------------------------------------------------------------------
 
-// MX-decoded FP4 rows to fp16: codes [R][L/2] (even element in the low
-// nibble), E8M0 scales [R][L/32]; one thread per 8 elements.  Out [R][L];
-// or, with vD > 0, rows are V's stored (batch*head, 64-token block, channel)
-// rows of L = 64 tokens and go to V^T [batch*head][vD][nb*64].
-// E2M1 times a power of two is exact in fp16 down to its subnormal range.
-__global__ __launch_bounds__(256) void decode_mx_kernel(const uint8_t* codes, const uint8_t* scales, size_t R,
-                                                        int L, _Float16* out, int vD, int vnb) {
+// E4M3 byte -> value (finite codes).
+__device__ inline float e4m3_value(uint32_t b) {
+  const uint32_t e = (b >> 3) & 0xF, m = b & 7;
+  const float v = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120) << 23) | (m << 20));
+  return (b & 0x80) ? -v : v;
+}
+
+// FP4 rows decoded to fp16: codes [R][L/2] (even element in the low
+// nibble), block scales [R][L/g] (MXFP4: E8M0, g = 32; NVFP4: E4M3, g = 16);
+// one thread per 8 elements.  Out [R][L]; or, with vD > 0, rows are V's
+// stored (batch*head, 64-token block, channel) rows of L = 64 tokens and go
+// to V^T [batch*head][vD][nb*64].  E2M1 times a power of two (MX) or times an
+// E4M3 value (NVFP4, at most 6 significant bits, 2^-10 .. 2688) is exact in
+// fp16; tsc (NVFP4 slice scales per batch*head of rows_per_bh rows, or
+// NULL) multiplies in before the one rounding.
+__global__ __launch_bounds__(256) void decode_fp4_kernel(const uint8_t* codes, const uint8_t* scales, size_t R,
+                                                         int L, int fmt, const float* tsc, size_t rows_per_bh,
+                                                         _Float16* out, int vD, int vnb) {
   const size_t e8 = (size_t)blockIdx.x * 256 + threadIdx.x;
   const size_t n8 = R * (size_t)(L / 8);
   if (e8 >= n8) return;
   const size_t row = e8 / (L / 8);
   const int c8 = (int)(e8 % (L / 8)) * 8;
   const uint32_t cw = *(const uint32_t*)(codes + row * (L / 2) + c8 / 2);
-  const int X = (int)scales[row * (L / 32) + c8 / 32] - 127;
+  const int g = fmt == THRIFT_MXFP4 ? 32 : 16;
+  const uint32_t sb = scales[row * (L / g) + c8 / g];
+  float f = fmt == THRIFT_MXFP4 ? ldexpf(1.0f, (int)sb - 127) : e4m3_value(sb);
+  if (tsc) f *= tsc[row / rows_per_bh];
   const v2f v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0),
                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1),
                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2),
                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 3)};
   v8h o;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = (_Float16)ldexpf(v[e / 2][e % 2], X);
+  for (int e = 0; e < 8; ++e) o[e] = (_Float16)(v[e / 2][e % 2] * f);
   size_t dst = row * L + c8;
   if (vD > 0) {
     const size_t d = row % vD, jb = (row / vD) % vnb, bh = row / ((size_t)vD * vnb);
@@ -109,10 +124,11 @@ __global__ __launch_bounds__(256) void decode_mx_kernel(const uint8_t* codes, co
   *(v8h*)(out + dst) = o;
 }
 
-// out[bh][c][r] = in[bh][r][c] for r < R, zero for R <= r < Rout; in rows of
-// C halves.  64x64 tiles through LDS.
+// out[bh][c][r] = in[bh][r][c] (times tsc[bh] when tsc is not NULL, one
+// rounding) for r < R, zero for R <= r < Rout; in rows of C halves.  64x64
+// tiles through LDS.
 __global__ __launch_bounds__(256) void transpose_kernel(const _Float16* in, int R, int C, int Rout,
-                                                        _Float16* out) {
+                                                        const float* tsc, _Float16* out) {
   __shared__ _Float16 tile[64][66];
   const size_t bh = blockIdx.y;
   const int ct = cdiv(C, 64);
@@ -127,7 +143,8 @@ __global__ __launch_bounds__(256) void transpose_kernel(const _Float16* in, int 
   _Float16* dst = out + bh * (size_t)C * Rout;
   for (int k = 0; k < 64; k += 4) {
     const int c = c0 + tr + k, r = r0 + tc;
-    if (c < C && r < Rout) dst[(size_t)c * Rout + r] = tile[tc][tr + k];
+    if (c < C && r < Rout)
+      dst[(size_t)c * Rout + r] = tsc ? (_Float16)((float)tile[tc][tr + k] * tsc[bh]) : tile[tc][tr + k];
   }
 }
 
@@ -219,6 +236,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
   }
   const float L2 = qok ? a.lse[(size_t)bhq * S + qrow] * kLog2eB : 0.0f;
   const float Dr = (MODE == kModeDq && qok) ? a.drow[(size_t)bhq * S + qrow] : 0.0f;
+  // NVFP4: FP4 pairs' scores and dP carry the slice scales (exact fp32 factors)
+  const float cq4 = a.tq ? a.c * a.tq[bhq] * a.tk[bhk] : a.c;
+  const float dpf4 = a.tv ? a.tv[bhk] : 1.0f;
 
   v16f acc[D / 32];
 #pragma unroll
@@ -303,9 +323,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
       for (int ii = 0; ii < 16; ++ii) {
         const int key = j * kBlkK + hi * 32 + mt * 16 + ii;
         const bool ok = qok && key < S && !(a.causal && key > qrow);
-        const float p = ok ? ex2(__builtin_fmaf(s[mt][ii], a.c, -L2)) : 0.0f;
+        const float p = ok ? ex2(__builtin_fmaf(s[mt][ii], f16 ? a.c : cq4, -L2)) : 0.0f;
         float v = p;
-        if constexpr (MODE == kModeDq) v = p * (dp[mt][ii] - Dr);
+        if constexpr (MODE == kModeDq) v = p * (dp[mt][ii] * (f16 ? 1.0f : dpf4) - Dr);
         pb[mt * 2 + ii / 8][ii % 8] = (_Float16)v;
       }
     const _Float16* ts = (const _Float16*)(smem + L::T);
@@ -336,7 +356,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
 // FP4-decoded, as needed), dO rows, their transposes, and the rows' LSE and
 // row terms; plus each wave's per-query MX factors.
 template <int D>
-struct KeyLds {
+struct KeyLds {  // (FA, FH: [wave][group][query]; HT: [wave][query] half-tile maxima, NVFP4)
   static constexpr int RR = D + 8;  // halves per query row
   static constexpr int TR = 32 + 8; // halves per transposed row (32 queries)
   static constexpr int QR16 = 0;
@@ -347,9 +367,10 @@ struct KeyLds {
   static constexpr int DOT = QTD + D * TR * 2;
   static constexpr int L2 = DOT + D * TR * 2;  // 32 floats
   static constexpr int DR = L2 + 32 * 4;       // 32 floats
-  static constexpr int FA = DR + 32 * 4;       // [4 waves][32] floats
-  static constexpr int FH = FA + 4 * 32 * 4;   // [4 waves][32] floats
-  static constexpr int SIZE = FH + 4 * 32 * 4;
+  static constexpr int FA = DR + 32 * 4;
+  static constexpr int FH = FA + 4 * 2 * 32 * 4;
+  static constexpr int HT = FH + 4 * 2 * 32 * 4;
+  static constexpr int SIZE = HT + 4 * 32 * 4;
 };
 
 // Workgroup = two key blocks (2 x 64 keys) of (batch, key head), four waves
@@ -364,7 +385,7 @@ struct KeyLds {
 // the key-major lanes through the wave's own LDS slot.  Then dV += pt^T dO
 // and dK += dS^T Q.  Only the K and V operands of the precision in use are
 // held in registers; they are reloaded when a step switches path.
-template <int D>
+template <int D, int FMT>
 __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   using L = KeyLds<D>;
   constexpr int PR = 32 * D / 8 / 256;  // 16-byte pieces of a 32-row tile per thread
@@ -377,7 +398,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   const size_t bhk = x % BHk;
   const int b = (int)(bhk / a.Hkv), hk = (int)(bhk % a.Hkv);
   const int S = a.S, Sp = a.Sp;
-  const int jb = j0 + (w >> 1);              // this wave's key block
+  const int jb = j0 + (w >> 1);              // this wave's key block (waves w, w ^ 1 share it)
   const int key = jb * kBlkK + (w & 1) * 32 + r32;  // this lane's key (column of S)
 
   const auto k16rs = rsrc(a.k16 + bhk * S * D, S * D * 2);
@@ -400,6 +421,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   v16f dk[D / 32], dv[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) dk[dt] = dv[dt] = v16f{};
+  const float dpf4 = a.tv ? a.tv[bhk] : 1.0f;
 
   // step sequence: for g < G, q0 from the first row that sees block j0, by 32
   const int qstart = a.causal ? (j0 * kBlkK / 32) * 32 : 0;
@@ -478,6 +500,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     int bhq, q0;
     step_at(n, bhq, q0);
     const bool f16 = bit(wcur, jb);
+    const float cq4 = a.tq ? a.c * a.tq[bhq] * a.tk[bhk] : a.c;
     __syncthreads();  // every wave is done with the previous step
     stash(need);
     __syncthreads();
@@ -498,37 +521,77 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
       s = mma16(*(const v8h*)(qrow + kk * 16), kr[kk], s);
       dp = mma16(*(const v8h*)(drow + kk * 16), vr[kk], dp);
     }
-    // FP4 pairs: per query, p * fa is P / 2^X of the MX group and pt = code * fh
-    const float* wa = (const float*)(smem + L::FA) + w * 32;
-    const float* wh = (const float*)(smem + L::FH) + w * 32;
+    // FP4 pairs: per query and P group, p * fa is the element over its block
+    // scale and pt = code * fh (this lane's key is in group grp of the wave)
+    const float cj = f16 ? a.c : cq4;
+    const int grp = FMT == THRIFT_MXFP4 ? 0 : r32 >> 4;
+    const float* wa = (const float*)(smem + L::FA) + (w * 2 + grp) * 32;
+    const float* wh = (const float*)(smem + L::FH) + (w * 2 + grp) * 32;
+    float gm0 = -INFINITY, gm1 = -INFINITY, Lq = 0.0f;  // group maxima (raw scores) of query qperm(r32)
     if (!f16) {
       v16f st = v16f{};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) st = mma16(kr[kk], *(const v8h*)(qrow + kk * 16), st);
       // column r32 is query q0 + qperm(r32); register ii is key (ii/4)*8 + hi*4 + ii%4 of the wave's 32
       const int qm = q0 + qperm(r32);
-      float gm = -INFINITY;
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) {
         const int kx = jb * kBlkK + (w & 1) * 32 + (ii >> 2) * 8 + hi * 4 + (ii & 3);
         const bool ok = qm < S && kx < S && !(a.causal && kx > qm);
-        gm = fmaxf(gm, ok ? st[ii] : -INFINITY);
+        const float v = ok ? st[ii] : -INFINITY;
+        if (ii < 8)
+          gm0 = fmaxf(gm0, v);
+        else
+          gm1 = fmaxf(gm1, v);
       }
-      gm = max_pair(gm);
-      const float Lq = ((const float*)(smem + L::L2))[qperm(r32)];
-      // MX level 1 is any power of two (the E8M0 block scale absorbs it):
-      // z = ceil(L2); block exponent from the group maximum's probability
-      const float z = ceilf(Lq);
-      const uint32_t E = (__float_as_uint(ex2(__builtin_fmaf(gm, a.c, -z))) >> 23) & 0xFF;
-      const int X = (int)(E > 3 ? E - 2 : 1) - 127;
-      const float zx = z + (float)X;
-      const bool any = gm > -INFINITY;
-      if (hi == 0) {
-        ((float*)wa)[qperm(r32)] = any ? ex2(Lq - zx) : 0.0f;
-        ((float*)wh)[qperm(r32)] = any ? ex2(zx - Lq) : 0.0f;
+      gm0 = max_pair(gm0);
+      gm1 = max_pair(gm1);
+      Lq = ((const float*)(smem + L::L2))[qperm(r32)];
+      if constexpr (FMT == THRIFT_MXFP4) {
+        // MX level 1 is any power of two (the E8M0 block scale absorbs it):
+        // z = ceil(L2); block exponent from the group maximum's probability
+        const float gm = fmaxf(gm0, gm1);
+        const float z = ceilf(Lq);
+        const uint32_t E = (__float_as_uint(ex2(__builtin_fmaf(gm, cj, -z))) >> 23) & 0xFF;
+        const int X = (int)(E > 3 ? E - 2 : 1) - 127;
+        const float zx = z + (float)X;
+        const bool any = gm > -INFINITY;
+        if (hi == 0) {
+          ((float*)wa)[qperm(r32)] = any ? ex2(Lq - zx) : 0.0f;
+          ((float*)wh)[qperm(r32)] = any ? ex2(zx - Lq) : 0.0f;
+        }
+        // the wave reads back its own slot: its LDS operations complete in order
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      } else {
+        if (hi == 0) ((float*)(smem + L::HT))[w * 32 + qperm(r32)] = fmaxf(gm0, gm1);
       }
-      // the wave reads back its own slot: its LDS operations complete in order
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    }
+    if constexpr (FMT == THRIFT_NVFP4) {
+      // level 1 of NVFP4 is the query's maximum over the whole 64-key tile:
+      // the two waves of the block exchange their halves (every wave passes
+      // this barrier on every step)
+      __syncthreads();
+      if (!f16) {
+        const float tm = fmaxf(fmaxf(gm0, gm1), ((const float*)(smem + L::HT))[(w ^ 1) * 32 + qperm(r32)]);
+        const float tml = tm * cj;
+        // a tile more than 2^60 below the row's total contributes nothing
+        const bool live = tm > -INFINITY && tml - Lq > -60.0f;
+#pragma unroll
+        for (int g = 0; g < 2; ++g) {
+          const float gv = 2688.0f * ex2(__builtin_fmaf(g ? gm1 : gm0, cj, -tml));
+          v2s_t sb = {0, 0};
+          sb = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(sb, fminf(gv * (1.0f / 6.0f), 448.0f), 0.0f, 1.0f, false);
+          const float s2 = e4m3_value((uint32_t)sb[0] & 0xFF);
+          const bool on = live && s2 > 0.0f;
+          if (hi == 0) {
+            float* fa = (float*)(smem + L::FA) + (w * 2 + g) * 32;
+            float* fh = (float*)(smem + L::FH) + (w * 2 + g) * 32;
+            fa[qperm(r32)] = on ? ex2(Lq - tml) * (2688.0f / s2) : 0.0f;
+            fh[qperm(r32)] = on ? s2 * ex2(tml - Lq) * (1.0f / 2688.0f) : 0.0f;
+          }
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      }
     }
     // A operands of the two products: step st holds queries hi*16 + 8 st + u;
     // this lane's queries are q0 + hi*16 + ii, four at a time
@@ -543,8 +606,8 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int ii = u * 4 + e, q = q0 + hi * 16 + ii;
         const bool ok = q < S && key < S && !(a.causal && key > q);
-        p[e] = ok ? ex2(__builtin_fmaf(s[ii], a.c, -lv[e])) : 0.0f;
-        sA[ii / 8][ii % 8] = (_Float16)(p[e] * (dp[ii] - rv[e]));
+        p[e] = ok ? ex2(__builtin_fmaf(s[ii], cj, -lv[e])) : 0.0f;
+        sA[ii / 8][ii % 8] = (_Float16)(p[e] * (dp[ii] * (f16 ? 1.0f : dpf4) - rv[e]));
         pt[e] = p[e];
       }
       if (!f16) {
@@ -623,18 +686,19 @@ BwdLayout bwd_layout(int B, int Hq, int Hkv, int S, int D, int bq) {
 }
 
 thrift_status check_bwd(const void* q16, const void* k16, const void* v16, const uint8_t* q4c,
-                        const uint8_t* q4s, const uint8_t* k4c, const uint8_t* k4s, const uint8_t* v4c,
-                        const uint8_t* v4s, thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                        const uint8_t* q4s, const float* q4t, const uint8_t* k4c, const uint8_t* k4s,
+                        const float* k4t, const uint8_t* v4c, const uint8_t* v4s, const float* v4t,
+                        thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax,
                         int B, int Hq, int Hkv, int S, int D, int block_q, int block_k, int causal,
                         float sm_scale, const float* lse, const void* workspace, size_t workspace_bytes) {
   if (!q16 || !k16 || !v16 || !q4c || !q4s || !k4c || !k4s || !v4c || !v4s || !idx || !cnt || !lse ||
       !workspace)
     return THRIFT_EINVAL;
   if (fmt != THRIFT_NVFP4 && fmt != THRIFT_MXFP4) return THRIFT_EINVAL;
+  if (fmt == THRIFT_NVFP4 && (!q4t || !k4t || !v4t)) return THRIFT_EINVAL;
   if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || kmax < 1 || Hq % Hkv != 0 || (causal != 0 && causal != 1))
     return THRIFT_EINVAL;
   if (!(sm_scale > 0.0f) || !(sm_scale < 1e30f)) return THRIFT_EINVAL;
-  if (fmt != THRIFT_MXFP4) return THRIFT_EUNSUPPORTED;
   if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
   if ((block_q != 64 && block_q != 128) || block_k != kBlkK || S > kMaxS) return THRIFT_EUNSUPPORTED;
   if ((size_t)S * D * 2 > 0x7fffffffu || (size_t)D * cdiv(S, kBlkK) * kBlkK * 2 > 0x7fffffffu)
@@ -646,23 +710,29 @@ thrift_status check_bwd(const void* q16, const void* k16, const void* v16, const
   return THRIFT_OK;
 }
 
-void launch_decode_mx(const uint8_t* codes, const uint8_t* scales, size_t R, int L, _Float16* out,
-                      hipStream_t stream, int vD = 0, int vnb = 0) {
+void launch_decode(const uint8_t* codes, const uint8_t* scales, size_t R, int L, int fmt, const float* tsc,
+                   size_t rows_per_bh, _Float16* out, hipStream_t stream, int vD = 0, int vnb = 0) {
   const size_t n8 = R * (size_t)(L / 8);
-  decode_mx_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, stream>>>(codes, scales, R, L, out, vD, vnb);
+  decode_fp4_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, stream>>>(codes, scales, R, L, fmt, tsc, rows_per_bh,
+                                                                       out, vD, vnb);
 }
 
-void launch_transpose(const _Float16* in, int BH, int R, int C, int Rout, _Float16* out, hipStream_t stream) {
+void launch_transpose(const _Float16* in, int BH, int R, int C, int Rout, _Float16* out, hipStream_t stream,
+                      const float* tsc = nullptr) {
   dim3 grid(cdiv(Rout > R ? Rout : R, 64) * cdiv(C, 64), BH);
-  transpose_kernel<<<grid, 256, 0, stream>>>(in, R, C, Rout, out);
+  transpose_kernel<<<grid, 256, 0, stream>>>(in, R, C, Rout, tsc, out);
 }
 
 // Fills the FP4-decoded and transposed operands both entry points share.
+// FP4-decoded operands keep NVFP4's slice scale out (exact fp16, the scale
+// applied to the fp32 scores and dP); the transposed copies that are only
+// ever the reduction-side operand (K^T for dQ, Q^T for dK, V^T for O')
+// carry it, rounded once.
 void prepare(BwdArgs& a, char* ws, const BwdLayout& l, const void* q16, const void* k16, const void* v16,
-             const uint8_t* q4c, const uint8_t* q4s, const uint8_t* k4c, const uint8_t* k4s,
-             const uint8_t* v4c, const uint8_t* v4s, const int32_t* idx, const int32_t* cnt, int kmax, int B,
-             int Hq, int Hkv, int S, int D, int block_q, int causal, float sm_scale, const float* lse,
-             bool backward, hipStream_t stream) {
+             const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c, const uint8_t* k4s,
+             const float* k4t, const uint8_t* v4c, const uint8_t* v4s, const float* v4t, int fmt,
+             const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D, int block_q,
+             int causal, float sm_scale, const float* lse, bool backward, hipStream_t stream) {
   const int Sp = cdiv(S, kBlkK) * kBlkK, nk = cdiv(S, kBlkK);
   a.q16 = (const _Float16*)q16;
   a.k16 = (const _Float16*)k16;
@@ -689,20 +759,27 @@ void prepare(BwdArgs& a, char* ws, const BwdLayout& l, const void* q16, const vo
   a.nq = cdiv(S, block_q);
   a.nkw = cdiv(nk, 32);
   a.causal = causal;
+  a.fmt = fmt;
+  const bool nv = fmt == THRIFT_NVFP4;
+  a.tq = nv ? q4t : nullptr;
+  a.tk = nv ? k4t : nullptr;
+  a.tv = nv ? v4t : nullptr;
   a.sm_scale = sm_scale;
   a.c = sm_scale * kLog2eB;
   const int BHq = B * Hq, BHk = B * Hkv;
-  launch_decode_mx(q4c, q4s, (size_t)BHq * S, D, (_Float16*)a.qd, stream);
-  launch_decode_mx(k4c, k4s, (size_t)BHk * S, D, (_Float16*)a.kd, stream);
-  launch_decode_mx(v4c, v4s, (size_t)BHk * nk * D, kBlkK, (_Float16*)a.vdt, stream, D, nk);  // to V^T
+  launch_decode(q4c, q4s, (size_t)BHq * S, D, fmt, nullptr, S, (_Float16*)a.qd, stream);
+  launch_decode(k4c, k4s, (size_t)BHk * S, D, fmt, nullptr, S, (_Float16*)a.kd, stream);
+  // V^T: with the slice scale for O' (reduction side), without for the rows of dP
+  launch_decode(v4c, v4s, (size_t)BHk * nk * D, kBlkK, fmt, backward ? nullptr : a.tv, (size_t)nk * D,
+                (_Float16*)a.vdt, stream, D, nk);
   const int nrows = BHq * a.nq;
   prom_bits_kernel<<<cdiv(nrows, 256), 256, 0, stream>>>(idx, cnt, nrows, kmax, nk, a.nkw, (uint32_t*)a.prom);
   if (backward) {
     launch_transpose(a.vdt, BHk, D, Sp, D, (_Float16*)a.vd, stream);  // [Sp][D]
     launch_transpose(a.q16, BHq, S, D, Sp, (_Float16*)a.qt, stream);
-    launch_transpose(a.qd, BHq, S, D, Sp, (_Float16*)a.qdt, stream);
+    launch_transpose(a.qd, BHq, S, D, Sp, (_Float16*)a.qdt, stream, a.tq);
     launch_transpose(a.k16, BHk, S, D, Sp, (_Float16*)a.kt, stream);
-    launch_transpose(a.kd, BHk, S, D, Sp, (_Float16*)a.kdt, stream);
+    launch_transpose(a.kd, BHk, S, D, Sp, (_Float16*)a.kdt, stream, a.tk);
   } else {
     launch_transpose(a.v16, BHk, S, D, Sp, (_Float16*)a.vt, stream);
   }
@@ -732,8 +809,10 @@ template __global__ void bwd_row_kernel<128, kModeOhp, 2>(BwdArgs);
 template __global__ void bwd_row_kernel<128, kModeDq, 2>(BwdArgs);
 template __global__ void bwd_row_kernel<64, kModeOhp, 2>(BwdArgs);
 template __global__ void bwd_row_kernel<64, kModeDq, 2>(BwdArgs);
-template __global__ void bwd_key_kernel<128>(BwdArgs);
-template __global__ void bwd_key_kernel<64>(BwdArgs);
+template __global__ void bwd_key_kernel<128, THRIFT_MXFP4>(BwdArgs);
+template __global__ void bwd_key_kernel<64, THRIFT_MXFP4>(BwdArgs);
+template __global__ void bwd_key_kernel<128, THRIFT_NVFP4>(BwdArgs);
+template __global__ void bwd_key_kernel<64, THRIFT_NVFP4>(BwdArgs);
 template __global__ void row_term_kernel<128>(const _Float16*, const float*, size_t, float*);
 template __global__ void row_term_kernel<64>(const _Float16*, const float*, size_t, float*);
 
@@ -750,20 +829,21 @@ extern "C" size_t thrift_attention_bwd_workspace_bytes(int B, int Hq, int Hkv, i
 
 extern "C" thrift_status thrift_attention_fwd_hp(
     const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes, const uint8_t* q4_scales,
-    const uint8_t* k4_codes, const uint8_t* k4_scales, const uint8_t* v4_codes, const uint8_t* v4_scales,
-    thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D,
+    const float* q4_tscale, const uint8_t* k4_codes, const uint8_t* k4_scales, const float* k4_tscale,
+    const uint8_t* v4_codes, const uint8_t* v4_scales, const float* v4_tscale, thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D,
     int block_q, int block_k, int causal, float sm_scale, const float* lse, float* ohp, void* workspace,
     size_t workspace_bytes, hipStream_t stream) {
-  thrift_status st = check_bwd(q16, k16, v16, q4_codes, q4_scales, k4_codes, k4_scales, v4_codes, v4_scales, fmt,
-                               idx, cnt, kmax, B, Hq, Hkv, S, D, block_q, block_k, causal, sm_scale, lse,
-                               workspace, workspace_bytes);
+  thrift_status st = check_bwd(q16, k16, v16, q4_codes, q4_scales, q4_tscale, k4_codes, k4_scales, k4_tscale,
+                               v4_codes, v4_scales, v4_tscale, fmt, idx, cnt, kmax, B, Hq, Hkv, S, D, block_q,
+                               block_k, causal, sm_scale, lse, workspace, workspace_bytes);
   if (st != THRIFT_OK) return st;
   if (!ohp) return THRIFT_EINVAL;
   if (!aligned16(ohp)) return THRIFT_EALIGN;
   const BwdLayout l = bwd_layout(B, Hq, Hkv, S, D, block_q);
   BwdArgs a{};
-  prepare(a, (char*)workspace, l, q16, k16, v16, q4_codes, q4_scales, k4_codes, k4_scales, v4_codes, v4_scales,
-          idx, cnt, kmax, B, Hq, Hkv, S, D, block_q, causal, sm_scale, lse, false, stream);
+  prepare(a, (char*)workspace, l, q16, k16, v16, q4_codes, q4_scales, q4_tscale, k4_codes, k4_scales, k4_tscale,
+          v4_codes, v4_scales, v4_tscale, fmt, idx, cnt, kmax, B, Hq, Hkv, S, D, block_q, causal, sm_scale, lse,
+          false, stream);
   a.out = ohp;
   if (D == 128)
     launch_row<128>(a, kModeOhp, stream);
@@ -774,13 +854,13 @@ extern "C" thrift_status thrift_attention_fwd_hp(
 
 extern "C" thrift_status thrift_attention_bwd(
     const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes, const uint8_t* q4_scales,
-    const uint8_t* k4_codes, const uint8_t* k4_scales, const uint8_t* v4_codes, const uint8_t* v4_scales,
-    thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D,
+    const float* q4_tscale, const uint8_t* k4_codes, const uint8_t* k4_scales, const float* k4_tscale,
+    const uint8_t* v4_codes, const uint8_t* v4_scales, const float* v4_tscale, thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D,
     int block_q, int block_k, int causal, float sm_scale, const float* lse, const float* ohp, const void* do16,
     float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  thrift_status st = check_bwd(q16, k16, v16, q4_codes, q4_scales, k4_codes, k4_scales, v4_codes, v4_scales, fmt,
-                               idx, cnt, kmax, B, Hq, Hkv, S, D, block_q, block_k, causal, sm_scale, lse,
-                               workspace, workspace_bytes);
+  thrift_status st = check_bwd(q16, k16, v16, q4_codes, q4_scales, q4_tscale, k4_codes, k4_scales, k4_tscale,
+                               v4_codes, v4_scales, v4_tscale, fmt, idx, cnt, kmax, B, Hq, Hkv, S, D, block_q,
+                               block_k, causal, sm_scale, lse, workspace, workspace_bytes);
   if (st != THRIFT_OK) return st;
   if (!ohp || !do16 || !dq || !dk || !dv) return THRIFT_EINVAL;
   for (const void* p : {(const void*)ohp, do16, (const void*)dq, (const void*)dk, (const void*)dv})
@@ -788,8 +868,8 @@ extern "C" thrift_status thrift_attention_bwd(
   const BwdLayout l = bwd_layout(B, Hq, Hkv, S, D, block_q);
   BwdArgs a{};
   char* ws = (char*)workspace;
-  prepare(a, ws, l, q16, k16, v16, q4_codes, q4_scales, k4_codes, k4_scales, v4_codes, v4_scales, idx, cnt, kmax,
-          B, Hq, Hkv, S, D, block_q, causal, sm_scale, lse, true, stream);
+  prepare(a, ws, l, q16, k16, v16, q4_codes, q4_scales, q4_tscale, k4_codes, k4_scales, k4_tscale, v4_codes,
+          v4_scales, v4_tscale, fmt, idx, cnt, kmax, B, Hq, Hkv, S, D, block_q, causal, sm_scale, lse, true, stream);
   const int Sp = a.Sp, BHq = B * Hq;
   a.do16 = (const _Float16*)do16;
   launch_transpose(a.do16, BHq, S, D, Sp, (_Float16*)a.dot, stream);
@@ -802,12 +882,19 @@ extern "C" thrift_status thrift_attention_bwd(
   a.dk = dk;
   a.dv = dv;
   const int kgrid = B * Hkv * cdiv(cdiv(S, kBlkK), 2);
+  const bool mx = fmt == THRIFT_MXFP4;
   if (D == 128) {
     launch_row<128>(a, kModeDq, stream);
-    bwd_key_kernel<128><<<kgrid, 256, 0, stream>>>(a);
+    if (mx)
+      bwd_key_kernel<128, THRIFT_MXFP4><<<kgrid, 256, 0, stream>>>(a);
+    else
+      bwd_key_kernel<128, THRIFT_NVFP4><<<kgrid, 256, 0, stream>>>(a);
   } else {
     launch_row<64>(a, kModeDq, stream);
-    bwd_key_kernel<64><<<kgrid, 256, 0, stream>>>(a);
+    if (mx)
+      bwd_key_kernel<64, THRIFT_MXFP4><<<kgrid, 256, 0, stream>>>(a);
+    else
+      bwd_key_kernel<64, THRIFT_NVFP4><<<kgrid, 256, 0, stream>>>(a);
   }
   return launch_status();
 }

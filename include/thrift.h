@@ -349,8 +349,9 @@ thrift_status thrift_attention_decode(const void* q16, const void* k16, const vo
  * precision): p = exp(sm_scale q.k - lse), dV[c] += pt dO[r],
  * dS = p (dO[r].v[c] - dO[r].O'[r]), dQ[r] += sm_scale dS k[c],
  * dK[c] += sm_scale dS q[r].  Training shape only: Sq = Sk = S.
- * Supported: THRIFT_MXFP4 (THRIFT_EUNSUPPORTED for NVFP4), D 64 or 128,
- * block_q 64 or 128, block_k 64. */
+ * Both formats; *_tscale are the NVFP4 slice scales (required for
+ * THRIFT_NVFP4, EINVAL if NULL; ignored for THRIFT_MXFP4).  Supported:
+ * D 64 or 128, block_q 64 or 128, block_k 64, S <= 262144. */
 
 /* Workspace bytes both calls below need: FP4-decoded and transposed fp16
  * copies of the operands, the promoted-block bit table and the row terms
@@ -364,9 +365,10 @@ size_t thrift_attention_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D
  * written.  The workspace contents are scratch. */
 thrift_status thrift_attention_fwd_hp(const void* q16, const void* k16, const void* v16,
                                       const uint8_t* q4_codes, const uint8_t* q4_scales,
-                                      const uint8_t* k4_codes, const uint8_t* k4_scales,
+                                      const float* q4_tscale, const uint8_t* k4_codes,
+                                      const uint8_t* k4_scales, const float* k4_tscale,
                                       const uint8_t* v4_codes, const uint8_t* v4_scales,
-                                      thrift_format fmt, const int32_t* idx, const int32_t* cnt,
+                                      const float* v4_tscale, thrift_format fmt, const int32_t* idx, const int32_t* cnt,
                                       int kmax, int B, int Hq, int Hkv, int S, int D, int block_q,
                                       int block_k, int causal, float sm_scale, const float* lse,
                                       float* ohp, void* workspace, size_t workspace_bytes,
@@ -377,9 +379,10 @@ thrift_status thrift_attention_fwd_hp(const void* q16, const void* k16, const vo
  * sharing a key head are summed into it).  Deterministic: no atomics. */
 thrift_status thrift_attention_bwd(const void* q16, const void* k16, const void* v16,
                                    const uint8_t* q4_codes, const uint8_t* q4_scales,
-                                   const uint8_t* k4_codes, const uint8_t* k4_scales,
+                                   const float* q4_tscale, const uint8_t* k4_codes,
+                                   const uint8_t* k4_scales, const float* k4_tscale,
                                    const uint8_t* v4_codes, const uint8_t* v4_scales,
-                                   thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                                   const float* v4_tscale, thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax,
                                    int B, int Hq, int Hkv, int S, int D, int block_q, int block_k,
                                    int causal, float sm_scale, const float* lse, const float* ohp,
                                    const void* do16, float* dq, float* dk, float* dv, void* workspace,

@@ -236,18 +236,20 @@ def test_backward_validation(lib):
     h = lib.thrift_attention_fwd_hp
 
     def call(q16=A, fmt=1, kmax=4, B=1, Hq=8, Hkv=2, S=512, D=128, bq=128, bk=64, causal=1, sm=0.088, lse=A,
-             ohp=A, do=A, dq=A, ws=A, wsb=1 << 40):
-        return f(q16, A, A, A, A, A, A, A, A, fmt, A, A, kmax, B, Hq, Hkv, S, D, bq, bk, causal, sm, lse, ohp,
-                 do, dq, A, A, ws, wsb, None)
+             ohp=A, do=A, dq=A, ws=A, wsb=1 << 40, tsc=None):
+        return f(q16, A, A, A, A, tsc, A, A, tsc, A, A, tsc, fmt, A, A, kmax, B, Hq, Hkv, S, D, bq, bk, causal, sm,
+                 lse, ohp, do, dq, A, A, ws, wsb, None)
 
-    def call_hp(q16=A, fmt=1, D=128, lse=A, ohp=A, ws=A, wsb=1 << 40):
-        return h(q16, A, A, A, A, A, A, A, A, fmt, A, A, 4, 1, 8, 2, 512, D, 128, 64, 1, 0.088, lse, ohp, ws, wsb,
-                 None)
+    def call_hp(q16=A, fmt=1, D=128, lse=A, ohp=A, ws=A, wsb=1 << 40, tsc=None):
+        return h(q16, A, A, A, A, tsc, A, A, tsc, A, A, tsc, fmt, A, A, 4, 1, 8, 2, 512, D, 128, 64, 1, 0.088, lse,
+                 ohp, ws, wsb, None)
 
     for bad in (dict(q16=None), dict(lse=None), dict(ohp=None), dict(do=None), dict(dq=None), dict(ws=None),
                 dict(fmt=5), dict(Hkv=3), dict(S=0), dict(causal=2), dict(sm=0.0)):
         assert call(**bad) == 1, bad
-    assert call(fmt=0) == 2  # NVFP4: not supported by the backward
+    assert call(fmt=0) == 1  # NVFP4 needs its slice scales
+    assert call(fmt=0, tsc=A, wsb=16) == 4
+    assert call(S=262145) == 2
     assert call(D=96) == 2
     assert call(bq=32) == 2
     assert call(bk=128) == 2
@@ -256,7 +258,8 @@ def test_backward_validation(lib):
     assert call(wsb=16) == 4
     assert call_hp(ohp=None) == 1
     assert call_hp(lse=None) == 1
-    assert call_hp(fmt=0) == 2
+    assert call_hp(fmt=0) == 1
+    assert call_hp(fmt=0, tsc=A, wsb=16) == 4
     assert call_hp(ohp=A + 8) == 3
     assert call_hp(wsb=16) == 4
     need = lib.thrift_attention_bwd_workspace_bytes(1, 8, 2, 512, 128, 128)
