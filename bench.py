@@ -20,8 +20,10 @@ sys.path.insert(0, ROOT)
 
 # committed profiler counters, per (workload, format) that has them
 TRAFFIC_FILES = {("long", "mx"): os.path.join(ROOT, "profiles", "attn_fwd_kernel_long_mx_traffic.txt"),
-                 ("decode", "mx"): os.path.join(ROOT, "profiles", "decode_kernels_decode_mx_traffic.txt")}
+                 ("decode", "mx"): os.path.join(ROOT, "profiles", "decode_kernels_decode_mx_traffic.txt"),
+                 ("prefill_bwd", "mx"): os.path.join(ROOT, "profiles", "backward_kernels_prefill_mx_traffic.txt")}
 KERNEL_SRC = os.path.join(ROOT, "fp16_attention_amd", "csrc", "attention.hip")
+BWD_SRC = os.path.join(ROOT, "fp16_attention_amd", "csrc", "backward.hip")
 
 P_FP4 = 10.1e15   # MI355X dense MXFP4 MFMA, FLOP/s
 P_FP16 = 2.5e15   # MI355X dense FP16 MFMA, FLOP/s
@@ -61,7 +63,7 @@ def promoted_pairs(idx, cnt, S, bq, bk, causal):
     return total
 
 
-def measured_traffic(workload, fmt_name):
+def measured_traffic(workload, fmt_name, src=KERNEL_SRC):
     """HBM bytes per forward from the committed profiler counters
     (FETCH_SIZE + WRITE_SIZE, each scaled by its reading on a copy kernel of
     known size), or None when none were taken on this workload or they were
@@ -77,7 +79,7 @@ def measured_traffic(workload, fmt_name):
             if ":" in ln and not ln.startswith((" ", "#", "|")):
                 k, v = ln.split(":", 1)
                 rec[k.strip()] = v.strip()
-    with open(KERNEL_SRC, "rb") as f:
+    with open(src, "rb") as f:
         h = hashlib.sha256(f.read()).hexdigest()
     if rec.get("kernel_source_sha256") != h:
         return None
@@ -383,15 +385,15 @@ def run_backward(args, w, d, gen_s):
     (Q, K, V, their FP4 copies, the selection, the forward's lse and O', and
     an output gradient dO ~ N(0, 1)).  Algorithmic flops: five products of
     2 D flops per unmasked pair (recomputed scores, dP, dV, dK, dQ), all on the
-    fp16 matrix cores (MX-decoded FP4 operands are exact in fp16)."""
+    fp16 matrix cores (FP4-decoded operands are exact in fp16; NVFP4's slice
+    scales enter as fp32 factors).  roofline: the whole backward call (operand
+    preparation and its kernels) against the fp16 peak; traffic: the HBM bytes
+    of all its kernels."""
     import torch
 
     from fp16_attention_amd import api
 
-    if args.fmt != "mx":
-        print("bench.py: the backward pass supports MXFP4 only", file=sys.stderr)
-        sys.exit(2)
-    fmt = api.THRIFT_MXFP4
+    fmt = api.THRIFT_MXFP4 if args.fmt == "mx" else api.THRIFT_NVFP4
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v"))
     rng = np.random.default_rng(w.seed + 1)
@@ -453,20 +455,21 @@ def run_backward(args, w, d, gen_s):
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp16 (MX-decoded FP4 operands)",
+        "dtype": "fp16 (FP4-decoded operands)",
         "data": "synthetic",
         "config": {"workload": f"{w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} S{w.S} D{w.D} "
                                f"{'causal' if w.causal else 'non-causal'} blocks {w.bq}x{w.bk} "
-                               f"top-k {w.topk_bp / 100}% mx, backward",
+                               f"top-k {w.topk_bp / 100}% {args.fmt}, backward",
                    "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)"},
         "roofline": {"bound": "mfma", "achieved": round(achieved / 1e12, 2), "peak": P_FP16 / 1e12,
-                     "unit": "TFLOP/s", "frac": round(achieved / P_FP16, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / P_FP16, 4),
+                     "traffic": measured_traffic(w.name + "_bwd", args.fmt, BWD_SRC),
                      "kernel": "thrift_attention_bwd (operand preparation, bwd_row_kernel, bwd_key_kernel)"},
         "breakdown_ms": {"attention_bwd": round(bwd_ms, 4), "fwd_hp_O_prime": round(hp_ms, 4)},
         "input_gen_s": round(gen_s, 1),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline_bwd(w, d, do_h)
+        line["cpu_baseline"] = cpu_baseline_bwd(w, d, do_h, fmt)
     s = json.dumps(line)
     print(s, flush=True)
     if args.out:
@@ -474,7 +477,7 @@ def run_backward(args, w, d, gen_s):
             f.write(s + "\n")
 
 
-def cpu_baseline_bwd(w, d, do_h):
+def cpu_baseline_bwd(w, d, do_h, fmt):
     """The oracle's backward of query head 0 and its key head (one head per key
     head in this workload): selection, quantisation, the forward with O' and
     the backward over every query and key block of that head."""
@@ -489,7 +492,7 @@ def cpu_baseline_bwd(w, d, do_h):
     O.lib()
     t0 = time.perf_counter()
     idx, cnt, _ = O.select(q1, k1, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
-    q4, k4, v4 = (O.quantize(x, ax, O.MX) for x, ax in ((q1, O.AXIS_D), (k1, O.AXIS_D), (v1, O.AXIS_S)))
+    q4, k4, v4 = (O.quantize(x, ax, fmt) for x, ax in ((q1, O.AXIS_D), (k1, O.AXIS_D), (v1, O.AXIS_S)))
     _, lse, ohp = O.attention_hp(q1, k1, v1, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal)
     O.attention_bwd(q1, k1, v1, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal, lse, ohp, do1)
     sec = time.perf_counter() - t0
