@@ -117,7 +117,8 @@ def main():
     ap.add_argument("--workload", default=None, help="default: long (forward), prefill (--pass bwd)")
     ap.add_argument("--pass", dest="pass_", default="fwd", choices=["fwd", "bwd"],
                     help="fwd: the forward path (default); bwd: the Attn-QAT backward pass")
-    ap.add_argument("--fmt", default="mx", choices=["mx", "nvfp4"])
+    ap.add_argument("--fmt", default="mx", choices=["mx", "nvfp4", "nvfp4_mxp"],
+                    help="nvfp4_mxp: NVFP4 Q/K/V with P quantised MX-style (forward only)")
     ap.add_argument("--topk-bp", type=int, default=None)
     ap.add_argument("--budget", default="block", choices=["block", "head"],
                     help="top-k per query block (default) or one budget per query head")
@@ -144,6 +145,10 @@ def main():
     if args.topk_bp is not None:
         w = w.with_(topk_count=-1, topk_bp=args.topk_bp)
     fmt = api.THRIFT_MXFP4 if args.fmt == "mx" else api.THRIFT_NVFP4
+    p_fmt = api.THRIFT_MXFP4 if args.fmt == "nvfp4_mxp" else None
+    if p_fmt is not None and (args.pass_ == "bwd" or W.WORKLOADS[args.workload].Sq):
+        print("bench.py: nvfp4_mxp is a forward variant (prefill shape only)", file=sys.stderr)
+        sys.exit(2)
     t0 = time.time()
     d = W.generate(w)
     gen_s = time.time() - t0
@@ -178,7 +183,7 @@ def main():
         idx, cnt = select(qbar, kbar, w.S, w.S, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp, kmax)
         if rec:
             rec[2].record()
-        api.thrift_attention_fwd(q, k, v, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal, out=o)
+        api.thrift_attention_fwd(q, k, v, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal, out=o, p_fmt=p_fmt)
         if rec:
             rec[3].record()
         return idx, cnt
@@ -220,7 +225,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "mxfp4+fp16" if fmt == api.THRIFT_MXFP4 else "nvfp4(fp16 math)+fp16",
+        "dtype": ("mxfp4+fp16" if fmt == api.THRIFT_MXFP4 else
+                  "nvfp4 q/k/v, mx p (fp16 math)+fp16" if p_fmt is not None else "nvfp4(fp16 math)+fp16"),
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} S{w.S} D{w.D} "
@@ -248,7 +254,7 @@ def main():
         "input_gen_s": round(gen_s, 1),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, d, fmt, args.budget)
+        line["cpu_baseline"] = cpu_baseline(w, d, fmt, args.budget, p_fmt)
     s = json.dumps(line)
     print(s, flush=True)
     if args.out:
@@ -504,7 +510,7 @@ def cpu_baseline_bwd(w, d, do_h, fmt):
                       f"fp64"}
 
 
-def cpu_baseline(w, d, fmt, budget="block"):
+def cpu_baseline(w, d, fmt, budget="block", p_fmt=None):
     """The oracle on one query head (and its key head) of the same workload:
     selection, quantisation of that head's Q, K, V and the forward pass."""
     from oracle import oracle as O
@@ -518,9 +524,9 @@ def cpu_baseline(w, d, fmt, budget="block"):
     if budget == "head":
         idx, cnt = O.select_head(q1, k1, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
         q4, k4, v4 = (O.quantize(x, ax, fmt) for x, ax in ((q1, O.AXIS_D), (k1, O.AXIS_D), (v1, O.AXIS_S)))
-        O.attention(q1, k1, v1, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal)
+        O.attention(q1, k1, v1, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal, p_fmt=p_fmt)
     else:
-        O.pipeline(q1, k1, v1, fmt, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
+        O.pipeline(q1, k1, v1, fmt, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp, p_fmt=p_fmt)
     sec = time.perf_counter() - t0
     f = 4.0 * w.D * unmasked_pairs(w.S, w.causal)
     return {"value": round(f / sec / 1e12, 5), "unit": "TFLOP/s", "cores": nthreads,

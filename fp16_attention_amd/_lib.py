@@ -6,7 +6,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libthrift.so")
 
 THRIFT_OK, THRIFT_EINVAL, THRIFT_EUNSUPPORTED, THRIFT_EALIGN, THRIFT_EWORKSPACE, THRIFT_EHIP = range(6)
-THRIFT_NVFP4, THRIFT_MXFP4 = 0, 1
+THRIFT_NVFP4, THRIFT_MXFP4, THRIFT_NVFP4_MXP = 0, 1, 2
 THRIFT_GROUP_D, THRIFT_GROUP_S = 0, 1
 
 EXPORTS = ("thrift_select_kmax", "thrift_select_workspace_bytes", "thrift_select_blocks",

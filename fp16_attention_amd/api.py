@@ -13,7 +13,7 @@ from dataclasses import dataclass
 import torch
 
 from . import _lib
-from ._lib import THRIFT_GROUP_D, THRIFT_GROUP_S, THRIFT_MXFP4, THRIFT_NVFP4, ThriftError
+from ._lib import THRIFT_GROUP_D, THRIFT_GROUP_S, THRIFT_MXFP4, THRIFT_NVFP4, THRIFT_NVFP4_MXP, ThriftError
 
 __all__ = ["thrift_select_kmax", "thrift_select_blocks", "thrift_block_means",
            "thrift_select_blocks_kbar", "thrift_select_blocks_means", "thrift_select_blocks_head",
@@ -21,7 +21,7 @@ __all__ = ["thrift_select_kmax", "thrift_select_blocks", "thrift_block_means",
            "thrift_quantize_fp4_means", "thrift_quantize_fp4_range", "thrift_cache_update",
            "thrift_attention_fwd", "thrift_attention_decode", "thrift_decode", "FP4Tensor",
            "fp4_transposed", "thrift_forward", "thrift_attention_bwd_workspace", "thrift_attention_fwd_hp",
-           "thrift_attention_bwd", "THRIFT_NVFP4", "THRIFT_MXFP4", "THRIFT_GROUP_D",
+           "thrift_attention_bwd", "THRIFT_NVFP4", "THRIFT_MXFP4", "THRIFT_NVFP4_MXP", "THRIFT_GROUP_D",
            "THRIFT_GROUP_S", "ThriftError"]
 
 
@@ -241,8 +241,9 @@ def fp4_transposed(t: FP4Tensor):
 
 def thrift_attention_fwd(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt,
                          block_q=128, block_k=64, causal=True, sm_scale=None, out_fp32=False,
-                         with_lse=False, out=None):
-    """Mixed FP4/FP16 forward.  Returns o (and lse if with_lse)."""
+                         with_lse=False, out=None, p_fmt=None):
+    """Mixed FP4/FP16 forward.  Returns o (and lse if with_lse).  p_fmt=THRIFT_MXFP4
+    with NVFP4 tensors quantises P MX-style (the THRIFT_NVFP4_MXP variant)."""
     B, Hq, S = q4.codes.shape[:3]
     D = q4.codes.shape[3] * 2
     Hkv = k4.codes.shape[1]
@@ -259,7 +260,8 @@ def thrift_attention_fwd(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Ten
     lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev) if with_lse else None
     _call("thrift_attention_fwd", _ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes),
           _ptr(q4.scales), _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales),
-          _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales), _ptr(v4.tensor_scale), q4.fmt,
+          _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales), _ptr(v4.tensor_scale),
+          THRIFT_NVFP4_MXP if (q4.fmt == THRIFT_NVFP4 and p_fmt == THRIFT_MXFP4) else q4.fmt,
           _ptr(idx), _ptr(cnt), idx.shape[-1], B, Hq, Hkv, S, D, block_q, block_k, int(causal),
           float(sm_scale), _ptr(out), int(out.dtype == torch.float32), _ptr(lse), _stream())
     return (out, lse) if with_lse else out

@@ -446,6 +446,54 @@ __device__ inline void fp4_nv_softmax_pv(RowState<D>& st, v16f s[2], const char*
   pv_f16<D>(st, (const _Float16*)(stage + Lds<D>::VT), pB, lane);
 }
 
+// The variant's FP4 tile: NVFP4 Q, K, V (dequantised to fp16 in the stage),
+// P quantised MX-style: level 1 the integer running offset m (lazy rescale),
+// level 2 an E8M0 scale per 32 keys (this lane's keys are one group), codes
+// back to fp16 (code * 2^X, exact down to fp16's subnormal range) for the
+// fp16 PV product.  V's slice scale is applied once at the end (st.g).
+template <int D>
+__device__ inline void fp4_nvmxp_tile(RowState<D>& st, const char* stage, const v8h* qh, float c, int key0,
+                                      int qrow, int S, int causal, bool need_mask, int lane) {
+  const int hi = lane >> 5;
+  v16f s[2];
+  qk_f16<D>(s, stage, qh, lane);
+  if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
+  const float gmax = fmaxf(max16(s[0]), max16(s[1]));
+  maybe_rescale<D>(st, gmax, c);
+  const float nm = -st.m;
+  float lsum = 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = exp2_fast(__builtin_fmaf(s[mt][i], c, nm));
+      s[mt][i] = p;
+      lsum += p;
+    }
+  st.l += lsum;
+  // E8M0 exponent floor(log2(max p)) - 2, as on the MX path
+  const uint32_t E = (__float_as_uint(exp2_fast(__builtin_fmaf(gmax, c, nm))) >> 23) & 0xFF;
+  const uint32_t psc = E > 3 ? E - 2 : 1;
+  const float sf = __uint_as_float(psc << 23);
+  v8h pB[4];
+#pragma unroll
+  for (int stp = 0; stp < 4; ++stp) {  // keys hi*32 + 8 stp + u: registers 8 (stp % 2) + u of tile stp / 2
+    const v16f& x = s[stp >> 1];
+    const int o = (stp & 1) * 8;
+    uint32_t cw = 0;
+    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, x[o + 0], x[o + 1], sf, 0);
+    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, x[o + 2], x[o + 3], sf, 1);
+    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, x[o + 4], x[o + 5], sf, 2);
+    cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, x[o + 6], x[o + 7], sf, 3);
+    const v2h h0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sf, 0);
+    const v2h h1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sf, 1);
+    const v2h h2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sf, 2);
+    const v2h h3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, sf, 3);
+    pB[stp] = v8h{h0.x, h0.y, h1.x, h1.y, h2.x, h2.y, h3.x, h3.y};
+  }
+  pv_f16<D>(st, (const _Float16*)(stage + Lds<D>::VT), pB, lane);
+}
+
 template <int D>
 __device__ inline void fp4_nv_tile(RowState<D>& st, const char* stage, const v8h* qh, float c,
                                    float sv, int key0, int qrow, int S, int causal, bool need_mask,
@@ -886,6 +934,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
       }
       const float c = a.sm_log2 * a.q4t[bhq] * a.k4t[bhk];
       const float sv = a.v4t[bhk];
+      if constexpr (FMT == THRIFT_NVFP4_MXP) st.g = sv;  // acc holds O^T / sv
       Nv4Stager<D, NT> stg;
       if (jc < nvalid) {
         stg.load(a, bhk, jc, t);
@@ -899,8 +948,12 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
         const int key0 = jc * kBk;
         const bool active = !a.causal || key0 <= q0 + 31;
         const bool need_mask = (a.causal && key0 + kBk - 1 > q0) || key0 + kBk > S;
-        if (active)
-          fp4_nv_tile<D>(st, smem + buf * L::STAGE, qh, c, sv, key0, qrow, S, a.causal, need_mask, lane);
+        if (active) {
+          if constexpr (FMT == THRIFT_NVFP4)
+            fp4_nv_tile<D>(st, smem + buf * L::STAGE, qh, c, sv, key0, qrow, S, a.causal, need_mask, lane);
+          else
+            fp4_nvmxp_tile<D>(st, smem + buf * L::STAGE, qh, c, key0, qrow, S, a.causal, need_mask, lane);
+        }
         if (jn < nvalid) stg.store(smem + (buf ^ 1) * L::STAGE, t);
         __syncthreads();
         buf ^= 1;
@@ -1432,6 +1485,10 @@ template __global__ void attn_fwd_kernel<128, 4, THRIFT_NVFP4>(AttnArgs);
 template __global__ void attn_fwd_kernel<128, 2, THRIFT_NVFP4>(AttnArgs);
 template __global__ void attn_fwd_kernel<64, 4, THRIFT_NVFP4>(AttnArgs);
 template __global__ void attn_fwd_kernel<64, 2, THRIFT_NVFP4>(AttnArgs);
+template __global__ void attn_fwd_kernel<128, 4, THRIFT_NVFP4_MXP>(AttnArgs);
+template __global__ void attn_fwd_kernel<128, 2, THRIFT_NVFP4_MXP>(AttnArgs);
+template __global__ void attn_fwd_kernel<64, 4, THRIFT_NVFP4_MXP>(AttnArgs);
+template __global__ void attn_fwd_kernel<64, 2, THRIFT_NVFP4_MXP>(AttnArgs);
 template __global__ void decode_mx_fused_kernel<128>(DecodeArgs, int, int);
 template __global__ void decode_mx_fused_kernel<64>(DecodeArgs, int, int);
 template __global__ void decode_nv4_kernel<128>(DecodeArgs);
@@ -1455,8 +1512,8 @@ extern "C" thrift_status thrift_attention_fwd(
   if (!q4_codes || !q4_scales || !k4_codes || !k4_scales || !v4_codes || !v4_scales || !idx ||
       !cnt || !o)
     return THRIFT_EINVAL;
-  if (fmt != THRIFT_NVFP4 && fmt != THRIFT_MXFP4) return THRIFT_EINVAL;
-  if (fmt == THRIFT_NVFP4 && (!q4_tscale || !k4_tscale || !v4_tscale)) return THRIFT_EINVAL;
+  if (fmt != THRIFT_NVFP4 && fmt != THRIFT_MXFP4 && fmt != THRIFT_NVFP4_MXP) return THRIFT_EINVAL;
+  if (fmt != THRIFT_MXFP4 && (!q4_tscale || !k4_tscale || !v4_tscale)) return THRIFT_EINVAL;
   if (B < 1 || Hq < 1 || Hkv < 1 || S < 1 || kmax < 1 || (causal != 0 && causal != 1)) return THRIFT_EINVAL;
   if (Hq % Hkv != 0 || (o_is_fp32 != 0 && o_is_fp32 != 1)) return THRIFT_EINVAL;
   if (!(sm_scale > 0.0f) || !(sm_scale < 1e30f)) return THRIFT_EINVAL;
@@ -1499,6 +1556,10 @@ extern "C" thrift_status thrift_attention_fwd(
   if (fmt == THRIFT_MXFP4) {
     if (D == 128) return block_q == 128 ? launch_attn<128, 4, THRIFT_MXFP4>(a, stream) : launch_attn<128, 2, THRIFT_MXFP4>(a, stream);
     return block_q == 128 ? launch_attn<64, 4, THRIFT_MXFP4>(a, stream) : launch_attn<64, 2, THRIFT_MXFP4>(a, stream);
+  }
+  if (fmt == THRIFT_NVFP4_MXP) {
+    if (D == 128) return block_q == 128 ? launch_attn<128, 4, THRIFT_NVFP4_MXP>(a, stream) : launch_attn<128, 2, THRIFT_NVFP4_MXP>(a, stream);
+    return block_q == 128 ? launch_attn<64, 4, THRIFT_NVFP4_MXP>(a, stream) : launch_attn<64, 2, THRIFT_NVFP4_MXP>(a, stream);
   }
   if (D == 128) return block_q == 128 ? launch_attn<128, 4, THRIFT_NVFP4>(a, stream) : launch_attn<128, 2, THRIFT_NVFP4>(a, stream);
   return block_q == 128 ? launch_attn<64, 4, THRIFT_NVFP4>(a, stream) : launch_attn<64, 2, THRIFT_NVFP4>(a, stream);

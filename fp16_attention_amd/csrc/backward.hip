@@ -59,9 +59,6 @@ __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
 __device__ inline v8h ld8h(__amdgpu_buffer_rsrc_t rs, int off) {
   return __builtin_bit_cast(v8h, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
 }
-__device__ inline v4f ld4f(__amdgpu_buffer_rsrc_t rs, int off) {
-  return __builtin_bit_cast(v4f, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, 0));
-}
 
 struct BwdArgs {
   const _Float16 *q16, *k16, *v16, *do16;  // [B,H,S,D]

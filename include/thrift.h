@@ -63,8 +63,12 @@ typedef enum {
  *     floor(log2 amax_block) - 2, element = E2M1(x / 2^exponent); this is the
  *     layout gfx950's block-scaled FP4 matrix instructions consume.
  * All roundings are to nearest, ties to even, saturating (E2M1 at 6, E4M3 at
- * 448); the sign of a value that rounds to zero is kept. */
-typedef enum { THRIFT_NVFP4 = 0, THRIFT_MXFP4 = 1 } thrift_format;
+ * 448); the sign of a value that rounds to zero is kept.
+ *   THRIFT_NVFP4_MXP: thrift_attention_fwd only, a variant of the FP4 path:
+ *     Q, K and V as THRIFT_NVFP4 tensors, but the probabilities quantised
+ *     MX-style (E8M0 per 32 keys under an integer level-1 offset) instead of
+ *     NVFP4's two levels.  Every other call rejects it (THRIFT_EINVAL). */
+typedef enum { THRIFT_NVFP4 = 0, THRIFT_MXFP4 = 1, THRIFT_NVFP4_MXP = 2 } thrift_format;
 
 /* Grouping axis of a quantised tensor.
  *   THRIFT_GROUP_D (Q, K): groups run along dim; codes [B,H,S,D/2] u8,

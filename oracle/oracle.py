@@ -14,6 +14,7 @@ import numpy as np
 
 NVFP4 = 0
 MX = 1
+NVFP4_MXP = 2  # attention only: NVFP4 tensors, P quantised MX-style
 AXIS_D = 0
 AXIS_S = 1
 
@@ -265,10 +266,11 @@ def fp4_scores(q4: FP4Tensor, k4: FP4Tensor, r, c0, c1):
 # ---- attention ----------------------------------------------------------------
 
 def attention(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt, bq, bk,
-              causal, sm_scale=None, work=None, with_u=False):
+              causal, sm_scale=None, work=None, with_u=False, p_fmt=None):
     """Forward pass.  Returns (o fp64 [B,Hq,S,D], lse fp64 [B,Hq,S]) and, with
     with_u, the decision-uncertainty bound u [B,Hq,S,D]; with a work list of
-    (b, hq, i) triples only those query blocks are filled (the rest stay NaN)."""
+    (b, hq, i) triples only those query blocks are filled (the rest stay NaN).
+    p_fmt=MX with NVFP4 tensors quantises P MX-style (the variant)."""
     B, Hq, S, D = q4.shape
     Hkv, Sk = k4.shape[1], k4.shape[2]
     if sm_scale is None:
@@ -287,7 +289,9 @@ def attention(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, c
     lib().tho_attention_kv(_ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
                            _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales),
                            _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales),
-                           _ptr(v4.tensor_scale), q4.fmt, _ptr(idx), _ptr(cnt), km, B, Hq, Hkv, S,
+                           _ptr(v4.tensor_scale),
+                           NVFP4_MXP if (q4.fmt == NVFP4 and p_fmt == MX) else q4.fmt, _ptr(idx), _ptr(cnt),
+                           km, B, Hq, Hkv, S,
                            Sk, D, bq, bk, int(causal), float(sm_scale), _ptr(w), nw, _ptr(o),
                            _ptr(lse), _ptr(u))
     return (o, lse, u) if with_u else (o, lse)
@@ -384,12 +388,12 @@ def row_probs(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, c
 
 
 def pipeline(q16, k16, v16, fmt, bq, bk, causal, topk_count=-1, topk_bp=0, sm_scale=None,
-             work=None):
+             work=None, p_fmt=None):
     """Selection, quantisation of Q/K/V and attention, all on the oracle."""
     idx, cnt, _ = select(q16, k16, bq, bk, causal, topk_count, topk_bp)
     q4 = quantize(q16, AXIS_D, fmt)
     k4 = quantize(k16, AXIS_D, fmt)
     v4 = quantize(v16, AXIS_S, fmt)
     o, lse, u = attention(q16, k16, v16, q4, k4, v4, idx, cnt, bq, bk, causal, sm_scale, work,
-                          with_u=True)
+                          with_u=True, p_fmt=p_fmt)
     return dict(idx=idx, cnt=cnt, q4=q4, k4=k4, v4=v4, o=o, lse=lse, u=u)

@@ -612,6 +612,7 @@ static void tho_quantize_p_tile(const double* t, const double* ta, const int* ma
 
 typedef struct {
   int B, Hq, Hkv, S, Sk, D, bq, bk, causal, fmt, kmax; /* S: queries, Sk: keys */
+  int pfmt; /* format of P's two-level quantisation (fmt, or MX for THO_NVFP4_MXP) */
   double sm_scale;
   const uint16_t *q16, *k16, *v16;
   const uint8_t *q4c, *q4s; /* FP4 query codes and scales as quantised */
@@ -671,12 +672,12 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
     }
     if (mt == -INFINITY) continue; /* every key of this block is masked for row r */
     double ref;
-    tho_quantize_p_tile(t, ta, mask, n, a->fmt, mt, pq, u_row ? dq : NULL, &ref);
+    tho_quantize_p_tile(t, ta, mask, n, a->pfmt, mt, pq, u_row ? dq : NULL, &ref);
     double m_new = m > mt ? m : mt;
     double alpha = exp2(m - m_new); /* 0 when m = -inf */
     double w = exp2(ref - m_new);
     double emt = 0.0; /* NVFP4: error of the level-1 factor 2^mt */
-    if (a->fmt == THO_NVFP4)
+    if (a->pfmt == THO_NVFP4)
       for (int c = 0; c < n; ++c)
         if (!mask[c] && t[c] == mt) emt = tho_eval_eps(ta[c]);
     if (u_row)
@@ -810,7 +811,9 @@ static void tho_attention_impl(const uint16_t* q16, const uint16_t* k16, const u
   a.bq = bq;
   a.bk = bk;
   a.causal = causal;
-  a.fmt = fmt;
+  /* THO_NVFP4_MXP: NVFP4 tensors, P quantised MX-style (a variant) */
+  a.fmt = fmt == THO_NVFP4_MXP ? THO_NVFP4 : fmt;
+  a.pfmt = fmt == THO_NVFP4_MXP ? THO_MX : fmt;
   a.kmax = kmax;
   a.sm_scale = sm_scale;
   a.q16 = q16;
@@ -820,8 +823,8 @@ static void tho_attention_impl(const uint16_t* q16, const uint16_t* k16, const u
   a.cnt = cnt;
   double* k4 = (double*)malloc(sizeof(double) * (size_t)B * Hkv * Sk * D);
   double* v4 = (double*)malloc(sizeof(double) * (size_t)B * Hkv * Sk * D);
-  tho_dequantize(k4c, k4s, k4t, B, Hkv, Sk, D, THO_AXIS_D, fmt, k4);
-  tho_dequantize(v4c, v4s, v4t, B, Hkv, Sk, D, THO_AXIS_S, fmt, v4);
+  tho_dequantize(k4c, k4s, k4t, B, Hkv, Sk, D, THO_AXIS_D, a.fmt, k4);
+  tho_dequantize(v4c, v4s, v4t, B, Hkv, Sk, D, THO_AXIS_S, a.fmt, v4);
   a.q4c = q4c;
   a.q4s = q4s;
   a.q4t = q4t;
@@ -961,7 +964,7 @@ static int tho_tile_probs(const tho_attn_args* a, const double* k16d, int b, int
   if (mt == -INFINITY) return n;
   if (!prom) {
     double ref;
-    tho_quantize_p_tile(t, ta, mask, n, a->fmt, mt, pq, dpt ? dq : NULL, &ref);
+    tho_quantize_p_tile(t, ta, mask, n, a->pfmt, mt, pq, dpt ? dq : NULL, &ref);
     for (int c = 0; c < n; ++c)
       if (!mask[c]) {
         kind[c] = 1;
@@ -999,6 +1002,7 @@ static void tho_bwd_setup(tho_attn_args* a, const uint16_t* q16, const uint16_t*
   a->bk = bk;
   a->causal = causal;
   a->fmt = fmt;
+  a->pfmt = fmt;
   a->kmax = kmax;
   a->sm_scale = sm_scale;
   a->q16 = q16;

@@ -11,6 +11,7 @@
 
 #define THO_NVFP4 0 /* E2M1 + per-16 E4M3 block scale + per-slice fp32 scale */
 #define THO_MX 1    /* E2M1 + per-32 E8M0 block scale */
+#define THO_NVFP4_MXP 2 /* attention only: NVFP4 Q, K, V with P quantised MX-style */
 #define THO_AXIS_D 0 /* groups along the head dimension (Q, K) */
 #define THO_AXIS_S 1 /* groups along the sequence, stored transposed (V) */
 

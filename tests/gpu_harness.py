@@ -16,7 +16,7 @@ def note(msg):
     sys.stdout.flush()
 
 
-def run_gpu(d, w, fmt, topk_count, topk_bp, no_fp16=False, fused=False):
+def run_gpu(d, w, fmt, topk_count, topk_bp, no_fp16=False, fused=False, p_fmt=None):
     """The path on the GPU: separate selection and quantisation calls, or
     (fused) Q and K each read once for means and codes, as the benchmark runs it."""
     import torch
@@ -37,7 +37,7 @@ def run_gpu(d, w, fmt, topk_count, topk_bp, no_fp16=False, fused=False):
     v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, fmt)
     args = (None, None, None) if no_fp16 else (q, k, v)
     o, lse = api.thrift_attention_fwd(*args, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal,
-                                      out_fp32=True, with_lse=True)
+                                      out_fp32=True, with_lse=True, p_fmt=p_fmt)
     torch.cuda.synchronize()
     cpu = lambda t: None if t is None else t.cpu().numpy()  # noqa: E731
     return dict(idx=cpu(idx), cnt=cpu(cnt), q4=q4, k4=k4, v4=v4, o=cpu(o).astype(np.float64),

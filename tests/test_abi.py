@@ -92,6 +92,9 @@ def test_attention_validation(lib):
     assert call(o=None) == 1
     assert call(k16=None) == 1  # all three fp16 tensors or none
     assert call(fmt=0, ts=None) == 1
+    assert call(fmt=2, ts=None) == 1  # the MX-P variant takes NVFP4 tensors with their slice scales
+    assert call(fmt=3) == 1
+    assert call(fmt=2, D=80) == 2  # the variant passes the format check
     assert call(Hq=3, Hkv=2) == 1
     assert call(sm=0.0) == 1
     assert call(sm=float("nan")) == 1

@@ -56,6 +56,28 @@ def test_parity(oracle, name):
     compare_out(g["o"], r["o"], g["lse"], r["lse"], r["u"])
 
 
+VARIANT_CASES = {
+    # NVFP4 Q, K, V with P quantised MX-style (THRIFT_NVFP4_MXP)
+    "prefill": (workload("prefill", Hq=4, Hkv=4, S=1000), -1, 500),
+    "gqa_ragged": (workload("sweep", B=2, Hq=4, Hkv=2, S=700), -1, 2500),
+    "none_fp16": (workload("prefill", Hq=2, Hkv=1, S=640), -1, 0),
+    "bq64_d64": (workload("dit", Hq=2, Hkv=2, S=513, bq=64), -1, 1000),
+}
+
+
+@pytest.mark.parametrize("name", list(VARIANT_CASES))
+def test_parity_nvfp4_tensors_mx_p(oracle, name):
+    w, tc, bp = VARIANT_CASES[name]
+    note(f"[parity, NVFP4 tensors + MX P] {name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} S{w.S} D{w.D} bq{w.bq} topk({tc},{bp})")
+    d = W.generate(w)
+    g = run_gpu(d, w, 0, tc, bp, no_fp16=(bp == 0 and tc <= 0), p_fmt=1)
+    r = oracle.pipeline(d["q"], d["k"], d["v"], 0, w.bq, w.bk, w.causal, tc, bp, p_fmt=1)
+    assert np.array_equal(g["cnt"], r["cnt"])
+    same_fp4(g["q4"], r["q4"])
+    same_fp4(g["v4"], r["v4"])
+    compare_out(g["o"], r["o"], g["lse"], r["lse"], r["u"])
+
+
 def test_determinism():
     import torch
 

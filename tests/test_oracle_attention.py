@@ -107,6 +107,27 @@ def test_p3_mixed_equals_two_pass(oracle, fmt, bp):
     np.testing.assert_allclose(r["lse"], L, rtol=1e-12, atol=1e-12)
 
 
+@pytest.mark.parametrize("bp", [0, 2500])
+def test_p3v_mx_p_with_nvfp4_tensors_equals_two_pass(oracle, bp):
+    """The variant: NVFP4 Q, K, V with P quantised MX-style (E8M0 per 32 keys,
+    integer level 1) equals the dense two-pass form on the NVFP4-decoded
+    operands with the MX P quantiser, and differs from the NVFP4 forward."""
+    S, Hq, Hkv, D, causal, bq, bk = 400, 2, 1, 64, True, 128, 64
+    q, k, v = _inputs(S, Hq, Hkv, D, 5)
+    sm = 1.0 / np.sqrt(D)
+    r = oracle.pipeline(q, k, v, oracle.NVFP4, bq, bk, causal, -1, bp, sm, p_fmt=oracle.MX)
+    dq = pins.decode_fp4(r["q4"].codes, r["q4"].scales, r["q4"].tensor_scale, 0, 0, q.shape)
+    dk = pins.decode_fp4(r["k4"].codes, r["k4"].scales, r["k4"].tensor_scale, 0, 0, k.shape)
+    dv = pins.decode_fp4(r["v4"].codes, r["v4"].scales, r["v4"].tensor_scale, 0, 1, v.shape)
+    O, L = pins.two_pass_attention(dq, dk, dv, q.astype(np.float64), k.astype(np.float64),
+                                   v.astype(np.float64), r["idx"], r["cnt"], 1, bq, bk, causal, sm)
+    np.testing.assert_allclose(r["o"], O, rtol=1e-9, atol=1e-7 * np.abs(O).max())
+    np.testing.assert_allclose(r["lse"], L, rtol=1e-12, atol=1e-12)
+    nv = oracle.pipeline(q, k, v, oracle.NVFP4, bq, bk, causal, -1, bp, sm)
+    assert np.abs(nv["o"] - r["o"]).max() > 1e-4  # the P quantiser is not NVFP4's
+    np.testing.assert_array_equal(nv["lse"], r["lse"])  # the row sum is the unquantised one
+
+
 def test_p6_fp4_products_exact(oracle):
     rng = np.random.default_rng(4)
     S, D = 64, 128
