@@ -424,24 +424,26 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   const int qstart = a.causal ? (j0 * kBlkK / 32) * 32 : 0;
   const int nsteps_g = cdiv(S - qstart, 32);
   const int nsteps = G * nsteps_g;
-  // the promoted bits of blocks j0 and j0+1 (one word: j0 is even) for step n,
-  // loaded two steps ahead so that no step waits for them
-  auto step_at = [&](int n, int& bhq, int& q0) {
-    const int g = n / nsteps_g;
-    q0 = qstart + (n - g * nsteps_g) * 32;
-    bhq = b * a.Hq + hk * G + g;
+  // steps advance (g, q0) incrementally; the promoted bits of blocks j0 and
+  // j0+1 (one word: j0 is even) are loaded two steps ahead so that no step
+  // waits for them
+  const int bq_shift = a.bq == 128 ? 7 : 6;
+  auto advance = [&](int& g, int& q0) {
+    q0 += 32;
+    if (q0 >= S) {
+      q0 = qstart;
+      ++g;
+    }
   };
-  auto word_addr = [&](int n) {
-    int bhq, q0;
-    step_at(n < nsteps ? n : nsteps - 1, bhq, q0);
-    return a.prom + ((size_t)bhq * a.nq + q0 / a.bq) * a.nkw + (j0 >> 5);
+  auto word_addr = [&](int g, int q0) {
+    const int bhq = b * a.Hq + hk * G + (g < G ? g : G - 1);
+    return a.prom + ((size_t)bhq * a.nq + (q0 >> bq_shift)) * a.nkw + (j0 >> 5);
   };
   auto bit = [&](uint32_t word, int j) { return j < nk && ((word >> (j & 31)) & 1u) != 0; };
   v4i pq16[PR], pqd[PR], pdo[PR], pt16[PR], ptd[PR], pdt[PR];
   float pl = 0.0f, pr = 0.0f;
-  auto fetch = [&](int n, uint32_t word) {
-    int bhq, q0;
-    step_at(n, bhq, q0);
+  auto fetch = [&](int g, int q0, uint32_t word) {
+    const int bhq = b * a.Hq + hk * G + g;
     const bool f0 = bit(word, j0), f1 = bit(word, j0 + 1);
     const bool need16 = f0 || f1, needd = !f0 || !f1;
     const auto qrs = rsrc(a.q16 + (size_t)bhq * S * D, S * D * 2);
@@ -490,21 +492,30 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     }
   };
 
-  uint32_t wcur = nsteps > 0 ? __builtin_amdgcn_readfirstlane(*word_addr(0)) : 0u;
-  uint32_t wnext = nsteps > 1 ? *word_addr(1) : 0u;  // in flight
-  int need = nsteps > 0 ? fetch(0, wcur) : 0;
+  int g = 0, q0 = qstart;          // this step
+  int g1 = 0, q01 = qstart;        // the next
+  advance(g1, q01);
+  int g2 = g1, q02 = q01;          // the one after
+  advance(g2, q02);
+  uint32_t wcur = nsteps > 0 ? __builtin_amdgcn_readfirstlane(*word_addr(g, q0)) : 0u;
+  uint32_t wnext = nsteps > 1 ? *word_addr(g1, q01) : 0u;  // in flight
+  int need = nsteps > 0 ? fetch(g, q0, wcur) : 0;
+  float cq4 = a.c;  // scale of FP4 pairs' scores (NVFP4: times the head's slice scales)
+  int cq_g = -1;
   for (int n = 0; n < nsteps; ++n) {
-    int bhq, q0;
-    step_at(n, bhq, q0);
+    const int bhq = b * a.Hq + hk * G + g;
     const bool f16 = bit(wcur, jb);
-    const float cq4 = a.tq ? a.c * a.tq[bhq] * a.tk[bhk] : a.c;
+    if (g != cq_g) {
+      cq4 = a.tq ? a.c * a.tq[bhq] * a.tk[bhk] : a.c;
+      cq_g = g;
+    }
     __syncthreads();  // every wave is done with the previous step
     stash(need);
     __syncthreads();
     if (n + 1 < nsteps) {
       const uint32_t w1 = __builtin_amdgcn_readfirstlane(wnext);
-      wnext = *word_addr(n + 2);
-      need = fetch(n + 1, w1);
+      wnext = *word_addr(g2, q02);
+      need = fetch(g1, q01, w1);
       wcur = w1;
     }
     // (steps whose pairs are all masked for this wave add zeros: a branch
@@ -632,6 +643,11 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
         dv[dt] = mma16(pA[st], *(const v8h*)(oT + off), dv[dt]);
         dk[dt] = mma16(sA[st], *(const v8h*)(qT + off), dk[dt]);
       }
+    g = g1;
+    q0 = q01;
+    g1 = g2;
+    q01 = q02;
+    advance(g2, q02);
   }
   // C layout: column d = dt*32 + r32, register ii is key (ii/4)*8 + hi*4 + ii%4 of the wave's 32
 #pragma unroll
