@@ -8,15 +8,15 @@
 // valid pair, in the precision of the path the pair's block takes for r's
 // query block (FP4-decoded Q, K, V on the FP4 path, fp16 on the FP16 path):
 //   t = sm_scale log2(e) q.k, p = 2^(t - L2), L2 = lse log2(e)
-//   pt = the forward's probability (FP4 path: MX two-level quantised; FP16
-//        path: p rounded to fp16)
+//   pt = the forward's probability (FP4 path: two-level quantised, MX or
+//        NVFP4; FP16 path: p rounded to fp16)
 //   dV[c] += pt dO[r], dS = p (dO[r].v[c] - dO[r].O'[r]),
 //   dQ[r] += sm_scale dS k[c], dK[c] += sm_scale dS q[r].
 //
-// All products run on the fp16 matrix cores: MX-decoded FP4 operands are
-// exact in fp16.  Three kernels after a preparation pass: the row kernel
-// (one lane per query, as the forward: O' or dQ), and the key kernel (one
-// lane per key: dK and dV).
+// All products run on the fp16 matrix cores: FP4-decoded operands are exact
+// in fp16 (NVFP4's slice scales enter as fp32 factors).  After a preparation
+// pass, the row kernel (one lane per query, as in the forward) computes O'
+// or dQ, and the key kernel (one lane per key) computes dK and dV.
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -71,7 +71,7 @@ struct BwdArgs {
   const float *tq, *tk, *tv;               // NVFP4 slice scales [B,H] (NULL for MXFP4)
   float* out;                              // row kernel: O' or dQ [B,Hq,S,D]
   float *dk, *dv;                          // [B,Hkv,S,D]
-  int B, Hq, Hkv, S, Sp, bq, nq, nkw, causal, fmt;
+  int B, Hq, Hkv, S, Sp, bq, nq, nkw, causal;
   float c;         // sm_scale * log2(e)
   float sm_scale;
 };
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
 
 // LDS stage of one 32-query step for the key kernel: query rows (fp16 and
 // FP4-decoded, as needed), dO rows, their transposes, and the rows' LSE and
-// row terms; plus each wave's per-query MX factors.
+// row terms; plus each wave's per-query factors of P's quantisation.
 template <int D>
 struct KeyLds {  // (FA, FH: [wave][group][query]; HT: [wave][query] half-tile maxima, NVFP4)
   static constexpr int RR = D + 8;  // halves per query row
@@ -377,9 +377,11 @@ struct KeyLds {  // (FA, FH: [wave][group][query]; HT: [wave][query] half-tile m
 // waves (the next step's are loaded into registers meanwhile).  Per step and
 // wave: S = Q K^T and dP = dO V^T with this lane's key as the column, p and
 // dS per element; on FP4 pairs the probability the forward used is rebuilt
-// from its MX group (the wave's 32 keys), whose maximum comes from
-// S^T = K Q^T (same operands swapped, one lane per query) and is handed to
-// the key-major lanes through the wave's own LDS slot.  Then dV += pt^T dO
+// from its quantisation groups (MX: the wave's 32 keys; NVFP4: 16-key groups
+// under the 64-key tile maximum, which the block's two waves exchange), whose
+// maxima come from S^T = K Q^T (same operands swapped, one lane per query)
+// and are handed to the key-major lanes through the wave's own LDS slot.
+// Then dV += pt^T dO
 // and dK += dS^T Q.  Only the K and V operands of the precision in use are
 // held in registers; they are reloaded when a step switches path.
 template <int D, int FMT>
@@ -772,7 +774,6 @@ void prepare(BwdArgs& a, char* ws, const BwdLayout& l, const void* q16, const vo
   a.nq = cdiv(S, block_q);
   a.nkw = cdiv(nk, 32);
   a.causal = causal;
-  a.fmt = fmt;
   const bool nv = fmt == THRIFT_NVFP4;
   a.tq = nv ? q4t : nullptr;
   a.tk = nv ? k4t : nullptr;
