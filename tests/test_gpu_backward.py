@@ -49,6 +49,8 @@ CASES = {
     "short_tail_nvfp4": (workload("prefill", Hq=1, Hkv=1, S=37), -1, 500, 0),
     "long_sink_planted_gqa4_mx": (workload("long", Hq=4, Hkv=1, S=1024, planted=2), -1, 500, 1),
     "long_sink_planted_gqa4_nvfp4": (workload("long", Hq=4, Hkv=1, S=1024, planted=2), -1, 500, 0),
+    "causal_d64_bq128_mx": (workload("prefill", Hq=2, Hkv=1, S=450, D=64), -1, 1500, 1),
+    "causal_d64_bq128_nvfp4": (workload("prefill", Hq=2, Hkv=1, S=450, D=64), -1, 1500, 0),
 }
 
 
