@@ -122,18 +122,8 @@ __device__ inline v16f mfma_fp4(v4i a, v4i b, v16f c, int sa, int sb) {
   return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(widen(a), widen(b), c, 4, 4, SA, sa, SB, sb);
 }
 
-__device__ inline v16f mfma_f16(v8h a, v8h b, v16f c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
 __device__ inline float xlane32(float v) { return __shfl_xor(v, 32, kWave); }
 __device__ inline uint32_t xlane32u(uint32_t v) { return __shfl_xor(v, 32, kWave); }
-
-// E4M3 byte -> value (finite codes only).
-__device__ inline float e4m3_to_float(uint32_t b) {
-  uint32_t e = (b >> 3) & 0xF, m = b & 7;
-  return e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120) << 23) | (m << 20));
-}
 
 // 4 E2M1 codes (2 bytes) -> 4 fp16 values, times an fp16 factor (exact when
 // the factor has at most 4 significant bits and the products stay normal).
@@ -146,11 +136,7 @@ __device__ inline v4h fp4x4_to_h(uint32_t codes16, _Float16 f) {
   return v4h{a.x, a.y, b.x, b.y};
 }
 
-// Key (within the 64-key tile) that A-operand row m of 32x32 S^T tile mt
-// reads.  The MFMA output puts row (i/4)*8 + hi*4 + i%4 in register i of a
-// lane of half hi, so register i of tile mt holds key hi*32 + mt*16 + i.
-__device__ inline int krow(int mt, int m) { return ((m >> 2) & 1) * 32 + mt * 16 + (m >> 3) * 4 + (m & 3); }
-// K tiles are stored in LDS in that read order (key krow(mt, m) at row
+// K tiles are stored in LDS in krow's read order (key krow(mt, m) at row
 // mt*32 + m), so the 32 lanes of a half-wave read consecutive rows; kslot is
 // the inverse map, key -> LDS row.
 __device__ inline int kslot(int key) {
@@ -158,14 +144,6 @@ __device__ inline int kslot(int key) {
   return mt * 32 + (i >> 2) * 8 + h * 4 + (i & 3);
 }
 __device__ inline int key_of(int mt, int i, int hi) { return hi * 32 + mt * 16 + i; }
-
-// Value of the other lane holding the same query (lane +- 32).
-__device__ inline float pair_max(float v) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ---- online-softmax state ------------------------------------------------------
 

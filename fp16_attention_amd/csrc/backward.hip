@@ -31,25 +31,8 @@ constexpr float kLog2eB = 1.44269504088896341f;
 
 typedef float v2f __attribute__((ext_vector_type(2)));
 
-__device__ inline v16f mma16(v8h a, v8h b, v16f c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-}
-
-__device__ inline float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
-
-// Maximum of this lane's value and the one of lane +- 32.
-__device__ inline float max_pair(float v) {
-  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-// Key of A-operand row m of 32x32 S^T tile mt in a 64-key block: the MFMA
-// output then puts key hi*32 + mt*16 + i in register i of a lane of half hi.
-__device__ inline int krow_b(int mt, int m) {
-  return ((m >> 2) & 1) * 32 + mt * 16 + (m >> 3) * 4 + (m & 3);
-}
-// The same for one 32-row tile: row m reads query qperm(m), so register i of
-// a lane of half hi holds query hi*16 + i.
+// The query-row counterpart of krow for one 32-row tile: row m reads query
+// qperm(m), so register i of a lane of half hi holds query hi*16 + i.
 __device__ inline int qperm(int m) { return ((m >> 2) & 1) * 16 + (m >> 3) * 4 + (m & 3); }
 
 __device__ inline __amdgpu_buffer_rsrc_t rsrc(const void* p, uint32_t bytes) {
@@ -78,13 +61,6 @@ struct BwdArgs {
 
 // ---- preparation ------------------------------------------------------------------
 
-// E4M3 byte -> value (finite codes).
-__device__ inline float e4m3_value(uint32_t b) {
-  const uint32_t e = (b >> 3) & 0xF, m = b & 7;
-  const float v = e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120) << 23) | (m << 20));
-  return (b & 0x80) ? -v : v;
-}
-
 // FP4 rows decoded to fp16: codes [R][L/2] (even element in the low
 // nibble), block scales [R][L/g] (MXFP4: E8M0, g = 32; NVFP4: E4M3, g = 16);
 // one thread per 8 elements.  Out [R][L]; or, with vD > 0, rows are V's
@@ -104,7 +80,7 @@ __global__ __launch_bounds__(256) void decode_fp4_kernel(const uint8_t* codes, c
   const uint32_t cw = *(const uint32_t*)(codes + row * (L / 2) + c8 / 2);
   const int g = fmt == THRIFT_MXFP4 ? 32 : 16;
   const uint32_t sb = scales[row * (L / g) + c8 / g];
-  float f = fmt == THRIFT_MXFP4 ? ldexpf(1.0f, (int)sb - 127) : e4m3_value(sb);
+  float f = fmt == THRIFT_MXFP4 ? ldexpf(1.0f, (int)sb - 127) : e4m3_to_float(sb);
   if (tsc) f *= tsc[row / rows_per_bh];
   const v2f v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0),
                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1),
@@ -193,7 +169,7 @@ struct RowLds {
 
 // Workgroup = query block i of (batch, query head), one wave per 32 rows.
 // Per valid key block j, in the precision of its path: S^T = K Q^T (keys in
-// krow_b order), p = 2^(t - L2); then O'^T += V^T P^T, or dP^T = V dO^T,
+// krow order), p = 2^(t - L2); then O'^T += V^T P^T, or dP^T = V dO^T,
 // dS = p (dP - Dr) and dQ^T += K^T dS^T.  The waves share each key block's
 // operands through one LDS stage; the next block's are loaded into
 // registers while the current one is computed.
@@ -296,9 +272,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       s[mt] = v16f{};
-      const _Float16* kr = ks + krow_b(mt, r32) * L::KR + hi * 8;
+      const _Float16* kr = ks + krow(mt, r32) * L::KR + hi * 8;
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) s[mt] = mma16(*(const v8h*)(kr + kk * 16), f16 ? qh[kk] : qd[kk], s[mt]);
+      for (int kk = 0; kk < D / 16; ++kk) s[mt] = mfma_f16(*(const v8h*)(kr + kk * 16), f16 ? qh[kk] : qd[kk], s[mt]);
     }
     v16f dp[2];
     if constexpr (MODE == kModeDq) {
@@ -306,9 +282,9 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         dp[mt] = v16f{};
-        const _Float16* vr = vs + krow_b(mt, r32) * L::KR + hi * 8;
+        const _Float16* vr = vs + krow(mt, r32) * L::KR + hi * 8;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) dp[mt] = mma16(*(const v8h*)(vr + kk * 16), dh[kk], dp[mt]);
+        for (int kk = 0; kk < D / 16; ++kk) dp[mt] = mfma_f16(*(const v8h*)(vr + kk * 16), dh[kk], dp[mt]);
       }
     }
     // B operand of the second product: step st holds keys hi*32 + 8 st + u,
@@ -320,7 +296,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
       for (int ii = 0; ii < 16; ++ii) {
         const int key = j * kBlkK + hi * 32 + mt * 16 + ii;
         const bool ok = qok && key < S && !(a.causal && key > qrow);
-        const float p = ok ? ex2(__builtin_fmaf(s[mt][ii], f16 ? a.c : cq4, -L2)) : 0.0f;
+        const float p = ok ? exp2_fast(__builtin_fmaf(s[mt][ii], f16 ? a.c : cq4, -L2)) : 0.0f;
         float v = p;
         if constexpr (MODE == kModeDq) v = p * (dp[mt][ii] * (f16 ? 1.0f : dpf4) - Dr);
         pb[mt * 2 + ii / 8][ii % 8] = (_Float16)v;
@@ -331,7 +307,7 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const v8h tv = *(const v8h*)(ts + (dt * 32 + r32) * L::TR + hi * 32 + st * 8);
-        acc[dt] = mma16(tv, pb[st], acc[dt]);
+        acc[dt] = mfma_f16(tv, pb[st], acc[dt]);
       }
   }
   if (!qok) return;
@@ -528,8 +504,8 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     v16f s = v16f{}, dp = v16f{};
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) {
-      s = mma16(*(const v8h*)(qrow + kk * 16), kr[kk], s);
-      dp = mma16(*(const v8h*)(drow + kk * 16), vr[kk], dp);
+      s = mfma_f16(*(const v8h*)(qrow + kk * 16), kr[kk], s);
+      dp = mfma_f16(*(const v8h*)(drow + kk * 16), vr[kk], dp);
     }
     // FP4 pairs: per query and P group, p * fa is the element over its block
     // scale and pt = code * fh (this lane's key is in group grp of the wave)
@@ -541,7 +517,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     if (!f16) {
       v16f st = v16f{};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) st = mma16(kr[kk], *(const v8h*)(qrow + kk * 16), st);
+      for (int kk = 0; kk < D / 16; ++kk) st = mfma_f16(kr[kk], *(const v8h*)(qrow + kk * 16), st);
       // column r32 is query q0 + qperm(r32); register ii is key (ii/4)*8 + hi*4 + ii%4 of the wave's 32
       const int qm = q0 + qperm(r32);
 #pragma unroll
@@ -554,21 +530,21 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
         else
           gm1 = fmaxf(gm1, v);
       }
-      gm0 = max_pair(gm0);
-      gm1 = max_pair(gm1);
+      gm0 = pair_max(gm0);
+      gm1 = pair_max(gm1);
       Lq = ((const float*)(smem + L::L2))[qperm(r32)];
       if constexpr (FMT == THRIFT_MXFP4) {
         // MX level 1 is any power of two (the E8M0 block scale absorbs it):
         // z = ceil(L2); block exponent from the group maximum's probability
         const float gm = fmaxf(gm0, gm1);
         const float z = ceilf(Lq);
-        const uint32_t E = (__float_as_uint(ex2(__builtin_fmaf(gm, cj, -z))) >> 23) & 0xFF;
+        const uint32_t E = (__float_as_uint(exp2_fast(__builtin_fmaf(gm, cj, -z))) >> 23) & 0xFF;
         const int X = (int)(E > 3 ? E - 2 : 1) - 127;
         const float zx = z + (float)X;
         const bool any = gm > -INFINITY;
         if (hi == 0) {
-          ((float*)wa)[qperm(r32)] = any ? ex2(Lq - zx) : 0.0f;
-          ((float*)wh)[qperm(r32)] = any ? ex2(zx - Lq) : 0.0f;
+          ((float*)wa)[qperm(r32)] = any ? exp2_fast(Lq - zx) : 0.0f;
+          ((float*)wh)[qperm(r32)] = any ? exp2_fast(zx - Lq) : 0.0f;
         }
         // the wave reads back its own slot: its LDS operations complete in order
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -588,16 +564,16 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
         const bool live = tm > -INFINITY && tml - Lq > -60.0f;
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-          const float gv = 2688.0f * ex2(__builtin_fmaf(g ? gm1 : gm0, cj, -tml));
+          const float gv = 2688.0f * exp2_fast(__builtin_fmaf(g ? gm1 : gm0, cj, -tml));
           v2s_t sb = {0, 0};
           sb = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(sb, fminf(gv * (1.0f / 6.0f), 448.0f), 0.0f, 1.0f, false);
-          const float s2 = e4m3_value((uint32_t)sb[0] & 0xFF);
+          const float s2 = e4m3_to_float((uint32_t)sb[0] & 0xFF);
           const bool on = live && s2 > 0.0f;
           if (hi == 0) {
             float* fa = (float*)(smem + L::FA) + (w * 2 + g) * 32;
             float* fh = (float*)(smem + L::FH) + (w * 2 + g) * 32;
-            fa[qperm(r32)] = on ? ex2(Lq - tml) * (2688.0f / s2) : 0.0f;
-            fh[qperm(r32)] = on ? s2 * ex2(tml - Lq) * (1.0f / 2688.0f) : 0.0f;
+            fa[qperm(r32)] = on ? exp2_fast(Lq - tml) * (2688.0f / s2) : 0.0f;
+            fh[qperm(r32)] = on ? s2 * exp2_fast(tml - Lq) * (1.0f / 2688.0f) : 0.0f;
           }
         }
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
@@ -616,7 +592,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
       for (int e = 0; e < 4; ++e) {
         const int ii = u * 4 + e, q = q0 + hi * 16 + ii;
         const bool ok = q < S && key < S && !(a.causal && key > q);
-        p[e] = ok ? ex2(__builtin_fmaf(s[ii], cj, -lv[e])) : 0.0f;
+        p[e] = ok ? exp2_fast(__builtin_fmaf(s[ii], cj, -lv[e])) : 0.0f;
         sA[ii / 8][ii % 8] = (_Float16)(p[e] * (dp[ii] * (f16 ? 1.0f : dpf4) - rv[e]));
         pt[e] = p[e];
       }
@@ -642,8 +618,8 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
         const int off = (dt * 32 + r32) * L::TR + hi * 16 + st * 8;
-        dv[dt] = mma16(pA[st], *(const v8h*)(oT + off), dv[dt]);
-        dk[dt] = mma16(sA[st], *(const v8h*)(qT + off), dk[dt]);
+        dv[dt] = mfma_f16(pA[st], *(const v8h*)(oT + off), dv[dt]);
+        dk[dt] = mfma_f16(sA[st], *(const v8h*)(qT + off), dk[dt]);
       }
     g = g1;
     q0 = q01;

@@ -59,6 +59,33 @@ inline thrift_status once_per_device(std::atomic<uint64_t>& done, F&& set_up) {
   return THRIFT_OK;
 }
 
+// ---- device helpers shared by the kernels ------------------------------------
+
+// One 32x32x16 fp16 matrix product with fp32 accumulation.
+__device__ inline v16f mfma_f16(v8h a, v8h b, v16f c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ inline float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Maximum of this lane's value and that of lane +- 32 (the other half of a
+// 32x32 product's column).
+__device__ inline float pair_max(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+// E4M3 byte -> value (finite codes; the sign bit of a block scale is 0).
+__device__ inline float e4m3_to_float(uint32_t b) {
+  const uint32_t e = (b >> 3) & 0xF, m = b & 7;
+  return e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120) << 23) | (m << 20));
+}
+
+// Key (within a 64-key tile) that A-operand row m of 32x32 S^T tile mt
+// reads.  The MFMA output puts row (i/4)*8 + hi*4 + i%4 in register i of a
+// lane of half hi, so register i of tile mt holds key hi*32 + mt*16 + i.
+__device__ inline int krow(int mt, int m) { return ((m >> 2) & 1) * 32 + mt * 16 + (m >> 3) * 4 + (m & 3); }
+
 inline thrift_status launch_status() {
   hipError_t e = hipGetLastError();
   return e == hipSuccess ? THRIFT_OK : THRIFT_EHIP;
