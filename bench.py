@@ -22,8 +22,10 @@ sys.path.insert(0, ROOT)
 TRAFFIC_FILES = {("long", "mx"): os.path.join(ROOT, "profiles", "attn_fwd_kernel_long_mx_traffic.txt"),
                  ("decode", "mx"): os.path.join(ROOT, "profiles", "decode_kernels_decode_mx_traffic.txt"),
                  ("prefill_bwd", "mx"): os.path.join(ROOT, "profiles", "backward_kernels_prefill_mx_traffic.txt")}
-KERNEL_SRC = os.path.join(ROOT, "fp16_attention_amd", "csrc", "attention.hip")
-BWD_SRC = os.path.join(ROOT, "fp16_attention_amd", "csrc", "backward.hip")
+CSRC = os.path.join(ROOT, "fp16_attention_amd", "csrc")
+# the sources a profiled kernel is built from (their hash dates the counters)
+KERNEL_SRC = (os.path.join(CSRC, "attention.hip"), os.path.join(CSRC, "common.h"))
+BWD_SRC = (os.path.join(CSRC, "backward.hip"), os.path.join(CSRC, "common.h"))
 
 P_FP4 = 10.1e15   # MI355X dense MXFP4 MFMA, FLOP/s
 P_FP16 = 2.5e15   # MI355X dense FP16 MFMA, FLOP/s
@@ -79,8 +81,11 @@ def measured_traffic(workload, fmt_name, src=KERNEL_SRC):
             if ":" in ln and not ln.startswith((" ", "#", "|")):
                 k, v = ln.split(":", 1)
                 rec[k.strip()] = v.strip()
-    with open(src, "rb") as f:
-        h = hashlib.sha256(f.read()).hexdigest()
+    h = hashlib.sha256()
+    for path in src:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    h = h.hexdigest()
     if rec.get("kernel_source_sha256") != h:
         return None
     return int(rec["traffic_bytes_per_launch"])
