@@ -91,7 +91,7 @@ def gpu_backward(d, w, do, tc, bp, fmt=1, lse_in=None, ohp_in=None):
                                           workspace=ws)
     torch.cuda.synchronize()
     cpu = lambda t: t.cpu().numpy()  # noqa: E731
-    return dict(idx=cpu(idx), cnt=cpu(cnt), q4=q4, k4=k4, v4=v4, ohp=cpu(ohp).astype(np.float64),
+    return dict(idx=cpu(idx), cnt=cpu(cnt), q4=q4, k4=k4, v4=v4, lse=cpu(lse), ohp=cpu(ohp).astype(np.float64),
                 dq=cpu(dq).astype(np.float64), dk=cpu(dk).astype(np.float64), dv=cpu(dv).astype(np.float64))
 
 
@@ -166,6 +166,43 @@ def test_backward_fullsize_prefill(oracle, fmt):
     compare("dQ (3 query blocks)", g["dq"][0, 0, rq], dq[0, 0, rq], widen=widen)
     compare("dK (3 key blocks)", g["dk"][0, 0, rk], dk[0, 0, rk], widen=widen)
     compare("dV (3 key blocks)", g["dv"][0, 0, rk], dv[0, 0, rk], udv[0, 0, rk], widen=widen)
+
+
+def test_backward_fullsize_long(oracle):
+    """The long workload at full size (B1 Hq32 Hkv8 S32768 D128 causal, sink,
+    planted pairs, 5%, MXFP4): the whole chain on the GPU, then O' and the
+    gradients again with head 0's LSE and O' taken from the oracle; the oracle
+    computes query head 0's O' (every row) and the dQ of three of its query
+    blocks."""
+    w = W.WORKLOADS["long"].with_(fmt=1)
+    note(f"[backward] long full size: B{w.B} Hq{w.Hq} Hkv{w.Hkv} S{w.S} D{w.D}")
+    d = W.generate(w)
+    do = output_grad(w, 98)
+    g = gpu_backward(d, w, do, w.topk_count, w.topk_bp, 1)
+    idx, cnt, _ = oracle.select(d["q"], d["k"], w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
+    assert np.array_equal(g["cnt"], cnt) and np.array_equal(g["idx"][..., :idx.shape[-1]], idx)
+    q4 = oracle.quantize(d["q"], oracle.AXIS_D, 1)
+    k4 = oracle.quantize(d["k"], oracle.AXIS_D, 1)
+    v4 = oracle.quantize(d["v"], oracle.AXIS_S, 1)
+    nq = -(-w.S // w.bq)
+    _, lse, ohp = oracle.attention_hp(d["q"], d["k"], d["v"], q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal,
+                                      work=[(0, 0, i) for i in range(nq)])
+    qb = [1, nq // 2, nq - 1]
+    nk = -(-w.S // w.bk)  # (one cheap key block: the work list may not be empty; its dK/dV is not compared)
+    dq, _, _ = oracle.attention_bwd(d["q"], d["k"], d["v"], q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal, lse, ohp,
+                                    do, qwork=[(0, 0, i) for i in qb], kwork=[(0, 0, nk - 1)])
+    rq = np.concatenate([np.arange(i * w.bq, min(w.S, (i + 1) * w.bq)) for i in qb])
+    note("    chain:")
+    compare("O' (head 0)", g["ohp"][0, 0], ohp[0, 0])
+    compare("dQ (3 query blocks)", g["dq"][0, 0, rq], dq[0, 0, rq])
+    # each entry point on the oracle's inputs for head 0 (a row's O' and dQ
+    # depend only on its own LSE and O'); the other heads keep the GPU's
+    lse_in, ohp_in = g["lse"].copy(), g["ohp"].copy()
+    lse_in[0, 0], ohp_in[0, 0] = lse[0, 0], ohp[0, 0]
+    u = gpu_backward(d, w, do, w.topk_count, w.topk_bp, 1, lse_in=lse_in, ohp_in=ohp_in)
+    note("    on the oracle's LSE and O':")
+    compare("O' (head 0)", u["ohp"][0, 0], ohp[0, 0])
+    compare("dQ (3 query blocks)", u["dq"][0, 0, rq], dq[0, 0, rq])
 
 
 def test_backward_deterministic():
