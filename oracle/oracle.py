@@ -91,6 +91,16 @@ def _declare(L):
                                     + [_P, _I, _P, _I] + [_P] * 4)
     L.tho_row_probs.restype = None
     L.tho_row_probs.argtypes = [_P] * 12 + [_I, _P, _P, _I] + [_I] * 8 + [_D, _P, _I, _I, _I] + [_P] * 3
+    L.tho_mx8_exponent.restype = _I
+    L.tho_mx8_exponent.argtypes = [_D]
+    L.tho_e4m3_encode_signed.restype = _I
+    L.tho_e4m3_encode_signed.argtypes = [_D, _D]
+    L.tho_quantize_fp8.restype = None
+    L.tho_quantize_fp8.argtypes = [_P, _I, _I, _I, _I, _I, _P, _P]
+    L.tho_dequantize_fp8.restype = None
+    L.tho_dequantize_fp8.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P]
+    L.tho_attention_tiers.restype = None
+    L.tho_attention_tiers.argtypes = [_P] * 17 + [_I, _P, _P, _I] + [_I] * 8 + [_D, _P, _I, _P, _P, _P]
     L.tho_fp4_scores.restype = None
     L.tho_fp4_scores.argtypes = [_P] * 6 + [_I] * 6 + [_P]
     L.tho_e2m1_encode_array.restype = None
@@ -254,6 +264,45 @@ def dequantize(t: FP4Tensor):
     return out
 
 
+class FP8Tensor:
+    """MXFP8 codes (one E4M3 byte per element) and E8M0 scales per 32."""
+
+    def __init__(self, codes, scales, axis, shape):
+        self.codes, self.scales, self.axis, self.shape = codes, scales, axis, shape
+
+
+def mx8_exponent(amax: float) -> int:
+    return lib().tho_mx8_exponent(float(amax))
+
+
+def e4m3_encode_signed(x: float, s: float) -> int:
+    return lib().tho_e4m3_encode_signed(float(x), float(s))
+
+
+def quantize_fp8(x16, axis) -> FP8Tensor:
+    """MXFP8 of x16 [B,H,S,D]: along D, codes [B,H,S,D] and scales
+    [B,H,S,D/32]; along the sequence (V), codes [B,H,D,Sp], scales
+    [B,H,D,Sp/32] with zero padding tokens."""
+    x16 = _c(x16, np.float16)
+    B, H, S, D = x16.shape
+    if axis == AXIS_D:
+        codes = np.empty((B, H, S, D), np.uint8)
+        scales = np.empty((B, H, S, D // 32), np.uint8)
+    else:
+        Sp = pad_s(S)
+        codes = np.empty((B, H, D, Sp), np.uint8)
+        scales = np.empty((B, H, D, Sp // 32), np.uint8)
+    lib().tho_quantize_fp8(_ptr(x16), B, H, S, D, axis, _ptr(codes), _ptr(scales))
+    return FP8Tensor(codes, scales, axis, (B, H, S, D))
+
+
+def dequantize_fp8(t: FP8Tensor):
+    B, H, S, D = t.shape
+    out = np.empty((B, H, S, D), np.float64)
+    lib().tho_dequantize_fp8(_ptr(t.codes), _ptr(t.scales), B, H, S, D, t.axis, _ptr(out))
+    return out
+
+
 def fp4_scores(q4: FP4Tensor, k4: FP4Tensor, r, c0, c1):
     """Raw FP4-path dot products of query row r with keys [c0, c1) (B = H = 1)."""
     _, _, S, D = q4.shape
@@ -294,6 +343,36 @@ def attention(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, c
                            km, B, Hq, Hkv, S,
                            Sk, D, bq, bk, int(causal), float(sm_scale), _ptr(w), nw, _ptr(o),
                            _ptr(lse), _ptr(u))
+    return (o, lse, u) if with_u else (o, lse)
+
+
+def attention_tiers(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, q8: FP8Tensor,
+                    k8: FP8Tensor, v8: FP8Tensor, idx, cnt, idx2, cnt2, bq, bk, causal, sm_scale=None,
+                    work=None, with_u=False):
+    """Forward with the middle (MXFP8) tier, MX format: blocks idx lists run
+    in FP16, blocks idx2 lists and idx does not in FP8, the rest in FP4.
+    Returns (o, lse) and with with_u the decision-uncertainty bound u."""
+    B, Hq, S, D = q4.shape
+    Hkv = k4.shape[1]
+    assert q4.fmt == MX
+    if sm_scale is None:
+        sm_scale = 1.0 / np.sqrt(D)
+    q16 = None if q16 is None else _c(q16, np.float16)
+    k16 = None if k16 is None else _c(k16, np.float16)
+    v16 = None if v16 is None else _c(v16, np.float16)
+    idx, cnt = _c(idx, np.int32), _c(cnt, np.int32)
+    idx2, cnt2 = _c(idx2, np.int32), _c(cnt2, np.int32)
+    o = np.full((B, Hq, S, D), np.nan, np.float64)
+    lse = np.full((B, Hq, S), np.nan, np.float64)
+    u = np.full((B, Hq, S, D), np.nan, np.float64) if with_u else None
+    w = None if work is None else _c(np.asarray(work).reshape(-1, 3), np.int32)
+    nw = 0 if w is None else w.shape[0]
+    lib().tho_attention_tiers(_ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
+                              _ptr(k4.codes), _ptr(k4.scales), _ptr(v4.codes), _ptr(v4.scales),
+                              _ptr(q8.codes), _ptr(q8.scales), _ptr(k8.codes), _ptr(k8.scales),
+                              _ptr(v8.codes), _ptr(v8.scales), _ptr(idx), _ptr(cnt), idx.shape[-1],
+                              _ptr(idx2), _ptr(cnt2), idx2.shape[-1], B, Hq, Hkv, S, D, bq, bk,
+                              int(causal), float(sm_scale), _ptr(w), nw, _ptr(o), _ptr(lse), _ptr(u))
     return (o, lse, u) if with_u else (o, lse)
 
 
@@ -397,3 +476,17 @@ def pipeline(q16, k16, v16, fmt, bq, bk, causal, topk_count=-1, topk_bp=0, sm_sc
     o, lse, u = attention(q16, k16, v16, q4, k4, v4, idx, cnt, bq, bk, causal, sm_scale, work,
                           with_u=True, p_fmt=p_fmt)
     return dict(idx=idx, cnt=cnt, q4=q4, k4=k4, v4=v4, o=o, lse=lse, u=u)
+
+
+def pipeline_tiers(q16, k16, v16, bq, bk, causal, bp16, bp8, sm_scale=None, work=None):
+    """The three-tier forward on the oracle (MX format): the FP16 tier is the
+    selection under budget bp16, the FP16 and FP8 tiers together the
+    selection under bp16 + bp8 (basis points each)."""
+    idx, cnt, _ = select(q16, k16, bq, bk, causal, -1, bp16)
+    idx2, cnt2, _ = select(q16, k16, bq, bk, causal, -1, bp16 + bp8)
+    q4, k4, v4 = quantize(q16, AXIS_D, MX), quantize(k16, AXIS_D, MX), quantize(v16, AXIS_S, MX)
+    q8, k8, v8 = quantize_fp8(q16, AXIS_D), quantize_fp8(k16, AXIS_D), quantize_fp8(v16, AXIS_S)
+    o, lse, u = attention_tiers(q16, k16, v16, q4, k4, v4, q8, k8, v8, idx, cnt, idx2, cnt2, bq, bk,
+                                causal, sm_scale, work, with_u=True)
+    return dict(idx=idx, cnt=cnt, idx2=idx2, cnt2=cnt2, q4=q4, k4=k4, v4=v4, q8=q8, k8=k8, v8=v8,
+                o=o, lse=lse, u=u)

@@ -142,6 +142,27 @@ int tho_mx_exponent(double amax) {
   return x;
 }
 
+/* MX shared exponent for an E4M3 group (MXFP8, the middle precision tier):
+ * the largest power of two not above amax, divided by 2^8 (the largest power
+ * of two among E4M3's finite values), clamped to the E8M0 range.  The group
+ * maximum then lands in [256, 512) and values above 448 saturate. */
+int tho_mx8_exponent(double amax) {
+  if (!(amax > 0.0)) return -127;
+  int e;
+  frexp(amax, &e);
+  int x = (e - 1) - 8;
+  if (x < -127) x = -127;
+  if (x > 127) x = 127;
+  return x;
+}
+
+/* E4M3 code of x / s (s > 0) with the sign of x kept: the magnitude's code
+ * from tho_e4m3_encode_ratio (ties to even, saturating at 448), bit 7 set
+ * for a negative x or -0, as for E2M1. */
+int tho_e4m3_encode_signed(double x, double s) {
+  return tho_e4m3_encode_ratio(fabs(x), s) | (signbit(x) ? 0x80 : 0);
+}
+
 /* ------------------------------------------------------------------ */
 /* Block selection (pages: "Heuristische Blokkenselectie")             */
 /* ------------------------------------------------------------------ */
@@ -443,6 +464,70 @@ void tho_quantize(const uint16_t* x16, int B, int H, int S, int D, int axis, int
   }
 }
 
+/* MXFP8 (the middle precision tier; reading: OCP MX with E4M3 elements, one
+ * E8M0 scale per 32 elements along the same axes as the FP4 tensors).
+ *  axis THO_AXIS_D (Q, K): codes [B,H,S,D] one byte each, scales [B,H,S,D/32];
+ *  axis THO_AXIS_S (V, stored transposed): codes [B,H,D,Sp], scales
+ *    [B,H,D,Sp/32], padding tokens zero.
+ * Per group: X = tho_mx8_exponent(amax), element = E4M3(x / 2^X), sign kept. */
+void tho_quantize_fp8(const uint16_t* x16, int B, int H, int S, int D, int axis, uint8_t* codes,
+                      uint8_t* scales) {
+  int Sp = tho_pad_s(S);
+  double vals[32];
+  for (int bh = 0; bh < B * H; ++bh) {
+    const uint16_t* x = x16 + (size_t)bh * S * D;
+    int rows = axis == THO_AXIS_D ? S : D;
+    int len = axis == THO_AXIS_D ? D : Sp;
+    for (int r = 0; r < rows; ++r)
+      for (int gi = 0; gi < len / 32; ++gi) {
+        double amax = 0.0;
+        for (int t = 0; t < 32; ++t) {
+          int e = gi * 32 + t;
+          double v;
+          if (axis == THO_AXIS_D)
+            v = tho_half_to_double(x[(size_t)r * D + e]);
+          else
+            v = e < S ? tho_half_to_double(x[(size_t)e * D + r]) : 0.0;
+          vals[t] = v;
+          if (fabs(v) > amax) amax = fabs(v);
+        }
+        int X = tho_mx8_exponent(amax);
+        double sc = ldexp(1.0, X);
+        scales[((size_t)bh * rows + r) * (len / 32) + gi] = (uint8_t)(X + 127);
+        uint8_t* dst = codes + ((size_t)bh * rows + r) * len + gi * 32;
+        for (int t = 0; t < 32; ++t) dst[t] = (uint8_t)tho_e4m3_encode_signed(vals[t], sc);
+      }
+  }
+}
+
+/* Row s of slice bh of an MXFP8 tensor quantised along D, decoded. */
+void tho_dequant8_row(const uint8_t* codes, const uint8_t* scales, size_t bh, int S, int D, int s,
+                      double* out) {
+  for (int d = 0; d < D; ++d) {
+    size_t row = (size_t)bh * S + s;
+    out[d] = tho_e4m3_value(codes[row * D + d]) * ldexp(1.0, scales[row * (D / 32) + d / 32] - 127);
+  }
+}
+
+/* An MXFP8 tensor back to fp64 in the [B, H, S, D] orientation. */
+void tho_dequantize_fp8(const uint8_t* codes, const uint8_t* scales, int B, int H, int S, int D,
+                        int axis, double* out) {
+  int Sp = tho_pad_s(S);
+  for (int bh = 0; bh < B * H; ++bh)
+    for (int s = 0; s < S; ++s)
+      for (int d = 0; d < D; ++d) {
+        size_t e, si;
+        if (axis == THO_AXIS_D) {
+          e = ((size_t)bh * S + s) * D + d;
+          si = ((size_t)bh * S + s) * (D / 32) + d / 32;
+        } else {
+          e = (size_t)bh * D * Sp + (size_t)d * Sp + s;
+          si = ((size_t)bh * D + d) * (Sp / 32) + s / 32;
+        }
+        out[((size_t)bh * S + s) * D + d] = tho_e4m3_value(codes[e]) * ldexp(1.0, scales[si] - 127);
+      }
+}
+
 /* Decoded scale of one group. */
 static double tho_group_scale(int fmt, int byte, double sg) {
   return fmt == THO_NVFP4 ? tho_e4m3_value(byte) * sg : ldexp(1.0, byte - 127);
@@ -610,6 +695,59 @@ static void tho_quantize_p_tile(const double* t, const double* ta, const int* ma
   }
 }
 
+/* One E4M3 spacing (in units of s) if y/s sits within relative eps of a
+ * rounding midpoint between two finite E4M3 values. */
+static double tho_e4m3_flip(double y, double s, double eps) {
+  if (!(y > 0.0) || !(s > 0.0)) return 0.0;
+  double q = y / s;
+  for (int k = 0; k < 126; ++k) {
+    double lo = tho_e4m3_value(k), hi = tho_e4m3_value(k + 1);
+    if (fabs(q - 0.5 * (lo + hi)) <= eps * q) return (hi - lo) * s;
+  }
+  return 0.0;
+}
+
+/* P of one tile on the middle (FP8) tier, two levels as on the MX FP4 path
+ * with E4M3 elements: v = 2^(t - z), z = ceil(mt); per 32 keys (V's groups)
+ * X = tho_mx8_exponent(max v), code E4M3(v / 2^X); the dequantised
+ * probability relative to 2^z is code * 2^X.  dq as for tho_quantize_p_tile. */
+static void tho_quantize_p_tile8(const double* t, const double* ta, const int* mask, int n, double mt,
+                                 double* pq, double* dq, double* ref) {
+  double v[64];
+  double z8 = ceil(mt);
+  *ref = z8;
+  for (int c = 0; c < n; ++c) v[c] = mask[c] ? 0.0 : exp2(t[c] - z8);
+  double ag = 0.0;
+  for (int c = 0; c < n; ++c)
+    if (!mask[c] && ta[c] > ag) ag = ta[c];
+  for (int g0 = 0; g0 < n; g0 += 32) {
+    int g1 = g0 + 32 < n ? g0 + 32 : n;
+    double amax = 0.0;
+    for (int c = g0; c < g1; ++c)
+      if (v[c] > amax) amax = v[c];
+    int X = tho_mx8_exponent(amax);
+    double s2 = ldexp(1.0, X);
+    for (int c = g0; c < g1; ++c) pq[c] = tho_e4m3_value(tho_e4m3_encode_ratio(v[c], s2)) * s2;
+    if (!dq) continue;
+    double eg = tho_eval_eps(ag);
+    int lo = tho_mx8_exponent(amax * (1.0 - 2.0 * eg));
+    int hi = tho_mx8_exponent(amax * (1.0 + 2.0 * eg));
+    double s2alt = ldexp(1.0, lo != X ? lo : hi);
+    for (int c = g0; c < g1; ++c) {
+      if (mask[c]) {
+        dq[c] = 0.0;
+        continue;
+      }
+      double ec = tho_eval_eps(ta[c]);
+      double d = tho_e4m3_flip(v[c], s2, ec);
+      if (s2alt != s2)
+        d += fabs(tho_e4m3_value(tho_e4m3_encode_ratio(v[c], s2alt)) * s2alt - pq[c]) +
+             tho_e4m3_flip(v[c], s2alt, ec);
+      dq[c] = d;
+    }
+  }
+}
+
 typedef struct {
   int B, Hq, Hkv, S, Sk, D, bq, bk, causal, fmt, kmax; /* S: queries, Sk: keys */
   int pfmt; /* format of P's two-level quantisation (fmt, or MX for THO_NVFP4_MXP) */
@@ -619,6 +757,13 @@ typedef struct {
   const float* q4t;
   const double *k4, *v4; /* dequantised FP4 keys and values, [B,Hkv,Sk,D] */
   const int32_t *idx, *cnt;
+  /* middle (FP8) tier, NULL when absent: idx2/cnt2 list the blocks of the
+   * FP16 and FP8 tiers together (the selection under the two budgets'
+   * sum); a listed block that idx also lists stays on the FP16 path */
+  const int32_t *idx2, *cnt2;
+  int kmax2;
+  const uint8_t *q8c, *q8s; /* MXFP8 queries as quantised */
+  const double *k8, *v8;    /* dequantised MXFP8 keys and values, [B,Hkv,Sk,D] */
 } tho_attn_args;
 
 /* One query row r of query block i of head (b, hq). */
@@ -632,6 +777,8 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
   size_t kvbase = ((size_t)b * a->Hkv + hk) * Sk;
   const int32_t* sel = a->idx + (((size_t)b * a->Hq + hq) * nq + i) * a->kmax;
   int nsel = a->cnt[((size_t)b * a->Hq + hq) * nq + i];
+  const int32_t* sel2 = a->idx2 ? a->idx2 + (((size_t)b * a->Hq + hq) * nq + i) * a->kmax2 : NULL;
+  int nsel2 = a->idx2 ? a->cnt2[((size_t)b * a->Hq + hq) * nq + i] : 0;
   int nvalid = tho_valid_blocks_kv(i, S, Sk, a->bq, bk, a->causal);
   double t[64], ta[64], pq[64], dq[64];
   int mask[64];
@@ -646,13 +793,20 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
   double m = -INFINITY, l = 0.0;
   tho_dequant_row(a->q4c, a->q4s, a->q4t, (size_t)b * a->Hq + hq, S, D, r, a->fmt, q4);
 
-  /* FP4 path first, over every valid key block not promoted, ascending. */
-  int sp = 0;
+  /* FP4 path first, over every valid key block not promoted (to either
+   * higher tier), ascending. */
+  int sp = 0, sp2 = 0;
   for (int j = 0; j < nvalid; ++j) {
+    int listed = 0;
     if (sp < nsel && sel[sp] == j) {
       ++sp;
-      continue;
+      listed = 1;
     }
+    if (sp2 < nsel2 && sel2[sp2] == j) {
+      ++sp2;
+      listed = 1;
+    }
+    if (listed) continue;
     int c0 = j * bk, n = (c0 + bk < Sk ? c0 + bk : Sk) - c0;
     double mt = -INFINITY;
     for (int c = 0; c < n; ++c) {
@@ -709,7 +863,65 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
     m = m_new;
   }
 
-  /* FP16 path second, over the promoted blocks, ascending; the FP16 query
+  /* Middle (FP8) tier, over the blocks idx2 lists and idx does not,
+   * ascending: MXFP8 scores, P quantised in two levels with E4M3 elements,
+   * MXFP8 values; the row sum takes the unquantised probabilities. */
+  double* q8 = (double*)malloc(sizeof(double) * (size_t)D);
+  if (nsel2 > 0) tho_dequant8_row(a->q8c, a->q8s, (size_t)b * a->Hq + hq, S, D, r, q8);
+  for (int p2 = 0; p2 < nsel2; ++p2) {
+    int j = sel2[p2], in16 = 0;
+    for (int p = 0; p < nsel; ++p)
+      if (sel[p] == j) in16 = 1;
+    if (in16) continue;
+    int c0 = j * bk, n = (c0 + bk < Sk ? c0 + bk : Sk) - c0;
+    double mt = -INFINITY;
+    for (int c = 0; c < n; ++c) {
+      mask[c] = a->causal && (c0 + c > qpos);
+      double s8 = 0.0, sa8 = 0.0;
+      if (!mask[c]) {
+        const double* kv = a->k8 + (kvbase + c0 + c) * D;
+        for (int d = 0; d < D; ++d) {
+          s8 += q8[d] * kv[d];
+          sa8 += fabs(q8[d] * kv[d]);
+        }
+      }
+      t[c] = mask[c] ? -INFINITY : s8 * a->sm_scale * THO_LOG2E;
+      ta[c] = sa8 * a->sm_scale * THO_LOG2E;
+      if (t[c] > mt) mt = t[c];
+    }
+    if (mt == -INFINITY) continue;
+    double ref;
+    tho_quantize_p_tile8(t, ta, mask, n, mt, pq, u_row ? dq : NULL, &ref);
+    double m_new = m > mt ? m : mt;
+    double alpha = exp2(m - m_new);
+    double w = exp2(ref - m_new);
+    if (u_row)
+      for (int d = 0; d < D; ++d) {
+        double uv = 0.0;
+        for (int c = 0; c < n; ++c) uv += dq[c] * fabs(a->v8[(kvbase + c0 + c) * D + d]);
+        uacc[d] = alpha * uacc[d] + w * uv;
+      }
+    double p8sum = 0.0, up8sum = 0.0;
+    for (int c = 0; c < n; ++c)
+      if (!mask[c]) {
+        p8sum += exp2(t[c] - m_new);
+        up8sum += exp2(t[c] - m_new) * tho_eval_eps(ta[c]);
+      }
+    l = alpha * l + p8sum;
+    ul = alpha * ul + up8sum;
+    for (int d = 0; d < D; ++d) {
+      double pv8 = 0.0, hv8 = 0.0;
+      for (int c = 0; c < n; ++c) {
+        pv8 += pq[c] * a->v8[(kvbase + c0 + c) * D + d];
+        if (!mask[c]) hv8 += exp2(t[c] - m_new) * a->v8[(kvbase + c0 + c) * D + d];
+      }
+      acc[d] = alpha * acc[d] + w * pv8;
+      hacc[d] = alpha * hacc[d] + hv8;
+    }
+    m = m_new;
+  }
+
+  /* FP16 path last, over the promoted blocks, ascending; the FP16 query
    * row is read only here. */
   if (nsel > 0)
     for (int d = 0; d < D; ++d) qh[d] = tho_half_to_double(a->q16[qoff + d]);
@@ -779,6 +991,7 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
   if (u_row)
     for (int d = 0; d < D; ++d) u_row[d] = uacc[d] / l + fabs(o_row[d]) * ul / l;
   if (lse_out) *lse_out = m * THO_LN2 + log(l);
+  free(q8);
   free(hacc);
   free(uacc);
   free(q4);
@@ -797,11 +1010,15 @@ static void tho_attention_impl(const uint16_t* q16, const uint16_t* k16, const u
                                const uint8_t* q4c, const uint8_t* q4s, const float* q4t,
                                const uint8_t* k4c, const uint8_t* k4s, const float* k4t,
                                const uint8_t* v4c, const uint8_t* v4s, const float* v4t, int fmt,
-                               const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq,
+                               const int32_t* idx, const int32_t* cnt, int kmax,
+                               const uint8_t* q8c, const uint8_t* q8s, const uint8_t* k8c,
+                               const uint8_t* k8s, const uint8_t* v8c, const uint8_t* v8s,
+                               const int32_t* idx2, const int32_t* cnt2, int kmax2, int B, int Hq,
                                int Hkv, int S, int Sk, int D, int bq, int bk, int causal,
                                double sm_scale, const int32_t* work, int nwork, double* o,
                                double* lse, double* u, double* ohp) {
   tho_attn_args a;
+  memset(&a, 0, sizeof a);
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -830,6 +1047,20 @@ static void tho_attention_impl(const uint16_t* q16, const uint16_t* k16, const u
   a.q4t = q4t;
   a.k4 = k4;
   a.v4 = v4;
+  double *k8 = NULL, *v8 = NULL;
+  if (idx2) {
+    k8 = (double*)malloc(sizeof(double) * (size_t)B * Hkv * Sk * D);
+    v8 = (double*)malloc(sizeof(double) * (size_t)B * Hkv * Sk * D);
+    tho_dequantize_fp8(k8c, k8s, B, Hkv, Sk, D, THO_AXIS_D, k8);
+    tho_dequantize_fp8(v8c, v8s, B, Hkv, Sk, D, THO_AXIS_S, v8);
+    a.idx2 = idx2;
+    a.cnt2 = cnt2;
+    a.kmax2 = kmax2;
+    a.q8c = q8c;
+    a.q8s = q8s;
+    a.k8 = k8;
+    a.v8 = v8;
+  }
   int nq = tho_cdiv(S, bq);
   int total = work ? nwork : B * Hq * nq;
 #pragma omp parallel for schedule(dynamic, 1)
@@ -851,6 +1082,8 @@ static void tho_attention_impl(const uint16_t* q16, const uint16_t* k16, const u
                      ohp ? ohp + row * D : NULL);
     }
   }
+  free(v8);
+  free(k8);
   free(v4);
   free(k4);
 }
@@ -863,7 +1096,26 @@ void tho_attention_kv(const uint16_t* q16, const uint16_t* k16, const uint16_t* 
                       double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
                       double* u) {
   tho_attention_impl(q16, k16, v16, q4c, q4s, q4t, k4c, k4s, k4t, v4c, v4s, v4t, fmt, idx, cnt, kmax,
-                     B, Hq, Hkv, S, Sk, D, bq, bk, causal, sm_scale, work, nwork, o, lse, u, NULL);
+                     NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, B, Hq, Hkv, S, Sk, D, bq, bk,
+                     causal, sm_scale, work, nwork, o, lse, u, NULL);
+}
+
+/* The forward with a middle precision tier (a variant): the blocks idx2
+ * lists and idx does not run on MXFP8 (q8/k8/v8 as written by
+ * tho_quantize_fp8, V along the sequence axis), between the FP4 path and the
+ * FP16 path.  MX format only. */
+void tho_attention_tiers(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
+                         const uint8_t* q4c, const uint8_t* q4s, const uint8_t* k4c,
+                         const uint8_t* k4s, const uint8_t* v4c, const uint8_t* v4s,
+                         const uint8_t* q8c, const uint8_t* q8s, const uint8_t* k8c,
+                         const uint8_t* k8s, const uint8_t* v8c, const uint8_t* v8s,
+                         const int32_t* idx, const int32_t* cnt, int kmax, const int32_t* idx2,
+                         const int32_t* cnt2, int kmax2, int B, int Hq, int Hkv, int S, int D,
+                         int bq, int bk, int causal, double sm_scale, const int32_t* work,
+                         int nwork, double* o, double* lse, double* u) {
+  tho_attention_impl(q16, k16, v16, q4c, q4s, NULL, k4c, k4s, NULL, v4c, v4s, NULL, THO_MX, idx, cnt,
+                     kmax, q8c, q8s, k8c, k8s, v8c, v8s, idx2, cnt2, kmax2, B, Hq, Hkv, S, S, D, bq,
+                     bk, causal, sm_scale, work, nwork, o, lse, u, NULL);
 }
 
 /* The forward with Attn-QAT's extra output: ohp [B,Hq,S,D] receives O', the
@@ -878,7 +1130,8 @@ void tho_attention_hp(const uint16_t* q16, const uint16_t* k16, const uint16_t* 
                       double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
                       double* ohp) {
   tho_attention_impl(q16, k16, v16, q4c, q4s, q4t, k4c, k4s, k4t, v4c, v4s, v4t, fmt, idx, cnt, kmax,
-                     B, Hq, Hkv, S, S, D, bq, bk, causal, sm_scale, work, nwork, o, lse, NULL, ohp);
+                     NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, B, Hq, Hkv, S, S, D, bq, bk,
+                     causal, sm_scale, work, nwork, o, lse, NULL, ohp);
 }
 
 void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
@@ -1060,6 +1313,7 @@ void tho_attention_bwd(const uint16_t* q16, const uint16_t* k16, const uint16_t*
                        const int32_t* qwork, int nqwork, const int32_t* kwork, int nkwork,
                        double* dq, double* dk, double* dv, double* udv) {
   tho_attn_args a;
+  memset(&a, 0, sizeof a);
   double *k16d, *v16d;
   tho_bwd_setup(&a, q16, k16, v16, q4c, q4s, q4t, k4c, k4s, k4t, v4c, v4s, v4t, fmt, idx, cnt, kmax,
                 B, Hq, Hkv, S, D, bq, bk, causal, sm_scale, &k16d, &v16d);
@@ -1171,6 +1425,7 @@ void tho_row_probs(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16
                    double sm_scale, const double* lse, int b, int hq, int r, int32_t* kind,
                    double* p, double* pt) {
   tho_attn_args a;
+  memset(&a, 0, sizeof a);
   double *k16d, *v16d;
   tho_bwd_setup(&a, q16, k16, v16, q4c, q4s, q4t, k4c, k4s, k4t, v4c, v4s, v4t, fmt, idx, cnt, kmax,
                 B, Hq, Hkv, S, D, bq, bk, causal, sm_scale, &k16d, &v16d);

@@ -88,6 +88,25 @@ void tho_row_probs(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16
                    int B, int Hq, int Hkv, int S, int D, int bq, int bk, int causal,
                    double sm_scale, const double* lse, int b, int hq, int r, int32_t* kind,
                    double* p, double* pt);
+/* Middle precision tier (a variant; MX format): MXFP8 tensors and the
+ * forward with the blocks idx2 lists and idx does not on the FP8 path. */
+int tho_mx8_exponent(double amax);
+int tho_e4m3_encode_signed(double x, double s);
+void tho_quantize_fp8(const uint16_t* x16, int B, int H, int S, int D, int axis, uint8_t* codes,
+                      uint8_t* scales);
+void tho_dequant8_row(const uint8_t* codes, const uint8_t* scales, size_t bh, int S, int D, int s,
+                      double* out);
+void tho_dequantize_fp8(const uint8_t* codes, const uint8_t* scales, int B, int H, int S, int D,
+                        int axis, double* out);
+void tho_attention_tiers(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
+                         const uint8_t* q4c, const uint8_t* q4s, const uint8_t* k4c,
+                         const uint8_t* k4s, const uint8_t* v4c, const uint8_t* v4s,
+                         const uint8_t* q8c, const uint8_t* q8s, const uint8_t* k8c,
+                         const uint8_t* k8s, const uint8_t* v8c, const uint8_t* v8s,
+                         const int32_t* idx, const int32_t* cnt, int kmax, const int32_t* idx2,
+                         const int32_t* cnt2, int kmax2, int B, int Hq, int Hkv, int S, int D,
+                         int bq, int bk, int causal, double sm_scale, const int32_t* work,
+                         int nwork, double* o, double* lse, double* u);
 void tho_fp4_scores(const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
                     const uint8_t* k4s, const float* k4t, int fmt, int S, int D, int r, int c0,
                     int c1, double* out);

@@ -86,6 +86,59 @@ def decode_fp4(codes_u8, scales_u8, tensor_scale, fmt, axis, shape):
     return np.swapaxes(vals[..., :S], -1, -2)
 
 
+def mx8_exponent(amax):
+    """MXFP8 shared exponent: the largest power of two not above amax over
+    E4M3's largest power of two, 2^8 (OCP MX); amax = 0 gives -127."""
+    amax = np.asarray(amax, np.float64)
+    _, e = np.frexp(np.where(amax > 0, amax, 1.0))
+    x = np.clip(e - 1 - 8, -127, 127)
+    return np.where(amax > 0, x, -127)
+
+
+def fp8_quantize(x, axis):
+    """MXFP8 restated: groups of 32 along D (axis 0) or along the sequence
+    (axis 1, stored transposed and padded to 64 with zeros); the element code
+    is the brute-force nearest E4M3 value of |x| / 2^X (ties to the even code,
+    saturating at 448) with the sign bit of x."""
+    x = np.asarray(x, np.float64)
+    B, H, S, D = x.shape
+    if axis == 1:
+        Sp = -(-S // 64) * 64
+        xt = np.zeros((B, H, D, Sp))
+        xt[..., :S] = np.swapaxes(x, -1, -2)
+        x = xt
+    g = x.reshape(*x.shape[:-1], -1, 32)
+    X = mx8_exponent(np.abs(g).max(-1))
+    q = np.abs(g) / 2.0 ** X[..., None]
+    codes = nearest_code(q, E4M3_POS) | np.where(np.signbit(g), 0x80, 0)
+    return codes.reshape(x.shape).astype(np.uint8), (X + 127).astype(np.uint8)
+
+
+def decode_fp8(codes_u8, scales_u8, axis, shape):
+    """MXFP8 codes (one E4M3 byte each) and E8M0 scales to fp64 [B,H,S,D]."""
+    B, H, S, D = shape
+    mag = E4M3_POS[np.minimum(codes_u8 & 0x7F, 126)]
+    vals = np.where(codes_u8 & 0x80, -mag, mag) * np.repeat(2.0 ** (scales_u8.astype(np.float64) - 127), 32, -1)
+    if axis == 0:
+        return vals
+    return np.swapaxes(vals[..., :S], -1, -2)
+
+
+def quantize_p_tile8(t, mask):
+    """P of a middle-tier (MXFP8) tile restated: v = 2^(t - ceil(max t)),
+    per 32 keys X = mx8_exponent(max v), brute-force E4M3 codes of v / 2^X.
+    Returns (pq, ref): probabilities relative to 2^ref."""
+    mt = np.max(np.where(mask, -np.inf, t))
+    z = np.ceil(mt)
+    v = np.where(mask, 0.0, np.exp2(np.where(mask, 0, t) - z))
+    pq = np.zeros(len(t))
+    for g0 in range(0, len(t), 32):
+        seg = v[g0:g0 + 32]
+        s2 = 2.0 ** mx8_exponent(seg.max())
+        pq[g0:g0 + 32] = E4M3_POS[nearest_code(seg / s2, E4M3_POS)] * s2
+    return pq, z
+
+
 def valid_blocks(i, S, bq, bk, causal, Sk=None):
     """Key blocks query block i may see; with Sk keys (default S) the S
     queries are the last S positions of the key sequence."""
@@ -127,14 +180,16 @@ def quantize_p_tile(t, mask, fmt):
 
 
 def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal, sm_scale,
-                       perturb=None):
+                       perturb=None, mid=None):
     """Dense two-pass restatement of the forward pass: every score first,
     then one global maximum per row, then the weighted sum.  q4/k4/v4 and
     q16/k16/v16 are fp64 [B,H,S,D] (dequantised FP4 / decoded fp16).
     perturb(t, a) -> t', if given, moves every score (the rounding decisions
     of P, the row sum and the NVFP4 level-1 factor alike), as a
     lower-precision evaluation would; a holds each score's sum of product
-    magnitudes in the same log2 units."""
+    magnitudes in the same log2 units.  mid = (q8, k8, v8, idx2, cnt2) adds the
+    middle tier: blocks idx2 lists and idx does not use the decoded MXFP8
+    operands and the E4M3 P quantiser (MX format)."""
     B, Hq, S, D = q4.shape
     Hkv, Sk = k4.shape[1], k4.shape[2]
     G = Hq // Hkv
@@ -149,8 +204,13 @@ def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal,
             t16 = None if q16 is None else (q16[b, hq] @ k16[b, hk].T) * sm_scale * LOG2E
             a4 = (np.abs(q4[b, hq]) @ np.abs(k4[b, hk]).T) * sm_scale * LOG2E
             a16 = None if q16 is None else (np.abs(q16[b, hq]) @ np.abs(k16[b, hk]).T) * sm_scale * LOG2E
+            if mid is not None:
+                t8 = (mid[0][b, hq] @ mid[1][b, hk].T) * sm_scale * LOG2E
+                a8 = (np.abs(mid[0][b, hq]) @ np.abs(mid[1][b, hk]).T) * sm_scale * LOG2E
             for i in range(nq):
                 promoted = set(int(j) for j in idx[b, hq, i, : cnt[b, hq, i]])
+                tier8 = set() if mid is None else set(int(j) for j in mid[3][b, hq, i, : mid[4][b, hq, i]])
+                tier8 -= promoted
                 nval = valid_blocks(i, S, bq, bk, causal, Sk)
                 for r in range(i * bq, min(S, (i + 1) * bq)):
                     tiles = []  # (t row, mask, is16, c0)
@@ -160,16 +220,20 @@ def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal,
                         mask = (keys > r + off) if causal else np.zeros(len(keys), bool)
                         if mask.all():
                             continue
-                        src, asrc = (t16, a16) if j in promoted else (t4, a4)
-                        tiles.append((src[r, c0:c1], mask, j in promoted, c0, c1, asrc[r, c0:c1]))
+                        kind = 16 if j in promoted else (8 if j in tier8 else 4)
+                        src, asrc = {16: (t16, a16), 8: (t8, a8) if mid is not None else None, 4: (t4, a4)}[kind]
+                        tiles.append((src[r, c0:c1], mask, kind, c0, c1, asrc[r, c0:c1]))
                     M = max(np.max(np.where(m, -np.inf, t)) for t, m, _, _, _, _ in tiles)
                     l = 0.0
                     acc = np.zeros(D)
-                    for t, m, is16, c0, c1, a in tiles:
+                    for t, m, kind, c0, c1, a in tiles:
                         tq = t if perturb is None else np.where(m, t, perturb(t, a))
                         e = np.where(m, 0.0, np.exp2(np.where(m, 0, tq) - M))
                         l += e.sum()
-                        if is16:
+                        if kind == 8:
+                            pq, ref = quantize_p_tile8(tq, m)
+                            acc += (pq * np.exp2(ref - M)) @ mid[2][b, hk, c0:c1]
+                        elif kind == 16:
                             z = np.ceil(M)
                             p = np.where(m, 0.0, fp16_round(np.exp2(np.where(m, 0, tq) - z))) * np.exp2(z - M)
                             acc += p @ v16[b, hk, c0:c1]

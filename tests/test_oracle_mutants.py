@@ -50,6 +50,14 @@ MUTANTS = {
     "bwd_dk_unscaled": ("dk[key * D + d] += sm_scale * dS * qv[d];", "dk[key * D + d] += dS * qv[d];"),
     "bwd_one_head_per_key_head": ("for (int hq = hk * G; hq < (hk + 1) * G; ++hq)",
                                   "for (int hq = hk; hq < hk + 1; ++hq)"),
+    # middle (FP8) tier
+    "fp8_exponent_offset": ("int x = (e - 1) - 8;", "int x = (e - 1) - 7;"),
+    "fp8_tier_recomputes_fp16_blocks": ("    if (in16) continue;\n", ""),
+    "fp8_tier_uses_fp4_query": ("s8 += q8[d] * kv[d];", "s8 += q4[d] * kv[d];"),
+    "fp8_tier_p_quantised_as_fp4": ("tho_quantize_p_tile8(t, ta, mask, n, mt, pq, u_row ? dq : NULL, &ref);",
+                                    "tho_quantize_p_tile(t, ta, mask, n, THO_MX, mt, pq, u_row ? dq : NULL, &ref);"),
+    "fp4_pass_keeps_fp8_blocks": ("      ++sp2;\n      listed = 1;", "      ++sp2;\n      listed = 0;"),
+    "fp8_v_not_transposed": ("e = (size_t)bh * D * Sp + (size_t)d * Sp + s;", "e = (size_t)bh * D * Sp + (size_t)s * D + d;"),
     "ohp_from_quantised_p": ("if (!mask[c]) hv += exp2(t[c] - m_new) * a->v4[(kvbase + c0 + c) * D + d];",
                              "if (!mask[c]) hv += w * pq[c] * a->v4[(kvbase + c0 + c) * D + d];"),
 }
@@ -70,6 +78,7 @@ def test_mutant_is_caught(tmp_path, name):
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_formats.py", "tests/test_oracle_select.py",
                         "tests/test_oracle_attention.py", "tests/test_oracle_decode.py",
-                        "tests/test_oracle_select_head.py", "tests/test_oracle_backward.py"],
+                        "tests/test_oracle_select_head.py", "tests/test_oracle_backward.py",
+                        "tests/test_oracle_fp8.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
