@@ -15,7 +15,7 @@ EXPORTS = ("thrift_select_kmax", "thrift_select_workspace_bytes", "thrift_select
            "thrift_select_head_kmax", "thrift_select_head_workspace_bytes", "thrift_select_blocks_head",
            "thrift_quantize_means_workspace_bytes", "thrift_quantize_fp4_means",
            "thrift_quantize_workspace_bytes", "thrift_quantize_fp4", "thrift_quantize_fp4_range", "thrift_cache_update",
-           "thrift_attention_fwd",
+           "thrift_attention_fwd", "thrift_quantize_fp8", "thrift_attention_fwd_tiered",
            "thrift_attention_decode_workspace_bytes", "thrift_attention_decode",
            "thrift_attention_bwd_workspace_bytes", "thrift_attention_fwd_hp", "thrift_attention_bwd",
            "thrift_status_string")
@@ -81,6 +81,10 @@ def load():
         L.thrift_quantize_fp4.argtypes = [P, I, I, I, I, I, I, P, P, P, P, SZ, P]
         L.thrift_attention_fwd.restype = I
         L.thrift_attention_fwd.argtypes = [P] * 12 + [I, P, P] + [I] * 9 + [F, P, I, P, P]
+        L.thrift_quantize_fp8.restype = I
+        L.thrift_quantize_fp8.argtypes = [P, I, I, I, I, I, P, P, P]
+        L.thrift_attention_fwd_tiered.restype = I
+        L.thrift_attention_fwd_tiered.argtypes = [P] * 15 + [P, P, I, P, P, I] + [I] * 8 + [F, P, I, P, P]
         L.thrift_attention_bwd_workspace_bytes.restype = SZ
         L.thrift_attention_bwd_workspace_bytes.argtypes = [I] * 6
         L.thrift_attention_fwd_hp.restype = I

@@ -22,7 +22,8 @@ __all__ = ["thrift_select_kmax", "thrift_select_blocks", "thrift_block_means",
            "thrift_attention_fwd", "thrift_attention_decode", "thrift_decode", "FP4Tensor",
            "fp4_transposed", "thrift_forward", "thrift_attention_bwd_workspace", "thrift_attention_fwd_hp",
            "thrift_attention_bwd", "THRIFT_NVFP4", "THRIFT_MXFP4", "THRIFT_NVFP4_MXP", "THRIFT_GROUP_D",
-           "THRIFT_GROUP_S", "ThriftError"]
+           "THRIFT_GROUP_S", "ThriftError", "FP8Tensor", "thrift_quantize_fp8", "thrift_attention_fwd_tiered",
+           "thrift_forward_tiered"]
 
 
 def _ptr(t):
@@ -267,6 +268,59 @@ def thrift_attention_fwd(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Ten
     return (out, lse) if with_lse else out
 
 
+@dataclass
+class FP8Tensor:
+    codes: torch.Tensor
+    scales: torch.Tensor
+    axis: int
+
+
+def thrift_quantize_fp8(x16, axis=THRIFT_GROUP_D) -> FP8Tensor:
+    """FP16 -> MXFP8 (E4M3 codes, E8M0 scale per 32) for the middle tier:
+    along D codes [B,H,S,D] and scales [B,H,S,D/32]; along S (V) codes
+    [B,H,D,Sp] and scales [B,H,D,Sp/32]."""
+    _check(x16, torch.float16, "x16")
+    B, H, S, D = x16.shape
+    dev = x16.device
+    if axis == THRIFT_GROUP_D:
+        codes = torch.empty((B, H, S, D), dtype=torch.uint8, device=dev)
+        scales = torch.empty((B, H, S, D // 32), dtype=torch.uint8, device=dev)
+    else:
+        Sp = -(-S // 64) * 64
+        codes = torch.empty((B, H, D, Sp), dtype=torch.uint8, device=dev)
+        scales = torch.empty((B, H, D, Sp // 32), dtype=torch.uint8, device=dev)
+    _call("thrift_quantize_fp8", _ptr(x16), B, H, S, D, axis, _ptr(codes), _ptr(scales), _stream())
+    return FP8Tensor(codes, scales, axis)
+
+
+def thrift_attention_fwd_tiered(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, q8: FP8Tensor,
+                                k8: FP8Tensor, v8: FP8Tensor, idx, cnt, idx2, cnt2, block_q=128, block_k=64,
+                                causal=True, sm_scale=None, out_fp32=False, with_lse=False, out=None):
+    """Three-tier forward (MX format): blocks idx lists in FP16, blocks idx2
+    lists and idx does not in MXFP8, the rest in MXFP4."""
+    B, Hq, S, D = q8.codes.shape
+    Hkv = k8.codes.shape[1]
+    if q4.fmt != THRIFT_MXFP4:
+        raise ValueError("the middle tier is built for the MX format")
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    for name, t in (("q16", q16), ("k16", k16), ("v16", v16)):
+        if t is not None:
+            _check(t, torch.float16, name)
+    for name, t in (("idx", idx), ("cnt", cnt), ("idx2", idx2), ("cnt2", cnt2)):
+        _check(t, torch.int32, name)
+    dev = q8.codes.device
+    if out is None:
+        out = torch.empty((B, Hq, S, D), dtype=torch.float32 if out_fp32 else torch.float16, device=dev)
+    lse = torch.empty((B, Hq, S), dtype=torch.float32, device=dev) if with_lse else None
+    _call("thrift_attention_fwd_tiered", _ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
+          _ptr(k4.codes), _ptr(k4.scales), _ptr(v4.codes), _ptr(v4.scales), _ptr(q8.codes), _ptr(q8.scales),
+          _ptr(k8.codes), _ptr(k8.scales), _ptr(v8.codes), _ptr(v8.scales), _ptr(idx), _ptr(cnt),
+          idx.shape[-1], _ptr(idx2), _ptr(cnt2), idx2.shape[-1], B, Hq, Hkv, S, D, block_q, block_k,
+          int(causal), float(sm_scale), _ptr(out), int(out.dtype == torch.float32), _ptr(lse), _stream())
+    return (out, lse) if with_lse else out
+
+
 def thrift_attention_bwd_workspace(B, Hq, Hkv, S, D, block_q=128, device="cuda"):
     """Workspace tensor for thrift_attention_fwd_hp / thrift_attention_bwd."""
     n = _lib.load().thrift_attention_bwd_workspace_bytes(B, Hq, Hkv, S, D, block_q)
@@ -378,3 +432,21 @@ def thrift_forward(q16, k16, v16, fmt=THRIFT_MXFP4, block_q=128, block_k=64, cau
     idx, cnt = sel(qbar, kbar, q16.shape[2], k16.shape[2], block_q, block_k, causal, topk_count, topk_bp)
     return thrift_attention_fwd(q16, k16, v16, q4, k4, v4, idx, cnt, block_q, block_k, causal,
                                 sm_scale, out_fp32, with_lse)
+
+
+def thrift_forward_tiered(q16, k16, v16, block_q=128, block_k=64, causal=True, bp16=500, bp8=1000,
+                          sm_scale=None, out_fp32=False, with_lse=False):
+    """The three-tier path (MX format): block means and FP4 codes of Q and K
+    in one pass, MXFP8 copies of Q, K and V, the selection from the means
+    under bp16 (the FP16 tier) and under bp16 + bp8 (FP16 and FP8 tiers
+    together), then the three-tier attention."""
+    q4, qbar = thrift_quantize_fp4_means(q16, THRIFT_MXFP4, block_q)
+    k4, kbar = thrift_quantize_fp4_means(k16, THRIFT_MXFP4, block_k)
+    v4 = thrift_quantize_fp4(v16, THRIFT_GROUP_S, THRIFT_MXFP4)
+    q8, k8 = thrift_quantize_fp8(q16, THRIFT_GROUP_D), thrift_quantize_fp8(k16, THRIFT_GROUP_D)
+    v8 = thrift_quantize_fp8(v16, THRIFT_GROUP_S)
+    Sq, Sk = q16.shape[2], k16.shape[2]
+    idx, cnt = thrift_select_blocks_means(qbar, kbar, Sq, Sk, block_q, block_k, causal, -1, bp16)
+    idx2, cnt2 = thrift_select_blocks_means(qbar, kbar, Sq, Sk, block_q, block_k, causal, -1, bp16 + bp8)
+    return thrift_attention_fwd_tiered(q16, k16, v16, q4, k4, v4, q8, k8, v8, idx, cnt, idx2, cnt2, block_q,
+                                       block_k, causal, sm_scale, out_fp32, with_lse)

@@ -67,6 +67,18 @@ struct AttnArgs {
   float* lse;
   int kmax, B, Hq, Hkv, S, Sp, nq, causal, o_fp32;
   float sm_log2;  // sm_scale * log2(e)
+  // middle (MXFP8) tier, read by the three-tier kernels only: codes one byte
+  // per element (Q, K [B,H,S,D]; V^T [B,H,D,Sp]) and E8M0 scales per 32;
+  // idx2/cnt2 list the FP16 and FP8 tiers' blocks together
+  const uint8_t* q8c;
+  const uint8_t* q8s;
+  const uint8_t* k8c;
+  const uint8_t* k8s;
+  const uint8_t* v8c;
+  const uint8_t* v8s;
+  const int32_t* idx2;
+  const int32_t* cnt2;
+  int kmax2;
 };
 
 // ---- MX stage layout -------------------------------------------------------
@@ -495,6 +507,78 @@ namespace thrift {
 // the buffer resource (scalar work).  The resource's record count ends at the
 // tensor's end, so key rows past S (last block) read as out of range and
 // never touch memory; their scores are masked.
+// ---- middle-tier (MXFP8) tile ------------------------------------------------------
+//
+// gfx950's block-scaled matrix instruction does not sum E4M3 products exactly:
+// its error reaches about 2^-12.6 of the sum of the products' magnitudes
+// (measured on random E4M3 operands), where E2M1 products, spanning few
+// binades, come out exact.  The middle tier therefore runs like NVFP4's FP4
+// path: its tiles are decoded to fp16 in LDS (an E4M3 value times a power of
+// two has 4 significant bits, exact in fp16 for every group whose maximum is
+// at least 2^-7; the elements of smaller groups round to fp16's 2^-24 grid)
+// and multiplied on the fp16 matrix cores; P is quantised to E4M3 and held
+// as the fp16 value code * 2^exponent.
+
+// 8 E4M3 codes (two dwords, byte u = element u) times the power of two
+// `scale`, to fp16: decoded and scaled exactly in fp32, then rounded to fp16.
+typedef float v2f_t __attribute__((ext_vector_type(2)));
+__device__ inline v8h fp8x8_to_h(uint32_t lo, uint32_t hi, float scale) {
+  const v2f_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)lo, 1.0f, false);
+  const v2f_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)lo, 1.0f, true);
+  const v2f_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)hi, 1.0f, false);
+  const v2f_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)hi, 1.0f, true);
+  return v8h{(_Float16)(a.x * scale), (_Float16)(a.y * scale), (_Float16)(b.x * scale), (_Float16)(b.y * scale),
+             (_Float16)(c.x * scale), (_Float16)(c.y * scale), (_Float16)(d.x * scale), (_Float16)(d.y * scale)};
+}
+
+// Promoted tile on the middle tier: scores from the decoded fp16 stage; this
+// lane's 32 keys are one P group (its E8M0 exponent floor(log2(max p)) - 8);
+// elements clamped to 448 times the scale, rounded to E4M3 by the scaled FP8
+// conversion (nearest even) and decoded back exactly; times the decoded V^T.
+template <int D>
+__device__ inline void fp8_tile(RowState<D>& st, const char* stage, const v8h* qh, float c, int key0, int qrow,
+                                int S, int causal, bool need_mask, int lane) {
+  const int hi = lane >> 5;
+  v16f s[2];
+  qk_f16<D>(s, stage, qh, lane);
+  if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
+  const float gmax = fmaxf(max16(s[0]), max16(s[1]));
+  maybe_rescale<D>(st, gmax, c);
+  const float nm = -st.m;
+  float lsum = 0.0f;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float p = exp2_fast(__builtin_fmaf(s[mt][i], c, nm));
+      s[mt][i] = p;
+      lsum += p;
+    }
+  st.l += lsum;
+  const uint32_t E = (__float_as_uint(exp2_fast(__builtin_fmaf(gmax, c, nm))) >> 23) & 0xFF;
+  const uint32_t psc = E > 9 ? E - 8 : 1;
+  const float sf = __uint_as_float(psc << 23);
+  const float cap = 448.0f * sf;
+  // P^T operand as pv_f16 takes it: step st, element u = key hi*32 + 8*st + u
+  v8h pB[4];
+#pragma unroll
+  for (int stp = 0; stp < 4; ++stp) {
+    const v16f& x = s[stp >> 1];
+    const int o = (stp & 1) * 8;
+    uint32_t w[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      v2s_t y = {0, 0};
+      y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, fminf(x[o + 4 * h], cap), fminf(x[o + 4 * h + 1], cap), sf, false);
+      y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, fminf(x[o + 4 * h + 2], cap), fminf(x[o + 4 * h + 3], cap), sf,
+                                                    true);
+      w[h] = __builtin_bit_cast(uint32_t, y);
+    }
+    pB[stp] = fp8x8_to_h(w[0], w[1], sf);
+  }
+  pv_f16<D>(st, (const _Float16*)(stage + Lds<D>::VT), pB, lane);
+}
+
 template <int D, int NW>
 struct MxDma {
   using M = MxStage<D>;
@@ -652,6 +736,68 @@ struct F16Stager {
   }
 };
 
+// MXFP8 tile of key block j decoded to the fp16 stage (K rows at kslot, V^T
+// rows), as F16Stager lays it out: each thread takes 16-byte chunks of codes
+// with the E8M0 byte of their group.  K rows past S read as zeros; V^T rows
+// are padded to Sp with zeros by the quantiser.
+template <int D, int NT>
+struct F8Stager {
+  static constexpr int NK = kBk * D / 16;  // 16-code chunks of K (row, 16 channels)
+  static constexpr int NV = D * kBk / 16;  // 16-code chunks of V^T (d, 16 keys)
+  static constexpr int PK = (NK + NT - 1) / NT, PV = (NV + NT - 1) / NT;
+  v4i kr[PK], vr[PV];
+  uint8_t ks[PK], vs[PV];
+
+  __device__ void load(const AttnArgs& a, size_t bhk, int j, int t) {
+#pragma unroll
+    for (int p = 0; p < PK; ++p) {
+      const int c = t + p * NT, row = c / (D / 16), col = (c % (D / 16)) * 16, key = j * kBk + row;
+      kr[p] = v4i{};
+      ks[p] = 127;
+      if (c < NK && key < a.S) {
+        kr[p] = *(const v4i*)(a.k8c + (bhk * a.S + key) * D + col);
+        ks[p] = a.k8s[(bhk * a.S + key) * (D / 32) + col / 32];
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PV; ++p) {
+      const int c = t + p * NT, d = c / (kBk / 16), k0 = (c % (kBk / 16)) * 16;
+      vr[p] = v4i{};
+      vs[p] = 127;
+      if (c < NV) {
+        vr[p] = *(const v4i*)(a.v8c + (bhk * D + d) * a.Sp + j * kBk + k0);
+        vs[p] = a.v8s[(bhk * D + d) * (a.Sp / 32) + (j * kBk + k0) / 32];
+      }
+    }
+  }
+
+  __device__ void store(char* stage, int t) const {
+    using L = Lds<D>;
+    _Float16* kh = (_Float16*)(stage + L::KH);
+    _Float16* vt = (_Float16*)(stage + L::VT);
+#pragma unroll
+    for (int p = 0; p < PK; ++p) {
+      const int c = t + p * NT;
+      if (c < NK) {
+        const float sc = __uint_as_float((uint32_t)ks[p] << 23);
+        _Float16* dst = kh + kslot(c / (D / 16)) * L::KROWH + (c % (D / 16)) * 16;
+        *(v8h*)dst = fp8x8_to_h((uint32_t)kr[p].x, (uint32_t)kr[p].y, sc);
+        *(v8h*)(dst + 8) = fp8x8_to_h((uint32_t)kr[p].z, (uint32_t)kr[p].w, sc);
+      }
+    }
+#pragma unroll
+    for (int p = 0; p < PV; ++p) {
+      const int c = t + p * NT;
+      if (c < NV) {
+        const float sc = __uint_as_float((uint32_t)vs[p] << 23);
+        _Float16* dst = vt + (c / (kBk / 16)) * L::VROWH + (c % (kBk / 16)) * 16;
+        *(v8h*)dst = fp8x8_to_h((uint32_t)vr[p].x, (uint32_t)vr[p].y, sc);
+        *(v8h*)(dst + 8) = fp8x8_to_h((uint32_t)vr[p].z, (uint32_t)vr[p].w, sc);
+      }
+    }
+  }
+};
+
 // NVFP4 tile: codes and E4M3 block scales, dequantised exactly to fp16 in LDS
 // (K row-major, V already transposed).  Per-slice scales are applied elsewhere.
 template <int D, int NT>
@@ -758,8 +904,11 @@ __device__ inline bool work_item(const AttnArgs& a, int id, int& i, int& bhq) {
   return true;
 }
 
-template <int D, int NW, int FMT>
+// T8: the three-tier variant (MX only): the blocks idx2 lists and idx does
+// not run on the middle MXFP8 tier, between the FP4 and FP16 paths.
+template <int D, int NW, int FMT, bool T8 = false>
 __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
+  static_assert(!T8 || FMT == THRIFT_MXFP4, "the middle tier is built for the MX format");
   using L = Lds<D>;
   constexpr int NT = NW * 64;
   constexpr int BQ = NW * 32;
@@ -777,16 +926,36 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
   const size_t rowid = (size_t)bhq * a.nq + i;
   int ncnt = a.cnt[rowid];
   ncnt = ncnt < 0 ? 0 : (ncnt > a.kmax ? a.kmax : ncnt);
+  int ncnt2 = 0;
+  if constexpr (T8) {
+    ncnt2 = a.cnt2[rowid];
+    ncnt2 = ncnt2 < 0 ? 0 : (ncnt2 > a.kmax2 ? a.kmax2 : ncnt2);
+  }
   int* prom = (int*)(smem + L::PROM);
-  uint32_t* pbits = (uint32_t*)prom + a.kmax;  // bit j: key block j is promoted
+  int* prom2 = prom + a.kmax;  // three-tier kernels: int[kmax2], the idx2 list
+  // bit j: key block j leaves the FP4 path (promoted to a higher tier)
+  uint32_t* pbits = (uint32_t*)prom2 + (T8 ? a.kmax2 : 0);
   const int nwords = (nvalid + 31) >> 5;
-  for (int e = t; e < nwords; e += NT) pbits[e] = 0;
+  uint32_t* pbits16 = pbits + nwords;  // three-tier kernels: bit j: block j is FP16
+  for (int e = t; e < nwords; e += NT) {
+    pbits[e] = 0;
+    if constexpr (T8) pbits16[e] = 0;
+  }
   __syncthreads();
   for (int e = t; e < ncnt; e += NT) {
     const int j = a.idx[rowid * a.kmax + e];
     prom[e] = j;
-    if (j >= 0 && j < nvalid) atomicOr(&pbits[j >> 5], 1u << (j & 31));
+    if (j >= 0 && j < nvalid) {
+      atomicOr(&pbits[j >> 5], 1u << (j & 31));
+      if constexpr (T8) atomicOr(&pbits16[j >> 5], 1u << (j & 31));
+    }
   }
+  if constexpr (T8)
+    for (int e = t; e < ncnt2; e += NT) {
+      const int j = a.idx2[rowid * a.kmax2 + e];
+      prom2[e] = j;
+      if (j >= 0 && j < nvalid) atomicOr(&pbits[j >> 5], 1u << (j & 31));
+    }
   __syncthreads();
 
   RowState<D> st;
@@ -840,7 +1009,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
         return (a.causal && key0 + kBk - 1 > q0) || key0 + kBk > S;
       };
       auto slot = [&](int k) { return smem + (k % 3) * M::SIZE; };
-      if (ncnt < nvalid) {
+      if (T8 || ncnt < nvalid) {
         const int nst = (nvalid + 1) / 2;  // stages
         dma.issue(slot(0), 0);
         dma.finish(slot(0), t);
@@ -944,6 +1113,50 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
     }
   }
 
+  // ---------------- middle tier (MXFP8): idx2's blocks not on the FP16 path ----------------
+  if constexpr (T8) {
+    if (ncnt2 > 0) {
+      // the query row decoded to fp16 in the fp16 path's operand order
+      const size_t qoff = (size_t)bhq * S + (qvalid ? qrow : 0);
+      v8h qh8[D / 16];
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        qh8[kk] = v8h{};
+        if (qvalid) {
+          const int ch = kk * 16 + hi * 8;
+          const uint2 cw = *(const uint2*)(a.q8c + qoff * D + ch);
+          qh8[kk] = fp8x8_to_h(cw.x, cw.y, __uint_as_float((uint32_t)a.q8s[qoff * (D / 32) + ch / 32] << 23));
+        }
+      }
+      auto tier8_j = [&](int p) {
+        const int j = prom2[p];
+        return j >= 0 && j < nvalid && !((pbits16[j >> 5] >> (j & 31)) & 1u) ? j : -1;
+      };
+      F8Stager<D, NT> stg;
+      int jc = tier8_j(0);
+      if (jc >= 0) stg.load(a, bhk, jc, t);
+      if (jc >= 0) stg.store(smem, t);
+      __syncthreads();
+      int buf = 0;
+      for (int p = 0; p < ncnt2; ++p) {
+        const bool more = p + 1 < ncnt2;
+        const int jn = more ? tier8_j(p + 1) : -1;
+        if (jn >= 0) stg.load(a, bhk, jn, t);
+        if (jc >= 0) {
+          const int key0 = jc * kBk;
+          const bool active = !a.causal || key0 <= q0 + 31;
+          const bool need_mask = (a.causal && key0 + kBk - 1 > q0) || key0 + kBk > S;
+          if (active)
+            fp8_tile<D>(st, smem + buf * L::STAGE, qh8, a.sm_log2, key0, qrow, S, a.causal, need_mask, lane);
+        }
+        if (jn >= 0) stg.store(smem + (buf ^ 1) * L::STAGE, t);
+        __syncthreads();
+        buf ^= 1;
+        jc = jn;
+      }
+    }
+  }
+
   // ---------------- FP16 path: promoted blocks only ----------------
   if (ncnt > 0) {
     v8h qh[D / 16];
@@ -999,13 +1212,14 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
   }
 }
 
-template <int D, int NW, int FMT>
+template <int D, int NW, int FMT, bool T8 = false>
 static thrift_status launch_attn(const AttnArgs& a, hipStream_t stream) {
   using L = Lds<D>;
-  const size_t lds = (size_t)L::PROM + (size_t)a.kmax * 4 + (size_t)((a.S + 64 * 32 - 1) / (64 * 32)) * 4;
+  const size_t nwords = (size_t)((a.S + 64 * 32 - 1) / (64 * 32));
+  const size_t lds = (size_t)L::PROM + (size_t)a.kmax * 4 + (T8 ? (size_t)a.kmax2 * 4 + nwords * 4 : 0) + nwords * 4;
   static std::atomic<uint64_t> configured{0};
   if (once_per_device(configured, [] {
-        return hipFuncSetAttribute((const void*)attn_fwd_kernel<D, NW, FMT>,
+        return hipFuncSetAttribute((const void*)attn_fwd_kernel<D, NW, FMT, T8>,
                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess
                    ? THRIFT_OK
                    : THRIFT_EHIP;
@@ -1013,7 +1227,7 @@ static thrift_status launch_attn(const AttnArgs& a, hipStream_t stream) {
     return THRIFT_EHIP;
   const int items = a.B * a.Hq * a.nq;
   const int grid = (items + kXcds - 1) / kXcds * kXcds;
-  attn_fwd_kernel<D, NW, FMT><<<grid, NW * 64, lds, stream>>>(a);
+  attn_fwd_kernel<D, NW, FMT, T8><<<grid, NW * 64, lds, stream>>>(a);
   return launch_status();
 }
 
@@ -1467,6 +1681,10 @@ template __global__ void attn_fwd_kernel<128, 4, THRIFT_NVFP4_MXP>(AttnArgs);
 template __global__ void attn_fwd_kernel<128, 2, THRIFT_NVFP4_MXP>(AttnArgs);
 template __global__ void attn_fwd_kernel<64, 4, THRIFT_NVFP4_MXP>(AttnArgs);
 template __global__ void attn_fwd_kernel<64, 2, THRIFT_NVFP4_MXP>(AttnArgs);
+template __global__ void attn_fwd_kernel<128, 4, THRIFT_MXFP4, true>(AttnArgs);
+template __global__ void attn_fwd_kernel<128, 2, THRIFT_MXFP4, true>(AttnArgs);
+template __global__ void attn_fwd_kernel<64, 4, THRIFT_MXFP4, true>(AttnArgs);
+template __global__ void attn_fwd_kernel<64, 2, THRIFT_MXFP4, true>(AttnArgs);
 template __global__ void decode_mx_fused_kernel<128>(DecodeArgs, int, int);
 template __global__ void decode_mx_fused_kernel<64>(DecodeArgs, int, int);
 template __global__ void decode_nv4_kernel<128>(DecodeArgs);
@@ -1480,13 +1698,13 @@ template __global__ void decode_merge_kernel<64>(DecodeArgs);
 
 using namespace thrift;
 
-extern "C" thrift_status thrift_attention_fwd(
+static thrift_status make_attn_args(
     const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes,
     const uint8_t* q4_scales, const float* q4_tscale, const uint8_t* k4_codes,
     const uint8_t* k4_scales, const float* k4_tscale, const uint8_t* v4_codes,
     const uint8_t* v4_scales, const float* v4_tscale, thrift_format fmt, const int32_t* idx,
     const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D, int block_q, int block_k,
-    int causal, float sm_scale, void* o, int o_is_fp32, float* lse, hipStream_t stream) {
+    int causal, float sm_scale, void* o, int o_is_fp32, float* lse, AttnArgs& a) {
   if (!q4_codes || !q4_scales || !k4_codes || !k4_scales || !v4_codes || !v4_scales || !idx ||
       !cnt || !o)
     return THRIFT_EINVAL;
@@ -1504,7 +1722,7 @@ extern "C" thrift_status thrift_attention_fwd(
     if (!aligned16(p)) return THRIFT_EALIGN;
   if (any16 && (!aligned16(q16) || !aligned16(k16) || !aligned16(v16))) return THRIFT_EALIGN;
   if (((uintptr_t)q4_scales | (uintptr_t)k4_scales | (uintptr_t)v4_scales) & 3) return THRIFT_EALIGN;
-  AttnArgs a;
+  a = AttnArgs{};
   a.q16 = (const _Float16*)q16;
   a.k16 = (const _Float16*)k16;
   a.v16 = (const _Float16*)v16;
@@ -1531,6 +1749,21 @@ extern "C" thrift_status thrift_attention_fwd(
   a.causal = causal;
   a.o_fp32 = o_is_fp32;
   a.sm_log2 = sm_scale * 1.4426950408889634f;
+  return THRIFT_OK;
+}
+
+extern "C" thrift_status thrift_attention_fwd(
+    const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes,
+    const uint8_t* q4_scales, const float* q4_tscale, const uint8_t* k4_codes,
+    const uint8_t* k4_scales, const float* k4_tscale, const uint8_t* v4_codes,
+    const uint8_t* v4_scales, const float* v4_tscale, thrift_format fmt, const int32_t* idx,
+    const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D, int block_q, int block_k,
+    int causal, float sm_scale, void* o, int o_is_fp32, float* lse, hipStream_t stream) {
+  AttnArgs a;
+  const thrift_status st = make_attn_args(q16, k16, v16, q4_codes, q4_scales, q4_tscale, k4_codes, k4_scales,
+                                          k4_tscale, v4_codes, v4_scales, v4_tscale, fmt, idx, cnt, kmax, B, Hq,
+                                          Hkv, S, D, block_q, block_k, causal, sm_scale, o, o_is_fp32, lse, a);
+  if (st != THRIFT_OK) return st;
   if (fmt == THRIFT_MXFP4) {
     if (D == 128) return block_q == 128 ? launch_attn<128, 4, THRIFT_MXFP4>(a, stream) : launch_attn<128, 2, THRIFT_MXFP4>(a, stream);
     return block_q == 128 ? launch_attn<64, 4, THRIFT_MXFP4>(a, stream) : launch_attn<64, 2, THRIFT_MXFP4>(a, stream);
@@ -1541,6 +1774,41 @@ extern "C" thrift_status thrift_attention_fwd(
   }
   if (D == 128) return block_q == 128 ? launch_attn<128, 4, THRIFT_NVFP4>(a, stream) : launch_attn<128, 2, THRIFT_NVFP4>(a, stream);
   return block_q == 128 ? launch_attn<64, 4, THRIFT_NVFP4>(a, stream) : launch_attn<64, 2, THRIFT_NVFP4>(a, stream);
+}
+
+extern "C" thrift_status thrift_attention_fwd_tiered(
+    const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes, const uint8_t* q4_scales,
+    const uint8_t* k4_codes, const uint8_t* k4_scales, const uint8_t* v4_codes, const uint8_t* v4_scales,
+    const uint8_t* q8_codes, const uint8_t* q8_scales, const uint8_t* k8_codes, const uint8_t* k8_scales,
+    const uint8_t* v8_codes, const uint8_t* v8_scales, const int32_t* idx, const int32_t* cnt, int kmax,
+    const int32_t* idx2, const int32_t* cnt2, int kmax2, int B, int Hq, int Hkv, int S, int D, int block_q,
+    int block_k, int causal, float sm_scale, void* o, int o_is_fp32, float* lse, hipStream_t stream) {
+  if (!q8_codes || !q8_scales || !k8_codes || !k8_scales || !v8_codes || !v8_scales || !idx2 || !cnt2)
+    return THRIFT_EINVAL;
+  if (kmax2 < 1) return THRIFT_EINVAL;
+  AttnArgs a;
+  const thrift_status st = make_attn_args(q16, k16, v16, q4_codes, q4_scales, nullptr, k4_codes, k4_scales,
+                                          nullptr, v4_codes, v4_scales, nullptr, THRIFT_MXFP4, idx, cnt, kmax, B,
+                                          Hq, Hkv, S, D, block_q, block_k, causal, sm_scale, o, o_is_fp32, lse, a);
+  if (st != THRIFT_OK) return st;
+  if (kmax2 > cdiv(S, block_k)) return THRIFT_EUNSUPPORTED;
+  for (const void* p : {(const void*)q8_codes, (const void*)k8_codes, (const void*)v8_codes})
+    if (!aligned16(p)) return THRIFT_EALIGN;
+  if (((uintptr_t)q8_scales | (uintptr_t)k8_scales | (uintptr_t)v8_scales) & 3) return THRIFT_EALIGN;
+  a.q8c = q8_codes;
+  a.q8s = q8_scales;
+  a.k8c = k8_codes;
+  a.k8s = k8_scales;
+  a.v8c = v8_codes;
+  a.v8s = v8_scales;
+  a.idx2 = idx2;
+  a.cnt2 = cnt2;
+  a.kmax2 = kmax2;
+  if (D == 128)
+    return block_q == 128 ? launch_attn<128, 4, THRIFT_MXFP4, true>(a, stream)
+                          : launch_attn<128, 2, THRIFT_MXFP4, true>(a, stream);
+  return block_q == 128 ? launch_attn<64, 4, THRIFT_MXFP4, true>(a, stream)
+                        : launch_attn<64, 2, THRIFT_MXFP4, true>(a, stream);
 }
 
 static size_t decode_part_floats(int B, int Hq, int Hkv, int Sq, int Sk, int D, int kmax,

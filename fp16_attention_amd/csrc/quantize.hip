@@ -381,6 +381,91 @@ __global__ __launch_bounds__(kQThreads) void means_quant_kernel(const _Float16* 
     }
 }
 
+// ---- MXFP8 (the middle precision tier) ------------------------------------------
+//
+// E4M3 elements under one E8M0 scale per 32: exponent floor(log2 amax) - 8
+// from the fp32 exponent field of amax (fp16 inputs are normal in fp32), so
+// the group maximum lands in [256, 512).  Elements are clamped to +-448 * 2^X
+// (the largest finite E4M3 value, which is where round-to-nearest-even with
+// saturation sends everything above it) and converted by gfx950's scaled FP8
+// conversion, which divides by the power of two exactly and rounds to nearest
+// even, keeping the sign (so -0 and negatives that round to zero give 0x80).
+
+// Group of 32: returns the E8M0 byte, fills 8 code dwords (byte u = element u).
+__device__ inline uint32_t encode_mx8_32(const float* v, uint32_t* w /*8 dwords*/) {
+  float amax = 0.0f;
+#pragma unroll
+  for (int u = 0; u < 32; ++u) amax = fmaxf(amax, fabsf(v[u]));
+  const int X = amax > 0.0f ? (int)((__float_as_uint(amax) >> 23) & 0xFF) - 127 - 8 : -127;
+  const float scale = amax > 0.0f ? __uint_as_float((uint32_t)(X + 127) << 23) : 1.0f;
+  const float cap = 448.0f * scale;
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const float* p = v + q * 4;
+    v2s_t y = {0, 0};
+    y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(p[0], -cap, cap),
+                                                  __builtin_amdgcn_fmed3f(p[1], -cap, cap), scale, false);
+    y = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(y, __builtin_amdgcn_fmed3f(p[2], -cap, cap),
+                                                  __builtin_amdgcn_fmed3f(p[3], -cap, cap), scale, true);
+    w[q] = __builtin_bit_cast(uint32_t, y);
+  }
+  return (uint32_t)(X + 127);
+}
+
+// Groups along D (Q, K): thread gi encodes elements [32 gi, 32 gi + 32).
+__global__ __launch_bounds__(kQThreads) void quant8_d_kernel(const _Float16* __restrict__ x, size_t ngroups,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+  const size_t gi = (size_t)blockIdx.x * kQThreads + threadIdx.x;
+  if (gi >= ngroups) return;
+  float v[32];
+  const v8h* src = reinterpret_cast<const v8h*>(x + gi * 32);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    v8h h = src[q];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[q * 8 + u] = (float)h[u];
+  }
+  uint32_t w[8];
+  scales[gi] = (uint8_t)encode_mx8_32(v, w);
+  uint4* dst = reinterpret_cast<uint4*>(codes + gi * 32);
+  dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+  dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+}
+
+// Groups along S (V): codes [B,H,D,Sp] and scales [B,H,D,Sp/32], the tile of
+// kVTile positions staged through LDS so that the reads stay row-contiguous.
+template <int D>
+__global__ __launch_bounds__(kQThreads) void quant8_s_kernel(const _Float16* __restrict__ x, int S, int Sp,
+                                                             uint8_t* __restrict__ codes,
+                                                             uint8_t* __restrict__ scales) {
+  __shared__ _Float16 tile[kVTile][D + 2];
+  const int t = threadIdx.x, bh = blockIdx.y, s0 = blockIdx.x * kVTile;
+  const _Float16* base = x + (size_t)bh * S * D;
+  for (int e = t; e < kVTile * D / 8; e += kQThreads) {
+    int r = e / (D / 8), c = (e % (D / 8)) * 8;
+    v8h h = {};
+    if (s0 + r < S) h = *reinterpret_cast<const v8h*>(base + (size_t)(s0 + r) * D + c);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) tile[r][c + u] = h[u];
+  }
+  __syncthreads();
+  constexpr int GPT = kVTile / 32;
+  for (int e = t; e < D * GPT; e += kQThreads) {
+    const int d = e / GPT, gq = e % GPT, tok0 = s0 + gq * 32;
+    if (tok0 >= Sp) continue;
+    float v[32];
+#pragma unroll
+    for (int u = 0; u < 32; ++u) v[u] = (float)tile[gq * 32 + u][d];
+    uint32_t w[8];
+    const size_t row = (size_t)bh * D + d;
+    scales[row * (Sp / 32) + tok0 / 32] = (uint8_t)encode_mx8_32(v, w);
+    uint4* dst = reinterpret_cast<uint4*>(codes + row * Sp + tok0);
+    dst[0] = make_uint4(w[0], w[1], w[2], w[3]);
+    dst[1] = make_uint4(w[4], w[5], w[6], w[7]);
+  }
+}
+
 }  // namespace thrift
 
 using namespace thrift;
@@ -572,5 +657,29 @@ extern "C" thrift_status thrift_cache_update(const void* k16, const void* v16, i
       THRIFT_CACHE_UPDATE(THRIFT_NVFP4, 64);
   }
 #undef THRIFT_CACHE_UPDATE
+  return launch_status();
+}
+
+extern "C" thrift_status thrift_quantize_fp8(const void* x16, int B, int H, int S, int D, thrift_group_axis axis,
+                                             uint8_t* codes, uint8_t* scales, hipStream_t stream) {
+  if (!x16 || !codes || !scales) return THRIFT_EINVAL;
+  if (B < 1 || H < 1 || S < 1) return THRIFT_EINVAL;
+  if (axis != THRIFT_GROUP_D && axis != THRIFT_GROUP_S) return THRIFT_EINVAL;
+  if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
+  if (S > 262144 || B * H > 65535) return THRIFT_EUNSUPPORTED;
+  if (!aligned16(x16) || !aligned16(codes)) return THRIFT_EALIGN;
+  auto x = (const _Float16*)x16;
+  if (axis == THRIFT_GROUP_D) {
+    const size_t ngroups = (size_t)B * H * S * (D / 32);
+    quant8_d_kernel<<<(int)((ngroups + kQThreads - 1) / kQThreads), kQThreads, 0, stream>>>(x, ngroups, codes,
+                                                                                          scales);
+  } else {
+    const int Sp = pad_s(S);
+    const dim3 grid(cdiv(Sp, kVTile), B * H);
+    if (D == 128)
+      quant8_s_kernel<128><<<grid, kQThreads, 0, stream>>>(x, S, Sp, codes, scales);
+    else
+      quant8_s_kernel<64><<<grid, kQThreads, 0, stream>>>(x, S, Sp, codes, scales);
+  }
   return launch_status();
 }

@@ -142,6 +142,9 @@ def _plant(rng, w: Workload, q, k):
     B, Hq, S, D = q.shape
     G = Hq // w.Hkv
     nq = -(-S // w.bq)
+    if w.planted > nq - 1:
+        raise ValueError(f"{w.planted} planted pairs per head need as many distinct query blocks after the "
+                         f"first; S = {S} has {nq - 1}")
     pairs = []
     for b in range(B):
         for hq in range(Hq):

@@ -293,6 +293,54 @@ thrift_status thrift_attention_fwd(const void* q16, const void* k16, const void*
                                    void* o, int o_is_fp32, float* lse, hipStream_t stream);
 
 /* ---------------------------------------------------------------------- */
+/* Middle precision tier (a variant): FP4, FP8 and FP16 in one kernel       */
+/* ---------------------------------------------------------------------- */
+/* The blog page on the method (hyperion-consulting.io, its introduction and
+ * the COMPUTE layer) names three precision levels, FP4, FP8 and BF16,
+ * switched inside one kernel; the method's other pages choose between two by
+ * block-mean scores.  This variant keeps their selection and inserts MXFP8
+ * between them: the blocks of the selection under budget bp16 run in FP16,
+ * the blocks the selection under bp16 + bp8 adds run in FP8, the rest in
+ * FP4 (MX format).
+ *
+ * MXFP8 quantisation of x16 [B,H,S,D] fp16 along `axis`: E4M3 elements
+ * (bias 7, largest 448, subnormals m 2^-9, no infinity) under one E8M0 scale
+ * per 32 elements, exponent floor(log2 amax) - 8 (so the group maximum lands
+ * in [256, 512)), element code = E4M3 of x / 2^exponent rounded to nearest
+ * even, saturating at 448, sign kept (-0 gives 0x80); an all-zero group has
+ * exponent -127.
+ *   THRIFT_GROUP_D (Q, K): codes [B,H,S,D] u8, scales [B,H,S,D/32] u8;
+ *   THRIFT_GROUP_S (V): codes [B,H,D,Sp] u8 (V transposed, Sp = S rounded up
+ *     to 64, padding tokens zero), scales [B,H,D,Sp/32] u8.
+ * codes 16-byte aligned; no workspace. */
+thrift_status thrift_quantize_fp8(const void* x16, int B, int H, int S, int D, thrift_group_axis axis,
+                                  uint8_t* codes, uint8_t* scales, hipStream_t stream);
+
+/* Three-tier forward (MX format).  As thrift_attention_fwd with
+ * fmt = THRIFT_MXFP4, plus a middle tier between its two paths: every valid
+ * block that idx2[.., :cnt2] lists and idx[.., :cnt] does not runs, after the
+ * FP4 path and before the FP16 path, ascending, with scores from the MXFP8 Q
+ * and K, the probabilities quantised in two levels as on the MXFP4 path but
+ * with E4M3 elements (v = 2^(t - z) with an integer z, E8M0 exponent
+ * floor(log2 max v) - 8 per 32 keys, E4M3 codes of v / 2^exponent), times the
+ * MXFP8 V.  FP4 runs on every valid block neither list holds.  The
+ * unquantised probabilities feed the row sum on all three tiers.
+ *   q8_*, k8_*: thrift_quantize_fp8 along THRIFT_GROUP_D; v8_*: along
+ *     THRIFT_GROUP_S; scales 4-byte aligned.
+ *   idx2, cnt2, kmax2: the FP16 and FP8 tiers' blocks together, e.g. from
+ *     thrift_select_blocks under the two budgets' sum (its top-k list then
+ *     contains idx's, as both come from one ranking); a block both lists
+ *     hold stays on the FP16 path.
+ * Everything else (layouts, o, lse, errors) as thrift_attention_fwd. */
+thrift_status thrift_attention_fwd_tiered(
+    const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes, const uint8_t* q4_scales,
+    const uint8_t* k4_codes, const uint8_t* k4_scales, const uint8_t* v4_codes, const uint8_t* v4_scales,
+    const uint8_t* q8_codes, const uint8_t* q8_scales, const uint8_t* k8_codes, const uint8_t* k8_scales,
+    const uint8_t* v8_codes, const uint8_t* v8_scales, const int32_t* idx, const int32_t* cnt, int kmax,
+    const int32_t* idx2, const int32_t* cnt2, int kmax2, int B, int Hq, int Hkv, int S, int D, int block_q,
+    int block_k, int causal, float sm_scale, void* o, int o_is_fp32, float* lse, hipStream_t stream);
+
+/* ---------------------------------------------------------------------- */
 /* Decode-shaped forward (new tokens against the dual FP16/FP4 KV cache;    */
 /* decode results in "Resultaten", the cache in "Betekenis en Beweringen")  */
 /* ---------------------------------------------------------------------- */

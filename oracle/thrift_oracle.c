@@ -473,8 +473,9 @@ void tho_quantize(const uint16_t* x16, int B, int H, int S, int D, int axis, int
 void tho_quantize_fp8(const uint16_t* x16, int B, int H, int S, int D, int axis, uint8_t* codes,
                       uint8_t* scales) {
   int Sp = tho_pad_s(S);
-  double vals[32];
+#pragma omp parallel for schedule(dynamic, 1)
   for (int bh = 0; bh < B * H; ++bh) {
+    double vals[32];
     const uint16_t* x = x16 + (size_t)bh * S * D;
     int rows = axis == THO_AXIS_D ? S : D;
     int len = axis == THO_AXIS_D ? D : Sp;

@@ -269,3 +269,28 @@ def test_backward_validation(lib):
     # 4 Q-sized and 6 K/V-sized fp16 tensors, the bit table and the row terms
     assert need >= (4 * 8 + 6 * 2) * 512 * 128 * 2 + 8 * 512 * 4
     assert lib.thrift_attention_bwd_workspace_bytes(0, 8, 2, 512, 128, 128) == 0
+
+
+def test_fp8_tier_validation(lib):
+    q = lib.thrift_quantize_fp8
+    assert q(None, 1, 1, 64, 128, 0, A, A, None) == 1
+    assert q(A, 1, 1, 64, 128, 2, A, A, None) == 1  # axis
+    assert q(A, 1, 1, 64, 96, 0, A, A, None) == 2  # D
+    assert q(A, 0, 1, 64, 128, 0, A, A, None) == 1
+    assert q(A + 4, 1, 1, 64, 128, 0, A, A, None) == 3
+    f = lib.thrift_attention_fwd_tiered
+
+    def call(q8=A, idx2=A, kmax2=4, q8s=A, S=512, D=128, bq=128, kmax=4, o=A):
+        return f(A, A, A, A, A, A, A, A, A, q8, q8s, A, A, A, A, A, A, kmax, idx2, A, kmax2, 1, 2, 1, S, D, bq, 64,
+                 1, 0.088, o, 1, None, None)
+
+    assert call(q8=None) == 1
+    assert call(idx2=None) == 1
+    assert call(kmax2=0) == 1
+    assert call(kmax2=9) == 2  # more than the 8 key blocks of S = 512
+    assert call(kmax=9) == 2
+    assert call(D=80) == 2
+    assert call(bq=96) == 2
+    assert call(o=None) == 1
+    assert call(q8=A + 4) == 3
+    assert call(q8s=A + 2) == 3

@@ -134,3 +134,13 @@ def test_planted_pairs_selected(oracle):
     assert len(d["planted"]) == 16
     for b, hq, i, j in d["planted"]:
         assert j in idx[b, hq, i, :cnt[b, hq, i]].tolist()
+
+
+def test_planted_pairs_need_distinct_query_blocks():
+    """The generator plants each head's pairs in distinct query blocks after
+    the first, so it refuses more pairs than that (instead of searching
+    forever)."""
+    w = W.WORKLOADS["long"].with_(Hq=2, Hkv=1, S=1024)  # 7 query blocks after the first, 16 pairs asked
+    with pytest.raises(ValueError):
+        W.generate(w)
+    assert len(W.generate(w.with_(planted=7))["planted"]) == 2 * 7
