@@ -127,6 +127,9 @@ def main():
     ap.add_argument("--topk-bp", type=int, default=None)
     ap.add_argument("--budget", default="block", choices=["block", "head"],
                     help="top-k per query block (default) or one budget per query head")
+    ap.add_argument("--tier8-bp", type=int, default=0,
+                    help="the three-tier variant (MX format, forward): this many basis points of the "
+                         "valid pairs beyond the FP16 tier's run on the MXFP8 middle tier")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--copy-mib", type=int, default=0,
@@ -154,6 +157,12 @@ def main():
     if p_fmt is not None and (args.pass_ == "bwd" or W.WORKLOADS[args.workload].Sq):
         print("bench.py: nvfp4_mxp is a forward variant (prefill shape only)", file=sys.stderr)
         sys.exit(2)
+    tier8 = args.tier8_bp
+    if tier8 and (args.pass_ == "bwd" or W.WORKLOADS[args.workload].Sq or fmt != api.THRIFT_MXFP4
+                  or args.budget != "block" or w.topk_count >= 0):
+        print("bench.py: --tier8-bp is a forward variant of the MX format with per-query-block budgets "
+              "in basis points (prefill shape only)", file=sys.stderr)
+        sys.exit(2)
     t0 = time.time()
     d = W.generate(w)
     gen_s = time.time() - t0
@@ -169,6 +178,7 @@ def main():
     else:
         select = api.thrift_select_blocks_means
         kmax = max(1, api.thrift_select_kmax(w.S, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp))
+    kmax2 = max(1, api.thrift_select_kmax(w.S, w.bq, w.bk, w.causal, -1, w.topk_bp + tier8)) if tier8 else 0
     o = torch.empty_like(q)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -183,15 +193,24 @@ def main():
         q4, qbar = api.thrift_quantize_fp4_means(q, fmt, w.bq)
         k4, kbar = api.thrift_quantize_fp4_means(k, fmt, w.bk)
         v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, fmt)
+        if tier8:
+            q8, k8 = api.thrift_quantize_fp8(q, api.THRIFT_GROUP_D), api.thrift_quantize_fp8(k, api.THRIFT_GROUP_D)
+            v8 = api.thrift_quantize_fp8(v, api.THRIFT_GROUP_S)
         if rec:
             rec[1].record()
         idx, cnt = select(qbar, kbar, w.S, w.S, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp, kmax)
+        if tier8:
+            idx2, cnt2 = select(qbar, kbar, w.S, w.S, w.bq, w.bk, w.causal, -1, w.topk_bp + tier8, kmax2)
         if rec:
             rec[2].record()
-        api.thrift_attention_fwd(q, k, v, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal, out=o, p_fmt=p_fmt)
+        if tier8:
+            api.thrift_attention_fwd_tiered(q, k, v, q4, k4, v4, q8, k8, v8, idx, cnt, idx2, cnt2, w.bq, w.bk,
+                                            w.causal, out=o)
+        else:
+            api.thrift_attention_fwd(q, k, v, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal, out=o, p_fmt=p_fmt)
         if rec:
             rec[3].record()
-        return idx, cnt
+        return (idx, cnt, idx2, cnt2) if tier8 else (idx, cnt, None, None)
 
     for _ in range(args.warmup):
         step()
@@ -200,7 +219,7 @@ def main():
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for r in recs:
-        idx, cnt = step(r)
+        idx, cnt, idx2, cnt2 = step(r)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = 1e3 * wall / args.steps
@@ -213,8 +232,13 @@ def main():
     f_alg = 4.0 * w.D * pairs
     p16 = promoted_pairs(idx_h, cnt_h, w.S, w.bq, w.bk, w.causal)
     f16 = 4.0 * w.D * p16
-    f4 = f_alg - f16
-    t_roof = f4 / P_FP4 + f16 / P_FP16
+    p8 = 0
+    if tier8:  # the middle tier's pairs: in the joint list, not in the FP16 one
+        p8 = promoted_pairs(idx2.cpu().numpy(), cnt2.cpu().numpy(), w.S, w.bq, w.bk, w.causal) - p16
+    f8 = 4.0 * w.D * p8
+    f4 = f_alg - f16 - f8
+    # the middle tier runs on the fp16 matrix cores (MXFP8 decoded exactly to fp16)
+    t_roof = f4 / P_FP4 + (f16 + f8) / P_FP16
     peak_mixed = f_alg / t_roof
     achieved = f_alg / (fwd_ms * 1e-3)
     value = f_alg / (ms_step * 1e-3) / 1e12
@@ -230,7 +254,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("mxfp4+fp16" if fmt == api.THRIFT_MXFP4 else
+        "dtype": ("mxfp4+mxfp8(fp16 math)+fp16" if tier8 else "mxfp4+fp16" if fmt == api.THRIFT_MXFP4 else
                   "nvfp4 q/k/v, mx p (fp16 math)+fp16" if p_fmt is not None else "nvfp4(fp16 math)+fp16"),
         "data": "synthetic",
         "config": {
@@ -238,7 +262,8 @@ def main():
                         f"{'causal' if w.causal else 'non-causal'} blocks {w.bq}x{w.bk} "
                         f"top-k {w.topk_bp / 100 if w.topk_count < 0 else w.topk_count}"
                         f"{'%' if w.topk_count < 0 else ' per query block'} {args.fmt}"
-                        f"{', one budget per query head' if args.budget == 'head' else ''}",
+                        f"{', one budget per query head' if args.budget == 'head' else ''}"
+                        f"{f', MXFP8 middle tier {tier8 / 100}% more' if tier8 else ''}",
             "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)",
         },
         "roofline": {
@@ -247,19 +272,22 @@ def main():
             "peak": round(peak_mixed / 1e12, 2),
             "unit": "TFLOP/s",
             "frac": round(achieved / peak_mixed, 4),
-            "traffic": measured_traffic(w.name, args.fmt),
+            "traffic": None if tier8 else measured_traffic(w.name, args.fmt),
             "traffic_algorithmic": algorithmic_bytes(w, int((cnt_h > 0).sum()), fmt),
             "kernel": "attn_fwd_kernel",
-            "peak_note": "F_alg / (F_fp4 / 10.1 PF + F_fp16 / 2.5 PF) for this launch's FP16 share",
+            "peak_note": ("F_alg / (F_fp4 / 10.1 PF + (F_fp8 + F_fp16) / 2.5 PF): the middle tier runs on the "
+                          "fp16 matrix cores" if tier8 else
+                          "F_alg / (F_fp4 / 10.1 PF + F_fp16 / 2.5 PF) for this launch's FP16 share"),
         },
         "breakdown_ms": {"means_and_quantize_qkv": round(q_ms, 4), "select_from_means": round(sel_ms, 4),
                          "attention_fwd": round(fwd_ms, 4)},
         "fp16_pair_share": round(p16 / pairs, 5),
+        **({"fp8_pair_share": round(p8 / pairs, 5)} if tier8 else {}),
         "attention_fwd_tflops": round(achieved / 1e12, 2),
         "input_gen_s": round(gen_s, 1),
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, d, fmt, args.budget, p_fmt)
+        line["cpu_baseline"] = cpu_baseline(w, d, fmt, args.budget, p_fmt, tier8)
     s = json.dumps(line)
     print(s, flush=True)
     if args.out:
@@ -515,7 +543,7 @@ def cpu_baseline_bwd(w, d, do_h, fmt):
                       f"fp64"}
 
 
-def cpu_baseline(w, d, fmt, budget="block", p_fmt=None):
+def cpu_baseline(w, d, fmt, budget="block", p_fmt=None, tier8=0):
     """The oracle on one query head (and its key head) of the same workload:
     selection, quantisation of that head's Q, K, V and the forward pass."""
     from oracle import oracle as O
@@ -526,7 +554,9 @@ def cpu_baseline(w, d, fmt, budget="block", p_fmt=None):
     v1 = np.ascontiguousarray(d["v"][:1, :1])
     O.lib()
     t0 = time.perf_counter()
-    if budget == "head":
+    if tier8:
+        O.pipeline_tiers(q1, k1, v1, w.bq, w.bk, w.causal, w.topk_bp, tier8)
+    elif budget == "head":
         idx, cnt = O.select_head(q1, k1, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
         q4, k4, v4 = (O.quantize(x, ax, fmt) for x, ax in ((q1, O.AXIS_D), (k1, O.AXIS_D), (v1, O.AXIS_S)))
         O.attention(q1, k1, v1, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal, p_fmt=p_fmt)
@@ -536,7 +566,9 @@ def cpu_baseline(w, d, fmt, budget="block", p_fmt=None):
     f = 4.0 * w.D * unmasked_pairs(w.S, w.causal)
     return {"value": round(f / sec / 1e12, 5), "unit": "TFLOP/s", "cores": nthreads,
             "kind": "oracle", "seconds": round(sec, 2),
-            "sample": f"query head 0 of batch 0 with its key head: selection ({budget} budget), FP4 quantisation of "
+            "sample": f"query head 0 of batch 0 with its key head: selection ({budget} budget"
+                      f"{', twice: FP16 tier and both tiers' if tier8 else ''}), FP4 "
+                      f"{'and MXFP8 ' if tier8 else ''}quantisation of "
                       f"its Q/K/V and the forward pass over all {-(-w.S // w.bq)} query blocks "
                       f"({f / 1e9:.1f} GFLOP of attention), fp64"}
 
