@@ -63,6 +63,16 @@ MUTANTS = {
 }
 
 
+# mutant name prefix -> the pin file aimed at that part of the oracle
+FIRST = [("fp8_", "tests/test_oracle_fp8.py"), ("fp4_pass_keeps_fp8", "tests/test_oracle_fp8.py"),
+         ("bwd_", "tests/test_oracle_backward.py"), ("ohp_", "tests/test_oracle_backward.py"),
+         ("head_budget", "tests/test_oracle_select_head.py"), ("decode_", "tests/test_oracle_decode.py"),
+         ("no_rescale", "tests/test_oracle_attention.py"), ("causal_", "tests/test_oracle_attention.py"),
+         ("rowsum_", "tests/test_oracle_attention.py"), ("mx_level1", "tests/test_oracle_attention.py"),
+         ("nvfp4_level1", "tests/test_oracle_attention.py"), ("gqa_", "tests/test_oracle_attention.py"),
+         ("fp16_pass", "tests/test_oracle_attention.py")]
+
+
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_mutant_is_caught(tmp_path, name):
     old, new = MUTANTS[name]
@@ -75,10 +85,14 @@ def test_mutant_is_caught(tmp_path, name):
 
     lib = build_oracle.build(src=str(mut), out=str(tmp_path / "libmut.so"))
     env = dict(os.environ, THRIFT_ORACLE_LIB=lib)
-    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_formats.py", "tests/test_oracle_select.py",
-                        "tests/test_oracle_attention.py", "tests/test_oracle_decode.py",
-                        "tests/test_oracle_select_head.py", "tests/test_oracle_backward.py",
-                        "tests/test_oracle_fp8.py"],
+    files = ["tests/test_oracle_formats.py", "tests/test_oracle_select.py", "tests/test_oracle_attention.py",
+             "tests/test_oracle_decode.py", "tests/test_oracle_select_head.py", "tests/test_oracle_backward.py",
+             "tests/test_oracle_fp8.py"]
+    # every pin file runs; the one aimed at the mutated part first, so that -x stops early
+    first = next((f for pre, f in FIRST if name.startswith(pre)), None)
+    if first:
+        files.remove(first)
+        files.insert(0, first)
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider"] + files,
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} survived the pins:\n{r.stdout[-2000:]}"
