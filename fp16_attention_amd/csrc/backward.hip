@@ -102,22 +102,35 @@ __global__ __launch_bounds__(256) void decode_fp4_kernel(const uint8_t* codes, c
 // tiles through LDS.
 __global__ __launch_bounds__(256) void transpose_kernel(const _Float16* in, int R, int C, int Rout,
                                                         const float* tsc, _Float16* out) {
+  // 64x64 tile through LDS with 16-byte loads and stores: a thread reads 8
+  // consecutive columns of one row and writes 8 consecutive rows of one
+  // output row (C and Rout are multiples of 8, the tile origin of 64)
   __shared__ _Float16 tile[64][66];
   const size_t bh = blockIdx.y;
   const int ct = cdiv(C, 64);
   const int r0 = (blockIdx.x / ct) * 64, c0 = (blockIdx.x % ct) * 64;
-  const int t = threadIdx.x, tc = t & 63, tr = t >> 6;
+  const int t = threadIdx.x, t8 = (t & 7) * 8, tr = t >> 3;
   const _Float16* src = in + bh * (size_t)R * C;
-  for (int k = 0; k < 64; k += 4) {
-    const int r = r0 + tr + k, c = c0 + tc;
-    tile[tr + k][tc] = (r < R && c < C) ? src[(size_t)r * C + c] : (_Float16)0.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = h * 32 + tr, r = r0 + row, c = c0 + t8;
+    v8h x = {};
+    if (r < R && c < C) x = *(const v8h*)(src + (size_t)r * C + c);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) tile[row][t8 + u] = x[u];
   }
   __syncthreads();
   _Float16* dst = out + bh * (size_t)C * Rout;
-  for (int k = 0; k < 64; k += 4) {
-    const int c = c0 + tr + k, r = r0 + tc;
-    if (c < C && r < Rout)
-      dst[(size_t)c * Rout + r] = tsc ? (_Float16)((float)tile[tc][tr + k] * tsc[bh]) : tile[tc][tr + k];
+  const float f = tsc ? tsc[bh] : 1.0f;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int col = h * 32 + tr, c = c0 + col, r = r0 + t8;
+    if (c < C && r < Rout) {
+      v8h y;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) y[u] = tsc ? (_Float16)((float)tile[t8 + u][col] * f) : tile[t8 + u][col];
+      *(v8h*)(dst + (size_t)c * Rout + r) = y;
+    }
   }
 }
 
