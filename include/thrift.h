@@ -13,6 +13,9 @@
  *   thrift_select_blocks  - block means, pair scores and per-query-block top-k
  *   thrift_quantize_fp4   - FP16 -> E2M1 codes + block scales (Q, K and V)
  *   thrift_attention_fwd  - the mixed FP4/FP16 forward pass
+ * Further sections declare the fused and cache-side variants of the first
+ * two, the decode-shaped forward, the middle-tier (MXFP8) variant and the
+ * Attn-QAT backward.
  *
  * Conventions (all calls):
  *   - Tensors are contiguous, row-major, [batch, head, seq, dim] unless stated.

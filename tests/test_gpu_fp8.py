@@ -85,6 +85,7 @@ CASES = {
     "all_fp8": (workload("prefill", Hq=2, Hkv=1, S=300), 0, 10000),
     "bq64_d64_noncausal": (workload("dit", Hq=2, Hkv=2, S=257, bq=64), 500, 2500),
     "sink_planted": (workload("long", Hq=4, Hkv=2, S=1024, planted=4), 500, 1000),
+    "one_ragged_block": (workload("prefill", Hq=2, Hkv=1, S=37), 0, 10000),
 }
 
 
