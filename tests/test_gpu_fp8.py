@@ -44,7 +44,7 @@ def test_quantize_fp8_bit_exact(oracle, S, D, axis):
     np.testing.assert_array_equal(gs, r.scales)
 
 
-def _run_tiered(d, w, bp16, bp8):
+def _run_tiered(d, w, bp16, bp8, no_fp16=False):
     import torch
 
     from fp16_attention_amd import api
@@ -57,7 +57,8 @@ def _run_tiered(d, w, bp16, bp8):
     v8 = api.thrift_quantize_fp8(v, api.THRIFT_GROUP_S)
     idx, cnt = api.thrift_select_blocks_means(qbar, kbar, w.S, w.S, w.bq, w.bk, w.causal, -1, bp16)
     idx2, cnt2 = api.thrift_select_blocks_means(qbar, kbar, w.S, w.S, w.bq, w.bk, w.causal, -1, bp16 + bp8)
-    o, lse = api.thrift_attention_fwd_tiered(q, k, v, q4, k4, v4, q8, k8, v8, idx, cnt, idx2, cnt2, w.bq, w.bk,
+    fp16 = (None, None, None) if no_fp16 else (q, k, v)  # fp16 tensors may be absent when no block is FP16
+    o, lse = api.thrift_attention_fwd_tiered(*fp16, q4, k4, v4, q8, k8, v8, idx, cnt, idx2, cnt2, w.bq, w.bk,
                                              w.causal, out_fp32=True, with_lse=True)
     torch.cuda.synchronize()
     cpu = lambda t: t.cpu().numpy()  # noqa: E731
@@ -95,7 +96,7 @@ def test_tiered_parity(oracle, name):
     note(f"[tiered] {name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} S{w.S} D{w.D} causal{int(w.causal)} bq{w.bq} "
          f"bp16 {bp16} bp8 {bp8}")
     d = W.generate(w)
-    g = _run_tiered(d, w, bp16, bp8)
+    g = _run_tiered(d, w, bp16, bp8, no_fp16=bp16 == 0)
     r = oracle.pipeline_tiers(d["q"], d["k"], d["v"], w.bq, w.bk, w.causal, bp16, bp8)
     _same_sel(g, r["idx"], r["cnt"], g["idx"], g["cnt"])
     _same_sel(g, r["idx2"], r["cnt2"], g["idx2"], g["cnt2"])
