@@ -298,8 +298,10 @@ thrift_status thrift_attention_fwd(const void* q16, const void* k16, const void*
 /* ---------------------------------------------------------------------- */
 /* Middle precision tier (a variant): FP4, FP8 and FP16 in one kernel       */
 /* ---------------------------------------------------------------------- */
-/* The blog page on the method (hyperion-consulting.io, its introduction and
- * the COMPUTE layer) names three precision levels, FP4, FP8 and BF16,
+/* The hyperion-consulting.io article on the method ("ThriftAttention:
+ * Selective Mixed Precision for Long-Context FP4 Attention", in German;
+ * sections "Einführung" and "COMPUTE-Schicht") names three precision levels,
+ * FP4, FP8 and BF16,
  * switched inside one kernel; the method's other pages choose between two by
  * block-mean scores.  This variant keeps their selection and inserts MXFP8
  * between them: the blocks of the selection under budget bp16 run in FP16,

@@ -2,8 +2,9 @@
 
 What pins what:
   - the E2M1 and E4M3 value tables against their bit-field definitions (the
-    Attn-QAT page's "15 representable values" and the blog page's 2-exponent,
-    1-mantissa FP4 split; OCP for E4M3 and E8M0);
+    Attn-QAT page's count of 15 distinct FP4 values and the hyperion-consulting.io
+    article's split of FP4 into 2 exponent bits and 1 mantissa bit; OCP for
+    E4M3 and E8M0);
   - E2M1 and E4M3 rounding against brute-force nearest-value search, with
     exact rational arithmetic on a sample;
   - the MX exponent against the property that the scaled group maximum

@@ -1,6 +1,7 @@
 """Pins of the oracle's middle precision tier (CPU only): MXFP8 tensors and
-the three-tier forward, a variant of the method.  The blog page on the
-method (hyperion-consulting.io, introduction and the COMPUTE layer) speaks of
+the three-tier forward, a variant of the method.  The hyperion-consulting.io
+article on the method (in German; sections "Einführung" and
+"COMPUTE-Schicht") speaks of
 FP4, FP8 and BF16 levels inside one kernel; the other pages fix two tiers
 chosen by block-mean scores.  The reading built here keeps their selection
 and adds the FP8 tier between the two: the FP16 tier is the top-k under
