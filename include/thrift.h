@@ -168,8 +168,8 @@ thrift_status thrift_select_blocks_means(const float* qbar, const float* kbar, i
                                          int topk_count, int topk_bp, int32_t* idx, int32_t* cnt,
                                          int kmax, hipStream_t stream);
 
-/* Per-head budget: the other reading of "the top-k highest-scoring block
- * pairs" (summaries "Heuristische Blokkenselectie"): one budget over all
+/* Per-head budget: the other reading of the pages' top-k over the best-scoring
+ * block pairs (summaries "Heuristische Blokkenselectie"): one budget over all
  * valid pairs of a query head, K = min(P, topk_count) or
  * ceil(P * topk_bp / 10^4) of its P valid pairs, the K best-scoring pairs
  * kept (ties: lower query block, then lower key block).  Scores as

@@ -257,9 +257,10 @@ static int tho_int_cmp(const void* a, const void* b) {
   return (x > y) - (x < y);
 }
 
-/* Per query block (reading of "the top-k highest-scoring block pairs": the
- * budget is taken per query block, so that every query block gets its share;
- * the pages' "5% of query-key blocks" is then met per block row), keep the
+/* Per query block (reading of the pages' top-k over the best-scoring block
+ * pairs: the budget is taken per query block, so that every query block gets
+ * its share; the pages' 5% share of query-key blocks is then met per block
+ * row), keep the
  * k_i best-scoring valid key blocks.  The query head hq reads key head
  * hq / (Hq / Hkv).  idx: [B, Hq, nQ, kmax], ascending, padded with -1;
  * cnt: [B, Hq, nQ].  scores (optional): [B, Hq, nQ, nK], NaN where invalid. */
@@ -315,8 +316,8 @@ static int tho_pair_cmp(const void* a, const void* b) {
   return x->j - y->j;
 }
 
-/* Per-head budget: the other reading of "the top-k highest-scoring block
- * pairs" (ThriftAttention summaries, "Heuristische Blokkenselectie"), one
+/* Per-head budget: the other reading of the pages' top-k over the best-scoring
+ * block pairs (ThriftAttention summaries, "Heuristische Blokkenselectie"), one
  * budget over all valid pairs of a query head: K = min(P, topk_count) or
  * ceil(P * topk_bp / 10^4) of its P valid pairs, the K best-scoring pairs
  * kept.  Scores as tho_select_kv.  idx [B, Hq, nQ, kmax]: each query block's
