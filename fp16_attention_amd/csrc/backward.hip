@@ -148,19 +148,24 @@ __global__ __launch_bounds__(256) void prom_bits_kernel(const int32_t* idx, cons
   }
 }
 
-// Row term dO[r] . O'[r], one wave per row.
+// Row term dO[r] . O'[r]: D/8 lanes per row (a 16-byte load of dO and two of
+// O' each), summed across those lanes; every lane reaches the shuffles.
 template <int D>
 __global__ __launch_bounds__(256) void row_term_kernel(const _Float16* do16, const float* ohp, size_t nrows,
                                                        float* drow) {
-  const size_t row = (size_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  if (row >= nrows) return;
+  constexpr int LPR = D / 8;  // lanes per row: 16 or 8, a divisor of the wave
+  const size_t row = ((size_t)blockIdx.x * 256 + threadIdx.x) / LPR;
+  const int sub = threadIdx.x % LPR;
   float s = 0.0f;
+  if (row < nrows) {
+    const v8h h = *(const v8h*)(do16 + row * D + sub * 8);
+    const float4 x = *(const float4*)(ohp + row * D + sub * 8), y = *(const float4*)(ohp + row * D + sub * 8 + 4);
+    s = (float)h[0] * x.x + (float)h[1] * x.y + (float)h[2] * x.z + (float)h[3] * x.w + (float)h[4] * y.x +
+        (float)h[5] * y.y + (float)h[6] * y.z + (float)h[7] * y.w;
+  }
 #pragma unroll
-  for (int d = lane; d < D; d += 64) s += (float)do16[row * D + d] * ohp[row * D + d];
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
-  if (lane == 0) drow[row] = s;
+  for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
+  if (row < nrows && sub == 0) drow[row] = s;
 }
 
 // ---- row kernel: one lane per query (O' or dQ) ---------------------------------
@@ -877,10 +882,11 @@ extern "C" thrift_status thrift_attention_bwd(
   a.do16 = (const _Float16*)do16;
   launch_transpose(a.do16, BHq, S, D, Sp, (_Float16*)a.dot, stream);
   const size_t nrows = (size_t)BHq * S;
+  const unsigned rt_grid = (unsigned)((nrows * (size_t)(D / 8) + 255) / 256);
   if (D == 128)
-    row_term_kernel<128><<<(unsigned)((nrows + 3) / 4), 256, 0, stream>>>(a.do16, ohp, nrows, (float*)a.drow);
+    row_term_kernel<128><<<rt_grid, 256, 0, stream>>>(a.do16, ohp, nrows, (float*)a.drow);
   else
-    row_term_kernel<64><<<(unsigned)((nrows + 3) / 4), 256, 0, stream>>>(a.do16, ohp, nrows, (float*)a.drow);
+    row_term_kernel<64><<<rt_grid, 256, 0, stream>>>(a.do16, ohp, nrows, (float*)a.drow);
   a.out = dq;
   a.dk = dk;
   a.dv = dv;
