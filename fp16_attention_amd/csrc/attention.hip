@@ -520,15 +520,14 @@ namespace thrift {
 // as the fp16 value code * 2^exponent.
 
 // 8 E4M3 codes (two dwords, byte u = element u) times the power of two
-// `scale`, to fp16: decoded and scaled exactly in fp32, then rounded to fp16.
-typedef float v2f_t __attribute__((ext_vector_type(2)));
+// `scale`, to fp16 by the scaled FP8 -> fp16 conversion (two values per
+// instruction; exact wherever fp16 holds the product).
 __device__ inline v8h fp8x8_to_h(uint32_t lo, uint32_t hi, float scale) {
-  const v2f_t a = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)lo, 1.0f, false);
-  const v2f_t b = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)lo, 1.0f, true);
-  const v2f_t c = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)hi, 1.0f, false);
-  const v2f_t d = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)hi, 1.0f, true);
-  return v8h{(_Float16)(a.x * scale), (_Float16)(a.y * scale), (_Float16)(b.x * scale), (_Float16)(b.y * scale),
-             (_Float16)(c.x * scale), (_Float16)(c.y * scale), (_Float16)(d.x * scale), (_Float16)(d.y * scale)};
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)lo, scale, false);
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)lo, scale, true);
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)hi, scale, false);
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((int)hi, scale, true);
+  return v8h{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
 // Promoted tile on the middle tier: scores from the decoded fp16 stage; this
