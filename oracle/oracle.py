@@ -81,9 +81,10 @@ def _declare(L):
     L.tho_dequantize.restype = None
     L.tho_dequantize.argtypes = [_P, _P, _P, _I, _I, _I, _I, _I, _I, _P]
     L.tho_attention.restype = None
-    L.tho_attention.argtypes = [_P] * 12 + [_I, _P, _P, _I] + [_I] * 8 + [_D, _P, _I, _P, _P, _P]
+    L.tho_attention.argtypes = [_P] * 12 + [_I, _P, _P, _I] + [_I] * 8 + [_D, _P, _I, _P, _P, _P, _P, _I, _P]
     L.tho_attention_kv.restype = None
-    L.tho_attention_kv.argtypes = [_P] * 12 + [_I, _P, _P, _I] + [_I] * 9 + [_D, _P, _I, _P, _P, _P]
+    L.tho_attention_kv.argtypes = ([_P] * 12 + [_I, _P, _P, _I] + [_I] * 9
+                                   + [_D, _P, _I, _P, _P, _P, _P, _I, _P])
     L.tho_attention_hp.restype = None
     L.tho_attention_hp.argtypes = [_P] * 12 + [_I, _P, _P, _I] + [_I] * 8 + [_D, _P, _I, _P, _P, _P]
     L.tho_attention_bwd.restype = None
@@ -100,7 +101,12 @@ def _declare(L):
     L.tho_dequantize_fp8.restype = None
     L.tho_dequantize_fp8.argtypes = [_P, _P, _I, _I, _I, _I, _I, _P]
     L.tho_attention_tiers.restype = None
-    L.tho_attention_tiers.argtypes = [_P] * 17 + [_I, _P, _P, _I] + [_I] * 8 + [_D, _P, _I, _P, _P, _P]
+    L.tho_attention_tiers.argtypes = ([_P] * 17 + [_I, _P, _P, _I] + [_I] * 8
+                                      + [_D, _P, _I, _P, _P, _P, _P, _I, _P])
+    L.tho_p_tile_decisions.restype = _I
+    L.tho_p_tile_decisions.argtypes = [_P, _P, _P, _I, _I, _I, _P, _P, _P, _P, _I]
+    L.tho_eval_rel.restype = _D
+    L.tho_eval_rel.argtypes = [_I, _D, _D, _D, _D]
     L.tho_fp4_scores.restype = None
     L.tho_fp4_scores.argtypes = [_P] * 6 + [_I] * 6 + [_P]
     L.tho_e2m1_encode_array.restype = None
@@ -314,12 +320,45 @@ def fp4_scores(q4: FP4Tensor, k4: FP4Tensor, r, c0, c1):
 
 # ---- attention ----------------------------------------------------------------
 
+class Ambiguity:
+    """Decisions of a forward whose exact input lies within device evaluation
+    error of its rounding boundary (both outcomes are valid results): for
+    decision k, rows[k] is the flat row index (b * Hq + hq) * S + r and
+    delta[k] the change of that output row if the decision takes its other
+    outcome."""
+
+    def __init__(self, rows, delta, shape):
+        self.rows, self.delta, self.shape = rows, delta, shape
+
+    def for_row(self, b, hq, r):
+        B, Hq, S, D = self.shape
+        return self.delta[self.rows == (b * Hq + hq) * S + r]
+
+    def count_rows(self):
+        return len(np.unique(self.rows))
+
+
+def _call_amb(call, B, Hq, S, D, rows_hint):
+    """Run call(amb_row, amb_delta, cap, n_ptr) with enough room for the list."""
+    cap = max(4096, 2 * rows_hint)
+    while True:
+        rows = np.zeros(cap, np.int32)
+        delta = np.zeros((cap, D), np.float64)
+        n = np.zeros(1, np.int32)
+        call(_ptr(rows), _ptr(delta), cap, _ptr(n))
+        k = int(n[0])
+        if k <= cap:
+            return Ambiguity(rows[:k].astype(np.int64), delta[:k], (B, Hq, S, D))
+        cap = k
+
+
 def attention(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt, bq, bk,
-              causal, sm_scale=None, work=None, with_u=False, p_fmt=None):
+              causal, sm_scale=None, work=None, with_amb=False, p_fmt=None):
     """Forward pass.  Returns (o fp64 [B,Hq,S,D], lse fp64 [B,Hq,S]) and, with
-    with_u, the decision-uncertainty bound u [B,Hq,S,D]; with a work list of
-    (b, hq, i) triples only those query blocks are filled (the rest stay NaN).
-    p_fmt=MX with NVFP4 tensors quantises P MX-style (the variant)."""
+    with_amb, the Ambiguity list of decisions within device evaluation error
+    of their boundary; with a work list of (b, hq, i) triples only those query
+    blocks are filled (the rest stay NaN).  p_fmt=MX with NVFP4 tensors
+    quantises P MX-style (the variant)."""
     B, Hq, S, D = q4.shape
     Hkv, Sk = k4.shape[1], k4.shape[2]
     if sm_scale is None:
@@ -332,26 +371,31 @@ def attention(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, c
     km = idx.shape[-1]
     o = np.full((B, Hq, S, D), np.nan, np.float64)
     lse = np.full((B, Hq, S), np.nan, np.float64)
-    u = np.full((B, Hq, S, D), np.nan, np.float64) if with_u else None
     w = None if work is None else _c(np.asarray(work).reshape(-1, 3), np.int32)
     nw = 0 if w is None else w.shape[0]
-    lib().tho_attention_kv(_ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
-                           _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales),
-                           _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales),
-                           _ptr(v4.tensor_scale),
-                           NVFP4_MXP if (q4.fmt == NVFP4 and p_fmt == MX) else q4.fmt, _ptr(idx), _ptr(cnt),
-                           km, B, Hq, Hkv, S,
-                           Sk, D, bq, bk, int(causal), float(sm_scale), _ptr(w), nw, _ptr(o),
-                           _ptr(lse), _ptr(u))
-    return (o, lse, u) if with_u else (o, lse)
+
+    def call(ar, ad, cap, n):
+        lib().tho_attention_kv(_ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
+                               _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales),
+                               _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales),
+                               _ptr(v4.tensor_scale),
+                               NVFP4_MXP if (q4.fmt == NVFP4 and p_fmt == MX) else q4.fmt, _ptr(idx),
+                               _ptr(cnt), km, B, Hq, Hkv, S, Sk, D, bq, bk, int(causal),
+                               float(sm_scale), _ptr(w), nw, _ptr(o), _ptr(lse), ar, ad, cap, n)
+
+    if not with_amb:
+        call(None, None, 0, None)
+        return o, lse
+    amb = _call_amb(call, B, Hq, S, D, (nw * bq if w is not None else B * Hq * S))
+    return o, lse, amb
 
 
 def attention_tiers(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, q8: FP8Tensor,
                     k8: FP8Tensor, v8: FP8Tensor, idx, cnt, idx2, cnt2, bq, bk, causal, sm_scale=None,
-                    work=None, with_u=False):
+                    work=None, with_amb=False):
     """Forward with the middle (MXFP8) tier, MX format: blocks idx lists run
     in FP16, blocks idx2 lists and idx does not in FP8, the rest in FP4.
-    Returns (o, lse) and with with_u the decision-uncertainty bound u."""
+    Returns (o, lse) and with with_amb the Ambiguity list."""
     B, Hq, S, D = q4.shape
     Hkv = k4.shape[1]
     assert q4.fmt == MX
@@ -364,16 +408,47 @@ def attention_tiers(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, 
     idx2, cnt2 = _c(idx2, np.int32), _c(cnt2, np.int32)
     o = np.full((B, Hq, S, D), np.nan, np.float64)
     lse = np.full((B, Hq, S), np.nan, np.float64)
-    u = np.full((B, Hq, S, D), np.nan, np.float64) if with_u else None
     w = None if work is None else _c(np.asarray(work).reshape(-1, 3), np.int32)
     nw = 0 if w is None else w.shape[0]
-    lib().tho_attention_tiers(_ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
-                              _ptr(k4.codes), _ptr(k4.scales), _ptr(v4.codes), _ptr(v4.scales),
-                              _ptr(q8.codes), _ptr(q8.scales), _ptr(k8.codes), _ptr(k8.scales),
-                              _ptr(v8.codes), _ptr(v8.scales), _ptr(idx), _ptr(cnt), idx.shape[-1],
-                              _ptr(idx2), _ptr(cnt2), idx2.shape[-1], B, Hq, Hkv, S, D, bq, bk,
-                              int(causal), float(sm_scale), _ptr(w), nw, _ptr(o), _ptr(lse), _ptr(u))
-    return (o, lse, u) if with_u else (o, lse)
+
+    def call(ar, ad, cap, n):
+        lib().tho_attention_tiers(_ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes), _ptr(q4.scales),
+                                  _ptr(k4.codes), _ptr(k4.scales), _ptr(v4.codes), _ptr(v4.scales),
+                                  _ptr(q8.codes), _ptr(q8.scales), _ptr(k8.codes), _ptr(k8.scales),
+                                  _ptr(v8.codes), _ptr(v8.scales), _ptr(idx), _ptr(cnt), idx.shape[-1],
+                                  _ptr(idx2), _ptr(cnt2), idx2.shape[-1], B, Hq, Hkv, S, D, bq, bk,
+                                  int(causal), float(sm_scale), _ptr(w), nw, _ptr(o), _ptr(lse), ar, ad,
+                                  cap, n)
+
+    if not with_amb:
+        call(None, None, 0, None)
+        return o, lse
+    amb = _call_amb(call, B, Hq, S, D, (nw * bq if w is not None else B * Hq * S))
+    return o, lse, amb
+
+
+def p_tile_decisions(t, tb, mask, prec, epath=None):
+    """Test hook: (pq, decisions) of one tile row: values relative to 2^max t
+    and a list of (k0, k1, change of each key's value) per decision that may
+    go either way."""
+    n = len(t)
+    t, tb = _c(t, np.float64), _c(tb, np.float64)
+    mask = _c(mask, np.int32)
+    pq = np.zeros(n)
+    cap = 600
+    k0, k1 = np.zeros(cap, np.int32), np.zeros(cap, np.int32)
+    dp = np.zeros((cap, 64))
+    nf = lib().tho_p_tile_decisions(_ptr(t), _ptr(tb), _ptr(mask), n, int(prec),
+                                    int(prec if epath is None else epath), _ptr(pq), _ptr(k0), _ptr(k1),
+                                    _ptr(dp), cap)
+    assert nf <= cap
+    return pq, [(int(k0[f]), int(k1[f]), dp[f, :n].copy()) for f in range(nf)]
+
+
+def eval_rel(path, b, bmax, dt, mt):
+    """The oracle's relative evaluation-error bound of a tile value (path 0 MX
+    FP4, 1 NVFP4 FP4, 2 MXFP8 tier, 3 FP16; b, bmax the chain sums)."""
+    return lib().tho_eval_rel(int(path), float(b), float(bmax), float(dt), float(mt))
 
 
 def attention_hp(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt, bq, bk,
@@ -473,9 +548,9 @@ def pipeline(q16, k16, v16, fmt, bq, bk, causal, topk_count=-1, topk_bp=0, sm_sc
     q4 = quantize(q16, AXIS_D, fmt)
     k4 = quantize(k16, AXIS_D, fmt)
     v4 = quantize(v16, AXIS_S, fmt)
-    o, lse, u = attention(q16, k16, v16, q4, k4, v4, idx, cnt, bq, bk, causal, sm_scale, work,
-                          with_u=True, p_fmt=p_fmt)
-    return dict(idx=idx, cnt=cnt, q4=q4, k4=k4, v4=v4, o=o, lse=lse, u=u)
+    o, lse, amb = attention(q16, k16, v16, q4, k4, v4, idx, cnt, bq, bk, causal, sm_scale, work,
+                            with_amb=True, p_fmt=p_fmt)
+    return dict(idx=idx, cnt=cnt, q4=q4, k4=k4, v4=v4, o=o, lse=lse, amb=amb)
 
 
 def pipeline_tiers(q16, k16, v16, bq, bk, causal, bp16, bp8, sm_scale=None, work=None):
@@ -486,7 +561,7 @@ def pipeline_tiers(q16, k16, v16, bq, bk, causal, bp16, bp8, sm_scale=None, work
     idx2, cnt2, _ = select(q16, k16, bq, bk, causal, -1, bp16 + bp8)
     q4, k4, v4 = quantize(q16, AXIS_D, MX), quantize(k16, AXIS_D, MX), quantize(v16, AXIS_S, MX)
     q8, k8, v8 = quantize_fp8(q16, AXIS_D), quantize_fp8(k16, AXIS_D), quantize_fp8(v16, AXIS_S)
-    o, lse, u = attention_tiers(q16, k16, v16, q4, k4, v4, q8, k8, v8, idx, cnt, idx2, cnt2, bq, bk,
-                                causal, sm_scale, work, with_u=True)
+    o, lse, amb = attention_tiers(q16, k16, v16, q4, k4, v4, q8, k8, v8, idx, cnt, idx2, cnt2, bq, bk,
+                                  causal, sm_scale, work, with_amb=True)
     return dict(idx=idx, cnt=cnt, idx2=idx2, cnt2=cnt2, q4=q4, k4=k4, v4=v4, q8=q8, k8=k8, v8=v8,
-                o=o, lse=lse, u=u)
+                o=o, lse=lse, amb=amb)

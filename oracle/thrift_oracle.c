@@ -576,178 +576,228 @@ void tho_dequantize(const uint8_t* codes, const uint8_t* scales, const float* te
 /* Attention forward (pages: "Gemengd-Precisie Berekening & Samenvoeging") */
 /* ------------------------------------------------------------------ */
 
-/* Two-level quantisation of one probability tile on the FP4 path (the pages
- * take the scheme from SageAttention3 without spelling it out; reading):
+/* Probabilities of one key tile.  Reading of the pages' two-level
+ * quantisation of the probability blocks (which they take from
+ * SageAttention3), applied alike to every precision a tile runs in:
  *   level 1, per query row and key tile: the tile's scores t (log2 units)
- *     are exponentiated against the tile maximum;
- *   level 2, per group of keys (16 for NVFP4-style, 32 for MX) aligned like
- *     the V groups: a block scale and E2M1 codes.
- *  NVFP4-style: v = 2688 * 2^(t - mt) (the row maximum lands on 6 * 448),
- *     block scale E4M3(max v / 6), code E2M1(v / block scale); the
- *     dequantised probability relative to 2^mt is code * scale / 2688.
- *  MX: v = 2^(t - z) with z = ceil(mt) (a power-of-two level-1 factor; the
- *     E8M0 block scales absorb any power of two, so every integer z gives the
- *     same codes), block exponent X from max v, code E2M1(v / 2^X); the
- *     dequantised probability relative to 2^z is code * 2^X.
- * Masked keys (mask[c] != 0) hold probability 0.
- * pq[c] receives the dequantised probability relative to 2^(*ref). */
-/* ---- decisions a finite-precision evaluation may take either way ----
- * The probabilities that feed a rounding decision (the fp16 rounding of P on
- * the FP16 path, the E2M1 codes and block scales of P on the FP4 path) come
- * from exponentials of scores.  An implementation that accumulates a score's
- * D products in fp32 carries an error of a few 2^-24 times the sum of the
- * products' magnitudes, A (in the score's log2 units; A >= |t|, and A >> |t|
- * where the products cancel), plus that of its exp2; a decision whose input
- * lies closer than that to its rounding boundary may legitimately go either
- * way, so the method's result is not unique there.  tho_eval_eps is that
- * error, taken sixteen times over; the uncertainty outputs below add up what
- * flipping such decisions can change in O, plus what the same error changes
- * continuously: the unquantised row sum, and (NVFP4) each tile's level-1
- * factor 2^mt.  Where one key dominates a row with a large score, the row
- * sum's part is |O| ln2 times the score's error, which no fp32 evaluation
- * avoids. */
-static double tho_eval_eps(double A) { return THO_LN2 * ldexp(A + 16.0, -20); }
+ *     are exponentiated against the tile's own maximum mt, v = 2^(t - mt),
+ *     so the tile's largest probability is exactly 1; the tile adds 2^mt
+ *     times its level-2 values (times V) to the numerator of the output;
+ *   level 2, by the tile's precision:
+ *     NVFP4-style: v' = 2688 v (the maximum lands on 6 * 448); per 16 keys
+ *       an E4M3 block scale s2 = E4M3(max v' / 6), codes E2M1(v' / s2),
+ *       value code * s2 / 2688;
+ *     MX: per 32 keys X = mx_exponent(max v), codes E2M1(v / 2^X), value
+ *       code * 2^X;
+ *     MXFP8 (the middle tier): per 32 keys X = mx8_exponent(max v), codes
+ *       E4M3(v / 2^X), value code * 2^X;
+ *     FP16: fp16(v).
+ * Key groups follow the value tensor's groups along the keys.  A tile's
+ * values then depend on its own scores only: not on the running maximum,
+ * not on the order in which tiles are processed, and not on a constant
+ * added to every score of a row (softmax's shift invariance holds exactly).
+ * The row sum takes the unquantised probabilities 2^t. */
 
-/* Change of the dequantised E2M1 value (in units of s) if y/s sits within
- * relative eps of a rounding midpoint and the other neighbour is taken. */
-static double tho_e2m1_flip(double y, double s, double eps) {
+/* ---- decisions a device implementation may take either way ----
+ * A device evaluates scores and exponentials in fp32.  A decision (a code, a
+ * block scale, an fp16 rounding) whose exact input lies closer to its
+ * rounding boundary than that evaluation error may come out either way; both
+ * outcomes are then valid results of the method.  Evaluation-error model
+ * (u = 2^-24):
+ *  - a score s = q.k comes from a chain of matrix instructions over
+ *    ascending slices of the contraction, each with exact products and
+ *    returning within kappa u (|C| + sum over its slice of |product|) of the
+ *    exact value (C the running accumulator), so s is within kappa u B of
+ *    exact, B = sum over the slices of (|exact partial sum before the slice|
+ *    + the slice's sum of |products|).  MX: the block-scaled FP4 instruction,
+ *    64 channels each, kappa = 2; NVFP4 (decoded operands), the middle tier
+ *    and FP16: the fp16 instruction, 16 channels each, kappa = 5.  These are
+ *    the measured maxima (1.88 and 4.28 on random operands with spread block
+ *    scales) rounded up;
+ *  - the softmax multiplier c = sm_scale log2(e) is an fp32 value carrying nc
+ *    roundings (sm_scale to fp32, log2(e), the product: 3; NVFP4's two slice
+ *    scales add 2), and the exponent's argument fma(s, c, -fl(c smax)) is
+ *    within c (ds + dsmax) + (nc + 1) u |t - mt| + u |mt| of t - mt (log2
+ *    units; B is taken in the same units, times sm_scale log2(e));
+ *  - exp2 is within 2^-23 relative (one ulp);
+ *  - NVFP4 adds four roundings to a value's decision input (the factor 2688,
+ *    the block scale's reciprocal, the products).
+ * tho_eval_rel is the resulting bound on the relative error of a tile value
+ * v, times 1 + 2^-10 for second-order terms. */
+#define THO_U 0x1p-24
+#define THO_EXP_REL 0x1p-23
+#define THO_PATH_MX4 0 /* FP4 path, MX format */
+#define THO_PATH_NV4 1 /* FP4 path, NVFP4 format */
+#define THO_PATH_F8 2  /* middle (MXFP8) tier */
+#define THO_PATH_F16 3 /* FP16 path */
+#define THO_PATH_NVMXP 4 /* FP4 path of the variant: NVFP4 tensors, P quantised MX-style */
+
+/* Channels per matrix instruction of a path's scores. */
+static int tho_path_slice(int path) { return path == THO_PATH_MX4 ? 64 : 16; }
+
+/* Evaluation path of a tile's scores: FP4 tiles follow the tensors' format
+ * (and the variant's P format), the other tiers their own. */
+static int tho_eval_path(int prec, int fmt) {
+  if (prec == THO_PATH_MX4 && fmt == THO_NVFP4) return THO_PATH_NVMXP;
+  return prec;
+}
+
+/* b, bmax: the chain sums B of the key's score and of the tile maximum's
+ * score (log2 units); dt = t - mt; mt the tile maximum (log2 units). */
+double tho_eval_rel(int path, double b, double bmax, double dt, double mt) {
+  double kappa = path == THO_PATH_MX4 ? 2.0 : 5.0;
+  double nc = path == THO_PATH_NV4 || path == THO_PATH_NVMXP ? 5.0 : 3.0;
+  double arg = kappa * THO_U * (b + bmax) + (nc + 1.0) * THO_U * fabs(dt) + THO_U * fabs(mt);
+  double rel = THO_LN2 * arg + THO_EXP_REL + (path == THO_PATH_NV4 ? 4.0 * THO_U : 0.0);
+  return rel * (1.0 + 0x1p-10);
+}
+
+/* The other outcome of rounding q to the nearest E2M1 magnitude (q >= 0) if q
+ * lies within relative rel of a rounding midpoint; -1 otherwise. */
+static double tho_e2m1_alt(double q, double rel) {
   static const double mid[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
-  if (!(y > 0.0) || !(s > 0.0)) return 0.0;
-  double q = y / s;
   for (int k = 0; k < 7; ++k)
-    if (fabs(q - mid[k]) <= eps * q) return (tho_e2m1_mag[k + 1] - tho_e2m1_mag[k]) * s;
-  return 0.0;
-}
-
-/* One fp16 spacing at y if y sits within relative eps of an fp16 midpoint. */
-static double tho_half_flip(double y, double eps) {
-  if (!(y > 0.0)) return 0.0;
-  int e;
-  frexp(y, &e);
-  int ue = e - 11 < -24 ? -24 : e - 11;
-  double sp = ldexp(1.0, ue);
-  double mid = floor(y / sp) * sp + 0.5 * sp;
-  return fabs(y - mid) <= eps * y ? sp : 0.0;
-}
-
-/* Quantise v[g0..g1) of one group with block scale s2 into out[] (values). */
-static void tho_quantize_group_values(const double* v, int g0, int g1, double s2, double* out) {
-  for (int c = g0; c < g1; ++c) out[c] = s2 > 0.0 ? tho_e2m1_value(tho_e2m1_encode(v[c], s2)) * s2 : 0.0;
-}
-
-static void tho_quantize_p_tile(const double* t, const double* ta, const int* mask, int n, int fmt,
-                                double mt, double* pq, double* dq, double* ref) {
-  int g = tho_group_size(fmt);
-  double v[64], alt[64];
-  if (fmt == THO_NVFP4) {
-    for (int c = 0; c < n; ++c) v[c] = mask[c] ? 0.0 : 2688.0 * exp2(t[c] - mt);
-    *ref = mt;
-  } else {
-    double z = ceil(mt);
-    for (int c = 0; c < n; ++c) v[c] = mask[c] ? 0.0 : exp2(t[c] - z);
-    *ref = z;
-  }
-  for (int g0 = 0; g0 < n; g0 += g) {
-    int g1 = g0 + g < n ? g0 + g : n;
-    double amax = 0.0;
-    for (int c = g0; c < g1; ++c)
-      if (v[c] > amax) amax = v[c];
-    if (fmt == THO_NVFP4) {
-      double s2 = tho_e4m3_value(tho_e4m3_encode_ratio(amax, 6.0));
-      for (int c = g0; c < g1; ++c)
-        pq[c] = s2 > 0.0 ? tho_e2m1_value(tho_e2m1_encode(v[c], s2)) * s2 / 2688.0 : 0.0;
-    } else {
-      double s2 = ldexp(1.0, tho_mx_exponent(amax));
-      for (int c = g0; c < g1; ++c) pq[c] = tho_e2m1_value(tho_e2m1_encode(v[c], s2)) * s2;
+    if (fabs(q - mid[k]) <= rel * q) {
+      double chosen = tho_e2m1_value(tho_e2m1_encode(q, 1.0));
+      return chosen == tho_e2m1_mag[k] ? tho_e2m1_mag[k + 1] : tho_e2m1_mag[k];
     }
-    if (!dq) continue;
-    /* uncertainty: element codes near a midpoint, and a block scale near its
-     * own rounding boundary (NVFP4 values carry the error of two
-     * exponentials, the element's and the tile maximum's) */
-    double unit = fmt == THO_NVFP4 ? 1.0 / 2688.0 : 1.0;
-    double ag = 0.0; /* largest magnitude sum among the tile's scores */
-    for (int c = 0; c < n; ++c)
-      if (!mask[c] && ta[c] > ag) ag = ta[c];
-    double eg = (fmt == THO_NVFP4 ? 2.0 : 1.0) * tho_eval_eps(ag);
-    double s2, s2alt;
-    if (fmt == THO_NVFP4) {
-      int code = tho_e4m3_encode_ratio(amax, 6.0);
-      int lo = tho_e4m3_encode_ratio(amax * (1.0 - 2.0 * eg), 6.0);
-      int hi = tho_e4m3_encode_ratio(amax * (1.0 + 2.0 * eg), 6.0);
-      s2 = tho_e4m3_value(code);
-      s2alt = tho_e4m3_value(lo != code ? lo : hi);
-    } else {
-      int X = tho_mx_exponent(amax);
-      int lo = tho_mx_exponent(amax * (1.0 - 2.0 * eg));
-      int hi = tho_mx_exponent(amax * (1.0 + 2.0 * eg));
-      s2 = ldexp(1.0, X);
-      s2alt = ldexp(1.0, lo != X ? lo : hi);
-    }
-    if (s2alt != s2) tho_quantize_group_values(v, g0, g1, s2alt, alt);
-    for (int c = g0; c < g1; ++c) {
-      if (mask[c]) {
-        dq[c] = 0.0;
-        continue;
-      }
-      double ec = fmt == THO_NVFP4 ? tho_eval_eps(ta[c]) + tho_eval_eps(ag) : tho_eval_eps(ta[c]);
-      double d = tho_e2m1_flip(v[c], s2, ec);
-      if (s2alt != s2) d += fabs(alt[c] - pq[c] / unit) + tho_e2m1_flip(v[c], s2alt, ec);
-      dq[c] = d * unit;
-    }
-  }
+  return -1.0;
 }
 
-/* One E4M3 spacing (in units of s) if y/s sits within relative eps of a
- * rounding midpoint between two finite E4M3 values. */
-static double tho_e4m3_flip(double y, double s, double eps) {
-  if (!(y > 0.0) || !(s > 0.0)) return 0.0;
-  double q = y / s;
+/* The same for the nearest finite E4M3 magnitude (q >= 0). */
+static double tho_e4m3_alt(double q, double rel) {
   for (int k = 0; k < 126; ++k) {
     double lo = tho_e4m3_value(k), hi = tho_e4m3_value(k + 1);
-    if (fabs(q - 0.5 * (lo + hi)) <= eps * q) return (hi - lo) * s;
-  }
-  return 0.0;
-}
-
-/* P of one tile on the middle (FP8) tier, two levels as on the MX FP4 path
- * with E4M3 elements: v = 2^(t - z), z = ceil(mt); per 32 keys (V's groups)
- * X = tho_mx8_exponent(max v), code E4M3(v / 2^X); the dequantised
- * probability relative to 2^z is code * 2^X.  dq as for tho_quantize_p_tile. */
-static void tho_quantize_p_tile8(const double* t, const double* ta, const int* mask, int n, double mt,
-                                 double* pq, double* dq, double* ref) {
-  double v[64];
-  double z8 = ceil(mt);
-  *ref = z8;
-  for (int c = 0; c < n; ++c) v[c] = mask[c] ? 0.0 : exp2(t[c] - z8);
-  double ag = 0.0;
-  for (int c = 0; c < n; ++c)
-    if (!mask[c] && ta[c] > ag) ag = ta[c];
-  for (int g0 = 0; g0 < n; g0 += 32) {
-    int g1 = g0 + 32 < n ? g0 + 32 : n;
-    double amax = 0.0;
-    for (int c = g0; c < g1; ++c)
-      if (v[c] > amax) amax = v[c];
-    int X = tho_mx8_exponent(amax);
-    double s2 = ldexp(1.0, X);
-    for (int c = g0; c < g1; ++c) pq[c] = tho_e4m3_value(tho_e4m3_encode_ratio(v[c], s2)) * s2;
-    if (!dq) continue;
-    double eg = tho_eval_eps(ag);
-    int lo = tho_mx8_exponent(amax * (1.0 - 2.0 * eg));
-    int hi = tho_mx8_exponent(amax * (1.0 + 2.0 * eg));
-    double s2alt = ldexp(1.0, lo != X ? lo : hi);
-    for (int c = g0; c < g1; ++c) {
-      if (mask[c]) {
-        dq[c] = 0.0;
-        continue;
-      }
-      double ec = tho_eval_eps(ta[c]);
-      double d = tho_e4m3_flip(v[c], s2, ec);
-      if (s2alt != s2)
-        d += fabs(tho_e4m3_value(tho_e4m3_encode_ratio(v[c], s2alt)) * s2alt - pq[c]) +
-             tho_e4m3_flip(v[c], s2alt, ec);
-      dq[c] = d;
+    if (fabs(q - 0.5 * (lo + hi)) <= rel * q) {
+      double chosen = tho_e4m3_value(tho_e4m3_encode_ratio(q, 1.0));
+      return chosen == lo ? hi : lo;
     }
   }
+  return -1.0;
+}
+
+/* The other outcomes of rounding q > 0 to fp16 when q may be off by a
+ * relative rel: every fp16 value some point of [q (1 - rel), q (1 + rel)]
+ * rounds to, other than fp16(q) (at most 8; returns their number). */
+static int tho_half_alts(double q, double rel, double* alt) {
+  if (!(q > 0.0)) return 0;
+  double r = tho_round_to_half(q), lo = tho_round_to_half(q * (1.0 - rel)), hi = tho_round_to_half(q * (1.0 + rel));
+  int n = 0;
+  for (double x = lo; x <= hi && n < 8;) {
+    if (x != r) alt[n++] = x;
+    int e;
+    frexp(x > 0.0 ? x : 0x1p-25, &e);
+    int ue = e - 11 < -24 ? -24 : e - 11;
+    x = x > 0.0 ? x + ldexp(1.0, ue) : 0x1p-24; /* the next fp16 value up */
+  }
+  return n;
+}
+
+/* One decision of a tile that may go either way: its other outcome changes
+ * the values (relative to 2^mt) of keys [k0, k1) of the tile by dp[]. */
+typedef struct {
+  int k0, k1;
+  double dp[64];
+} tho_flip;
+
+static int tho_add_flip(tho_flip* flips, int nf, int maxf, int k0, int k1, const double* dp) {
+  if (!flips || nf >= maxf) return nf + (flips ? 1 : 0);
+  flips[nf].k0 = k0;
+  flips[nf].k1 = k1;
+  for (int c = k0; c < k1; ++c) flips[nf].dp[c] = dp[c];
+  return nf + 1;
+}
+
+/* Block scale of a level-2 group from its largest value vmax. */
+static double tho_p_scale(int prec, double vmax) {
+  if (prec == THO_PATH_NV4) return tho_e4m3_value(tho_e4m3_encode_ratio(vmax, 6.0));
+  if (prec == THO_PATH_F8) return ldexp(1.0, tho_mx8_exponent(vmax));
+  return ldexp(1.0, tho_mx_exponent(vmax));
+}
+
+/* Level-2 value of v under block scale s2 (relative to the level-1 unit). */
+static double tho_p_value(int prec, double v, double s2) {
+  if (prec == THO_PATH_NV4) return s2 > 0.0 ? tho_e2m1_value(tho_e2m1_encode(v, s2)) * s2 / 2688.0 : 0.0;
+  if (prec == THO_PATH_F8) return tho_e4m3_value(tho_e4m3_encode_ratio(v, s2)) * s2;
+  return tho_e2m1_value(tho_e2m1_encode(v, s2)) * s2;
+}
+
+/* Level-2 values pq[] (relative to 2^mt) of one tile row of n keys in
+ * precision prec (THO_PATH_MX4, _NV4 or _F8) from scores t, chain sums ta
+ * and mask (masked keys: value 0); epath is the scores' evaluation path.  With
+ * flips != NULL also every decision within evaluation error of its boundary
+ * (tho_eval_rel): element codes near a rounding midpoint, and block scales
+ * whose group maximum lies near the scale rule's boundary.  A group holding
+ * the tile maximum has its largest value exactly at the top of the scale
+ * rule (1, or 2688 for NVFP4); its scale is decided unless a key outside it
+ * could evaluate as the tile's maximum.  Returns the number of decisions
+ * (at most maxf are stored). */
+static int tho_quantize_p_tile(const double* t, const double* ta, const int* mask, int n, int prec,
+                               int epath, double mt, double* pq, tho_flip* flips, int maxf) {
+  int gs = prec == THO_PATH_NV4 ? 16 : 32;
+  double top = prec == THO_PATH_NV4 ? 2688.0 : 1.0;
+  double v[64], rel[64], dp[64];
+  int imax = -1, nf = 0;
+  for (int c = 0; c < n; ++c) {
+    v[c] = mask[c] ? 0.0 : top * exp2(t[c] - mt);
+    if (!mask[c] && t[c] == mt && imax < 0) imax = c;
+  }
+  for (int c = 0; c < n; ++c)
+    rel[c] = mask[c] ? 0.0 : tho_eval_rel(epath, ta[c], ta[imax], t[c] - mt, mt);
+  for (int g0 = 0; g0 < n; g0 += gs) {
+    int g1 = g0 + gs < n ? g0 + gs : n;
+    double amax = 0.0;
+    int cm = -1;
+    for (int c = g0; c < g1; ++c)
+      if (v[c] > amax) {
+        amax = v[c];
+        cm = c;
+      }
+    double s2 = tho_p_scale(prec, amax);
+    for (int c = g0; c < g1; ++c) pq[c] = mask[c] ? 0.0 : tho_p_value(prec, v[c], s2);
+    if (!flips || cm < 0) continue;
+    for (int c = g0; c < g1; ++c) {
+      double alt = mask[c] ? -1.0
+                   : prec == THO_PATH_F8 ? tho_e4m3_alt(v[c] / s2, rel[c])
+                                         : (s2 > 0.0 ? tho_e2m1_alt(v[c] / s2, rel[c]) : -1.0);
+      if (alt < 0.0) continue;
+      for (int k = g0; k < g1; ++k) dp[k] = 0.0;
+      dp[c] = alt * s2 / (prec == THO_PATH_NV4 ? 2688.0 : 1.0) - pq[c];
+      nf = tho_add_flip(flips, nf, maxf, c, c + 1, dp);
+    }
+    int decided = t[cm] == mt;
+    for (int c = 0; c < n && decided; ++c)
+      if ((c < g0 || c >= g1) && !mask[c] && top - v[c] <= rel[c] * top) decided = 0;
+    if (decided) continue;
+    double lo = tho_p_scale(prec, amax * (1.0 - rel[cm])), hi = tho_p_scale(prec, amax * (1.0 + rel[cm]));
+    double s2alt = lo != s2 ? lo : hi;
+    if (s2alt == s2) continue;
+    for (int c = g0; c < g1; ++c) dp[c] = mask[c] ? 0.0 : tho_p_value(prec, v[c], s2alt) - pq[c];
+    nf = tho_add_flip(flips, nf, maxf, g0, g1, dp);
+  }
+  return nf;
+}
+
+/* FP16-path values of one tile row: pq[c] = fp16(2^(t - mt)), and the fp16
+ * roundings within evaluation error of a midpoint. */
+static int tho_quantize_p_tile16(const double* t, const double* ta, const int* mask, int n, double mt,
+                                 double* pq, tho_flip* flips, int maxf) {
+  double dp[64];
+  int imax = -1, nf = 0;
+  for (int c = 0; c < n; ++c)
+    if (!mask[c] && t[c] == mt && imax < 0) imax = c;
+  for (int c = 0; c < n; ++c) pq[c] = mask[c] ? 0.0 : tho_round_to_half(exp2(t[c] - mt));
+  if (!flips) return 0;
+  for (int c = 0; c < n; ++c) {
+    if (mask[c]) continue;
+    double alt[8];
+    int na = tho_half_alts(exp2(t[c] - mt), tho_eval_rel(THO_PATH_F16, ta[c], ta[imax], t[c] - mt, mt), alt);
+    for (int k = 0; k < na; ++k) {
+      dp[c] = alt[k] - pq[c];
+      nf = tho_add_flip(flips, nf, maxf, c, c + 1, dp);
+    }
+  }
+  return nf;
 }
 
 typedef struct {
@@ -766,11 +816,49 @@ typedef struct {
   int kmax2;
   const uint8_t *q8c, *q8s; /* MXFP8 queries as quantised */
   const double *k8, *v8;    /* dequantised MXFP8 keys and values, [B,Hkv,Sk,D] */
+  /* decisions that may go either way (NULL: not wanted): row index
+   * ((b * Hq + hq) * S + r) and the change of that row of O if the decision
+   * takes its other outcome; *amb_n counts them (capacity amb_cap) */
+  int32_t* amb_row;
+  double* amb_delta;
+  int amb_cap;
+  int* amb_n;
 } tho_attn_args;
+
+#define THO_TILE_FLIPS 520 /* at most 64 keys x 8 fp16 outcomes, or 64 codes and 4 block scales, per tile */
+
+/* Scores of query row r against the n keys of key block j from query qv and
+ * keys kv ([keys, D], dequantised to fp64); masked keys get -inf.  tb[c]
+ * receives the score's chain sum B for slices of `slice` channels (see the
+ * evaluation-error model), in the same log2 units. */
+static double tho_tile_scores(const tho_attn_args* a, const double* qv, const double* kv, int c0, int n,
+                              int qpos, int slice, double* t, double* tb, int* mask) {
+  int D = a->D;
+  double mt = -INFINITY;
+  for (int c = 0; c < n; ++c) {
+    mask[c] = a->causal && (c0 + c > qpos);
+    double s = 0.0, b = 0.0;
+    if (!mask[c])
+      for (int d0 = 0; d0 < D; d0 += slice) {
+        double part = 0.0, sa = 0.0;
+        for (int d = d0; d < d0 + slice && d < D; ++d) {
+          double pr = qv[d] * kv[(size_t)c * D + d];
+          part += pr;
+          sa += fabs(pr);
+        }
+        b += fabs(s) + sa;
+        s += part;
+      }
+    t[c] = mask[c] ? -INFINITY : s * a->sm_scale * THO_LOG2E;
+    tb[c] = b * a->sm_scale * THO_LOG2E;
+    if (t[c] > mt) mt = t[c];
+  }
+  return mt;
+}
 
 /* One query row r of query block i of head (b, hq). */
 static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, double* o_row,
-                           double* lse_out, double* u_row, double* ohp_row) {
+                           double* lse_out, double* ohp_row) {
   int D = a->D, S = a->S, Sk = a->Sk, bk = a->bk;
   int hk = hq / (a->Hq / a->Hkv);
   int nq = tho_cdiv(S, a->bq);
@@ -782,232 +870,160 @@ static void tho_attend_row(const tho_attn_args* a, int b, int hq, int i, int r, 
   const int32_t* sel2 = a->idx2 ? a->idx2 + (((size_t)b * a->Hq + hq) * nq + i) * a->kmax2 : NULL;
   int nsel2 = a->idx2 ? a->cnt2[((size_t)b * a->Hq + hq) * nq + i] : 0;
   int nvalid = tho_valid_blocks_kv(i, S, Sk, a->bq, bk, a->causal);
-  double t[64], ta[64], pq[64], dq[64];
+  double t[64], ta[64], pq[64];
   int mask[64];
   double* acc = (double*)calloc((size_t)D, sizeof(double));
-  double* uacc = (double*)calloc((size_t)D, sizeof(double)); /* uncertainty, like acc */
   /* the high-precision output O' (Attn-QAT): the same sum with the exact
    * probabilities in place of the quantised or fp16-rounded ones */
   double* hacc = (double*)calloc((size_t)D, sizeof(double));
-  double ul = 0.0; /* uncertainty of the row sum, like l */
   double* qh = (double*)malloc(sizeof(double) * (size_t)D);
   double* q4 = (double*)malloc(sizeof(double) * (size_t)D);
+  double* q8 = (double*)malloc(sizeof(double) * (size_t)D);
+  double* k16t = (double*)malloc(sizeof(double) * (size_t)bk * D);
+  double* v16t = (double*)malloc(sizeof(double) * (size_t)bk * D);
+  int want = a->amb_row != NULL;
+  tho_flip* tf = want ? (tho_flip*)malloc(sizeof(tho_flip) * THO_TILE_FLIPS) : NULL;
+  /* this row's decisions: the tile's level-1 exponent mt and the change of
+   * the numerator (in units of 2^mt) if the decision flips */
+  int nrf = 0, caprf = 0;
+  double* rref = NULL;
+  double* rvec = NULL;
   double m = -INFINITY, l = 0.0;
   tho_dequant_row(a->q4c, a->q4s, a->q4t, (size_t)b * a->Hq + hq, S, D, r, a->fmt, q4);
+  if (nsel2 > 0) tho_dequant8_row(a->q8c, a->q8s, (size_t)b * a->Hq + hq, S, D, r, q8);
+  if (nsel > 0)
+    for (int d = 0; d < D; ++d) qh[d] = tho_half_to_double(a->q16[qoff + d]);
 
-  /* FP4 path first, over every valid key block not promoted (to either
-   * higher tier), ascending. */
+  /* Tiles in the pages' order: the FP4 path first, over every valid key
+   * block that no higher tier lists, ascending; then the middle tier over
+   * the blocks idx2 lists and idx does not; then the FP16 path over the
+   * promoted blocks, ascending (the FP16 query row is read only then). */
+  int npass = nvalid + nsel2 + nsel;
   int sp = 0, sp2 = 0;
-  for (int j = 0; j < nvalid; ++j) {
-    int listed = 0;
-    if (sp < nsel && sel[sp] == j) {
-      ++sp;
-      listed = 1;
-    }
-    if (sp2 < nsel2 && sel2[sp2] == j) {
-      ++sp2;
-      listed = 1;
-    }
-    if (listed) continue;
-    int c0 = j * bk, n = (c0 + bk < Sk ? c0 + bk : Sk) - c0;
-    double mt = -INFINITY;
-    for (int c = 0; c < n; ++c) {
-      mask[c] = a->causal && (c0 + c > qpos);
-      double s = 0.0, sa = 0.0;
-      if (!mask[c]) {
-        const double* qv = q4;
-        const double* kv = a->k4 + (kvbase + c0 + c) * D;
-        for (int d = 0; d < D; ++d) {
-          s += qv[d] * kv[d];
-          sa += fabs(qv[d] * kv[d]);
-        }
+  for (int step = 0; step < npass; ++step) {
+    int j, prec;
+    if (step < nvalid) {
+      j = step;
+      int listed = 0;
+      if (sp < nsel && sel[sp] == j) {
+        ++sp;
+        listed = 1;
       }
-      t[c] = mask[c] ? -INFINITY : s * a->sm_scale * THO_LOG2E;
-      ta[c] = sa * a->sm_scale * THO_LOG2E;
-      if (t[c] > mt) mt = t[c];
+      if (sp2 < nsel2 && sel2[sp2] == j) {
+        ++sp2;
+        listed = 1;
+      }
+      if (listed) continue;
+      prec = a->pfmt == THO_NVFP4 ? THO_PATH_NV4 : THO_PATH_MX4;
+    } else if (step < nvalid + nsel2) {
+      j = sel2[step - nvalid];
+      int in16 = 0;
+      for (int p = 0; p < nsel; ++p)
+        if (sel[p] == j) in16 = 1;
+      if (in16) continue;
+      prec = THO_PATH_F8;
+    } else {
+      j = sel[step - nvalid - nsel2];
+      prec = THO_PATH_F16;
+    }
+    int c0 = j * bk, n = (c0 + bk < Sk ? c0 + bk : Sk) - c0;
+    const double* vt;
+    double mt;
+    if (prec == THO_PATH_F16) {
+      for (size_t e = 0; e < (size_t)n * D; ++e) {
+        k16t[e] = tho_half_to_double(a->k16[(kvbase + c0) * D + e]);
+        v16t[e] = tho_half_to_double(a->v16[(kvbase + c0) * D + e]);
+      }
+      mt = tho_tile_scores(a, qh, k16t, c0, n, qpos, tho_path_slice(THO_PATH_F16), t, ta, mask);
+      vt = v16t;
+    } else if (prec == THO_PATH_F8) {
+      mt = tho_tile_scores(a, q8, a->k8 + (kvbase + c0) * D, c0, n, qpos, tho_path_slice(THO_PATH_F8), t, ta,
+                           mask);
+      vt = a->v8 + (kvbase + c0) * D;
+    } else {
+      mt = tho_tile_scores(a, q4, a->k4 + (kvbase + c0) * D, c0, n, qpos,
+                           tho_path_slice(tho_eval_path(prec, a->fmt)), t, ta, mask);
+      vt = a->v4 + (kvbase + c0) * D;
     }
     if (mt == -INFINITY) continue; /* every key of this block is masked for row r */
-    double ref;
-    tho_quantize_p_tile(t, ta, mask, n, a->pfmt, mt, pq, u_row ? dq : NULL, &ref);
+    /* the pages' FP4 tiles use the variant's P format for THO_NVFP4_MXP */
+    int nf = prec == THO_PATH_F16 ? tho_quantize_p_tile16(t, ta, mask, n, mt, pq, tf, THO_TILE_FLIPS)
+                                  : tho_quantize_p_tile(t, ta, mask, n, prec, tho_eval_path(prec, a->fmt), mt, pq,
+                                                        tf, THO_TILE_FLIPS);
     double m_new = m > mt ? m : mt;
     double alpha = exp2(m - m_new); /* 0 when m = -inf */
-    double w = exp2(ref - m_new);
-    double emt = 0.0; /* NVFP4: error of the level-1 factor 2^mt */
-    if (a->pfmt == THO_NVFP4)
-      for (int c = 0; c < n; ++c)
-        if (!mask[c] && t[c] == mt) emt = tho_eval_eps(ta[c]);
-    if (u_row)
-      for (int d = 0; d < D; ++d) {
-        double uv = 0.0, pv = 0.0;
-        for (int c = 0; c < n; ++c) {
-          uv += dq[c] * fabs(a->v4[(kvbase + c0 + c) * D + d]);
-          pv += fabs(pq[c] * a->v4[(kvbase + c0 + c) * D + d]);
-        }
-        uacc[d] = alpha * uacc[d] + w * (uv + emt * pv);
-      }
-    double psum = 0.0, upsum = 0.0;
+    double w = exp2(mt - m_new);    /* level 1 relative to the running maximum */
+    double psum = 0.0;
     for (int c = 0; c < n; ++c)
-      if (!mask[c]) {
-        psum += exp2(t[c] - m_new);
-        upsum += exp2(t[c] - m_new) * tho_eval_eps(ta[c]);
-      }
+      if (!mask[c]) psum += exp2(t[c] - m_new);
     l = alpha * l + psum;
-    ul = alpha * ul + upsum;
     for (int d = 0; d < D; ++d) {
       double pv = 0.0, hv = 0.0;
       for (int c = 0; c < n; ++c) {
-        pv += pq[c] * a->v4[(kvbase + c0 + c) * D + d];
-        if (!mask[c]) hv += exp2(t[c] - m_new) * a->v4[(kvbase + c0 + c) * D + d];
+        pv += pq[c] * vt[(size_t)c * D + d];
+        if (!mask[c]) hv += exp2(t[c] - m_new) * vt[(size_t)c * D + d];
       }
       acc[d] = alpha * acc[d] + w * pv;
       hacc[d] = alpha * hacc[d] + hv;
     }
     m = m_new;
-  }
-
-  /* Middle (FP8) tier, over the blocks idx2 lists and idx does not,
-   * ascending: MXFP8 scores, P quantised in two levels with E4M3 elements,
-   * MXFP8 values; the row sum takes the unquantised probabilities. */
-  double* q8 = (double*)malloc(sizeof(double) * (size_t)D);
-  if (nsel2 > 0) tho_dequant8_row(a->q8c, a->q8s, (size_t)b * a->Hq + hq, S, D, r, q8);
-  for (int p2 = 0; p2 < nsel2; ++p2) {
-    int j = sel2[p2], in16 = 0;
-    for (int p = 0; p < nsel; ++p)
-      if (sel[p] == j) in16 = 1;
-    if (in16) continue;
-    int c0 = j * bk, n = (c0 + bk < Sk ? c0 + bk : Sk) - c0;
-    double mt = -INFINITY;
-    for (int c = 0; c < n; ++c) {
-      mask[c] = a->causal && (c0 + c > qpos);
-      double s8 = 0.0, sa8 = 0.0;
-      if (!mask[c]) {
-        const double* kv = a->k8 + (kvbase + c0 + c) * D;
+    if (want) {
+      for (int f = 0; f < nf; ++f) {
+        if (nrf == caprf) {
+          caprf = caprf ? 2 * caprf : 16;
+          rref = (double*)realloc(rref, sizeof(double) * (size_t)caprf);
+          rvec = (double*)realloc(rvec, sizeof(double) * (size_t)caprf * D);
+        }
+        rref[nrf] = mt;
         for (int d = 0; d < D; ++d) {
-          s8 += q8[d] * kv[d];
-          sa8 += fabs(q8[d] * kv[d]);
+          double s = 0.0;
+          for (int c = tf[f].k0; c < tf[f].k1; ++c) s += tf[f].dp[c] * vt[(size_t)c * D + d];
+          rvec[(size_t)nrf * D + d] = s;
         }
+        ++nrf;
       }
-      t[c] = mask[c] ? -INFINITY : s8 * a->sm_scale * THO_LOG2E;
-      ta[c] = sa8 * a->sm_scale * THO_LOG2E;
-      if (t[c] > mt) mt = t[c];
     }
-    if (mt == -INFINITY) continue;
-    double ref;
-    tho_quantize_p_tile8(t, ta, mask, n, mt, pq, u_row ? dq : NULL, &ref);
-    double m_new = m > mt ? m : mt;
-    double alpha = exp2(m - m_new);
-    double w = exp2(ref - m_new);
-    if (u_row)
-      for (int d = 0; d < D; ++d) {
-        double uv = 0.0;
-        for (int c = 0; c < n; ++c) uv += dq[c] * fabs(a->v8[(kvbase + c0 + c) * D + d]);
-        uacc[d] = alpha * uacc[d] + w * uv;
-      }
-    double p8sum = 0.0, up8sum = 0.0;
-    for (int c = 0; c < n; ++c)
-      if (!mask[c]) {
-        p8sum += exp2(t[c] - m_new);
-        up8sum += exp2(t[c] - m_new) * tho_eval_eps(ta[c]);
-      }
-    l = alpha * l + p8sum;
-    ul = alpha * ul + up8sum;
-    for (int d = 0; d < D; ++d) {
-      double pv8 = 0.0, hv8 = 0.0;
-      for (int c = 0; c < n; ++c) {
-        pv8 += pq[c] * a->v8[(kvbase + c0 + c) * D + d];
-        if (!mask[c]) hv8 += exp2(t[c] - m_new) * a->v8[(kvbase + c0 + c) * D + d];
-      }
-      acc[d] = alpha * acc[d] + w * pv8;
-      hacc[d] = alpha * hacc[d] + hv8;
-    }
-    m = m_new;
-  }
-
-  /* FP16 path last, over the promoted blocks, ascending; the FP16 query
-   * row is read only here. */
-  if (nsel > 0)
-    for (int d = 0; d < D; ++d) qh[d] = tho_half_to_double(a->q16[qoff + d]);
-  for (int p = 0; p < nsel; ++p) {
-    int j = sel[p];
-    int c0 = j * bk, n = (c0 + bk < Sk ? c0 + bk : Sk) - c0;
-    double mt = -INFINITY;
-    for (int c = 0; c < n; ++c) {
-      mask[c] = a->causal && (c0 + c > qpos);
-      double s = 0.0, sa = 0.0;
-      if (!mask[c])
-        for (int d = 0; d < D; ++d) {
-          double pr = qh[d] * tho_half_to_double(a->k16[(kvbase + c0 + c) * D + d]);
-          s += pr;
-          sa += fabs(pr);
-        }
-      t[c] = mask[c] ? -INFINITY : s * a->sm_scale * THO_LOG2E;
-      ta[c] = sa * a->sm_scale * THO_LOG2E;
-      if (t[c] > mt) mt = t[c];
-    }
-    if (mt == -INFINITY) continue;
-    double m_new = m > mt ? m : mt;
-    double alpha = exp2(m - m_new);
-    /* The probabilities enter the FP16 product as fp16 values.  Reading: they
-     * are rounded to fp16 on a power-of-two footing, as fp16(2^(t - z)) with
-     * z = ceil(m_new), which rounds 2^t to fp16's 11 significant bits
-     * whichever integer z is used. */
-    double z = ceil(m_new);
-    double psum = 0.0, upsum = 0.0;
-    for (int c = 0; c < n; ++c) {
-      if (mask[c]) {
-        pq[c] = 0.0;
-        dq[c] = 0.0;
-        continue;
-      }
-      psum += exp2(t[c] - m_new);
-      upsum += exp2(t[c] - m_new) * tho_eval_eps(ta[c]);
-      pq[c] = tho_round_to_half(exp2(t[c] - z)) * exp2(z - m_new);
-      dq[c] = tho_half_flip(exp2(t[c] - z), tho_eval_eps(ta[c])) * exp2(z - m_new);
-    }
-    if (u_row)
-      for (int d = 0; d < D; ++d) {
-        double uv = 0.0;
-        for (int c = 0; c < n; ++c)
-          if (!mask[c]) uv += dq[c] * fabs(tho_half_to_double(a->v16[(kvbase + c0 + c) * D + d]));
-        uacc[d] = alpha * uacc[d] + uv;
-      }
-    l = alpha * l + psum;
-    ul = alpha * ul + upsum;
-    for (int d = 0; d < D; ++d) {
-      double pv = 0.0, hv = 0.0;
-      for (int c = 0; c < n; ++c)
-        if (!mask[c]) {
-          double vv = tho_half_to_double(a->v16[(kvbase + c0 + c) * D + d]);
-          pv += pq[c] * vv;
-          hv += exp2(t[c] - m_new) * vv;
-        }
-      acc[d] = alpha * acc[d] + pv;
-      hacc[d] = alpha * hacc[d] + hv;
-    }
-    m = m_new;
   }
 
   for (int d = 0; d < D; ++d) o_row[d] = acc[d] / l;
   if (ohp_row)
     for (int d = 0; d < D; ++d) ohp_row[d] = hacc[d] / l;
-  if (u_row)
-    for (int d = 0; d < D; ++d) u_row[d] = uacc[d] / l + fabs(o_row[d]) * ul / l;
   if (lse_out) *lse_out = m * THO_LN2 + log(l);
+  if (want && nrf > 0) {
+    int base;
+#pragma omp atomic capture
+    {
+      base = *a->amb_n;
+      *a->amb_n += nrf;
+    }
+    for (int f = 0; f < nrf; ++f) {
+      if (base + f >= a->amb_cap) break;
+      a->amb_row[base + f] = (int32_t)(((size_t)b * a->Hq + hq) * S + r);
+      double scale = exp2(rref[f] - m) / l;
+      for (int d = 0; d < D; ++d) a->amb_delta[(size_t)(base + f) * D + d] = rvec[(size_t)f * D + d] * scale;
+    }
+  }
+  free(rvec);
+  free(rref);
+  free(tf);
+  free(v16t);
+  free(k16t);
   free(q8);
-  free(hacc);
-  free(uacc);
   free(q4);
   free(qh);
+  free(hacc);
   free(acc);
 }
 
 /* Full forward for a list of work items (b, hq, i) (NULL: all of them).
  * q4/k4/v4 are the FP4 tensors as written by tho_quantize (V along the
  * sequence axis); q16/k16/v16 may be NULL when no block is promoted.
- * o: [B, Hq, S, D] fp64, lse: [B, Hq, S] (may be NULL) and u: [B, Hq, S, D]
- * (may be NULL), the bound on what decisions within fp32 evaluation error of
- * their rounding boundary can change in o; rows outside the work items are
- * left untouched. */
+ * o: [B, Hq, S, D] fp64, lse: [B, Hq, S] (may be NULL).  With amb_row !=
+ * NULL every decision within evaluation error of its rounding boundary
+ * (tho_eval_rel) is listed: amb_row[k] the row ((b * Hq + hq) * S + r) and
+ * amb_delta[k * D ...] the change of that row of o if the decision takes its
+ * other outcome; *amb_n receives their number, of which the first amb_cap
+ * are stored.  Rows outside the work items are left untouched. */
 static void tho_attention_impl(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
                                const uint8_t* q4c, const uint8_t* q4s, const float* q4t,
                                const uint8_t* k4c, const uint8_t* k4s, const float* k4t,
@@ -1018,9 +1034,15 @@ static void tho_attention_impl(const uint16_t* q16, const uint16_t* k16, const u
                                const int32_t* idx2, const int32_t* cnt2, int kmax2, int B, int Hq,
                                int Hkv, int S, int Sk, int D, int bq, int bk, int causal,
                                double sm_scale, const int32_t* work, int nwork, double* o,
-                               double* lse, double* u, double* ohp) {
+                               double* lse, int32_t* amb_row, double* amb_delta, int amb_cap,
+                               int* amb_n, double* ohp) {
   tho_attn_args a;
   memset(&a, 0, sizeof a);
+  a.amb_row = amb_row;
+  a.amb_delta = amb_delta;
+  a.amb_cap = amb_cap;
+  a.amb_n = amb_n;
+  if (amb_n) *amb_n = 0;
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -1080,8 +1102,7 @@ static void tho_attention_impl(const uint16_t* q16, const uint16_t* k16, const u
     int r0 = i * bq, r1 = r0 + bq < S ? r0 + bq : S;
     for (int r = r0; r < r1; ++r) {
       size_t row = ((size_t)b * Hq + hq) * S + r;
-      tho_attend_row(&a, b, hq, i, r, o + row * D, lse ? lse + row : NULL, u ? u + row * D : NULL,
-                     ohp ? ohp + row * D : NULL);
+      tho_attend_row(&a, b, hq, i, r, o + row * D, lse ? lse + row : NULL, ohp ? ohp + row * D : NULL);
     }
   }
   free(v8);
@@ -1096,10 +1117,10 @@ void tho_attention_kv(const uint16_t* q16, const uint16_t* k16, const uint16_t* 
                       const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
                       int B, int Hq, int Hkv, int S, int Sk, int D, int bq, int bk, int causal,
                       double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
-                      double* u) {
+                      int32_t* amb_row, double* amb_delta, int amb_cap, int* amb_n) {
   tho_attention_impl(q16, k16, v16, q4c, q4s, q4t, k4c, k4s, k4t, v4c, v4s, v4t, fmt, idx, cnt, kmax,
                      NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, B, Hq, Hkv, S, Sk, D, bq, bk,
-                     causal, sm_scale, work, nwork, o, lse, u, NULL);
+                     causal, sm_scale, work, nwork, o, lse, amb_row, amb_delta, amb_cap, amb_n, NULL);
 }
 
 /* The forward with a middle precision tier (a variant): the blocks idx2
@@ -1114,10 +1135,11 @@ void tho_attention_tiers(const uint16_t* q16, const uint16_t* k16, const uint16_
                          const int32_t* idx, const int32_t* cnt, int kmax, const int32_t* idx2,
                          const int32_t* cnt2, int kmax2, int B, int Hq, int Hkv, int S, int D,
                          int bq, int bk, int causal, double sm_scale, const int32_t* work,
-                         int nwork, double* o, double* lse, double* u) {
+                         int nwork, double* o, double* lse, int32_t* amb_row, double* amb_delta,
+                         int amb_cap, int* amb_n) {
   tho_attention_impl(q16, k16, v16, q4c, q4s, NULL, k4c, k4s, NULL, v4c, v4s, NULL, THO_MX, idx, cnt,
                      kmax, q8c, q8s, k8c, k8s, v8c, v8s, idx2, cnt2, kmax2, B, Hq, Hkv, S, S, D, bq,
-                     bk, causal, sm_scale, work, nwork, o, lse, u, NULL);
+                     bk, causal, sm_scale, work, nwork, o, lse, amb_row, amb_delta, amb_cap, amb_n, NULL);
 }
 
 /* The forward with Attn-QAT's extra output: ohp [B,Hq,S,D] receives O', the
@@ -1133,7 +1155,7 @@ void tho_attention_hp(const uint16_t* q16, const uint16_t* k16, const uint16_t* 
                       double* ohp) {
   tho_attention_impl(q16, k16, v16, q4c, q4s, q4t, k4c, k4s, k4t, v4c, v4s, v4t, fmt, idx, cnt, kmax,
                      NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL, 0, B, Hq, Hkv, S, S, D, bq, bk,
-                     causal, sm_scale, work, nwork, o, lse, NULL, ohp);
+                     causal, sm_scale, work, nwork, o, lse, NULL, NULL, 0, NULL, ohp);
 }
 
 void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
@@ -1142,9 +1164,10 @@ void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16
                    const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
                    int B, int Hq, int Hkv, int S, int D, int bq, int bk, int causal,
                    double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
-                   double* u) {
+                   int32_t* amb_row, double* amb_delta, int amb_cap, int* amb_n) {
   tho_attention_kv(q16, k16, v16, q4c, q4s, q4t, k4c, k4s, k4t, v4c, v4s, v4t, fmt, idx, cnt, kmax, B,
-                   Hq, Hkv, S, S, D, bq, bk, causal, sm_scale, work, nwork, o, lse, u);
+                   Hq, Hkv, S, S, D, bq, bk, causal, sm_scale, work, nwork, o, lse, amb_row, amb_delta,
+                   amb_cap, amb_n);
 }
 
 /* ------------------------------------------------------------------ */
@@ -1175,10 +1198,13 @@ void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16
 
 /* Probabilities of query row r against key block j (the block must be
  * valid for r's query block): kind[c] 0 masked, 1 FP4 path, 2 FP16 path;
- * p, pt as above; dpt (may be NULL) the change in pt that a decision within
- * fp32 evaluation error of its rounding boundary can make.  q4 and qh are
- * the row's dequantised FP4 and fp16 query; k16d, v16d the fp16 keys and
- * values as doubles.  Returns the number of keys in the block. */
+ * p, pt as above; dpt (may be NULL) the largest change in pt that decisions
+ * within evaluation error of their rounding boundary can make (FP4: the
+ * forward's decisions, tho_quantize_p_tile; FP16: the rounding of p, whose
+ * input also carries the error of an fp32 log-sum-exp, allowed for as 2^-16
+ * in log2 units).  q4 and qh are the row's dequantised FP4 and fp16 query;
+ * k16d, v16d the fp16 keys and values as doubles.  Returns the number of keys
+ * in the block. */
 static int tho_tile_probs(const tho_attn_args* a, const double* k16d, int b, int hq, int r, int j,
                           double L2, const double* q4, const double* qh, int* kind, double* p,
                           double* pt, double* dpt) {
@@ -1193,24 +1219,11 @@ static int tho_tile_probs(const tho_attn_args* a, const double* k16d, int b, int
   for (int s = 0; s < nsel; ++s)
     if (sel[s] == j) prom = 1;
   int c0 = j * bk, n = (c0 + bk < Sk ? c0 + bk : Sk) - c0;
-  double t[64], ta[64], pq[64], dq[64];
+  double t[64], ta[64], pq[64];
   int mask[64];
-  double mt = -INFINITY;
-  for (int c = 0; c < n; ++c) {
-    mask[c] = a->causal && (c0 + c > qpos);
-    double sd = 0.0, sa = 0.0;
-    if (!mask[c]) {
-      const double* qv = prom ? qh : q4;
-      const double* kv = (prom ? k16d : a->k4) + (kvbase + c0 + c) * D;
-      for (int d = 0; d < D; ++d) {
-        sd += qv[d] * kv[d];
-        sa += fabs(qv[d] * kv[d]);
-      }
-    }
-    t[c] = mask[c] ? -INFINITY : sd * a->sm_scale * THO_LOG2E;
-    ta[c] = sa * a->sm_scale * THO_LOG2E;
-    if (t[c] > mt) mt = t[c];
-  }
+  int fpath = a->pfmt == THO_NVFP4 ? THO_PATH_NV4 : THO_PATH_MX4;
+  double mt = tho_tile_scores(a, prom ? qh : q4, (prom ? k16d : a->k4) + (kvbase + c0) * D, c0, n, qpos,
+                              tho_path_slice(prom ? THO_PATH_F16 : tho_eval_path(fpath, a->fmt)), t, ta, mask);
   for (int c = 0; c < n; ++c) {
     kind[c] = 0;
     p[c] = pt[c] = 0.0;
@@ -1218,23 +1231,29 @@ static int tho_tile_probs(const tho_attn_args* a, const double* k16d, int b, int
   }
   if (mt == -INFINITY) return n;
   if (!prom) {
-    double ref;
-    tho_quantize_p_tile(t, ta, mask, n, a->pfmt, mt, pq, dpt ? dq : NULL, &ref);
+    tho_flip* tf = dpt ? (tho_flip*)malloc(sizeof(tho_flip) * THO_TILE_FLIPS) : NULL;
+    int nf = tho_quantize_p_tile(t, ta, mask, n, fpath, tho_eval_path(fpath, a->fmt), mt, pq, tf, THO_TILE_FLIPS);
     for (int c = 0; c < n; ++c)
       if (!mask[c]) {
         kind[c] = 1;
         p[c] = exp2(t[c] - L2);
-        pt[c] = pq[c] * exp2(ref - L2);
-        if (dpt) dpt[c] = dq[c] * exp2(ref - L2);
+        pt[c] = pq[c] * exp2(mt - L2);
       }
+    for (int f = 0; f < nf && dpt; ++f)
+      for (int c = tf[f].k0; c < tf[f].k1; ++c) dpt[c] += fabs(tf[f].dp[c]) * exp2(mt - L2);
+    free(tf);
   } else {
     for (int c = 0; c < n; ++c)
       if (!mask[c]) {
         kind[c] = 2;
         p[c] = exp2(t[c] - L2);
         pt[c] = tho_round_to_half(p[c]);
-        /* p carries the score's error and that of an fp32 log-sum-exp */
-        if (dpt) dpt[c] = tho_half_flip(p[c], tho_eval_eps(ta[c]) + tho_eval_eps(fabs(L2)));
+        if (dpt) {
+          double rel = tho_eval_rel(THO_PATH_F16, ta[c], 0.0, t[c] - L2, L2) + THO_LN2 * 0x1p-16, alt[8];
+          int na = tho_half_alts(p[c], rel, alt);
+          for (int k = 0; k < na; ++k)
+            if (fabs(alt[k] - pt[c]) > dpt[c]) dpt[c] = fabs(alt[k] - pt[c]);
+        }
       }
   }
   return n;
@@ -1470,6 +1489,29 @@ void tho_fp4_scores(const uint8_t* q4c, const uint8_t* q4s, const float* q4t, co
   }
   free(k);
   free(q);
+}
+
+/* Test hook: the values and the decisions that may go either way of one
+ * tile row of n <= 64 keys (t and tb in log2 units, mask != 0 for masked
+ * keys) in precision prec (0 MX, 1 NVFP4, 2 MXFP8 tier, 3 FP16) with score
+ * evaluation path epath.  pq[n] receives the values relative to 2^max t;
+ * decision f changes keys [k0[f], k1[f]) by dp[f * 64 + c]; returns the
+ * number of decisions (at most maxf are stored). */
+int tho_p_tile_decisions(const double* t, const double* tb, const int* mask, int n, int prec, int epath,
+                         double* pq, int* k0, int* k1, double* dp, int maxf) {
+  double mt = -INFINITY;
+  for (int c = 0; c < n; ++c)
+    if (!mask[c] && t[c] > mt) mt = t[c];
+  tho_flip* fl = (tho_flip*)malloc(sizeof(tho_flip) * THO_TILE_FLIPS);
+  int nf = prec == THO_PATH_F16 ? tho_quantize_p_tile16(t, tb, mask, n, mt, pq, fl, THO_TILE_FLIPS)
+                                : tho_quantize_p_tile(t, tb, mask, n, prec, epath, mt, pq, fl, THO_TILE_FLIPS);
+  for (int f = 0; f < nf && f < maxf && f < THO_TILE_FLIPS; ++f) {
+    k0[f] = fl[f].k0;
+    k1[f] = fl[f].k1;
+    for (int c = 0; c < 64; ++c) dp[f * 64 + c] = (c >= fl[f].k0 && c < fl[f].k1) ? fl[f].dp[c] : 0.0;
+  }
+  free(fl);
+  return nf;
 }
 
 /* ------------------------------------------------------------------ */

@@ -54,14 +54,14 @@ void tho_attention(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16
                    const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
                    int B, int Hq, int Hkv, int S, int D, int bq, int bk, int causal,
                    double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
-                   double* u);
+                   int32_t* amb_row, double* amb_delta, int amb_cap, int* amb_n);
 void tho_attention_kv(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
                       const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
                       const uint8_t* k4s, const float* k4t, const uint8_t* v4c, const uint8_t* v4s,
                       const float* v4t, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
                       int B, int Hq, int Hkv, int S, int Sk, int D, int bq, int bk, int causal,
                       double sm_scale, const int32_t* work, int nwork, double* o, double* lse,
-                      double* u);
+                      int32_t* amb_row, double* amb_delta, int amb_cap, int* amb_n);
 /* Forward with Attn-QAT's high-precision output O' (ohp [B,Hq,S,D]); Sq = Sk. */
 void tho_attention_hp(const uint16_t* q16, const uint16_t* k16, const uint16_t* v16,
                       const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
@@ -106,10 +106,20 @@ void tho_attention_tiers(const uint16_t* q16, const uint16_t* k16, const uint16_
                          const int32_t* idx, const int32_t* cnt, int kmax, const int32_t* idx2,
                          const int32_t* cnt2, int kmax2, int B, int Hq, int Hkv, int S, int D,
                          int bq, int bk, int causal, double sm_scale, const int32_t* work,
-                         int nwork, double* o, double* lse, double* u);
+                         int nwork, double* o, double* lse, int32_t* amb_row, double* amb_delta,
+                         int amb_cap, int* amb_n);
 void tho_fp4_scores(const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c,
                     const uint8_t* k4s, const float* k4t, int fmt, int S, int D, int r, int c0,
                     int c1, double* out);
+
+/* Relative evaluation-error bound of a tile value (path: 0 MX FP4, 1 NVFP4
+ * FP4, 2 MXFP8 tier, 3 FP16, 4 NVFP4 tensors with MX-style P; b, bmax: the chain sums of the key's and the
+ * tile maximum's scores, dt = t - mt, mt: log2 units). */
+double tho_eval_rel(int path, double b, double bmax, double dt, double mt);
+
+/* Test hook: values and decisions of one tile row (see the source). */
+int tho_p_tile_decisions(const double* t, const double* tb, const int* mask, int n, int prec, int epath,
+                         double* pq, int* k0, int* k1, double* dp, int maxf);
 
 void tho_e2m1_encode_array(const double* x, const double* s, size_t n, uint8_t* out);
 void tho_e4m3_encode_ratio_array(const double* num, const double* den, size_t n, uint8_t* out);

@@ -124,19 +124,21 @@ def decode_fp8(codes_u8, scales_u8, axis, shape):
     return np.swapaxes(vals[..., :S], -1, -2)
 
 
-def quantize_p_tile8(t, mask):
-    """P of a middle-tier (MXFP8) tile restated: v = 2^(t - ceil(max t)),
-    per 32 keys X = mx8_exponent(max v), brute-force E4M3 codes of v / 2^X.
-    Returns (pq, ref): probabilities relative to 2^ref."""
+def quantize_p_tile8(t, mask, eta=None):
+    """P of a middle-tier (MXFP8) tile restated: v = 2^(t - max t) (level 1,
+    the tile maximum), per 32 keys X = mx8_exponent(max v), brute-force E4M3
+    codes of v / 2^X.  eta (optional) multiplies each v before its decisions.
+    Returns (pq, mt): values relative to 2^mt."""
     mt = np.max(np.where(mask, -np.inf, t))
-    z = np.ceil(mt)
-    v = np.where(mask, 0.0, np.exp2(np.where(mask, 0, t) - z))
+    v = np.where(mask, 0.0, np.exp2(np.where(mask, 0, t) - mt))
+    if eta is not None:
+        v = v * eta
     pq = np.zeros(len(t))
     for g0 in range(0, len(t), 32):
         seg = v[g0:g0 + 32]
         s2 = 2.0 ** mx8_exponent(seg.max())
         pq[g0:g0 + 32] = E4M3_POS[nearest_code(seg / s2, E4M3_POS)] * s2
-    return pq, z
+    return pq, mt
 
 
 def valid_blocks(i, S, bq, bk, causal, Sk=None):
@@ -153,47 +155,62 @@ def fp16_round(x):
     return np.asarray(x, np.float64).astype(np.float16).astype(np.float64)
 
 
-def quantize_p_tile(t, mask, fmt):
-    """Two-level P quantisation of one tile row (same reading as the oracle,
-    restated with brute-force rounding).  Returns (pq, ref): probabilities
-    relative to 2^ref."""
+def quantize_p_tile(t, mask, fmt, eta=None):
+    """Two-level P quantisation of one tile row (the oracle's reading of the
+    pages: level 1 the tile maximum, v = 2^(t - max t); level 2 by format),
+    restated with brute-force rounding.  eta (optional) multiplies each v
+    before its decisions.  Returns (pq, mt): values relative to 2^mt."""
     mt = np.max(np.where(mask, -np.inf, t))
     n = len(t)
     pq = np.zeros(n)
+    v = np.where(mask, 0.0, np.exp2(np.where(mask, 0, t) - mt))
+    if eta is not None:
+        v = v * eta
     if fmt == 0:
-        v = np.where(mask, 0.0, 2688.0 * np.exp2(np.where(mask, 0, t) - mt))
-        ref = mt
+        v = 2688.0 * v
         for g0 in range(0, n, 16):
             seg = v[g0:g0 + 16]
             s2 = E4M3_POS[nearest_code(seg.max() / 6.0, E4M3_POS)]
             if s2 > 0:
                 pq[g0:g0 + 16] = E2M1_POS[nearest_code(seg / s2, E2M1_POS)] * s2 / 2688.0
     else:
-        z = np.ceil(mt)
-        v = np.where(mask, 0.0, np.exp2(np.where(mask, 0, t) - z))
-        ref = z
         for g0 in range(0, n, 32):
             seg = v[g0:g0 + 32]
             s2 = 2.0 ** mx_exponent(seg.max())
             pq[g0:g0 + 32] = E2M1_POS[nearest_code(seg / s2, E2M1_POS)] * s2
-    return pq, ref
+    return pq, mt
+
+
+def fp16_tile(t, mask, eta=None):
+    """FP16-path values of one tile row: fp16(2^(t - max t)) (level 1 the tile
+    maximum, as the FP4 path).  Returns (pq, mt)."""
+    mt = np.max(np.where(mask, -np.inf, t))
+    v = np.where(mask, 0.0, np.exp2(np.where(mask, 0, t) - mt))
+    if eta is not None:
+        v = v * eta
+    return np.where(mask, 0.0, fp16_round(v)), mt
 
 
 def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal, sm_scale,
-                       perturb=None, mid=None):
+                       eta_fn=None, mid=None, record=None):
     """Dense two-pass restatement of the forward pass: every score first,
     then one global maximum per row, then the weighted sum.  q4/k4/v4 and
     q16/k16/v16 are fp64 [B,H,S,D] (dequantised FP4 / decoded fp16).
-    perturb(t, a) -> t', if given, moves every score (the rounding decisions
-    of P, the row sum and the NVFP4 level-1 factor alike), as a
-    lower-precision evaluation would; a holds each score's sum of product
-    magnitudes in the same log2 units.  mid = (q8, k8, v8, idx2, cnt2) adds the
-    middle tier: blocks idx2 lists and idx does not use the decoded MXFP8
-    operands and the E4M3 P quantiser (MX format)."""
+    eta_fn(t, b, mask, kind) -> eta, if given, multiplies every tile value
+    before its rounding decisions (only the decisions: level 1 and the row sum
+    stay exact), as a lower-precision evaluation of the decision inputs would;
+    b holds each score's chain sum (chain_sum) in the same log2 units.
+    record (a list), with eta_fn: receives (b, hq, r, change) for every
+    decision the perturbation flipped, change being that decision's effect
+    on the output row (a block scale that flipped counts as one decision
+    over its group, otherwise each element's code or fp16 rounding).
+    mid = (q8, k8, v8, idx2, cnt2) adds the middle tier: blocks idx2 lists and
+    idx does not use the decoded MXFP8 operands and the E4M3 P quantiser (MX
+    format)."""
     B, Hq, S, D = q4.shape
     Hkv, Sk = k4.shape[1], k4.shape[2]
     G = Hq // Hkv
-    nq, nk = -(-S // bq), -(-Sk // bk)
+    nq = -(-S // bq)
     off = Sk - S  # queries are the last S positions
     O = np.zeros((B, Hq, S, D))
     L = np.zeros((B, Hq, S))
@@ -202,18 +219,21 @@ def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal,
             hk = hq // G
             t4 = (q4[b, hq] @ k4[b, hk].T) * sm_scale * LOG2E
             t16 = None if q16 is None else (q16[b, hq] @ k16[b, hk].T) * sm_scale * LOG2E
-            a4 = (np.abs(q4[b, hq]) @ np.abs(k4[b, hk]).T) * sm_scale * LOG2E
-            a16 = None if q16 is None else (np.abs(q16[b, hq]) @ np.abs(k16[b, hk]).T) * sm_scale * LOG2E
+            a4 = a16 = a8 = None
+            if eta_fn is not None:
+                a4 = chain_sum(q4[b, hq], k4[b, hk], 64 if fmt == 1 else 16) * sm_scale * LOG2E
+                a16 = None if q16 is None else chain_sum(q16[b, hq], k16[b, hk], 16) * sm_scale * LOG2E
             if mid is not None:
                 t8 = (mid[0][b, hq] @ mid[1][b, hk].T) * sm_scale * LOG2E
-                a8 = (np.abs(mid[0][b, hq]) @ np.abs(mid[1][b, hk]).T) * sm_scale * LOG2E
+                if eta_fn is not None:
+                    a8 = chain_sum(mid[0][b, hq], mid[1][b, hk], 16) * sm_scale * LOG2E
             for i in range(nq):
                 promoted = set(int(j) for j in idx[b, hq, i, : cnt[b, hq, i]])
                 tier8 = set() if mid is None else set(int(j) for j in mid[3][b, hq, i, : mid[4][b, hq, i]])
                 tier8 -= promoted
                 nval = valid_blocks(i, S, bq, bk, causal, Sk)
                 for r in range(i * bq, min(S, (i + 1) * bq)):
-                    tiles = []  # (t row, mask, is16, c0)
+                    tiles = []  # (t row, mask, kind, c0, c1, a row)
                     for j in range(nval):
                         c0, c1 = j * bk, min(Sk, (j + 1) * bk)
                         keys = np.arange(c0, c1)
@@ -222,27 +242,48 @@ def two_pass_attention(q4, k4, v4, q16, k16, v16, idx, cnt, fmt, bq, bk, causal,
                             continue
                         kind = 16 if j in promoted else (8 if j in tier8 else 4)
                         src, asrc = {16: (t16, a16), 8: (t8, a8) if mid is not None else None, 4: (t4, a4)}[kind]
-                        tiles.append((src[r, c0:c1], mask, kind, c0, c1, asrc[r, c0:c1]))
+                        tiles.append((src[r, c0:c1], mask, kind, c0, c1, None if asrc is None else asrc[r, c0:c1]))
                     M = max(np.max(np.where(m, -np.inf, t)) for t, m, _, _, _, _ in tiles)
                     l = 0.0
                     acc = np.zeros(D)
+                    changes = []
                     for t, m, kind, c0, c1, a in tiles:
-                        tq = t if perturb is None else np.where(m, t, perturb(t, a))
-                        e = np.where(m, 0.0, np.exp2(np.where(m, 0, tq) - M))
-                        l += e.sum()
-                        if kind == 8:
-                            pq, ref = quantize_p_tile8(tq, m)
-                            acc += (pq * np.exp2(ref - M)) @ mid[2][b, hk, c0:c1]
-                        elif kind == 16:
-                            z = np.ceil(M)
-                            p = np.where(m, 0.0, fp16_round(np.exp2(np.where(m, 0, tq) - z))) * np.exp2(z - M)
-                            acc += p @ v16[b, hk, c0:c1]
-                        else:
-                            pq, ref = quantize_p_tile(tq, m, fmt)
-                            acc += (pq * np.exp2(ref - M)) @ v4[b, hk, c0:c1]
+                        eta = None if eta_fn is None else eta_fn(t, a, m, kind)
+                        l += np.where(m, 0.0, np.exp2(np.where(m, 0, t) - M)).sum()
+                        vt = {8: mid[2] if mid is not None else None, 16: v16, 4: v4}[kind][b, hk, c0:c1]
+                        quant = {8: quantize_p_tile8, 16: fp16_tile,
+                                 4: lambda t_, m_, e_: quantize_p_tile(t_, m_, fmt, e_)}[kind]
+                        pq, mt = quant(t, m, eta)
+                        acc += (pq * np.exp2(mt - M)) @ vt
+                        if record is not None and eta is not None:
+                            p0, _ = quant(t, m, None)
+                            gs = 1 if kind == 16 else (16 if (kind == 4 and fmt == 0) else 32)
+                            for g0 in range(0, len(t), gs):
+                                diff = (pq - p0)[g0:g0 + gs]
+                                idxs = np.nonzero(diff)[0]
+                                if len(idxs) == 0:
+                                    continue
+                                changes.append((diff * np.exp2(mt - M)) @ vt[g0:g0 + gs])
                     O[b, hq, r] = acc / l
                     L[b, hq, r] = M * LN2 + np.log(l)
+                    for ch in changes:
+                        record.append((b, hq, r, ch / l))
     return O, L
+
+
+def chain_sum(q, k, width):
+    """Per (query, key) score the chain sum of the evaluation-error model: over
+    the contraction's slices of `width` channels in ascending order, the
+    magnitude of the exact partial sum before the slice plus the slice's sum
+    of |products|."""
+    D = q.shape[-1]
+    b = np.zeros((q.shape[0], k.shape[0]))
+    part = np.zeros_like(b)
+    for d0 in range(0, D, width):
+        sl = slice(d0, min(D, d0 + width))
+        b += np.abs(part) + np.abs(q[:, sl]) @ np.abs(k[:, sl]).T
+        part += q[:, sl] @ k[:, sl].T
+    return b
 
 
 def exact_attention(q, k, v, causal, sm_scale):

@@ -61,7 +61,7 @@ def _run(oracle, w, bp, fmt=1):
     same_fp4(k4, r["k4"])
     same_fp4(v4, r["v4"])
     compare_out(o.cpu().numpy().astype(np.float64), r["o"], lse.cpu().numpy().astype(np.float64),
-                r["lse"], r["u"])
+                r["lse"], r["amb"])
     return o, r
 
 

@@ -107,7 +107,7 @@ def test_tiered_parity(oracle, name):
         same_fp4(g[gn], r[rn])
     for n in ("q8", "k8", "v8"):
         _same_fp8(g[n], r[n])
-    compare_out(g["o"], r["o"], g["lse"], r["lse"], r["u"])
+    compare_out(g["o"], r["o"], g["lse"], r["lse"], r["amb"])
 
 
 def test_tiered_without_fp8_blocks_is_two_tier():
@@ -140,7 +140,7 @@ def test_tiered_long_fullsize(oracle):
     pb, ph, pi = d["planted"][0][:3]
     work = sorted({(0, 0, 0), (0, w.Hq - 1, nq - 1), (0, 5, nq // 2), (0, 6, nq // 2), (pb, ph, pi)})
     note(f"    sampled query blocks (b, hq, i): {work}")
-    o, lse, u = oracle.attention_tiers(d["q"], d["k"], d["v"], q4, k4, v4, q8, k8, v8, idx, cnt, idx2, cnt2,
-                                       w.bq, w.bk, w.causal, work=work, with_u=True)
+    o, lse, amb = oracle.attention_tiers(d["q"], d["k"], d["v"], q4, k4, v4, q8, k8, v8, idx, cnt, idx2, cnt2,
+                                       w.bq, w.bk, w.causal, work=work, with_amb=True)
     rows = [(b, h, slice(i * w.bq, min(w.S, (i + 1) * w.bq))) for b, h, i in work]
-    compare_out(g["o"], o, g["lse"], lse, u, rows=rows)
+    compare_out(g["o"], o, g["lse"], lse, amb, rows=rows)

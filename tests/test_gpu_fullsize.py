@@ -92,7 +92,7 @@ def test_fullsize_parity(oracle, name):
     nq = idx.shape[2]
     work = _work_items(w, d, nq, seed=len(name))
     note(f"    sampled query blocks (b, hq, i): {work}")
-    o, lse, u = oracle.attention(d["q"], d["k"], d["v"], q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal,
-                                 work=work, with_u=True)
+    o, lse, amb = oracle.attention(d["q"], d["k"], d["v"], q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal,
+                                 work=work, with_amb=True)
     rows = [(b, h, slice(i * w.bq, min(w.S, (i + 1) * w.bq))) for b, h, i in work]
-    compare_out(g["o"], o, g["lse"], lse, u, rows=rows)
+    compare_out(g["o"], o, g["lse"], lse, amb, rows=rows)

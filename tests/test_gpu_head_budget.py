@@ -84,8 +84,8 @@ def test_head_budget_forward(oracle):
     ridx, rcnt = oracle.select_head(q, k, 128, 64, True, -1, 500)
     q4, k4 = oracle.quantize(q, oracle.AXIS_D, oracle.MX), oracle.quantize(k, oracle.AXIS_D, oracle.MX)
     v4 = oracle.quantize(v, oracle.AXIS_S, oracle.MX)
-    ro, rl, u = oracle.attention(q, k, v, q4, k4, v4, ridx, rcnt, 128, 64, True, with_u=True)
-    compare_out(o.cpu().numpy().astype(np.float64), ro, lse.cpu().numpy().astype(np.float64), rl, u)
+    ro, rl, amb = oracle.attention(q, k, v, q4, k4, v4, ridx, rcnt, 128, 64, True, with_amb=True)
+    compare_out(o.cpu().numpy().astype(np.float64), ro, lse.cpu().numpy().astype(np.float64), rl, amb)
 
 
 @pytest.mark.slow

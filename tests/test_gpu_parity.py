@@ -53,7 +53,7 @@ def test_parity(oracle, name):
     same_fp4(g["q4"], r["q4"])
     same_fp4(g["k4"], r["k4"])
     same_fp4(g["v4"], r["v4"])
-    compare_out(g["o"], r["o"], g["lse"], r["lse"], r["u"])
+    compare_out(g["o"], r["o"], g["lse"], r["lse"], r["amb"])
 
 
 VARIANT_CASES = {
@@ -75,7 +75,7 @@ def test_parity_nvfp4_tensors_mx_p(oracle, name):
     assert np.array_equal(g["cnt"], r["cnt"])
     same_fp4(g["q4"], r["q4"])
     same_fp4(g["v4"], r["v4"])
-    compare_out(g["o"], r["o"], g["lse"], r["lse"], r["u"])
+    compare_out(g["o"], r["o"], g["lse"], r["lse"], r["amb"])
 
 
 def test_determinism():
