@@ -30,11 +30,12 @@
 //    the FP16 MFMA v_mfma_f32_32x32x16_f16; the per-slice fp32 scales fold
 //    into the softmax multiplier (Q, K) and into the accumulator (V).
 //  * FP16 path: fp16 MFMA over the promoted tiles after all FP4 tiles.
-//  * Online softmax with a lazy, integer running offset m (log2 units): the
-//    accumulator is rescaled only when a tile's maximum exceeds m by more
-//    than kTau, always by an exact power of two.  P codes do not depend on m
-//    (MX: E8M0 scales absorb powers of two; NVFP4: level 1 normalises by the
-//    tile maximum), so this is the pages' online softmax up to fp32 rounding.
+//  * Two-level P (the pages take it from SageAttention3): level 1 of every
+//    tile is the tile's own maximum, so each tile's probabilities are
+//    2^(t - mt) with the largest exactly 1, quantised in the tile's
+//    precision (level 2); the accumulator and row sum follow each tile's
+//    level-1 unit (one rescale per tile), so the online softmax merges tiles
+//    whose values do not depend on the running maximum or the order.
 //  * K/V tiles stream through double-buffered LDS, one barrier per tile; the
 //    next tile's global loads are in flight while the current one computes.
 #include <type_traits>
@@ -44,8 +45,8 @@
 namespace thrift {
 
 constexpr float kLn2 = 0.69314718055994530942f;
-constexpr float kTau = 8.0f;        // lazy-rescale threshold, log2 units
-constexpr float kMInit = -1.0e30f;  // running offset before the first key
+constexpr float kMInit = -1.0e30f;  // unit and running maximum before the first key
+constexpr float kDead = 60.0f;      // tiles this far (log2) below the running maximum add nothing
 constexpr int kBk = 64;             // key block
 
 struct AttnArgs {
@@ -159,30 +160,45 @@ __device__ inline int key_of(int mt, int i, int hi) { return hi * 32 + mt * 16 +
 
 // ---- online-softmax state ------------------------------------------------------
 
+// acc and l are held in units of 2^lu.  lu is the level-1 exponent of the
+// latest tile (its maximum in log2 units, plus the log2 of any factor its
+// values carry, see tile_unit); mrun is the running maximum of the tiles'
+// maxima.  Both lanes of a query (halves hi = 0, 1 of its keys and of its
+// output channels) hold the same lu and mrun.
 template <int D>
 struct RowState {
   v16f acc[D / 32];  // O^T for this lane's query: d = dt*32 + (i/4)*8 + hi*4 + i%4
-  float m;           // running integer offset (log2 units)
+  float lu;          // log2 of the unit of acc and l
+  float mrun;        // running maximum of the tiles' maxima (log2 units)
   float l;           // this lane's half of the running sum
-  float g;           // acc holds O^T / g (NVFP4 FP4 path; 1 elsewhere)
 };
 
-// Lazy rescale: if the tile maximum (log2 units) of a query exceeds m +
-// kTau, move m to its ceiling and rescale by the exact power of two.  own is
-// this lane's half of the tile maximum (raw score units, c > 0); both lanes
-// of the query decide on the pair's maximum, so they keep the same m.
 template <int D>
-__device__ inline void maybe_rescale(RowState<D>& st, float own, float c) {
-  if (__builtin_amdgcn_ballot_w64(own * c > st.m + kTau)) {
-    const float tml2 = pair_max(own) * c;
-    const bool need = tml2 > st.m + kTau;
-    const float mn = need ? ceilf(tml2) : st.m;
-    const float f = need ? exp2f(st.m - mn) : 1.0f;  // integer difference: exact
+__device__ inline void init_state(RowState<D>& st) {
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] *= f;
-    st.l *= f;
-    st.m = mn;
-  }
+  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] = v16f{};
+  st.lu = kMInit;
+  st.mrun = kMInit;
+  st.l = 0.0f;
+}
+
+// Level 1 of a tile whose maximum is mtc (log2 units): acc and l move to the
+// unit 2^(mtc + lk), lk the log2 of the factor the tile's quantised values
+// carry beyond 2^mtc (NVFP4 tensors: V's slice scale, and 1/2688 on the FP4
+// path; 0 elsewhere).  A tile more than kDead below the running maximum adds
+// nothing (it is below the row sum's fp32 resolution); the return value says
+// whether the tile contributes.
+template <int D>
+__device__ inline bool tile_unit(RowState<D>& st, float mtc, float lk) {
+  const bool live = mtc > st.mrun - kDead;
+  const float nu = mtc + lk;
+  const float r = live ? exp2_fast(st.lu - nu) : 1.0f;
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] *= r;
+  st.l *= r;
+  st.lu = live ? nu : st.lu;
+  st.mrun = fmaxf(st.mrun, mtc);
+  return live;
 }
 
 // Causal / tail mask: keys past the query row or past S become -inf.
@@ -265,12 +281,14 @@ __device__ inline void softmax_pv_mx(RowState<D>& st, v16f s[2], const MxVOps<D>
   const int hi = lane >> 5;
   if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
 
-  // this lane's 32 keys are one P group: its maximum sets the E8M0 exponent
+  // this lane's 32 keys are one P group (level 2); level 1 is the query's
+  // tile maximum over both lane halves
   const float gmax = fmaxf(max16(s[0]), max16(s[1]));
-  maybe_rescale<D>(st, gmax, c);
-  const float nm = -st.m;
+  const float tmax = pair_max(gmax);
+  const float mtc = tmax * c;
+  const float nm = tile_unit<D>(st, mtc, 0.0f) ? -mtc : -INFINITY;  // dead tile: every p = 0
 
-  // probabilities relative to 2^m, unquantised row sum
+  // probabilities relative to the tile maximum, unquantised row sum
   float lsum = 0.0f;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -282,9 +300,10 @@ __device__ inline void softmax_pv_mx(RowState<D>& st, v16f s[2], const MxVOps<D>
     }
   st.l += lsum;
 
-  // E8M0 exponent floor(log2(max p)) - 2 from the exponent field of the
-  // group maximum's probability (computed like the elements' own)
-  const uint32_t E = (__float_as_uint(exp2_fast(__builtin_fmaf(gmax, c, nm))) >> 23) & 0xFF;
+  // E8M0 exponent floor(log2(max p)) - 2: -2 for the group holding the tile
+  // maximum (its p is 1 up to the rounding of mtc), else from the exponent
+  // field of the group maximum's probability, computed like the elements'
+  const uint32_t E = gmax == tmax ? 127u : (__float_as_uint(exp2_fast(__builtin_fmaf(gmax, c, nm))) >> 23) & 0xFF;
   const uint32_t psc = E > 3 ? E - 2 : 1;
   const float sf = __uint_as_float(psc << 23);
 
@@ -350,8 +369,9 @@ __device__ inline void fp16_softmax_pv(RowState<D>& st, v16f s[2], const _Float1
                                        int qrow, int S, int causal, bool need_mask, int lane) {
   const int hi = lane >> 5;
   if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
-  maybe_rescale<D>(st, fmaxf(max16(s[0]), max16(s[1])), c);
-  const float nm = -st.m;
+  // probabilities relative to the tile maximum (level 1), rounded to fp16
+  const float mtc = pair_max(fmaxf(max16(s[0]), max16(s[1]))) * c;
+  const float nm = tile_unit<D>(st, mtc, 0.0f) ? -mtc : -INFINITY;
   float lsum = 0.0f;
   v8h pB[4];
 #pragma unroll
@@ -376,20 +396,22 @@ __device__ inline void fp16_tile(RowState<D>& st, const char* stage, const v8h* 
 }
 
 // NVFP4 FP4 tile: scores from the dequantised fp16 stage, P quantised in two
-// levels (level 1 per row and tile: v = 2688 p / p_max; level 2 per 16 keys:
-// E4M3 scale s2, E2M1 codes of v / s2).  The product with V uses code * s2,
-// which fp16 holds exactly, so the per-row level-1 factor p_max / 2688 (and
-// V's per-slice scale) is carried in the accumulator scale g instead of being
-// rounded into P: acc becomes acc * g / f before the tile and g becomes f.
+// levels (level 1 per row and tile: v = 2688 p / p_max, p_max the tile
+// maximum's probability, so the maximum lands on 6 * 448; level 2 per 16
+// keys: E4M3 scale s2, E2M1 codes of v / s2).  The product with V uses
+// code * s2, which fp16 holds exactly; the factor p_max / 2688 and V's slice
+// scale are the tile's unit (lk = log2(sv / 2688)), so P is never rounded
+// beyond the method.  ilk = 2688 / sv brings the row sum to that unit.
 template <int D>
-__device__ inline void fp4_nv_softmax_pv(RowState<D>& st, v16f s[2], const char* stage, float c, float sv,
-                                         int key0, int qrow, int S, int causal, bool need_mask, int lane) {
+__device__ inline void fp4_nv_softmax_pv(RowState<D>& st, v16f s[2], const char* stage, float c, float lk,
+                                         float ilk, int key0, int qrow, int S, int causal, bool need_mask,
+                                         int lane) {
   const int hi = lane >> 5;
   if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
   const float gm0 = max16(s[0]), gm1 = max16(s[1]);  // this lane's two 16-key groups
-  maybe_rescale<D>(st, fmaxf(gm0, gm1), c);
-  const float tm = pair_max(fmaxf(gm0, gm1));  // the query's tile maximum (level 1)
-  const float nm = -st.m;
+  const float tmax = pair_max(fmaxf(gm0, gm1));      // the query's tile maximum (level 1)
+  const float mtc = tmax * c;
+  const float nm = tile_unit<D>(st, mtc, lk) ? -mtc : -INFINITY;
   float lsum = 0.0f;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -399,27 +421,21 @@ __device__ inline void fp4_nv_softmax_pv(RowState<D>& st, v16f s[2], const char*
       s[mt][i] = p;
       lsum += p;
     }
-  st.l += lsum;
-  const float em = exp2_fast(__builtin_fmaf(tm, c, nm));  // probability of the tile maximum
-  // a tile more than 2^60 below the running maximum contributes nothing
-  const bool live = em > 0x1p-60f;
-  const float r = live ? 2688.0f / em : 0.0f;  // level 1: maximum -> 6 * 448
-  const float f = live ? em * (sv * (1.0f / 2688.0f)) : st.g;
-  const float ratio = st.g / f;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] *= ratio;
-  st.g = f;
+  st.l += lsum * ilk;
   v8h pB[4];
 #pragma unroll
   for (int g = 0; g < 2; ++g) {  // group g = keys hi*32 + 16g .. +15 = registers of tile g
     const v16f& v = s[g];
-    const float gm = exp2_fast(__builtin_fmaf(g ? gm1 : gm0, c, nm)) * r;
-    // level 2: E4M3 block scale (the conversion does not saturate: clamp)
+    const float gmg = g ? gm1 : gm0;
+    // level 2: E4M3 block scale of the group's largest value / 6 (the group
+    // holding the tile maximum: 2688 / 6 = 448); the conversion does not
+    // saturate: clamp
+    const float gv = gmg == tmax ? 2688.0f : 2688.0f * exp2_fast(__builtin_fmaf(gmg, c, nm));
     v2s_t sb = {0, 0};
-    sb = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(sb, fminf(gm * (1.0f / 6.0f), 448.0f), 0.0f, 1.0f, false);
+    sb = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(sb, fminf(gv * (1.0f / 6.0f), 448.0f), 0.0f, 1.0f, false);
     const float s2 = e4m3_to_float((uint32_t)sb[0] & 0xFF);
-    const float k = s2 > 0.0f ? r / s2 : 0.0f;
-    const _Float16 s2h = (_Float16)(live ? s2 : 0.0f);  // exact: E4M3 has 4 significant bits
+    const float k = s2 > 0.0f ? 2688.0f / s2 : 0.0f;
+    const _Float16 s2h = (_Float16)s2;  // exact: E4M3 has 4 significant bits
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // 8 keys per P^T operand
       const int o = h * 8;
@@ -437,20 +453,21 @@ __device__ inline void fp4_nv_softmax_pv(RowState<D>& st, v16f s[2], const char*
 }
 
 // The variant's FP4 tile: NVFP4 Q, K, V (dequantised to fp16 in the stage),
-// P quantised MX-style: level 1 the integer running offset m (lazy rescale),
-// level 2 an E8M0 scale per 32 keys (this lane's keys are one group), codes
-// back to fp16 (code * 2^X, exact down to fp16's subnormal range) for the
-// fp16 PV product.  V's slice scale is applied once at the end (st.g).
+// P quantised MX-style: level 1 the tile maximum, level 2 an E8M0 scale per
+// 32 keys (this lane's keys are one group), codes back to fp16 (code * 2^X,
+// exact down to fp16's subnormal range) for the fp16 PV product.  V's slice
+// scale is part of the tile's unit (lk = log2 sv, ilk = 1 / sv).
 template <int D>
-__device__ inline void fp4_nvmxp_tile(RowState<D>& st, const char* stage, const v8h* qh, float c, int key0,
-                                      int qrow, int S, int causal, bool need_mask, int lane) {
+__device__ inline void fp4_nvmxp_tile(RowState<D>& st, const char* stage, const v8h* qh, float c, float lk,
+                                      float ilk, int key0, int qrow, int S, int causal, bool need_mask, int lane) {
   const int hi = lane >> 5;
   v16f s[2];
   qk_f16<D>(s, stage, qh, lane);
   if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
   const float gmax = fmaxf(max16(s[0]), max16(s[1]));
-  maybe_rescale<D>(st, gmax, c);
-  const float nm = -st.m;
+  const float tmax = pair_max(gmax);
+  const float mtc = tmax * c;
+  const float nm = tile_unit<D>(st, mtc, lk) ? -mtc : -INFINITY;
   float lsum = 0.0f;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -460,9 +477,9 @@ __device__ inline void fp4_nvmxp_tile(RowState<D>& st, const char* stage, const 
       s[mt][i] = p;
       lsum += p;
     }
-  st.l += lsum;
+  st.l += lsum * ilk;
   // E8M0 exponent floor(log2(max p)) - 2, as on the MX path
-  const uint32_t E = (__float_as_uint(exp2_fast(__builtin_fmaf(gmax, c, nm))) >> 23) & 0xFF;
+  const uint32_t E = gmax == tmax ? 127u : (__float_as_uint(exp2_fast(__builtin_fmaf(gmax, c, nm))) >> 23) & 0xFF;
   const uint32_t psc = E > 3 ? E - 2 : 1;
   const float sf = __uint_as_float(psc << 23);
   v8h pB[4];
@@ -485,12 +502,11 @@ __device__ inline void fp4_nvmxp_tile(RowState<D>& st, const char* stage, const 
 }
 
 template <int D>
-__device__ inline void fp4_nv_tile(RowState<D>& st, const char* stage, const v8h* qh, float c,
-                                   float sv, int key0, int qrow, int S, int causal, bool need_mask,
-                                   int lane) {
+__device__ inline void fp4_nv_tile(RowState<D>& st, const char* stage, const v8h* qh, float c, float lk,
+                                   float ilk, int key0, int qrow, int S, int causal, bool need_mask, int lane) {
   v16f s[2];
   qk_f16<D>(s, stage, qh, lane);
-  fp4_nv_softmax_pv<D>(st, s, stage, c, sv, key0, qrow, S, causal, need_mask, lane);
+  fp4_nv_softmax_pv<D>(st, s, stage, c, lk, ilk, key0, qrow, S, causal, need_mask, lane);
 }
 
 }  // namespace thrift
@@ -542,8 +558,9 @@ __device__ inline void fp8_tile(RowState<D>& st, const char* stage, const v8h* q
   qk_f16<D>(s, stage, qh, lane);
   if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
   const float gmax = fmaxf(max16(s[0]), max16(s[1]));
-  maybe_rescale<D>(st, gmax, c);
-  const float nm = -st.m;
+  const float tmax = pair_max(gmax);  // level 1: the tile maximum
+  const float mtc = tmax * c;
+  const float nm = tile_unit<D>(st, mtc, 0.0f) ? -mtc : -INFINITY;
   float lsum = 0.0f;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -554,7 +571,8 @@ __device__ inline void fp8_tile(RowState<D>& st, const char* stage, const v8h* q
       lsum += p;
     }
   st.l += lsum;
-  const uint32_t E = (__float_as_uint(exp2_fast(__builtin_fmaf(gmax, c, nm))) >> 23) & 0xFF;
+  // E8M0 exponent floor(log2(max p)) - 8 (-8 for the tile maximum's group)
+  const uint32_t E = gmax == tmax ? 127u : (__float_as_uint(exp2_fast(__builtin_fmaf(gmax, c, nm))) >> 23) & 0xFF;
   const uint32_t psc = E > 9 ? E - 8 : 1;
   const float sf = __uint_as_float(psc << 23);
   const float cap = 448.0f * sf;
@@ -958,11 +976,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
   __syncthreads();
 
   RowState<D> st;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] = v16f{};
-  st.m = kMInit;
-  st.l = 0.0f;
-  st.g = 1.0f;
+  init_state<D>(st);
 
   // ---------------- FP4 path: every valid key block not promoted ----------------
   int pj = 0;
@@ -1079,8 +1093,10 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
         }
       }
       const float c = a.sm_log2 * a.q4t[bhq] * a.k4t[bhk];
+      // the tiles' unit carries V's slice scale (and NVFP4's 1/2688 of level 1)
       const float sv = a.v4t[bhk];
-      if constexpr (FMT == THRIFT_NVFP4_MXP) st.g = sv;  // acc holds O^T / sv
+      const float lk = FMT == THRIFT_NVFP4 ? log2f(sv) - log2f(2688.0f) : log2f(sv);
+      const float ilk = FMT == THRIFT_NVFP4 ? 2688.0f / sv : 1.0f / sv;
       Nv4Stager<D, NT> stg;
       if (jc < nvalid) {
         stg.load(a, bhk, jc, t);
@@ -1096,19 +1112,16 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
         const bool need_mask = (a.causal && key0 + kBk - 1 > q0) || key0 + kBk > S;
         if (active) {
           if constexpr (FMT == THRIFT_NVFP4)
-            fp4_nv_tile<D>(st, smem + buf * L::STAGE, qh, c, sv, key0, qrow, S, a.causal, need_mask, lane);
+            fp4_nv_tile<D>(st, smem + buf * L::STAGE, qh, c, lk, ilk, key0, qrow, S, a.causal, need_mask, lane);
           else
-            fp4_nvmxp_tile<D>(st, smem + buf * L::STAGE, qh, c, key0, qrow, S, a.causal, need_mask, lane);
+            fp4_nvmxp_tile<D>(st, smem + buf * L::STAGE, qh, c, lk, ilk, key0, qrow, S, a.causal, need_mask,
+                              lane);
         }
         if (jn < nvalid) stg.store(smem + (buf ^ 1) * L::STAGE, t);
         __syncthreads();
         buf ^= 1;
         jc = jn;
       }
-      // back to plain units: acc holds O^T / g
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] *= st.g;
-      st.g = 1.0f;
     }
   }
 
@@ -1207,7 +1220,7 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
           *(v4h*)((_Float16*)a.o + obase + d0) = v4h{(_Float16)x0, (_Float16)x1, (_Float16)x2, (_Float16)x3};
         }
       }
-    if (a.lse && hi == 0) a.lse[(size_t)bhq * S + qrow] = (st.m + log2f(lt)) * kLn2;
+    if (a.lse && hi == 0) a.lse[(size_t)bhq * S + qrow] = (st.lu + log2f(lt)) * kLn2;
   }
 }
 
@@ -1270,7 +1283,7 @@ __device__ inline void store_partial(float* dst, const RowState<D>& st, int lane
     }
   const float lt = st.l + xlane32(st.l);
   if (hi == 0) {
-    dst[D] = st.m;
+    dst[D] = st.lu;
     dst[D + 1] = lt;
   }
 }
@@ -1318,11 +1331,7 @@ __device__ inline void decode_fp4_body(const DecodeArgs& d, int unit, char* smem
   qsc >>= 8 * hi;
 
   RowState<D> st;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] = v16f{};
-  st.m = kMInit;
-  st.l = 0.0f;
-  st.g = 1.0f;
+  init_state<D>(st);
 
   // Two ring halves of four blocks (two MX stages each); wave w computes
   // block j0 + w of every super-stage.
@@ -1434,13 +1443,10 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void decode_nv4_kernel(DecodeArg
   }
   const float c = a.sm_log2 * a.q4t[(size_t)b * a.Hq + hq] * a.k4t[bhk];
   const float sv = a.v4t[bhk];
+  const float lk = log2f(sv) - log2f(2688.0f), ilk = 2688.0f / sv;  // the FP4 tiles' unit factor
 
   RowState<D> st;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] = v16f{};
-  st.m = kMInit;
-  st.l = 0.0f;
-  st.g = 1.0f;
+  init_state<D>(st);
 
   const int nss = je > jb ? cdiv(je - jb, kDecWaves) : 0;
   Nv4Stager<D, 64> stg;
@@ -1466,15 +1472,12 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void decode_nv4_kernel(DecodeArg
         for (int i = 0; i < 16; ++i) sc[mt][i] = fminf(sc[mt][i], lim);
       const int key0 = j * kBk;
       const bool need_mask = (a.causal && key0 + kBk - 1 > Sk - Sq) || key0 + kBk > Sk;
-      fp4_nv_softmax_pv<D>(st, sc, stage, c, sv, key0, qpos, Sk, a.causal, need_mask, lane);
+      fp4_nv_softmax_pv<D>(st, sc, stage, c, lk, ilk, key0, qpos, Sk, a.causal, need_mask, lane);
     }
     __syncthreads();
     if (next) stg.store(stage, lane);
     __syncthreads();
   }
-  // back to plain units: acc holds O^T / g
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] *= st.g;
   if (col_ok) {
     const size_t u4 = (bhk * d.nsplit + sidx) * kDecWaves + w;
     store_partial<D>(d.part4 + (u4 * ncol + col) * kPartStride<D>, st, lane);
@@ -1501,11 +1504,7 @@ __device__ inline void decode_f16_body(const DecodeArgs& d, int unit, char* vt_s
   const bool act = j >= 0 && j < d.nvalid;
 
   RowState<D> st;
-#pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) st.acc[dt] = v16f{};
-  st.m = kMInit;
-  st.l = 0.0f;
-  st.g = 1.0f;
+  init_state<D>(st);
   using L = Lds<D>;
   _Float16* vt = (_Float16*)vt_smem;  // V^T: D rows of VROWH halves
   v8h qh[D / 16], ka[2][D / 16];
@@ -1628,7 +1627,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeArgs 
     const float* q = part(u);
     const float2 ml = *(const float2*)(q + D);
     const float4 x = *(const float4*)(q + 4 * c4);
-    const float f = exp2f(ml.x - M);  // partial offsets are integers: exact powers of two
+    const float f = exp2f(ml.x - M);  // the partial's unit relative to the largest
     l += f * ml.y;
     acc.x += f * x.x;
     acc.y += f * x.y;

@@ -551,38 +551,34 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
       gm0 = pair_max(gm0);
       gm1 = pair_max(gm1);
       Lq = ((const float*)(smem + L::L2))[qperm(r32)];
-      if constexpr (FMT == THRIFT_MXFP4) {
-        // MX level 1 is any power of two (the E8M0 block scale absorbs it):
-        // z = ceil(L2); block exponent from the group maximum's probability
-        const float gm = fmaxf(gm0, gm1);
-        const float z = ceilf(Lq);
-        const uint32_t E = (__float_as_uint(exp2_fast(__builtin_fmaf(gm, cj, -z))) >> 23) & 0xFF;
-        const int X = (int)(E > 3 ? E - 2 : 1) - 127;
-        const float zx = z + (float)X;
-        const bool any = gm > -INFINITY;
-        if (hi == 0) {
-          ((float*)wa)[qperm(r32)] = any ? exp2_fast(Lq - zx) : 0.0f;
-          ((float*)wh)[qperm(r32)] = any ? exp2_fast(zx - Lq) : 0.0f;
-        }
-        // the wave reads back its own slot: its LDS operations complete in order
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-      } else {
-        if (hi == 0) ((float*)(smem + L::HT))[w * 32 + qperm(r32)] = fmaxf(gm0, gm1);
-      }
+      if (hi == 0) ((float*)(smem + L::HT))[w * 32 + qperm(r32)] = fmaxf(gm0, gm1);
     }
-    if constexpr (FMT == THRIFT_NVFP4) {
-      // level 1 of NVFP4 is the query's maximum over the whole 64-key tile:
-      // the two waves of the block exchange their halves (every wave passes
-      // this barrier on every step)
-      __syncthreads();
-      if (!f16) {
-        const float tm = fmaxf(fmaxf(gm0, gm1), ((const float*)(smem + L::HT))[(w ^ 1) * 32 + qperm(r32)]);
-        const float tml = tm * cj;
-        // a tile more than 2^60 below the row's total contributes nothing
-        const bool live = tm > -INFINITY && tml - Lq > -60.0f;
+    // level 1 is the query's maximum over the whole 64-key tile: the two
+    // waves of the block exchange their halves (every wave passes this
+    // barrier on every step)
+    __syncthreads();
+    if (!f16) {
+      const float tm = fmaxf(fmaxf(gm0, gm1), ((const float*)(smem + L::HT))[(w ^ 1) * 32 + qperm(r32)]);
+      const float tml = tm * cj;
+      // a tile more than 2^60 below the row's total contributes nothing
+      const bool live = tm > -INFINITY && tml - Lq > -60.0f;
+      if constexpr (FMT == THRIFT_MXFP4) {
+        // level 2: this wave's 32 keys are one group; E8M0 exponent
+        // floor(log2(max p)) - 2 relative to the tile maximum (-2 for the
+        // group holding it)
+        const float gm = fmaxf(gm0, gm1);
+        const uint32_t E = gm == tm ? 127u : (__float_as_uint(exp2_fast(__builtin_fmaf(gm, cj, -tml))) >> 23) & 0xFF;
+        const float X = (float)((int)(E > 3 ? E - 2 : 1) - 127);
+        const bool on = live && gm > -INFINITY;
+        if (hi == 0) {
+          ((float*)wa)[qperm(r32)] = on ? exp2_fast(Lq - tml - X) : 0.0f;
+          ((float*)wh)[qperm(r32)] = on ? exp2_fast(X + tml - Lq) : 0.0f;
+        }
+      } else {
 #pragma unroll
         for (int g = 0; g < 2; ++g) {
-          const float gv = 2688.0f * exp2_fast(__builtin_fmaf(g ? gm1 : gm0, cj, -tml));
+          const float gmg = g ? gm1 : gm0;
+          const float gv = gmg == tm ? 2688.0f : 2688.0f * exp2_fast(__builtin_fmaf(gmg, cj, -tml));
           v2s_t sb = {0, 0};
           sb = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(sb, fminf(gv * (1.0f / 6.0f), 448.0f), 0.0f, 1.0f, false);
           const float s2 = e4m3_to_float((uint32_t)sb[0] & 0xFF);
@@ -594,8 +590,9 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
             fh[qperm(r32)] = on ? s2 * exp2_fast(tml - Lq) * (1.0f / 2688.0f) : 0.0f;
           }
         }
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
+      // the wave reads back its own slot: its LDS operations complete in order
+      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     }
     // A operands of the two products: step st holds queries hi*16 + 8 st + u;
     // this lane's queries are q0 + hi*16 + ii, four at a time
