@@ -17,6 +17,7 @@ EXPORTS = ("thrift_select_kmax", "thrift_select_workspace_bytes", "thrift_select
            "thrift_quantize_workspace_bytes", "thrift_quantize_fp4", "thrift_quantize_fp4_range", "thrift_cache_update",
            "thrift_attention_fwd", "thrift_quantize_fp8", "thrift_attention_fwd_tiered",
            "thrift_attention_decode_workspace_bytes", "thrift_attention_decode",
+           "thrift_attention_decode_noalloc",
            "thrift_attention_bwd_workspace_bytes", "thrift_attention_fwd_hp", "thrift_attention_bwd",
            "thrift_status_string")
 
@@ -75,6 +76,8 @@ def load():
         L.thrift_attention_decode_workspace_bytes.argtypes = [I] * 7
         L.thrift_attention_decode.restype = I
         L.thrift_attention_decode.argtypes = [P] * 12 + [I, P, P] + [I] * 9 + [F, P, I, P, P, SZ, P]
+        L.thrift_attention_decode_noalloc.restype = I
+        L.thrift_attention_decode_noalloc.argtypes = [P] * 12 + [I, P, P] + [I] * 9 + [F, P, I, P, P]
         L.thrift_quantize_workspace_bytes.restype = SZ
         L.thrift_quantize_workspace_bytes.argtypes = [I] * 5
         L.thrift_quantize_fp4.restype = I

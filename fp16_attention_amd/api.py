@@ -19,7 +19,8 @@ __all__ = ["thrift_select_kmax", "thrift_select_blocks", "thrift_block_means",
            "thrift_select_blocks_kbar", "thrift_select_blocks_means", "thrift_select_blocks_head",
            "thrift_quantize_fp4",
            "thrift_quantize_fp4_means", "thrift_quantize_fp4_range", "thrift_cache_update",
-           "thrift_attention_fwd", "thrift_attention_decode", "thrift_decode", "FP4Tensor",
+           "thrift_attention_fwd", "thrift_attention_decode", "thrift_attention_decode_noalloc",
+           "thrift_decode", "FP4Tensor",
            "fp4_transposed", "thrift_forward", "thrift_attention_bwd_workspace", "thrift_attention_fwd_hp",
            "thrift_attention_bwd", "THRIFT_NVFP4", "THRIFT_MXFP4", "THRIFT_NVFP4_MXP", "THRIFT_GROUP_D",
            "THRIFT_GROUP_S", "ThriftError", "FP8Tensor", "thrift_quantize_fp8", "thrift_attention_fwd_tiered",
@@ -406,6 +407,31 @@ def thrift_attention_decode(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4
           _ptr(idx), _ptr(cnt), kmax, B, Hq, Hkv, Sq, Sk, D, block_k, int(causal), float(sm_scale),
           _ptr(out), int(out.dtype == torch.float32), _ptr(lse), _ptr(ws), wsb, _stream())
     return (out, lse) if with_lse else out
+
+
+def thrift_attention_decode_noalloc(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, cnt,
+                                    block_k=64, causal=True, sm_scale=None, out=None, lse=None):
+    """thrift_attention_decode without any device allocation inside the call:
+    the split partials live in the library's static per-GPU array; the
+    caller passes the output (and optional lse) tensors."""
+    B, Hq, Sq, D = q16.shape
+    Hkv, Sk = k16.shape[1], k16.shape[2]
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(D)
+    for name, t in (("q16", q16), ("k16", k16), ("v16", v16)):
+        _check(t, torch.float16, name)
+    _check(idx, torch.int32, "idx")
+    _check(cnt, torch.int32, "cnt")
+    if out is None or tuple(out.shape) != (B, Hq, Sq, D) or out.dtype not in (torch.float16, torch.float32):
+        raise ValueError("out must be a [B, Hq, Sq, D] fp16 or fp32 tensor")
+    if lse is not None:
+        _check(lse, torch.float32, "lse")
+    _call("thrift_attention_decode_noalloc", _ptr(q16), _ptr(k16), _ptr(v16), _ptr(q4.codes),
+          _ptr(q4.scales), _ptr(q4.tensor_scale), _ptr(k4.codes), _ptr(k4.scales),
+          _ptr(k4.tensor_scale), _ptr(v4.codes), _ptr(v4.scales), _ptr(v4.tensor_scale), q4.fmt,
+          _ptr(idx), _ptr(cnt), idx.shape[-1], B, Hq, Hkv, Sq, Sk, D, block_k, int(causal), float(sm_scale),
+          _ptr(out), int(out.dtype == torch.float32), _ptr(lse), _stream())
+    return out
 
 
 def thrift_decode(q16, k16, v16, k4: FP4Tensor, v4: FP4Tensor, fmt=THRIFT_MXFP4, block_q=128,

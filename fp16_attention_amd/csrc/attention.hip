@@ -1917,6 +1917,45 @@ extern "C" thrift_status thrift_attention_decode(
   return D == 128 ? launch_decode<128>(d, fmt, stream) : launch_decode<64>(d, fmt, stream);
 }
 
+// ---- decode without allocation --------------------------------------------------
+//
+// The split partials of thrift_attention_decode_noalloc live in a file-scope
+// device array instead of a caller workspace: THRIFT_DECODE_SCRATCH_BYTES per
+// GPU, held until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in for the symbol): the device
+// address comes from hipGetSymbolAddress once per device, with that device
+// current, and is kept per device.  Every call on one GPU shares the array;
+// nothing in it has to start at zero (each partial the merge reads is written
+// by the same call first), and calls that overlap on one GPU race.
+static __device__ __align__(256) float scratch[THRIFT_DECODE_SCRATCH_BYTES / sizeof(float)];
+static float* scratch_ptr[64];
+static std::atomic<uint64_t> scratch_ready{0};
+
+extern "C" thrift_status thrift_attention_decode_noalloc(
+    const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes,
+    const uint8_t* q4_scales, const float* q4_tscale, const uint8_t* k4_codes,
+    const uint8_t* k4_scales, const float* k4_tscale, const uint8_t* v4_codes,
+    const uint8_t* v4_scales, const float* v4_tscale, thrift_format fmt, const int32_t* idx,
+    const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int Sq, int Sk, int D, int block_k,
+    int causal, float sm_scale, void* o, int o_is_fp32, float* lse, hipStream_t stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return THRIFT_EHIP;
+  if (once_per_device(scratch_ready, [dev] {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) return THRIFT_EHIP;
+        scratch_ptr[dev] = (float*)ptr;
+        return THRIFT_OK;
+      }) != THRIFT_OK)
+    return THRIFT_EHIP;
+  if (B >= 1 && Hq >= 1 && Hkv >= 1 && Hq % Hkv == 0 && Sq >= 1 && Sk >= Sq && D >= 1 && kmax >= 1 &&
+      thrift_attention_decode_workspace_bytes(B, Hq, Hkv, Sq, Sk, D, kmax) > THRIFT_DECODE_SCRATCH_BYTES)
+    return THRIFT_EWORKSPACE;
+  return thrift_attention_decode(q16, k16, v16, q4_codes, q4_scales, q4_tscale, k4_codes, k4_scales, k4_tscale,
+                                 v4_codes, v4_scales, v4_tscale, fmt, idx, cnt, kmax, B, Hq, Hkv, Sq, Sk, D,
+                                 block_k, causal, sm_scale, o, o_is_fp32, lse, scratch_ptr[dev],
+                                 THRIFT_DECODE_SCRATCH_BYTES, stream);
+}
+
 extern "C" const char* thrift_status_string(thrift_status s) {
   switch (s) {
     case THRIFT_OK: return "ok";

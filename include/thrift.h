@@ -385,6 +385,29 @@ thrift_status thrift_attention_decode(const void* q16, const void* k16, const vo
                                       float* lse, void* workspace, size_t workspace_bytes,
                                       hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc):
+ * thrift_attention_decode with the split partials in the library's own
+ * static device array of THRIFT_DECODE_SCRATCH_BYTES per GPU (held until the
+ * process ends) instead of a caller workspace.  Same arguments, results and
+ * validation as thrift_attention_decode, minus workspace and
+ * workspace_bytes; returns THRIFT_EWORKSPACE when the shape's partials
+ * (thrift_attention_decode_workspace_bytes) exceed the array, THRIFT_EHIP
+ * when the array's device address cannot be taken.  Allocates nothing.
+ * Every call on one GPU shares the array: calls that overlap on one GPU (on
+ * different streams, or from different threads) race. */
+#define THRIFT_DECODE_SCRATCH_BYTES ((size_t)16 << 20)
+thrift_status thrift_attention_decode_noalloc(const void* q16, const void* k16, const void* v16,
+                                              const uint8_t* q4_codes, const uint8_t* q4_scales,
+                                              const float* q4_tscale, const uint8_t* k4_codes,
+                                              const uint8_t* k4_scales, const float* k4_tscale,
+                                              const uint8_t* v4_codes, const uint8_t* v4_scales,
+                                              const float* v4_tscale, thrift_format fmt,
+                                              const int32_t* idx, const int32_t* cnt, int kmax, int B,
+                                              int Hq, int Hkv, int Sq, int Sk, int D, int block_k,
+                                              int causal, float sm_scale, void* o, int o_is_fp32,
+                                              float* lse, hipStream_t stream);
+
 /* ---------------------------------------------------------------------- */
 /* Backward pass for quantisation-aware training ("Attn-QAT: 4-Bit         */
 /* Attention With Quantization-Aware Training"; gist.science summary in     */
