@@ -1,4 +1,5 @@
-"""Build the gfx950 HIP library libthrift.so in-tree.
+"""Build the gfx950 HIP library libthrift.so in-tree (and the test-only
+arithmetic probes, tests/libarith_probe.so).
 
 Each HIP source is compiled for gfx950 only, in parallel, then linked into
 one shared library next to this file.  Packed fp32 instructions are turned
@@ -35,6 +36,23 @@ def _compile(src: str, obj: str, verbose: bool) -> None:
         print("\n".join(errs))
 
 
+PROBE_SRC = os.path.join(ROOT, "tests", "arith_probe.hip")
+PROBE_LIB = os.path.join(ROOT, "tests", "libarith_probe.so")
+
+
+def build_probe(verbose: bool = False) -> str:
+    """The arithmetic probes of the tests (not part of the library)."""
+    tmp = PROBE_LIB + ".tmp"
+    cmd = [HIPCC] + FLAGS + ["-shared", "-o", tmp, PROBE_SRC]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError("hipcc failed on arith_probe.hip:\n" + r.stderr)
+    os.replace(tmp, PROBE_LIB)
+    return PROBE_LIB
+
+
 def build(verbose: bool = False) -> str:
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
@@ -47,6 +65,7 @@ def build(verbose: bool = False) -> str:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
     os.replace(tmp, LIB)
+    build_probe(verbose)
     return LIB
 
 

@@ -6,7 +6,8 @@ Bit-exact over the whole tensors: selected block indices and counts, FP4
 codes, block scales and slice scales.  The output is compared on sampled
 query blocks that the oracle computes one by one (first, last, random, GQA
 sibling heads, a planted pair's query block), to the same bounds as the
-small-size parity tests.  Planted high-similarity pairs must be selected.
+small-size parity tests.  The sweep covers both formats at every budget of
+its workload (0, 1, 5, 25 and 100%).  Planted high-similarity pairs must be selected.
 """
 import numpy as np
 import pytest
@@ -26,7 +27,9 @@ CASES = {
     "sweep_mx_25pct": ("sweep", 1, -1, 2500),
     "sweep_mx_100pct": ("sweep", 1, -1, 10000),
     "sweep_nvfp4_0pct": ("sweep", 0, -1, 0),
+    "sweep_nvfp4_1pct": ("sweep", 0, -1, 100),
     "sweep_nvfp4_5pct": ("sweep", 0, -1, 500),
+    "sweep_nvfp4_25pct": ("sweep", 0, -1, 2500),
     "sweep_nvfp4_100pct": ("sweep", 0, -1, 10000),
     "long_mx_5pct": ("long", 1, -1, 500),
     "long_nvfp4_5pct": ("long", 0, -1, 500),

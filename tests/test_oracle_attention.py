@@ -267,12 +267,12 @@ def test_p14_single_key_row_is_its_value(oracle, fmt, promoted):
 
 def _model_rel(path, b, bmax, dt, mt):
     """The evaluation-error model restated (u = 2^-24): kappa u times the
-    chain sums of the key's and the maximum's scores (kappa 2 for the MX
-    block-scaled FP4 instruction, 5 for the fp16 one); the multiplier's
+    chain sums of the key's and the maximum's scores (kappa 2.5 for the MX
+    block-scaled FP4 instruction, 6 for the fp16 one); the multiplier's
     roundings (3; 5 with NVFP4 tensors) and the fused multiply-add on t - mt, one on mt;
     exp2 within one ulp; NVFP4 four more roundings; times 1 + 2^-10."""
     u = 2.0 ** -24
-    kappa = 2.0 if path == 0 else 5.0
+    kappa = 2.5 if path == 0 else 6.0
     nc = 5 if path in (1, 4) else 3
     arg = kappa * u * (b + bmax) + (nc + 1) * u * abs(dt) + u * abs(mt)
     return (np.log(2.0) * arg + 2.0 ** -23 + (4 * u if path == 1 else 0.0)) * (1 + 2.0 ** -10)
