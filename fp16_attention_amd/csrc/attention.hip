@@ -36,8 +36,14 @@
 //    precision (level 2); the accumulator and row sum follow each tile's
 //    level-1 unit (one rescale per tile), so the online softmax merges tiles
 //    whose values do not depend on the running maximum or the order.
-//  * K/V tiles stream through double-buffered LDS, one barrier per tile; the
-//    next tile's global loads are in flight while the current one computes.
+//  * Three workgroups per compute unit (12 waves, at most 168 VGPRs each):
+//    the per-tile accumulator rescale of the two-level P makes the FP4 path
+//    VALU-bound, and the third wave per SIMD hides one wave's MFMA and LDS
+//    latency behind the others' VALU work.  MX K/V tiles stream through a
+//    three-slot LDS ring of direct global->LDS loads, one barrier per two
+//    blocks; the fp16 tiles (FP16 path, NVFP4, the middle tier) go through
+//    one LDS stage inside the same space, loaded after the previous tile's
+//    compute so that no registers are held across it.
 #include <type_traits>
 
 #include "common.h"
@@ -122,7 +128,7 @@ struct Lds {
   static constexpr int VT = KH + kBk * KROWH * 2;
   static constexpr int STAGEH = VT + D * VROWH * 2;
   static constexpr int STAGE = (STAGEH + 255) / 256 * 256;
-  static constexpr int RING = (3 * MxStage<D>::SIZE > 2 * STAGE ? 3 * MxStage<D>::SIZE : 2 * STAGE);
+  static constexpr int RING = (3 * MxStage<D>::SIZE > STAGE ? 3 * MxStage<D>::SIZE : STAGE);
   static constexpr int PROM = RING;  // int[kmax] promoted list
 };
 
@@ -513,7 +519,7 @@ __device__ inline void fp4_nv_tile(RowState<D>& st, const char* stage, const v8h
 
 namespace thrift {
 
-// ---- staging: global -> registers (next tile) -> LDS --------------------------
+// ---- staging: global -> registers -> LDS ----------------------------------------
 
 // MX stage fill.  K codes, V^T codes and (D = 128) K scales go global -> LDS
 // directly with buffer loads (buffer_load_dwordx4 / _dword ... lds: no
@@ -924,7 +930,7 @@ __device__ inline bool work_item(const AttnArgs& a, int id, int& i, int& bhq) {
 // T8: the three-tier variant (MX only): the blocks idx2 lists and idx does
 // not run on the middle MXFP8 tier, between the FP4 and FP16 paths.
 template <int D, int NW, int FMT, bool T8 = false>
-__global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
+__global__ __launch_bounds__(NW * 64, 3) void attn_fwd_kernel(AttnArgs a) {
   static_assert(!T8 || FMT == THRIFT_MXFP4, "the middle tier is built for the MX format");
   using L = Lds<D>;
   constexpr int NT = NW * 64;
@@ -1008,9 +1014,9 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
       // computed (their FP16 pass comes later), which keeps the load stream
       // regular.  Iteration s issues the direct loads of stage s+2 into ring
       // slot s+2 (whose previous stage, s-1, every wave finished before the
-      // last barrier) and computes blocks 2s and 2s+1; each block's QK MFMAs
-      // are issued before the previous block's softmax, so the matrix core
-      // works while this wave's VALU does.
+      // last barrier) and computes blocks 2s and 2s+1, each QK product right
+      // before its softmax (one score tile in registers: the other waves of
+      // the SIMD cover the product's latency).
       using Dma = MxDma<D, NW>;
       using M = MxStage<D>;
       Dma dma(a, bhk, nvalid, w, lane, t);
@@ -1031,47 +1037,30 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
           dma.finish(slot(1), t);
         }
         __syncthreads();
-        v16f sA[2], sB[2];
+        v16f sA[2];
         MxKOps<D> kop;
         MxVOps<D> vop;
-        bool act0 = active_of(0);
-        if (act0) {
-          load_k_mx<D>(kop, slot(0), 0, lane);
-          qk_mx<D>(sA, kop, qB, qsc);
-        }
         int sg = 0;
         // one stage; the ring slot is a compile-time constant so that every
         // LDS address is a per-lane base plus an immediate offset
         auto stage_step = [&](auto slot_c) {
           constexpr int SL = decltype(slot_c)::value;
           char* const cur = smem + SL * M::SIZE;
-          char* const nxt = smem + ((SL + 1) % 3) * M::SIZE;
           char* const fut = smem + ((SL + 2) % 3) * M::SIZE;
           const int j0 = 2 * sg;
           const bool more = sg + 2 < nst;
           if (more) dma.issue(fut, j0 + 4);
-          // block j0 (scores in sA), then j0+1 (scores in sB)
-          const bool act1 = active_of(j0 + 1);
-          if (act1) {
-            load_k_mx<D>(kop, cur, 1, lane);
-            qk_mx<D>(sB, kop, qB, qsc);
-          }
-          if (act0) {
-            load_v_mx<D>(vop, cur, 0, lane);
-            softmax_pv_mx<D>(st, sA, vop, c, j0 * kBk, qrow, S, a.causal, mask_of(j0), lane);
-          }
-          const bool act2 = active_of(j0 + 2);
-          if (act2) {
-            load_k_mx<D>(kop, nxt, 0, lane);
-            qk_mx<D>(sA, kop, qB, qsc);
-          }
-          if (act1) {
-            load_v_mx<D>(vop, cur, 1, lane);
-            softmax_pv_mx<D>(st, sB, vop, c, (j0 + 1) * kBk, qrow, S, a.causal, mask_of(j0 + 1), lane);
+#pragma unroll
+          for (int tb = 0; tb < 2; ++tb) {
+            if (active_of(j0 + tb)) {
+              load_k_mx<D>(kop, cur, tb, lane);
+              qk_mx<D>(sA, kop, qB, qsc);
+              load_v_mx<D>(vop, cur, tb, lane);
+              softmax_pv_mx<D>(st, sA, vop, c, (j0 + tb) * kBk, qrow, S, a.causal, mask_of(j0 + tb), lane);
+            }
           }
           if (more) dma.finish(fut, t);
           __syncthreads();
-          act0 = act2;
           return ++sg < nst;
         };
         using I0 = std::integral_constant<int, 0>;
@@ -1098,28 +1087,21 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
       const float lk = FMT == THRIFT_NVFP4 ? log2f(sv) - log2f(2688.0f) : log2f(sv);
       const float ilk = FMT == THRIFT_NVFP4 ? 2688.0f / sv : 1.0f / sv;
       Nv4Stager<D, NT> stg;
-      if (jc < nvalid) {
-        stg.load(a, bhk, jc, t);
-        stg.store(smem, t);
-      }
-      __syncthreads();
-      int buf = 0;
       while (jc < nvalid) {
         const int jn = next_fp4(jc + 1);
-        if (jn < nvalid) stg.load(a, bhk, jn, t);
+        stg.load(a, bhk, jc, t);
+        stg.store(smem, t);
+        __syncthreads();
         const int key0 = jc * kBk;
         const bool active = !a.causal || key0 <= q0 + 31;
         const bool need_mask = (a.causal && key0 + kBk - 1 > q0) || key0 + kBk > S;
         if (active) {
           if constexpr (FMT == THRIFT_NVFP4)
-            fp4_nv_tile<D>(st, smem + buf * L::STAGE, qh, c, lk, ilk, key0, qrow, S, a.causal, need_mask, lane);
+            fp4_nv_tile<D>(st, smem, qh, c, lk, ilk, key0, qrow, S, a.causal, need_mask, lane);
           else
-            fp4_nvmxp_tile<D>(st, smem + buf * L::STAGE, qh, c, lk, ilk, key0, qrow, S, a.causal, need_mask,
-                              lane);
+            fp4_nvmxp_tile<D>(st, smem, qh, c, lk, ilk, key0, qrow, S, a.causal, need_mask, lane);
         }
-        if (jn < nvalid) stg.store(smem + (buf ^ 1) * L::STAGE, t);
         __syncthreads();
-        buf ^= 1;
         jc = jn;
       }
     }
@@ -1145,26 +1127,19 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
         return j >= 0 && j < nvalid && !((pbits16[j >> 5] >> (j & 31)) & 1u) ? j : -1;
       };
       F8Stager<D, NT> stg;
-      int jc = tier8_j(0);
-      if (jc >= 0) stg.load(a, bhk, jc, t);
-      if (jc >= 0) stg.store(smem, t);
-      __syncthreads();
-      int buf = 0;
       for (int p = 0; p < ncnt2; ++p) {
-        const bool more = p + 1 < ncnt2;
-        const int jn = more ? tier8_j(p + 1) : -1;
-        if (jn >= 0) stg.load(a, bhk, jn, t);
+        const int jc = tier8_j(p);
+        if (jc >= 0) stg.load(a, bhk, jc, t);
+        if (jc >= 0) stg.store(smem, t);
+        __syncthreads();
         if (jc >= 0) {
           const int key0 = jc * kBk;
           const bool active = !a.causal || key0 <= q0 + 31;
           const bool need_mask = (a.causal && key0 + kBk - 1 > q0) || key0 + kBk > S;
           if (active)
-            fp8_tile<D>(st, smem + buf * L::STAGE, qh8, a.sm_log2, key0, qrow, S, a.causal, need_mask, lane);
+            fp8_tile<D>(st, smem, qh8, a.sm_log2, key0, qrow, S, a.causal, need_mask, lane);
         }
-        if (jn >= 0) stg.store(smem + (buf ^ 1) * L::STAGE, t);
         __syncthreads();
-        buf ^= 1;
-        jc = jn;
       }
     }
   }
@@ -1176,29 +1151,20 @@ __global__ __launch_bounds__(NW * 64, 2) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qh[kk] = qvalid ? *(const v8h*)(a.q16 + qoff + kk * 16) : v8h{};
     F16Stager<D, NT> stg;
-    auto valid_j = [&](int p) { int j = prom[p]; return j >= 0 && j < nvalid ? j : -1; };
-    int jc = valid_j(0);
-    if (jc >= 0) stg.load(a, bhk, jc, t);
-    stg.store(smem, t);
-    __syncthreads();
-    int buf = 0;
     for (int p = 0; p < ncnt; ++p) {
-      const bool more = p + 1 < ncnt;
-      const int jn = more ? valid_j(p + 1) : -1;
-      if (more) {
-        if (jn >= 0) stg.load(a, bhk, jn, t);
-      }
+      const int j = prom[p];
+      const int jc = j >= 0 && j < nvalid ? j : -1;
+      if (jc >= 0) stg.load(a, bhk, jc, t);
+      if (jc >= 0) stg.store(smem, t);
+      __syncthreads();
       if (jc >= 0) {
         const int key0 = jc * kBk;
         const bool active = !a.causal || key0 <= q0 + 31;
         const bool need_mask = (a.causal && key0 + kBk - 1 > q0) || key0 + kBk > S;
         if (active)
-          fp16_tile<D>(st, smem + buf * L::STAGE, qh, a.sm_log2, key0, qrow, S, a.causal, need_mask, lane);
+          fp16_tile<D>(st, smem, qh, a.sm_log2, key0, qrow, S, a.causal, need_mask, lane);
       }
-      if (more && jn >= 0) stg.store(smem + (buf ^ 1) * L::STAGE, t);
       __syncthreads();
-      buf ^= 1;
-      jc = jn;
     }
   }
 
