@@ -555,13 +555,13 @@ def cpu_baseline(w, d, fmt, budget="block", p_fmt=None, tier8=0):
     O.lib()
     t0 = time.perf_counter()
     if tier8:
-        O.pipeline_tiers(q1, k1, v1, w.bq, w.bk, w.causal, w.topk_bp, tier8)
+        O.pipeline_tiers(q1, k1, v1, w.bq, w.bk, w.causal, w.topk_bp, tier8, with_amb=False)
     elif budget == "head":
         idx, cnt = O.select_head(q1, k1, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp)
         q4, k4, v4 = (O.quantize(x, ax, fmt) for x, ax in ((q1, O.AXIS_D), (k1, O.AXIS_D), (v1, O.AXIS_S)))
         O.attention(q1, k1, v1, q4, k4, v4, idx, cnt, w.bq, w.bk, w.causal, p_fmt=p_fmt)
     else:
-        O.pipeline(q1, k1, v1, fmt, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp, p_fmt=p_fmt)
+        O.pipeline(q1, k1, v1, fmt, w.bq, w.bk, w.causal, w.topk_count, w.topk_bp, p_fmt=p_fmt, with_amb=False)
     sec = time.perf_counter() - t0
     f = 4.0 * w.D * unmasked_pairs(w.S, w.causal)
     return {"value": round(f / sec / 1e12, 5), "unit": "TFLOP/s", "cores": nthreads,

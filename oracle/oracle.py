@@ -542,18 +542,19 @@ def row_probs(q16, k16, v16, q4: FP4Tensor, k4: FP4Tensor, v4: FP4Tensor, idx, c
 
 
 def pipeline(q16, k16, v16, fmt, bq, bk, causal, topk_count=-1, topk_bp=0, sm_scale=None,
-             work=None, p_fmt=None):
-    """Selection, quantisation of Q/K/V and attention, all on the oracle."""
+             work=None, p_fmt=None, with_amb=True):
+    """Selection, quantisation of Q/K/V and attention, all on the oracle
+    (with_amb: also the list of decisions that may go either way)."""
     idx, cnt, _ = select(q16, k16, bq, bk, causal, topk_count, topk_bp)
     q4 = quantize(q16, AXIS_D, fmt)
     k4 = quantize(k16, AXIS_D, fmt)
     v4 = quantize(v16, AXIS_S, fmt)
-    o, lse, amb = attention(q16, k16, v16, q4, k4, v4, idx, cnt, bq, bk, causal, sm_scale, work,
-                            with_amb=True, p_fmt=p_fmt)
-    return dict(idx=idx, cnt=cnt, q4=q4, k4=k4, v4=v4, o=o, lse=lse, amb=amb)
+    res = attention(q16, k16, v16, q4, k4, v4, idx, cnt, bq, bk, causal, sm_scale, work, with_amb=with_amb,
+                    p_fmt=p_fmt)
+    return dict(idx=idx, cnt=cnt, q4=q4, k4=k4, v4=v4, o=res[0], lse=res[1], amb=res[2] if with_amb else None)
 
 
-def pipeline_tiers(q16, k16, v16, bq, bk, causal, bp16, bp8, sm_scale=None, work=None):
+def pipeline_tiers(q16, k16, v16, bq, bk, causal, bp16, bp8, sm_scale=None, work=None, with_amb=True):
     """The three-tier forward on the oracle (MX format): the FP16 tier is the
     selection under budget bp16, the FP16 and FP8 tiers together the
     selection under bp16 + bp8 (basis points each)."""
@@ -561,7 +562,7 @@ def pipeline_tiers(q16, k16, v16, bq, bk, causal, bp16, bp8, sm_scale=None, work
     idx2, cnt2, _ = select(q16, k16, bq, bk, causal, -1, bp16 + bp8)
     q4, k4, v4 = quantize(q16, AXIS_D, MX), quantize(k16, AXIS_D, MX), quantize(v16, AXIS_S, MX)
     q8, k8, v8 = quantize_fp8(q16, AXIS_D), quantize_fp8(k16, AXIS_D), quantize_fp8(v16, AXIS_S)
-    o, lse, amb = attention_tiers(q16, k16, v16, q4, k4, v4, q8, k8, v8, idx, cnt, idx2, cnt2, bq, bk,
-                                  causal, sm_scale, work, with_amb=True)
+    res = attention_tiers(q16, k16, v16, q4, k4, v4, q8, k8, v8, idx, cnt, idx2, cnt2, bq, bk,
+                          causal, sm_scale, work, with_amb=with_amb)
     return dict(idx=idx, cnt=cnt, idx2=idx2, cnt2=cnt2, q4=q4, k4=k4, v4=v4, q8=q8, k8=k8, v8=v8,
-                o=o, lse=lse, amb=amb)
+                o=res[0], lse=res[1], amb=res[2] if with_amb else None)
