@@ -6,7 +6,11 @@ one shared library next to this file.  Packed fp32 instructions are turned
 off (-packed-fp32-ops): fp32 code stays on the scalar-per-lane VALU forms.
 The backward's kernels ask for the VGPR form of the matrix instructions:
 their products feed VALU work directly, and with results in accumulation
-registers the compiler copied every one of them back per tile.
+registers the compiler copied every one of them back per tile.  The forward
+source is built without NaN semantics (-fno-honor-nans): its inputs are
+finite, masked scores are -inf and never NaN, and with NaNs honoured every
+maximum of matrix-instruction results is preceded by a canonicalising
+self-maximum (five VALU instructions of the MX tile's 219).
 """
 import concurrent.futures as cf
 import os
@@ -21,7 +25,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SOURCES = ["select.hip", "quantize.hip", "attention.hip", "backward.hip"]
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-I", os.path.join(ROOT, "include"),
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-Wall"]
-EXTRA = {"backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+EXTRA = {"backward.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"], "attention.hip": ["-fno-honor-nans"]}
 
 
 def _compile(src: str, obj: str, verbose: bool) -> None:

@@ -292,10 +292,10 @@ __device__ inline void softmax_pv_mx(RowState<D>& st, v16f s[2], const MxVOps<D>
   const float gmax = fmaxf(max16(s[0]), max16(s[1]));
   const float tmax = pair_max(gmax);
   const float mtc = tmax * c;
-  const float nm = tile_unit<D>(st, mtc, 0.0f) ? -mtc : -INFINITY;  // dead tile: every p = 0
+  const float nm = tile_unit<D>(st, mtc, -0.0f) ? -mtc : -INFINITY;  // dead tile: every p = 0
 
   // probabilities relative to the tile maximum, unquantised row sum
-  float lsum = 0.0f;
+  float lsum = -0.0f;  // x + -0 folds to x
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -319,7 +319,7 @@ __device__ inline void softmax_pv_mx(RowState<D>& st, v16f s[2], const MxVOps<D>
   for (int r = 0; r < 4; ++r) {
     const v16f& x = s[r >> 1];
     const int o = (r & 1) * 8;
-    uint32_t y = 0;
+    uint32_t y = __float_as_uint(x[o]);  // every byte is written below
     y = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(y, x[o + 0], x[o + 1], sf, 0);
     y = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(y, x[o + 2], x[o + 3], sf, 1);
     y = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(y, x[o + 4], x[o + 5], sf, 2);
@@ -377,8 +377,8 @@ __device__ inline void fp16_softmax_pv(RowState<D>& st, v16f s[2], const _Float1
   if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
   // probabilities relative to the tile maximum (level 1), rounded to fp16
   const float mtc = pair_max(fmaxf(max16(s[0]), max16(s[1]))) * c;
-  const float nm = tile_unit<D>(st, mtc, 0.0f) ? -mtc : -INFINITY;
-  float lsum = 0.0f;
+  const float nm = tile_unit<D>(st, mtc, -0.0f) ? -mtc : -INFINITY;
+  float lsum = -0.0f;  // x + -0 folds to x
   v8h pB[4];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
@@ -418,7 +418,7 @@ __device__ inline void fp4_nv_softmax_pv(RowState<D>& st, v16f s[2], const char*
   const float tmax = pair_max(fmaxf(gm0, gm1));      // the query's tile maximum (level 1)
   const float mtc = tmax * c;
   const float nm = tile_unit<D>(st, mtc, lk) ? -mtc : -INFINITY;
-  float lsum = 0.0f;
+  float lsum = -0.0f;  // x + -0 folds to x
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -474,7 +474,7 @@ __device__ inline void fp4_nvmxp_tile(RowState<D>& st, const char* stage, const 
   const float tmax = pair_max(gmax);
   const float mtc = tmax * c;
   const float nm = tile_unit<D>(st, mtc, lk) ? -mtc : -INFINITY;
-  float lsum = 0.0f;
+  float lsum = -0.0f;  // x + -0 folds to x
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -566,8 +566,8 @@ __device__ inline void fp8_tile(RowState<D>& st, const char* stage, const v8h* q
   const float gmax = fmaxf(max16(s[0]), max16(s[1]));
   const float tmax = pair_max(gmax);  // level 1: the tile maximum
   const float mtc = tmax * c;
-  const float nm = tile_unit<D>(st, mtc, 0.0f) ? -mtc : -INFINITY;
-  float lsum = 0.0f;
+  const float nm = tile_unit<D>(st, mtc, -0.0f) ? -mtc : -INFINITY;
+  float lsum = -0.0f;  // x + -0 folds to x
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -1666,7 +1666,7 @@ static thrift_status make_attn_args(
     const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes,
     const uint8_t* q4_scales, const float* q4_tscale, const uint8_t* k4_codes,
     const uint8_t* k4_scales, const float* k4_tscale, const uint8_t* v4_codes,
-    const uint8_t* v4_scales, const float* v4_tscale, thrift_format fmt, const int32_t* idx,
+    const uint8_t* v4_scales, const float* v4_tscale, int fmt, const int32_t* idx,
     const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D, int block_q, int block_k,
     int causal, float sm_scale, void* o, int o_is_fp32, float* lse, AttnArgs& a) {
   if (!q4_codes || !q4_scales || !k4_codes || !k4_scales || !v4_codes || !v4_scales || !idx ||
@@ -1720,7 +1720,7 @@ extern "C" thrift_status thrift_attention_fwd(
     const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes,
     const uint8_t* q4_scales, const float* q4_tscale, const uint8_t* k4_codes,
     const uint8_t* k4_scales, const float* k4_tscale, const uint8_t* v4_codes,
-    const uint8_t* v4_scales, const float* v4_tscale, thrift_format fmt, const int32_t* idx,
+    const uint8_t* v4_scales, const float* v4_tscale, int fmt, const int32_t* idx,
     const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D, int block_q, int block_k,
     int causal, float sm_scale, void* o, int o_is_fp32, float* lse, hipStream_t stream) {
   AttnArgs a;
@@ -1823,7 +1823,7 @@ extern "C" thrift_status thrift_attention_decode(
     const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes,
     const uint8_t* q4_scales, const float* q4_tscale, const uint8_t* k4_codes,
     const uint8_t* k4_scales, const float* k4_tscale, const uint8_t* v4_codes,
-    const uint8_t* v4_scales, const float* v4_tscale, thrift_format fmt, const int32_t* idx,
+    const uint8_t* v4_scales, const float* v4_tscale, int fmt, const int32_t* idx,
     const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int Sq, int Sk, int D, int block_k,
     int causal, float sm_scale, void* o, int o_is_fp32, float* lse, void* workspace,
     size_t workspace_bytes, hipStream_t stream) {
@@ -1901,7 +1901,7 @@ extern "C" thrift_status thrift_attention_decode_noalloc(
     const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes,
     const uint8_t* q4_scales, const float* q4_tscale, const uint8_t* k4_codes,
     const uint8_t* k4_scales, const float* k4_tscale, const uint8_t* v4_codes,
-    const uint8_t* v4_scales, const float* v4_tscale, thrift_format fmt, const int32_t* idx,
+    const uint8_t* v4_scales, const float* v4_tscale, int fmt, const int32_t* idx,
     const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int Sq, int Sk, int D, int block_k,
     int causal, float sm_scale, void* o, int o_is_fp32, float* lse, hipStream_t stream) {
   int dev = 0;
@@ -1922,7 +1922,7 @@ extern "C" thrift_status thrift_attention_decode_noalloc(
                                  THRIFT_DECODE_SCRATCH_BYTES, stream);
 }
 
-extern "C" const char* thrift_status_string(thrift_status s) {
+extern "C" const char* thrift_status_string(int s) {
   switch (s) {
     case THRIFT_OK: return "ok";
     case THRIFT_EINVAL: return "invalid argument";
