@@ -694,7 +694,7 @@ BwdLayout bwd_layout(int B, int Hq, int Hkv, int S, int D, int bq) {
 thrift_status check_bwd(const void* q16, const void* k16, const void* v16, const uint8_t* q4c,
                         const uint8_t* q4s, const float* q4t, const uint8_t* k4c, const uint8_t* k4s,
                         const float* k4t, const uint8_t* v4c, const uint8_t* v4s, const float* v4t,
-                        thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                        int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
                         int B, int Hq, int Hkv, int S, int D, int block_q, int block_k, int causal,
                         float sm_scale, const float* lse, const void* workspace, size_t workspace_bytes) {
   if (!q16 || !k16 || !v16 || !q4c || !q4s || !k4c || !k4s || !v4c || !v4s || !idx || !cnt || !lse ||
@@ -835,7 +835,7 @@ extern "C" size_t thrift_attention_bwd_workspace_bytes(int B, int Hq, int Hkv, i
 extern "C" thrift_status thrift_attention_fwd_hp(
     const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes, const uint8_t* q4_scales,
     const float* q4_tscale, const uint8_t* k4_codes, const uint8_t* k4_scales, const float* k4_tscale,
-    const uint8_t* v4_codes, const uint8_t* v4_scales, const float* v4_tscale, thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D,
+    const uint8_t* v4_codes, const uint8_t* v4_scales, const float* v4_tscale, int fmt, const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D,
     int block_q, int block_k, int causal, float sm_scale, const float* lse, float* ohp, void* workspace,
     size_t workspace_bytes, hipStream_t stream) {
   thrift_status st = check_bwd(q16, k16, v16, q4_codes, q4_scales, q4_tscale, k4_codes, k4_scales, k4_tscale,
@@ -860,7 +860,7 @@ extern "C" thrift_status thrift_attention_fwd_hp(
 extern "C" thrift_status thrift_attention_bwd(
     const void* q16, const void* k16, const void* v16, const uint8_t* q4_codes, const uint8_t* q4_scales,
     const float* q4_tscale, const uint8_t* k4_codes, const uint8_t* k4_scales, const float* k4_tscale,
-    const uint8_t* v4_codes, const uint8_t* v4_scales, const float* v4_tscale, thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D,
+    const uint8_t* v4_codes, const uint8_t* v4_scales, const float* v4_tscale, int fmt, const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D,
     int block_q, int block_k, int causal, float sm_scale, const float* lse, const float* ohp, const void* do16,
     float* dq, float* dk, float* dv, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   thrift_status st = check_bwd(q16, k16, v16, q4_codes, q4_scales, q4_tscale, k4_codes, k4_scales, k4_tscale,

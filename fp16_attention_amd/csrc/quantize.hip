@@ -472,7 +472,7 @@ using namespace thrift;
 
 static int pad_s(int S) { return cdiv(S, 64) * 64; }
 
-extern "C" size_t thrift_quantize_workspace_bytes(int B, int H, int S, int D, thrift_format fmt) {
+extern "C" size_t thrift_quantize_workspace_bytes(int B, int H, int S, int D, int fmt) {
   if (B < 1 || H < 1 || S < 1 || D < 1) return 0;
   if (fmt != THRIFT_NVFP4) return 0;
   size_t nchunk = ((size_t)S * D + kAmaxChunk - 1) / kAmaxChunk;
@@ -480,7 +480,7 @@ extern "C" size_t thrift_quantize_workspace_bytes(int B, int H, int S, int D, th
 }
 
 extern "C" thrift_status thrift_quantize_fp4(const void* x16, int B, int H, int S, int D,
-                                             thrift_group_axis axis, thrift_format fmt,
+                                             int axis, int fmt,
                                              uint8_t* codes, uint8_t* scales, float* tensor_scale,
                                              void* workspace, size_t workspace_bytes,
                                              hipStream_t stream) {
@@ -533,7 +533,7 @@ extern "C" thrift_status thrift_quantize_fp4(const void* x16, int B, int H, int 
 }
 
 extern "C" thrift_status thrift_quantize_fp4_range(const void* x16, int B, int H, int S, int D,
-                                                   thrift_group_axis axis, thrift_format fmt, int s0,
+                                                   int axis, int fmt, int s0,
                                                    int s1, uint8_t* codes, uint8_t* scales,
                                                    const float* tensor_scale, hipStream_t stream) {
   if (!x16 || !codes || !scales) return THRIFT_EINVAL;
@@ -576,7 +576,7 @@ extern "C" thrift_status thrift_quantize_fp4_range(const void* x16, int B, int H
   return launch_status();
 }
 
-extern "C" size_t thrift_quantize_means_workspace_bytes(int B, int H, int S, int D, thrift_format fmt,
+extern "C" size_t thrift_quantize_means_workspace_bytes(int B, int H, int S, int D, int fmt,
                                                         int blk) {
   if (B < 1 || H < 1 || S < 1 || D < 1 || blk < 1) return 0;
   if (fmt != THRIFT_NVFP4) return 0;
@@ -584,7 +584,7 @@ extern "C" size_t thrift_quantize_means_workspace_bytes(int B, int H, int S, int
 }
 
 extern "C" thrift_status thrift_quantize_fp4_means(const void* x16, int B, int H, int S, int D,
-                                                   thrift_format fmt, int blk, uint8_t* codes,
+                                                   int fmt, int blk, uint8_t* codes,
                                                    uint8_t* scales, float* tensor_scale, float* means,
                                                    void* workspace, size_t workspace_bytes,
                                                    hipStream_t stream) {
@@ -622,7 +622,7 @@ extern "C" thrift_status thrift_quantize_fp4_means(const void* x16, int B, int H
 }
 
 extern "C" thrift_status thrift_cache_update(const void* k16, const void* v16, int B, int H, int S, int D,
-                                             int block_k, int s0, int s1, thrift_format fmt, float* kbar,
+                                             int block_k, int s0, int s1, int fmt, float* kbar,
                                              uint8_t* k4_codes, uint8_t* k4_scales, const float* k4_tscale,
                                              uint8_t* v4_codes, uint8_t* v4_scales, const float* v4_tscale,
                                              hipStream_t stream) {
@@ -660,7 +660,7 @@ extern "C" thrift_status thrift_cache_update(const void* k16, const void* v16, i
   return launch_status();
 }
 
-extern "C" thrift_status thrift_quantize_fp8(const void* x16, int B, int H, int S, int D, thrift_group_axis axis,
+extern "C" thrift_status thrift_quantize_fp8(const void* x16, int B, int H, int S, int D, int axis,
                                              uint8_t* codes, uint8_t* scales, hipStream_t stream) {
   if (!x16 || !codes || !scales) return THRIFT_EINVAL;
   if (B < 1 || H < 1 || S < 1) return THRIFT_EINVAL;

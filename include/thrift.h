@@ -69,7 +69,7 @@ typedef enum {
  * 448); the sign of a value that rounds to zero is kept.
  *   THRIFT_NVFP4_MXP: thrift_attention_fwd only, a variant of the FP4 path:
  *     Q, K and V as THRIFT_NVFP4 tensors, but the probabilities quantised
- *     MX-style (E8M0 per 32 keys under an integer level-1 offset) instead of
+ *     MX-style (level 1 the tile maximum, E8M0 per 32 keys) instead of
  *     NVFP4's two levels.  Every other call rejects it (THRIFT_EINVAL). */
 typedef enum { THRIFT_NVFP4 = 0, THRIFT_MXFP4 = 1, THRIFT_NVFP4_MXP = 2 } thrift_format;
 
@@ -193,7 +193,7 @@ thrift_status thrift_select_blocks_head(const float* qbar, const float* kbar, in
 
 /* Workspace bytes thrift_quantize_fp4 needs (per-slice maxima, NVFP4 only;
  * 0 for MXFP4). */
-size_t thrift_quantize_workspace_bytes(int B, int H, int S, int D, thrift_format fmt);
+size_t thrift_quantize_workspace_bytes(int B, int H, int S, int D, int fmt);
 
 /* Quantise x16 [B,H,S,D] fp16 to FP4 along `axis` (layouts above).
  *   codes, scales (out): as laid out for the axis;
@@ -203,7 +203,7 @@ size_t thrift_quantize_workspace_bytes(int B, int H, int S, int D, thrift_format
  * the rule stated with thrift_format, whatever the hardware's own
  * conversion instructions do. */
 thrift_status thrift_quantize_fp4(const void* x16, int B, int H, int S, int D,
-                                  thrift_group_axis axis, thrift_format fmt, uint8_t* codes,
+                                  int axis, int fmt, uint8_t* codes,
                                   uint8_t* scales, float* tensor_scale, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
 
@@ -217,8 +217,8 @@ thrift_status thrift_quantize_fp4(const void* x16, int B, int H, int S, int D,
  * NVFP4 reads x16 twice (its slice scale must precede the codes) and needs
  * thrift_quantize_means_workspace_bytes of workspace; MXFP4 reads it once
  * and needs none. */
-size_t thrift_quantize_means_workspace_bytes(int B, int H, int S, int D, thrift_format fmt, int blk);
-thrift_status thrift_quantize_fp4_means(const void* x16, int B, int H, int S, int D, thrift_format fmt,
+size_t thrift_quantize_means_workspace_bytes(int B, int H, int S, int D, int fmt, int blk);
+thrift_status thrift_quantize_fp4_means(const void* x16, int B, int H, int S, int D, int fmt,
                                         int blk, uint8_t* codes, uint8_t* scales, float* tensor_scale,
                                         float* means, void* workspace, size_t workspace_bytes,
                                         hipStream_t stream);
@@ -236,7 +236,7 @@ thrift_status thrift_quantize_fp4_means(const void* x16, int B, int H, int S, in
  *     whose new tokens do re-encodes the slice with thrift_quantize_fp4).
  * 0 <= s0 < s1 <= S, else THRIFT_EINVAL. */
 thrift_status thrift_quantize_fp4_range(const void* x16, int B, int H, int S, int D,
-                                        thrift_group_axis axis, thrift_format fmt, int s0, int s1,
+                                        int axis, int fmt, int s0, int s1,
                                         uint8_t* codes, uint8_t* scales, const float* tensor_scale,
                                         hipStream_t stream);
 
@@ -248,7 +248,7 @@ thrift_status thrift_quantize_fp4_range(const void* x16, int B, int H, int S, in
  * THRIFT_GROUP_S).  Byte for byte the results of those three calls; the
  * NVFP4 slice scales k4_tscale, v4_tscale are read, not changed. */
 thrift_status thrift_cache_update(const void* k16, const void* v16, int B, int H, int S, int D, int block_k,
-                                  int s0, int s1, thrift_format fmt, float* kbar, uint8_t* k4_codes,
+                                  int s0, int s1, int fmt, float* kbar, uint8_t* k4_codes,
                                   uint8_t* k4_scales, const float* k4_tscale, uint8_t* v4_codes,
                                   uint8_t* v4_scales, const float* v4_tscale, hipStream_t stream);
 
@@ -290,7 +290,7 @@ thrift_status thrift_attention_fwd(const void* q16, const void* k16, const void*
                                    const float* q4_tscale, const uint8_t* k4_codes,
                                    const uint8_t* k4_scales, const float* k4_tscale,
                                    const uint8_t* v4_codes, const uint8_t* v4_scales,
-                                   const float* v4_tscale, thrift_format fmt, const int32_t* idx,
+                                   const float* v4_tscale, int fmt, const int32_t* idx,
                                    const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S,
                                    int D, int block_q, int block_k, int causal, float sm_scale,
                                    void* o, int o_is_fp32, float* lse, hipStream_t stream);
@@ -318,7 +318,7 @@ thrift_status thrift_attention_fwd(const void* q16, const void* k16, const void*
  *   THRIFT_GROUP_S (V): codes [B,H,D,Sp] u8 (V transposed, Sp = S rounded up
  *     to 64, padding tokens zero), scales [B,H,D,Sp/32] u8.
  * codes 16-byte aligned; no workspace. */
-thrift_status thrift_quantize_fp8(const void* x16, int B, int H, int S, int D, thrift_group_axis axis,
+thrift_status thrift_quantize_fp8(const void* x16, int B, int H, int S, int D, int axis,
                                   uint8_t* codes, uint8_t* scales, hipStream_t stream);
 
 /* Three-tier forward (MX format).  As thrift_attention_fwd with
@@ -378,7 +378,7 @@ thrift_status thrift_attention_decode(const void* q16, const void* k16, const vo
                                       const float* q4_tscale, const uint8_t* k4_codes,
                                       const uint8_t* k4_scales, const float* k4_tscale,
                                       const uint8_t* v4_codes, const uint8_t* v4_scales,
-                                      const float* v4_tscale, thrift_format fmt,
+                                      const float* v4_tscale, int fmt,
                                       const int32_t* idx, const int32_t* cnt, int kmax, int B,
                                       int Hq, int Hkv, int Sq, int Sk, int D, int block_k,
                                       int causal, float sm_scale, void* o, int o_is_fp32,
@@ -402,7 +402,7 @@ thrift_status thrift_attention_decode_noalloc(const void* q16, const void* k16, 
                                               const float* q4_tscale, const uint8_t* k4_codes,
                                               const uint8_t* k4_scales, const float* k4_tscale,
                                               const uint8_t* v4_codes, const uint8_t* v4_scales,
-                                              const float* v4_tscale, thrift_format fmt,
+                                              const float* v4_tscale, int fmt,
                                               const int32_t* idx, const int32_t* cnt, int kmax, int B,
                                               int Hq, int Hkv, int Sq, int Sk, int D, int block_k,
                                               int causal, float sm_scale, void* o, int o_is_fp32,
@@ -448,7 +448,7 @@ thrift_status thrift_attention_fwd_hp(const void* q16, const void* k16, const vo
                                       const float* q4_tscale, const uint8_t* k4_codes,
                                       const uint8_t* k4_scales, const float* k4_tscale,
                                       const uint8_t* v4_codes, const uint8_t* v4_scales,
-                                      const float* v4_tscale, thrift_format fmt, const int32_t* idx, const int32_t* cnt,
+                                      const float* v4_tscale, int fmt, const int32_t* idx, const int32_t* cnt,
                                       int kmax, int B, int Hq, int Hkv, int S, int D, int block_q,
                                       int block_k, int causal, float sm_scale, const float* lse,
                                       float* ohp, void* workspace, size_t workspace_bytes,
@@ -462,14 +462,15 @@ thrift_status thrift_attention_bwd(const void* q16, const void* k16, const void*
                                    const float* q4_tscale, const uint8_t* k4_codes,
                                    const uint8_t* k4_scales, const float* k4_tscale,
                                    const uint8_t* v4_codes, const uint8_t* v4_scales,
-                                   const float* v4_tscale, thrift_format fmt, const int32_t* idx, const int32_t* cnt, int kmax,
+                                   const float* v4_tscale, int fmt, const int32_t* idx, const int32_t* cnt, int kmax,
                                    int B, int Hq, int Hkv, int S, int D, int block_q, int block_k,
                                    int causal, float sm_scale, const float* lse, const float* ohp,
                                    const void* do16, float* dq, float* dk, float* dv, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream);
 
-/* Static string for a status code (host). */
-const char* thrift_status_string(thrift_status s);
+/* Static string for a status code (host): s is a thrift_status value;
+ * any other value gives "unknown status". */
+const char* thrift_status_string(int s);
 
 #ifdef __cplusplus
 }
