@@ -22,6 +22,9 @@ sys.path.insert(0, ROOT)
 TRAFFIC_FILES = {("long", "mx"): os.path.join(ROOT, "profiles", "attn_fwd_kernel_long_mx_traffic.txt"),
                  ("decode", "mx"): os.path.join(ROOT, "profiles", "decode_kernels_decode_mx_traffic.txt"),
                  ("prefill_bwd", "mx"): os.path.join(ROOT, "profiles", "backward_kernels_prefill_mx_traffic.txt")}
+# committed rocprofv3 --pmc utilisation summaries of the attention kernel
+PMC_FILES = {("long", "mx"): os.path.join(ROOT, "profiles", "attn_fwd_kernel_long_mx_pmc.txt"),
+             ("long", "nvfp4"): os.path.join(ROOT, "profiles", "attn_fwd_kernel_long_nvfp4_pmc.txt")}
 CSRC = os.path.join(ROOT, "fp16_attention_amd", "csrc")
 # the sources a profiled kernel is built from (their hash dates the counters)
 KERNEL_SRC = (os.path.join(CSRC, "attention.hip"), os.path.join(CSRC, "common.h"))
@@ -70,9 +73,16 @@ def measured_traffic(workload, fmt_name, src=KERNEL_SRC):
     (FETCH_SIZE + WRITE_SIZE, each scaled by its reading on a copy kernel of
     known size), or None when none were taken on this workload or they were
     taken on an attention kernel source other than the one built now."""
+    rec = _counter_file(TRAFFIC_FILES.get((workload, fmt_name)), src)
+    return None if rec is None else int(rec["traffic_bytes_per_launch"])
+
+
+def _counter_file(path, src):
+    """The machine-readable "key: value" lines of a committed profiler summary,
+    or None when it is missing or was taken on sources other than the ones
+    built now (kernel_source_sha256 over src)."""
     import hashlib
 
-    path = TRAFFIC_FILES.get((workload, fmt_name))
     if path is None or not os.path.exists(path):
         return None
     rec = {}
@@ -82,13 +92,24 @@ def measured_traffic(workload, fmt_name, src=KERNEL_SRC):
                 k, v = ln.split(":", 1)
                 rec[k.strip()] = v.strip()
     h = hashlib.sha256()
-    for path in src:
-        with open(path, "rb") as f:
+    for p in src:
+        with open(p, "rb") as f:
             h.update(f.read())
-    h = h.hexdigest()
-    if rec.get("kernel_source_sha256") != h:
-        return None
-    return int(rec["traffic_bytes_per_launch"])
+    return rec if rec.get("kernel_source_sha256") == h.hexdigest() else None
+
+
+def measured_utilisation(workload, fmt_name, scores, src=KERNEL_SRC):
+    """MFMA busy fraction and VALU wave-instructions per score of the attention
+    kernel from the committed rocprofv3 --pmc summary of this workload and
+    format (SQ_VALU_MFMA_BUSY_CYCLES over SQ_BUSY_CYCLES scaled to SIMDs;
+    SQ_INSTS_VALU per launch over 64 lanes' worth of scores), or {} when none
+    was taken on the kernel source built now."""
+    rec = _counter_file(PMC_FILES.get((workload, fmt_name)), src)
+    if rec is None:
+        return {}
+    valu = float(rec["sq_insts_valu_per_launch"])
+    return {"mfma_busy": float(rec["mfma_busy_frac"]), "valu_busy_est": float(rec["valu_busy_frac_est"]),
+            "valu_insts_per_score": round(valu * 64 / scores, 3)}
 
 
 def copy_calibration(torch, dev, mib):
@@ -131,6 +152,11 @@ def main():
                     help="the three-tier variant (MX format, forward): this many basis points of the "
                          "valid pairs beyond the FP16 tier's run on the MXFP8 middle tier")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-nvfp4", action="store_true",
+                    help="skip the NVFP4 forward that the default (MX) line reports beside its own")
+    ap.add_argument("--all-configs", action="store_true",
+                    help="one line per workload, format and top-k of the benchmark's configurations "
+                         "(forward, no CPU baseline) instead of the single line")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
     ap.add_argument("--copy-mib", type=int, default=0,
                     help="run one plain device copy of this many MiB before the steps (a "
@@ -163,6 +189,8 @@ def main():
         print("bench.py: --tier8-bp is a forward variant of the MX format with per-query-block budgets "
               "in basis points (prefill shape only)", file=sys.stderr)
         sys.exit(2)
+    if args.all_configs:
+        return run_all_configs(args)
     t0 = time.time()
     d = W.generate(w)
     gen_s = time.time() - t0
@@ -170,9 +198,40 @@ def main():
         return run_decode(args, w, d, gen_s)
     if args.pass_ == "bwd":
         return run_backward(args, w, d, gen_s)
+    m = measure_forward(args, w, d, fmt, p_fmt, tier8, args.budget, args.steps, args.warmup, args.copy_mib)
+    line = forward_line(args, w, m, fmt, p_fmt, tier8, gen_s)
+    if fmt == api.THRIFT_MXFP4 and not tier8 and args.budget == "block" and not args.no_nvfp4:
+        # the pages' own format on the same input: its FP4 path runs on the fp16
+        # matrix cores (decoded operands), so its bound is F_alg / fp16 peak
+        mn = measure_forward(args, w, d, api.THRIFT_NVFP4, None, 0, "block", args.steps, args.warmup, 0)
+        line["nvfp4"] = {"ms_per_step": round(mn["ms_step"], 4), "attention_fwd_ms": round(mn["fwd_ms"], 4),
+                         "attention_fwd_tflops": round(mn["f_alg"] / mn["fwd_ms"] / 1e9, 2),
+                         "frac_of_fp16_bound": round(mn["f_alg"] / P_FP16 / (mn["fwd_ms"] * 1e-3), 4),
+                         "fp16_pair_share": round(mn["p16"] / mn["pairs"], 5)}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w, d, fmt, args.budget, p_fmt, tier8)
+    emit(line, args.out)
+
+
+def emit(line, out=None):
+    s = json.dumps(line)
+    print(s, flush=True)
+    if out:
+        with open(out, "a") as f:
+            f.write(s + "\n")
+
+
+def measure_forward(args, w, d, fmt, p_fmt, tier8, budget, steps, warmup, copy_mib):
+    """Time `steps` forward steps (after `warmup`) of workload w on input d:
+    means + FP4 codes of Q and K in one pass, V's codes, selection, the
+    attention forward.  Returns the timings (ms) and pair counts."""
+    import torch
+
+    from fp16_attention_amd import api
+
     dev = torch.device("cuda:0")
     q, k, v = (torch.from_numpy(d[n]).to(dev) for n in ("q", "k", "v"))
-    if args.budget == "head":
+    if budget == "head":
         select = api.thrift_select_blocks_head
         kmax = api._lib.load().thrift_select_head_kmax(w.S, w.S, w.bq, w.bk, int(w.causal))
     else:
@@ -182,8 +241,8 @@ def main():
     o = torch.empty_like(q)
 
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    if args.copy_mib:
-        copy_calibration(torch, dev, args.copy_mib)
+    if copy_mib:
+        copy_calibration(torch, dev, copy_mib)
 
     def step(rec=None):
         # Q and K each read once for their block means and FP4 codes; V
@@ -212,45 +271,76 @@ def main():
             rec[3].record()
         return (idx, cnt, idx2, cnt2) if tier8 else (idx, cnt, None, None)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    recs = [[ev() for _ in range(4)] for _ in range(args.steps)]
+    recs = [[ev() for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for r in recs:
         idx, cnt, idx2, cnt2 = step(r)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = 1e3 * wall / args.steps
-    q_ms = float(np.mean([r[0].elapsed_time(r[1]) for r in recs]))
-    sel_ms = float(np.mean([r[1].elapsed_time(r[2]) for r in recs]))
-    fwd_ms = float(np.mean([r[2].elapsed_time(r[3]) for r in recs]))
 
     idx_h, cnt_h = idx.cpu().numpy(), cnt.cpu().numpy()
     pairs = w.B * w.Hq * unmasked_pairs(w.S, w.causal)
-    f_alg = 4.0 * w.D * pairs
     p16 = promoted_pairs(idx_h, cnt_h, w.S, w.bq, w.bk, w.causal)
-    f16 = 4.0 * w.D * p16
     p8 = 0
     if tier8:  # the middle tier's pairs: in the joint list, not in the FP16 one
         p8 = promoted_pairs(idx2.cpu().numpy(), cnt2.cpu().numpy(), w.S, w.bq, w.bk, w.causal) - p16
-    f8 = 4.0 * w.D * p8
-    f4 = f_alg - f16 - f8
-    # the middle tier runs on the fp16 matrix cores (MXFP8 decoded exactly to fp16)
-    t_roof = f4 / P_FP4 + (f16 + f8) / P_FP16
-    peak_mixed = f_alg / t_roof
-    achieved = f_alg / (fwd_ms * 1e-3)
-    value = f_alg / (ms_step * 1e-3) / 1e12
+    return {"ms_step": 1e3 * wall / steps,
+            "q_ms": float(np.mean([r[0].elapsed_time(r[1]) for r in recs])),
+            "sel_ms": float(np.mean([r[1].elapsed_time(r[2]) for r in recs])),
+            "fwd_ms": float(np.mean([r[2].elapsed_time(r[3]) for r in recs])),
+            "pairs": pairs, "p16": p16, "p8": p8, "f_alg": 4.0 * w.D * pairs,
+            "qblocks_with_fp16": int((cnt_h > 0).sum()), "steps": steps, "warmup": warmup}
 
-    line = {
+
+def fmt_name(api, fmt, p_fmt):
+    return "mx" if fmt == api.THRIFT_MXFP4 else "nvfp4_mxp" if p_fmt is not None else "nvfp4"
+
+
+def forward_line(args, w, m, fmt, p_fmt, tier8, gen_s):
+    """The JSON line of one forward measurement m (measure_forward)."""
+    from fp16_attention_amd import api
+
+    name = fmt_name(api, fmt, p_fmt)
+    f_alg = m["f_alg"]
+    f16, f8 = 4.0 * w.D * m["p16"], 4.0 * w.D * m["p8"]
+    f4 = f_alg - f16 - f8
+    if fmt == api.THRIFT_MXFP4:
+        # the middle tier runs on the fp16 matrix cores (MXFP8 decoded exactly to fp16)
+        t_roof = f4 / P_FP4 + (f16 + f8) / P_FP16
+        note = ("F_alg / (F_fp4 / 10.1 PF + (F_fp8 + F_fp16) / 2.5 PF): the middle tier runs on the "
+                "fp16 matrix cores" if tier8 else
+                "F_alg / (F_fp4 / 10.1 PF + F_fp16 / 2.5 PF) for this launch's FP16 share")
+    else:
+        t_roof = f_alg / P_FP16
+        note = "F_alg / 2.5 PF: the NVFP4 FP4 path runs on the fp16 matrix cores (operands decoded exactly)"
+    peak = f_alg / t_roof
+    achieved = f_alg / (m["fwd_ms"] * 1e-3)
+    value = f_alg / (m["ms_step"] * 1e-3) / 1e12
+    roof = {
+        "bound": "mfma",
+        "achieved": round(achieved / 1e12, 2),
+        "peak": round(peak / 1e12, 2),
+        "unit": "TFLOP/s",
+        "frac": round(achieved / peak, 4),
+        "traffic": None if tier8 else measured_traffic(w.name, name),
+        "traffic_algorithmic": algorithmic_bytes(w, m["qblocks_with_fp16"], fmt),
+        "kernel": "attn_fwd_kernel",
+        "peak_note": note,
+    }
+    if not tier8 and p_fmt is None:
+        roof.update(measured_utilisation(w.name, name, m["pairs"]))
+    return {
         "metric": "attention-fwd TFLOPS + % of mixed FP4/FP16 MFMA roofline at S=32K, D=128, 5% top-k",
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
+        "steps": m["steps"],
+        "warmup": m["warmup"],
+        "ms_per_step": round(m["ms_step"], 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -261,38 +351,47 @@ def main():
             "workload": f"{w.name}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} S{w.S} D{w.D} "
                         f"{'causal' if w.causal else 'non-causal'} blocks {w.bq}x{w.bk} "
                         f"top-k {w.topk_bp / 100 if w.topk_count < 0 else w.topk_count}"
-                        f"{'%' if w.topk_count < 0 else ' per query block'} {args.fmt}"
+                        f"{'%' if w.topk_count < 0 else ' per query block'} {name}"
                         f"{', one budget per query head' if args.budget == 'head' else ''}"
                         f"{f', MXFP8 middle tier {tier8 / 100}% more' if tier8 else ''}",
             "global_batch": w.B, "seq_len": w.S, "parallelism": "none (1 GPU)",
         },
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(achieved / 1e12, 2),
-            "peak": round(peak_mixed / 1e12, 2),
-            "unit": "TFLOP/s",
-            "frac": round(achieved / peak_mixed, 4),
-            "traffic": None if tier8 else measured_traffic(w.name, args.fmt),
-            "traffic_algorithmic": algorithmic_bytes(w, int((cnt_h > 0).sum()), fmt),
-            "kernel": "attn_fwd_kernel",
-            "peak_note": ("F_alg / (F_fp4 / 10.1 PF + (F_fp8 + F_fp16) / 2.5 PF): the middle tier runs on the "
-                          "fp16 matrix cores" if tier8 else
-                          "F_alg / (F_fp4 / 10.1 PF + F_fp16 / 2.5 PF) for this launch's FP16 share"),
-        },
-        "breakdown_ms": {"means_and_quantize_qkv": round(q_ms, 4), "select_from_means": round(sel_ms, 4),
-                         "attention_fwd": round(fwd_ms, 4)},
-        "fp16_pair_share": round(p16 / pairs, 5),
-        **({"fp8_pair_share": round(p8 / pairs, 5)} if tier8 else {}),
+        "roofline": roof,
+        "breakdown_ms": {"means_and_quantize_qkv": round(m["q_ms"], 4), "select_from_means": round(m["sel_ms"], 4),
+                         "attention_fwd": round(m["fwd_ms"], 4)},
+        "fp16_pair_share": round(m["p16"] / m["pairs"], 5),
+        **({"fp8_pair_share": round(m["p8"] / m["pairs"], 5)} if tier8 else {}),
         "attention_fwd_tflops": round(achieved / 1e12, 2),
         "input_gen_s": round(gen_s, 1),
     }
-    if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w, d, fmt, args.budget, p_fmt, tier8)
-    s = json.dumps(line)
-    print(s, flush=True)
-    if args.out:
-        with open(args.out, "a") as f:
-            f.write(s + "\n")
+
+
+# (workload, top-k basis points or None for the workload's own, formats): one
+# line each in --all-configs mode
+ALL_CONFIGS = [("tiny", None), ("prefill", None)] + [("sweep", bp) for bp in (0, 100, 500, 2500, 10000)] + \
+              [("long", None), ("verylong", None), ("dit", None)]
+
+
+def run_all_configs(args):
+    """One JSON line per workload, format and top-k of the benchmark's
+    configurations (tiny, prefill, the top-k sweep at 0/1/5/25/100%, long,
+    very long, DiT-shaped), both FP4 formats; no CPU baseline."""
+    from fp16_attention_amd import api
+    from fp16_attention_amd import workloads as W
+
+    data = {}
+    for wname, bp in ALL_CONFIGS:
+        if wname not in data:  # one input set in host memory at a time (the sweep shares one)
+            data.clear()
+            t0 = time.time()
+            data[wname] = (W.generate(W.WORKLOADS[wname]), time.time() - t0)
+        d, gen_s = data[wname]
+        w = W.WORKLOADS[wname]
+        if bp is not None:
+            w = w.with_(topk_count=-1, topk_bp=bp)
+        for fmt in (api.THRIFT_MXFP4, api.THRIFT_NVFP4):
+            m = measure_forward(args, w, d, fmt, None, 0, "block", args.steps, args.warmup, 0)
+            emit(forward_line(args, w, m, fmt, None, 0, gen_s), args.out)
 
 
 def run_decode(args, w, d, gen_s):
