@@ -144,15 +144,16 @@ __device__ inline v16f mfma_fp4(v4i a, v4i b, v16f c, int sa, int sb) {
 __device__ inline float xlane32(float v) { return __shfl_xor(v, 32, kWave); }
 __device__ inline uint32_t xlane32u(uint32_t v) { return __shfl_xor(v, 32, kWave); }
 
-// 4 E2M1 codes (2 bytes) -> 4 fp16 values, times an fp16 factor (exact when
-// the factor has at most 4 significant bits and the products stay normal).
-__device__ inline v4h fp4x4_to_h(uint32_t codes16, _Float16 f) {
-  v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes16, 1.0f, 0);
-  v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes16, 1.0f, 1);
-  v2h ff = {f, f};
-  a = a * ff;
-  b = b * ff;
-  return v4h{a.x, a.y, b.x, b.y};
+// 8 E2M1 codes (one dword, low nibble first) -> 8 fp16 values, times an
+// fp16 factor (exact when the factor has at most 4 significant bits and the
+// products stay normal).
+__device__ inline v8h fp4x8_to_h(uint32_t cw, _Float16 f) {
+  const v2h ff = {f, f};
+  const v2h a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * ff;
+  const v2h b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * ff;
+  const v2h c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * ff;
+  const v2h d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * ff;
+  return v8h{a.x, a.y, b.x, b.y, c.x, c.y, d.x, d.y};
 }
 
 // K tiles are stored in LDS in krow's read order (key krow(mt, m) at row
@@ -207,15 +208,17 @@ __device__ inline bool tile_unit(RowState<D>& st, float mtc, float lk) {
   return live;
 }
 
-// Causal / tail mask: keys past the query row or past S become -inf.
+// Causal / tail mask: keys past the query row or past S become -inf.  A
+// lane's 32 keys are consecutive (key_of), so both conditions are one
+// threshold on the element index: one compare and one select per element.
 __device__ inline void mask_tile(v16f s[2], int key0, int qrow, int S, int causal, int hi) {
+  const int last = causal && qrow < S - 1 ? qrow : S - 1;  // the last key the row sees
+  const int lim = last - (key0 + key_of(0, 0, hi));       // elements past lim are masked
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      int key = key0 + key_of(mt, i, hi);
-      if (key >= S || (causal && key > qrow)) s[mt][i] = -INFINITY;
-    }
+    for (int i = 0; i < 16; ++i)
+      if (mt * 16 + i > lim) s[mt][i] = -INFINITY;
 }
 
 __device__ inline float max16(const v16f& v) {
@@ -440,7 +443,7 @@ __device__ inline void fp4_nv_softmax_pv(RowState<D>& st, v16f s[2], const char*
     v2s_t sb = {0, 0};
     sb = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(sb, fminf(gv * (1.0f / 6.0f), 448.0f), 0.0f, 1.0f, false);
     const float s2 = e4m3_to_float((uint32_t)sb[0] & 0xFF);
-    const float k = s2 > 0.0f ? 2688.0f / s2 : 0.0f;
+    const float k = nv_p_factor(s2);
     const _Float16 s2h = (_Float16)s2;  // exact: E4M3 has 4 significant bits
 #pragma unroll
     for (int h = 0; h < 2; ++h) {  // 8 keys per P^T operand
@@ -450,9 +453,7 @@ __device__ inline void fp4_nv_softmax_pv(RowState<D>& st, v16f s[2], const char*
       cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[o + 2] * k, v[o + 3] * k, 1.0f, 1);
       cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[o + 4] * k, v[o + 5] * k, 1.0f, 2);
       cw = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(cw, v[o + 6] * k, v[o + 7] * k, 1.0f, 3);
-      v4h lo = fp4x4_to_h(cw & 0xFFFFu, s2h);
-      v4h hi4 = fp4x4_to_h(cw >> 16, s2h);
-      pB[g * 2 + h] = v8h{lo.x, lo.y, lo.z, lo.w, hi4.x, hi4.y, hi4.z, hi4.w};
+      pB[g * 2 + h] = fp4x8_to_h(cw, s2h);
     }
   }
   pv_f16<D>(st, (const _Float16*)(stage + Lds<D>::VT), pB, lane);
@@ -865,9 +866,7 @@ struct Nv4Stager {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {  // 8 elements per dword; dwords 0-1 group 0, 2-3 group 1
       const _Float16 f = q < 2 ? f0 : f1;
-      v4h lo = fp4x4_to_h((uint32_t)codes[q] & 0xFFFFu, f);
-      v4h hi = fp4x4_to_h((uint32_t)codes[q] >> 16, f);
-      *(v8h*)(dst + q * 8) = v8h{lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      *(v8h*)(dst + q * 8) = fp4x8_to_h((uint32_t)codes[q], f);
     }
   }
 
@@ -1077,8 +1076,7 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_fwd_kernel(AttnArgs a) {
         if (qvalid) {
           uint32_t cw = *(const uint32_t*)(a.q4c + qoff * (D / 2) + kk * 8 + hi * 4);
           _Float16 f = (_Float16)e4m3_to_float(a.q4s[qoff * (D / 16) + kk]);
-          v4h lo = fp4x4_to_h(cw & 0xFFFFu, f), h4 = fp4x4_to_h(cw >> 16, f);
-          qh[kk] = v8h{lo.x, lo.y, lo.z, lo.w, h4.x, h4.y, h4.z, h4.w};
+          qh[kk] = fp4x8_to_h(cw, f);
         }
       }
       const float c = a.sm_log2 * a.q4t[bhq] * a.k4t[bhk];
@@ -1403,8 +1401,7 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void decode_nv4_kernel(DecodeArg
     if (col_ok) {
       const uint32_t cw = *(const uint32_t*)(a.q4c + qoff * (D / 2) + kk * 8 + hi * 4);
       const _Float16 f = (_Float16)e4m3_to_float(a.q4s[qoff * (D / 16) + kk]);
-      const v4h lo = fp4x4_to_h(cw & 0xFFFFu, f), h4 = fp4x4_to_h(cw >> 16, f);
-      qh[kk] = v8h{lo.x, lo.y, lo.z, lo.w, h4.x, h4.y, h4.z, h4.w};
+      qh[kk] = fp4x8_to_h(cw, f);
     }
   }
   const float c = a.sm_log2 * a.q4t[(size_t)b * a.Hq + hq] * a.k4t[bhk];

@@ -586,7 +586,7 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
           if (hi == 0) {
             float* fa = (float*)(smem + L::FA) + (w * 2 + g) * 32;
             float* fh = (float*)(smem + L::FH) + (w * 2 + g) * 32;
-            fa[qperm(r32)] = on ? exp2_fast(Lq - tml) * (2688.0f / s2) : 0.0f;
+            fa[qperm(r32)] = on ? exp2_fast(Lq - tml) * nv_p_factor(s2) : 0.0f;
             fh[qperm(r32)] = on ? s2 * exp2_fast(tml - Lq) * (1.0f / 2688.0f) : 0.0f;
           }
         }

@@ -75,11 +75,14 @@ __device__ inline float pair_max(float v) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// E4M3 byte -> value (finite codes; the sign bit of a block scale is 0).
-__device__ inline float e4m3_to_float(uint32_t b) {
-  const uint32_t e = (b >> 3) & 0xF, m = b & 7;
-  return e == 0 ? (float)m * 0x1p-9f : __uint_as_float(((e + 120) << 23) | (m << 20));
-}
+// E4M3 byte -> value by the hardware conversion (OCP E4M3, exact; block
+// scales are finite and non-negative).
+__device__ inline float e4m3_to_float(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
+
+// 2688 / s2 for an NVFP4 level-2 block scale s2 (0 for s2 = 0), through the
+// hardware reciprocal: within 2 u of the quotient (u = 2^-24) for every
+// positive E4M3 value, which the arithmetic probes check exhaustively.
+__device__ inline float nv_p_factor(float s2) { return s2 > 0.0f ? 2688.0f * __builtin_amdgcn_rcpf(s2) : 0.0f; }
 
 // Key (within a 64-key tile) that A-operand row m of 32x32 S^T tile mt
 // reads.  The MFMA output puts row (i/4)*8 + hi*4 + i%4 in register i of a

@@ -3,7 +3,9 @@
 //  - the block-scaled FP4 matrix instruction v_mfma_scale_f32_32x32x64_f8f6f4
 //    (E2M1 operands, E8M0 block scales, fp32 accumulator C);
 //  - the fp16 matrix instruction v_mfma_f32_32x32x16_f16;
-//  - the hardware exp2 (v_exp_f32).
+//  - the hardware exp2 (v_exp_f32);
+//  - NVFP4's level-2 factor 2688 / s2 as the kernels form it, 2688 times the
+//    hardware reciprocal (v_rcp_f32) of the E4M3 block scale s2.
 // One wavefront per matrix launch; every access is within the buffers the
 // caller sizes from ntest (64 lanes x ntest tests).  Built with the library
 // (fp16_attention_amd/build.py) into tests/libarith_probe.so; not part of it.
@@ -59,6 +61,17 @@ extern "C" int arith_probe_fp4(const void* a, const void* b, const void* sa, con
 extern "C" int arith_probe_f16(const void* a, const void* b, void* c, int ntest, hipStream_t stream) {
   if (ntest < 1) return 1;
   probe_f16<<<1, 64, 0, stream>>>((const v8h*)a, (const v8h*)b, (float*)c, ntest);
+  return hipGetLastError() == hipSuccess ? 0 : 2;
+}
+
+__global__ void probe_nv_factor(const float* x, float* y, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) y[i] = 2688.0f * __builtin_amdgcn_rcpf(x[i]);
+}
+
+extern "C" int arith_probe_nv_factor(const void* x, void* y, int n, hipStream_t stream) {
+  if (n < 1) return 1;
+  probe_nv_factor<<<(n + 255) / 256, 256, 0, stream>>>((const float*)x, (float*)y, n);
   return hipGetLastError() == hipSuccess ? 0 : 2;
 }
 

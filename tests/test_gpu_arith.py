@@ -36,6 +36,7 @@ def _lib():
     L.arith_probe_fp4.argtypes = [P] * 5 + [I, P]
     L.arith_probe_f16.argtypes = [P] * 3 + [I, P]
     L.arith_probe_exp2.argtypes = [P, P, I, P]
+    L.arith_probe_nv_factor.argtypes = [P, P, I, P]
     return L
 
 
@@ -160,3 +161,27 @@ def test_exp2():
     print(f"exp2: max error {err:.3f} ulp", flush=True)
     assert err <= 1.0 and err >= 0.25
     assert np.all(y[~normal] <= 2.0 ** -126)  # results below the normal range flush toward zero
+
+
+def test_nvfp4_level2_factor():
+    """The NVFP4 P quantisation scales a probability by 2688 / s2 (s2 the
+    group's E4M3 block scale), formed as 2688 times the hardware reciprocal.
+    The model allows that value four roundings in all (u each: the factor
+    2688, the reciprocal, the products); the factor must stay within two of
+    them, checked over every positive finite E4M3 value."""
+    import torch
+
+    vals = []
+    for b in range(1, 127):  # positive finite E4M3 (0x7F is NaN)
+        e, m = (b >> 3) & 0xF, b & 7
+        vals.append(m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    x = np.array(vals, np.float32)
+    xd = _dev(x)
+    yd = torch.empty_like(xd)
+    assert _lib().arith_probe_nv_factor(_ptr(xd), _ptr(yd), len(x), _stream()) == 0
+    torch.cuda.synchronize()
+    y = yd.cpu().numpy().astype(np.float64)
+    ex = 2688.0 / x.astype(np.float64)
+    err = float((np.abs(y - ex) / ex).max() / U)
+    print(f"2688 * rcp(s2): max error {err:.3f} u over all {len(x)} positive E4M3 values", flush=True)
+    assert err <= 2.0
