@@ -213,6 +213,24 @@ def main():
     emit(line, args.out)
 
 
+WARM_S = 0.3  # --all-configs: each line's warm-up runs at least this long
+
+
+def warm_up(step, n, torch, min_s=0.0):
+    """n untimed steps, continued until min_s seconds have passed (the GPU
+    raises its clocks over the first tens of milliseconds of work, which a
+    few steps of a small workload do not cover)."""
+    t0 = time.perf_counter()
+    done = 0
+    while done < n or time.perf_counter() - t0 < min_s:
+        step()
+        done += 1
+        if done >= n:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+    return done
+
+
 def emit(line, out=None):
     s = json.dumps(line)
     print(s, flush=True)
@@ -221,7 +239,7 @@ def emit(line, out=None):
             f.write(s + "\n")
 
 
-def measure_forward(args, w, d, fmt, p_fmt, tier8, budget, steps, warmup, copy_mib):
+def measure_forward(args, w, d, fmt, p_fmt, tier8, budget, steps, warmup, copy_mib, min_warm_s=0.0):
     """Time `steps` forward steps (after `warmup`) of workload w on input d:
     means + FP4 codes of Q and K in one pass, V's codes, selection, the
     attention forward.  Returns the timings (ms) and pair counts."""
@@ -271,9 +289,7 @@ def measure_forward(args, w, d, fmt, p_fmt, tier8, budget, steps, warmup, copy_m
             rec[3].record()
         return (idx, cnt, idx2, cnt2) if tier8 else (idx, cnt, None, None)
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
+    nwarm = warm_up(step, warmup, torch, min_warm_s)
     recs = [[ev() for _ in range(4)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -293,7 +309,7 @@ def measure_forward(args, w, d, fmt, p_fmt, tier8, budget, steps, warmup, copy_m
             "sel_ms": float(np.mean([r[1].elapsed_time(r[2]) for r in recs])),
             "fwd_ms": float(np.mean([r[2].elapsed_time(r[3]) for r in recs])),
             "pairs": pairs, "p16": p16, "p8": p8, "f_alg": 4.0 * w.D * pairs,
-            "qblocks_with_fp16": int((cnt_h > 0).sum()), "steps": steps, "warmup": warmup}
+            "qblocks_with_fp16": int((cnt_h > 0).sum()), "steps": steps, "warmup": warmup, "warmup_run": nwarm}
 
 
 def fmt_name(api, fmt, p_fmt):
@@ -390,8 +406,10 @@ def run_all_configs(args):
         if bp is not None:
             w = w.with_(topk_count=-1, topk_bp=bp)
         for fmt in (api.THRIFT_MXFP4, api.THRIFT_NVFP4):
-            m = measure_forward(args, w, d, fmt, None, 0, "block", args.steps, args.warmup, 0)
-            emit(forward_line(args, w, m, fmt, None, 0, gen_s), args.out)
+            m = measure_forward(args, w, d, fmt, None, 0, "block", args.steps, args.warmup, 0, WARM_S)
+            line = forward_line(args, w, m, fmt, None, 0, gen_s)
+            line["warmup_run"] = m["warmup_run"]  # at least WARM_S seconds of warm-up steps
+            emit(line, args.out)
 
 
 def run_decode(args, w, d, gen_s):
@@ -433,8 +451,7 @@ def run_decode(args, w, d, gen_s):
             rec[2].record()
         return idx, cnt
 
-    for _ in range(args.warmup):
-        step()
+    warm_up(step, args.warmup, torch)
     recs = [[ev() for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -562,9 +579,7 @@ def run_backward(args, w, d, gen_s):
         return grads
 
     hp()
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    warm_up(step, args.warmup, torch)
     hp_recs = [[ev(), ev()] for _ in range(3)]
     for r in hp_recs:
         r[0].record()
