@@ -208,6 +208,14 @@ __device__ inline bool tile_unit(RowState<D>& st, float mtc, float lk) {
   return live;
 }
 
+// Whether some row of the wave keeps the tile (tile_unit's test).  A tile
+// that every row drops adds exactly nothing (its probabilities are all 0 and
+// the state's unit does not move), so the wave skips the rest of it.
+template <int D>
+__device__ inline bool wave_live(const RowState<D>& st, float mtc) {
+  return __builtin_amdgcn_ballot_w64(mtc > st.mrun - kDead) != 0;
+}
+
 // Causal / tail mask: keys past the query row or past S become -inf.  A
 // lane's 32 keys are consecutive (key_of), so both conditions are one
 // threshold on the element index: one compare and one select per element.
@@ -295,6 +303,7 @@ __device__ inline void softmax_pv_mx(RowState<D>& st, v16f s[2], const MxVOps<D>
   const float gmax = fmaxf(max16(s[0]), max16(s[1]));
   const float tmax = pair_max(gmax);
   const float mtc = tmax * c;
+  if (!wave_live<D>(st, mtc)) return;
   const float nm = tile_unit<D>(st, mtc, -0.0f) ? -mtc : -INFINITY;  // dead tile: every p = 0
 
   // probabilities relative to the tile maximum, unquantised row sum
@@ -380,6 +389,7 @@ __device__ inline void fp16_softmax_pv(RowState<D>& st, v16f s[2], const _Float1
   if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
   // probabilities relative to the tile maximum (level 1), rounded to fp16
   const float mtc = pair_max(fmaxf(max16(s[0]), max16(s[1]))) * c;
+  if (!wave_live<D>(st, mtc)) return;
   const float nm = tile_unit<D>(st, mtc, -0.0f) ? -mtc : -INFINITY;
   float lsum = -0.0f;  // x + -0 folds to x
   v8h pB[4];
@@ -420,6 +430,7 @@ __device__ inline void fp4_nv_softmax_pv(RowState<D>& st, v16f s[2], const char*
   const float gm0 = max16(s[0]), gm1 = max16(s[1]);  // this lane's two 16-key groups
   const float tmax = pair_max(fmaxf(gm0, gm1));      // the query's tile maximum (level 1)
   const float mtc = tmax * c;
+  if (!wave_live<D>(st, mtc)) return;
   const float nm = tile_unit<D>(st, mtc, lk) ? -mtc : -INFINITY;
   float lsum = -0.0f;  // x + -0 folds to x
 #pragma unroll
@@ -474,6 +485,7 @@ __device__ inline void fp4_nvmxp_tile(RowState<D>& st, const char* stage, const 
   const float gmax = fmaxf(max16(s[0]), max16(s[1]));
   const float tmax = pair_max(gmax);
   const float mtc = tmax * c;
+  if (!wave_live<D>(st, mtc)) return;
   const float nm = tile_unit<D>(st, mtc, lk) ? -mtc : -INFINITY;
   float lsum = -0.0f;  // x + -0 folds to x
 #pragma unroll
@@ -567,6 +579,7 @@ __device__ inline void fp8_tile(RowState<D>& st, const char* stage, const v8h* q
   const float gmax = fmaxf(max16(s[0]), max16(s[1]));
   const float tmax = pair_max(gmax);  // level 1: the tile maximum
   const float mtc = tmax * c;
+  if (!wave_live<D>(st, mtc)) return;
   const float nm = tile_unit<D>(st, mtc, -0.0f) ? -mtc : -INFINITY;
   float lsum = -0.0f;  // x + -0 folds to x
 #pragma unroll
