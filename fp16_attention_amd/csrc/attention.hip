@@ -380,19 +380,20 @@ __device__ inline void pv_f16(RowState<D>& st, const _Float16* vt, const v8h* pB
     }
 }
 
-// Promoted tile after its scores: mask, probabilities rounded to fp16, times
-// fp16 V^T (vt: D rows of Lds<D>::VROWH halves).
+// Promoted tile after its scores: mask, probabilities relative to the tile
+// maximum rounded to fp16 (pB, the P^T operand: step st holds keys
+// hi*32 + 8*st + u), the row sum; false when every row of the wave drops
+// the tile (nothing to add).
 template <int D>
-__device__ inline void fp16_softmax_pv(RowState<D>& st, v16f s[2], const _Float16* vt, float c, int key0,
-                                       int qrow, int S, int causal, bool need_mask, int lane) {
+__device__ inline bool fp16_probs(RowState<D>& st, v16f s[2], v8h pB[4], float c, int key0, int qrow, int S,
+                                  int causal, bool need_mask, int lane) {
   const int hi = lane >> 5;
   if (need_mask) mask_tile(s, key0, qrow, S, causal, hi);
   // probabilities relative to the tile maximum (level 1), rounded to fp16
   const float mtc = pair_max(fmaxf(max16(s[0]), max16(s[1]))) * c;
-  if (!wave_live<D>(st, mtc)) return;
+  if (!wave_live<D>(st, mtc)) return false;
   const float nm = tile_unit<D>(st, mtc, -0.0f) ? -mtc : -INFINITY;
   float lsum = -0.0f;  // x + -0 folds to x
-  v8h pB[4];
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -402,16 +403,16 @@ __device__ inline void fp16_softmax_pv(RowState<D>& st, v16f s[2], const _Float1
       pB[mt * 2 + i / 8][i % 8] = (_Float16)p;
     }
   st.l += lsum;
-  pv_f16<D>(st, vt, pB, lane);
+  return true;
 }
 
-// Promoted tile: fp16 scores, probabilities rounded to fp16.
+// Promoted tile after its scores: mask, probabilities rounded to fp16, times
+// fp16 V^T (vt: D rows of Lds<D>::VROWH halves).
 template <int D>
-__device__ inline void fp16_tile(RowState<D>& st, const char* stage, const v8h* qh, float c, int key0,
-                                 int qrow, int S, int causal, bool need_mask, int lane) {
-  v16f s[2];
-  qk_f16<D>(s, stage, qh, lane);
-  fp16_softmax_pv<D>(st, s, (const _Float16*)(stage + Lds<D>::VT), c, key0, qrow, S, causal, need_mask, lane);
+__device__ inline void fp16_softmax_pv(RowState<D>& st, v16f s[2], const _Float16* vt, float c, int key0,
+                                       int qrow, int S, int causal, bool need_mask, int lane) {
+  v8h pB[4];
+  if (fp16_probs<D>(st, s, pB, c, key0, qrow, S, causal, need_mask, lane)) pv_f16<D>(st, vt, pB, lane);
 }
 
 // NVFP4 FP4 tile: scores from the dequantised fp16 stage, P quantised in two
@@ -709,72 +710,111 @@ struct MxDma {
   }
 };
 
-// fp16 tile of the promoted path: K row-major (rows in MFMA read order), V
-// transposed into V^T.  The transpose goes through registers: a thread takes
-// two consecutive keys x 8 channels and writes eight 4-byte (key pair) words,
-// so a wavefront's stores hit consecutive words of one V^T row.
-template <int D, int NT>
-struct F16Stager {
-  static constexpr int NK = kBk * D / 8;        // 16-byte chunks of K
-  static constexpr int NV = (kBk / 2) * (D / 8);  // (key pair, 8 channels) items of V
-  static constexpr int PK = (NK + NT - 1) / NT, PV = (NV + NT - 1) / NT;
-  v8h kr[PK], v0[PV], v1[PV];
+// ---- the FP16 path's pipelined stage ------------------------------------------
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+//
+// K and V rows of a promoted block go from HBM straight into LDS
+// (buffer_load_dwordx4 ... lds: no staging registers, no LDS stores).  Two K
+// buffers and one V buffer: while a block's scores and probabilities are
+// computed, the next block's V and the one after's K are in flight.  Each
+// buffer is chunk-column-major: 16-byte chunk c of row r at c * CS + r * 16,
+// one direct wave load per chunk column (K rows in MFMA read order, row r
+// holding key krow(r >> 5, r & 31); V rows in key order).  The column stride
+// CS = 1024 + 64 bytes staggers the columns by 64 bytes across the banks, so
+// that both the K reads (16 rows of one chunk per half-wave) and the
+// transposed V reads (ds_read_b64_tr_b16: per 16 lanes, 4 keys of 16
+// channels, two chunk columns) are free of bank conflicts, and every address
+// is a per-lane base plus an immediate.  The buffers take the ring's memory,
+// free once the FP4 pass is done.
+template <int D>
+struct F16Pipe {
+  static constexpr int CS = 1024 + 64;         // bytes per chunk column (64 rows + stagger)
+  static constexpr int TILE = (D / 8) * CS;    // one K or V block
+  static constexpr int KB = 0;                 // [2][TILE]
+  static constexpr int VB = 2 * TILE;          // [TILE]
+  static constexpr int SIZE = 3 * TILE;
+};
 
-  __device__ void load(const AttnArgs& a, size_t bhk, int j, int t) {
-#pragma unroll
-    for (int p = 0; p < PK; ++p) {
-      int c = t + p * NT;
-      kr[p] = v8h{};
-      if (c < NK) {
-        int row = c / (D / 8), col = (c % (D / 8)) * 8, key = j * kBk + row;
-        if (key < a.S) kr[p] = *(const v8h*)(a.k16 + (bhk * a.S + key) * D + col);
-      }
-    }
-#pragma unroll
-    for (int p = 0; p < PV; ++p) {
-      int c = t + p * NT;
-      v0[p] = v8h{};
-      v1[p] = v8h{};
-      if (c < NV) {
-        int kp = c % (kBk / 2), col = (c / (kBk / 2)) * 8, key = j * kBk + 2 * kp;
-        const _Float16* src = a.v16 + (bhk * a.S + key) * D + col;
-        if (key < a.S) v0[p] = *(const v8h*)src;
-        if (key + 1 < a.S) v1[p] = *(const v8h*)(src + D);
-      }
-    }
+// This wave's share of one block's direct loads: chunk columns w*NI ..
+// w*NI + NI - 1 of the K or V buffer, one wave load (64 rows x 16 bytes) each.
+template <int D, int NW>
+struct F16Dma {
+  using P = F16Pipe<D>;
+  static constexpr int NI = (D / 8) / NW;  // chunk columns per wave and tensor
+  static_assert(NI * NW == D / 8, "chunk columns must split evenly over the waves");
+  static constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+  __amdgpu_buffer_rsrc_t kr, vr;                 // this head's fp16 K and V; rows past S read as zeros
+  uint32_t koff, voff;                           // this lane's row: key krow(lane) of K, key lane of V
+  int w;
+
+  __device__ F16Dma(const AttnArgs& a, size_t bhk, int w_, int lane) : w(w_) {
+    const int bytes = a.S * D * 2;
+    kr = __builtin_amdgcn_make_buffer_rsrc((void*)(a.k16 + bhk * a.S * D), 0, bytes, kRsrcWord3);
+    vr = __builtin_amdgcn_make_buffer_rsrc((void*)(a.v16 + bhk * a.S * D), 0, bytes, kRsrcWord3);
+    koff = krow(lane >> 5, lane & 31) * (D * 2) + w * NI * 16;
+    voff = lane * (D * 2) + w * NI * 16;
   }
-
-  __device__ void store(char* stage, int t) const {
-    using L = Lds<D>;
-    _Float16* kh = (_Float16*)(stage + L::KH);
-    _Float16* vt = (_Float16*)(stage + L::VT);
+  __device__ static __attribute__((address_space(3))) void* lds(char* p) {
+    return (__attribute__((address_space(3))) void*)p;
+  }
+  __device__ void issue_k(char* buf, int j) const {
 #pragma unroll
-    for (int p = 0; p < PK; ++p) {
-      int c = t + p * NT;
-      if (c < NK) {
-        int row = c / (D / 8), col = (c % (D / 8)) * 8;
-        *(v8h*)(kh + kslot(row) * L::KROWH + col) = kr[p];
-      }
-    }
+    for (int k = 0; k < NI; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, lds(buf + (w * NI + k) * P::CS), 16,
+                                               koff + j * (kBk * D * 2) + k * 16, 0, 0, 0);
+  }
+  __device__ void issue_v(char* buf, int j) const {
 #pragma unroll
-    for (int p = 0; p < PV; ++p) {
-      int c = t + p * NT;
-      if (c < NV) {
-        int kp = c % (kBk / 2), col = (c / (kBk / 2)) * 8;
-        const v4i a = __builtin_bit_cast(v4i, v0[p]), b = __builtin_bit_cast(v4i, v1[p]);
-        uint32_t* dst = (uint32_t*)(vt + col * L::VROWH + 2 * kp);
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {  // channels 2w, 2w+1: (key, key+1) half pairs
-          dst[(2 * w) * (L::VROWH / 2)] = __builtin_amdgcn_perm((uint32_t)b[w], (uint32_t)a[w], 0x05040100u);
-          dst[(2 * w + 1) * (L::VROWH / 2)] = __builtin_amdgcn_perm((uint32_t)b[w], (uint32_t)a[w], 0x07060302u);
-        }
-      }
-    }
+    for (int k = 0; k < NI; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, lds(buf + (w * NI + k) * P::CS), 16,
+                                               voff + j * (kBk * D * 2) + k * 16, 0, 0, 0);
   }
 };
 
+// S^T = K Q^T from a K buffer: lane (r32, hi) reads chunk kk*2 + hi of row
+// mt*32 + r32.
+template <int D>
+__device__ inline void qk_f16p(v16f s[2], const char* kb, const v8h* qh, int lane) {
+  using P = F16Pipe<D>;
+  const int hi = lane >> 5, r32 = lane & 31;
+  const char* base = kb + hi * P::CS + r32 * 16;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+    s[mt] = v16f{};
+#pragma unroll
+    for (int kk = 0; kk < D / 16; ++kk)
+      s[mt] = mfma_f16(*(const v8h*)(base + kk * 2 * P::CS + mt * 32 * 16), qh[kk], s[mt]);
+  }
+}
+
+// O^T += V^T P^T with the V^T operand read transposed from the V buffer:
+// ds_read_b64_tr_b16 gives lane i of each 16 lanes element i % 4 of the
+// 8-byte pieces that lanes i / 4, i / 4 + 4, i / 4 + 8, i / 4 + 12 address;
+// so lane r addresses key key0 + r / 4, channels d0 + 4 (r % 4) .. + 3, and
+// lane i receives channel d0 + i of keys key0 .. key0 + 3.  In step st this
+// lane supplies keys hi*32 + 8*st + u of channel dt*32 + r32.
+template <int D>
+__device__ inline void pv_f16p(RowState<D>& st, const char* vb, const v8h* pB, int lane) {
+  using P = F16Pipe<D>;
+  const int hi = lane >> 5, r32 = lane & 31, r = r32 & 15;
+  const int col = (r32 >> 4) * 16 + 4 * (r & 3);  // channel within a 32-channel tile
+  const char* base = vb + (col >> 3) * P::CS + (hi * 32 + (r >> 2)) * 16 + (col & 7) * 2;
+#pragma unroll
+  for (int stp = 0; stp < 4; ++stp)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) {
+      const char* q = base + dt * 4 * P::CS + stp * 8 * 16;
+      const v4h lo = __builtin_bit_cast(
+          v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(char*)q));
+      const v4h up = __builtin_bit_cast(
+          v4h, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4s_t*)(char*)(q + 64)));
+      const v8h av = {lo.x, lo.y, lo.z, lo.w, up.x, up.y, up.z, up.w};
+      st.acc[dt] = mfma_f16(av, pB[stp], st.acc[dt]);
+    }
+}
+
 // MXFP8 tile of key block j decoded to the fp16 stage (K rows at kslot, V^T
-// rows), as F16Stager lays it out: each thread takes 16-byte chunks of codes
+// rows, the fp16 stage's layout): each thread takes 16-byte chunks of codes
 // with the E8M0 byte of their group.  K rows past S read as zeros; V^T rows
 // are padded to Sp with zeros by the quantiser.
 template <int D, int NT>
@@ -1156,26 +1196,55 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_fwd_kernel(AttnArgs a) {
   }
 
   // ---------------- FP16 path: promoted blocks only ----------------
+  // Pipelined through F16Pipe's buffers (the ring's memory: the passes before
+  // ended with a barrier).  Block p: its scores and probabilities (K[p % 2]),
+  // a barrier (V_p in LDS), PV, a barrier (every wave done with V and K[p % 2];
+  // K_{p+1} in LDS), then the loads of V_{p+1} and K_{p+2} go out, in flight
+  // during block p+1's scores and probabilities.  Every wave waits for its own
+  // direct loads before each barrier.
   if (ncnt > 0) {
+    using FP = F16Pipe<D>;
+    static_assert(FP::SIZE <= L::RING, "the fp16 pipeline's buffers fit in the ring");
     v8h qh[D / 16];
     const size_t qoff = ((size_t)bhq * S + qrow) * D + hi * 8;
 #pragma unroll
     for (int kk = 0; kk < D / 16; ++kk) qh[kk] = qvalid ? *(const v8h*)(a.q16 + qoff + kk * 16) : v8h{};
-    F16Stager<D, NT> stg;
-    for (int p = 0; p < ncnt; ++p) {
-      const int j = prom[p];
-      const int jc = j >= 0 && j < nvalid ? j : -1;
-      if (jc >= 0) stg.load(a, bhk, jc, t);
-      if (jc >= 0) stg.store(smem, t);
-      __syncthreads();
-      if (jc >= 0) {
-        const int key0 = jc * kBk;
-        const bool active = !a.causal || key0 <= q0 + 31;
-        const bool need_mask = (a.causal && key0 + kBk - 1 > q0) || key0 + kBk > S;
-        if (active)
-          fp16_tile<D>(st, smem, qh, a.sm_log2, key0, qrow, S, a.causal, need_mask, lane);
+    F16Dma<D, NW> fd(a, bhk, w, lane);
+    auto prom_j = [&](int p) {
+      const int j = p < ncnt ? prom[p] : -1;
+      return j >= 0 && j < nvalid ? j : -1;
+    };
+    auto kbuf = [&](int p) { return smem + FP::KB + (p & 1) * FP::TILE; };
+    {
+      const int j0 = prom_j(0), j1 = prom_j(1);
+      if (j0 >= 0) {
+        fd.issue_k(kbuf(0), j0);
+        fd.issue_v(smem + FP::VB, j0);
       }
+      if (j1 >= 0) fd.issue_k(kbuf(1), j1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
+    }
+    for (int p = 0; p < ncnt; ++p) {
+      const int jc = prom_j(p);
+      const int key0 = jc * kBk;
+      const bool active = jc >= 0 && (!a.causal || key0 <= q0 + 31);
+      const bool need_mask = (a.causal && key0 + kBk - 1 > q0) || key0 + kBk > S;
+      v8h pB[4];
+      bool live = false;
+      if (active) {
+        v16f sc[2];
+        qk_f16p<D>(sc, kbuf(p), qh, lane);
+        live = fp16_probs<D>(st, sc, pB, a.sm_log2, key0, qrow, S, a.causal, need_mask, lane);
+      }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // V_p in LDS
+      if (live) pv_f16p<D>(st, smem + FP::VB, pB, lane);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // V and K[p % 2] free; K_{p+1} in LDS
+      const int jn = prom_j(p + 1), jn2 = prom_j(p + 2);
+      if (jn >= 0) fd.issue_v(smem + FP::VB, jn);
+      if (jn2 >= 0) fd.issue_k(kbuf(p), jn2);
     }
   }
 
