@@ -940,6 +940,103 @@ struct Nv4Stager {
   }
 };
 
+// NVFP4 FP4 pass through LDS twice: one block's codes and scales come by
+// direct loads into a raw buffer (a byte copy of the block's stretch of each
+// tensor: K codes, V^T codes, K scales, V^T scales, all contiguous per
+// block), are decoded from there into the fp16 stage, and the raw buffer
+// then takes the next block's loads while the current block is computed.
+// The raw buffer sits after the fp16 stage in the ring's memory.
+template <int D>
+struct NvRaw {
+  static constexpr int KC = Lds<D>::STAGE;        // [kBk][D/2]
+  static constexpr int VC = KC + kBk * D / 2;      // [D][32]
+  static constexpr int KS = VC + D * 32;           // [kBk][D/16]
+  static constexpr int VS = KS + kBk * D / 16;     // [D][4]
+  static constexpr int END = VS + D * 4;
+  static_assert(END <= Lds<D>::RING, "the raw buffer must fit the ring");
+  // wave loads per block: 1 KB of codes (64 lanes x 16 B) or 256 B of
+  // scales (64 lanes x 4 B) each
+  static constexpr int NCODE = D / 32;  // per tensor
+  static constexpr int NSC = D / 64;    // per tensor
+  static constexpr int NLOAD = 2 * NCODE + 2 * NSC;
+};
+
+template <int D, int NW>
+struct NvDma {
+  using R = NvRaw<D>;
+  static constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+  // this head's tensors; record counts end at their ends, so K rows past S
+  // read as zeros
+  __amdgpu_buffer_rsrc_t kc, ks, vc, vs;
+  int w, lane;
+
+  __device__ static __amdgpu_buffer_rsrc_t rsrc(const uint8_t* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kRsrcWord3);
+  }
+  __device__ static __attribute__((address_space(3))) void* lds(char* p) {
+    return (__attribute__((address_space(3))) void*)p;
+  }
+  __device__ NvDma(const AttnArgs& a, size_t bhk, int w_, int lane_)
+      : kc(rsrc(a.k4c + bhk * a.S * (D / 2), a.S * (D / 2))),
+        ks(rsrc(a.k4s + bhk * a.S * (D / 16), a.S * (D / 16))),
+        vc(rsrc(a.v4c + bhk * (a.Sp / 64) * D * 32, (a.Sp / 64) * D * 32)),
+        vs(rsrc(a.v4s + bhk * (a.Sp / 64) * D * 4, (a.Sp / 64) * D * 4)),
+        w(w_), lane(lane_) {}
+
+  // Wave w issues loads w, w + NW, ... of block j's NLOAD.
+  __device__ void issue(char* smem, int j) const {
+#pragma unroll
+    for (int g = 0; g < R::NLOAD; ++g) {
+      if (g % NW != w) continue;
+      if (g < R::NCODE)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kc, lds(smem + R::KC + g * 1024), 16,
+                                                 j * (kBk * D / 2) + g * 1024 + lane * 16, 0, 0, 0);
+      else if (g < 2 * R::NCODE)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vc, lds(smem + R::VC + (g - R::NCODE) * 1024), 16,
+                                                 j * (D * 32) + (g - R::NCODE) * 1024 + lane * 16, 0, 0, 0);
+      else if (g < 2 * R::NCODE + R::NSC)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ks, lds(smem + R::KS + (g - 2 * R::NCODE) * 256), 4,
+                                                 j * (kBk * D / 16) + (g - 2 * R::NCODE) * 256 + lane * 4, 0, 0,
+                                                 0);
+      else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vs, lds(smem + R::VS + (g - 2 * R::NCODE - R::NSC) * 256), 4,
+                                                 j * (D * 4) + (g - 2 * R::NCODE - R::NSC) * 256 + lane * 4, 0,
+                                                 0, 0);
+    }
+  }
+};
+
+// Raw buffer -> fp16 stage, in Nv4Stager's layout: thread t decodes 16-byte
+// chunks t, t + NT, ... of the K codes (row c / (D/32), 32 channels) and of
+// the V^T codes (row c / 2, 32 keys).
+template <int D, int NT>
+__device__ inline void nv_decode(char* smem, int t) {
+  using R = NvRaw<D>;
+  using L = Lds<D>;
+  using St = Nv4Stager<D, NT>;
+  _Float16* kh = (_Float16*)(smem + L::KH);
+  _Float16* vt = (_Float16*)(smem + L::VT);
+#pragma unroll
+  for (int p = 0; p < St::PK; ++p) {
+    const int c = t + p * NT;
+    if (c < St::NKC) {
+      const int row = c / (D / 32), col = c % (D / 32);
+      const v4i codes = *(const v4i*)(smem + R::KC + c * 16);
+      const uint32_t sc = *(const uint16_t*)(smem + R::KS + row * (D / 16) + col * 2);
+      St::expand(kh + kslot(row) * L::KROWH + col * 32, codes, sc);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < St::PV; ++p) {
+    const int c = t + p * NT;
+    if (c < St::NVC) {
+      const v4i codes = *(const v4i*)(smem + R::VC + c * 16);
+      const uint32_t sc = *(const uint16_t*)(smem + R::VS + c * 2);
+      St::expand(vt + (c / 2) * L::VROWH + (c % 2) * 32, codes, sc);
+    }
+  }
+}
+
 // ---- the kernel ----------------------------------------------------------------------
 
 // Work item of workgroup `id`.  Workgroups are dispatched round-robin over
@@ -1137,12 +1234,16 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_fwd_kernel(AttnArgs a) {
       const float sv = a.v4t[bhk];
       const float lk = FMT == THRIFT_NVFP4 ? log2f(sv) - log2f(2688.0f) : log2f(sv);
       const float ilk = FMT == THRIFT_NVFP4 ? 2688.0f / sv : 1.0f / sv;
-      Nv4Stager<D, NT> stg;
+      // the next block's codes arrive in the raw buffer while this one is computed
+      NvDma<D, NW> dma(a, bhk, w, lane);
+      if (jc < nvalid) dma.issue(smem, jc);
       while (jc < nvalid) {
         const int jn = next_fp4(jc + 1);
-        stg.load(a, bhk, jc, t);
-        stg.store(smem, t);
-        __syncthreads();
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        __syncthreads();  // the raw buffer holds block jc; the fp16 stage is free
+        nv_decode<D, NT>(smem, t);
+        __syncthreads();  // the stage holds block jc; the raw buffer is free
+        if (jn < nvalid) dma.issue(smem, jn);
         const int key0 = jc * kBk;
         const bool active = !a.causal || key0 <= q0 + 31;
         const bool need_mask = (a.causal && key0 + kBk - 1 > q0) || key0 + kBk > S;
@@ -1152,9 +1253,9 @@ __global__ __launch_bounds__(NW * 64, 3) void attn_fwd_kernel(AttnArgs a) {
           else
             fp4_nvmxp_tile<D>(st, smem, qh, c, lk, ilk, key0, qrow, S, a.causal, need_mask, lane);
         }
-        __syncthreads();
         jc = jn;
       }
+      __syncthreads();  // every wave is done with the stage
     }
   }
 

@@ -265,14 +265,13 @@ thrift_status thrift_cache_update(const void* k16, const void* v16, int B, int H
  *     groups):
  *       NVFP4: v = 2688 * 2^(t - tile max), per-16 E4M3 scale E4M3(max v / 6),
  *              E2M1 codes of v / scale;
- *       MXFP4: v = 2^(t - z), z an integer (the E8M0 scales absorb any power
- *              of two, so the codes do not depend on z), per-32 E8M0 scale
- *              from max v, E2M1 codes of v / 2^exponent;
+ *       MXFP4: v = 2^(t - tile max), per-32 E8M0 scale 2^(floor(log2 max v)
+ *              - 2), E2M1 codes of v / scale;
  *     then multiplied with the FP4 V.
  *  2. FP16 path, over the promoted blocks idx[.., :cnt] ascending (FP16 Q is
  *     read only for query blocks with cnt > 0, FP16 K/V only for promoted
- *     blocks): scores from fp16 Q and K, probabilities rounded to fp16 (on a
- *     power-of-two footing: 2^t to 11 significant bits), times fp16 V.
+ *     blocks): scores from fp16 Q and K, probabilities relative to the
+ *     tile maximum (2^(t - tile max)) rounded to fp16, times fp16 V.
  *  3. Both paths feed one online softmax (running max, running sum of the
  *     unquantised probabilities, fp32 accumulator); O = acc / sum.
  * Arguments:
@@ -326,7 +325,7 @@ thrift_status thrift_quantize_fp8(const void* x16, int B, int H, int S, int D, i
  * block that idx2[.., :cnt2] lists and idx[.., :cnt] does not runs, after the
  * FP4 path and before the FP16 path, ascending, with scores from the MXFP8 Q
  * and K, the probabilities quantised in two levels as on the MXFP4 path but
- * with E4M3 elements (v = 2^(t - z) with an integer z, E8M0 exponent
+ * with E4M3 elements (v = 2^(t - tile max), E8M0 exponent
  * floor(log2 max v) - 8 per 32 keys, E4M3 codes of v / 2^exponent), times the
  * MXFP8 V.  FP4 runs on every valid block neither list holds.  The
  * unquantised probabilities feed the row sum on all three tiers.
