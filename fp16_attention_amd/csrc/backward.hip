@@ -46,11 +46,11 @@ __device__ inline v8h ld8h(__amdgpu_buffer_rsrc_t rs, int off) {
 struct BwdArgs {
   const _Float16 *q16, *k16, *v16, *do16;  // [B,H,S,D]
   const _Float16 *qd, *kd;                 // FP4-decoded Q, K rows [B,H,S,D]
+  const _Float16* qds;                     // FP4-decoded Q times its slice scale (NVFP4) [B,Hq,S,D]
   const _Float16* vd;                      // FP4-decoded V rows [B,Hkv,Sp,D]
-  const _Float16 *qt, *qdt, *dot;          // transposed [B,Hq,D,Sp]
   const _Float16 *kt, *kdt, *vt, *vdt;     // transposed [B,Hkv,D,Sp]
   const uint32_t* prom;                    // promoted-block bits [B,Hq,nq,nkw]
-  const float *lse, *drow;                 // [B,Hq,S]
+  const float *lse, *drow, *lse2;          // [B,Hq,S]; lse2 = lse * log2(e)
   const float *tq, *tk, *tv;               // NVFP4 slice scales [B,H] (NULL for MXFP4)
   float* out;                              // row kernel: O' or dQ [B,Hq,S,D]
   float *dk, *dv;                          // [B,Hkv,S,D]
@@ -149,10 +149,11 @@ __global__ __launch_bounds__(256) void prom_bits_kernel(const int32_t* idx, cons
 }
 
 // Row term dO[r] . O'[r]: D/8 lanes per row (a 16-byte load of dO and two of
-// O' each), summed across those lanes; every lane reaches the shuffles.
+// O' each), summed across those lanes; every lane reaches the shuffles.  Also
+// the row's log-sum-exp in log2 units, lse[r] * log2(e).
 template <int D>
-__global__ __launch_bounds__(256) void row_term_kernel(const _Float16* do16, const float* ohp, size_t nrows,
-                                                       float* drow) {
+__global__ __launch_bounds__(256) void row_term_kernel(const _Float16* do16, const float* ohp, const float* lse,
+                                                       size_t nrows, float* drow, float* lse2) {
   constexpr int LPR = D / 8;  // lanes per row: 16 or 8, a divisor of the wave
   const size_t row = ((size_t)blockIdx.x * 256 + threadIdx.x) / LPR;
   const int sub = threadIdx.x % LPR;
@@ -165,7 +166,10 @@ __global__ __launch_bounds__(256) void row_term_kernel(const _Float16* do16, con
   }
 #pragma unroll
   for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
-  if (row < nrows && sub == 0) drow[row] = s;
+  if (row < nrows && sub == 0) {
+    drow[row] = s;
+    lse2[row] = lse[row] * kLog2eB;
+  }
 }
 
 // ---- row kernel: one lane per query (O' or dQ) ---------------------------------
@@ -343,45 +347,117 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
 
 // ---- key kernel: one lane per key (dK, dV) -------------------------------------
 
-// LDS stage of one 32-query step for the key kernel: query rows (fp16 and
-// FP4-decoded, as needed), dO rows, their transposes, and the rows' LSE and
-// row terms; plus each wave's per-query factors of P's quantisation.
-template <int D>
-struct KeyLds {  // (FA, FH: [wave][group][query]; HT: [wave][query] half-tile maxima, NVFP4)
-  static constexpr int RR = D + 8;  // halves per query row
-  static constexpr int TR = 32 + 8; // halves per transposed row (32 queries)
-  static constexpr int QR16 = 0;
-  static constexpr int QRD = QR16 + 32 * RR * 2;
-  static constexpr int DOR = QRD + 32 * RR * 2;
-  static constexpr int QT16 = DOR + 32 * RR * 2;
-  static constexpr int QTD = QT16 + D * TR * 2;
-  static constexpr int DOT = QTD + D * TR * 2;
-  static constexpr int L2 = DOT + D * TR * 2;  // 32 floats
-  static constexpr int DR = L2 + 32 * 4;       // 32 floats
-  static constexpr int FA = DR + 32 * 4;
+__device__ inline __attribute__((address_space(3))) void* lds_ptr(char* p) {
+  return (__attribute__((address_space(3))) void*)p;
+}
+
+// Eight halves of a transposed operand: ds_read_b64_tr_b16 at tile + o0 and
+// tile + o1 (elements 0-3 and 4-7).
+__device__ inline v8h tr_read(const char* tile, uint32_t o0, uint32_t o1) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s* lp;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(tile + o0));
+  const v4s up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(tile + o1));
+  return __builtin_bit_cast(v8h, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// The key kernels: one for dV, one for dK (each holds one set of
+// accumulators, which keeps them at two or three waves per SIMD).
+constexpr int kKeyDv = 0, kKeyDk = 1;
+
+// Key kernel LDS: two stages of one 32-query step each (the next step's
+// tiles arrive by direct loads while a step is computed); the dV kernel adds
+// each wave's per-query factors of P's quantisation.  A stage holds tiles of
+// 32 query rows (fp16 Q, FP4-decoded Q, for NVFP4's dK the decoded Q times
+// its slice scale, dO) and the rows' LSE (log2 units) and row terms.  Tile
+// layout: 16-byte chunk c of the row at slot m (query q0 + qperm(m)) sits at
+// c * 512 + ((m + 4c) % 32) * 16: chunk-column-major with the rows rotated
+// by four slots per column.  One direct wave load fills two chunk columns
+// (lanes 0-31 column 2p, lanes 32-63 column 2p + 1), and both reads are free
+// of bank conflicts: the row reads of the S and dP products (a half-wave
+// reads 16 slots of one chunk) and the transposed reads of the dV and dK
+// products (ds_read_b64_tr_b16: per 16 lanes, 4 queries of 16 channels).
+template <int D, int FMT, int MODE>
+struct KeyStage {
+  static constexpr bool QSCALED = FMT == THRIFT_NVFP4 && MODE == kKeyDk;
+  static constexpr int TILE = (D / 8) * 512;
+  static constexpr int NTL = QSCALED ? 4 : 3;
+  static constexpr int Q16 = 0;
+  static constexpr int QD = TILE;
+  static constexpr int QS = QSCALED ? 2 * TILE : TILE;  // dK's operand on FP4 pairs
+  static constexpr int DO = (NTL - 1) * TILE;
+  static constexpr int L2 = NTL * TILE;  // 32 floats, query order
+  static constexpr int DR = L2 + 128;    // 32 floats, query order
+  static constexpr int SIZE = DR + 128;
+};
+template <int D, int FMT, int MODE>
+struct KeyLds {  // (FA, FH: [wave][group][query]; HT: [wave][query] half-tile maxima)
+  static constexpr int FA = 2 * KeyStage<D, FMT, MODE>::SIZE;
   static constexpr int FH = FA + 4 * 2 * 32 * 4;
   static constexpr int HT = FH + 4 * 2 * 32 * 4;
-  static constexpr int SIZE = HT + 4 * 32 * 4;
+  static constexpr int SIZE = MODE == kKeyDv ? HT + 4 * 32 * 4 : FA;
 };
+
+// The direct loads of one step (query head bhq, rows q0 .. q0 + 31) into
+// stage buffer buf: the Q tiles the step's paths need (f0, f1: the two key
+// blocks are on the FP16 path), dO, the rows' LSE (wave 0) and, for dK,
+// their row terms (wave 1).  Wave w loads chunk-column pairs w + 4k of every
+// tile, lane l the row at slot l % 32 of column 2p + l / 32 (voff).  Rows
+// past S read as zeros (each tensor's buffer resource ends at its end).
+template <int D, int FMT, int MODE>
+__device__ inline void key_issue(const BwdArgs& a, char* buf, size_t bhq, int q0, bool f0, bool f1,
+                                 const uint32_t* voff, int w, int lane) {
+  using St = KeyStage<D, FMT, MODE>;
+  constexpr int PW = D / 64;
+  const int S = a.S;
+  const uint32_t qo = q0 * (D * 2);
+  auto tile = [&](const _Float16* base, int at) {
+    const auto rs = rsrc(base + bhq * S * D, S * D * 2);
+#pragma unroll
+    for (int k = 0; k < PW; ++k)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(buf + at + (w + 4 * k) * 1024), 16, voff[k] + qo, 0, 0, 0);
+  };
+  if (f0 || f1) tile(a.q16, St::Q16);
+  if (!f0 || !f1) {
+    tile(a.qd, St::QD);
+    if constexpr (St::QSCALED) tile(a.qds, St::QS);
+  }
+  tile(a.do16, St::DO);
+  auto rows = [&](const float* base, int at) {
+    // the row's base made visibly uniform (the load sits under a lane mask)
+    const uint64_t p = (uint64_t)(base + bhq * S);
+    const uint32_t ph = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+    const uint32_t pl = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);  // (int: no sign extension)
+    const uint64_t pu = (uint64_t)ph << 32 | pl;
+    const auto rs = rsrc((const void*)pu, S * 4);
+    if (lane < 32) __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, lds_ptr(buf + at), 4, (q0 + lane) * 4, 0, 0, 0);
+  };
+  if (w == 0) rows(a.lse2, St::L2);
+  if (MODE == kKeyDk && w == 1) rows(a.drow, St::DR);
+}
 
 // Workgroup = two key blocks (2 x 64 keys) of (batch, key head), four waves
 // of 32 keys each, one lane per key.  Steps of 32 query rows run over the G
 // query heads of the key head and the rows that see the blocks; each step's
-// query rows, dO rows and their transposes come once into LDS for all four
-// waves (the next step's are loaded into registers meanwhile).  Per step and
-// wave: S = Q K^T and dP = dO V^T with this lane's key as the column, p and
-// dS per element; on FP4 pairs the probability the forward used is rebuilt
-// from its quantisation groups (MX: the wave's 32 keys; NVFP4: 16-key groups
-// under the 64-key tile maximum, which the block's two waves exchange), whose
-// maxima come from S^T = K Q^T (same operands swapped, one lane per query)
-// and are handed to the key-major lanes through the wave's own LDS slot.
-// Then dV += pt^T dO
-// and dK += dS^T Q.  Only the K and V operands of the precision in use are
-// held in registers; they are reloaded when a step switches path.
-template <int D, int FMT>
-__global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
-  using L = KeyLds<D>;
-  constexpr int PR = 32 * D / 8 / 256;  // 16-byte pieces of a 32-row tile per thread
+// query rows and dO rows come once into LDS for all four waves, by direct
+// loads one step ahead.  Per step and wave, with this lane's key as the
+// column of S = Q K^T:
+//  - dV (MODE kKeyDv): p per element; on FP4 pairs the probability the
+//    forward used is rebuilt from its quantisation groups (MX: the wave's 32
+//    keys; NVFP4: 16-key groups under the 64-key tile maximum, which the
+//    block's two waves exchange), whose maxima come from S^T = K Q^T (same
+//    operands swapped, one lane per query) and are handed to the key-major
+//    lanes through the wave's own LDS slot; then dV += pt^T dO;
+//  - dK (MODE kKeyDk): dP = dO V^T, dS = p (dP - Dr); dK += dS^T Q.
+// The dV and dK products read their dO and Q operands transposed from the
+// row tiles.  Only the K (and for dK the V) operands of the precision in use
+// are held in registers; they are reloaded when a step switches path.
+template <int D, int FMT, int MODE>
+__global__ __launch_bounds__(256, MODE == kKeyDv ? 3 : 2) void bwd_key_kernel(BwdArgs a) {
+  using L = KeyLds<D, FMT, MODE>;
+  using St = KeyStage<D, FMT, MODE>;
+  constexpr bool DV = MODE == kKeyDv;
+  constexpr int PW = D / 64;  // chunk-column pairs per wave and tile
   __shared__ __attribute__((aligned(16))) char smem[L::SIZE];
   const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), hi = lane >> 5, r32 = lane & 31;
   const int BHk = a.B * a.Hkv, G = a.Hq / a.Hkv;
@@ -390,16 +466,16 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   const int j0 = (x / BHk) * 2;  // causal: the lowest key blocks have the most rows
   const size_t bhk = x % BHk;
   const int b = (int)(bhk / a.Hkv), hk = (int)(bhk % a.Hkv);
-  const int S = a.S, Sp = a.Sp;
+  const int S = a.S;
   const int jb = j0 + (w >> 1);              // this wave's key block (waves w, w ^ 1 share it)
   const int key = jb * kBlkK + (w & 1) * 32 + r32;  // this lane's key (column of S)
 
   const auto k16rs = rsrc(a.k16 + bhk * S * D, S * D * 2);
   const auto kdrs = rsrc(a.kd + bhk * S * D, S * D * 2);
   const auto v16rs = rsrc(a.v16 + bhk * S * D, S * D * 2);
-  const auto vdrs = rsrc(a.vd + bhk * Sp * D, Sp * D * 2);
-  v8h kr[D / 16], vr[D / 16];
-  int cur = -1;  // path whose K and V operands kr, vr hold (1 FP16, 0 FP4)
+  const auto vdrs = rsrc(a.vd + bhk * a.Sp * D, a.Sp * D * 2);
+  v8h kr[D / 16], vr[DV ? 1 : D / 16];
+  int cur = -1;  // path whose K (and V) operands kr, vr hold (1 FP16, 0 FP4)
   auto load_kv = [&](bool f16) {
     const auto krs = f16 ? k16rs : kdrs;
     const auto vrs = f16 ? v16rs : vdrs;
@@ -407,14 +483,34 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     for (int kk = 0; kk < D / 16; ++kk) {
       const int off = (key * D + kk * 16 + hi * 8) * 2;
       kr[kk] = ld8h(krs, off);
-      vr[kk] = ld8h(vrs, off);
+      if constexpr (!DV) vr[kk] = ld8h(vrs, off);
     }
     cur = f16;
   };
-  v16f dk[D / 32], dv[D / 32];
+  v16f acc[D / 32];  // dV or dK (unscaled)
 #pragma unroll
-  for (int dt = 0; dt < D / 32; ++dt) dk[dt] = dv[dt] = v16f{};
+  for (int dt = 0; dt < D / 32; ++dt) acc[dt] = v16f{};
   const float dpf4 = a.tv ? a.tv[bhk] : 1.0f;
+
+  // this lane's byte offsets: direct-load sources (row of slot r32 of column
+  // 2p + hi, p = w + 4k), row reads (column 2kk + hi, by kk % 4) and
+  // transposed reads (by (2 st + h2 + 2 dt) % 4, see below)
+  uint32_t voff[PW];
+#pragma unroll
+  for (int k = 0; k < PW; ++k) {
+    const int c = 2 * (w + 4 * k) + hi;
+    voff[k] = qperm((r32 - 4 * c) & 31) * (D * 2) + c * 16;
+  }
+  uint32_t rrow[4], rtr[4];
+  {
+    const int r = r32 & 15, g = r32 >> 4;
+    const int xq = hi * 4 + (r >> 2) + 8 * g + 4 * ((r & 3) >> 1);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      rrow[k] = hi * 512 + ((r32 + 8 * k + 4 * hi) & 31) * 16;
+      rtr[k] = ((xq + 8 * k) & 31) * 16 + (2 * g + ((r & 3) >> 1)) * 512 + (r & 1) * 8;
+    }
+  }
 
   // step sequence: for g < G, q0 from the first row that sees block j0, by 32
   const int qstart = a.causal ? (j0 * kBlkK / 32) * 32 : 0;
@@ -436,57 +532,6 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     return a.prom + ((size_t)bhq * a.nq + (q0 >> bq_shift)) * a.nkw + (j0 >> 5);
   };
   auto bit = [&](uint32_t word, int j) { return j < nk && ((word >> (j & 31)) & 1u) != 0; };
-  v4i pq16[PR], pqd[PR], pdo[PR], pt16[PR], ptd[PR], pdt[PR];
-  float pl = 0.0f, pr = 0.0f;
-  auto fetch = [&](int g, int q0, uint32_t word) {
-    const int bhq = b * a.Hq + hk * G + g;
-    const bool f0 = bit(word, j0), f1 = bit(word, j0 + 1);
-    const bool need16 = f0 || f1, needd = !f0 || !f1;
-    const auto qrs = rsrc(a.q16 + (size_t)bhq * S * D, S * D * 2);
-    const auto qdrs = rsrc(a.qd + (size_t)bhq * S * D, S * D * 2);
-    const auto drs = rsrc(a.do16 + (size_t)bhq * S * D, S * D * 2);
-    const size_t tb = (size_t)bhq * D * Sp;
-#pragma unroll
-    for (int u = 0; u < PR; ++u) {
-      const int c = t + u * 256;
-      const int row = c / (D / 8), c8 = c % (D / 8);  // row-major tiles
-      const int off = ((q0 + row) * D + c8 * 8) * 2;
-      if (need16) pq16[u] = __builtin_amdgcn_raw_buffer_load_b128(qrs, off, 0, 0);
-      if (needd) pqd[u] = __builtin_amdgcn_raw_buffer_load_b128(qdrs, off, 0, 0);
-      pdo[u] = __builtin_amdgcn_raw_buffer_load_b128(drs, off, 0, 0);
-      const int d = c / 4, c4 = c % 4;  // transposed tiles: row d, 8 queries
-      const size_t toff = tb + (size_t)d * Sp + q0 + c4 * 8;
-      if (need16) pt16[u] = *(const v4i*)(a.qt + toff);
-      if (needd) ptd[u] = *(const v4i*)(a.qdt + toff);
-      pdt[u] = *(const v4i*)(a.dot + toff);
-    }
-    if (t < 32) {
-      const int q = q0 + t;
-      pl = q < S ? a.lse[(size_t)bhq * S + q] * kLog2eB : 0.0f;
-      pr = q < S ? a.drow[(size_t)bhq * S + q] : 0.0f;
-    }
-    return need16 * 2 + needd;
-  };
-  auto stash = [&](int need) {
-#pragma unroll
-    for (int u = 0; u < PR; ++u) {
-      const int c = t + u * 256;
-      const int row = c / (D / 8), c8 = c % (D / 8);
-      const int ro = (row * L::RR + c8 * 8) * 2;
-      if (need & 2) *(v4i*)(smem + L::QR16 + ro) = pq16[u];
-      if (need & 1) *(v4i*)(smem + L::QRD + ro) = pqd[u];
-      *(v4i*)(smem + L::DOR + ro) = pdo[u];
-      const int d = c / 4, c4 = c % 4;
-      const int to = (d * L::TR + c4 * 8) * 2;
-      if (need & 2) *(v4i*)(smem + L::QT16 + to) = pt16[u];
-      if (need & 1) *(v4i*)(smem + L::QTD + to) = ptd[u];
-      *(v4i*)(smem + L::DOT + to) = pdt[u];
-    }
-    if (t < 32) {
-      ((float*)(smem + L::L2))[t] = pl;
-      ((float*)(smem + L::DR))[t] = pr;
-    }
-  };
 
   int g = 0, q0 = qstart;          // this step
   int g1 = 0, q01 = qstart;        // the next
@@ -495,7 +540,8 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
   advance(g2, q02);
   uint32_t wcur = nsteps > 0 ? __builtin_amdgcn_readfirstlane(*word_addr(g, q0)) : 0u;
   uint32_t wnext = nsteps > 1 ? *word_addr(g1, q01) : 0u;  // in flight
-  int need = nsteps > 0 ? fetch(g, q0, wcur) : 0;
+  if (nsteps > 0)
+    key_issue<D, FMT, MODE>(a, smem, b * a.Hq + hk * G + g, q0, bit(wcur, j0), bit(wcur, j0 + 1), voff, w, lane);
   float cq4 = a.c;  // scale of FP4 pairs' scores (NVFP4: times the head's slice scales)
   int cq_g = -1;
   for (int n = 0; n < nsteps; ++n) {
@@ -505,137 +551,160 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
       cq4 = a.tq ? a.c * a.tq[bhq] * a.tk[bhk] : a.c;
       cq_g = g;
     }
-    __syncthreads();  // every wave is done with the previous step
-    stash(need);
-    __syncthreads();
+    char* const buf = smem + (n & 1) * St::SIZE;
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // this step's tiles are in; every wave is done with the previous step
+    uint32_t wn = 0;
     if (n + 1 < nsteps) {
-      const uint32_t w1 = __builtin_amdgcn_readfirstlane(wnext);
+      wn = __builtin_amdgcn_readfirstlane(wnext);
       wnext = *word_addr(g2, q02);
-      need = fetch(g1, q01, w1);
-      wcur = w1;
+      key_issue<D, FMT, MODE>(a, smem + ((n + 1) & 1) * St::SIZE, b * a.Hq + hk * G + g1, q01, bit(wn, j0),
+                              bit(wn, j0 + 1), voff, w, lane);
     }
     // (steps whose pairs are all masked for this wave add zeros: a branch
     // around the products would make the compiler copy the accumulators)
     if ((int)f16 != cur) load_kv(f16);
-    const _Float16* qrow = (const _Float16*)(smem + (f16 ? L::QR16 : L::QRD)) + qperm(r32) * L::RR + hi * 8;
-    const _Float16* drow = (const _Float16*)(smem + L::DOR) + qperm(r32) * L::RR + hi * 8;
-    v16f s = v16f{}, dp = v16f{};
-#pragma unroll
-    for (int kk = 0; kk < D / 16; ++kk) {
-      s = mfma_f16(*(const v8h*)(qrow + kk * 16), kr[kk], s);
-      dp = mfma_f16(*(const v8h*)(drow + kk * 16), vr[kk], dp);
-    }
-    // FP4 pairs: per query and P group, p * fa is the element over its block
-    // scale and pt = code * fh (this lane's key is in group grp of the wave)
+    const char* qrows = buf + (f16 ? St::Q16 : St::QD);
+    const char* dob = buf + St::DO;
+    const float* l2 = (const float*)(buf + St::L2);
     const float cj = f16 ? a.c : cq4;
-    const int grp = FMT == THRIFT_MXFP4 ? 0 : r32 >> 4;
-    const float* wa = (const float*)(smem + L::FA) + (w * 2 + grp) * 32;
-    const float* wh = (const float*)(smem + L::FH) + (w * 2 + grp) * 32;
-    float gm0 = -INFINITY, gm1 = -INFINITY, Lq = 0.0f;  // group maxima (raw scores) of query qperm(r32)
-    if (!f16) {
-      v16f st = v16f{};
+    v8h opA[2];  // A operand of the product: pt (dV) or dS (dK); step st holds queries hi*16 + 8 st + u
+    if constexpr (DV) {
+      // FP4 pairs: per query and P group, p * fa is the element over its
+      // block scale and pt = code * fh (this lane's key is in group grp)
+      const int grp = FMT == THRIFT_MXFP4 ? 0 : r32 >> 4;
+      const float* wa = (const float*)(smem + L::FA) + (w * 2 + grp) * 32;
+      const float* wh = (const float*)(smem + L::FH) + (w * 2 + grp) * 32;
+      float gm0 = -INFINITY, gm1 = -INFINITY, Lq = 0.0f;  // group maxima (raw scores) of query qperm(r32)
+      if (!f16) {
+        v16f st = v16f{};
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) st = mfma_f16(kr[kk], *(const v8h*)(qrow + kk * 16), st);
-      // column r32 is query q0 + qperm(r32); register ii is key (ii/4)*8 + hi*4 + ii%4 of the wave's 32
-      const int qm = q0 + qperm(r32);
+        for (int kk = 0; kk < D / 16; ++kk)
+          st = mfma_f16(kr[kk], *(const v8h*)(qrows + kk * 1024 + rrow[kk & 3]), st);
+        // column r32 is query q0 + qperm(r32); register ii is key (ii/4)*8 + hi*4 + ii%4 of the wave's 32
+        const int qm = q0 + qperm(r32);
 #pragma unroll
-      for (int ii = 0; ii < 16; ++ii) {
-        const int kx = jb * kBlkK + (w & 1) * 32 + (ii >> 2) * 8 + hi * 4 + (ii & 3);
-        const bool ok = qm < S && kx < S && !(a.causal && kx > qm);
-        const float v = ok ? st[ii] : -INFINITY;
-        if (ii < 8)
-          gm0 = fmaxf(gm0, v);
-        else
-          gm1 = fmaxf(gm1, v);
-      }
-      gm0 = pair_max(gm0);
-      gm1 = pair_max(gm1);
-      Lq = ((const float*)(smem + L::L2))[qperm(r32)];
-      if (hi == 0) ((float*)(smem + L::HT))[w * 32 + qperm(r32)] = fmaxf(gm0, gm1);
-    }
-    // level 1 is the query's maximum over the whole 64-key tile: the two
-    // waves of the block exchange their halves (every wave passes this
-    // barrier on every step)
-    __syncthreads();
-    if (!f16) {
-      const float tm = fmaxf(fmaxf(gm0, gm1), ((const float*)(smem + L::HT))[(w ^ 1) * 32 + qperm(r32)]);
-      const float tml = tm * cj;
-      // a tile more than 2^60 below the row's total contributes nothing
-      const bool live = tm > -INFINITY && tml - Lq > -60.0f;
-      if constexpr (FMT == THRIFT_MXFP4) {
-        // level 2: this wave's 32 keys are one group; E8M0 exponent
-        // floor(log2(max p)) - 2 relative to the tile maximum (-2 for the
-        // group holding it)
-        const float gm = fmaxf(gm0, gm1);
-        const uint32_t E = gm == tm ? 127u : (__float_as_uint(exp2_fast(__builtin_fmaf(gm, cj, -tml))) >> 23) & 0xFF;
-        const float X = (float)((int)(E > 3 ? E - 2 : 1) - 127);
-        const bool on = live && gm > -INFINITY;
-        if (hi == 0) {
-          ((float*)wa)[qperm(r32)] = on ? exp2_fast(Lq - tml - X) : 0.0f;
-          ((float*)wh)[qperm(r32)] = on ? exp2_fast(X + tml - Lq) : 0.0f;
+        for (int ii = 0; ii < 16; ++ii) {
+          const int kx = jb * kBlkK + (w & 1) * 32 + (ii >> 2) * 8 + hi * 4 + (ii & 3);
+          const bool ok = qm < S && kx < S && !(a.causal && kx > qm);
+          const float v = ok ? st[ii] : -INFINITY;
+          if (ii < 8)
+            gm0 = fmaxf(gm0, v);
+          else
+            gm1 = fmaxf(gm1, v);
         }
-      } else {
+        gm0 = pair_max(gm0);
+        gm1 = pair_max(gm1);
+        Lq = l2[qperm(r32)];
+        if (hi == 0) ((float*)(smem + L::HT))[w * 32 + qperm(r32)] = fmaxf(gm0, gm1);
+      }
+      v16f s = v16f{};
 #pragma unroll
-        for (int g = 0; g < 2; ++g) {
-          const float gmg = g ? gm1 : gm0;
-          const float gv = gmg == tm ? 2688.0f : 2688.0f * exp2_fast(__builtin_fmaf(gmg, cj, -tml));
-          v2s_t sb = {0, 0};
-          sb = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(sb, fminf(gv * (1.0f / 6.0f), 448.0f), 0.0f, 1.0f, false);
-          const float s2 = e4m3_to_float((uint32_t)sb[0] & 0xFF);
-          const bool on = live && s2 > 0.0f;
+      for (int kk = 0; kk < D / 16; ++kk) s = mfma_f16(*(const v8h*)(qrows + kk * 1024 + rrow[kk & 3]), kr[kk], s);
+      // level 1 is the query's maximum over the whole 64-key tile: the two
+      // waves of the block exchange their halves (every wave passes this
+      // barrier on every step)
+      __syncthreads();
+      if (!f16) {
+        const float tm = fmaxf(fmaxf(gm0, gm1), ((const float*)(smem + L::HT))[(w ^ 1) * 32 + qperm(r32)]);
+        const float tml = tm * cj;
+        // a tile more than 2^60 below the row's total contributes nothing
+        const bool live = tm > -INFINITY && tml - Lq > -60.0f;
+        if constexpr (FMT == THRIFT_MXFP4) {
+          // level 2: this wave's 32 keys are one group; E8M0 exponent
+          // floor(log2(max p)) - 2 relative to the tile maximum (-2 for the
+          // group holding it)
+          const float gm = fmaxf(gm0, gm1);
+          const uint32_t E =
+              gm == tm ? 127u : (__float_as_uint(exp2_fast(__builtin_fmaf(gm, cj, -tml))) >> 23) & 0xFF;
+          const float X = (float)((int)(E > 3 ? E - 2 : 1) - 127);
+          const bool on = live && gm > -INFINITY;
           if (hi == 0) {
-            float* fa = (float*)(smem + L::FA) + (w * 2 + g) * 32;
-            float* fh = (float*)(smem + L::FH) + (w * 2 + g) * 32;
-            fa[qperm(r32)] = on ? exp2_fast(Lq - tml) * nv_p_factor(s2) : 0.0f;
-            fh[qperm(r32)] = on ? s2 * exp2_fast(tml - Lq) * (1.0f / 2688.0f) : 0.0f;
+            ((float*)wa)[qperm(r32)] = on ? exp2_fast(Lq - tml - X) : 0.0f;
+            ((float*)wh)[qperm(r32)] = on ? exp2_fast(X + tml - Lq) : 0.0f;
+          }
+        } else {
+#pragma unroll
+          for (int gg = 0; gg < 2; ++gg) {
+            const float gmg = gg ? gm1 : gm0;
+            const float gv = gmg == tm ? 2688.0f : 2688.0f * exp2_fast(__builtin_fmaf(gmg, cj, -tml));
+            v2s_t sb = {0, 0};
+            sb = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(sb, fminf(gv * (1.0f / 6.0f), 448.0f), 0.0f, 1.0f, false);
+            const float s2 = e4m3_to_float((uint32_t)sb[0] & 0xFF);
+            const bool on = live && s2 > 0.0f;
+            if (hi == 0) {
+              float* fa = (float*)(smem + L::FA) + (w * 2 + gg) * 32;
+              float* fh = (float*)(smem + L::FH) + (w * 2 + gg) * 32;
+              fa[qperm(r32)] = on ? exp2_fast(Lq - tml) * nv_p_factor(s2) : 0.0f;
+              fh[qperm(r32)] = on ? s2 * exp2_fast(tml - Lq) * (1.0f / 2688.0f) : 0.0f;
+            }
           }
         }
+        // the wave reads back its own slot: its LDS operations complete in order
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
       }
-      // the wave reads back its own slot: its LDS operations complete in order
-      asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+      // this lane's queries are q0 + hi*16 + ii, four at a time
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 l4 = *(const float4*)(l2 + hi * 16 + u * 4);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        float pt[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ii = u * 4 + e, q = q0 + hi * 16 + ii;
+          const bool ok = q < S && key < S && !(a.causal && key > q);
+          pt[e] = ok ? exp2_fast(__builtin_fmaf(s[ii], cj, -lv[e])) : 0.0f;
+        }
+        if (!f16) {
+          const float4 a4 = *(const float4*)(wa + hi * 16 + u * 4);
+          const float4 h4 = *(const float4*)(wh + hi * 16 + u * 4);
+          const uint32_t y0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, pt[0] * a4.x, pt[1] * a4.y, 1.0f, 0);
+          const uint32_t y1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, pt[2] * a4.z, pt[3] * a4.w, 1.0f, 0);
+          const v2f c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(y0, 1.0f, 0);
+          const v2f c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(y1, 1.0f, 0);
+          pt[0] = c0[0] * h4.x;
+          pt[1] = c0[1] * h4.y;
+          pt[2] = c1[0] * h4.z;
+          pt[3] = c1[1] * h4.w;
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) opA[(u * 4 + e) / 8][(u * 4 + e) % 8] = (_Float16)pt[e];
+      }
+    } else {
+      v16f s = v16f{}, dp = v16f{};
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) {
+        s = mfma_f16(*(const v8h*)(qrows + kk * 1024 + rrow[kk & 3]), kr[kk], s);
+        dp = mfma_f16(*(const v8h*)(dob + kk * 1024 + rrow[kk & 3]), vr[kk], dp);
+      }
+      const float* dr = (const float*)(buf + St::DR);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float4 l4 = *(const float4*)(l2 + hi * 16 + u * 4);
+        const float4 r4 = *(const float4*)(dr + hi * 16 + u * 4);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int ii = u * 4 + e, q = q0 + hi * 16 + ii;
+          const bool ok = q < S && key < S && !(a.causal && key > q);
+          const float p = ok ? exp2_fast(__builtin_fmaf(s[ii], cj, -lv[e])) : 0.0f;
+          opA[ii / 8][ii % 8] = (_Float16)(p * (dp[ii] * (f16 ? 1.0f : dpf4) - rv[e]));
+        }
+      }
     }
-    // A operands of the two products: step st holds queries hi*16 + 8 st + u;
-    // this lane's queries are q0 + hi*16 + ii, four at a time
-    v8h pA[2], sA[2];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const float4 l4 = *(const float4*)(smem + L::L2 + (hi * 16 + u * 4) * 4);
-      const float4 r4 = *(const float4*)(smem + L::DR + (hi * 16 + u * 4) * 4);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
-      float p[4], pt[4];
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int ii = u * 4 + e, q = q0 + hi * 16 + ii;
-        const bool ok = q < S && key < S && !(a.causal && key > q);
-        p[e] = ok ? exp2_fast(__builtin_fmaf(s[ii], cj, -lv[e])) : 0.0f;
-        sA[ii / 8][ii % 8] = (_Float16)(p[e] * (dp[ii] * (f16 ? 1.0f : dpf4) - rv[e]));
-        pt[e] = p[e];
-      }
-      if (!f16) {
-        const float4 a4 = *(const float4*)(wa + hi * 16 + u * 4);
-        const float4 h4 = *(const float4*)(wh + hi * 16 + u * 4);
-        const uint32_t y0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, p[0] * a4.x, p[1] * a4.y, 1.0f, 0);
-        const uint32_t y1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, p[2] * a4.z, p[3] * a4.w, 1.0f, 0);
-        const v2f c0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(y0, 1.0f, 0);
-        const v2f c1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(y1, 1.0f, 0);
-        pt[0] = c0[0] * h4.x;
-        pt[1] = c0[1] * h4.y;
-        pt[2] = c1[0] * h4.z;
-        pt[3] = c1[1] * h4.w;
-      }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) pA[(u * 4 + e) / 8][(u * 4 + e) % 8] = (_Float16)pt[e];
-    }
-    const _Float16* qT = (const _Float16*)(smem + (f16 ? L::QT16 : L::QTD));
-    const _Float16* oT = (const _Float16*)(smem + L::DOT);
+    // B operand read transposed: in step st, lane (r32, hi) takes channel
+    // dt*32 + r32 of queries hi*16 + 8 st + 4 h2 + (0..3) from two
+    // ds_read_b64_tr_b16, h2 = 0, 1 (rtr's index (2 st + h2 + 2 dt) % 4):
+    // dO for dV, Q for dK
+    const char* opB = DV ? dob : buf + (f16 ? St::Q16 : St::QS);
 #pragma unroll
     for (int st = 0; st < 2; ++st)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const int off = (dt * 32 + r32) * L::TR + hi * 16 + st * 8;
-        dv[dt] = mfma_f16(pA[st], *(const v8h*)(oT + off), dv[dt]);
-        dk[dt] = mfma_f16(sA[st], *(const v8h*)(qT + off), dk[dt]);
+        const int k0 = (2 * st + 2 * dt) & 3, k1 = (2 * st + 1 + 2 * dt) & 3;
+        acc[dt] = mfma_f16(opA[st], tr_read(opB + dt * 2048, rtr[k0], rtr[k1]), acc[dt]);
       }
+    wcur = wn;
     g = g1;
     q0 = q01;
     g1 = g2;
@@ -643,23 +712,21 @@ __global__ __launch_bounds__(256) void bwd_key_kernel(BwdArgs a) {
     advance(g2, q02);
   }
   // C layout: column d = dt*32 + r32, register ii is key (ii/4)*8 + hi*4 + ii%4 of the wave's 32
+  float* out = DV ? a.dv : a.dk;
+  const float osc = DV ? 1.0f : a.sm_scale;
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
     for (int ii = 0; ii < 16; ++ii) {
       const int kx = jb * kBlkK + (w & 1) * 32 + (ii >> 2) * 8 + hi * 4 + (ii & 3);
-      if (kx < S) {
-        const size_t e = (bhk * S + kx) * D + dt * 32 + r32;
-        a.dk[e] = dk[dt][ii] * a.sm_scale;
-        a.dv[e] = dv[dt][ii];
-      }
+      if (kx < S) out[(bhk * S + kx) * D + dt * 32 + r32] = acc[dt][ii] * osc;
     }
 }
 
 // ---- host side -----------------------------------------------------------------------
 
 struct BwdLayout {
-  size_t qd, qt, qdt, dot, kd, kt, kdt, vd, vt, vdt, prom, drow, total;
+  size_t qd, qds, kd, kt, kdt, vd, vt, vdt, prom, drow, lse2, total;
 };
 
 inline size_t al256(size_t x) { return (x + 255) / 256 * 256; }
@@ -676,9 +743,7 @@ BwdLayout bwd_layout(int B, int Hq, int Hkv, int S, int D, int bq) {
     return at;
   };
   l.qd = take(bhq * S * D * 2);
-  l.qt = take(bhq * D * Sp * 2);
-  l.qdt = take(bhq * D * Sp * 2);
-  l.dot = take(bhq * D * Sp * 2);
+  l.qds = take(bhq * S * D * 2);
   l.kd = take(bhk * S * D * 2);
   l.kt = take(bhk * D * Sp * 2);
   l.kdt = take(bhk * D * Sp * 2);
@@ -687,6 +752,7 @@ BwdLayout bwd_layout(int B, int Hq, int Hkv, int S, int D, int bq) {
   l.vdt = take(bhk * D * Sp * 2);
   l.prom = take(bhq * nq * nkw * 4);
   l.drow = take(bhq * S * 4);
+  l.lse2 = take(bhq * S * 4);
   l.total = o;
   return l;
 }
@@ -731,9 +797,9 @@ void launch_transpose(const _Float16* in, int BH, int R, int C, int Rout, _Float
 
 // Fills the FP4-decoded and transposed operands both entry points share.
 // FP4-decoded operands keep NVFP4's slice scale out (exact fp16, the scale
-// applied to the fp32 scores and dP); the transposed copies that are only
-// ever the reduction-side operand (K^T for dQ, Q^T for dK, V^T for O')
-// carry it, rounded once.
+// applied to the fp32 scores and dP); the operands that are only ever on
+// the reduction side (K^T for dQ, V^T for O', and for dK the decoded Q rows,
+// which the key kernel reads transposed) carry it, rounded once.
 void prepare(BwdArgs& a, char* ws, const BwdLayout& l, const void* q16, const void* k16, const void* v16,
              const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c, const uint8_t* k4s,
              const float* k4t, const uint8_t* v4c, const uint8_t* v4s, const float* v4t, int fmt,
@@ -746,9 +812,7 @@ void prepare(BwdArgs& a, char* ws, const BwdLayout& l, const void* q16, const vo
   a.qd = (const _Float16*)(ws + l.qd);
   a.kd = (const _Float16*)(ws + l.kd);
   a.vd = (const _Float16*)(ws + l.vd);
-  a.qt = (const _Float16*)(ws + l.qt);
-  a.qdt = (const _Float16*)(ws + l.qdt);
-  a.dot = (const _Float16*)(ws + l.dot);
+  a.qds = (const _Float16*)(ws + l.qds);
   a.kt = (const _Float16*)(ws + l.kt);
   a.kdt = (const _Float16*)(ws + l.kdt);
   a.vt = (const _Float16*)(ws + l.vt);
@@ -756,6 +820,7 @@ void prepare(BwdArgs& a, char* ws, const BwdLayout& l, const void* q16, const vo
   a.prom = (const uint32_t*)(ws + l.prom);
   a.lse = lse;
   a.drow = (const float*)(ws + l.drow);
+  a.lse2 = (const float*)(ws + l.lse2);
   a.B = B;
   a.Hq = Hq;
   a.Hkv = Hkv;
@@ -781,8 +846,7 @@ void prepare(BwdArgs& a, char* ws, const BwdLayout& l, const void* q16, const vo
   prom_bits_kernel<<<cdiv(nrows, 256), 256, 0, stream>>>(idx, cnt, nrows, kmax, nk, a.nkw, (uint32_t*)a.prom);
   if (backward) {
     launch_transpose(a.vdt, BHk, D, Sp, D, (_Float16*)a.vd, stream);  // [Sp][D]
-    launch_transpose(a.q16, BHq, S, D, Sp, (_Float16*)a.qt, stream);
-    launch_transpose(a.qd, BHq, S, D, Sp, (_Float16*)a.qdt, stream, a.tq);
+    if (nv) launch_decode(q4c, q4s, (size_t)BHq * S, D, fmt, a.tq, S, (_Float16*)a.qds, stream);
     launch_transpose(a.k16, BHk, S, D, Sp, (_Float16*)a.kt, stream);
     launch_transpose(a.kd, BHk, S, D, Sp, (_Float16*)a.kdt, stream, a.tk);
   } else {
@@ -806,6 +870,12 @@ void launch_row(const BwdArgs& a, int mode, hipStream_t stream) {
   }
 }
 
+template <int D, int FMT>
+void launch_key(const BwdArgs& a, int kgrid, hipStream_t stream) {
+  bwd_key_kernel<D, FMT, kKeyDv><<<kgrid, 256, 0, stream>>>(a);
+  bwd_key_kernel<D, FMT, kKeyDk><<<kgrid, 256, 0, stream>>>(a);
+}
+
 template __global__ void bwd_row_kernel<128, kModeOhp, 4>(BwdArgs);
 template __global__ void bwd_row_kernel<128, kModeDq, 4>(BwdArgs);
 template __global__ void bwd_row_kernel<64, kModeOhp, 4>(BwdArgs);
@@ -814,12 +884,8 @@ template __global__ void bwd_row_kernel<128, kModeOhp, 2>(BwdArgs);
 template __global__ void bwd_row_kernel<128, kModeDq, 2>(BwdArgs);
 template __global__ void bwd_row_kernel<64, kModeOhp, 2>(BwdArgs);
 template __global__ void bwd_row_kernel<64, kModeDq, 2>(BwdArgs);
-template __global__ void bwd_key_kernel<128, THRIFT_MXFP4>(BwdArgs);
-template __global__ void bwd_key_kernel<64, THRIFT_MXFP4>(BwdArgs);
-template __global__ void bwd_key_kernel<128, THRIFT_NVFP4>(BwdArgs);
-template __global__ void bwd_key_kernel<64, THRIFT_NVFP4>(BwdArgs);
-template __global__ void row_term_kernel<128>(const _Float16*, const float*, size_t, float*);
-template __global__ void row_term_kernel<64>(const _Float16*, const float*, size_t, float*);
+template __global__ void row_term_kernel<128>(const _Float16*, const float*, const float*, size_t, float*, float*);
+template __global__ void row_term_kernel<64>(const _Float16*, const float*, const float*, size_t, float*, float*);
 
 }  // namespace
 
@@ -875,15 +941,14 @@ extern "C" thrift_status thrift_attention_bwd(
   char* ws = (char*)workspace;
   prepare(a, ws, l, q16, k16, v16, q4_codes, q4_scales, q4_tscale, k4_codes, k4_scales, k4_tscale, v4_codes,
           v4_scales, v4_tscale, fmt, idx, cnt, kmax, B, Hq, Hkv, S, D, block_q, causal, sm_scale, lse, true, stream);
-  const int Sp = a.Sp, BHq = B * Hq;
+  const int BHq = B * Hq;
   a.do16 = (const _Float16*)do16;
-  launch_transpose(a.do16, BHq, S, D, Sp, (_Float16*)a.dot, stream);
   const size_t nrows = (size_t)BHq * S;
   const unsigned rt_grid = (unsigned)((nrows * (size_t)(D / 8) + 255) / 256);
   if (D == 128)
-    row_term_kernel<128><<<rt_grid, 256, 0, stream>>>(a.do16, ohp, nrows, (float*)a.drow);
+    row_term_kernel<128><<<rt_grid, 256, 0, stream>>>(a.do16, ohp, lse, nrows, (float*)a.drow, (float*)a.lse2);
   else
-    row_term_kernel<64><<<rt_grid, 256, 0, stream>>>(a.do16, ohp, nrows, (float*)a.drow);
+    row_term_kernel<64><<<rt_grid, 256, 0, stream>>>(a.do16, ohp, lse, nrows, (float*)a.drow, (float*)a.lse2);
   a.out = dq;
   a.dk = dk;
   a.dv = dv;
@@ -892,15 +957,15 @@ extern "C" thrift_status thrift_attention_bwd(
   if (D == 128) {
     launch_row<128>(a, kModeDq, stream);
     if (mx)
-      bwd_key_kernel<128, THRIFT_MXFP4><<<kgrid, 256, 0, stream>>>(a);
+      launch_key<128, THRIFT_MXFP4>(a, kgrid, stream);
     else
-      bwd_key_kernel<128, THRIFT_NVFP4><<<kgrid, 256, 0, stream>>>(a);
+      launch_key<128, THRIFT_NVFP4>(a, kgrid, stream);
   } else {
     launch_row<64>(a, kModeDq, stream);
     if (mx)
-      bwd_key_kernel<64, THRIFT_MXFP4><<<kgrid, 256, 0, stream>>>(a);
+      launch_key<64, THRIFT_MXFP4>(a, kgrid, stream);
     else
-      bwd_key_kernel<64, THRIFT_NVFP4><<<kgrid, 256, 0, stream>>>(a);
+      launch_key<64, THRIFT_NVFP4>(a, kgrid, stream);
   }
   return launch_status();
 }
