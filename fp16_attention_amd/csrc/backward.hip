@@ -48,7 +48,7 @@ struct BwdArgs {
   const _Float16 *qd, *kd;                 // FP4-decoded Q, K rows [B,H,S,D]
   const _Float16* qds;                     // FP4-decoded Q times its slice scale (NVFP4) [B,Hq,S,D]
   const _Float16* vd;                      // FP4-decoded V rows [B,Hkv,Sp,D]
-  const _Float16 *kt, *kdt, *vt, *vdt;     // transposed [B,Hkv,D,Sp]
+  const _Float16* vdt;                     // FP4-decoded V^T [B,Hkv,D,Sp] (vd's source)
   const uint32_t* prom;                    // promoted-block bits [B,Hq,nq,nkw]
   const float *lse, *drow, *lse2;          // [B,Hq,S]; lse2 = lse * log2(e)
   const float *tq, *tk, *tv;               // NVFP4 slice scales [B,H] (NULL for MXFP4)
@@ -174,34 +174,74 @@ __global__ __launch_bounds__(256) void row_term_kernel(const _Float16* do16, con
 
 // ---- row kernel: one lane per query (O' or dQ) ---------------------------------
 
+__device__ inline __attribute__((address_space(3))) void* lds_ptr(char* p) {
+  return (__attribute__((address_space(3))) void*)p;
+}
+
+// Eight halves of a transposed operand: ds_read_b64_tr_b16 at tile + o0 and
+// tile + o1 (elements 0-3 and 4-7).
+__device__ inline v8h tr_read(const char* tile, uint32_t o0, uint32_t o1) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) v4s* lp;
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(tile + o0));
+  const v4s up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(tile + o1));
+  return __builtin_bit_cast(v8h, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+
 constexpr int kModeOhp = 0;
 constexpr int kModeDq = 1;
 
-// LDS stage of one key block for the row kernel: K rows, V rows (dQ mode)
-// and the transposed operand of the second product (K^T or V^T).
+// Row kernel LDS: two stages of one key block each (the next block's K and
+// V rows arrive by direct loads while a block is computed).  Each tile holds
+// the block's 64 key rows in krow order (slot mt*32 + m holds key
+// krow(mt, m)), chunk-column-major: 16-byte chunk c of slot r at
+// c * 1088 + r * 16, one direct wave load per chunk column.  The 64-byte
+// stagger per column keeps both reads free of bank conflicts: the rows as
+// the A operand of S^T = K Q^T and dP^T = V dO^T (16 slots of one chunk per
+// half-wave) and the transposed reads of the K^T and V^T operands
+// (ds_read_b64_tr_b16: per 16 lanes, 4 keys of 16 channels).
 template <int D>
-struct RowLds {
-  static constexpr int KR = D + 8;      // halves per K/V row
-  static constexpr int TR = kBlkK + 8;  // halves per transposed row
+struct RowStage {
+  static constexpr int CS = 1024 + 64;
+  static constexpr int TILE = (D / 8) * CS;
   static constexpr int K = 0;
-  static constexpr int V = K + kBlkK * KR * 2;
-  static constexpr int T = V + kBlkK * KR * 2;
-  static constexpr int SIZE = T + D * TR * 2;
+  static constexpr int V = TILE;
+  static constexpr int SIZE = 2 * TILE;
 };
 
-// Workgroup = query block i of (batch, query head), one wave per 32 rows.
-// Per valid key block j, in the precision of its path: S^T = K Q^T (keys in
-// krow order), p = 2^(t - L2); then O'^T += V^T P^T, or dP^T = V dO^T,
-// dS = p (dP - Dr) and dQ^T += K^T dS^T.  The waves share each key block's
-// operands through one LDS stage; the next block's are loaded into
-// registers while the current one is computed.
+// Slot of key k (0..63) in krow order.
+__device__ constexpr int kslot_of(int k) {
+  return ((k >> 4) & 1) * 32 + ((k >> 2) & 3) * 8 + ((k >> 5) & 1) * 4 + (k & 3);
+}
+
+// One key block's K and V rows into a row-kernel stage: wave w loads chunk
+// columns w, w + NW, ... of each tile (lane l: the row of slot l, source
+// byte offset o plus the column's 16 bytes).
+template <int D, int NW>
+__device__ inline void row_issue(char* buf, __amdgpu_buffer_rsrc_t krs, __amdgpu_buffer_rsrc_t vrs, uint32_t o,
+                                 int w) {
+  using R = RowStage<D>;
+#pragma unroll
+  for (int k = 0; k < (D / 8) / NW; ++k) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, lds_ptr(buf + R::K + (w + k * NW) * R::CS), 16, o + k * NW * 16, 0,
+                                             0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, lds_ptr(buf + R::V + (w + k * NW) * R::CS), 16, o + k * NW * 16, 0,
+                                             0, 0);
+  }
+}
+
+// Workgroup = query block i of (batch, query head), one wave per 32 rows,
+// one lane per query.  The valid key blocks run FP4 blocks first, then the
+// promoted ones, each ascending.  Per block, in the precision of its path:
+// S^T = K Q^T (keys in krow order), p = 2^(t - L2); then O'^T += V^T P^T,
+// or dP^T = V dO^T, dS = p (dP - Dr) and dQ^T += K^T dS^T.  K^T and V^T are
+// read transposed from the row tiles; NVFP4's slice scale of K (dQ) or V
+// (O') multiplies the accumulator once, after the FP4 blocks.
 template <int D, int MODE, int NW>
-__global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
-  using L = RowLds<D>;
-  constexpr int NT = NW * 64;
-  constexpr int PK = kBlkK * D / 8 / NT;  // 16-byte pieces of a K or V block per thread
-  constexpr int PT = D * kBlkK / 8 / NT;  // of the transposed block
-  __shared__ __attribute__((aligned(16))) char smem[L::SIZE];
+__global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void bwd_row_kernel(BwdArgs a) {
+  using R = RowStage<D>;
+  __shared__ __attribute__((aligned(16))) char smem[2 * R::SIZE];
   __shared__ uint32_t pmw[kMaxKw];  // this row of promoted-block bits
   const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), hi = lane >> 5, r32 = lane & 31;
   const int BHq = a.B * a.Hq, G = a.Hq / a.Hkv;
@@ -215,15 +255,12 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
   const int qrow = q0 + r32;
   const bool qok = qrow < S;  // waves past S still pass every barrier
 
+  // B operands: Q of the current path (FP4-decoded first), dO (dQ mode)
   const auto qrs = rsrc(a.q16 + (size_t)bhq * S * D, S * D * 2);
   const auto qdrs = rsrc(a.qd + (size_t)bhq * S * D, S * D * 2);
-  v8h qh[D / 16], qd[D / 16], dh[D / 16];
+  v8h qx[D / 16], dh[MODE == kModeDq ? D / 16 : 1];
 #pragma unroll
-  for (int kk = 0; kk < D / 16; ++kk) {
-    const int off = (qrow * D + kk * 16 + hi * 8) * 2;
-    qh[kk] = ld8h(qrs, off);
-    qd[kk] = ld8h(qdrs, off);
-  }
+  for (int kk = 0; kk < D / 16; ++kk) qx[kk] = ld8h(qdrs, (qrow * D + kk * 16 + hi * 8) * 2);
   if constexpr (MODE == kModeDq) {
     const auto drs = rsrc(a.do16 + (size_t)bhq * S * D, S * D * 2);
 #pragma unroll
@@ -234,79 +271,85 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
   // NVFP4: FP4 pairs' scores and dP carry the slice scales (exact fp32 factors)
   const float cq4 = a.tq ? a.c * a.tq[bhq] * a.tk[bhk] : a.c;
   const float dpf4 = a.tv ? a.tv[bhk] : 1.0f;
+  const float tacc = MODE == kModeDq ? (a.tk ? a.tk[bhk] : 1.0f) : dpf4;  // the FP4 blocks' operand scale
 
   v16f acc[D / 32];
 #pragma unroll
   for (int dt = 0; dt < D / 32; ++dt) acc[dt] = v16f{};
 
-  const auto k16rs = rsrc(a.k16 + bhk * S * D, S * D * 2);
+  const auto k16rs = rsrc(a.k16 + bhk * S * D, S * D * 2);  // rows past S read as zeros
   const auto kdrs = rsrc(a.kd + bhk * S * D, S * D * 2);
   const auto v16rs = rsrc(a.v16 + bhk * S * D, S * D * 2);
   const auto vdrs = rsrc(a.vd + bhk * Sp * D, Sp * D * 2);
   const uint32_t* pm = a.prom + ((size_t)bhq * a.nq + i) * a.nkw;
   const int nvalid = valid_kv_blocks(i, S, a.bq, kBlkK, a.causal);
-  for (int k = t; k < a.nkw; k += NT) pmw[k] = pm[k];
+  for (int k = t; k < a.nkw; k += NW * 64) pmw[k] = pm[k];
   __syncthreads();
 
-  v4i pk[PK], pv[PK], pt[PT];
-  auto promoted = [&](int j) { return ((pmw[j >> 5] >> (j & 31)) & 1u) != 0; };
-  auto fetch = [&](int j) {
-    const bool f16 = promoted(j);
-    const auto krs = f16 ? k16rs : kdrs;
-    const auto vrs = f16 ? v16rs : vdrs;
-    const _Float16* T = (MODE == kModeOhp ? (f16 ? a.vt : a.vdt) : (f16 ? a.kt : a.kdt)) + bhk * D * Sp;
-#pragma unroll
-    for (int u = 0; u < PK; ++u) {
-      const int c = t + u * NT, row = c / (D / 8), c8 = c % (D / 8);
-      const int off = ((j * kBlkK + row) * D + c8 * 8) * 2;
-      pk[u] = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);
-      if constexpr (MODE == kModeDq) pv[u] = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);
+  // the first block j' >= j of path ph (1: promoted), or nvalid
+  auto next_blk = [&](int j, int ph) {
+    while (j < nvalid) {
+      uint32_t wd = __builtin_amdgcn_readfirstlane(pmw[j >> 5]);
+      wd = (ph ? wd : ~wd) & (~0u << (j & 31));
+      if (wd) {
+        const int jj = (j & ~31) + __builtin_ctz(wd);
+        return jj < nvalid ? jj : nvalid;
+      }
+      j = (j & ~31) + 32;
     }
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int c = t + u * NT, d = c / (kBlkK / 8), k8 = c % (kBlkK / 8);
-      pt[u] = *(const v4i*)(T + (size_t)d * Sp + j * kBlkK + k8 * 8);
-    }
+    return nvalid;
   };
-  auto stash = [&]() {
-#pragma unroll
-    for (int u = 0; u < PK; ++u) {
-      const int c = t + u * NT, row = c / (D / 8), c8 = c % (D / 8);
-      *(v4i*)(smem + L::K + (row * L::KR + c8 * 8) * 2) = pk[u];
-      if constexpr (MODE == kModeDq) *(v4i*)(smem + L::V + (row * L::KR + c8 * 8) * 2) = pv[u];
-    }
-#pragma unroll
-    for (int u = 0; u < PT; ++u) {
-      const int c = t + u * NT, d = c / (kBlkK / 8), k8 = c % (kBlkK / 8);
-      *(v4i*)(smem + L::T + (d * L::TR + k8 * 8) * 2) = pt[u];
-    }
+  // this lane's direct-load source row (key krow(hi, r32) of a block, chunk
+  // column w of the tile) and its transposed-read base (see below)
+  const uint32_t loff = krow(hi, r32) * (D * 2) + w * 16;
+  const int rr = r32 & 15;
+  const uint32_t tb = (2 * (r32 >> 4) + ((rr & 3) >> 1)) * R::CS + (hi * 4 + (rr >> 2)) * 16 + (rr & 1) * 8;
+  auto issue = [&](char* buf, int j, int ph) {
+    row_issue<D, NW>(buf, ph ? k16rs : kdrs, ph ? v16rs : vdrs, loff + j * (kBlkK * D * 2), w);
   };
 
-  if (nvalid > 0) fetch(0);
-  for (int j = 0; j < nvalid; ++j) {
-    const bool f16 = promoted(j);
-    __syncthreads();  // every wave is done with the previous block
-    stash();
-    __syncthreads();
-    if (j + 1 < nvalid) fetch(j + 1);
-    const _Float16* ks = (const _Float16*)(smem + L::K);
-    v16f s[2];
+  int jc = next_blk(0, 0), pc = 0;
+  if (jc >= nvalid) {
+    jc = next_blk(0, 1);
+    pc = 1;
+  }
+  int qph = 0;  // path whose Q operand qx holds
+  if (jc < nvalid) issue(smem, jc, pc);
+  for (int n = 0; jc < nvalid; ++n) {
+    int jn = next_blk(jc + 1, pc), pn = pc;
+    if (jn >= nvalid && pc == 0) {
+      jn = next_blk(0, 1);
+      pn = 1;
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // this block's tiles are in; every wave is done with the previous block
+    if (jn < nvalid) issue(smem + ((n + 1) & 1) * R::SIZE, jn, pn);
+    if (pc != qph) {  // from the FP4 blocks to the promoted ones
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= tacc;
+#pragma unroll
+      for (int kk = 0; kk < D / 16; ++kk) qx[kk] = ld8h(qrs, (qrow * D + kk * 16 + hi * 8) * 2);
+      qph = pc;
+    }
+    const bool f16 = pc != 0;
+    const char* buf = smem + (n & 1) * R::SIZE;
+    // S^T (and dP^T): lane (r32, hi) reads chunk 2 kk + hi of slot mt*32 + r32
+    const char* kb = buf + R::K + hi * R::CS + r32 * 16;
+    const char* vb = buf + R::V + hi * R::CS + r32 * 16;
+    v16f s[2], dp[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
       s[mt] = v16f{};
-      const _Float16* kr = ks + krow(mt, r32) * L::KR + hi * 8;
 #pragma unroll
-      for (int kk = 0; kk < D / 16; ++kk) s[mt] = mfma_f16(*(const v8h*)(kr + kk * 16), f16 ? qh[kk] : qd[kk], s[mt]);
+      for (int kk = 0; kk < D / 16; ++kk) s[mt] = mfma_f16(*(const v8h*)(kb + kk * 2 * R::CS + mt * 512), qx[kk], s[mt]);
     }
-    v16f dp[2];
     if constexpr (MODE == kModeDq) {
-      const _Float16* vs = (const _Float16*)(smem + L::V);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         dp[mt] = v16f{};
-        const _Float16* vr = vs + krow(mt, r32) * L::KR + hi * 8;
 #pragma unroll
-        for (int kk = 0; kk < D / 16; ++kk) dp[mt] = mfma_f16(*(const v8h*)(vr + kk * 16), dh[kk], dp[mt]);
+        for (int kk = 0; kk < D / 16; ++kk)
+          dp[mt] = mfma_f16(*(const v8h*)(vb + kk * 2 * R::CS + mt * 512), dh[kk], dp[mt]);
       }
     }
     // B operand of the second product: step st holds keys hi*32 + 8 st + u,
@@ -316,21 +359,32 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) {
-        const int key = j * kBlkK + hi * 32 + mt * 16 + ii;
+        const int key = jc * kBlkK + hi * 32 + mt * 16 + ii;
         const bool ok = qok && key < S && !(a.causal && key > qrow);
         const float p = ok ? exp2_fast(__builtin_fmaf(s[mt][ii], f16 ? a.c : cq4, -L2)) : 0.0f;
         float v = p;
         if constexpr (MODE == kModeDq) v = p * (dp[mt][ii] * (f16 ? 1.0f : dpf4) - Dr);
         pb[mt * 2 + ii / 8][ii % 8] = (_Float16)v;
       }
-    const _Float16* ts = (const _Float16*)(smem + L::T);
+    // A operand K^T (dQ) or V^T (O') read transposed: lane r of each 16
+    // addresses key hi*32 + 8 st + 4 h2 + r / 4 (slot kslot_of) and channels
+    // dt*32 + 16 (r32 / 16) + 4 (r % 4) .. + 3; it receives channel
+    // dt*32 + r32 of 4 keys per read (h2 = 0, 1: the step's 8 keys)
+    const char* tt = buf + (MODE == kModeDq ? R::K : R::V) + tb;
 #pragma unroll
     for (int st = 0; st < 4; ++st)
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const v8h tv = *(const v8h*)(ts + (dt * 32 + r32) * L::TR + hi * 32 + st * 8);
-        acc[dt] = mfma_f16(tv, pb[st], acc[dt]);
+        const int o0 = 4 * dt * R::CS + kslot_of(8 * st) * 16;
+        const int o1 = 4 * dt * R::CS + kslot_of(8 * st + 4) * 16;
+        acc[dt] = mfma_f16(tr_read(tt, o0, o1), pb[st], acc[dt]);
       }
+    jc = jn;
+    pc = pn;
+  }
+  if (qph == 0) {  // only FP4 blocks (or none)
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= tacc;
   }
   if (!qok) return;
   const float f = MODE == kModeDq ? a.sm_scale : 1.0f;
@@ -343,22 +397,6 @@ __global__ __launch_bounds__(NW * 64) void bwd_row_kernel(BwdArgs a) {
       *(float4*)(dst + d0) = make_float4(acc[dt][i4 * 4] * f, acc[dt][i4 * 4 + 1] * f, acc[dt][i4 * 4 + 2] * f,
                                          acc[dt][i4 * 4 + 3] * f);
     }
-}
-
-// ---- key kernel: one lane per key (dK, dV) -------------------------------------
-
-__device__ inline __attribute__((address_space(3))) void* lds_ptr(char* p) {
-  return (__attribute__((address_space(3))) void*)p;
-}
-
-// Eight halves of a transposed operand: ds_read_b64_tr_b16 at tile + o0 and
-// tile + o1 (elements 0-3 and 4-7).
-__device__ inline v8h tr_read(const char* tile, uint32_t o0, uint32_t o1) {
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  typedef __attribute__((address_space(3))) v4s* lp;
-  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(tile + o0));
-  const v4s up = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lp)(tile + o1));
-  return __builtin_bit_cast(v8h, __builtin_shufflevector(lo, up, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
 // The key kernels: one for dV, one for dK (each holds one set of
@@ -726,7 +764,7 @@ __global__ __launch_bounds__(256, MODE == kKeyDv ? 3 : 2) void bwd_key_kernel(Bw
 // ---- host side -----------------------------------------------------------------------
 
 struct BwdLayout {
-  size_t qd, qds, kd, kt, kdt, vd, vt, vdt, prom, drow, lse2, total;
+  size_t qd, qds, kd, vd, vdt, prom, drow, lse2, total;
 };
 
 inline size_t al256(size_t x) { return (x + 255) / 256 * 256; }
@@ -745,10 +783,7 @@ BwdLayout bwd_layout(int B, int Hq, int Hkv, int S, int D, int bq) {
   l.qd = take(bhq * S * D * 2);
   l.qds = take(bhq * S * D * 2);
   l.kd = take(bhk * S * D * 2);
-  l.kt = take(bhk * D * Sp * 2);
-  l.kdt = take(bhk * D * Sp * 2);
   l.vd = take(bhk * Sp * D * 2);
-  l.vt = take(bhk * D * Sp * 2);
   l.vdt = take(bhk * D * Sp * 2);
   l.prom = take(bhq * nq * nkw * 4);
   l.drow = take(bhq * S * 4);
@@ -795,11 +830,11 @@ void launch_transpose(const _Float16* in, int BH, int R, int C, int Rout, _Float
   transpose_kernel<<<grid, 256, 0, stream>>>(in, R, C, Rout, tsc, out);
 }
 
-// Fills the FP4-decoded and transposed operands both entry points share.
-// FP4-decoded operands keep NVFP4's slice scale out (exact fp16, the scale
-// applied to the fp32 scores and dP); the operands that are only ever on
-// the reduction side (K^T for dQ, V^T for O', and for dK the decoded Q rows,
-// which the key kernel reads transposed) carry it, rounded once.
+// Fills the FP4-decoded operands both entry points share.  They keep
+// NVFP4's slice scale out (exact fp16): the scale multiplies the fp32 scores
+// and dP, and the row kernel's accumulator after its FP4 blocks; only the
+// key kernel's dK operand, the decoded Q rows times Q's slice scale, carries
+// it, rounded once.
 void prepare(BwdArgs& a, char* ws, const BwdLayout& l, const void* q16, const void* k16, const void* v16,
              const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c, const uint8_t* k4s,
              const float* k4t, const uint8_t* v4c, const uint8_t* v4s, const float* v4t, int fmt,
@@ -813,9 +848,6 @@ void prepare(BwdArgs& a, char* ws, const BwdLayout& l, const void* q16, const vo
   a.kd = (const _Float16*)(ws + l.kd);
   a.vd = (const _Float16*)(ws + l.vd);
   a.qds = (const _Float16*)(ws + l.qds);
-  a.kt = (const _Float16*)(ws + l.kt);
-  a.kdt = (const _Float16*)(ws + l.kdt);
-  a.vt = (const _Float16*)(ws + l.vt);
   a.vdt = (const _Float16*)(ws + l.vdt);
   a.prom = (const uint32_t*)(ws + l.prom);
   a.lse = lse;
@@ -839,19 +871,13 @@ void prepare(BwdArgs& a, char* ws, const BwdLayout& l, const void* q16, const vo
   const int BHq = B * Hq, BHk = B * Hkv;
   launch_decode(q4c, q4s, (size_t)BHq * S, D, fmt, nullptr, S, (_Float16*)a.qd, stream);
   launch_decode(k4c, k4s, (size_t)BHk * S, D, fmt, nullptr, S, (_Float16*)a.kd, stream);
-  // V^T: with the slice scale for O' (reduction side), without for the rows of dP
-  launch_decode(v4c, v4s, (size_t)BHk * nk * D, kBlkK, fmt, backward ? nullptr : a.tv, (size_t)nk * D,
-                (_Float16*)a.vdt, stream, D, nk);
+  // V decodes to V^T blocks (its storage order), then to rows
+  launch_decode(v4c, v4s, (size_t)BHk * nk * D, kBlkK, fmt, nullptr, (size_t)nk * D, (_Float16*)a.vdt, stream, D,
+                nk);
+  launch_transpose(a.vdt, BHk, D, Sp, D, (_Float16*)a.vd, stream);  // [Sp][D]
   const int nrows = BHq * a.nq;
   prom_bits_kernel<<<cdiv(nrows, 256), 256, 0, stream>>>(idx, cnt, nrows, kmax, nk, a.nkw, (uint32_t*)a.prom);
-  if (backward) {
-    launch_transpose(a.vdt, BHk, D, Sp, D, (_Float16*)a.vd, stream);  // [Sp][D]
-    if (nv) launch_decode(q4c, q4s, (size_t)BHq * S, D, fmt, a.tq, S, (_Float16*)a.qds, stream);
-    launch_transpose(a.k16, BHk, S, D, Sp, (_Float16*)a.kt, stream);
-    launch_transpose(a.kd, BHk, S, D, Sp, (_Float16*)a.kdt, stream, a.tk);
-  } else {
-    launch_transpose(a.v16, BHk, S, D, Sp, (_Float16*)a.vt, stream);
-  }
+  if (backward && nv) launch_decode(q4c, q4s, (size_t)BHq * S, D, fmt, a.tq, S, (_Float16*)a.qds, stream);
 }
 
 template <int D>

@@ -433,9 +433,10 @@ thrift_status thrift_attention_decode_noalloc(const void* q16, const void* k16, 
  * D 64 or 128, block_q 64 or 128, block_k 64, S <= 262144. */
 
 /* Workspace bytes both calls below need: FP4-decoded fp16 copies of Q (and
- * of Q times its NVFP4 slice scale), FP4-decoded and transposed fp16 copies
- * of K and V, the promoted-block bit table, the row terms and the rows'
- * log-sum-exp in log2 units (about 2 Q-sized and 6 K-sized fp16 tensors). */
+ * of Q times its NVFP4 slice scale), K and V (V in rows and in its stored
+ * transposed order), the promoted-block bit table, the row terms and the
+ * rows' log-sum-exp in log2 units (about 2 Q-sized and 3 K-sized fp16
+ * tensors). */
 size_t thrift_attention_bwd_workspace_bytes(int B, int Hq, int Hkv, int S, int D, int block_q);
 
 /* O' of the forward: ohp [B,Hq,S,D] fp32 (out) from the same inputs as
