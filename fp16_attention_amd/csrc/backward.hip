@@ -286,11 +286,17 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void bwd_row_kernel(BwdAr
   for (int k = t; k < a.nkw; k += NW * 64) pmw[k] = pm[k];
   __syncthreads();
 
-  // the first block j' >= j of path ph (1: promoted), or nvalid
+  // the first block j' >= j of path ph (1: promoted), or nvalid; the last
+  // bit word read stays in a register
+  int cwi = -1;
+  uint32_t cw = 0;
   auto next_blk = [&](int j, int ph) {
     while (j < nvalid) {
-      uint32_t wd = __builtin_amdgcn_readfirstlane(pmw[j >> 5]);
-      wd = (ph ? wd : ~wd) & (~0u << (j & 31));
+      if ((j >> 5) != cwi) {
+        cwi = j >> 5;
+        cw = __builtin_amdgcn_readfirstlane(pmw[cwi]);
+      }
+      const uint32_t wd = (ph ? cw : ~cw) & (~0u << (j & 31));
       if (wd) {
         const int jj = (j & ~31) + __builtin_ctz(wd);
         return jj < nvalid ? jj : nvalid;
@@ -352,6 +358,18 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void bwd_row_kernel(BwdAr
           dp[mt] = mfma_f16(*(const v8h*)(vb + kk * 2 * R::CS + mt * 512), dh[kk], dp[mt]);
       }
     }
+    // causal and tail mask, on the diagonal and tail blocks only: a lane's 32
+    // keys are consecutive, so both conditions are one threshold (rows past
+    // S keep their values: their outputs are never written)
+    if ((a.causal && jc * kBlkK + kBlkK - 1 > q0) || jc * kBlkK + kBlkK > S) {
+      const int last = a.causal && qrow < S - 1 ? qrow : S - 1;
+      const int lim = last - (jc * kBlkK + hi * 32);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii)
+          if (mt * 16 + ii > lim) s[mt][ii] = -INFINITY;
+    }
     // B operand of the second product: step st holds keys hi*32 + 8 st + u,
     // registers 8 (st % 2) + u of tile st / 2
     v8h pb[4];
@@ -359,9 +377,7 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void bwd_row_kernel(BwdAr
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) {
-        const int key = jc * kBlkK + hi * 32 + mt * 16 + ii;
-        const bool ok = qok && key < S && !(a.causal && key > qrow);
-        const float p = ok ? exp2_fast(__builtin_fmaf(s[mt][ii], f16 ? a.c : cq4, -L2)) : 0.0f;
+        const float p = exp2_fast(__builtin_fmaf(s[mt][ii], f16 ? a.c : cq4, -L2));
         float v = p;
         if constexpr (MODE == kModeDq) v = p * (dp[mt][ii] * (f16 ? 1.0f : dpf4) - Dr);
         pb[mt * 2 + ii / 8][ii % 8] = (_Float16)v;
@@ -606,6 +622,18 @@ __global__ __launch_bounds__(256, MODE == kKeyDv ? 3 : 2) void bwd_key_kernel(Bw
     const char* dob = buf + St::DO;
     const float* l2 = (const float*)(buf + St::L2);
     const float cj = f16 ? a.c : cq4;
+    // causal and tail mask, on diagonal and tail steps only: register ii of
+    // S holds query q0 + hi*16 + ii, so the valid queries of this lane's key
+    // are one range of ii
+    const int kw0 = jb * kBlkK + (w & 1) * 32;  // the wave's first key
+    const bool need_mask = (a.causal && kw0 + 31 > q0) || q0 + 31 >= S || kw0 + 31 >= S;
+    auto mask_s = [&](v16f& sc) {
+      const int qb = q0 + hi * 16;
+      const int lo = a.causal ? key - qb : 0, up = key < S ? S - 1 - qb : -1;
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii)
+        if (ii < lo || ii > up) sc[ii] = -INFINITY;
+    };
     v8h opA[2];  // A operand of the product: pt (dV) or dS (dK); step st holds queries hi*16 + 8 st + u
     if constexpr (DV) {
       // FP4 pairs: per query and P group, p * fa is the element over its
@@ -621,15 +649,18 @@ __global__ __launch_bounds__(256, MODE == kKeyDv ? 3 : 2) void bwd_key_kernel(Bw
           st = mfma_f16(kr[kk], *(const v8h*)(qrows + kk * 1024 + rrow[kk & 3]), st);
         // column r32 is query q0 + qperm(r32); register ii is key (ii/4)*8 + hi*4 + ii%4 of the wave's 32
         const int qm = q0 + qperm(r32);
+        if (need_mask) {  // keys past the query (causal) or past S, queries past S
+          const int lim = qm < S ? (a.causal && qm < S - 1 ? qm : S - 1) - kw0 : -1;
+#pragma unroll
+          for (int ii = 0; ii < 16; ++ii)
+            if ((ii >> 2) * 8 + hi * 4 + (ii & 3) > lim) st[ii] = -INFINITY;
+        }
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) {
-          const int kx = jb * kBlkK + (w & 1) * 32 + (ii >> 2) * 8 + hi * 4 + (ii & 3);
-          const bool ok = qm < S && kx < S && !(a.causal && kx > qm);
-          const float v = ok ? st[ii] : -INFINITY;
           if (ii < 8)
-            gm0 = fmaxf(gm0, v);
+            gm0 = fmaxf(gm0, st[ii]);
           else
-            gm1 = fmaxf(gm1, v);
+            gm1 = fmaxf(gm1, st[ii]);
         }
         gm0 = pair_max(gm0);
         gm1 = pair_max(gm1);
@@ -639,6 +670,7 @@ __global__ __launch_bounds__(256, MODE == kKeyDv ? 3 : 2) void bwd_key_kernel(Bw
       v16f s = v16f{};
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) s = mfma_f16(*(const v8h*)(qrows + kk * 1024 + rrow[kk & 3]), kr[kk], s);
+      if (need_mask) mask_s(s);
       // level 1 is the query's maximum over the whole 64-key tile: the two
       // waves of the block exchange their halves (every wave passes this
       // barrier on every step)
@@ -688,11 +720,7 @@ __global__ __launch_bounds__(256, MODE == kKeyDv ? 3 : 2) void bwd_key_kernel(Bw
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
         float pt[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int ii = u * 4 + e, q = q0 + hi * 16 + ii;
-          const bool ok = q < S && key < S && !(a.causal && key > q);
-          pt[e] = ok ? exp2_fast(__builtin_fmaf(s[ii], cj, -lv[e])) : 0.0f;
-        }
+        for (int e = 0; e < 4; ++e) pt[e] = exp2_fast(__builtin_fmaf(s[u * 4 + e], cj, -lv[e]));
         if (!f16) {
           const float4 a4 = *(const float4*)(wa + hi * 16 + u * 4);
           const float4 h4 = *(const float4*)(wh + hi * 16 + u * 4);
@@ -715,6 +743,7 @@ __global__ __launch_bounds__(256, MODE == kKeyDv ? 3 : 2) void bwd_key_kernel(Bw
         s = mfma_f16(*(const v8h*)(qrows + kk * 1024 + rrow[kk & 3]), kr[kk], s);
         dp = mfma_f16(*(const v8h*)(dob + kk * 1024 + rrow[kk & 3]), vr[kk], dp);
       }
+      if (need_mask) mask_s(s);
       const float* dr = (const float*)(buf + St::DR);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
@@ -723,9 +752,8 @@ __global__ __launch_bounds__(256, MODE == kKeyDv ? 3 : 2) void bwd_key_kernel(Bw
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w}, rv[4] = {r4.x, r4.y, r4.z, r4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int ii = u * 4 + e, q = q0 + hi * 16 + ii;
-          const bool ok = q < S && key < S && !(a.causal && key > q);
-          const float p = ok ? exp2_fast(__builtin_fmaf(s[ii], cj, -lv[e])) : 0.0f;
+          const int ii = u * 4 + e;
+          const float p = exp2_fast(__builtin_fmaf(s[ii], cj, -lv[e]));
           opA[ii / 8][ii % 8] = (_Float16)(p * (dp[ii] * (f16 ? 1.0f : dpf4) - rv[e]));
         }
       }
