@@ -548,23 +548,28 @@ __global__ __launch_bounds__(256, MODE == kKeyDv ? 3 : 2) void bwd_key_kernel(Bw
 
   // this lane's byte offsets: direct-load sources (row of slot r32 of column
   // 2p + hi, p = w + 4k), row reads (column 2kk + hi, by kk % 4) and
-  // transposed reads (by (2 st + h2 + 2 dt) % 4, see below)
-  uint32_t voff[PW];
+  // transposed reads (by (2 st + h2 + 2 dt) % 4, see below).  They are
+  // recomputed where used from an opaque copy of the lane index: held across
+  // the loop they were spilled, and each reload from scratch waited for the
+  // step's direct loads in flight before it.
+  uint32_t voff[PW], rrow[4], rtr[4];
+  auto lane_offsets = [&]() {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int h = ln >> 5, l32 = ln & 31, r = l32 & 15, g = l32 >> 4;
 #pragma unroll
-  for (int k = 0; k < PW; ++k) {
-    const int c = 2 * (w + 4 * k) + hi;
-    voff[k] = qperm((r32 - 4 * c) & 31) * (D * 2) + c * 16;
-  }
-  uint32_t rrow[4], rtr[4];
-  {
-    const int r = r32 & 15, g = r32 >> 4;
-    const int xq = hi * 4 + (r >> 2) + 8 * g + 4 * ((r & 3) >> 1);
+    for (int k = 0; k < PW; ++k) {
+      const int c = 2 * (w + 4 * k) + h;
+      voff[k] = qperm((l32 - 4 * c) & 31) * (D * 2) + c * 16;
+    }
+    const int xq = h * 4 + (r >> 2) + 8 * g + 4 * ((r & 3) >> 1);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      rrow[k] = hi * 512 + ((r32 + 8 * k + 4 * hi) & 31) * 16;
+      rrow[k] = h * 512 + ((l32 + 8 * k + 4 * h) & 31) * 16;
       rtr[k] = ((xq + 8 * k) & 31) * 16 + (2 * g + ((r & 3) >> 1)) * 512 + (r & 1) * 8;
     }
-  }
+  };
+  lane_offsets();
 
   // step sequence: for g < G, q0 from the first row that sees block j0, by 32
   const int qstart = a.causal ? (j0 * kBlkK / 32) * 32 : 0;
@@ -608,6 +613,7 @@ __global__ __launch_bounds__(256, MODE == kKeyDv ? 3 : 2) void bwd_key_kernel(Bw
     char* const buf = smem + (n & 1) * St::SIZE;
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // this step's tiles are in; every wave is done with the previous step
+    lane_offsets();
     uint32_t wn = 0;
     if (n + 1 < nsteps) {
       wn = __builtin_amdgcn_readfirstlane(wnext);
