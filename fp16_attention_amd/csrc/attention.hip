@@ -256,16 +256,16 @@ __device__ inline void load_k_mx(MxKOps<D>& k, const char* stage, int t, int lan
   const int hi = lane >> 5, r32 = lane & 31;
   const uint8_t* kc = (const uint8_t*)(stage + M::KC + t * M::KCODE);
   const uint8_t* ks = (const uint8_t*)(stage + M::KS + t * kBk * M::KSB);
+  // the scales' address from an opaque copy of the lane index: computed once
+  // and held across the key sweep it was spilled, and each reload from
+  // scratch waited for the ring's direct loads in flight
+  int lo = lane;
+  asm volatile("" : "+v"(lo));
+  const uint8_t* ksl = ks + (lo & 31) * (D == 128 ? 4 : 2);
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
     const int row = mt * 32 + r32;  // holds key krow(mt, r32)
-    // the scale's address from an opaque copy of the lane index: computed
-    // once and held across the key sweep it was spilled, and each reload
-    // from scratch waited for the ring's direct loads in flight
-    int lo = lane;
-    asm volatile("" : "+v"(lo));
-    const int rowo = mt * 32 + (lo & 31);
-    k.sc[mt] = (D == 128 ? *(const uint32_t*)(ks + rowo * 4) : (uint32_t)(*(const uint16_t*)(ks + rowo * 2))) >> (8 * hi);
+    k.sc[mt] = (D == 128 ? *(const uint32_t*)(ksl + mt * 128) : (uint32_t)(*(const uint16_t*)(ksl + mt * 64))) >> (8 * hi);
 #pragma unroll
     for (int kk = 0; kk < D / 64; ++kk)
       k.a[mt][kk] = *(const v4i*)(kc + row * (D / 2) + M::kswz(row, kk * 2 + hi) * 16);

@@ -52,6 +52,7 @@ CASES = {
     "dit_noncausal_d64_bq64_mx": (workload("dit", Hq=2, Hkv=2, S=300, bq=64), -1, 500, 1),
     "dit_noncausal_d64_bq64_nvfp4": (workload("dit", Hq=2, Hkv=2, S=300, bq=64), -1, 500, 0),
     "all_fp16": (workload("prefill", Hq=2, Hkv=1, S=256), -1, 10000, 1),
+    "all_fp16_nvfp4": (workload("prefill", Hq=2, Hkv=1, S=256), -1, 10000, 0),
     "no_fp16_mx": (workload("prefill", Hq=2, Hkv=1, S=256), -1, 0, 1),
     "no_fp16_nvfp4": (workload("prefill", Hq=2, Hkv=1, S=256), -1, 0, 0),
     "short_tail_mx": (workload("prefill", Hq=1, Hkv=1, S=37), -1, 500, 1),
