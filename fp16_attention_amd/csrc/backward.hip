@@ -16,7 +16,10 @@
 // All products run on the fp16 matrix cores: FP4-decoded operands are exact
 // in fp16 (NVFP4's slice scales enter as fp32 factors).  After a preparation
 // pass, the row kernel (one lane per query, as in the forward) computes O'
-// or dQ, and the key kernel (one lane per key) computes dK and dV.
+// or dQ, and the key kernel (one lane per key) computes dV in one launch and
+// dK in another.  Every kernel streams its operand tiles into LDS by direct
+// loads one step ahead and reads the transposed operands of its second
+// product from those row tiles (ds_read_b64_tr_b16).
 #include <hip/hip_runtime.h>
 
 #include "common.h"
@@ -97,11 +100,9 @@ __global__ __launch_bounds__(256) void decode_fp4_kernel(const uint8_t* codes, c
   *(v8h*)(out + dst) = o;
 }
 
-// out[bh][c][r] = in[bh][r][c] (times tsc[bh] when tsc is not NULL, one
-// rounding) for r < R, zero for R <= r < Rout; in rows of C halves.  64x64
-// tiles through LDS.
-__global__ __launch_bounds__(256) void transpose_kernel(const _Float16* in, int R, int C, int Rout,
-                                                        const float* tsc, _Float16* out) {
+// out[bh][c][r] = in[bh][r][c] for r < R, zero for R <= r < Rout; in rows
+// of C halves.  64x64 tiles through LDS.
+__global__ __launch_bounds__(256) void transpose_kernel(const _Float16* in, int R, int C, int Rout, _Float16* out) {
   // 64x64 tile through LDS with 16-byte loads and stores: a thread reads 8
   // consecutive columns of one row and writes 8 consecutive rows of one
   // output row (C and Rout are multiples of 8, the tile origin of 64)
@@ -121,14 +122,13 @@ __global__ __launch_bounds__(256) void transpose_kernel(const _Float16* in, int 
   }
   __syncthreads();
   _Float16* dst = out + bh * (size_t)C * Rout;
-  const float f = tsc ? tsc[bh] : 1.0f;
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int col = h * 32 + tr, c = c0 + col, r = r0 + t8;
     if (c < C && r < Rout) {
       v8h y;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) y[u] = tsc ? (_Float16)((float)tile[t8 + u][col] * f) : tile[t8 + u][col];
+      for (int u = 0; u < 8; ++u) y[u] = tile[t8 + u][col];
       *(v8h*)(dst + (size_t)c * Rout + r) = y;
     }
   }
@@ -858,10 +858,9 @@ void launch_decode(const uint8_t* codes, const uint8_t* scales, size_t R, int L,
                                                                        out, vD, vnb);
 }
 
-void launch_transpose(const _Float16* in, int BH, int R, int C, int Rout, _Float16* out, hipStream_t stream,
-                      const float* tsc = nullptr) {
+void launch_transpose(const _Float16* in, int BH, int R, int C, int Rout, _Float16* out, hipStream_t stream) {
   dim3 grid(cdiv(Rout > R ? Rout : R, 64) * cdiv(C, 64), BH);
-  transpose_kernel<<<grid, 256, 0, stream>>>(in, R, C, Rout, tsc, out);
+  transpose_kernel<<<grid, 256, 0, stream>>>(in, R, C, Rout, out);
 }
 
 // Fills the FP4-decoded operands both entry points share.  They keep
