@@ -35,6 +35,9 @@ CASES = {
     "none_fp16_nvfp4": (workload("prefill", Hq=2, Hkv=1, S=640), 0, -1, 0),
     "single_block": (workload("tiny", S=64), 1, 1, 0),
     "short_tail": (workload("prefill", Hq=1, Hkv=1, S=37), 1, -1, 500),
+    "short_tail_nvfp4": (workload("prefill", Hq=1, Hkv=1, S=37), 0, -1, 500),
+    "bq64_nvfp4": (workload("prefill", Hq=2, Hkv=2, S=513, bq=64), 0, -1, 1000),
+    "single_block_nvfp4": (workload("tiny", S=64), 0, 1, 0),
 }
 
 
