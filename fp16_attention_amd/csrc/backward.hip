@@ -498,10 +498,10 @@ __device__ inline void key_issue(const BwdArgs& a, char* buf, size_t bhq, int q0
 // column of S = Q K^T:
 //  - dV (MODE kKeyDv): p per element; on FP4 pairs the probability the
 //    forward used is rebuilt from its quantisation groups (MX: the wave's 32
-//    keys; NVFP4: 16-key groups under the 64-key tile maximum, which the
-//    block's two waves exchange), whose maxima come from S^T = K Q^T (same
-//    operands swapped, one lane per query) and are handed to the key-major
-//    lanes through the wave's own LDS slot; then dV += pt^T dO;
+//    keys; NVFP4: 16-key groups) under the 64-key tile maximum, which the
+//    block's two waves exchange; the maxima come from S^T = K Q^T (same
+//    operands swapped, one lane per query), and the per-query factors reach
+//    the key-major lanes through the wave's own LDS slot; then dV += pt^T dO;
 //  - dK (MODE kKeyDk): dP = dO V^T, dS = p (dP - Dr); dK += dS^T Q.
 // The dV and dK products read their dO and Q operands transposed from the
 // row tiles.  Only the K (and for dK the V) operands of the precision in use
