@@ -65,6 +65,8 @@ constexpr int kRegChunks = 8;
 //   1. T = the k-th largest key: the largest t with at least k keys >= t,
 //      found one bit at a time from the top; each count is a sum of ballot
 //      popcounts over the row's chunks (lane l of chunk c holds block c*64+l).
+//      The search stops early at a prefix with exactly k keys at or above
+//      it: those keys are then the selection whatever the lower bits of T.
 //   2. Every block with key > T is selected (fewer than k of them); of the
 //      blocks with key == T the lowest-indexed k - count(> T) are selected,
 //      ranked by a running ballot prefix in ascending block order.
@@ -95,7 +97,11 @@ __device__ inline void wave_topk(const float* srow, int n, int k, int32_t* __res
   if (k > 0)
     for (int bit = 31; bit >= 0; --bit) {
       const uint32_t cand = thr | (1u << bit);
-      if (count_ge(cand) >= k) thr = cand;
+      const int m = count_ge(cand);
+      if (m >= k) {
+        thr = cand;
+        if (m == k) break;  // step 2 then takes every key >= thr
+      }
     }
   // k > 0: thr >= the smallest finite key > 0, so padding (key 0) never ties
   const int need = k > 0 ? k - (thr == 0xFFFFFFFFu ? 0 : count_ge(thr + 1)) : 0;

@@ -68,6 +68,41 @@ VARIANT_CASES = {
 }
 
 
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("ties", ["groups", "all"])
+def test_selection_ties(oracle, causal, ties):
+    """Key blocks holding the same data score exactly alike.  For every
+    budget k the GPU selection equals the oracle's bit for bit: the k-th
+    largest score is found exactly (the search may stop early, once exactly
+    k scores lie at or above a prefix), and of the blocks tied at it the
+    lower-indexed ones are taken."""
+    import torch
+
+    from fp16_attention_amd import api
+
+    w = workload("prefill", Hq=2, Hkv=1, S=1024)  # 16 key blocks of 64, 8 query blocks of 128
+    note(f"[selection ties] {ties} causal{int(causal)}: B{w.B} Hq{w.Hq} Hkv{w.Hkv} S{w.S}")
+    d = W.generate(w)
+    k = d["k"].copy()
+    if ties == "groups":  # blocks 3, 5, 8, 12 alike, and 1, 9
+        for j in (5, 8, 12):
+            k[:, :, j * 64:(j + 1) * 64] = k[:, :, 3 * 64:4 * 64]
+        k[:, :, 9 * 64:10 * 64] = k[:, :, 64:128]
+    else:  # every block alike
+        for j in range(1, 16):
+            k[:, :, j * 64:(j + 1) * 64] = k[:, :, :64]
+    dev = torch.device("cuda:0")
+    qd, kd = torch.from_numpy(d["q"]).to(dev), torch.from_numpy(k).to(dev)
+    for tc in range(0, 17):
+        idx, cnt = api.thrift_select_blocks(qd, kd, w.bq, w.bk, causal, tc, 0)
+        r_idx, r_cnt, _ = oracle.select(d["q"], k, w.bq, w.bk, causal, tc, 0)
+        gi, gc = idx.cpu().numpy(), cnt.cpu().numpy()
+        assert np.array_equal(gc, r_cnt), f"cnt differs at k={tc}"
+        km = r_idx.shape[-1]
+        assert np.array_equal(gi[..., :km], r_idx), f"idx differs at k={tc}"
+        assert np.all(gi[..., km:] == -1)
+
+
 @pytest.mark.parametrize("name", list(VARIANT_CASES))
 def test_parity_nvfp4_tensors_mx_p(oracle, name):
     w, tc, bp = VARIANT_CASES[name]
