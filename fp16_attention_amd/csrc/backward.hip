@@ -51,7 +51,6 @@ struct BwdArgs {
   const _Float16 *qd, *kd;                 // FP4-decoded Q, K rows [B,H,S,D]
   const _Float16* qds;                     // FP4-decoded Q times its slice scale (NVFP4) [B,Hq,S,D]
   const _Float16* vd;                      // FP4-decoded V rows [B,Hkv,Sp,D]
-  const _Float16* vdt;                     // FP4-decoded V^T [B,Hkv,D,Sp] (vd's source)
   const uint32_t* prom;                    // promoted-block bits [B,Hq,nq,nkw]
   const float *lse, *drow, *lse2;          // [B,Hq,S]; lse2 = lse * log2(e)
   const float *tq, *tk, *tv;               // NVFP4 slice scales [B,H] (NULL for MXFP4)
@@ -63,28 +62,45 @@ struct BwdArgs {
 };
 
 // ---- preparation ------------------------------------------------------------------
+//
+// One launch fills every operand the backward kernels read.  Its workgroups
+// take, in blockIdx order, these roles:
+//   V    one per (batch*head, 64-key block): the block's stored V^T codes
+//        (key-block-major) decoded and written as 64 rows of D channels
+//        through an LDS tile, so no transposed copy is written;
+//   Q, K FP4 rows decoded to fp16 rows, one thread per 8 elements;
+//   QS   (NVFP4 backward) the decoded Q rows times Q's slice scale;
+//   RT   (backward) the row term dO[r] . O'[r] and the LSE in log2 units;
+//   PB   the promoted-block bits of each (batch, query head, query block).
+// E2M1 times a power of two (MX) or times an E4M3 value (NVFP4, at most 6
+// significant bits, 2^-10 .. 2688) is exact in fp16; a slice scale
+// multiplies in before the one rounding.
 
-// FP4 rows decoded to fp16: codes [R][L/2] (even element in the low
-// nibble), block scales [R][L/g] (MXFP4: E8M0, g = 32; NVFP4: E4M3, g = 16);
-// one thread per 8 elements.  Out [R][L]; or, with vD > 0, rows are V's
-// stored (batch*head, 64-token block, channel) rows of L = 64 tokens and go
-// to V^T [batch*head][vD][nb*64].  E2M1 times a power of two (MX) or times an
-// E4M3 value (NVFP4, at most 6 significant bits, 2^-10 .. 2688) is exact in
-// fp16; tsc (NVFP4 slice scales per batch*head of rows_per_bh rows, or
-// NULL) multiplies in before the one rounding.
-__global__ __launch_bounds__(256) void decode_fp4_kernel(const uint8_t* codes, const uint8_t* scales, size_t R,
-                                                         int L, int fmt, const float* tsc, size_t rows_per_bh,
-                                                         _Float16* out, int vD, int vnb) {
-  const size_t e8 = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const size_t n8 = R * (size_t)(L / 8);
-  if (e8 >= n8) return;
-  const size_t row = e8 / (L / 8);
-  const int c8 = (int)(e8 % (L / 8)) * 8;
+struct PrepArgs {
+  const uint8_t *q4c, *q4s, *k4c, *k4s, *v4c, *v4s;
+  const float* tq;  // NVFP4 slice scales of Q (QS role)
+  const int32_t *idx, *cnt;
+  const _Float16* do16;
+  const float *ohp, *lse;
+  _Float16 *qd, *kd, *vd, *qds;
+  uint32_t* prom;
+  float *drow, *lse2;
+  int fmt, S, nk, kmax, nkw;
+  size_t rq, rk, nrows_rt;  // rows of Q, of K, and of the row term
+  int nrows_pb;
+  // first workgroup of each role (V starts at 0); end is the grid size
+  unsigned wq, wk, wqs, wrt, wpb, wend;
+};
+
+// 8 FP4 elements of a row of L (codes [R][L/2], block scales [R][L/g]) at
+// element c8, times f0 (the slice scale, or 1), to fp16.
+__device__ inline v8h decode8(const uint8_t* codes, const uint8_t* scales, size_t row, int L, int c8, int fmt,
+                              float f0) {
   const uint32_t cw = *(const uint32_t*)(codes + row * (L / 2) + c8 / 2);
   const int g = fmt == THRIFT_MXFP4 ? 32 : 16;
   const uint32_t sb = scales[row * (L / g) + c8 / g];
   float f = fmt == THRIFT_MXFP4 ? ldexpf(1.0f, (int)sb - 127) : e4m3_to_float(sb);
-  if (tsc) f *= tsc[row / rows_per_bh];
+  f *= f0;
   const v2f v[4] = {__builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 0),
                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 1),
                     __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw, 1.0f, 2),
@@ -92,83 +108,97 @@ __global__ __launch_bounds__(256) void decode_fp4_kernel(const uint8_t* codes, c
   v8h o;
 #pragma unroll
   for (int e = 0; e < 8; ++e) o[e] = (_Float16)(v[e / 2][e % 2] * f);
-  size_t dst = row * L + c8;
-  if (vD > 0) {
-    const size_t d = row % vD, jb = (row / vD) % vnb, bh = row / ((size_t)vD * vnb);
-    dst = (bh * vD + d) * ((size_t)vnb * 64) + jb * 64 + c8;
-  }
-  *(v8h*)(out + dst) = o;
+  return o;
 }
 
-// out[bh][c][r] = in[bh][r][c] for r < R, zero for R <= r < Rout; in rows
-// of C halves.  64x64 tiles through LDS.
-__global__ __launch_bounds__(256) void transpose_kernel(const _Float16* in, int R, int C, int Rout, _Float16* out) {
-  // 64x64 tile through LDS with 16-byte loads and stores: a thread reads 8
-  // consecutive columns of one row and writes 8 consecutive rows of one
-  // output row (C and Rout are multiples of 8, the tile origin of 64)
-  __shared__ _Float16 tile[64][66];
-  const size_t bh = blockIdx.y;
-  const int ct = cdiv(C, 64);
-  const int r0 = (blockIdx.x / ct) * 64, c0 = (blockIdx.x % ct) * 64;
-  const int t = threadIdx.x, t8 = (t & 7) * 8, tr = t >> 3;
-  const _Float16* src = in + bh * (size_t)R * C;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int row = h * 32 + tr, r = r0 + row, c = c0 + t8;
-    v8h x = {};
-    if (r < R && c < C) x = *(const v8h*)(src + (size_t)r * C + c);
-#pragma unroll
-    for (int u = 0; u < 8; ++u) tile[row][t8 + u] = x[u];
-  }
-  __syncthreads();
-  _Float16* dst = out + bh * (size_t)C * Rout;
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int col = h * 32 + tr, c = c0 + col, r = r0 + t8;
-    if (c < C && r < Rout) {
-      v8h y;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) y[u] = tile[t8 + u][col];
-      *(v8h*)(dst + (size_t)c * Rout + r) = y;
-    }
-  }
-}
-
-// Promoted-block bits of each (batch, query head, query block).
-__global__ __launch_bounds__(256) void prom_bits_kernel(const int32_t* idx, const int32_t* cnt, int nrows,
-                                                        int kmax, int nk, int nkw, uint32_t* bits) {
-  const int row = blockIdx.x * 256 + threadIdx.x;
-  if (row >= nrows) return;
-  uint32_t* w = bits + (size_t)row * nkw;
-  for (int k = 0; k < nkw; ++k) w[k] = 0;
-  const int n = min(max(cnt[row], 0), kmax);
-  for (int s = 0; s < n; ++s) {
-    const int j = idx[(size_t)row * kmax + s];
-    if (j >= 0 && j < nk) w[j >> 5] |= 1u << (j & 31);
-  }
-}
-
-// Row term dO[r] . O'[r]: D/8 lanes per row (a 16-byte load of dO and two of
-// O' each), summed across those lanes; every lane reaches the shuffles.  Also
-// the row's log-sum-exp in log2 units, lse[r] * log2(e).
+// Rows [0, R) of L = D elements: thread e8 decodes elements 8*(e8 % (D/8))..
+// of row e8 / (D/8); tsc (or NULL) holds one slice scale per S rows.
 template <int D>
-__global__ __launch_bounds__(256) void row_term_kernel(const _Float16* do16, const float* ohp, const float* lse,
-                                                       size_t nrows, float* drow, float* lse2) {
-  constexpr int LPR = D / 8;  // lanes per row: 16 or 8, a divisor of the wave
-  const size_t row = ((size_t)blockIdx.x * 256 + threadIdx.x) / LPR;
-  const int sub = threadIdx.x % LPR;
-  float s = 0.0f;
-  if (row < nrows) {
-    const v8h h = *(const v8h*)(do16 + row * D + sub * 8);
-    const float4 x = *(const float4*)(ohp + row * D + sub * 8), y = *(const float4*)(ohp + row * D + sub * 8 + 4);
-    s = (float)h[0] * x.x + (float)h[1] * x.y + (float)h[2] * x.z + (float)h[3] * x.w + (float)h[4] * y.x +
-        (float)h[5] * y.y + (float)h[6] * y.z + (float)h[7] * y.w;
-  }
+__device__ inline void decode_rows(const uint8_t* codes, const uint8_t* scales, size_t R, int fmt, const float* tsc,
+                                   int S, _Float16* out, size_t e8) {
+  if (e8 >= R * (size_t)(D / 8)) return;
+  const size_t row = e8 / (D / 8);
+  const int c8 = (int)(e8 % (D / 8)) * 8;
+  const float f0 = tsc ? tsc[row / (size_t)S] : 1.0f;
+  *(v8h*)(out + row * D + c8) = decode8(codes, scales, row, D, c8, fmt, f0);
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(PrepArgs a) {
+  const unsigned wg = blockIdx.x;
+  const int t = threadIdx.x;
+  if (wg < a.wq) {
+    // V: stored block blk = bh * nk + j holds, per channel d, the codes of
+    // its 64 keys (32 bytes) and their block scales.  Thread (dp, kq)
+    // decodes channels 2dp and 2dp+1 of keys kq*KPG .. kq*KPG+KPG-1 and
+    // writes each key's channel pair as one word of the LDS tile [key][d]
+    // (a wave's lanes cover every bank once); the tile then goes out as
+    // rows, 16 bytes per thread and step.
+    constexpr int NP = D / 2, KPG = 64 / (256 / NP);  // channel pairs; keys per thread (16 or 8)
+    constexpr int RS = D + 8;                         // tile row stride in halves
+    __shared__ __attribute__((aligned(16))) _Float16 tile[64 * RS];
+    const size_t blk = wg;
+    const int j = (int)(blk % (size_t)a.nk);
+    const size_t bh = blk / (size_t)a.nk;
+    const int dp = t % NP, kq = t / NP;
+    v8h h[2][KPG / 8];
 #pragma unroll
-  for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
-  if (row < nrows && sub == 0) {
-    drow[row] = s;
-    lse2[row] = lse[row] * kLog2eB;
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+      for (int q = 0; q < KPG / 8; ++q) h[u][q] = decode8(a.v4c, a.v4s, blk * D + 2 * dp + u, 64, kq * KPG + q * 8, a.fmt, 1.0f);
+#pragma unroll
+    for (int e = 0; e < KPG; ++e) {
+      const v2h pr = {h[0][e / 8][e % 8], h[1][e / 8][e % 8]};
+      *(v2h*)(tile + (kq * KPG + e) * RS + 2 * dp) = pr;
+    }
+    __syncthreads();
+    _Float16* dst = a.vd + (bh * (size_t)a.nk + (size_t)j) * 64 * D;
+#pragma unroll
+    for (int it = 0; it < (64 * D / 8) / 256; ++it) {
+      const int c = t + it * 256, r = c / (D / 8), c8 = (c % (D / 8)) * 8;
+      *(v8h*)(dst + (size_t)r * D + c8) = *(const v8h*)(tile + r * RS + c8);
+    }
+    return;
+  }
+  // the other roles: element e of the role's range
+  const unsigned w0 = wg < a.wk ? a.wq : wg < a.wqs ? a.wk : wg < a.wrt ? a.wqs : wg < a.wpb ? a.wrt : a.wpb;
+  const size_t e = (size_t)(wg - w0) * 256 + t;
+  if (wg < a.wk) {
+    decode_rows<D>(a.q4c, a.q4s, a.rq, a.fmt, nullptr, a.S, a.qd, e);
+  } else if (wg < a.wqs) {
+    decode_rows<D>(a.k4c, a.k4s, a.rk, a.fmt, nullptr, a.S, a.kd, e);
+  } else if (wg < a.wrt) {
+    decode_rows<D>(a.q4c, a.q4s, a.rq, a.fmt, a.tq, a.S, a.qds, e);
+  } else if (wg < a.wpb) {
+    // row term: D/8 lanes per row (a 16-byte load of dO and two of O'
+    // each), summed across those lanes; every lane reaches the shuffles
+    constexpr int LPR = D / 8;  // 16 or 8, a divisor of the wave
+    const size_t row = e / LPR;
+    const int sub = t % LPR;
+    float s = 0.0f;
+    if (row < a.nrows_rt) {
+      const v8h h = *(const v8h*)(a.do16 + row * D + sub * 8);
+      const float4 x = *(const float4*)(a.ohp + row * D + sub * 8),
+                   y = *(const float4*)(a.ohp + row * D + sub * 8 + 4);
+      s = (float)h[0] * x.x + (float)h[1] * x.y + (float)h[2] * x.z + (float)h[3] * x.w + (float)h[4] * y.x +
+          (float)h[5] * y.y + (float)h[6] * y.z + (float)h[7] * y.w;
+    }
+#pragma unroll
+    for (int o = LPR / 2; o >= 1; o >>= 1) s += __shfl_xor(s, o, kWave);
+    if (row < a.nrows_rt && sub == 0) {
+      a.drow[row] = s;
+      a.lse2[row] = a.lse[row] * kLog2eB;
+    }
+  } else {
+    const size_t row = e;
+    if (row >= (size_t)a.nrows_pb) return;
+    uint32_t* w = a.prom + row * a.nkw;
+    for (int k = 0; k < a.nkw; ++k) w[k] = 0;
+    const int n = min(max(a.cnt[row], 0), a.kmax);
+    for (int s = 0; s < n; ++s) {
+      const int jj = a.idx[row * a.kmax + s];
+      if (jj >= 0 && jj < a.nk) w[jj >> 5] |= 1u << (jj & 31);
+    }
   }
 }
 
@@ -798,7 +828,7 @@ __global__ __launch_bounds__(256, MODE == kKeyDv ? 3 : 2) void bwd_key_kernel(Bw
 // ---- host side -----------------------------------------------------------------------
 
 struct BwdLayout {
-  size_t qd, qds, kd, vd, vdt, prom, drow, lse2, total;
+  size_t qd, qds, kd, vd, prom, drow, lse2, total;
 };
 
 inline size_t al256(size_t x) { return (x + 255) / 256 * 256; }
@@ -818,7 +848,6 @@ BwdLayout bwd_layout(int B, int Hq, int Hkv, int S, int D, int bq) {
   l.qds = take(bhq * S * D * 2);
   l.kd = take(bhk * S * D * 2);
   l.vd = take(bhk * Sp * D * 2);
-  l.vdt = take(bhk * D * Sp * 2);
   l.prom = take(bhq * nq * nkw * 4);
   l.drow = take(bhq * S * 4);
   l.lse2 = take(bhq * S * 4);
@@ -851,18 +880,6 @@ thrift_status check_bwd(const void* q16, const void* k16, const void* v16, const
   return THRIFT_OK;
 }
 
-void launch_decode(const uint8_t* codes, const uint8_t* scales, size_t R, int L, int fmt, const float* tsc,
-                   size_t rows_per_bh, _Float16* out, hipStream_t stream, int vD = 0, int vnb = 0) {
-  const size_t n8 = R * (size_t)(L / 8);
-  decode_fp4_kernel<<<(unsigned)((n8 + 255) / 256), 256, 0, stream>>>(codes, scales, R, L, fmt, tsc, rows_per_bh,
-                                                                       out, vD, vnb);
-}
-
-void launch_transpose(const _Float16* in, int BH, int R, int C, int Rout, _Float16* out, hipStream_t stream) {
-  dim3 grid(cdiv(Rout > R ? Rout : R, 64) * cdiv(C, 64), BH);
-  transpose_kernel<<<grid, 256, 0, stream>>>(in, R, C, Rout, out);
-}
-
 // Fills the FP4-decoded operands both entry points share.  They keep
 // NVFP4's slice scale out (exact fp16): the scale multiplies the fp32 scores
 // and dP, and the row kernel's accumulator after its FP4 blocks; only the
@@ -872,16 +889,17 @@ void prepare(BwdArgs& a, char* ws, const BwdLayout& l, const void* q16, const vo
              const uint8_t* q4c, const uint8_t* q4s, const float* q4t, const uint8_t* k4c, const uint8_t* k4s,
              const float* k4t, const uint8_t* v4c, const uint8_t* v4s, const float* v4t, int fmt,
              const int32_t* idx, const int32_t* cnt, int kmax, int B, int Hq, int Hkv, int S, int D, int block_q,
-             int causal, float sm_scale, const float* lse, bool backward, hipStream_t stream) {
+             int causal, float sm_scale, const float* lse, const void* do16, const float* ohp, hipStream_t stream) {
+  const bool backward = do16 != nullptr;
   const int Sp = cdiv(S, kBlkK) * kBlkK, nk = cdiv(S, kBlkK);
   a.q16 = (const _Float16*)q16;
   a.k16 = (const _Float16*)k16;
   a.v16 = (const _Float16*)v16;
+  a.do16 = (const _Float16*)do16;
   a.qd = (const _Float16*)(ws + l.qd);
   a.kd = (const _Float16*)(ws + l.kd);
   a.vd = (const _Float16*)(ws + l.vd);
   a.qds = (const _Float16*)(ws + l.qds);
-  a.vdt = (const _Float16*)(ws + l.vdt);
   a.prom = (const uint32_t*)(ws + l.prom);
   a.lse = lse;
   a.drow = (const float*)(ws + l.drow);
@@ -901,16 +919,47 @@ void prepare(BwdArgs& a, char* ws, const BwdLayout& l, const void* q16, const vo
   a.tv = nv ? v4t : nullptr;
   a.sm_scale = sm_scale;
   a.c = sm_scale * kLog2eB;
-  const int BHq = B * Hq, BHk = B * Hkv;
-  launch_decode(q4c, q4s, (size_t)BHq * S, D, fmt, nullptr, S, (_Float16*)a.qd, stream);
-  launch_decode(k4c, k4s, (size_t)BHk * S, D, fmt, nullptr, S, (_Float16*)a.kd, stream);
-  // V decodes to V^T blocks (its storage order), then to rows
-  launch_decode(v4c, v4s, (size_t)BHk * nk * D, kBlkK, fmt, nullptr, (size_t)nk * D, (_Float16*)a.vdt, stream, D,
-                nk);
-  launch_transpose(a.vdt, BHk, D, Sp, D, (_Float16*)a.vd, stream);  // [Sp][D]
-  const int nrows = BHq * a.nq;
-  prom_bits_kernel<<<cdiv(nrows, 256), 256, 0, stream>>>(idx, cnt, nrows, kmax, nk, a.nkw, (uint32_t*)a.prom);
-  if (backward && nv) launch_decode(q4c, q4s, (size_t)BHq * S, D, fmt, a.tq, S, (_Float16*)a.qds, stream);
+  const size_t BHq = (size_t)B * Hq, BHk = (size_t)B * Hkv;
+  PrepArgs p{};
+  p.q4c = q4c;
+  p.q4s = q4s;
+  p.k4c = k4c;
+  p.k4s = k4s;
+  p.v4c = v4c;
+  p.v4s = v4s;
+  p.tq = a.tq;
+  p.idx = idx;
+  p.cnt = cnt;
+  p.do16 = a.do16;
+  p.ohp = ohp;
+  p.lse = lse;
+  p.qd = (_Float16*)a.qd;
+  p.kd = (_Float16*)a.kd;
+  p.vd = (_Float16*)a.vd;
+  p.qds = (_Float16*)a.qds;
+  p.prom = (uint32_t*)a.prom;
+  p.drow = (float*)a.drow;
+  p.lse2 = (float*)a.lse2;
+  p.fmt = fmt;
+  p.S = S;
+  p.nk = nk;
+  p.kmax = kmax;
+  p.nkw = a.nkw;
+  p.rq = BHq * S;
+  p.rk = BHk * S;
+  p.nrows_rt = backward ? BHq * S : 0;
+  p.nrows_pb = (int)BHq * a.nq;
+  auto wgs = [](size_t threads) { return (unsigned)((threads + 255) / 256); };
+  p.wq = (unsigned)(BHk * nk);
+  p.wk = p.wq + wgs(p.rq * (D / 8));
+  p.wqs = p.wk + wgs(p.rk * (D / 8));
+  p.wrt = p.wqs + (backward && nv ? wgs(p.rq * (D / 8)) : 0);
+  p.wpb = p.wrt + wgs(p.nrows_rt * (D / 8));
+  p.wend = p.wpb + wgs((size_t)p.nrows_pb);
+  if (D == 128)
+    bwd_prep_kernel<128><<<p.wend, 256, 0, stream>>>(p);
+  else
+    bwd_prep_kernel<64><<<p.wend, 256, 0, stream>>>(p);
 }
 
 template <int D>
@@ -943,8 +992,6 @@ template __global__ void bwd_row_kernel<128, kModeOhp, 2>(BwdArgs);
 template __global__ void bwd_row_kernel<128, kModeDq, 2>(BwdArgs);
 template __global__ void bwd_row_kernel<64, kModeOhp, 2>(BwdArgs);
 template __global__ void bwd_row_kernel<64, kModeDq, 2>(BwdArgs);
-template __global__ void row_term_kernel<128>(const _Float16*, const float*, const float*, size_t, float*, float*);
-template __global__ void row_term_kernel<64>(const _Float16*, const float*, const float*, size_t, float*, float*);
 
 }  // namespace
 
@@ -973,7 +1020,7 @@ extern "C" thrift_status thrift_attention_fwd_hp(
   BwdArgs a{};
   prepare(a, (char*)workspace, l, q16, k16, v16, q4_codes, q4_scales, q4_tscale, k4_codes, k4_scales, k4_tscale,
           v4_codes, v4_scales, v4_tscale, fmt, idx, cnt, kmax, B, Hq, Hkv, S, D, block_q, causal, sm_scale, lse,
-          false, stream);
+          nullptr, nullptr, stream);
   a.out = ohp;
   if (D == 128)
     launch_row<128>(a, kModeOhp, stream);
@@ -999,15 +1046,8 @@ extern "C" thrift_status thrift_attention_bwd(
   BwdArgs a{};
   char* ws = (char*)workspace;
   prepare(a, ws, l, q16, k16, v16, q4_codes, q4_scales, q4_tscale, k4_codes, k4_scales, k4_tscale, v4_codes,
-          v4_scales, v4_tscale, fmt, idx, cnt, kmax, B, Hq, Hkv, S, D, block_q, causal, sm_scale, lse, true, stream);
-  const int BHq = B * Hq;
-  a.do16 = (const _Float16*)do16;
-  const size_t nrows = (size_t)BHq * S;
-  const unsigned rt_grid = (unsigned)((nrows * (size_t)(D / 8) + 255) / 256);
-  if (D == 128)
-    row_term_kernel<128><<<rt_grid, 256, 0, stream>>>(a.do16, ohp, lse, nrows, (float*)a.drow, (float*)a.lse2);
-  else
-    row_term_kernel<64><<<rt_grid, 256, 0, stream>>>(a.do16, ohp, lse, nrows, (float*)a.drow, (float*)a.lse2);
+          v4_scales, v4_tscale, fmt, idx, cnt, kmax, B, Hq, Hkv, S, D, block_q, causal, sm_scale, lse, do16, ohp,
+          stream);
   a.out = dq;
   a.dk = dk;
   a.dv = dv;
