@@ -31,6 +31,9 @@ constexpr int kBlkK = 64;  // key block
 constexpr int kMaxS = 262144;
 constexpr int kMaxKw = kMaxS / kBlkK / 32;  // promoted-bit words per query block row
 constexpr float kLog2eB = 1.44269504088896341f;
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt at their maxima), as an instruction
+// the compiler's wait insertion sees (an inline-asm wait it cannot read)
+constexpr int kWaitVm0 = 0x0F70;
 
 typedef float v2f __attribute__((ext_vector_type(2)));
 
@@ -271,8 +274,11 @@ __device__ inline void row_issue(char* buf, __amdgpu_buffer_rsrc_t krs, __amdgpu
 template <int D, int MODE, int NW>
 __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void bwd_row_kernel(BwdArgs a) {
   using R = RowStage<D>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * R::SIZE];
-  __shared__ uint32_t pmw[kMaxKw];  // this row of promoted-block bits
+  // one LDS object: the two stages, then this row of promoted-block bits
+  // (with a second __shared__ array the compiler waited for the next
+  // stage's direct loads before every read of the current one)
+  __shared__ __attribute__((aligned(16))) char smem[2 * R::SIZE + kMaxKw * 4];
+  uint32_t* const pmw = (uint32_t*)(smem + 2 * R::SIZE);
   const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), hi = lane >> 5, r32 = lane & 31;
   const int BHq = a.B * a.Hq, G = a.Hq / a.Hkv;
   const int x = blockIdx.x;
@@ -359,14 +365,19 @@ __global__ __launch_bounds__(NW * 64, NW == 4 ? 2 : 1) void bwd_row_kernel(BwdAr
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // this block's tiles are in; every wave is done with the previous block
-    if (jn < nvalid) issue(smem + ((n + 1) & 1) * R::SIZE, jn, pn);
+    // the Q operand's reload completes inside its branch, before the next
+    // block's direct loads go out: left pending, it made the compiler wait
+    // at the products of every step (switching or not) for every load in
+    // flight, the prefetch included
     if (pc != qph) {  // from the FP4 blocks to the promoted ones
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) acc[dt] *= tacc;
 #pragma unroll
       for (int kk = 0; kk < D / 16; ++kk) qx[kk] = ld8h(qrs, (qrow * D + kk * 16 + hi * 8) * 2);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
       qph = pc;
     }
+    if (jn < nvalid) issue(smem + ((n + 1) & 1) * R::SIZE, jn, pn);
     const bool f16 = pc != 0;
     const char* buf = smem + (n & 1) * R::SIZE;
     // S^T (and dP^T): lane (r32, hi) reads chunk 2 kk + hi of slot mt*32 + r32
@@ -644,6 +655,14 @@ __global__ __launch_bounds__(256, MODE == kKeyDv ? 3 : 2) void bwd_key_kernel(Bw
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();  // this step's tiles are in; every wave is done with the previous step
     lane_offsets();
+    // a path switch reloads the K (and V) operands and waits for them
+    // before the next step's direct loads go out: left pending, the reload
+    // made the compiler wait at the products of every step for every load
+    // in flight, the prefetch included
+    if ((int)f16 != cur) {
+      load_kv(f16);
+      __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    }
     uint32_t wn = 0;
     if (n + 1 < nsteps) {
       wn = __builtin_amdgcn_readfirstlane(wnext);
@@ -653,7 +672,6 @@ __global__ __launch_bounds__(256, MODE == kKeyDv ? 3 : 2) void bwd_key_kernel(Bw
     }
     // (steps whose pairs are all masked for this wave add zeros: a branch
     // around the products would make the compiler copy the accumulators)
-    if ((int)f16 != cur) load_kv(f16);
     const char* qrows = buf + (f16 ? St::Q16 : St::QD);
     const char* dob = buf + St::DO;
     const float* l2 = (const float*)(buf + St::L2);
