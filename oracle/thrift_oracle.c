@@ -27,6 +27,10 @@
  * (-ffp-contract=off): every rounding is the one written.
  *
  * Parity pins for each function live in tests/ (see the test files' headers).
+ * Two readings are pinned only as implemented, since nothing on the pages
+ * confirms or refutes them (parity unpinned as readings): the NVFP4
+ * second-level scale taken per (batch, head) slice, and the row sum taken
+ * over the unquantised probabilities on both paths.
  */
 #include "thrift_oracle.h"
 
