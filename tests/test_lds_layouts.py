@@ -160,3 +160,45 @@ def test_forward_mx_stage(D):
     for dt in range(D // 32):
         addrs = [(dt * 32 + (l & 31)) * 32 + vswz(dt * 32 + (l & 31), l >> 5) * 16 for l in range(64)]
         assert worst_conflict(addrs, 16, 8) == 1 and worst_conflict(addrs, 16, 16) == 1
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_backward_prep_v_tile(D):
+    """backward.hip bwd_prep_kernel, V role: thread t of 256 decodes channels
+    2dp, 2dp+1 (dp = t % (D/2)) of keys kq*KPG .. kq*KPG+KPG-1 (kq = t // (D/2),
+    KPG = 64 / (256 // (D/2))) and writes each key's channel pair as one word at
+    half (key*RS + 2dp) of the tile (RS = D + 8 halves per row); the tile then
+    leaves as 16-byte row chunks, thread c reading row c // (D/8), halves
+    8 (c % (D/8)) ..  Every element is written once and read once, each wave's
+    word writes hit every bank at most once, and the chunk reads are free of
+    conflicts within each 8-lane pass."""
+    NP, RS = D // 2, D + 8
+    KPG = 64 // (256 // NP)
+    written = collections.Counter()
+    for w in range(4):
+        addrs_by_e = collections.defaultdict(list)
+        for lane in range(64):
+            t = w * 64 + lane
+            dp, kq = t % NP, t // NP
+            for e in range(KPG):
+                key = kq * KPG + e
+                half = key * RS + 2 * dp
+                written[(key, 2 * dp)] += 1
+                written[(key, 2 * dp + 1)] += 1
+                addrs_by_e[e].append(half * 2)
+        for e, addrs in addrs_by_e.items():  # one ds_write_b32 per element index
+            assert worst_conflict(addrs, 4, 64) == 1
+    assert set(written) == {(k, d) for k in range(64) for d in range(D)}
+    assert all(v == 1 for v in written.values())
+    read = collections.Counter()
+    for it in range((64 * D // 8) // 256):
+        addrs = []
+        for t in range(256):
+            c = t + it * 256
+            r, c8 = c // (D // 8), (c % (D // 8)) * 8
+            addrs.append((r * RS + c8) * 2)
+            for u in range(8):
+                read[(r, c8 + u)] += 1
+        for w in range(4):
+            assert worst_conflict(addrs[w * 64:(w + 1) * 64], 16, 8) == 1
+    assert read == written
