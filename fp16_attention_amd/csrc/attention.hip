@@ -1401,8 +1401,10 @@ static thrift_status launch_attn(const AttnArgs& a, hipStream_t stream) {
 // The new queries are the last Sq positions (causal masks aligned at the
 // sequence ends).  One query block holds all of them, so each query head has
 // one promoted list.  The G query heads sharing a key head and their Sq rows
-// are packed as the 32 query columns of the transposed products (column c =
-// g*Sq + r), so one K/V tile serves the whole group; the key range is split
+// are packed as the query columns of the transposed products (column c =
+// g*Sq + r), 32 per column group, so one K/V tile serves 32 columns of the
+// group (a workgroup takes one column group; with more than 32 columns the
+// key head's K/V are read once per group); the key range is split
 // across workgroups and, inside one, across its four waves (each wave its own
 // blocks of the shared stages), every wave leaving a partial (m, l, acc)
 // per column.  Promoted blocks run in one-wave units of their own (one per
@@ -1413,6 +1415,7 @@ static thrift_status launch_attn(const AttnArgs& a, hipStream_t stream) {
 struct DecodeArgs {
   AttnArgs kv;     // K/V (S = Sk keys), Q pointers with Sq rows, idx/cnt of the one query block
   int Sq, G, nsplit, bpw, nvalid;
+  int ncg;         // column groups: ceil(G*Sq / 32)
   float* part4;    // [B*Hkv*nsplit*4][G*Sq][D + 4]: acc[D], m, l, 2 pad
   float* part16;   // [B*Hq*kmax][Sq][D + 4]
 };
@@ -1447,12 +1450,12 @@ __device__ inline void decode_fp4_body(const DecodeArgs& d, int unit, char* smem
   constexpr int NT = kDecWaves * 64;
   const AttnArgs& a = d.kv;
   const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), hi = lane >> 5;
-  const int sidx = unit % d.nsplit;
-  const size_t bhk = unit / d.nsplit;
+  const int sidx = unit % d.nsplit, cg = (unit / d.nsplit) % d.ncg;
+  const size_t bhk = unit / d.nsplit / d.ncg;
   const int b = (int)(bhk / a.Hkv), hk = (int)(bhk % a.Hkv);
   const int Sk = a.S, Sq = d.Sq, G = d.G, ncol = G * Sq;
   const int jb = sidx * d.bpw, je = min(jb + d.bpw, d.nvalid);
-  const int col = lane & 31, g = col / Sq, r = col % Sq;
+  const int col = cg * 32 + (lane & 31), g = col / Sq, r = col % Sq;
   const bool col_ok = col < ncol;
   const int hq = hk * G + (col_ok ? g : 0);
   const int qpos = Sk - Sq + r;
@@ -1557,12 +1560,12 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void decode_nv4_kernel(DecodeArg
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const AttnArgs& a = d.kv;
   const int t = threadIdx.x, lane = t & 63, w = __builtin_amdgcn_readfirstlane(t >> 6), hi = lane >> 5;
-  const int unit = blockIdx.x, sidx = unit % d.nsplit;
-  const size_t bhk = unit / d.nsplit;
+  const int unit = blockIdx.x, sidx = unit % d.nsplit, cg = (unit / d.nsplit) % d.ncg;
+  const size_t bhk = unit / d.nsplit / d.ncg;
   const int b = (int)(bhk / a.Hkv), hk = (int)(bhk % a.Hkv);
   const int Sk = a.S, Sq = d.Sq, G = d.G, ncol = G * Sq;
   const int jb = sidx * d.bpw, je = min(jb + d.bpw, d.nvalid);
-  const int col = lane & 31, g = col / Sq, r = col % Sq;
+  const int col = cg * 32 + (lane & 31), g = col / Sq, r = col % Sq;
   const bool col_ok = col < ncol;
   const int hq = hk * G + (col_ok ? g : 0);
   const int qpos = Sk - Sq + r;
@@ -1991,8 +1994,12 @@ static thrift_status launch_decode(DecodeArgs& d, int fmt, hipStream_t stream) {
         return THRIFT_OK;
       }) != THRIFT_OK)
     return THRIFT_EHIP;
+  // the split kernels' LDS: their stages and the group's promoted-bit table
+  // (G words per 32 key blocks); shapes it does not fit launch nothing
   const size_t pbytes = (size_t)d.G * ((d.nvalid + 31) / 32) * 4;
-  const int n4wg = a.B * a.Hkv * d.nsplit, n16 = a.B * a.Hq * a.kmax;
+  const size_t lsplit = (fmt == THRIFT_MXFP4 ? 4 * (size_t)M::SIZE : kDecWaves * (size_t)Lds<D>::STAGE) + pbytes;
+  if (lsplit > 160 * 1024) return THRIFT_EUNSUPPORTED;
+  const int n4wg = a.B * a.Hkv * d.ncg * d.nsplit, n16 = a.B * a.Hq * a.kmax;
   if (fmt == THRIFT_MXFP4) {
     const size_t l4 = 4 * (size_t)M::SIZE + pbytes, l16 = (size_t)kDecWaves * D * Lds<D>::VROWH * 2;
     const size_t lds = l4 > l16 ? l4 : l16;
@@ -2023,7 +2030,7 @@ extern "C" thrift_status thrift_attention_decode(
   if (Hq % Hkv != 0 || (o_is_fp32 != 0 && o_is_fp32 != 1)) return THRIFT_EINVAL;
   if (!(sm_scale > 0.0f) || !(sm_scale < 1e30f)) return THRIFT_EINVAL;
   if (D != 64 && D != 128) return THRIFT_EUNSUPPORTED;
-  if (block_k != 64 || (Hq / Hkv) * Sq > 32 || Sq > 128) return THRIFT_EUNSUPPORTED;
+  if (block_k != 64 || Sq > 32 || (Hq / Hkv) * Sq > 128) return THRIFT_EUNSUPPORTED;
   if (Sk > 262144 || kmax > cdiv(Sk, block_k)) return THRIFT_EUNSUPPORTED;
   for (const void* p : {q16, k16, v16, (const void*)q4_codes, (const void*)k4_codes,
                         (const void*)v4_codes, (const void*)o, (const void*)workspace})
@@ -2062,6 +2069,7 @@ extern "C" thrift_status thrift_attention_decode(
   a.sm_log2 = sm_scale * 1.4426950408889634f;
   d.Sq = Sq;
   d.G = Hq / Hkv;
+  d.ncg = cdiv(d.G * Sq, 32);
   d.nvalid = valid_kv_blocks_kv(0, Sq, Sk, 128, 64, causal);
   decode_split(B, Hkv, d.nvalid, d.nsplit, d.bpw);
   d.part4 = (float*)workspace;

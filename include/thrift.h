@@ -369,9 +369,14 @@ size_t thrift_attention_decode_workspace_bytes(int B, int Hq, int Hkv, int Sq, i
  *     aligned; its contents are scratch.
  *   q4_tscale, k4_tscale, v4_tscale: the slice scales, required for
  *     THRIFT_NVFP4 (EINVAL if NULL), ignored for THRIFT_MXFP4.
- * Supported: both formats, D 64 or 128, block_k 64, Sq <= 128 and
- * (Hq/Hkv)*Sq <= 32 (the query heads of a key head and their rows share one
- * 32-column tile), Sk <= 262144. */
+ * Supported: both formats, D 64 or 128, block_k 64, Sq <= 32 and
+ * (Hq/Hkv)*Sq <= 128 (the query heads of a key head and their rows are the
+ * columns of 32-column tiles; the key head's K/V are read once per 32
+ * columns), Sk <= 262144, and the promoted-block table of a key head's
+ * query heads (Hq/Hkv words per 32 valid key blocks) beside the split
+ * kernel's stages in 160 KB of LDS, which limits only THRIFT_NVFP4 at D 128:
+ * Hq/Hkv * ceil(ceil(Sk/64)/32) <= 5120.  Other shapes return
+ * THRIFT_EUNSUPPORTED and launch nothing. */
 thrift_status thrift_attention_decode(const void* q16, const void* k16, const void* v16,
                                       const uint8_t* q4_codes, const uint8_t* q4_scales,
                                       const float* q4_tscale, const uint8_t* k4_codes,

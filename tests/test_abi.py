@@ -126,7 +126,8 @@ def test_decode_validation(lib):
     assert call(fmt=0) == 1  # NVFP4 needs its slice scales
     assert call(fmt=5) == 1
     assert call(Sq=600) == 1  # more queries than keys
-    assert call(Sq=9, Hq=8, Hkv=2) == 2  # 4 heads x 9 rows > 32 columns
+    assert call(Sq=33, Hq=2, Hkv=2) == 2  # more than 32 rows
+    assert call(Sq=9, Hq=32, Hkv=2) == 2  # 16 heads x 9 rows > 128 columns
     assert call(D=96) == 2
     assert call(kmax=9) == 2
     assert call(o=A + 4) == 3

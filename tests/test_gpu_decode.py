@@ -33,6 +33,12 @@ CASES = {
     "nv_no_fp16": (1, 8, 2, 2, 1500, 128, True, 0, 0),
     "nv_g32_one_token": (1, 32, 1, 1, 3000, 128, True, 500, 0),
     "nv_long_cache": (1, 8, 2, 1, 8192, 128, True, 500, 0),
+    # more than 32 query columns per key head: one workgroup per 32-column group
+    "rows8_gqa8": (1, 16, 2, 8, 2048, 128, True, 500, 1),  # 64 columns
+    "g16_rows8": (1, 16, 1, 8, 1500, 128, True, 1000, 1),  # 128 columns
+    "d64_g6_rows9": (1, 12, 2, 9, 777, 64, False, 2500, 1),  # 54: a ragged last group
+    "nv_rows8_gqa8": (1, 16, 2, 8, 2048, 128, True, 500, 0),
+    "nv_g4_rows32": (1, 8, 2, 32, 1200, 128, True, 1000, 0),  # 128 columns of 32 rows per head
 }
 
 
