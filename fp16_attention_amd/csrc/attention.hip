@@ -1553,6 +1553,14 @@ __device__ inline void decode_fp4_body(const DecodeArgs& d, int unit, char* smem
 // registers) and runs the NVFP4 tile of the prefill kernel on the fp16
 // matrix cores.  Each column's score scale carries its own head's Q slice
 // scale.
+// Orders this wave's LDS accesses before and after it (its lanes' writes
+// before its later reads, its reads before its later writes); no other wave
+// takes part.
+__device__ inline void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+}
+
 template <int D>
 __global__ __launch_bounds__(kDecWaves * 64, 1) void decode_nv4_kernel(DecodeArgs d) {
   using L = Lds<D>;
@@ -1603,13 +1611,16 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void decode_nv4_kernel(DecodeArg
   RowState<D> st;
   init_state<D>(st);
 
+  // each wave fills and reads only its own stage, and one wave's LDS
+  // operations complete in order, so the waves order their stages with
+  // wavefront-scope fences instead of workgroup barriers
   const int nss = je > jb ? cdiv(je - jb, kDecWaves) : 0;
   Nv4Stager<D, 64> stg;
   if (nss > 0 && jb + w < je) {
     stg.load(a, bhk, jb + w, lane);
     stg.store(stage, lane);
   }
-  __syncthreads();
+  wave_lds_fence();
   for (int k = 0; k < nss; ++k) {
     const int j = jb + kDecWaves * k + w, jn = j + kDecWaves;
     const bool next = k + 1 < nss && jn < je;
@@ -1629,9 +1640,9 @@ __global__ __launch_bounds__(kDecWaves * 64, 1) void decode_nv4_kernel(DecodeArg
       const bool need_mask = (a.causal && key0 + kBk - 1 > Sk - Sq) || key0 + kBk > Sk;
       fp4_nv_softmax_pv<D>(st, sc, stage, c, lk, ilk, key0, qpos, Sk, a.causal, need_mask, lane);
     }
-    __syncthreads();
+    wave_lds_fence();
     if (next) stg.store(stage, lane);
-    __syncthreads();
+    wave_lds_fence();
   }
   if (col_ok) {
     const size_t u4 = (bhk * d.nsplit + sidx) * kDecWaves + w;
