@@ -12,8 +12,11 @@ from fp16_attention_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-# (B, Hq, Hkv, Sq, Sk, D, causal, topk_bp): the larger call first, then the smaller
-CALLS = [(4, 16, 4, 4, 5000, 128, True, 500), (1, 4, 2, 1, 700, 64, True, 1000)]
+# (B, Hq, Hkv, Sq, Sk, D, causal, topk_bp): calls in a row on the shared array, each
+# later one smaller than the one before (the first with 64 query columns per key
+# head, two 32-column groups)
+CALLS = [(2, 16, 2, 8, 3000, 128, True, 500), (2, 16, 4, 4, 2500, 128, True, 500),
+         (1, 4, 2, 1, 700, 64, True, 1000)]
 
 
 def _inputs(dev, fmt, B, Hq, Hkv, Sq, Sk, D, causal, bp, seed):
