@@ -166,3 +166,35 @@ def test_cache_maintenance_matches_oracle(oracle, fmt):
     ridx, rcnt, _ = oracle.select(d["q"], knew, 128, 64, True, -1, 1000)
     assert np.array_equal(cnt_a.cpu().numpy(), rcnt)
     assert np.array_equal(idx_a.cpu().numpy()[..., : ridx.shape[-1]], ridx)
+
+
+def test_decode_nvfp4_rejects_a_promoted_table_beyond_its_lds():
+    """64 query heads on one key head against a 262144-key cache: the NVFP4
+    split kernel's promoted-block table (64 heads x 128 words) does not fit
+    beside its four fp16 stages, so the call returns THRIFT_EUNSUPPORTED and
+    launches nothing; MXFP4 (smaller stages) takes the same shape.  Every
+    buffer is real and sized for the shape."""
+    import torch
+
+    from fp16_attention_amd import _lib, api
+
+    dev = torch.device("cuda:0")
+    Hq, Hkv, Sq, Sk, D = 64, 1, 1, 262144, 128
+    note(f"[decode] lds budget: Hq{Hq} Hkv{Hkv} Sq{Sq} Sk{Sk} D{D}")
+    g = torch.Generator(device="cpu").manual_seed(5)
+    q = torch.randn((1, Hq, Sq, D), generator=g).to(torch.float16).to(dev)
+    k = torch.randn((1, Hkv, Sk, D), generator=g).to(torch.float16).to(dev)
+    v = torch.randn((1, Hkv, Sk, D), generator=g).to(torch.float16).to(dev)
+    idx, cnt = api.thrift_select_blocks(q, k, 128, 64, True, -1, 500)
+    for fmt in (api.THRIFT_NVFP4, api.THRIFT_MXFP4):
+        q4 = api.thrift_quantize_fp4(q, api.THRIFT_GROUP_D, fmt)
+        k4 = api.thrift_quantize_fp4(k, api.THRIFT_GROUP_D, fmt)
+        v4 = api.thrift_quantize_fp4(v, api.THRIFT_GROUP_S, fmt)
+        if fmt == api.THRIFT_NVFP4:
+            with pytest.raises(_lib.ThriftError) as e:
+                api.thrift_attention_decode(q, k, v, q4, k4, v4, idx, cnt, 64, True, out_fp32=True)
+            assert e.value.status == _lib.THRIFT_EUNSUPPORTED
+        else:
+            o = api.thrift_attention_decode(q, k, v, q4, k4, v4, idx, cnt, 64, True, out_fp32=True)
+            torch.cuda.synchronize()
+            assert torch.isfinite(o).all()
